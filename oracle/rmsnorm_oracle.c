@@ -1,0 +1,264 @@
+/*
+ * Plain fp64 CPU reference for RMSNorm forward and backward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no source,
+ * header, table or helper with the GPU library, and neither includes the other.
+ *
+ * What it computes (the plain definition; every stored input is widened
+ * exactly to double, eps and offset arrive as float and are widened exactly):
+ *
+ *   forward   (RMSNorm; Liger-Kernel PR #1388 "Summary" and FlyDSL PR #855
+ *              "Implementation": per-row two-pass RMS math with eps and offset
+ *              as runtime scalars)
+ *       ms_i   = (1/N) sum_j v_ij^2
+ *       rstd_i = 1 / sqrt(ms_i + eps)
+ *       y_ij   = v_ij * rstd_i * (gamma_j + offset)
+ *     One rounding to the storage type happens after the gamma multiply
+ *     ("llama mode" of Liger-Kernel PR #1388 "Results", read as fp32 compute
+ *     and a single cast of the final product).
+ *
+ *   fused residual add (FlyDSL PR #855 "Hybrid atomic / two-stage backward":
+ *              fused-add is a specialization of the same op)
+ *       h_ij = round_T(x_ij + r_ij);  (y, rstd) = forward(h)
+ *
+ *   backward  (chain rule of the forward; rstd recomputed here from v)
+ *       w_j   = gamma_j + offset,  g_ij = dy_ij * w_j,  xhat_ij = v_ij * rstd_i
+ *       c_i   = (1/N) sum_j g_ij * xhat_ij
+ *       dx_ij = rstd_i * (g_ij - xhat_ij * c_i)      [+ dh_ij, fused-add]
+ *       dgamma_j = sum_i dy_ij * xhat_ij              (fp32 accumulation and a
+ *                  write in the parameter dtype: FlyDSL PR #855
+ *                  "512-thread vec8 fast path" and "Hybrid ... backward")
+ *     The fused-add backward adds the gradient flowing into the residual
+ *     output, dh, to dx; dx is the residual gradient (FlyDSL PR #855,
+ *     "Hybrid atomic / two-stage backward" and "Fused-add RMSNorm backward").
+ *
+ * Rounding to a storage type is round-to-nearest, ties to even (FlyDSL PR #855,
+ * "512-thread vec8 fast path": software RNE / hardware conversion).
+ *
+ * Parallelism: OpenMP over independent rows (forward, dx) and over independent
+ * column ranges (dgamma, each column summed over rows in row order).  No sum is
+ * reordered.
+ *
+ * Pins (tests/test_oracle_pins.py): finite differences, the RMS invariant, the
+ * sum_j v_j dx_j identity, closed forms (N = 1, constant rows, eps = 0 scale
+ * invariance, gamma/offset equivalence, fused-add reductions), the fp64
+ * torch.nn.functional.rms_norm with autograd, hand-worked fixtures under
+ * tests/golden/, and brute-force nearest-value rounding.
+ */
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+enum { ORACLE_OK = 0, ORACLE_EINVAL = 1, ORACLE_ENOMEM = 2 };
+
+static int dtype_ok(int dt) { return dt == ORACLE_F32 || dt == ORACLE_BF16 || dt == ORACLE_F64; }
+
+/* Widen one stored element to double (exact for all three storage types). */
+static double load_elem(int dt, const void *base, int64_t i)
+{
+    if (dt == ORACLE_F64)
+        return ((const double *)base)[i];
+    if (dt == ORACLE_F32)
+        return (double)((const float *)base)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Nearest bf16 to v, ties to even, as a bit pattern.
+ * bf16 keeps 8 significant bits and float32's exponent range; below 2^-126 the
+ * spacing is fixed at 2^-133.  v / spacing is an exact power-of-two scaling,
+ * so nearbyint (ties to even in the default rounding mode) gives the answer. */
+static uint16_t bf16_bits_from_double(double v)
+{
+    if (isnan(v))
+        return (uint16_t)(signbit(v) ? 0xFFC0u : 0x7FC0u);
+    if (isinf(v) || v == 0.0) {
+        float f = (float)v;
+        uint32_t b;
+        memcpy(&b, &f, sizeof b);
+        return (uint16_t)(b >> 16);
+    }
+    int e;
+    frexp(fabs(v), &e); /* |v| = m * 2^e with m in [0.5, 1), so floor(log2|v|) = e - 1 */
+    int q = e - 1;
+    if (q < -126)
+        q = -126;
+    double spacing = ldexp(1.0, q - 7);
+    double r = nearbyint(v / spacing) * spacing;
+    if (fabs(r) >= 0x1p128) /* rounded past the largest finite bf16 */
+        return (uint16_t)(r < 0 ? 0xFF80u : 0x7F80u);
+    float f = (float)r; /* exact: r has at most 8 significant bits */
+    uint32_t b;
+    memcpy(&b, &f, sizeof b);
+    return (uint16_t)(b >> 16);
+}
+
+/* Store v rounded (nearest, ties to even) into element i of a storage array. */
+static void store_elem(int dt, void *base, int64_t i, double v)
+{
+    if (dt == ORACLE_F64)
+        ((double *)base)[i] = v;
+    else if (dt == ORACLE_F32)
+        ((float *)base)[i] = (float)v; /* C conversion: nearest, ties to even */
+    else
+        ((uint16_t *)base)[i] = bf16_bits_from_double(v);
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* Round n doubles to the storage type dt. */
+int oracle_round(int dt, const double *src, int64_t n, void *dst)
+{
+    if (!dtype_ok(dt) || !src || !dst || n < 0)
+        return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i)
+        store_elem(dt, dst, i, src[i]);
+    return ORACLE_OK;
+}
+
+/* rstd_i = 1 / sqrt((1/N) sum_j v_ij^2 + eps) */
+static double row_rstd(int dt, const void *v, int64_t row, int64_t N, double eps)
+{
+    double ss = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+        double a = load_elem(dt, v, row * N + j);
+        ss += a * a;
+    }
+    double ms = ss / (double)N;
+    return 1.0 / sqrt(ms + eps);
+}
+
+/* Forward.  y64 [M, N] (may be NULL), rstd64 [M] (may be NULL). */
+int oracle_fwd(int dt, const void *v, const void *gamma, int64_t M, int64_t N,
+               float eps, float offset, double *y64, double *rstd64)
+{
+    if (!dtype_ok(dt) || !v || !gamma || M < 0 || N <= 0)
+        return ORACLE_EINVAL;
+    const double e = (double)eps, off = (double)offset;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        double rstd = row_rstd(dt, v, i, N, e);
+        if (rstd64)
+            rstd64[i] = rstd;
+        if (y64) {
+            for (int64_t j = 0; j < N; ++j) {
+                double w = load_elem(dt, gamma, j) + off;
+                y64[i * N + j] = load_elem(dt, v, i * N + j) * rstd * w;
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Fused residual add then forward.  h_out [M, N] in storage type dt receives
+ * round_T(x + r); the forward normalises that stored h. */
+int oracle_fused_add_fwd(int dt, const void *x, const void *r, const void *gamma,
+                         int64_t M, int64_t N, float eps, float offset,
+                         void *h_out, double *y64, double *rstd64)
+{
+    if (!dtype_ok(dt) || !x || !r || !gamma || !h_out || M < 0 || N <= 0)
+        return ORACLE_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            store_elem(dt, h_out, i * N + j,
+                       load_elem(dt, x, i * N + j) + load_elem(dt, r, i * N + j));
+    return oracle_fwd(dt, h_out, gamma, M, N, eps, offset, y64, rstd64);
+}
+
+/* Backward.  v is the forward's input (h for the fused-add variant); dh, when
+ * not NULL, is added to dx.  Outputs (each may be NULL):
+ *   dx64 [M, N]; dgamma64 [N];
+ *   c64 [M]     = (1/N) sum_j g_ij xhat_ij;
+ *   sabs64 [M]  = (1/N) sum_j |g_ij xhat_ij|  (the size of the terms that
+ *                 cancel in dx, used by the tests' tolerance floor). */
+int oracle_bwd(int dt, const void *dy, const void *v, const void *gamma, const void *dh,
+               int64_t M, int64_t N, float eps, float offset,
+               double *dx64, double *dgamma64, double *c64, double *sabs64)
+{
+    if (!dtype_ok(dt) || !dy || !v || !gamma || M < 0 || N <= 0)
+        return ORACLE_EINVAL;
+    const double e = (double)eps, off = (double)offset;
+
+    double *rstd = (double *)malloc((size_t)(M > 0 ? M : 1) * sizeof(double));
+    if (!rstd)
+        return ORACLE_ENOMEM;
+
+    /* rows: rstd, c, sabs, dx */
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        rstd[i] = row_rstd(dt, v, i, N, e);
+        double dot = 0.0, dabs = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            double w = load_elem(dt, gamma, j) + off;
+            double g = load_elem(dt, dy, i * N + j) * w;
+            double xhat = load_elem(dt, v, i * N + j) * rstd[i];
+            dot += g * xhat;
+            dabs += fabs(g * xhat);
+        }
+        double c = dot / (double)N;
+        if (c64)
+            c64[i] = c;
+        if (sabs64)
+            sabs64[i] = dabs / (double)N;
+        if (dx64) {
+            for (int64_t j = 0; j < N; ++j) {
+                double w = load_elem(dt, gamma, j) + off;
+                double g = load_elem(dt, dy, i * N + j) * w;
+                double xhat = load_elem(dt, v, i * N + j) * rstd[i];
+                double d = rstd[i] * (g - xhat * c);
+                if (dh)
+                    d += load_elem(dt, dh, i * N + j);
+                dx64[i * N + j] = d;
+            }
+        }
+    }
+
+    /* columns: dgamma_j = sum_i dy_ij * xhat_ij, each column summed over the
+     * rows in row order; threads own disjoint column ranges */
+    if (dgamma64) {
+#pragma omp parallel
+        {
+            int64_t nt = 1, t = 0;
+#ifdef _OPENMP
+            nt = omp_get_num_threads();
+            t = omp_get_thread_num();
+#endif
+            int64_t j0 = N * t / nt, j1 = N * (t + 1) / nt;
+            for (int64_t j = j0; j < j1; ++j)
+                dgamma64[j] = 0.0;
+            for (int64_t i = 0; i < M; ++i)
+                for (int64_t j = j0; j < j1; ++j)
+                    dgamma64[j] += load_elem(dt, dy, i * N + j) * (load_elem(dt, v, i * N + j) * rstd[i]);
+        }
+    }
+    free(rstd);
+    return ORACLE_OK;
+}

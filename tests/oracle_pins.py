@@ -1,0 +1,407 @@
+"""Pins of the fp64 CPU reference against facts fixed outside it.
+
+Each pin takes a loaded reference library (so the mutation tests can run the
+same pins against deliberately broken builds) and raises AssertionError on a
+mismatch.  What pins what:
+
+  finite_differences   backward and fused-add backward (dx, dgamma, d/dresidual)
+  rms_invariant        forward: RMS_j(y_ij / w_j) = sqrt(ms / (ms + eps))
+  orthogonality        dx: sum_j v_j dx_j = eps * rstd^3 * sum_j v_j g_j
+  closed_form_n1       forward and backward at N = 1
+  constant_row         forward on a constant row
+  scale_invariance     eps = 0: y(a v) = y(v), dx(a v) = dx(v) / a, dgamma(a v) = dgamma(v)
+  offset_equivalence   (gamma, offset) gives the same as (gamma + offset, 0)
+  fused_reductions     fused-add with r = 0 / dh = 0 reduces to the plain op
+  torch_fp64           torch.nn.functional.rms_norm in float64 with autograd
+  golden               hand-worked fixtures (tests/golden/hand_worked.txt)
+  storage_widening     bf16/f32 storage widened exactly (same answers as f64 storage)
+  rounding             nearest-even rounding vs torch casts and brute force
+"""
+
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from rmsnorm_inputs import bf16_bits_to_f32, f32_to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_worked.txt")
+
+
+def _f32(x: float) -> float:
+    """The value the reference sees for a float argument (widened float32)."""
+    return float(np.float32(x))
+
+
+def _rand(rng, shape, scale=1.0):
+    return (scale * rng.standard_normal(shape)).astype(np.float64)
+
+
+def _loss(lib, v, gamma, dy, eps, offset):
+    y, _ = oracle.fwd(v, gamma, "f64", eps, offset, lib=lib)
+    return float(np.sum(dy * y))
+
+
+def _cancel_scale(v, gamma, dy, eps, offset, out):
+    """s_ij = rstd_i (|g_ij| + |xhat_ij| (|c_i| + S_i)): size of the terms that cancel in dx."""
+    w = gamma + _f32(offset)
+    rstd = 1.0 / np.sqrt(np.mean(v * v, axis=1) + _f32(eps))
+    g = dy * w
+    xhat = v * rstd[:, None]
+    return rstd[:, None] * (np.abs(g) + np.abs(xhat) * (np.abs(out["c64"]) + out["sabs64"])[:, None])
+
+
+def finite_differences(lib):
+    rng = np.random.default_rng(11)
+    worst = 0.0
+    for M in (1, 2, 3):
+        for N in (1, 2, 3, 7, 8, 16):
+            for eps in (1e-6, 0.5):
+                for offset in (0.0, 1.0):
+                    v = _rand(rng, (M, N))
+                    gamma = _rand(rng, (N,), 0.5) + 1.0
+                    dy = _rand(rng, (M, N))
+                    out = oracle.bwd(dy, v, gamma, "f64", eps, offset, lib=lib)
+                    s = _cancel_scale(v, gamma, dy, eps, offset, out)
+                    for i in range(M):
+                        for j in range(N):
+                            h = 1e-6 * max(1.0, abs(v[i, j]))
+                            vp, vm = v.copy(), v.copy()
+                            vp[i, j] += h
+                            vm[i, j] -= h
+                            fd = (_loss(lib, vp, gamma, dy, eps, offset) - _loss(lib, vm, gamma, dy, eps, offset)) / (vp[i, j] - vm[i, j])
+                            ref = out["dx64"][i, j]
+                            tol = 1e-7 * max(abs(ref), s[i, j])
+                            err = abs(fd - ref)
+                            worst = max(worst, err / max(abs(ref), s[i, j]))
+                            assert err <= tol, f"dx FD M={M} N={N} eps={eps} off={offset} ({i},{j}): fd={fd} ref={ref}"
+                    for j in range(N):
+                        h = 1e-6 * max(1.0, abs(gamma[j]))
+                        gp, gm = gamma.copy(), gamma.copy()
+                        gp[j] += h
+                        gm[j] -= h
+                        fd = (_loss(lib, v, gp, dy, eps, offset) - _loss(lib, v, gm, dy, eps, offset)) / (gp[j] - gm[j])
+                        ref = out["dgamma64"][j]
+                        rstd = 1.0 / np.sqrt(np.mean(v * v, axis=1) + _f32(eps))
+                        scale = max(abs(ref), float(np.sum(np.abs(dy[:, j] * v[:, j] * rstd))))
+                        assert abs(fd - ref) <= 1e-7 * scale, f"dgamma FD M={M} N={N} j={j}: fd={fd} ref={ref}"
+    # fused-add: L = sum dy * y(h) + sum dh * h with h = x + r; dL/dx = dL/dr = dx
+    for M, N in ((1, 1), (2, 3), (3, 8)):
+        for eps in (1e-6, 0.5):
+            x = _rand(rng, (M, N))
+            r = _rand(rng, (M, N))
+            gamma = _rand(rng, (N,), 0.5) + 1.0
+            dy = _rand(rng, (M, N))
+            dh = _rand(rng, (M, N))
+
+            def loss(xa, ra):
+                hh, y, _ = oracle.fused_add_fwd(xa, ra, gamma, "f64", eps, 0.0, lib=lib)
+                return float(np.sum(dy * y) + np.sum(dh * hh))
+
+            h_store, _, _ = oracle.fused_add_fwd(x, r, gamma, "f64", eps, 0.0, lib=lib)
+            out = oracle.bwd(dy, h_store, gamma, "f64", eps, 0.0, dh=dh, lib=lib)
+            s = _cancel_scale(h_store, gamma, dy, eps, 0.0, out) + np.abs(dh)
+            for i in range(M):
+                for j in range(N):
+                    for which in ("x", "r"):
+                        a = x if which == "x" else r
+                        hstep = 1e-6 * max(1.0, abs(a[i, j]))
+                        ap, am = a.copy(), a.copy()
+                        ap[i, j] += hstep
+                        am[i, j] -= hstep
+                        if which == "x":
+                            fd = (loss(ap, r) - loss(am, r)) / (ap[i, j] - am[i, j])
+                        else:
+                            fd = (loss(x, ap) - loss(x, am)) / (ap[i, j] - am[i, j])
+                        ref = out["dx64"][i, j]
+                        assert abs(fd - ref) <= 1e-7 * max(abs(ref), s[i, j]), f"fused FD d{which} ({i},{j}): fd={fd} ref={ref}"
+    return worst
+
+
+def rms_invariant(lib):
+    rng = np.random.default_rng(12)
+    for N in (1, 5, 64, 1000):
+        for eps in (1e-6, 0.25):
+            v = _rand(rng, (4, N), 2.0)
+            gamma = _rand(rng, (N,), 0.1) + 1.0
+            y, rstd = oracle.fwd(v, gamma, "f64", eps, 0.0, lib=lib)
+            ms = np.mean(v * v, axis=1)
+            lhs = np.sqrt(np.mean((y / gamma) ** 2, axis=1))
+            rhs = np.sqrt(ms / (ms + _f32(eps)))
+            assert np.all(np.abs(lhs - rhs) <= 1e-13 * rhs), (N, eps, lhs, rhs)
+            assert np.all(np.abs(rstd - 1.0 / np.sqrt(ms + _f32(eps))) <= 1e-13 * rstd)
+
+
+def orthogonality(lib):
+    rng = np.random.default_rng(13)
+    for N in (1, 3, 64, 777):
+        for eps in (1e-6, 0.3):
+            for offset in (0.0, 1.0):
+                v = _rand(rng, (5, N))
+                gamma = _rand(rng, (N,), 0.3) + (0.0 if offset else 1.0)
+                dy = _rand(rng, (5, N))
+                out = oracle.bwd(dy, v, gamma, "f64", eps, offset, lib=lib)
+                w = gamma + _f32(offset)
+                g = dy * w
+                ms = np.mean(v * v, axis=1)
+                rstd = 1.0 / np.sqrt(ms + _f32(eps))
+                lhs = np.sum(v * out["dx64"], axis=1)
+                rhs = _f32(eps) * rstd ** 3 * np.sum(v * g, axis=1)
+                s = _cancel_scale(v, gamma, dy, eps, offset, out)
+                bound = 1e-12 * np.sum(np.abs(v) * s, axis=1)
+                assert np.all(np.abs(lhs - rhs) <= bound), (N, eps, offset, lhs, rhs)
+
+
+def closed_form_n1(lib):
+    rng = np.random.default_rng(14)
+    for eps in (1e-6, 0.5, 2.0):
+        v = _rand(rng, (6, 1), 3.0)
+        gamma = np.array([0.7])
+        dy = _rand(rng, (6, 1))
+        e = _f32(eps)
+        y, rstd = oracle.fwd(v, gamma, "f64", eps, 0.0, lib=lib)
+        out = oracle.bwd(dy, v, gamma, "f64", eps, 0.0, lib=lib)
+        den = v * v + e
+        np.testing.assert_allclose(y, v * 0.7 / np.sqrt(den), rtol=1e-14, atol=0)
+        np.testing.assert_allclose(rstd, 1.0 / np.sqrt(den[:, 0]), rtol=1e-14, atol=0)
+        dx_ref = dy * 0.7 * e / den ** 1.5
+        scale = np.abs(dy * 0.7) / np.sqrt(den)  # size of the cancelling terms
+        assert np.all(np.abs(out["dx64"] - dx_ref) <= 1e-13 * np.maximum(np.abs(dx_ref), scale)), (out["dx64"], dx_ref)
+        np.testing.assert_allclose(out["dgamma64"], [np.sum(dy * v / np.sqrt(den))], rtol=1e-13)
+
+
+def constant_row(lib):
+    for a in (0.5, -3.0, 1e-3):
+        for N in (1, 4, 1000):
+            v = np.full((1, N), a)
+            gamma = np.linspace(0.5, 1.5, N)
+            eps = 1e-6
+            y, rstd = oracle.fwd(v, gamma, "f64", eps, 0.0, lib=lib)
+            r = 1.0 / np.sqrt(a * a + _f32(eps))
+            np.testing.assert_allclose(rstd, [r], rtol=1e-14)
+            np.testing.assert_allclose(y[0], a * r * gamma, rtol=1e-14)
+
+
+def scale_invariance(lib):
+    rng = np.random.default_rng(15)
+    for N in (2, 17, 256):
+        v = _rand(rng, (3, N))
+        gamma = _rand(rng, (N,), 0.2) + 1.0
+        dy = _rand(rng, (3, N))
+        y1, _ = oracle.fwd(v, gamma, "f64", 0.0, 0.0, lib=lib)
+        o1 = oracle.bwd(dy, v, gamma, "f64", 0.0, 0.0, lib=lib)
+        for alpha in (4.0, 0.37):
+            y2, _ = oracle.fwd(alpha * v, gamma, "f64", 0.0, 0.0, lib=lib)
+            o2 = oracle.bwd(dy, alpha * v, gamma, "f64", 0.0, 0.0, lib=lib)
+            np.testing.assert_allclose(y2, y1, rtol=1e-13, atol=1e-15)
+            s = _cancel_scale(v, gamma, dy, 0.0, 0.0, o1)
+            assert np.all(np.abs(o2["dx64"] * alpha - o1["dx64"]) <= 1e-13 * np.maximum(np.abs(o1["dx64"]), s))
+            np.testing.assert_allclose(o2["dgamma64"], o1["dgamma64"], rtol=1e-12, atol=1e-13)
+
+
+def offset_equivalence(lib):
+    rng = np.random.default_rng(16)
+    v = _rand(rng, (4, 33))
+    gamma = _rand(rng, (33,), 0.1)
+    dy = _rand(rng, (4, 33))
+    for off in (1.0, 0.5, -2.0):
+        y1, r1 = oracle.fwd(v, gamma, "f64", 1e-6, off, lib=lib)
+        y2, r2 = oracle.fwd(v, gamma + off, "f64", 1e-6, 0.0, lib=lib)
+        np.testing.assert_array_equal(y1, y2)
+        np.testing.assert_array_equal(r1, r2)
+        o1 = oracle.bwd(dy, v, gamma, "f64", 1e-6, off, lib=lib)
+        o2 = oracle.bwd(dy, v, gamma + off, "f64", 1e-6, 0.0, lib=lib)
+        np.testing.assert_array_equal(o1["dx64"], o2["dx64"])
+        np.testing.assert_array_equal(o1["dgamma64"], o2["dgamma64"])
+        # dgamma does not depend on the offset at all
+        o0 = oracle.bwd(dy, v, gamma, "f64", 1e-6, 0.0, lib=lib)
+        np.testing.assert_array_equal(o1["dgamma64"], o0["dgamma64"])
+
+
+def fused_reductions(lib):
+    rng = np.random.default_rng(17)
+    for dt in ("f64", "f32", "bf16"):
+        M, N = 3, 40
+        x64 = rng.standard_normal((M, N)).astype(np.float32)
+        g64 = (1 + 0.1 * rng.standard_normal(N)).astype(np.float32)
+        dy32 = rng.standard_normal((M, N)).astype(np.float32)
+        dh32 = rng.standard_normal((M, N)).astype(np.float32)
+        conv = {"f64": lambda a: a.astype(np.float64), "f32": lambda a: a, "bf16": f32_to_bf16_bits}[dt]
+        x, gamma, dy, dh = conv(x64), conv(g64), conv(dy32), conv(dh32)
+        zero = np.zeros_like(x)
+        h, yf, rf = oracle.fused_add_fwd(x, zero, gamma, dt, 1e-6, 0.0, lib=lib)
+        yp, rp = oracle.fwd(x, gamma, dt, 1e-6, 0.0, lib=lib)
+        np.testing.assert_array_equal(h, x)
+        np.testing.assert_array_equal(yf, yp)
+        np.testing.assert_array_equal(rf, rp)
+        op = oracle.bwd(dy, x, gamma, dt, 1e-6, 0.0, lib=lib)
+        oz = oracle.bwd(dy, x, gamma, dt, 1e-6, 0.0, dh=zero, lib=lib)
+        np.testing.assert_array_equal(op["dx64"], oz["dx64"])
+        od = oracle.bwd(dy, x, gamma, dt, 1e-6, 0.0, dh=dh, lib=lib)
+        dh_wide = {"f64": dh, "f32": dh.astype(np.float64), "bf16": bf16_bits_to_f32(dh).astype(np.float64)}[dt]
+        np.testing.assert_allclose(od["dx64"] - op["dx64"], dh_wide, rtol=1e-12, atol=1e-15)
+        np.testing.assert_array_equal(od["dgamma64"], op["dgamma64"])
+
+
+def torch_fp64(lib):
+    import torch
+
+    rng = np.random.default_rng(18)
+    for M, N, eps, offset in ((4, 64, 1e-6, 0.0), (3, 1000, 1e-5, 1.0), (2, 7, 0.5, 0.0), (5, 1, 1e-6, 0.0)):
+        v = _rand(rng, (M, N))
+        gamma = _rand(rng, (N,), 0.1) + (0.0 if offset else 1.0)
+        dy = _rand(rng, (M, N))
+        y, rstd = oracle.fwd(v, gamma, "f64", eps, offset, lib=lib)
+        out = oracle.bwd(dy, v, gamma, "f64", eps, offset, lib=lib)
+        tv = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+        tw = torch.tensor(gamma + _f32(offset), dtype=torch.float64, requires_grad=True)
+        ty = torch.nn.functional.rms_norm(tv, (N,), weight=tw, eps=_f32(eps))
+        ty.backward(torch.tensor(dy, dtype=torch.float64))
+        np.testing.assert_allclose(y, ty.detach().numpy(), rtol=1e-12, atol=1e-14)
+        s = _cancel_scale(v, gamma, dy, eps, offset, out)
+        assert np.all(np.abs(out["dx64"] - tv.grad.numpy()) <= 1e-12 * np.maximum(np.abs(out["dx64"]), s))
+        np.testing.assert_allclose(out["dgamma64"], tw.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def load_golden(path: str = GOLDEN):
+    cases, cur = {}, None
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            if line.startswith("case "):
+                cur = {}
+                cases[line[5:].strip()] = cur
+                continue
+            key, _, val = line.partition(":")
+            toks = val.split()
+            if key.strip() == "bits":
+                cur["bits"] = [int(t, 16) for t in toks]
+            else:
+                cur[key.strip()] = [float(t) for t in toks]
+    return cases
+
+
+def golden(lib):
+    cases = load_golden()
+    for name, c in cases.items():
+        if name == "bf16_round":
+            got = oracle.round_to(np.array(c["values"]), "bf16", lib=lib)
+            assert list(map(int, got)) == c["bits"], (name, [hex(int(b)) for b in got])
+            continue
+        N = int(c["N"][0])
+        eps, off = c["eps"][0], c["offset"][0]
+        x = np.array(c["x"]).reshape(-1, N)
+        gamma = np.array(c["gamma"])
+        dy = np.array(c["dy"]).reshape(-1, N)
+        if "r" in c:
+            r = np.array(c["r"]).reshape(-1, N)
+            h, y, rstd = oracle.fused_add_fwd(x, r, gamma, "f64", eps, off, lib=lib)
+            np.testing.assert_allclose(h.ravel(), c["h"], rtol=0, atol=0)
+            v = h
+            dh = np.array(c["dh"]).reshape(-1, N)
+        else:
+            y, rstd = oracle.fwd(x, gamma, "f64", eps, off, lib=lib)
+            v, dh = x, None
+        out = oracle.bwd(dy, v, gamma, "f64", eps, off, dh=dh, lib=lib)
+        np.testing.assert_allclose(rstd, c["rstd"], rtol=1e-15, err_msg=name)
+        np.testing.assert_allclose(y.ravel(), c["y"], rtol=1e-15, atol=1e-16, err_msg=name)
+        np.testing.assert_allclose(out["dx64"].ravel(), c["dx"], rtol=1e-14, atol=1e-16, err_msg=name)
+        np.testing.assert_allclose(out["dgamma64"], c["dgamma"], rtol=1e-15, atol=1e-16, err_msg=name)
+
+
+def storage_widening(lib):
+    rng = np.random.default_rng(19)
+    M, N = 3, 50
+    for dt in ("f32", "bf16"):
+        conv = (lambda a: a.astype(np.float32)) if dt == "f32" else f32_to_bf16_bits
+        widen = (lambda a: a.astype(np.float64)) if dt == "f32" else (lambda a: bf16_bits_to_f32(a).astype(np.float64))
+        x = conv(rng.standard_normal((M, N)).astype(np.float32))
+        r = conv(rng.standard_normal((M, N)).astype(np.float32))
+        gamma = conv((1 + 0.1 * rng.standard_normal(N)).astype(np.float32))
+        dy = conv(rng.standard_normal((M, N)).astype(np.float32))
+        y_s, r_s = oracle.fwd(x, gamma, dt, 1e-6, 0.5, lib=lib)
+        y_d, r_d = oracle.fwd(widen(x), widen(gamma), "f64", 1e-6, 0.5, lib=lib)
+        np.testing.assert_array_equal(y_s, y_d)
+        np.testing.assert_array_equal(r_s, r_d)
+        o_s = oracle.bwd(dy, x, gamma, dt, 1e-6, 0.5, dh=r, lib=lib)
+        o_d = oracle.bwd(widen(dy), widen(x), widen(gamma), "f64", 1e-6, 0.5, dh=widen(r), lib=lib)
+        np.testing.assert_array_equal(o_s["dx64"], o_d["dx64"])
+        np.testing.assert_array_equal(o_s["dgamma64"], o_d["dgamma64"])
+        # the fused-add residual sum in storage precision: nearest to the exact sum
+        h, _, _ = oracle.fused_add_fwd(x, r, gamma, dt, 1e-6, 0.0, lib=lib)
+        exact = widen(x) + widen(r)  # exact in float64 for these magnitudes
+        np.testing.assert_array_equal(h, oracle.round_to(exact, dt, lib=lib))
+        np.testing.assert_array_equal(widen(h), _brute_round(exact.ravel(), dt).reshape(h.shape))
+
+
+def _bf16_neighbours(v: float):
+    """All bf16 values adjacent to v (brute force over the bit patterns near it)."""
+    f = np.float32(v)
+    b = int(f32_to_bf16_bits(np.array([f]))[0])
+    cands = []
+    for d in range(-2, 3):
+        bb = (b + d) & 0xFFFF
+        val = float(bf16_bits_to_f32(np.array([bb], np.uint16))[0])
+        if np.isfinite(val):
+            cands.append(val)
+    return cands
+
+
+def _brute_round(vals, dt):
+    """Nearest representable value, ties to the even significand, by exact rational search."""
+    out = []
+    for v in vals:
+        v = float(v)
+        if dt == "f32":
+            cands = [float(np.float32(v)), float(np.nextafter(np.float32(v), np.float32(np.inf))),
+                     float(np.nextafter(np.float32(v), np.float32(-np.inf)))]
+            bits = lambda c: int(np.array([c], np.float32).view(np.uint32)[0])
+        else:
+            cands = _bf16_neighbours(v)
+            bits = lambda c: int(f32_to_bf16_bits(np.array([c], np.float32))[0])
+        fv = Fraction(v)
+        best = min(cands, key=lambda c: (abs(Fraction(c) - fv), bits(c) & 1))
+        out.append(best)
+    return np.array(out)
+
+
+def rounding(lib):
+    import torch
+
+    rng = np.random.default_rng(20)
+    # float32-representable values: torch's float32 -> bfloat16 cast rounds to nearest even
+    f = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 20000).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, 1.00390625, 1.01171875, 3.3895314e38, 1e-40, -1e-41,
+                  1.1754944e-38, np.float32(2.0) ** -133, np.float32(2.0) ** -134, np.inf, -np.inf], np.float32),
+    ])
+    # bf16/float32 subnormals and the normal/subnormal boundary, mostly off the bf16 grid
+    sub = (rng.integers(1, 1 << 23, 4000).astype(np.uint32)).view(np.float32)
+    sub = np.concatenate([sub, -sub, sub * np.float32(1.9)])
+    f = np.concatenate([f, sub])
+    f = f[np.isfinite(f) | np.isinf(f)]
+    got = oracle.round_to(f.astype(np.float64), "bf16", lib=lib)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+    # float64 values that float32 cannot hold (double rounding through float32 would be wrong)
+    d = np.array([1 + 2.0 ** -8 + 2.0 ** -30, 1 + 2.0 ** -8 - 2.0 ** -30, -(1 + 3 * 2.0 ** -8 - 2.0 ** -40),
+                  0.2, 1.4, np.pi, -np.e * 1e20, 2.0 ** -130 * 1.25])
+    d = np.concatenate([d, rng.standard_normal(300) * 7.0])
+    got = oracle.round_to(d, "bf16", lib=lib)
+    np.testing.assert_array_equal(bf16_bits_to_f32(got).astype(np.float64), _brute_round(d, "bf16"))
+    # float32 storage rounding
+    got32 = oracle.round_to(d, "f32", lib=lib)
+    np.testing.assert_array_equal(got32.astype(np.float64), _brute_round(d, "f32"))
+    # NaN stays NaN
+    assert np.isnan(bf16_bits_to_f32(oracle.round_to(np.array([np.nan]), "bf16", lib=lib)))[0]
+
+
+ALL_PINS = [
+    finite_differences, rms_invariant, orthogonality, closed_form_n1, constant_row, scale_invariance,
+    offset_equivalence, fused_reductions, torch_fp64, golden, storage_widening, rounding,
+]

@@ -1,0 +1,64 @@
+"""The pins have teeth: each plausible mistake planted in a copy of the
+reference (dropped term, wrong sign, wrong index, swapped operand, wrong
+rounding) is caught by at least one pin.  CPU only; the planted copies are
+compiled into a temporary directory and never touch the real build."""
+
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+# (name, original text, mutated text, replace-all)
+MUTATIONS = [
+    ("eps_dropped", "return 1.0 / sqrt(ms + eps);", "return 1.0 / sqrt(ms);", False),
+    ("divisor_n_minus_1", "double ms = ss / (double)N;", "double ms = ss / (double)(N > 1 ? N - 1 : N);", False),
+    ("offset_dropped_fwd", "y64[i * N + j] = load_elem(dt, v, i * N + j) * rstd * w;",
+     "y64[i * N + j] = load_elem(dt, v, i * N + j) * rstd * (w - off);", False),
+    ("dx_sign", "double d = rstd[i] * (g - xhat * c);", "double d = rstd[i] * (g + xhat * c);", False),
+    ("c_missing_mean", "double c = dot / (double)N;", "double c = dot;", False),
+    ("dx_missing_rstd", "double d = rstd[i] * (g - xhat * c);", "double d = (g - xhat * c);", False),
+    ("dgamma_unnormalised", "dgamma64[j] += load_elem(dt, dy, i * N + j) * (load_elem(dt, v, i * N + j) * rstd[i]);",
+     "dgamma64[j] += load_elem(dt, dy, i * N + j) * load_elem(dt, v, i * N + j);", False),
+    ("g_uses_v_not_dy", "double g = load_elem(dt, dy, i * N + j) * w;", "double g = load_elem(dt, v, i * N + j) * w;", True),
+    ("rstd_reads_row0", "double a = load_elem(dt, v, row * N + j);", "double a = load_elem(dt, v, j);", False),
+    ("dgamma_wrong_row_rstd", "(load_elem(dt, v, i * N + j) * rstd[i]);", "(load_elem(dt, v, i * N + j) * rstd[0]);", False),
+    ("dh_sign", "d += load_elem(dt, dh, i * N + j);", "d -= load_elem(dt, dh, i * N + j);", False),
+    ("fused_subtracts", "load_elem(dt, x, i * N + j) + load_elem(dt, r, i * N + j)",
+     "load_elem(dt, x, i * N + j) - load_elem(dt, r, i * N + j)", False),
+    ("ties_away", "double r = nearbyint(v / spacing) * spacing;", "double r = round(v / spacing) * spacing;", False),
+    ("bf16_truncates", "double r = nearbyint(v / spacing) * spacing;", "double r = trunc(v / spacing) * spacing;", False),
+    ("bf16_widen_shift", "uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;",
+     "uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 15;", False),
+    ("subnormal_spacing", "if (q < -126)\n        q = -126;", "if (q < -149)\n        q = -149;", False),
+]
+
+# fast pins first so a mutant usually fails within a second
+PIN_ORDER = [
+    oracle_pins.golden, oracle_pins.closed_form_n1, oracle_pins.constant_row, oracle_pins.rms_invariant,
+    oracle_pins.orthogonality, oracle_pins.offset_equivalence, oracle_pins.scale_invariance,
+    oracle_pins.fused_reductions, oracle_pins.storage_widening, oracle_pins.rounding, oracle_pins.torch_fp64,
+    oracle_pins.finite_differences,
+]
+
+
+@pytest.mark.parametrize("name,old,new,replace_all", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(tmp_path, name, old, new, replace_all):
+    src = open(oracle.SOURCE).read()
+    assert old in src, f"mutation site for {name} no longer present in the reference source"
+    mutated = src.replace(old, new) if replace_all else src.replace(old, new, 1)
+    path = tmp_path / "mutant.c"
+    path.write_text(mutated)
+    lib_path = str(tmp_path / "libmutant.so")
+    subprocess.run(oracle.compile_command(str(path), lib_path), check=True, capture_output=True)
+    lib = oracle.load(lib_path)
+    caught_by = None
+    for pin in PIN_ORDER:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught_by = pin.__name__
+            break
+    assert caught_by is not None, f"mutation {name} passed every pin"

@@ -1,0 +1,67 @@
+"""The parity checker accepts exact answers and rejects planted errors (CPU only)."""
+
+import numpy as np
+
+import oracle
+from rmsnorm_inputs import bf16_bits_to_f32
+from tolerance import (DGAMMA_TOL, check_bf16, check_f32, dgamma_error, rel_l2,
+                       ulp_bf16)
+
+
+def test_ulp_bf16_values():
+    assert ulp_bf16(1.0) == 2.0 ** -7
+    assert ulp_bf16(1.99) == 2.0 ** -7
+    assert ulp_bf16(2.0) == 2.0 ** -6
+    assert ulp_bf16(-0.75) == 2.0 ** -8
+    assert ulp_bf16(2.0 ** -130) == 2.0 ** -133
+    assert ulp_bf16(0.0) == 2.0 ** -133
+
+
+def test_bf16_rule_accepts_exact_and_one_ulp():
+    rng = np.random.default_rng(0)
+    ref = rng.standard_normal(10000)
+    bits = oracle.round_to(ref, "bf16")
+    assert check_bf16("exact", bits, ref).ok
+    # one ulp up everywhere is still within 2 ulp
+    assert check_bf16("1ulp", (bits.astype(np.int32) + np.where(ref >= 0, 1, 1)).astype(np.uint16), ref).ok
+
+
+def test_bf16_rule_rejects_three_ulp_at_one_element():
+    rng = np.random.default_rng(1)
+    ref = rng.standard_normal(5000) + 3.0  # positive, away from binade edges issues
+    bits = oracle.round_to(ref, "bf16").copy()
+    bits[1234] += 3
+    r = check_bf16("planted", bits, ref)
+    assert not r.ok and r.fails == 1 and r.worst_index == 1234
+
+
+def test_bf16_floor_only_relaxes_cancelling_elements():
+    ref = np.array([1e-6, 1.0])
+    scale = np.array([1.0, 1.0])
+    got = oracle.round_to(ref + np.array([3e-7, 0.0]), "bf16")  # 30% error on a value cancelled 1e6-fold
+    assert not check_bf16("nofloor", got, ref).ok
+    r = check_bf16("floor", got, ref, scale=scale)
+    assert r.ok and r.floor_active == 1 and r.pure_fails == 1
+    # beyond the floor's own 2 ulp it fails again
+    worse = oracle.round_to(ref + np.array([2e-6, 0.0]), "bf16")
+    assert not check_bf16("floor2", worse, ref, scale=scale).ok
+
+
+def test_f32_rule():
+    ref = np.array([1.0, -2.0, 1e-3])
+    assert check_f32("ok", (ref * (1 + 5e-6)).astype(np.float32), ref).ok
+    assert not check_f32("bad", (ref * (1 + 2e-5)).astype(np.float32), ref).ok
+    assert not check_f32("nan", np.array([np.nan, -2.0, 1e-3], np.float32), ref).ok
+
+
+def test_dgamma_rules():
+    rng = np.random.default_rng(2)
+    ref = rng.standard_normal(4096) * 30
+    good = oracle.round_to(ref, "bf16")
+    assert dgamma_error(good, ref, "bf16") == 0.0
+    scaled = oracle.round_to(ref * (1 + 2e-3), "bf16")
+    assert dgamma_error(scaled, ref, "bf16") > DGAMMA_TOL["bf16"]
+    assert dgamma_error(ref.astype(np.float32), ref, "f32") < DGAMMA_TOL["f32"]
+    assert dgamma_error((ref * (1 + 2e-5)).astype(np.float32), ref, "f32") > DGAMMA_TOL["f32"]
+    # the unrounded fp64 reference would be the wrong target for bf16 (final rounding alone ~1e-3)
+    assert rel_l2(bf16_bits_to_f32(good), ref) > 1e-3

@@ -1,0 +1,127 @@
+"""Parity rules for GPU results against the fp64 reference.
+
+Tolerances (stated for this op: fp32 elementwise relative error <= 1e-5 and
+dgamma relative L2 <= 1e-5; bf16 outputs within 2 bf16 ulp of the fp64 result
+rounded to bf16 and bf16 dgamma relative L2 <= 1e-3), with these readings:
+
+  * ulp_bf16(a) = 2^(floor(log2|a|) - 7), with the fixed subnormal spacing
+    2^-133 below 2^-126.
+  * dx is a difference of terms that can cancel (dy*w against xhat*c).  Any
+    float32 computation carries an absolute error proportional to the size of
+    those terms, s_ij = rstd_i (|g_ij| + |xhat_ij| (|c_i| + S_i)) [+ |dh_ij|],
+    so the bf16 rule is taken at magnitude max(|dx|, 2^-14 s) and the fp32
+    relative rule at max(|dx|, s).  Every report also counts how many elements
+    needed that floor and how many would fail the rule without it.
+  * bf16 dgamma is compared with the fp64 dgamma rounded once to bf16; fp32
+    dgamma with the fp64 dgamma itself.
+  * Fused-add h = round(x + r) must be bit-exact.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+import oracle
+from rmsnorm_inputs import bf16_bits_to_f32
+
+BF16_FLOOR = 2.0 ** -14
+
+
+def ulp_bf16(a) -> np.ndarray:
+    a = np.abs(np.asarray(a, dtype=np.float64))
+    _, e = np.frexp(a)  # a = m 2^e, m in [0.5, 1)
+    q = np.maximum(e - 1, -126)
+    u = np.ldexp(1.0, q - 7)
+    return np.where(a == 0, 2.0 ** -133, u)
+
+
+@dataclasses.dataclass
+class Report:
+    what: str
+    n: int
+    fails: int
+    pure_fails: int  # failures under the rule without the cancellation floor
+    floor_active: int
+    worst: float  # worst error in units of the allowed tolerance
+    worst_index: int
+
+    @property
+    def ok(self) -> bool:
+        return self.fails == 0
+
+    def __str__(self):
+        return (f"{self.what}: n={self.n} fails={self.fails} pure_rule_fails={self.pure_fails} "
+                f"floor_active={self.floor_active} worst={self.worst:.3g} of tolerance at flat index {self.worst_index}")
+
+
+def _report(what, err, tol, tol_pure, floor_mask):
+    bad = ~(err <= tol)  # NaN counts as a failure
+    ratio = np.where(tol > 0, err / np.where(tol > 0, tol, 1.0), np.where(err > 0, np.inf, 0.0))
+    ratio = np.where(np.isnan(ratio), np.inf, ratio)
+    wi = int(np.argmax(ratio)) if ratio.size else -1
+    return Report(what, int(err.size), int(bad.sum()), int((~(err <= tol_pure)).sum()),
+                  int(floor_mask.sum()), float(ratio.flat[wi]) if ratio.size else 0.0, wi)
+
+
+def check_bf16(what, got_bits, ref64, *, scale=None, ulps=2.0) -> Report:
+    """got_bits (uint16 bf16) within `ulps` bf16 ulp of round_bf16(ref64)."""
+    ref64 = np.asarray(ref64, dtype=np.float64).ravel()
+    got = bf16_bits_to_f32(np.asarray(got_bits).ravel()).astype(np.float64)
+    ref_r = bf16_bits_to_f32(oracle.round_to(ref64, "bf16")).astype(np.float64)
+    mag = np.abs(ref64)
+    if scale is not None:
+        floor = BF16_FLOOR * np.asarray(scale, dtype=np.float64).ravel()
+        floor_mask = floor > mag
+        mag = np.maximum(mag, floor)
+    else:
+        floor_mask = np.zeros(mag.shape, bool)
+    err = np.abs(got - ref_r)
+    return _report(what, err, ulps * ulp_bf16(mag), ulps * ulp_bf16(np.abs(ref64)), floor_mask)
+
+
+def check_f32(what, got, ref64, *, scale=None, rel=1e-5) -> Report:
+    """|got - ref64| <= rel * max(|ref64|, scale)."""
+    ref64 = np.asarray(ref64, dtype=np.float64).ravel()
+    got = np.asarray(got, dtype=np.float64).ravel()
+    mag = np.abs(ref64)
+    if scale is not None:
+        s = np.asarray(scale, dtype=np.float64).ravel()
+        floor_mask = s > mag
+        mag = np.maximum(mag, s)
+    else:
+        floor_mask = np.zeros(mag.shape, bool)
+    err = np.abs(got - ref64)
+    return _report(what, err, rel * mag, rel * np.abs(ref64), floor_mask)
+
+
+def rel_l2(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(got - ref)
+    if den == 0:
+        return 0.0 if num == 0 else float("inf")
+    return float(num / den)
+
+
+def dgamma_error(got_storage, ref64, dtype: str) -> float:
+    """Relative L2 of dgamma: bf16 against round_bf16(ref64), fp32 against ref64."""
+    if dtype == "bf16":
+        got = bf16_bits_to_f32(np.asarray(got_storage)).astype(np.float64)
+        ref = bf16_bits_to_f32(oracle.round_to(ref64, "bf16")).astype(np.float64)
+        return rel_l2(got, ref)
+    return rel_l2(np.asarray(got_storage, dtype=np.float64), ref64)
+
+
+DGAMMA_TOL = {"bf16": 1e-3, "f32": 1e-5}
+
+
+def cancel_scale(v_wide, gamma_wide, dy_wide, rstd64, c64, sabs64, offset, dh_wide=None):
+    """s_ij = rstd_i (|dy w| + |v rstd| (|c_i| + S_i)) [+ |dh|]; all inputs float64."""
+    w = gamma_wide + float(np.float32(offset))
+    s = rstd64[:, None] * (np.abs(dy_wide * w) + np.abs(v_wide * rstd64[:, None]) * (np.abs(c64) + sabs64)[:, None])
+    if dh_wide is not None:
+        s = s + np.abs(dh_wide)
+    return s
