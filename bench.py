@@ -1,0 +1,411 @@
+#!/usr/bin/env python3
+"""RMSNorm forward + backward on one MI355X: throughput and roofline.
+
+One step = one pass of the whole path over a batch: the forward (rstd, y) of
+one buffer set and the backward (dx, dgamma partials, dgamma finalizer) of
+another, so that no step re-reads data an earlier kernel just left in the
+256 MB last-level cache.  Buffers rotate over enough sets to exceed 1 GiB
+("cold" data); a "hot" variant that reuses one set is reported beside it.
+
+Default workload: bf16 rows of M=4096 x N=4096, eps 1e-6, offset 0.
+
+Prints ONE JSON line (driver contract) with, among others:
+  value       achieved GB/s of the whole step (algorithmic bytes / time)
+  roofline    the dominant kernel (backward main) against the 8 TB/s HBM peak
+  cpu_baseline the fp64 reference timed on the host cores on the same workload
+
+Other modes:
+  --report PATH      write a detailed JSON report (every op, cold/hot, direct/graph)
+  --all-workloads    add every workload to the report
+  --counters-run     a short fixed sequence of launches for rocprofv3 --pmc runs
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "RMSNorm fwd+bwd µs/call and achieved HBM GB/s (% of peak), bf16 4096x4096"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "bwd_main_bf16_4096x4096_hbm_traffic.txt")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "transformer_normalization_rmsnorm_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "rmsnorm.h"))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Sets:
+    """K rotating device buffer sets for one workload, plus raw C-ABI call closures."""
+
+    def __init__(self, w, lib, rn, torch, n_sets: int):
+        from rmsnorm_inputs import make_workload_inputs
+
+        self.w, self.lib, self.rn, self.torch = w, lib, rn, torch
+        dev = torch.device("cuda:0")
+        inp = make_workload_inputs(w)
+        td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        import numpy as np
+
+        def up(a):
+            if w.dtype == "bf16":
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        base = {k: up(v) for k, v in inp.items()}
+        del inp
+        M, N = w.M, w.N
+        self.dt = rn.BF16 if w.dtype == "bf16" else rn.F32
+        self.ws_bytes = rn.rmsnorm_bwd_workspace_bytes(M, N, self.dt)
+        self.sets = []
+        for _ in range(n_sets):
+            s = {
+                "x": base["x"].clone(), "dy": base["dy"].clone(), "gamma": base["gamma"].clone(),
+                "y": torch.empty(M, N, dtype=td, device=dev), "rstd": torch.empty(M, dtype=torch.float32, device=dev),
+                "dx": torch.empty(M, N, dtype=td, device=dev), "dg": torch.empty(N, dtype=td, device=dev),
+                "ws": torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev),
+            }
+            if w.fused:
+                s["residual"] = base["residual"].clone()
+                s["h"] = torch.empty(M, N, dtype=td, device=dev)
+                s["dh"] = base["dh"].clone()
+            self.sets.append(s)
+        del base
+        torch.cuda.synchronize()
+        self.programs = rn.rmsnorm_query_plan(rn.OP_FUSED_ADD_BWD if w.fused else rn.OP_BWD, M, N, self.dt)["programs"]
+
+    def stream(self):
+        return ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: status {rc}: {self.lib.rmsnorm_last_error().decode()}")
+
+    def fwd(self, i, st):
+        s, w, L = self.sets[i % len(self.sets)], self.w, self.lib
+        if w.fused:
+            rc = L.rmsnorm_fused_add_fwd(s["x"].data_ptr(), s["residual"].data_ptr(), s["gamma"].data_ptr(),
+                                         s["y"].data_ptr(), s["h"].data_ptr(), s["rstd"].data_ptr(), w.M, w.N,
+                                         w.eps, w.offset, self.dt, st)
+        else:
+            rc = L.rmsnorm_fwd(s["x"].data_ptr(), s["gamma"].data_ptr(), s["y"].data_ptr(), s["rstd"].data_ptr(),
+                               w.M, w.N, w.eps, w.offset, self.dt, st)
+        self._check(rc, "fwd")
+
+    def bwd(self, i, st):
+        s, w, L = self.sets[i % len(self.sets)], self.w, self.lib
+        if w.fused:  # dx written over dh: dx is the residual gradient
+            rc = L.rmsnorm_fused_add_bwd(s["dy"].data_ptr(), s["dh"].data_ptr(), s["h"].data_ptr(),
+                                         s["gamma"].data_ptr(), s["rstd"].data_ptr(), s["dh"].data_ptr(),
+                                         s["dg"].data_ptr(), s["ws"].data_ptr(), self.ws_bytes, w.M, w.N, w.eps,
+                                         w.offset, self.dt, st)
+        else:
+            rc = L.rmsnorm_bwd(s["dy"].data_ptr(), s["x"].data_ptr(), s["gamma"].data_ptr(), s["rstd"].data_ptr(),
+                               s["dx"].data_ptr(), s["dg"].data_ptr(), s["ws"].data_ptr(), self.ws_bytes, w.M, w.N,
+                               w.eps, w.offset, self.dt, st)
+        self._check(rc, "bwd")
+
+    def bwd_main(self, i, st):
+        s, w, L = self.sets[i % len(self.sets)], self.w, self.lib
+        p = ctypes.c_int64(0)
+        v = s["h"] if w.fused else s["x"]
+        dh = s["dh"].data_ptr() if w.fused else None
+        dx = s["dh"].data_ptr() if w.fused else s["dx"].data_ptr()
+        rc = L.rmsnorm_bwd_partials(s["dy"].data_ptr(), v.data_ptr(), s["gamma"].data_ptr(), s["rstd"].data_ptr(),
+                                    dh, dx, s["ws"].data_ptr(), self.ws_bytes, ctypes.byref(p), w.M, w.N, w.eps,
+                                    w.offset, self.dt, st)
+        self._check(rc, "bwd_main")
+
+    def finalize(self, i, st):
+        s = self.sets[i % len(self.sets)]
+        rc = self.lib.rmsnorm_dgamma_finalize(s["ws"].data_ptr(), self.programs, self.w.N, s["dg"].data_ptr(),
+                                              self.dt, st)
+        self._check(rc, "finalize")
+
+
+def time_direct(torch, fn, iters, warmup, repeats=5, rotate=True):
+    """Median over `repeats` of (event time of `iters` back-to-back calls) / iters, in us."""
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i in range(warmup):
+        fn(i, st)
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            fn(i if rotate else 0, st)
+        e1.record()
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1) * 1000.0 / iters)
+    return statistics.median(out)
+
+
+def time_graph(torch, fn, iters, repeats=5, rotate=True):
+    """Median per-call time of a HIP graph holding `iters` calls, in us."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        fn(0, st)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(iters):
+            fn(i if rotate else 0, st)
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1) * 1000.0 / iters)
+    del g
+    return statistics.median(out)
+
+
+def n_sets_for(w, cold: bool) -> int:
+    if not cold:
+        return 1
+    per_set = (6 if w.fused else 4) * w.M * w.N * w.elem_bytes
+    return max(2, min(16, math.ceil((1 << 30) / per_set) + 1))
+
+
+def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
+    from rmsnorm_inputs import algorithmic_bytes
+
+    res = {"workload": w.name, "M": w.M, "N": w.N, "dtype": w.dtype, "fused": w.fused, "offset": w.offset}
+    fop, bop = ("fused_fwd", "fused_bwd") if w.fused else ("fwd", "bwd")
+    bytes_f = algorithmic_bytes(fop, w.M, w.N, w.elem_bytes)
+    bytes_b = algorithmic_bytes(bop, w.M, w.N, w.elem_bytes)
+    bytes_main = algorithmic_bytes(bop + "_main", w.M, w.N, w.elem_bytes)
+    res["bytes"] = {"fwd": bytes_f, "bwd": bytes_b, "bwd_main": bytes_main}
+    for mode in ("cold", "hot"):
+        S = Sets(w, lib, rn, torch, n_sets_for(w, mode == "cold"))
+        K = len(S.sets)
+        r = {"sets": K}
+        # every set's rstd must exist before a backward reads it
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(K):
+            S.fwd(i, st)
+        r["fwd_us"] = time_direct(torch, S.fwd, iters, warmup)
+        r["bwd_us"] = time_direct(torch, lambda i, s: S.bwd(i + K // 2, s), iters, warmup)
+        r["bwd_main_us"] = time_direct(torch, S.bwd_main, iters, warmup)
+        r["finalize_us"] = time_graph(torch, S.finalize, iters)
+        if detailed:
+            r["fwd_graph_us"] = time_graph(torch, S.fwd, iters)
+            r["bwd_graph_us"] = time_graph(torch, lambda i, s: S.bwd(i + K // 2, s), iters)
+        for op, b in (("fwd", bytes_f), ("bwd", bytes_b), ("bwd_main", bytes_main)):
+            r[op + "_GBs"] = b / (r[op + "_us"] * 1e3)
+            r[op + "_pct_peak"] = 100.0 * r[op + "_GBs"] / HBM_PEAK_GBS
+        res[mode] = r
+        del S
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, seconds: float):
+    """The fp64 reference, as it stands, on the host cores (bounded run)."""
+    import numpy as np
+
+    import oracle
+    from rmsnorm_inputs import algorithmic_bytes, make_workload_inputs
+
+    lib = oracle.load()
+    inp = make_workload_inputs(w)
+    fop, bop = ("fused_fwd", "fused_bwd") if w.fused else ("fwd", "bwd")
+    nbytes = algorithmic_bytes(fop, w.M, w.N, w.elem_bytes) + algorithmic_bytes(bop, w.M, w.N, w.elem_bytes)
+    times = []
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end or len(times) < 1:
+        t0 = time.perf_counter()
+        if w.fused:
+            h, _, _ = oracle.fused_add_fwd(inp["x"], inp["residual"], inp["gamma"], w.dtype, w.eps, w.offset, lib=lib)
+            oracle.bwd(inp["dy"], h, inp["gamma"], w.dtype, w.eps, w.offset, dh=inp["dh"], lib=lib)
+        else:
+            oracle.fwd(inp["x"], inp["gamma"], w.dtype, w.eps, w.offset, lib=lib)
+            oracle.bwd(inp["dy"], inp["x"], inp["gamma"], w.dtype, w.eps, w.offset, lib=lib)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {
+        "value": nbytes / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(lib), "kind": "oracle",
+        "sample": f"whole {w.name} workload (fwd + bwd, fp64 C reference, OpenMP), median of {len(times)} "
+                  f"runs in ~{seconds:.0f} s; {t * 1e6:.0f} us per fwd+bwd",
+        "us_per_call": t * 1e6,
+    }
+
+
+def counters_traffic():
+    """HBM bytes per backward-main dispatch from committed rocprofv3 counters,
+    or None when missing or taken on different kernel sources."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def counters_run(rn, torch):
+    """Fixed launch sequence for rocprofv3 --pmc: a plain copy of known size,
+    then forward, backward main and finalizer on the default workload."""
+    from rmsnorm_inputs import WORKLOADS
+
+    w = WORKLOADS["bf16_4096x4096"]
+    lib = rn.load_library()
+    S = Sets(w, lib, rn, torch, 2)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i in range(5):
+        dst.copy_(src)  # 256 MiB read + 256 MiB written
+    for i in range(5):
+        S.fwd(i, st)
+    for i in range(5):
+        S.bwd_main(i + 1, st)
+    for i in range(5):
+        S.finalize(i, st)
+    torch.cuda.synchronize()
+    print("counters run done", flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="bf16_4096x4096")
+    ap.add_argument("--report", default=None)
+    ap.add_argument("--all-workloads", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters-run", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} (WORLD_SIZE={world}) is not supported; "
+              "RMSNorm rows shard across GPUs with no exchange except dgamma, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import transformer_normalization_rmsnorm_amd as rn
+    from rmsnorm_inputs import WORKLOADS, algorithmic_bytes
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.counters_run:
+        counters_run(rn, torch)
+        return
+    lib = rn.load_library()
+    w = WORKLOADS[args.workload]
+    fop, bop = ("fused_fwd", "fused_bwd") if w.fused else ("fwd", "bwd")
+    step_bytes = algorithmic_bytes(fop, w.M, w.N, w.elem_bytes) + algorithmic_bytes(bop, w.M, w.N, w.elem_bytes)
+
+    # ---- the timed steps (contract): W warmup steps, then exactly K steps ----
+    S = Sets(w, lib, rn, torch, n_sets_for(w, True))
+    K = len(S.sets)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i in range(K):
+        S.fwd(i, st)
+
+    def step(i):
+        S.fwd(i, st)
+        S.bwd(i + K // 2, st)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    del S
+    torch.cuda.empty_cache()
+
+    # ---- per-op and per-kernel timings ----
+    detail = measure_workload(w, lib, rn, torch, iters=200, warmup=30)
+    cold = detail["cold"]
+    main_us = cold["bwd_main_us"]
+    roofline = {
+        "kernel": f"backward main ({'fused-add ' if w.fused else ''}rows, dx + dgamma partials)",
+        "bound": "hbm", "achieved": detail["bytes"]["bwd_main"] / (main_us * 1e3), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": None, "traffic": counters_traffic(),
+        "bytes_per_launch": detail["bytes"]["bwd_main"], "avg_launch_us": main_us,
+    }
+    roofline["frac"] = roofline["achieved"] / roofline["peak"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    value = step_bytes / (ms_per_step * 1e6)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"RMSNorm fwd+bwd {w.dtype} M={w.M} N={w.N} eps={w.eps} offset={w.offset}"
+                               f"{' fused residual add' if w.fused else ''}, rotating cold buffers",
+                   "M": w.M, "N": w.N, "storage": w.dtype, "fused_add": w.fused, "parallelism": "none (1 GPU)"},
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "fwd_us": round(cold["fwd_us"], 3), "bwd_us": round(cold["bwd_us"], 3),
+        "fwd_GBs": round(cold["fwd_GBs"], 1), "bwd_GBs": round(cold["bwd_GBs"], 1),
+        "fwd_graph_us": round(cold["fwd_graph_us"], 3), "bwd_graph_us": round(cold["bwd_graph_us"], 3),
+        "hot_fwd_us": round(detail["hot"]["fwd_us"], 3), "hot_bwd_us": round(detail["hot"]["bwd_us"], 3),
+        "finalize_us": round(cold["finalize_us"], 3),
+        "roofline": roofline, "cpu_baseline": cpu,
+        "source_hash": source_hash(), "wall_s_timed_region": round(wall, 4),
+    }
+    if args.report:
+        report = {"bench_line": line, "workloads": [detail]}
+        if args.all_workloads:
+            for name, ww in WORKLOADS.items():
+                if name != w.name:
+                    print(f"measuring {name}", file=sys.stderr, flush=True)
+                    report["workloads"].append(measure_workload(ww, lib, rn, torch, iters=100, warmup=20))
+        os.makedirs(os.path.dirname(os.path.abspath(args.report)), exist_ok=True)
+        with open(args.report, "w") as f:
+            json.dump(report, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

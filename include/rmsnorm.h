@@ -1,0 +1,201 @@
+/*
+ * rmsnorm.h - C ABI of the MI355X (gfx950) RMSNorm library.
+ *
+ * RMSNorm forward and backward, plain and with a fused residual add, for
+ * bfloat16 and float32 storage with float32 arithmetic.
+ *
+ *   forward   rstd_i = 1 / sqrt((1/N) sum_j v_ij^2 + eps)
+ *             y_ij   = round_T(v_ij * rstd_i * (gamma_j + offset))
+ *   backward  w_j = gamma_j + offset, g = dy * w, xhat = v * rstd_i,
+ *             c_i = (1/N) sum_j g_ij xhat_ij,
+ *             dx_ij = round_T(rstd_i (g_ij - xhat_ij c_i) [+ dh_ij]),
+ *             dgamma_j = round_T(sum_i dy_ij xhat_ij)
+ *
+ * Sources: Liger-Kernel PR #1388 "perf(cutedsl): add Blackwell fast path to
+ * RMSNorm" (Summary; "1. TVM-FFI direct-call launch": eps and offset are
+ * runtime float scalars, the caller's stream is used; "Results": "llama mode",
+ * read as float32 compute with one cast after the gamma multiply) and ROCm/FlyDSL
+ * PR #855 "[Perf] Optimize RMSNorm backward with staged reduction and vec8 I/O"
+ * (Implementation: a bounded persistent backward grid writes dx and one float32
+ * dgamma partial row per program, a finalizer reduces the [programs, N]
+ * partials and writes dgamma in the parameter dtype with no atomics; fused-add
+ * keeps the dx == dresidual aliasing contract; non-16-byte-aligned storage
+ * offsets are supported; "Runtime configuration and ownership": the workspace
+ * is per invocation and caller-owned, M is a runtime argument).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are device pointers on the current HIP device.  [M, N]
+ *     tensors are contiguous and row-major (row stride N); gamma and dgamma
+ *     are [N]; rstd is [M] float32.  Any element-aligned address is accepted;
+ *     16-byte alignment of every pointer enables the 128-bit access path.
+ *   - dtype: RMSNORM_BF16 or RMSNORM_F32 for every T-typed tensor of a call.
+ *   - Ownership: the caller owns every buffer, including the backward
+ *     workspace.  The library allocates no device memory, keeps no per-call
+ *     state, never synchronises, and launches only on `stream` (NULL = the
+ *     null stream), so every call may be captured into a HIP graph.
+ *   - Errors: every function returns an rmsnorm_status.  All argument checks
+ *     happen before any HIP call; a failed launch returns RMSNORM_EHIP.
+ *     rmsnorm_last_error() gives a message for the calling thread's last
+ *     failure.  Faults inside a kernel surface at the caller's next
+ *     synchronisation, as for any asynchronous HIP work.
+ *   - Aliasing: only h_out may alias residual (fused forward) and only dx may
+ *     alias dh (fused backward); any other overlap is undefined.
+ *   - M = 0 is valid: the forward does nothing; the backward writes
+ *     dgamma = 0.  N must be in [1, 2^31 - 1].
+ *   - Results are deterministic: for a given device, shape, dtype and pointer
+ *     alignment every output, dgamma included, is bit-identical run to run.
+ */
+#ifndef RMSNORM_AMD_H
+#define RMSNORM_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP stream type (hipStream_t is `struct ihipStream_t *`). */
+struct ihipStream_t;
+typedef struct ihipStream_t *rmsnorm_stream_t;
+
+typedef enum rmsnorm_dtype {
+    RMSNORM_F32 = 0,
+    RMSNORM_BF16 = 1
+} rmsnorm_dtype;
+
+typedef enum rmsnorm_status {
+    RMSNORM_OK = 0,
+    RMSNORM_EINVAL = 1,       /* bad argument (null pointer, size, alignment, eps) */
+    RMSNORM_EUNSUPPORTED = 2, /* dtype or configuration not available */
+    RMSNORM_EWORKSPACE = 3,   /* workspace missing or smaller than required */
+    RMSNORM_EHIP = 4          /* a HIP runtime call or kernel launch failed */
+} rmsnorm_status;
+
+/* Forward (Liger-Kernel PR #1388, Summary and "Results" llama mode; FlyDSL
+ * PR #855 "Implementation": two-pass row math with a block reduction).
+ *   x      [M, N] T   input rows
+ *   gamma  [N] T      scale; the kernel uses gamma_j + offset
+ *   y      [M, N] T   output, may be NULL to compute rstd only
+ *   rstd   [M] f32    saved 1/rms per row for the backward, may be NULL
+ *   eps >= 0 and offset: float32 runtime scalars. */
+int rmsnorm_fwd(const void *x, const void *gamma, void *y, float *rstd,
+                int64_t M, int64_t N, float eps, float offset,
+                int dtype, rmsnorm_stream_t stream);
+
+/* Fused residual add then forward (FlyDSL PR #855 "Hybrid atomic / two-stage
+ * backward": fused-add is a specialization of the same op).
+ *   h_out [M, N] T receives round_T(x + residual), computed in float32; the
+ *   forward normalises that stored h.  h_out may alias residual.
+ *   y may be NULL (h and rstd only); rstd may be NULL. */
+int rmsnorm_fused_add_fwd(const void *x, const void *residual, const void *gamma,
+                          void *y, void *h_out, float *rstd,
+                          int64_t M, int64_t N, float eps, float offset,
+                          int dtype, rmsnorm_stream_t stream);
+
+/* Workspace the backward needs on the current device (FlyDSL PR #855
+ * "Runtime configuration and ownership": programs * N * sizeof(float) of
+ * partials, here with each partial row padded to 64 floats, plus M floats used
+ * only when rstd is not supplied).  Writes the byte count to *bytes; depends
+ * only on (M, N, dtype) and the device's compute-unit count. */
+int rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *bytes);
+
+/* Backward (FlyDSL PR #855 "Hybrid atomic / two-stage backward"): a bounded
+ * persistent grid writes dx and float32 dgamma partials into `workspace`, then
+ * a finalizer sums the partials in a fixed order and writes dgamma in T.
+ *   dy, x  [M, N] T;  gamma [N] T;
+ *   rstd   [M] f32 from the forward, or NULL to recompute it from x with eps;
+ *   dx     [M, N] T;  dgamma [N] T;
+ *   workspace: device memory of at least rmsnorm_bwd_workspace_bytes(), 16-byte
+ *   aligned, contents ignored on entry and undefined on return. */
+int rmsnorm_bwd(const void *dy, const void *x, const void *gamma, const float *rstd,
+                void *dx, void *dgamma, void *workspace, size_t workspace_bytes,
+                int64_t M, int64_t N, float eps, float offset,
+                int dtype, rmsnorm_stream_t stream);
+
+/* Fused-add backward (FlyDSL PR #855 "Fused-add RMSNorm backward": the
+ * residual-gradient addition; "Hybrid ... backward": dx == dresidual).
+ *   h   [M, N] T, the stored residual sum from rmsnorm_fused_add_fwd;
+ *   dh  [M, N] T, gradient arriving at h_out, or NULL for zero;
+ *   dx  [M, N] T = d(loss)/dx = d(loss)/dresidual; may alias dh (in place).
+ *   Other arguments as rmsnorm_bwd (rstd NULL recomputes from h). */
+int rmsnorm_fused_add_bwd(const void *dy, const void *dh, const void *h, const void *gamma,
+                          const float *rstd, void *dx, void *dgamma,
+                          void *workspace, size_t workspace_bytes,
+                          int64_t M, int64_t N, float eps, float offset,
+                          int dtype, rmsnorm_stream_t stream);
+
+/* The two backward stages on their own, for callers that reduce the dgamma
+ * partials themselves (for example across devices, in rank order) and for
+ * per-stage timing.
+ *
+ * rmsnorm_bwd_partials: dx as rmsnorm_bwd / rmsnorm_fused_add_bwd (dh NULL
+ * for the plain op, v = x or h), and partials[p * ld + j] (float32, p <
+ * *programs, j < N) with ld = N rounded up to a multiple of 64.  *programs
+ * receives the number of partial rows written.  `workspace` is as for
+ * rmsnorm_bwd; the partials are its first *programs * ld floats. */
+int rmsnorm_bwd_partials(const void *dy, const void *v, const void *gamma, const float *rstd,
+                         const void *dh, void *dx, void *workspace, size_t workspace_bytes,
+                         int64_t *programs, int64_t M, int64_t N, float eps, float offset,
+                         int dtype, rmsnorm_stream_t stream);
+
+/* dgamma_j = round_T(sum_{p < programs} partials[p * ld + j]), summed in a
+ * fixed order; ld = N rounded up to a multiple of 64; programs may be 0
+ * (dgamma = 0).  partials must be 16-byte aligned. */
+int rmsnorm_dgamma_finalize(const float *partials, int64_t programs, int64_t N,
+                            void *dgamma, int dtype, rmsnorm_stream_t stream);
+
+/* Launch plan chosen by the shape/dtype selector. */
+typedef enum rmsnorm_op {
+    RMSNORM_OP_FWD = 0,
+    RMSNORM_OP_FUSED_ADD_FWD = 1,
+    RMSNORM_OP_BWD = 2,
+    RMSNORM_OP_FUSED_ADD_BWD = 3
+} rmsnorm_op;
+
+typedef enum rmsnorm_path {
+    RMSNORM_PATH_ROWS = 0, /* each row held in registers by a team of lanes */
+    RMSNORM_PATH_LOOP = 1  /* rows streamed in passes (any N) */
+} rmsnorm_path;
+
+typedef struct rmsnorm_plan {
+    int32_t op;          /* rmsnorm_op */
+    int32_t path;        /* rmsnorm_path */
+    int32_t vec;         /* elements per memory access: 16 / sizeof(T), or 1 */
+    int32_t team;        /* lanes per row: 8, 16, 32, 64, or 0 = the whole workgroup */
+    int32_t threads;     /* threads per workgroup of the main kernel */
+    int32_t chunks;      /* vector accesses per lane per row and tensor (ROWS path) */
+    int32_t depth;       /* rows a team loads ahead of the one it computes (ROWS path) */
+    int64_t grid;        /* workgroups of the main kernel (backward: partial programs) */
+    int64_t programs;    /* backward: dgamma partial rows (= grid); forward: 0 */
+    int64_t workspace_bytes; /* backward workspace; forward 0 */
+    int32_t fin_threads; /* backward finalizer workgroup size */
+    int64_t fin_grid;    /* backward finalizer workgroups */
+} rmsnorm_plan;
+
+/* Pure selector query: the plan for `op` at (M, N, dtype).  vec_ok != 0 says
+ * every pointer of the call will be 16-byte aligned.  num_cus > 0 gives the
+ * compute-unit count explicitly (no HIP call is made); num_cus <= 0 reads it
+ * from the current device. */
+int rmsnorm_query_plan(int op, int64_t M, int64_t N, int dtype, int vec_ok, int num_cus,
+                       rmsnorm_plan *out);
+
+/* Tuning and testing aid (the analogue of Liger-Kernel PR #1388's force
+ * switches, "Behavior when the fast path does not apply"): later calls of `op`
+ * use path, vec, team, threads and depth from *plan, and its grid when
+ * grid > 0 (else the selector's grid for that layout); chunks and the
+ * workspace follow.
+ * vec = 1 forces scalar accesses on aligned data.  NULL clears.  Process-wide
+ * and not thread-safe; a call that the override does not fit returns
+ * RMSNORM_EINVAL. */
+int rmsnorm_set_plan_override(int op, const rmsnorm_plan *plan);
+
+const char *rmsnorm_status_string(int status);
+const char *rmsnorm_last_error(void);
+int rmsnorm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_AMD_H */

@@ -1,0 +1,112 @@
+"""Helpers for the GPU parity tests: move storage arrays to and from the
+device, run the library through its C ABI binding, and compare against the
+fp64 reference with the rules in tolerance.py."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import transformer_normalization_rmsnorm_amd as rn
+from rmsnorm_inputs import BF16, bf16_bits_to_f32
+from tolerance import (DGAMMA_TOL, cancel_scale, check_bf16, check_f32,
+                       dgamma_error)
+
+DEV = "cuda:0"
+TORCH_DTYPE = {BF16: torch.bfloat16, "f32": torch.float32}
+
+
+def to_dev(a: np.ndarray, dtype: str, device=DEV) -> torch.Tensor:
+    if dtype == BF16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def from_dev(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    return (bf16_bits_to_f32(a) if dtype == BF16 else np.asarray(a, np.float32)).astype(np.float64)
+
+
+def check_values(what, got, ref64, dtype, scale=None):
+    r = check_bf16(what, got, ref64, scale=scale) if dtype == BF16 else check_f32(what, got, ref64, scale=scale)
+    assert r.ok, str(r)
+    return r
+
+
+def check_forward(inp, dtype, eps, offset, y, rstd, h=None, rows=None):
+    """Compare GPU forward outputs (numpy, possibly a row sample) with the reference."""
+    x = inp["x"] if rows is None else inp["x"][rows]
+    g = inp["gamma"]
+    if h is not None:
+        r = inp["residual"] if rows is None else inp["residual"][rows]
+        h_ref, y64, rstd64 = oracle.fused_add_fwd(x, r, g, dtype, eps, offset)
+        assert np.array_equal(h, h_ref), f"h differs at {np.argwhere(h != h_ref)[:5].tolist()}"
+    else:
+        y64, rstd64 = oracle.fwd(x, g, dtype, eps, offset)
+    reports = []
+    if y is not None:
+        reports.append(check_values("y", y, y64, dtype))
+    if rstd is not None:
+        rr = check_f32("rstd", rstd, rstd64)
+        assert rr.ok, str(rr)
+        reports.append(rr)
+    return reports
+
+
+def reference_h(inp, dtype, eps=1e-6, offset=0.0):
+    """h = round(x + residual) from the reference (the backward input of fused-add)."""
+    h, _, _ = oracle.fused_add_fwd(inp["x"], inp["residual"], inp["gamma"], dtype, eps, offset, want_y=False)
+    return h
+
+
+def check_backward(inp, dtype, eps, offset, dx, dgamma, *, v_full, dh_full=None, rows=None):
+    """Compare GPU backward outputs with the reference.
+
+    v_full: the forward input from the reference side: x, or reference_h() for
+    fused-add (never an output of the GPU path), all rows.
+    dx: GPU dx for `rows` (all rows if None); dgamma: GPU dgamma (always all rows)."""
+    g = inp["gamma"]
+    sel = (lambda a: a) if rows is None else (lambda a: a[rows])
+    v = sel(v_full)
+    dy = sel(inp["dy"])
+    dh = None if dh_full is None else sel(dh_full)
+    out = oracle.bwd(dy, v, g, dtype, eps, offset, dh=dh, want_dgamma=rows is None)
+    rstd64 = 1.0 / np.sqrt(np.mean(widen(v, dtype) ** 2, axis=1) + float(np.float32(eps)))
+    s = cancel_scale(widen(v, dtype), widen(g, dtype), widen(dy, dtype), rstd64, out["c64"], out["sabs64"], offset,
+                     None if dh is None else widen(dh, dtype))
+    reports = [check_values("dx", dx, out["dx64"], dtype, scale=s)]
+    if dgamma is not None:
+        dg64 = out["dgamma64"] if rows is None else oracle.bwd(inp["dy"], v_full, g, dtype, eps, offset,
+                                                               want_dx=False)["dgamma64"]
+        err = dgamma_error(dgamma, dg64, dtype)
+        assert err <= DGAMMA_TOL[dtype], f"dgamma relative L2 {err:.3g} > {DGAMMA_TOL[dtype]}"
+    return reports
+
+
+def gpu_forward(inp, dtype, eps, offset, fused):
+    x = to_dev(inp["x"], dtype)
+    g = to_dev(inp["gamma"], dtype)
+    if fused:
+        r = to_dev(inp["residual"], dtype)
+        y, h, rstd = rn.rmsnorm_fused_add_fwd(x, r, g, eps, offset)
+        return {"y": y, "h": h, "rstd": rstd, "x": x, "gamma": g}
+    y, rstd = rn.rmsnorm_fwd(x, g, eps, offset)
+    return {"y": y, "rstd": rstd, "x": x, "gamma": g}
+
+
+def gpu_backward(inp, dtype, eps, offset, fwd_out, fused, rstd="gpu"):
+    dy = to_dev(inp["dy"], dtype)
+    rs = fwd_out["rstd"] if rstd == "gpu" else (None if rstd is None else rstd)
+    if fused:
+        dh = to_dev(inp["dh"], dtype)
+        dx, dg = rn.rmsnorm_fused_add_bwd(dy, dh, fwd_out["h"], fwd_out["gamma"], rs, eps, offset)
+    else:
+        dx, dg = rn.rmsnorm_bwd(dy, fwd_out["x"], fwd_out["gamma"], rs, eps, offset)
+    return dx, dg

@@ -1,0 +1,224 @@
+"""C ABI checks that need no GPU: the library loads and exports every symbol the
+header declares; argument errors come back as status codes before any HIP
+call; the selector is a pure function of (op, M, N, dtype, alignment, CUs).
+
+Calls here use fake device addresses only where an argument check must reject
+the call before anything touches a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_normalization_rmsnorm_amd as rn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmsnorm.h")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+CUS = 256
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rn.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rmsnorm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_match_header(lib):
+    declared = header_functions()
+    assert declared == sorted(rn.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {rn.library_path()}").read()
+    exported = set(re.findall(r" T (rmsnorm_\w+)", out))
+    assert exported == set(declared)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.rmsnorm_version() >= 1
+    assert lib.rmsnorm_status_string(0) == b"ok"
+    assert lib.rmsnorm_status_string(3).startswith(b"workspace")
+    assert lib.rmsnorm_status_string(99) == b"unknown status"
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails its checks first
+ODD = 0x10001
+
+
+def fwd(lib, x=FAKE, g=FAKE, y=FAKE, rstd=FAKE, M=4, N=8, eps=1e-6, off=0.0, dt=rn.BF16):
+    return lib.rmsnorm_fwd(x, g, y, rstd, M, N, eps, off, dt, None)
+
+
+def test_fwd_argument_errors(lib):
+    assert fwd(lib, dt=7) == EUNSUPPORTED
+    assert fwd(lib, M=-1) == EINVAL
+    assert fwd(lib, N=0) == EINVAL
+    assert fwd(lib, N=2 ** 31) == EINVAL
+    assert fwd(lib, eps=-1e-6) == EINVAL
+    assert fwd(lib, eps=float("nan")) == EINVAL
+    assert fwd(lib, off=float("inf")) == EINVAL
+    assert fwd(lib, x=None) == EINVAL
+    assert fwd(lib, g=None) == EINVAL
+    assert fwd(lib, y=None, rstd=None) == EINVAL
+    assert fwd(lib, x=ODD) == EINVAL  # bf16 needs 2-byte alignment
+    assert fwd(lib, rstd=FAKE + 2) == EINVAL
+    assert fwd(lib, y=FAKE + 64, x=FAKE + 64) == EINVAL  # y aliases x
+    assert b"aliases" in lib.rmsnorm_last_error()
+    # M = 0 is a successful no-op that needs no pointers at all
+    assert fwd(lib, x=None, g=None, y=None, rstd=None, M=0) == OK
+
+
+def test_fused_fwd_argument_errors(lib):
+    f = lib.rmsnorm_fused_add_fwd
+    assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 8, 1e-6, 0.0, rn.BF16, None) == EINVAL  # residual
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 8, 1e-6, 0.0, rn.BF16, None) == EINVAL  # h_out
+    assert f(FAKE, FAKE + 256, FAKE + 512, FAKE + 768, FAKE, FAKE + 1024, 4, 8, 1e-6, 0.0, rn.BF16, None) == EINVAL  # h_out == x
+    assert f(FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 1e-6, 0.0, rn.F32, None) == EINVAL  # f32 misaligned
+
+
+def test_bwd_argument_errors(lib):
+    b = lib.rmsnorm_bwd
+    args = dict(dy=FAKE, x=FAKE + 4096, g=FAKE + 8192, rstd=None, dx=FAKE + 12288, dg=FAKE + 16384, ws=FAKE + 32768)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return b(a["dy"], a["x"], a["g"], a["rstd"], a["dx"], a["dg"], a["ws"], 1 << 20, kw.get("M", 4),
+                 kw.get("N", 8), 1e-6, 0.0, kw.get("dt", rn.BF16), None)
+
+    assert call(dg=None) == EINVAL
+    assert call(dy=None) == EINVAL
+    assert call(dt=5) == EUNSUPPORTED
+    assert call(M=-3) == EINVAL
+    assert call(ws=FAKE + 32768 + 8) == EINVAL  # workspace must be 16-byte aligned
+    assert call(dx=args["dy"]) == EINVAL  # dx may alias only dh
+    assert call(dg=FAKE + 1) == EINVAL
+    fin = lib.rmsnorm_dgamma_finalize
+    assert fin(None, 3, 8, FAKE, rn.BF16, None) == EINVAL
+    assert fin(FAKE + 8, 3, 8, FAKE, rn.BF16, None) == EINVAL
+    assert fin(FAKE, -1, 8, FAKE, rn.BF16, None) == EINVAL
+    assert fin(FAKE, 3, 8, None, rn.BF16, None) == EINVAL
+    programs = ctypes.c_int64(-1)
+    assert lib.rmsnorm_bwd_partials(FAKE, FAKE, FAKE, None, None, FAKE + 4096, FAKE, 0, None, 4, 8, 1e-6, 0.0,
+                                    rn.BF16, None) == EINVAL
+    assert lib.rmsnorm_bwd_partials(FAKE, FAKE, FAKE, None, None, FAKE + 4096, FAKE, 0, ctypes.byref(programs), 4,
+                                    0, 1e-6, 0.0, rn.BF16, None) == EINVAL
+
+
+def plan(op, M, N, dt=rn.BF16, vec_ok=True, cus=CUS):
+    return rn.rmsnorm_query_plan(op, M, N, dt, vec_ok, cus)
+
+
+def covers(p, N):
+    lanes = p["team"] or p["threads"]
+    return lanes * p["chunks"] * p["vec"] >= N
+
+
+@pytest.mark.parametrize("M,N,dt,fused", [
+    (512, 2048, rn.BF16, False), (4096, 4096, rn.BF16, False), (1024, 8192, rn.BF16, False),
+    (16384, 8192, rn.BF16, False), (16384, 6144, rn.F32, False), (16384, 7168, rn.BF16, True),
+    (262144, 128, rn.BF16, False),
+])
+def test_plans_for_workloads(M, N, dt, fused):
+    fop = rn.OP_FUSED_ADD_FWD if fused else rn.OP_FWD
+    bop = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
+    f = plan(fop, M, N, dt)
+    b = plan(bop, M, N, dt)
+    vec = 8 if dt == rn.BF16 else 4
+    for p in (f, b):
+        assert p["path"] == rn.PATH_ROWS and p["vec"] == vec and covers(p, N)
+        assert p["threads"] % 64 == 0 and 64 <= p["threads"] <= 1024
+    rows_per_block = 1 if b["team"] == 0 else b["threads"] // b["team"]
+    assert b["grid"] == min(2 * CUS, -(-M // rows_per_block))
+    assert b["programs"] == b["grid"]
+    ld = -(-N // 64) * 64
+    assert b["workspace_bytes"] == -(-b["programs"] * ld * 4 // 256) * 256 + -(-M * 4 // 256) * 256
+    assert b["fin_grid"] == ld // 32
+    assert f["workspace_bytes"] == 0
+
+
+def test_plan_shapes_by_width():
+    assert plan(rn.OP_FWD, 1000, 128)["team"] == 16      # 16 lanes x 8 bf16
+    assert plan(rn.OP_BWD, 1000, 128)["team"] == 16
+    assert plan(rn.OP_FWD, 1000, 64, rn.F32)["team"] == 16
+    assert plan(rn.OP_FWD, 1000, 8)["team"] == 8
+    p = plan(rn.OP_FWD, 1000, 4096)
+    assert p["path"] == rn.PATH_ROWS and p["vec"] == 8 and covers(p, 4096)
+    p = plan(rn.OP_BWD, 4096, 4096)
+    assert (p["team"], p["threads"], p["chunks"]) == (0, 512, 1)
+    p = plan(rn.OP_BWD, 1024, 7168)
+    assert (p["team"], p["threads"], p["chunks"]) == (0, 896, 1)
+    p = plan(rn.OP_FWD, 1024, 6144, rn.F32)
+    assert (p["team"], p["threads"], p["chunks"]) == (0, 512, 3)
+
+
+def test_unaligned_and_ragged_take_scalar_access():
+    assert plan(rn.OP_FWD, 100, 4096, vec_ok=False)["vec"] == 1
+    assert plan(rn.OP_FWD, 100, 4097)["vec"] == 1          # N % 8 != 0
+    assert plan(rn.OP_FWD, 100, 5000)["vec"] == 8          # 5000 % 8 == 0
+    for N in (1, 7, 127, 4097, 5000, 8200, 12345):
+        for op in range(4):
+            for vec_ok in (True, False):
+                p = plan(op, 77, N, rn.BF16, vec_ok)
+                if p["path"] == rn.PATH_ROWS:
+                    assert covers(p, N), (op, N, p)
+
+
+def test_loop_path_beyond_registers():
+    p = plan(rn.OP_BWD, 64, 100000)
+    assert p["path"] == rn.PATH_LOOP and p["grid"] == 64
+    p = plan(rn.OP_FWD, 64, 1 << 20, rn.F32)
+    assert p["path"] == rn.PATH_LOOP
+
+
+def test_grid_caps_and_zero_rows():
+    assert plan(rn.OP_BWD, 3, 4096)["grid"] == 3
+    assert plan(rn.OP_BWD, 10, 128)["grid"] == 1          # 16 rows per workgroup
+    z = plan(rn.OP_BWD, 0, 4096)
+    assert z["grid"] == 0 and z["programs"] == 0
+    assert plan(rn.OP_FWD, 0, 4096)["grid"] == 0
+    assert plan(rn.OP_BWD, 10 ** 6, 4096, cus=80)["grid"] == 160
+
+
+def test_selector_rejects_bad_queries():
+    with pytest.raises(rn.RMSNormError):
+        plan(9, 4, 4)
+    with pytest.raises(rn.RMSNormError):
+        plan(rn.OP_FWD, 4, 0)
+    with pytest.raises(rn.RMSNormError):
+        plan(rn.OP_FWD, 4, 4, dt=3)
+
+
+def test_override_round_trip():
+    base = plan(rn.OP_BWD, 4096, 2048)
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=1, team=0, threads=512, grid=100):
+        p = plan(rn.OP_BWD, 4096, 2048)
+        assert (p["vec"], p["team"], p["threads"], p["chunks"], p["depth"], p["grid"]) == (1, 0, 512, 4, 1, 100)
+        assert p["workspace_bytes"] == 100 * 2048 * 4 + 4096 * 4
+    assert plan(rn.OP_BWD, 4096, 2048) == base
+    # a workgroup team holding two chunks per lane is compiled for at most 512 threads
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=1024):
+        with pytest.raises(rn.RMSNormError):
+            plan(rn.OP_BWD, 100, 16384)
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=512, depth=3):
+        assert plan(rn.OP_BWD, 100, 4096)["depth"] == 3
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=512, depth=4):
+        with pytest.raises(rn.RMSNormError):  # no such depth compiled
+            plan(rn.OP_BWD, 100, 4096)
+    with rn.plan_override(rn.OP_FWD, path=rn.PATH_LOOP, vec=8, team=0, threads=256):
+        p = plan(rn.OP_FWD, 10, 4096)
+        assert p["path"] == rn.PATH_LOOP and p["grid"] == 10
+    # an override that cannot hold the row is refused for that call
+    with rn.plan_override(rn.OP_FWD, path=rn.PATH_ROWS, vec=8, team=16, threads=256):
+        with pytest.raises(rn.RMSNormError):
+            plan(rn.OP_FWD, 10, 4096)
+    # 16-byte accesses cannot be forced onto unaligned data
+    with rn.plan_override(rn.OP_FWD, path=rn.PATH_ROWS, vec=8, team=64, threads=256):
+        with pytest.raises(rn.RMSNormError):
+            plan(rn.OP_FWD, 10, 4096, vec_ok=False)

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 reference.
+
+Sizes span several workgroup tiles with ragged tails; every selector path
+(narrow-row teams, one wavefront per row, workgroup teams, scalar access,
+looped rows) is exercised, plus the edge cases (N = 1, odd N, unaligned
+storage offsets, M smaller than the grid, M = 0)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_normalization_rmsnorm_amd as rn
+from gpu_util import (check_backward, check_forward, from_dev, gpu_backward,
+                      gpu_forward, reference_h, to_dev)
+from rmsnorm_inputs import EPS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+# (M, N, dtype, fused, gemma)
+CASES = [
+    (300, 4096, "bf16", False, False),    # wavefront rows fwd, 512-thread bwd, ragged vs the grid
+    (257, 8192, "bf16", False, False),    # wide rows
+    (130, 6144, "f32", False, True),      # float32, gamma + offset
+    (200, 7168, "bf16", True, False),     # fused residual add, 896-thread bwd
+    (1000, 128, "bf16", False, False),    # narrow rows: 16-lane teams
+    (1000, 128, "bf16", True, False),
+    (37, 64, "f32", False, False),        # 16-lane teams of float32
+    (64, 2048, "bf16", False, False),
+    (33, 5000, "bf16", False, False),     # vector path with a ragged last vector group
+    (17, 4097, "bf16", False, False),     # N % 8 != 0: scalar access
+    (9, 8200, "bf16", True, False),
+    (5, 1, "bf16", False, False),         # N = 1
+    (7, 7, "f32", False, True),
+    (11, 127, "bf16", True, False),
+    (6, 20000, "bf16", False, False),     # beyond the register path: looped rows
+    (4, 40000, "f32", True, True),
+    (3, 4096, "bf16", False, False),      # fewer rows than programs
+    (1, 3000, "f32", False, False),
+]
+
+
+def case_id(c):
+    M, N, dt, fused, gemma = c
+    return f"{dt}_{M}x{N}" + ("_fused" if fused else "") + ("_offset1" if gemma else "")
+
+
+def run_case(M, N, dt, fused, gemma, seed=0):
+    inp = make_inputs(M, N, dt, fused=fused, gemma=gemma, seed=seed)
+    offset = 1.0 if gemma else 0.0
+    out = gpu_forward(inp, dt, EPS, offset, fused)
+    torch.cuda.synchronize()
+    y, rstd = from_dev(out["y"]), from_dev(out["rstd"])
+    h = from_dev(out["h"]) if fused else None
+    check_forward(inp, dt, EPS, offset, y, rstd, h)
+    v_ref = reference_h(inp, dt, EPS, offset) if fused else inp["x"]
+    dx, dg = gpu_backward(inp, dt, EPS, offset, out, fused)
+    torch.cuda.synchronize()
+    check_backward(inp, dt, EPS, offset, from_dev(dx), from_dev(dg), v_full=v_ref,
+                   dh_full=inp["dh"] if fused else None)
+    return inp, out, dx, dg
+
+
+@pytest.mark.parametrize("case", CASES, ids=case_id)
+def test_fwd_bwd_parity(case):
+    run_case(*case)
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[3], CASES[4], CASES[9], CASES[14]], ids=case_id)
+def test_bwd_recomputes_rstd(case):
+    M, N, dt, fused, gemma = case
+    inp = make_inputs(M, N, dt, fused=fused, gemma=gemma)
+    offset = 1.0 if gemma else 0.0
+    out = gpu_forward(inp, dt, EPS, offset, fused)
+    dx, dg = gpu_backward(inp, dt, EPS, offset, out, fused, rstd=None)
+    torch.cuda.synchronize()
+    check_backward(inp, dt, EPS, offset, from_dev(dx), from_dev(dg),
+                   v_full=reference_h(inp, dt, EPS, offset) if fused else inp["x"],
+                   dh_full=inp["dh"] if fused else None)
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[3]], ids=case_id)
+def test_bwd_fed_reference_rstd(case):
+    """Backward in isolation, fed the reference forward's float32 rstd."""
+    M, N, dt, fused, gemma = case
+    inp = make_inputs(M, N, dt, fused=fused, gemma=gemma)
+    offset = 1.0 if gemma else 0.0
+    if fused:
+        h_ref, _, rstd64 = oracle.fused_add_fwd(inp["x"], inp["residual"], inp["gamma"], dt, EPS, offset, want_y=False)
+        v = h_ref
+    else:
+        _, rstd64 = oracle.fwd(inp["x"], inp["gamma"], dt, EPS, offset, want_y=False)
+        v = inp["x"]
+    rs = torch.from_numpy(oracle.round_to(rstd64, "f32")).cuda()
+    fwd_out = {"x": to_dev(v, dt), "h": to_dev(v, dt), "gamma": to_dev(inp["gamma"], dt)}
+    dx, dg = gpu_backward(inp, dt, EPS, offset, fwd_out, fused, rstd=rs)
+    torch.cuda.synchronize()
+    check_backward(inp, dt, EPS, offset, from_dev(dx), from_dev(dg), v_full=v, dh_full=inp["dh"] if fused else None)
+
+
+# Every compiled layout on one shape each: forced through the test override.
+FORCED = [
+    # (op-kind, M, N, dtype, plan fields)
+    ("fwd", 300, 4096, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=0, threads=512)),
+    ("fwd", 300, 4096, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=0, threads=256)),
+    ("fwd", 300, 4096, "bf16", dict(path=rn.PATH_ROWS, vec=1, team=0, threads=512)),
+    ("fwd", 300, 4096, "bf16", dict(path=rn.PATH_LOOP, vec=8, team=0, threads=256)),
+    ("fwd", 300, 4096, "bf16", dict(path=rn.PATH_LOOP, vec=1, team=0, threads=1024)),
+    ("fwd", 300, 512, "bf16", dict(path=rn.PATH_ROWS, vec=1, team=64, threads=256)),
+    ("fwd", 100, 4096, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=64, threads=256)),
+    ("fwd", 300, 4096, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=0, threads=256, depth=2, grid=100)),
+    ("fwd", 300, 2048, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=0, threads=128, depth=3, grid=37)),
+    ("fwd", 100, 6144, "f32", dict(path=rn.PATH_ROWS, vec=4, team=0, threads=256)),
+    ("fwd", 1000, 256, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=32, threads=256)),
+    ("bwd", 300, 4096, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=0, threads=256)),
+    ("bwd", 300, 4096, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=0, threads=1024, grid=7)),
+    ("bwd", 300, 2048, "bf16", dict(path=rn.PATH_ROWS, vec=1, team=0, threads=512)),
+    ("bwd", 300, 4096, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=0, threads=512, depth=3, grid=61)),
+    ("bwd", 300, 4096, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=0, threads=512, depth=2)),
+    ("bwd", 300, 4096, "bf16", dict(path=rn.PATH_LOOP, vec=8, team=0, threads=512)),
+    ("bwd", 300, 4096, "bf16", dict(path=rn.PATH_LOOP, vec=1, team=0, threads=1024, grid=300)),
+    ("bwd", 300, 1024, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=64, threads=256)),
+    ("bwd", 300, 128, "bf16", dict(path=rn.PATH_ROWS, vec=1, team=64, threads=256)),
+    ("bwd", 1000, 128, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=16, threads=128)),
+    ("bwd", 100, 6144, "f32", dict(path=rn.PATH_ROWS, vec=4, team=0, threads=512)),
+    ("bwd", 300, 8192, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=0, threads=512, depth=2)),
+    ("bwd", 1000, 128, "bf16", dict(path=rn.PATH_ROWS, vec=8, team=16, threads=256, depth=2, grid=5)),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["plain", "fused"])
+@pytest.mark.parametrize("kind,M,N,dt,fields", FORCED,
+                         ids=[f"{k}_{dt}_{M}x{N}_" + "_".join(f"{a}{b}" for a, b in f.items()) for k, M, N, dt, f in FORCED])
+def test_forced_layouts(kind, M, N, dt, fields, fused):
+    if kind == "fwd":
+        op = rn.OP_FUSED_ADD_FWD if fused else rn.OP_FWD
+    else:
+        op = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
+    with rn.plan_override(op, **fields):
+        p = rn.rmsnorm_query_plan(op, M, N, rn.BF16 if dt == "bf16" else rn.F32, True)
+        for k, v in fields.items():
+            assert p[k] == v, (k, p)
+        run_case(M, N, dt, fused, dt == "f32")
+
+
+def _offset_view(a: torch.Tensor, elems: int) -> torch.Tensor:
+    """The same values at a storage offset of `elems` elements (not 16-byte aligned)."""
+    flat = torch.empty(a.numel() + elems, dtype=a.dtype, device=a.device)
+    v = flat[elems:].view(a.shape)
+    v.copy_(a)
+    return v
+
+
+@pytest.mark.parametrize("M,N,dt", [(100, 4096, "bf16"), (50, 6144, "f32"), (300, 128, "bf16")])
+def test_unaligned_storage_offsets(M, N, dt):
+    for fused in (False, True):
+        inp = make_inputs(M, N, dt, fused=fused)
+        x = _offset_view(to_dev(inp["x"], dt), 1)
+        g = _offset_view(to_dev(inp["gamma"], dt), 3)
+        assert x.data_ptr() % 16 != 0
+        if fused:
+            r = _offset_view(to_dev(inp["residual"], dt), 1)
+            y, h, rstd = rn.rmsnorm_fused_add_fwd(x, r, g, EPS, 0.0, y=_offset_view(torch.empty_like(x), 1),
+                                                  h_out=_offset_view(torch.empty_like(x), 5))
+        else:
+            y, rstd = rn.rmsnorm_fwd(x, g, EPS, 0.0, y=_offset_view(torch.empty_like(x), 1))
+            h = None
+        torch.cuda.synchronize()
+        check_forward(inp, dt, EPS, 0.0, from_dev(y), from_dev(rstd), None if h is None else from_dev(h))
+        dy = _offset_view(to_dev(inp["dy"], dt), 1)
+        dx_out = _offset_view(torch.empty_like(x), 7)
+        if fused:
+            dh = _offset_view(to_dev(inp["dh"], dt), 1)
+            dx, dg = rn.rmsnorm_fused_add_bwd(dy, dh, h, g, rstd, EPS, 0.0, dx=dx_out)
+        else:
+            dx, dg = rn.rmsnorm_bwd(dy, x, g, rstd, EPS, 0.0, dx=dx_out)
+        torch.cuda.synchronize()
+        check_backward(inp, dt, EPS, 0.0, from_dev(dx), from_dev(dg),
+                       v_full=reference_h(inp, dt) if fused else inp["x"], dh_full=inp["dh"] if fused else None)
+
+
+def test_zero_rows_writes_zero_dgamma():
+    for dt, td in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+        x = torch.empty(0, 4096, dtype=td, device="cuda")
+        g = torch.ones(4096, dtype=td, device="cuda")
+        y, rstd = rn.rmsnorm_fwd(x, g)
+        dg = torch.full((4096,), float("nan"), dtype=td, device="cuda")
+        dx, dg = rn.rmsnorm_bwd(torch.empty_like(x), x, g, rstd, dgamma=dg)
+        torch.cuda.synchronize()
+        assert y.shape == (0, 4096) and torch.all(dg == 0)
+
+
+def test_in_place_fused_aliases():
+    """h_out may overwrite residual; dx may overwrite dh."""
+    M, N, dt = 500, 7168, "bf16"
+    inp = make_inputs(M, N, dt, fused=True)
+    x, g = to_dev(inp["x"], dt), to_dev(inp["gamma"], dt)
+    r = to_dev(inp["residual"], dt)
+    y, h, rstd = rn.rmsnorm_fused_add_fwd(x, r, g, EPS, 0.0, h_out=r)
+    assert h.data_ptr() == r.data_ptr()
+    torch.cuda.synchronize()
+    check_forward(inp, dt, EPS, 0.0, from_dev(y), from_dev(rstd), from_dev(h))
+    dy, dh = to_dev(inp["dy"], dt), to_dev(inp["dh"], dt)
+    dx, dg = rn.rmsnorm_fused_add_bwd(dy, dh, h, g, rstd, EPS, 0.0, dx=dh)
+    assert dx.data_ptr() == dh.data_ptr()
+    torch.cuda.synchronize()
+    check_backward(inp, dt, EPS, 0.0, from_dev(dx), from_dev(dg), v_full=reference_h(inp, dt), dh_full=inp["dh"])
+
+
+def test_workspace_too_small_is_refused_before_launch():
+    M, N = 4096, 4096
+    x = torch.randn(M, N, device="cuda").to(torch.bfloat16)
+    g = torch.ones(N, dtype=torch.bfloat16, device="cuda")
+    need = rn.rmsnorm_bwd_workspace_bytes(M, N, rn.BF16)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    dx = torch.full_like(x, 7.0)
+    with pytest.raises(rn.RMSNormError) as e:
+        rn.rmsnorm_bwd(x, x, g, None, dx=dx, workspace=ws)
+    assert e.value.status == 3
+    torch.cuda.synchronize()
+    assert torch.all(dx == 7.0)  # nothing ran
+
+
+def test_stage_entry_points_match_one_call():
+    M, N, dt = 1000, 4096, "bf16"
+    inp = make_inputs(M, N, dt)
+    out = gpu_forward(inp, dt, EPS, 0.0, False)
+    dy = to_dev(inp["dy"], dt)
+    dx1, dg1 = rn.rmsnorm_bwd(dy, out["x"], out["gamma"], out["rstd"])
+    dx2, ws, programs = rn.rmsnorm_bwd_partials(dy, out["x"], out["gamma"], out["rstd"])
+    dg2 = torch.empty_like(dg1)
+    rn.rmsnorm_dgamma_finalize(ws, programs, N, dg2)
+    torch.cuda.synchronize()
+    assert programs == rn.rmsnorm_query_plan(rn.OP_BWD, M, N, rn.BF16)["programs"]
+    assert torch.equal(dx1, dx2) and torch.equal(dg1.view(torch.int16), dg2.view(torch.int16))
+    # the partials themselves sum (in float64) to the reference dgamma
+    part = ws.view(torch.float32)[: programs * rn.partial_ld(N)].view(programs, -1)[:, :N].double().sum(0).cpu().numpy()
+    ref = oracle.bwd(inp["dy"], inp["x"], inp["gamma"], dt, EPS, 0.0, want_dx=False)["dgamma64"]
+    assert np.linalg.norm(part - ref) / np.linalg.norm(ref) < 1e-5

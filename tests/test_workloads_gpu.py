@@ -1,0 +1,44 @@
+"""The benchmark workloads at full size, in the launch configuration the
+benchmark times.  Forward outputs and dx are checked on a sample of rows that
+the reference computes one by one (always including the first and last row);
+dgamma, a reduction over every row, is checked in full."""
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_normalization_rmsnorm_amd as rn
+from gpu_util import (check_backward, check_forward, from_dev, gpu_forward,
+                      reference_h, to_dev)
+from rmsnorm_inputs import WORKLOADS, make_workload_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full_size(name):
+    w = WORKLOADS[name]
+    print(f"workload {name}", flush=True)
+    inp = make_workload_inputs(w)
+    rows = sample_rows(w.M, 48)
+    out = gpu_forward(inp, w.dtype, w.eps, w.offset, w.fused)
+    dy = to_dev(inp["dy"], w.dtype)
+    if w.fused:
+        dh = to_dev(inp["dh"], w.dtype)
+        # the workload's contract: dx is written over dh (dresidual in place)
+        dx, dg = rn.rmsnorm_fused_add_bwd(dy, dh, out["h"], out["gamma"], out["rstd"], w.eps, w.offset, dx=dh)
+    else:
+        dx, dg = rn.rmsnorm_bwd(dy, out["x"], out["gamma"], out["rstd"], w.eps, w.offset)
+    torch.cuda.synchronize()
+    sel = torch.from_numpy(rows).cuda()
+    y_s = from_dev(out["y"].index_select(0, sel))
+    r_s = from_dev(out["rstd"].index_select(0, sel))
+    h_full = from_dev(out["h"]) if w.fused else None
+    check_forward(inp, w.dtype, w.eps, w.offset, y_s, r_s, None if h_full is None else h_full[rows], rows=rows)
+    dx_s = from_dev(dx.index_select(0, sel))
+    check_backward(inp, w.dtype, w.eps, w.offset, dx_s, from_dev(dg),
+                   v_full=reference_h(inp, w.dtype, w.eps, w.offset) if w.fused else inp["x"],
+                   dh_full=inp["dh"] if w.fused else None, rows=rows)
+    # a property that holds at any size: no non-finite values anywhere
+    for t in (out["y"], dx):
+        assert bool(torch.isfinite(t).all())

@@ -1,0 +1,352 @@
+"""Python binding of the gfx950 RMSNorm library (``librmsnorm_amd.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/rmsnorm.h``.  PyTorch supplies
+device memory (``torch.empty``) and the current stream; nothing here computes.
+If the library has not been built, importing works but every call raises.
+
+Functions mirror the C entry points:
+  rmsnorm_fwd(x, gamma, eps, offset)                    -> (y, rstd)
+  rmsnorm_fused_add_fwd(x, residual, gamma, eps, offset) -> (y, h, rstd)
+  rmsnorm_bwd(dy, x, gamma, rstd, eps, offset)          -> (dx, dgamma)
+  rmsnorm_fused_add_bwd(dy, dh, h, gamma, rstd, eps, offset) -> (dx, dgamma)
+  rmsnorm_bwd_partials / rmsnorm_dgamma_finalize        (the two backward stages)
+  rmsnorm_bwd_workspace_bytes, rmsnorm_query_plan, rmsnorm_set_plan_override
+"""
+
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(PKG_DIR, "librmsnorm_amd.so")
+
+F32, BF16 = 0, 1
+OP_FWD, OP_FUSED_ADD_FWD, OP_BWD, OP_FUSED_ADD_BWD = 0, 1, 2, 3
+PATH_ROWS, PATH_LOOP = 0, 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
+
+# Exported symbols (kept equal to include/rmsnorm.h; a CPU test checks both).
+EXPORTS = (
+    "rmsnorm_fwd", "rmsnorm_fused_add_fwd", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd",
+    "rmsnorm_fused_add_bwd", "rmsnorm_bwd_partials", "rmsnorm_dgamma_finalize", "rmsnorm_query_plan",
+    "rmsnorm_set_plan_override", "rmsnorm_status_string", "rmsnorm_last_error", "rmsnorm_version",
+)
+
+
+class RMSNormError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        super().__init__(f"{func} failed: {STATUS.get(status, status)} ({detail})")
+        self.status = status
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("op", ctypes.c_int32), ("path", ctypes.c_int32), ("vec", ctypes.c_int32), ("team", ctypes.c_int32),
+        ("threads", ctypes.c_int32), ("chunks", ctypes.c_int32), ("depth", ctypes.c_int32),
+        ("grid", ctypes.c_int64),
+        ("programs", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64), ("fin_threads", ctypes.c_int32),
+        ("fin_grid", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def _bind(lib):
+    vp, i64, f, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "rmsnorm_fwd": [vp, vp, vp, vp, i64, i64, f, f, i32, vp],
+        "rmsnorm_fused_add_fwd": [vp, vp, vp, vp, vp, vp, i64, i64, f, f, i32, vp],
+        "rmsnorm_bwd_workspace_bytes": [i64, i64, i32, ctypes.POINTER(sz)],
+        "rmsnorm_bwd": [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, f, f, i32, vp],
+        "rmsnorm_fused_add_bwd": [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, f, f, i32, vp],
+        "rmsnorm_bwd_partials": [vp, vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(i64), i64, i64, f, f, i32, vp],
+        "rmsnorm_dgamma_finalize": [vp, i64, i64, vp, i32, vp],
+        "rmsnorm_query_plan": [i32, i64, i64, i32, i32, i32, ctypes.POINTER(Plan)],
+        "rmsnorm_set_plan_override": [i32, ctypes.POINTER(Plan)],
+        "rmsnorm_status_string": [i32],
+        "rmsnorm_last_error": [],
+        "rmsnorm_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name in ("rmsnorm_status_string", "rmsnorm_last_error") else ctypes.c_int
+    return lib
+
+
+def library_path() -> str:
+    return LIBRARY_PATH
+
+
+def load_library():
+    """Load the built C library; raise if it is missing (there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY_PATH):
+            raise RuntimeError(
+                f"{LIBRARY_PATH} is not built; run `python -m transformer_normalization_rmsnorm_amd._build` "
+                "(or __graft_entry__.build()) first")
+        _lib = _bind(ctypes.CDLL(LIBRARY_PATH))
+    return _lib
+
+
+def _check(rc: int, func: str):
+    if rc != 0:
+        detail = load_library().rmsnorm_last_error().decode(errors="replace")
+        raise RMSNormError(rc, func, detail)
+
+
+# ---- torch marshalling --------------------------------------------------------
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require(t, name, shape=None, dtype=None, device=None):
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _rows(x):
+    if x.dim() < 1:
+        raise ValueError("input must have at least one dimension")
+    N = x.shape[-1]
+    M = x.numel() // N if N else 0
+    return M, N
+
+
+@contextlib.contextmanager
+def _on_device(device):
+    """Enter the tensors' device only when it is not already current."""
+    torch = _torch()
+    if torch.cuda.current_device() == device.index:
+        yield
+    else:
+        with torch.cuda.device(device):
+            yield
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+def rmsnorm_fwd(x, gamma, eps: float = 1e-6, offset: float = 0.0, *, y=None, rstd=None, save_rstd: bool = True):
+    """y = x * rstd * (gamma + offset) over the last dimension; returns (y, rstd)."""
+    torch = _torch()
+    lib = load_library()
+    _require(x, "x")
+    M, N = _rows(x)
+    dev = x.device
+    _require(gamma, "gamma", (N,), x.dtype, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _require(y, "y", x.shape, x.dtype, dev)
+    if rstd is None and save_rstd:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev)
+    if rstd is not None:
+        _require(rstd, "rstd", x.shape[:-1], torch.float32, dev)
+    with _on_device(dev):
+        _check(lib.rmsnorm_fwd(_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, eps, offset, _dtype_code(x),
+                               _stream(dev)), "rmsnorm_fwd")
+    return y, rstd
+
+
+def rmsnorm_fused_add_fwd(x, residual, gamma, eps: float = 1e-6, offset: float = 0.0, *, y=None, h_out=None,
+                          rstd=None, save_rstd: bool = True):
+    """h = x + residual (rounded to the storage dtype), y = rmsnorm(h); returns (y, h, rstd).
+
+    Pass h_out=residual to update the residual stream in place."""
+    torch = _torch()
+    lib = load_library()
+    _require(x, "x")
+    M, N = _rows(x)
+    dev = x.device
+    _require(residual, "residual", x.shape, x.dtype, dev)
+    _require(gamma, "gamma", (N,), x.dtype, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    if h_out is None:
+        h_out = torch.empty_like(x)
+    _require(y, "y", x.shape, x.dtype, dev)
+    _require(h_out, "h_out", x.shape, x.dtype, dev)
+    if rstd is None and save_rstd:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev)
+    if rstd is not None:
+        _require(rstd, "rstd", x.shape[:-1], torch.float32, dev)
+    with _on_device(dev):
+        _check(lib.rmsnorm_fused_add_fwd(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(y), _ptr(h_out), _ptr(rstd),
+                                         M, N, eps, offset, _dtype_code(x), _stream(dev)), "rmsnorm_fused_add_fwd")
+    return y, h_out, rstd
+
+
+def rmsnorm_bwd_workspace_bytes(M: int, N: int, dtype_code: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    _check(lib.rmsnorm_bwd_workspace_bytes(M, N, dtype_code, ctypes.byref(out)), "rmsnorm_bwd_workspace_bytes")
+    return int(out.value)
+
+
+def alloc_workspace(M: int, N: int, dtype_code: int, device, op: Optional[int] = None):
+    """Workspace for a backward call; with `op`, also large enough for a plan
+    forced by rmsnorm_set_plan_override."""
+    torch = _torch()
+    nbytes = rmsnorm_bwd_workspace_bytes(M, N, dtype_code)
+    if op is not None:
+        for vec_ok in (True, False):
+            try:
+                nbytes = max(nbytes, rmsnorm_query_plan(op, M, N, dtype_code, vec_ok)["workspace_bytes"])
+            except RMSNormError:
+                pass  # a forced vector layout has no unaligned plan
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device), nbytes
+
+
+def _bwd_common(name, dy, dh, v, gamma, rstd, eps, offset, dx, dgamma, workspace):
+    torch = _torch()
+    lib = load_library()
+    _require(v, "x" if dh is None else "h")
+    M, N = _rows(v)
+    dev = v.device
+    _require(dy, "dy", v.shape, v.dtype, dev)
+    if dh is not None:
+        _require(dh, "dh", v.shape, v.dtype, dev)
+    _require(gamma, "gamma", (N,), v.dtype, dev)
+    if rstd is not None:
+        _require(rstd, "rstd", v.shape[:-1], torch.float32, dev)
+    if dx is None:
+        dx = torch.empty_like(v)
+    if dgamma is None:
+        dgamma = torch.empty_like(gamma)
+    _require(dx, "dx", v.shape, v.dtype, dev)
+    _require(dgamma, "dgamma", (N,), v.dtype, dev)
+    with _on_device(dev):
+        if workspace is None:
+            op = OP_BWD if name == "rmsnorm_bwd" else OP_FUSED_ADD_BWD
+            workspace, nbytes = alloc_workspace(M, N, _dtype_code(v), dev, op)
+        else:
+            _require(workspace, "workspace", device=dev)
+            nbytes = workspace.numel() * workspace.element_size()
+        if name == "rmsnorm_bwd":
+            rc = lib.rmsnorm_bwd(_ptr(dy), _ptr(v), _ptr(gamma), _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(workspace),
+                                 nbytes, M, N, eps, offset, _dtype_code(v), _stream(dev))
+        else:
+            rc = lib.rmsnorm_fused_add_bwd(_ptr(dy), _ptr(dh), _ptr(v), _ptr(gamma), _ptr(rstd), _ptr(dx),
+                                           _ptr(dgamma), _ptr(workspace), nbytes, M, N, eps, offset, _dtype_code(v),
+                                           _stream(dev))
+        _check(rc, name)
+    return dx, dgamma
+
+
+def rmsnorm_bwd(dy, x, gamma, rstd, eps: float = 1e-6, offset: float = 0.0, *, dx=None, dgamma=None,
+                workspace=None):
+    """Gradients of rmsnorm_fwd; rstd=None recomputes it.  Returns (dx, dgamma)."""
+    return _bwd_common("rmsnorm_bwd", dy, None, x, gamma, rstd, eps, offset, dx, dgamma, workspace)
+
+
+def rmsnorm_fused_add_bwd(dy, dh, h, gamma, rstd, eps: float = 1e-6, offset: float = 0.0, *, dx=None,
+                          dgamma=None, workspace=None):
+    """Gradients of rmsnorm_fused_add_fwd: dx (= dresidual) and dgamma.  dh may be None;
+    pass dx=dh to accumulate in place."""
+    return _bwd_common("rmsnorm_fused_add_bwd", dy, dh, h, gamma, rstd, eps, offset, dx, dgamma, workspace)
+
+
+def rmsnorm_bwd_partials(dy, v, gamma, rstd, dh=None, eps: float = 1e-6, offset: float = 0.0, *, dx=None,
+                         workspace=None):
+    """First backward stage: returns (dx, workspace, programs); the float32 partials
+    are workspace.view(float32)[: programs * ld] with ld = N rounded up to 64."""
+    torch = _torch()
+    lib = load_library()
+    M, N = _rows(v)
+    dev = v.device
+    if dx is None:
+        dx = torch.empty_like(v)
+    if workspace is None:
+        workspace, nbytes = alloc_workspace(M, N, _dtype_code(v), dev, OP_BWD if dh is None else OP_FUSED_ADD_BWD)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    programs = ctypes.c_int64(0)
+    with _on_device(dev):
+        _check(lib.rmsnorm_bwd_partials(_ptr(dy), _ptr(v), _ptr(gamma), _ptr(rstd), _ptr(dh), _ptr(dx),
+                                        _ptr(workspace), nbytes, ctypes.byref(programs), M, N, eps, offset,
+                                        _dtype_code(v), _stream(dev)), "rmsnorm_bwd_partials")
+    return dx, workspace, int(programs.value)
+
+
+def rmsnorm_dgamma_finalize(partials, programs: int, N: int, dgamma):
+    """Second backward stage: dgamma = fixed-order sum of `programs` partial rows."""
+    lib = load_library()
+    dev = dgamma.device
+    with _on_device(dev):
+        _check(lib.rmsnorm_dgamma_finalize(_ptr(partials), programs, N, _ptr(dgamma), _dtype_code(dgamma),
+                                           _stream(dev)), "rmsnorm_dgamma_finalize")
+    return dgamma
+
+
+def partial_ld(N: int) -> int:
+    return (N + 63) // 64 * 64
+
+
+def rmsnorm_query_plan(op: int, M: int, N: int, dtype_code: int, vec_ok: bool = True, num_cus: int = 0) -> dict:
+    lib = load_library()
+    p = Plan()
+    _check(lib.rmsnorm_query_plan(op, M, N, dtype_code, 1 if vec_ok else 0, num_cus, ctypes.byref(p)),
+           "rmsnorm_query_plan")
+    return p.as_dict()
+
+
+def rmsnorm_set_plan_override(op: int, plan: Optional[dict]):
+    """Force (path, vec, team, threads[, depth][, grid]) for later calls of `op`;
+    None clears.  A missing depth means 1."""
+    lib = load_library()
+    if plan is None:
+        _check(lib.rmsnorm_set_plan_override(op, None), "rmsnorm_set_plan_override")
+        return
+    p = Plan()
+    p.depth = 1
+    for k, v in plan.items():
+        setattr(p, k, v)
+    _check(lib.rmsnorm_set_plan_override(op, ctypes.byref(p)), "rmsnorm_set_plan_override")
+
+
+@contextlib.contextmanager
+def plan_override(op: int, **fields):
+    """Context manager around rmsnorm_set_plan_override (tests and tuning)."""
+    rmsnorm_set_plan_override(op, fields)
+    try:
+        yield
+    finally:
+        rmsnorm_set_plan_override(op, None)

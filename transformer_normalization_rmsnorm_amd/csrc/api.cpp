@@ -1,0 +1,350 @@
+// C ABI entry points: argument checks (before any HIP call), plan selection,
+// launches on the caller's stream.  No allocation, synchronisation, copy or
+// device-property query happens per call (the compute-unit count is read once
+// per device), so every entry point can be captured into a HIP graph; that
+// keeps small, host-bound shapes cheap (Liger-Kernel PR #1388, "Why the op was
+// slow in the first place"; FlyDSL PR #855, "Hot-cache launch path").
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "rmsnorm_internal.h"
+
+using namespace rmsnorm;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+thread_local char g_err[512];
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok()
+{
+    g_err[0] = '\0';
+    return RMSNORM_OK;
+}
+
+// Test/tuning override per op.
+struct Override {
+    bool set = false;
+    rmsnorm_plan plan = {};
+};
+Override g_override[4];
+
+int device_cus(int *cus)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(RMSNORM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(RMSNORM_EHIP, "device %d out of range", dev);
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || n <= 0)
+            return fail(RMSNORM_EHIP, "compute-unit count of device %d: %s", dev, hipGetErrorString(e));
+        g_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    *cus = n;
+    return RMSNORM_OK;
+}
+
+bool aligned(const void *p, size_t a) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_common(int64_t M, int64_t N, int dtype, float eps, float offset)
+{
+    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_F32)
+        return fail(RMSNORM_EUNSUPPORTED, "dtype %d not supported (0 = f32, 1 = bf16)", dtype);
+    if (M < 0)
+        return fail(RMSNORM_EINVAL, "M = %lld < 0", (long long)M);
+    if (N <= 0 || N > INT32_MAX)
+        return fail(RMSNORM_EINVAL, "N = %lld outside [1, 2^31-1]", (long long)N);
+    if (M > 0 && M > INT64_MAX / N / 4)
+        return fail(RMSNORM_EINVAL, "M * N too large");
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return fail(RMSNORM_EINVAL, "eps must be finite and >= 0");
+    if (!std::isfinite(offset))
+        return fail(RMSNORM_EINVAL, "offset must be finite");
+    return RMSNORM_OK;
+}
+
+// Plan for this call: the selector's, or the override's layout fitted to it.
+int plan_for(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int cus, rmsnorm_plan *p)
+{
+    int rc = select_plan(op, M, N, dtype, vec_ok, cus, p);
+    if (rc != RMSNORM_OK)
+        return fail(rc, "no plan for op %d M=%lld N=%lld dtype %d", op, (long long)M, (long long)N, dtype);
+    const Override &o = g_override[op];
+    if (o.set) {
+        rmsnorm_plan q = *p;
+        q.path = o.plan.path;
+        q.vec = o.plan.vec;
+        q.team = o.plan.team;
+        q.threads = o.plan.threads;
+        q.depth = o.plan.depth;
+        q.grid = o.plan.grid;
+        if (q.vec != 1 && !vec_ok)
+            return fail(RMSNORM_EINVAL, "override asks for 16-byte accesses on unaligned data");
+        if (!complete_plan(&q, M, N, dtype, cus, true))
+            return fail(RMSNORM_EINVAL, "override plan does not fit M=%lld N=%lld", (long long)M, (long long)N);
+        *p = q;
+    }
+    return RMSNORM_OK;
+}
+
+int launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(RMSNORM_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int do_fwd(const void *x, const void *r, const void *gamma, void *y, void *h, float *rstd, int64_t M,
+           int64_t N, float eps, float offset, int dtype, hipStream_t stream, bool fused)
+{
+    int rc = check_common(M, N, dtype, eps, offset);
+    if (rc)
+        return rc;
+    if (M == 0)
+        return ok();
+    if (!x || !gamma || (fused && (!r || !h)))
+        return fail(RMSNORM_EINVAL, "null input pointer");
+    if (!fused && !y && !rstd)
+        return fail(RMSNORM_EINVAL, "y and rstd are both null: nothing to compute");
+    const size_t eb = (size_t)elem_bytes(dtype);
+    if (!aligned(x, eb) || !aligned(gamma, eb) || !aligned(y, eb) || !aligned(r, eb) || !aligned(h, eb) ||
+        !aligned(rstd, 4))
+        return fail(RMSNORM_EINVAL, "pointer not aligned to its element size");
+    if (y && (y == x || y == gamma || (fused && (y == r || y == h))))
+        return fail(RMSNORM_EINVAL, "y aliases an input");
+    if (fused && h == x)
+        return fail(RMSNORM_EINVAL, "h_out aliases x (only residual may be overwritten)");
+    const bool vec_ok = aligned(x, 16) && aligned(gamma, 16) && aligned(y, 16) && aligned(r, 16) && aligned(h, 16);
+    int cus = 0;
+    if ((rc = device_cus(&cus)))
+        return rc;
+    rmsnorm_plan p;
+    if ((rc = plan_for(fused ? RMSNORM_OP_FUSED_ADD_FWD : RMSNORM_OP_FWD, M, N, dtype, vec_ok, cus, &p)))
+        return rc;
+    FwdArgs a{x, r, gamma, y, h, rstd, M, (int32_t)N, eps, offset};
+    return launched(launch_fwd(dtype, fused, p, a, stream), "forward");
+}
+
+// Shared by the backward entry points.  Writes dx and the partials; returns
+// the number of partial rows in *programs.
+int do_partials(const void *dy, const void *v, const void *gamma, const float *rstd, const void *dh, void *dx,
+                void *workspace, size_t workspace_bytes, int64_t *programs, int64_t M, int64_t N, float eps,
+                float offset, int dtype, hipStream_t stream)
+{
+    int rc = check_common(M, N, dtype, eps, offset);
+    if (rc)
+        return rc;
+    const bool fused = (dh != nullptr);
+    if (M > 0 && (!dy || !v || !gamma || !dx))
+        return fail(RMSNORM_EINVAL, "null input pointer");
+    const size_t eb = (size_t)elem_bytes(dtype);
+    if (!aligned(dy, eb) || !aligned(v, eb) || !aligned(gamma, eb) || !aligned(dh, eb) || !aligned(dx, eb) ||
+        !aligned(rstd, 4))
+        return fail(RMSNORM_EINVAL, "pointer not aligned to its element size");
+    if (!aligned(workspace, 16))
+        return fail(RMSNORM_EINVAL, "workspace must be 16-byte aligned");
+    if (M > 0 && (dx == dy || dx == v || dx == gamma))
+        return fail(RMSNORM_EINVAL, "dx aliases an input other than dh");
+    const bool vec_ok = aligned(dy, 16) && aligned(v, 16) && aligned(gamma, 16) && aligned(dh, 16) && aligned(dx, 16);
+    int cus = 0;
+    if ((rc = device_cus(&cus)))
+        return rc;
+    rmsnorm_plan p;
+    if ((rc = plan_for(fused ? RMSNORM_OP_FUSED_ADD_BWD : RMSNORM_OP_BWD, M, N, dtype, vec_ok, cus, &p)))
+        return rc;
+    if (p.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < (size_t)p.workspace_bytes))
+        return fail(RMSNORM_EWORKSPACE, "workspace of %zu bytes at %p; %lld bytes needed", workspace_bytes,
+                    workspace, (long long)p.workspace_bytes);
+    *programs = p.programs;
+    if (M == 0)
+        return ok();
+    const int64_t ld = partial_ld(N);
+    float *partials = static_cast<float *>(workspace);
+    const float *rs = rstd;
+    if (rs == nullptr) {
+        // recompute rstd from v into the workspace tail with an rstd-only forward
+        float *tail = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                                (p.workspace_bytes - ((M * 4 + 255) / 256) * 256));
+        rmsnorm_plan fp;
+        rc = select_plan(RMSNORM_OP_FWD, M, N, dtype, aligned(v, 16) && aligned(gamma, 16), cus, &fp);
+        if (rc)
+            return fail(rc, "no plan for the rstd recompute");
+        FwdArgs fa{v, nullptr, gamma, nullptr, nullptr, tail, M, (int32_t)N, eps, offset};
+        if ((rc = launched(launch_fwd(dtype, false, fp, fa, stream), "rstd recompute")))
+            return rc;
+        rs = tail;
+    }
+    BwdArgs a{dy, v, gamma, rs, dh, dx, partials, ld, M, (int32_t)N, offset};
+    return launched(launch_bwd(dtype, fused, p, a, stream), "backward");
+}
+
+int do_finalize(const float *partials, int64_t programs, int64_t N, void *dgamma, int dtype, hipStream_t stream)
+{
+    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_F32)
+        return fail(RMSNORM_EUNSUPPORTED, "dtype %d not supported", dtype);
+    if (N <= 0 || N > INT32_MAX || programs < 0)
+        return fail(RMSNORM_EINVAL, "bad N or programs");
+    if (!dgamma || (programs > 0 && !partials))
+        return fail(RMSNORM_EINVAL, "null pointer");
+    if (!aligned(partials, 16) || !aligned(dgamma, (size_t)elem_bytes(dtype)))
+        return fail(RMSNORM_EINVAL, "misaligned partials or dgamma");
+    return launched(launch_finalize(dtype, partials, programs, partial_ld(N), N, dgamma, stream), "finalize");
+}
+
+int do_bwd(const void *dy, const void *dh, const void *v, const void *gamma, const float *rstd, void *dx,
+           void *dgamma, void *workspace, size_t workspace_bytes, int64_t M, int64_t N, float eps, float offset,
+           int dtype, hipStream_t stream)
+{
+    if (!dgamma)
+        return fail(RMSNORM_EINVAL, "dgamma is null");
+    if (!aligned(dgamma, (size_t)elem_bytes(dtype == RMSNORM_BF16 ? RMSNORM_BF16 : RMSNORM_F32)))
+        return fail(RMSNORM_EINVAL, "dgamma not aligned to its element size");
+    int64_t programs = 0;
+    int rc = do_partials(dy, v, gamma, rstd, dh, dx, workspace, workspace_bytes, &programs, M, N, eps, offset,
+                         dtype, stream);
+    if (rc)
+        return rc;
+    return do_finalize(static_cast<const float *>(workspace), programs, N, dgamma, dtype, stream);
+}
+
+} // namespace
+
+extern "C" {
+
+int rmsnorm_fwd(const void *x, const void *gamma, void *y, float *rstd, int64_t M, int64_t N, float eps,
+                float offset, int dtype, rmsnorm_stream_t stream)
+{
+    return do_fwd(x, nullptr, gamma, y, nullptr, rstd, M, N, eps, offset, dtype, stream, false);
+}
+
+int rmsnorm_fused_add_fwd(const void *x, const void *residual, const void *gamma, void *y, void *h_out,
+                          float *rstd, int64_t M, int64_t N, float eps, float offset, int dtype,
+                          rmsnorm_stream_t stream)
+{
+    return do_fwd(x, residual, gamma, y, h_out, rstd, M, N, eps, offset, dtype, stream, true);
+}
+
+int rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *bytes)
+{
+    if (!bytes)
+        return fail(RMSNORM_EINVAL, "bytes is null");
+    int rc = check_common(M, N, dtype, 0.0f, 0.0f);
+    if (rc)
+        return rc;
+    int cus = 0;
+    if ((rc = device_cus(&cus)))
+        return rc;
+    int64_t need = 0;
+    for (int op : {RMSNORM_OP_BWD, RMSNORM_OP_FUSED_ADD_BWD})
+        for (bool vec_ok : {true, false}) {
+            rmsnorm_plan p;
+            if (select_plan(op, M, N, dtype, vec_ok, cus, &p) == RMSNORM_OK && p.workspace_bytes > need)
+                need = p.workspace_bytes;
+        }
+    *bytes = (size_t)need;
+    return ok();
+}
+
+int rmsnorm_bwd(const void *dy, const void *x, const void *gamma, const float *rstd, void *dx, void *dgamma,
+                void *workspace, size_t workspace_bytes, int64_t M, int64_t N, float eps, float offset, int dtype,
+                rmsnorm_stream_t stream)
+{
+    return do_bwd(dy, nullptr, x, gamma, rstd, dx, dgamma, workspace, workspace_bytes, M, N, eps, offset, dtype,
+                  stream);
+}
+
+int rmsnorm_fused_add_bwd(const void *dy, const void *dh, const void *h, const void *gamma, const float *rstd,
+                          void *dx, void *dgamma, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                          float eps, float offset, int dtype, rmsnorm_stream_t stream)
+{
+    // With no incoming residual gradient the fused backward is the plain one on h.
+    return do_bwd(dy, dh, h, gamma, rstd, dx, dgamma, workspace, workspace_bytes, M, N, eps, offset, dtype,
+                  stream);
+}
+
+int rmsnorm_bwd_partials(const void *dy, const void *v, const void *gamma, const float *rstd, const void *dh,
+                         void *dx, void *workspace, size_t workspace_bytes, int64_t *programs, int64_t M,
+                         int64_t N, float eps, float offset, int dtype, rmsnorm_stream_t stream)
+{
+    if (!programs)
+        return fail(RMSNORM_EINVAL, "programs is null");
+    return do_partials(dy, v, gamma, rstd, dh, dx, workspace, workspace_bytes, programs, M, N, eps, offset, dtype,
+                       stream);
+}
+
+int rmsnorm_dgamma_finalize(const float *partials, int64_t programs, int64_t N, void *dgamma, int dtype,
+                            rmsnorm_stream_t stream)
+{
+    return do_finalize(partials, programs, N, dgamma, dtype, stream);
+}
+
+int rmsnorm_query_plan(int op, int64_t M, int64_t N, int dtype, int vec_ok, int num_cus, rmsnorm_plan *out)
+{
+    if (!out)
+        return fail(RMSNORM_EINVAL, "out is null");
+    int cus = num_cus;
+    if (cus <= 0) {
+        int rc = device_cus(&cus);
+        if (rc)
+            return rc;
+    }
+    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_FUSED_ADD_BWD)
+        return fail(RMSNORM_EINVAL, "op %d unknown", op);
+    rmsnorm_plan p;
+    int rc = plan_for(op, M, N, dtype, vec_ok != 0, cus, &p);
+    if (rc)
+        return rc;
+    *out = p;
+    return ok();
+}
+
+int rmsnorm_set_plan_override(int op, const rmsnorm_plan *plan)
+{
+    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_FUSED_ADD_BWD)
+        return fail(RMSNORM_EINVAL, "op %d unknown", op);
+    if (plan == nullptr) {
+        g_override[op].set = false;
+        return ok();
+    }
+    g_override[op].plan = *plan;
+    g_override[op].plan.op = op;
+    g_override[op].set = true;
+    return ok();
+}
+
+const char *rmsnorm_status_string(int status)
+{
+    switch (status) {
+    case RMSNORM_OK: return "ok";
+    case RMSNORM_EINVAL: return "invalid argument";
+    case RMSNORM_EUNSUPPORTED: return "unsupported dtype or configuration";
+    case RMSNORM_EWORKSPACE: return "workspace missing or too small";
+    case RMSNORM_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *rmsnorm_last_error(void) { return g_err; }
+
+int rmsnorm_version(void) { return 1; }
+
+} // extern "C"

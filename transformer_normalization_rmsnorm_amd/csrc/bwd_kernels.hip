@@ -1,0 +1,346 @@
+// RMSNorm backward kernels for gfx950 (plain and fused residual add).
+//
+// With w = gamma + offset, g = dy * w, xhat = v * rstd and
+// c = (1/N) sum_j g_j xhat_j, a row's input gradient is
+//     dx = rstd * (g - xhat * c)  [+ dh for the fused-add op],
+// evaluated here as dx = rstd * g - v * (rstd^3 * dot / N) with
+// dot = sum_j g_j v_j, and dgamma_j = sum over rows of dy_j * xhat_j.
+//
+// Structure (FlyDSL PR #855, "Hybrid atomic / two-stage backward" and
+// "512-thread vec8 fast path"): a bounded persistent grid of P workgroups walks
+// the rows in a grid-stride loop, loads w once per workgroup, keeps each row's
+// v and dy in VGPRs across both passes, writes dx with 16-byte stores and
+// accumulates float32 dgamma partials in registers; at the end each workgroup
+// writes one partial row.  A finalizer then sums the [P, N] partials in a
+// fixed order and writes dgamma in the parameter dtype: no atomics, no clear
+// and no separate conversion kernel.  Unlike the page's kernel, each team keeps
+// D further rows in flight (row_pipeline) while it reduces and writes the
+// current one, so HBM latency overlaps the work instead of stalling it.
+#include "device_common.h"
+#include "rmsnorm_internal.h"
+
+namespace rmsnorm {
+
+template <typename T, int V, int K, bool FUSED>
+struct BwdRow {
+    Chunk<T, V> v[K];
+    Chunk<T, V> dy[K];
+    Chunk<T, V> dh[FUSED ? K : 1];
+    float rs;
+};
+
+template <typename T, int V, int TEAM, int K, int D, bool FUSED, bool EXACT>
+__global__ void __launch_bounds__(rows_max_threads(true, TEAM, K)) bwd_rows_kernel(BwdArgs a)
+{
+    using Row = BwdRow<T, V, K, FUSED>;
+    const int tl = TEAM ? TEAM : a.threads;
+    const int lane = TEAM ? (int)(threadIdx.x & (TEAM - 1)) : (int)threadIdx.x;
+    const int tpb = TEAM ? a.threads / TEAM : 1;
+    const int team = TEAM ? (int)(threadIdx.x / TEAM) : 0;
+    const int N = a.N;
+    const int nchunks = N / V;
+    const float inv_n = 1.0f / (float)N;
+    const T *__restrict__ dyp = static_cast<const T *>(a.dy);
+    const T *__restrict__ vp = static_cast<const T *>(a.v);
+    const T *__restrict__ gp = static_cast<const T *>(a.gamma);
+    const T *dhp = static_cast<const T *>(a.dh); // dx may alias dh
+    T *dxp = static_cast<T *>(a.dx);
+    const float *__restrict__ rstd = a.rstd;
+
+    float w[K][V], acc[K][V];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int c = k * tl + lane;
+        Chunk<T, V> g;
+        if (EXACT || c < nchunks)
+            g.load(gp + (int64_t)c * V);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            w[k][e] = (EXACT || c < nchunks) ? g.get(e) + a.offset : 0.0f;
+            acc[k][e] = 0.0f;
+        }
+    }
+
+    auto load = [&](Row &b, int64_t row) __attribute__((always_inline)) {
+        const int64_t base = row * N;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * tl + lane;
+            if (EXACT || c < nchunks) {
+                b.v[k].load(vp + base + (int64_t)c * V);
+                b.dy[k].load(dyp + base + (int64_t)c * V);
+                if constexpr (FUSED)
+                    b.dh[k].load(dhp + base + (int64_t)c * V);
+            }
+        }
+        b.rs = rstd[row];
+    };
+
+    __shared__ float red[2][16];
+    int parity = 0;
+    auto proc = [&](Row &b, int64_t row) __attribute__((always_inline)) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * tl + lane;
+            if (EXACT || c < nchunks) {
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    dot = fmaf(b.dy[k].get(e) * w[k][e], b.v[k].get(e), dot);
+            }
+        }
+        if constexpr (TEAM == 0) {
+            dot = block_sum(dot, red[parity], a.threads);
+            parity ^= 1;
+        } else {
+            dot = team_sum<TEAM>(dot);
+        }
+        const float rs = b.rs;
+        const float kc = rs * rs * rs * dot * inv_n; // dx = rs * g - v * kc
+        const int64_t base = row * N;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * tl + lane;
+            if (EXACT || c < nchunks) {
+                float o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float xv = b.v[k].get(e);
+                    const float d = b.dy[k].get(e);
+                    float dxv = fmaf(rs, d * w[k][e], -xv * kc);
+                    if constexpr (FUSED)
+                        dxv += b.dh[k].get(e);
+                    o[e] = dxv;
+                    acc[k][e] = fmaf(d, xv * rs, acc[k][e]);
+                }
+                Chunk<T, V> out;
+                out.set(o);
+                out.store(dxp + base + (int64_t)c * V);
+            }
+        }
+    };
+
+    row_pipeline<D, Row>((int64_t)blockIdx.x * tpb + team, a.grid * tpb, a.M, load, proc);
+
+    float *__restrict__ part = a.partials + (int64_t)blockIdx.x * a.ld;
+    if constexpr (TEAM == 0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * tl + lane;
+            if (EXACT || c < nchunks)
+                store_f32<V>(part + (int64_t)c * V, acc[k]);
+        }
+    } else {
+        // Several teams per workgroup: add their partials in team order.
+        extern __shared__ float team_acc[]; // [tpb][N]
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * tl + lane;
+            if (EXACT || c < nchunks) {
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    team_acc[team * N + c * V + e] = acc[k][e];
+            }
+        }
+        __syncthreads();
+        for (int j = threadIdx.x; j < N; j += a.threads) {
+            float s = team_acc[j];
+            for (int t = 1; t < tpb; ++t)
+                s += team_acc[t * N + j];
+            part[j] = s;
+        }
+    }
+}
+
+// Any N: per row, pass 1 forms dot, pass 2 re-reads the row, writes dx and
+// accumulates this workgroup's partial row in place (each lane always owns the
+// same columns, so the read-modify-write is private to the lane).
+template <typename T, int V, bool FUSED>
+__global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
+{
+    using C = Chunk<T, V>;
+    const int nt = a.threads;
+    const int N = a.N;
+    const int nchunks = N / V;
+    const float inv_n = 1.0f / (float)N;
+    const T *__restrict__ dyp = static_cast<const T *>(a.dy);
+    const T *__restrict__ vp = static_cast<const T *>(a.v);
+    const T *__restrict__ gp = static_cast<const T *>(a.gamma);
+    const T *dhp = static_cast<const T *>(a.dh);
+    T *dxp = static_cast<T *>(a.dx);
+    float *part = a.partials + (int64_t)blockIdx.x * a.ld;
+
+    __shared__ float red[2][16];
+    int parity = 0;
+    for (int64_t row = blockIdx.x; row < a.M; row += a.grid) {
+        const bool first = (row == (int64_t)blockIdx.x);
+        const int64_t base = row * N;
+        float dot = 0.0f;
+        for (int c = threadIdx.x; c < nchunks; c += nt) {
+            C v, d, g;
+            v.load(vp + base + (int64_t)c * V);
+            d.load(dyp + base + (int64_t)c * V);
+            g.load(gp + (int64_t)c * V);
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                dot = fmaf(d.get(e) * (g.get(e) + a.offset), v.get(e), dot);
+        }
+        dot = block_sum(dot, red[parity], a.threads);
+        parity ^= 1;
+        const float rs = a.rstd[row];
+        const float kc = rs * rs * rs * dot * inv_n;
+        for (int c = threadIdx.x; c < nchunks; c += nt) {
+            C v, d, g;
+            v.load(vp + base + (int64_t)c * V);
+            d.load(dyp + base + (int64_t)c * V);
+            g.load(gp + (int64_t)c * V);
+            float o[V], pa[V];
+            if (first) {
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    pa[e] = 0.0f;
+            } else {
+                load_f32<V>(part + (int64_t)c * V, pa);
+            }
+            C dh;
+            if constexpr (FUSED)
+                dh.load(dhp + base + (int64_t)c * V);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float xv = v.get(e);
+                const float dv = d.get(e);
+                float dxv = fmaf(rs, dv * (g.get(e) + a.offset), -xv * kc);
+                if constexpr (FUSED)
+                    dxv += dh.get(e);
+                o[e] = dxv;
+                pa[e] = fmaf(dv, xv * rs, pa[e]);
+            }
+            C out;
+            out.set(o);
+            out.store(dxp + base + (int64_t)c * V);
+            store_f32<V>(part + (int64_t)c * V, pa);
+        }
+    }
+}
+
+// dgamma_j = round_T(sum_p partials[p, j]).  Workgroup b owns the 32 columns
+// [32b, 32b + 32) (one 128-byte line per partial row): lane (cg, pg) sums
+// float4 column group cg over the rows p = pg, pg + 32, pg + 64, ... in
+// increasing p, issuing kFinDepth loads before adding them so that their
+// latencies overlap; the 32 group sums are then added in pg order.  The order
+// depends only on P, so dgamma is bit-reproducible.
+template <typename T>
+__global__ void __launch_bounds__(kFinThreads) finalize_kernel(const float *__restrict__ part, int64_t P,
+                                                               int64_t ld, int64_t N, T *__restrict__ dg)
+{
+    constexpr int CG = kFinColsPerBlock / 4; // float4 groups per workgroup
+    constexpr int PG = kFinThreads / CG;     // partial-row groups
+    constexpr int kFinDepth = 16;
+    const int cg = threadIdx.x % CG;
+    const int pg = threadIdx.x / CG;
+    const int64_t col = (int64_t)blockIdx.x * kFinColsPerBlock + cg * 4;
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (col < ld) {
+        for (int64_t p0 = pg; p0 < P; p0 += (int64_t)PG * kFinDepth) {
+            float4 t[kFinDepth];
+#pragma unroll
+            for (int i = 0; i < kFinDepth; ++i) {
+                const int64_t p = p0 + (int64_t)i * PG;
+                t[i] = p < P ? *reinterpret_cast<const float4 *>(part + p * ld + col)
+                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int i = 0; i < kFinDepth; ++i) {
+                s.x += t[i].x;
+                s.y += t[i].y;
+                s.z += t[i].z;
+                s.w += t[i].w;
+            }
+        }
+    }
+    __shared__ float4 red[PG][CG];
+    red[pg][cg] = s;
+    __syncthreads();
+    if (pg == 0) {
+        float4 t = red[0][cg];
+        for (int i = 1; i < PG; ++i) {
+            const float4 u = red[i][cg];
+            t.x += u.x;
+            t.y += u.y;
+            t.z += u.z;
+            t.w += u.w;
+        }
+        const float f[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (col + e < N) {
+                if constexpr (sizeof(T) == 2)
+                    dg[col + e] = to_bf16(f[e]);
+                else
+                    dg[col + e] = f[e];
+            }
+        }
+    }
+}
+
+template <typename T, int V, int TEAM, int K, int D, bool FUSED>
+static void launch_bwd_rows(const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
+    const int lanes = TEAM ? TEAM : p.threads;
+    const size_t lds = TEAM ? (size_t)(p.threads / TEAM) * (size_t)a.N * sizeof(float) : 0;
+    if constexpr (V > 1) {
+        if ((int64_t)lanes * K == a.N / V) {
+            hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, FUSED, true>), grid, block, lds, s, a);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, FUSED, false>), grid, block, lds, s, a);
+}
+
+template <typename T, bool FUSED>
+static hipError_t dispatch_bwd(const rmsnorm_plan &p, BwdArgs a, hipStream_t s)
+{
+    constexpr int VV = 16 / (int)sizeof(T);
+    a.threads = p.threads;
+    a.grid = p.grid;
+    const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
+    if (p.path == RMSNORM_PATH_LOOP) {
+        if (p.vec == VV)
+            hipLaunchKernelGGL((bwd_loop_kernel<T, VV, FUSED>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((bwd_loop_kernel<T, 1, FUSED>), grid, block, 0, s, a);
+        return hipGetLastError();
+    }
+    const bool vec = (p.vec == VV);
+#define RMSNORM_CASE(VEC, TEAM, K, D)                                                        \
+    if (vec == (VEC == 1) && p.team == TEAM && p.chunks == K && p.depth == D) {              \
+        launch_bwd_rows<T, (VEC == 1 ? VV : 1), TEAM, K, D, FUSED>(p, a, s);                 \
+        return hipGetLastError();                                                            \
+    }
+    RMSNORM_BWD_ROWS_CONFIGS(RMSNORM_CASE)
+#undef RMSNORM_CASE
+    return hipErrorInvalidConfiguration;
+}
+
+hipError_t launch_bwd(int dtype, bool fused, const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s)
+{
+    if (dtype == RMSNORM_BF16)
+        return fused ? dispatch_bwd<bf16_t, true>(p, a, s) : dispatch_bwd<bf16_t, false>(p, a, s);
+    return fused ? dispatch_bwd<float, true>(p, a, s) : dispatch_bwd<float, false>(p, a, s);
+}
+
+hipError_t launch_finalize(int dtype, const float *partials, int64_t programs, int64_t ld, int64_t N,
+                           void *dgamma, hipStream_t s)
+{
+    const dim3 grid((unsigned)((ld + kFinColsPerBlock - 1) / kFinColsPerBlock)), block(kFinThreads);
+    if (dtype == RMSNORM_BF16)
+        hipLaunchKernelGGL((finalize_kernel<bf16_t>), grid, block, 0, s, partials, programs, ld, N,
+                           static_cast<bf16_t *>(dgamma));
+    else
+        hipLaunchKernelGGL((finalize_kernel<float>), grid, block, 0, s, partials, programs, ld, N,
+                           static_cast<float *>(dgamma));
+    return hipGetLastError();
+}
+
+} // namespace rmsnorm

@@ -1,0 +1,251 @@
+// Device helpers for the gfx950 RMSNorm kernels: vector chunks of a row,
+// bf16 <-> f32 conversion, and wavefront / workgroup sum reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmsnorm {
+
+// bf16 is carried as its raw 16-bit pattern.
+using bf16_t = uint16_t;
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 -> f32 is exact: the bf16 bits are the high half of the f32 bits.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two f32 -> packed bf16x2, round to nearest even, with gfx950's
+// v_cvt_pk_bf16_f32 (the hardware conversion FlyDSL PR #855 uses on gfx95,
+// "512-thread vec8 fast path").  Element 0 lands in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float f)
+{
+    return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
+}
+
+// A chunk is the V consecutive elements of a row that one lane moves with one
+// memory instruction: 16 bytes (bf16 x8, f32 x4) on the vector path, one
+// element on the scalar path.
+template <typename T, int V>
+struct Chunk;
+
+template <>
+struct Chunk<bf16_t, 8> {
+    uint32_t w[4];
+    __device__ __forceinline__ void load(const bf16_t *p)
+    {
+        const uint4 u = *reinterpret_cast<const uint4 *>(p);
+        w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    }
+    __device__ __forceinline__ void store(bf16_t *p) const
+    {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    __device__ __forceinline__ float get(int e) const { return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]); }
+    __device__ __forceinline__ void set(const float (&f)[8])
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    }
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = 0u;
+    }
+};
+
+template <>
+struct Chunk<bf16_t, 1> {
+    uint16_t b;
+    __device__ __forceinline__ void load(const bf16_t *p) { b = *p; }
+    __device__ __forceinline__ void store(bf16_t *p) const { *p = b; }
+    __device__ __forceinline__ float get(int) const { return __uint_as_float((uint32_t)b << 16); }
+    __device__ __forceinline__ void set(const float (&f)[1]) { b = to_bf16(f[0]); }
+    __device__ __forceinline__ void zero() { b = 0; }
+};
+
+template <>
+struct Chunk<float, 4> {
+    float v[4];
+    __device__ __forceinline__ void load(const float *p)
+    {
+        const float4 u = *reinterpret_cast<const float4 *>(p);
+        v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+    }
+    __device__ __forceinline__ void store(float *p) const
+    {
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    __device__ __forceinline__ float get(int e) const { return v[e]; }
+    __device__ __forceinline__ void set(const float (&f)[4])
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = f[i];
+    }
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = 0.0f;
+    }
+};
+
+template <>
+struct Chunk<float, 1> {
+    float v;
+    __device__ __forceinline__ void load(const float *p) { v = *p; }
+    __device__ __forceinline__ void store(float *p) const { *p = v; }
+    __device__ __forceinline__ float get(int) const { return v; }
+    __device__ __forceinline__ void set(const float (&f)[1]) { v = f[0]; }
+    __device__ __forceinline__ void zero() { v = 0.0f; }
+};
+
+// V float32 values of a dgamma partial row: 16-byte accesses when V >= 4.
+template <int V>
+__device__ __forceinline__ void store_f32(float *p, const float (&a)[V])
+{
+    if constexpr (V % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < V; i += 4)
+            *reinterpret_cast<float4 *>(p + i) = make_float4(a[i], a[i + 1], a[i + 2], a[i + 3]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            p[i] = a[i];
+    }
+}
+
+template <int V>
+__device__ __forceinline__ void load_f32(const float *p, float (&a)[V])
+{
+    if constexpr (V % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < V; i += 4) {
+            const float4 u = *reinterpret_cast<const float4 *>(p + i);
+            a[i] = u.x; a[i + 1] = u.y; a[i + 2] = u.z; a[i + 3] = u.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            a[i] = p[i];
+    }
+}
+
+// ---- reductions -----------------------------------------------------------
+
+// DPP lane permutations within a 16-lane row (gfx9 encodings).
+enum : int {
+    kDppQuadXor1 = 0xB1,    // quad_perm [1,0,3,2]
+    kDppQuadXor2 = 0x4E,    // quad_perm [2,3,0,1]
+    kDppRowHalfMirror = 0x141,
+    kDppRowMirror = 0x140,
+};
+// ds_swizzle bit mode: and_mask 0x1f, or_mask 0, xor_mask 0x10 (swap 16-lane halves of 32).
+constexpr int kSwizzleXor16 = 0x401F;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over an aligned group of TEAM lanes (8, 16, 32 or 64); every lane of the
+// group gets the same total.  The butterfly stays inside the group, so groups
+// of a wavefront may be active independently.
+template <int TEAM>
+__device__ __forceinline__ float team_sum(float v)
+{
+    static_assert(TEAM == 8 || TEAM == 16 || TEAM == 32 || TEAM == 64, "team size");
+    v += dpp<kDppQuadXor1>(v);
+    v += dpp<kDppQuadXor2>(v);
+    v += dpp<kDppRowHalfMirror>(v); // lane i <- lane 7-i within each 8: quads combine
+    if constexpr (TEAM >= 16)
+        v += dpp<kDppRowMirror>(v); // lane i <- lane 15-i: 8-lane halves combine
+    if constexpr (TEAM >= 32)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), kSwizzleXor16));
+    if constexpr (TEAM == 64) {
+        const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+        const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+        v = lo + hi;
+    }
+    return v;
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
+// memory, which makes the compiler wait for every outstanding global load
+// (s_waitcnt vmcnt(0)) and so drains the rows a team has in flight; the
+// reductions here exchange data through LDS alone.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Sum over the whole workgroup of `threads` lanes (a multiple of 64, at most
+// 1024): wavefront sums, then a fixed-order sum of the per-wave totals through
+// LDS.  `slot` holds 16 floats; callers alternate between two slots on
+// consecutive calls so that one barrier per call suffices.
+__device__ __forceinline__ float block_sum(float v, float *slot, int threads)
+{
+    v = team_sum<64>(v);
+    const int nw = threads >> 6;
+    if (nw == 1)
+        return v;
+    if ((threadIdx.x & 63) == 0)
+        slot[threadIdx.x >> 6] = v;
+    lds_barrier();
+    float s = slot[0];
+    for (int i = 1; i < nw; ++i)
+        s += slot[i];
+    return s;
+}
+
+// ---- row pipeline ---------------------------------------------------------
+
+// A team walks rows row0, row0 + stride, ... < M.  It keeps D rows in flight:
+// the loads of row i + D * stride are issued before row i is reduced and
+// written, so each row's memory latency overlaps the work on the D rows before
+// it.  The D + 1 row buffers form a ring whose indices are compile-time
+// constants after unrolling, so the buffers live in VGPRs.
+//
+// Every load is issued unconditionally: a row index past the team's last row
+// is clamped to that last row (a repeat load that hits in cache).  The
+// compiler's wait counting does not follow values across branches, so a load
+// that may be skipped on some path makes it wait for all outstanding loads
+// (s_waitcnt vmcnt(0)), which would drain the rows in flight.  The row test
+// is uniform across the team (across the workgroup for workgroup teams), so
+// `proc` may contain workgroup barriers.
+template <int D, typename Row, typename LoadF, typename ProcF>
+__device__ __forceinline__ void row_pipeline(int64_t row0, int64_t stride, int64_t M, LoadF &&load, ProcF &&proc)
+{
+    const int64_t last = row0 < M ? row0 + (M - 1 - row0) / stride * stride : M - 1;
+    auto clamp = [&](int64_t r) __attribute__((always_inline)) { return r < last ? r : last; };
+    Row buf[D + 1];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        load(buf[d], clamp(row0 + (int64_t)d * stride));
+    for (int64_t base = row0; base < M; base += (int64_t)(D + 1) * stride) {
+#pragma unroll
+        for (int s = 0; s <= D; ++s) {
+            const int64_t r = base + (int64_t)s * stride;
+            if (r >= M)
+                break;
+            load(buf[(s + D) % (D + 1)], clamp(r + (int64_t)D * stride));
+            proc(buf[s], r);
+        }
+    }
+}
+
+} // namespace rmsnorm

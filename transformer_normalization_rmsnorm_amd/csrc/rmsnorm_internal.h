@@ -1,0 +1,116 @@
+// Internal interfaces between the C ABI layer, the selector and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rmsnorm.h"
+
+namespace rmsnorm {
+
+// Launch geometry travels in the arguments: reading blockDim/gridDim inside a
+// kernel costs a 16-bit vector load from the implicit arguments on gfx9,
+// whose wait drains every outstanding load.
+struct FwdArgs {
+    const void *x;
+    const void *r;     // residual (fused-add only)
+    const void *gamma;
+    void *y;           // may be null: rstd only
+    void *h;           // fused-add output round(x + r)
+    float *rstd;       // may be null
+    int64_t M;
+    int32_t N;
+    float eps;
+    float offset;
+    int32_t threads; // workgroup size of the launch
+    int64_t grid;    // workgroups of the launch
+};
+
+struct BwdArgs {
+    const void *dy;
+    const void *v;     // x, or h for the fused-add op
+    const void *gamma;
+    const float *rstd;
+    const void *dh;    // fused-add only (non-null)
+    void *dx;
+    float *partials;   // [programs, ld]
+    int64_t ld;        // partial row stride in floats (multiple of 64)
+    int64_t M;
+    int32_t N;
+    float offset;
+    int32_t threads; // workgroup size of the launch
+    int64_t grid;    // workgroups of the launch
+};
+
+// Partial rows are padded to this many floats (256 bytes).
+constexpr int64_t kPartialAlign = 64;
+inline int64_t partial_ld(int64_t N) { return (N + kPartialAlign - 1) / kPartialAlign * kPartialAlign; }
+
+// Finalizer geometry: each workgroup owns 32 columns (8 lanes x float4) and
+// splits the partial rows over 32 groups of lanes.
+constexpr int kFinThreads = 256;
+constexpr int kFinColsPerBlock = 32;
+
+// The compiled register-path configurations: X(vector access, team lanes
+// (0 = whole workgroup), chunks per lane, rows loaded ahead).  This list is
+// the one owner of "which kernels exist"; the selector and the dispatchers
+// both expand it.
+#define RMSNORM_FWD_ROWS_CONFIGS(X)                                                      \
+    X(1, 8, 1, 1) X(1, 16, 1, 1) X(1, 32, 1, 1) X(1, 16, 1, 2) X(1, 32, 1, 2)            \
+    X(1, 64, 1, 1) X(1, 64, 2, 1) X(1, 64, 4, 1) X(1, 64, 8, 1) X(1, 64, 2, 2)          \
+    X(1, 64, 4, 2)                                                                       \
+    X(1, 0, 1, 1) X(1, 0, 2, 1) X(1, 0, 3, 1) X(1, 0, 4, 1) X(1, 0, 6, 1)                \
+    X(1, 0, 1, 2) X(1, 0, 2, 2) X(1, 0, 3, 2) X(1, 0, 4, 2) X(1, 0, 1, 3) X(1, 0, 2, 3)  \
+    X(0, 64, 1, 1) X(0, 64, 2, 1) X(0, 64, 4, 1) X(0, 64, 8, 1)                          \
+    X(0, 0, 1, 1) X(0, 0, 2, 1) X(0, 0, 4, 1) X(0, 0, 8, 1) X(0, 0, 16, 1)
+
+#define RMSNORM_BWD_ROWS_CONFIGS(X)                                                      \
+    X(1, 8, 1, 1) X(1, 16, 1, 1) X(1, 32, 1, 1) X(1, 8, 1, 2) X(1, 16, 1, 2)             \
+    X(1, 32, 1, 2) X(1, 64, 1, 1) X(1, 64, 2, 1) X(1, 64, 1, 2)                          \
+    X(1, 0, 1, 1) X(1, 0, 1, 2) X(1, 0, 1, 3) X(1, 0, 2, 1) X(1, 0, 2, 2) X(1, 0, 3, 1)  \
+    X(0, 64, 1, 1) X(0, 64, 2, 1) X(0, 0, 1, 1) X(0, 0, 2, 1) X(0, 0, 4, 1)
+
+inline bool fwd_rows_compiled(bool vec, int team, int chunks, int depth)
+{
+#define RMSNORM_MATCH(V, TEAM, K, D) \
+    || ((V) == (vec ? 1 : 0) && (TEAM) == team && (K) == chunks && (D) == depth)
+    return false RMSNORM_FWD_ROWS_CONFIGS(RMSNORM_MATCH);
+#undef RMSNORM_MATCH
+}
+
+inline bool bwd_rows_compiled(bool vec, int team, int chunks, int depth)
+{
+#define RMSNORM_MATCH(V, TEAM, K, D) \
+    || ((V) == (vec ? 1 : 0) && (TEAM) == team && (K) == chunks && (D) == depth)
+    return false RMSNORM_BWD_ROWS_CONFIGS(RMSNORM_MATCH);
+#undef RMSNORM_MATCH
+}
+
+// Workgroup-size bound each kernel is compiled for (its __launch_bounds__):
+// teams of at most a wavefront run in 256-thread workgroups; a workgroup team
+// holding more chunks per lane (backward: more than one, forward: more than
+// two) is capped at 512 threads so that it may use up to 256 VGPRs instead of
+// spilling.
+constexpr int rows_max_threads(bool bwd, int team, int chunks)
+{
+    return team != 0 ? 256 : (chunks > (bwd ? 1 : 2) ? 512 : 1024);
+}
+
+// Elements per 16-byte access.
+inline int vec_elems(int dtype) { return dtype == RMSNORM_BF16 ? 8 : 4; }
+inline int elem_bytes(int dtype) { return dtype == RMSNORM_BF16 ? 2 : 4; }
+
+// Selector (pure; selector.cpp).
+int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cus, rmsnorm_plan *out);
+// Fill the derived fields (chunks, grid, programs, workspace, finalizer) of a
+// plan whose path/vec/team/threads are set; returns false if it cannot run.
+bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus, bool keep_grid);
+int64_t bwd_workspace_bytes(int64_t programs, int64_t M, int64_t N);
+
+// Kernel launchers (fwd_kernels.hip, bwd_kernels.hip).
+hipError_t launch_fwd(int dtype, bool fused, const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s);
+hipError_t launch_bwd(int dtype, bool fused, const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s);
+hipError_t launch_finalize(int dtype, const float *partials, int64_t programs, int64_t ld, int64_t N,
+                           void *dgamma, hipStream_t s);
+
+} // namespace rmsnorm

@@ -1,0 +1,189 @@
+// Shape/dtype selector: a pure function from (op, M, N, dtype, alignment,
+// compute-unit count) to a launch plan.  No HIP calls.
+//
+// Prior art it starts from (FlyDSL PR #855, "Runtime configuration and
+// ownership" and "512-thread vec8 fast path"): a vector path for 16-byte
+// aligned rows with N a multiple of the vector width, a scalar path otherwise,
+// a persistent backward grid of about one to two programs per compute unit
+// capped by the row count, and one owner for the vector/scalar decision.  Here
+// that owner is the configuration table in rmsnorm_internal.h.  Narrow rows
+// (up to 32 vectors) are shared by teams of 8-32 lanes so a wavefront holds
+// several rows, and rows too wide for registers take the looped path.
+#include <algorithm>
+
+#include "rmsnorm_internal.h"
+
+namespace rmsnorm {
+
+namespace {
+
+constexpr int kRowsThreads = 256;   // workgroup size when a team is at most one wavefront
+constexpr int kLoopThreads = 1024;  // looped path workgroup size
+constexpr int kBwdProgramsPerCU = 2; // persistent backward programs per compute unit
+constexpr int64_t kMaxGrid = int64_t(1) << 30;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+int pow2_at_least(int64_t v)
+{
+    int p = 1;
+    while (p < v)
+        p <<= 1;
+    return p;
+}
+
+bool is_bwd(int op) { return op == RMSNORM_OP_BWD || op == RMSNORM_OP_FUSED_ADD_BWD; }
+
+bool compiled(bool bwd, bool vec, int team, int k, int depth)
+{
+    return bwd ? bwd_rows_compiled(vec, team, k, depth) : fwd_rows_compiled(vec, team, k, depth);
+}
+
+// Smallest compiled chunk count >= need for (vec, team, depth).
+int pick_chunks(bool bwd, bool vec, int team, int depth, int64_t need)
+{
+    for (int k = 1; k <= 16; ++k)
+        if (k >= need && compiled(bwd, vec, team, k, depth))
+            return k;
+    return 0;
+}
+
+// Workgroup-wide team: the fewest chunks per lane whose thread count (a
+// multiple of 64) fits the kernel's launch bound, preferring `cap` threads.
+// The backward prefers one chunk per lane (its registers also hold w, the
+// dgamma accumulators and the rows in flight).
+bool pick_block_team(bool bwd, bool vec, int64_t nchunks, int depth, rmsnorm_plan *p)
+{
+    const int caps_fwd[2] = {512, 1024}, caps_bwd[2] = {1024, 1024};
+    for (int cap : bwd ? caps_bwd : caps_fwd) {
+        for (int k = 1; k <= 16; ++k) {
+            if (!compiled(bwd, vec, 0, k, depth))
+                continue;
+            const int64_t threads = std::max<int64_t>(64, round_up(ceil_div(nchunks, k), 64));
+            if (threads <= cap && threads <= rows_max_threads(bwd, 0, k)) {
+                p->team = 0;
+                p->threads = (int32_t)threads;
+                p->chunks = k;
+                p->depth = depth;
+                return true;
+            }
+        }
+    }
+    return false;
+}
+
+} // namespace
+
+int64_t bwd_workspace_bytes(int64_t programs, int64_t M, int64_t N)
+{
+    return round_up(programs * partial_ld(N) * (int64_t)sizeof(float), 256) +
+           round_up(M * (int64_t)sizeof(float), 256);
+}
+
+bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus, bool keep_grid)
+{
+    const bool bwd = is_bwd(p->op);
+    const int VV = vec_elems(dtype);
+    if (p->vec != 1 && p->vec != VV)
+        return false;
+    if (N % p->vec != 0)
+        return false;
+    if (p->threads < 64 || p->threads > 1024 || p->threads % 64 != 0)
+        return false;
+    const int64_t nchunks = N / p->vec;
+    int64_t rows_per_block = 1;
+    if (p->path == RMSNORM_PATH_ROWS) {
+        if (p->team != 0) {
+            if (p->team != 8 && p->team != 16 && p->team != 32 && p->team != 64)
+                return false;
+            if (p->threads % p->team != 0 || p->threads > 256)
+                return false;
+            rows_per_block = p->threads / p->team;
+        }
+        const int lanes = p->team ? p->team : p->threads;
+        const int k = pick_chunks(bwd, p->vec != 1, p->team, p->depth, ceil_div(nchunks, lanes));
+        if (k == 0 || p->threads > rows_max_threads(bwd, p->team, k))
+            return false;
+        p->chunks = k;
+        if (bwd && p->team != 0 && rows_per_block * N * (int64_t)sizeof(float) > 65536)
+            return false; // team partials are combined in LDS
+    } else if (p->path == RMSNORM_PATH_LOOP) {
+        p->team = 0;
+        p->chunks = 0;
+        p->depth = 0;
+    } else {
+        return false;
+    }
+    const int64_t blocks_needed = std::max<int64_t>(1, ceil_div(M, rows_per_block));
+    if (bwd) {
+        const int64_t want = keep_grid && p->grid > 0 ? p->grid : (int64_t)kBwdProgramsPerCU * std::max(num_cus, 1);
+        p->grid = M == 0 ? 0 : std::min(want, blocks_needed);
+        p->programs = p->grid;
+        p->workspace_bytes = bwd_workspace_bytes(p->programs, M, N);
+        p->fin_threads = kFinThreads;
+        p->fin_grid = ceil_div(partial_ld(N), kFinColsPerBlock);
+    } else {
+        const int64_t want = keep_grid && p->grid > 0 ? p->grid : blocks_needed;
+        p->grid = M == 0 ? 0 : std::min(std::min(want, blocks_needed), kMaxGrid);
+        p->programs = 0;
+        p->workspace_bytes = 0;
+        p->fin_threads = 0;
+        p->fin_grid = 0;
+    }
+    return true;
+}
+
+int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cus, rmsnorm_plan *out)
+{
+    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_FUSED_ADD_BWD)
+        return RMSNORM_EINVAL;
+    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_F32)
+        return RMSNORM_EUNSUPPORTED;
+    if (M < 0 || N <= 0 || N > INT32_MAX)
+        return RMSNORM_EINVAL;
+    const bool bwd = is_bwd(op);
+    const int VV = vec_elems(dtype);
+    rmsnorm_plan p = {};
+    p.op = op;
+    p.path = RMSNORM_PATH_ROWS;
+    const bool vec = vec_ok && (N % VV == 0);
+    p.vec = vec ? VV : 1;
+    p.depth = 1;
+    const int64_t nchunks = N / p.vec;
+    bool placed = false;
+    if (vec) {
+        if (nchunks <= 32) {
+            // narrow rows: several rows per wavefront
+            p.team = std::max(8, pow2_at_least(nchunks));
+            p.threads = kRowsThreads;
+            placed = true;
+        } else if (bwd && nchunks <= 128) {
+            // one wavefront per row
+            p.team = 64;
+            p.threads = kRowsThreads;
+            placed = true;
+        } else {
+            placed = pick_block_team(bwd, true, nchunks, bwd ? 2 : 1, &p) ||
+                     pick_block_team(bwd, true, nchunks, 1, &p);
+        }
+    } else {
+        if (nchunks <= (bwd ? 128 : 512)) {
+            p.team = 64;
+            p.threads = kRowsThreads;
+            placed = true;
+        } else {
+            placed = pick_block_team(bwd, false, nchunks, 1, &p);
+        }
+    }
+    if (!placed) {
+        p.path = RMSNORM_PATH_LOOP;
+        p.team = 0;
+        p.threads = kLoopThreads;
+    }
+    if (!complete_plan(&p, M, N, dtype, num_cus, false))
+        return RMSNORM_EUNSUPPORTED;
+    *out = p;
+    return RMSNORM_OK;
+}
+
+} // namespace rmsnorm
