@@ -194,6 +194,9 @@ def n_sets_for(w, cold: bool) -> int:
 
 
 def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
+    """Per-op timings of one workload.  Always: cold buffers, direct launches
+    (fwd, bwd, bwd main) and the finalizer from a graph.  detailed: also hot
+    buffers and graph replays of fwd and bwd."""
     from rmsnorm_inputs import algorithmic_bytes
 
     res = {"workload": w.name, "M": w.M, "N": w.N, "dtype": w.dtype, "fused": w.fused, "offset": w.offset}
@@ -202,7 +205,7 @@ def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
     bytes_b = algorithmic_bytes(bop, w.M, w.N, w.elem_bytes)
     bytes_main = algorithmic_bytes(bop + "_main", w.M, w.N, w.elem_bytes)
     res["bytes"] = {"fwd": bytes_f, "bwd": bytes_b, "bwd_main": bytes_main}
-    for mode in ("cold", "hot"):
+    for mode in (("cold", "hot") if detailed else ("cold",)):
         S = Sets(w, lib, rn, torch, n_sets_for(w, mode == "cold"))
         K = len(S.sets)
         r = {"sets": K}
@@ -283,7 +286,7 @@ def counters_run(rn, torch):
 
     w = WORKLOADS["bf16_4096x4096"]
     lib = rn.load_library()
-    S = Sets(w, lib, rn, torch, 2)
+    S = Sets(w, lib, rn, torch, 4)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -360,8 +363,8 @@ def main():
     del S
     torch.cuda.empty_cache()
 
-    # ---- per-op and per-kernel timings ----
-    detail = measure_workload(w, lib, rn, torch, iters=200, warmup=30)
+    # ---- per-op and per-kernel timings (cold, direct launches) ----
+    detail = measure_workload(w, lib, rn, torch, iters=200, warmup=30, detailed=bool(args.report))
     cold = detail["cold"]
     main_us = cold["bwd_main_us"]
     roofline = {
@@ -388,13 +391,16 @@ def main():
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "fwd_us": round(cold["fwd_us"], 3), "bwd_us": round(cold["bwd_us"], 3),
         "fwd_GBs": round(cold["fwd_GBs"], 1), "bwd_GBs": round(cold["bwd_GBs"], 1),
-        "fwd_graph_us": round(cold["fwd_graph_us"], 3), "bwd_graph_us": round(cold["bwd_graph_us"], 3),
-        "hot_fwd_us": round(detail["hot"]["fwd_us"], 3), "hot_bwd_us": round(detail["hot"]["bwd_us"], 3),
-        "finalize_us": round(cold["finalize_us"], 3),
+        "fwd_pct_peak": round(cold["fwd_pct_peak"], 2), "bwd_pct_peak": round(cold["bwd_pct_peak"], 2),
+        "bwd_main_us": round(main_us, 3), "finalize_us": round(cold["finalize_us"], 3),
         "roofline": roofline, "cpu_baseline": cpu,
         "source_hash": source_hash(), "wall_s_timed_region": round(wall, 4),
     }
     if args.report:
+        line["hot_fwd_us"] = round(detail["hot"]["fwd_us"], 3)
+        line["hot_bwd_us"] = round(detail["hot"]["bwd_us"], 3)
+        line["fwd_graph_us"] = round(cold["fwd_graph_us"], 3)
+        line["bwd_graph_us"] = round(cold["bwd_graph_us"], 3)
         report = {"bench_line": line, "workloads": [detail]}
         if args.all_workloads:
             for name, ww in WORKLOADS.items():

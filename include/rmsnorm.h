@@ -182,9 +182,9 @@ int rmsnorm_query_plan(int op, int64_t M, int64_t N, int dtype, int vec_ok, int 
 
 /* Tuning and testing aid (the analogue of Liger-Kernel PR #1388's force
  * switches, "Behavior when the fast path does not apply"): later calls of `op`
- * use path, vec, team, threads and depth from *plan, and its grid when
- * grid > 0 (else the selector's grid for that layout); chunks and the
- * workspace follow.
+ * use path, vec, team and threads from *plan, its depth when depth >= 0
+ * and its grid when grid > 0 (else the selector's depth and grid for that
+ * layout); chunks and the workspace follow.
  * vec = 1 forces scalar accesses on aligned data.  NULL clears.  Process-wide
  * and not thread-safe; a call that the override does not fit returns
  * RMSNORM_EINVAL. */

@@ -135,7 +135,16 @@ def test_plans_for_workloads(M, N, dt, fused):
         assert p["path"] == rn.PATH_ROWS and p["vec"] == vec and covers(p, N)
         assert p["threads"] % 64 == 0 and 64 <= p["threads"] <= 1024
     rows_per_block = 1 if b["team"] == 0 else b["threads"] // b["team"]
-    assert b["grid"] == min(2 * CUS, -(-M // rows_per_block))
+    per_cu = 1 if b["team"] == 0 else 2
+    assert b["grid"] == min(per_cu * CUS, -(-M // rows_per_block))
+    # the forward tiles these rows exactly: no masked lanes
+    lanes = f["team"] or f["threads"]
+    assert lanes * f["chunks"] * f["vec"] == N
+    # persistent (one row ahead) only with 2..16 rows per compute unit
+    if f["team"] == 0 and 2 * CUS < M <= 16 * CUS:
+        assert (f["depth"], f["grid"]) == (1, 2 * CUS)
+    else:
+        assert f["depth"] == 0 and f["grid"] == -(-M // (1 if f["team"] == 0 else f["threads"] // f["team"]))
     assert b["programs"] == b["grid"]
     ld = -(-N // 64) * 64
     assert b["workspace_bytes"] == -(-b["programs"] * ld * 4 // 256) * 256 + -(-M * 4 // 256) * 256
@@ -155,7 +164,11 @@ def test_plan_shapes_by_width():
     p = plan(rn.OP_BWD, 1024, 7168)
     assert (p["team"], p["threads"], p["chunks"]) == (0, 896, 1)
     p = plan(rn.OP_FWD, 1024, 6144, rn.F32)
-    assert (p["team"], p["threads"], p["chunks"]) == (0, 512, 3)
+    assert (p["team"], p["threads"], p["chunks"]) == (0, 256, 6)
+    p = plan(rn.OP_FWD, 1024, 7168)
+    assert (p["team"], p["threads"], p["chunks"]) == (0, 448, 2)
+    p = plan(rn.OP_BWD, 1024, 6144, rn.F32)
+    assert (p["team"], p["threads"], p["chunks"], p["depth"]) == (0, 512, 3, 1)
 
 
 def test_unaligned_and_ragged_take_scalar_access():
@@ -183,7 +196,7 @@ def test_grid_caps_and_zero_rows():
     z = plan(rn.OP_BWD, 0, 4096)
     assert z["grid"] == 0 and z["programs"] == 0
     assert plan(rn.OP_FWD, 0, 4096)["grid"] == 0
-    assert plan(rn.OP_BWD, 10 ** 6, 4096, cus=80)["grid"] == 160
+    assert plan(rn.OP_BWD, 10 ** 6, 4096, cus=80)["grid"] == 80
 
 
 def test_selector_rejects_bad_queries():

@@ -330,13 +330,13 @@ def rmsnorm_query_plan(op: int, M: int, N: int, dtype_code: int, vec_ok: bool = 
 
 def rmsnorm_set_plan_override(op: int, plan: Optional[dict]):
     """Force (path, vec, team, threads[, depth][, grid]) for later calls of `op`;
-    None clears.  A missing depth means 1."""
+    None clears.  A missing depth or grid keeps the selector's."""
     lib = load_library()
     if plan is None:
         _check(lib.rmsnorm_set_plan_override(op, None), "rmsnorm_set_plan_override")
         return
     p = Plan()
-    p.depth = 1
+    p.depth = -1
     for k, v in plan.items():
         setattr(p, k, v)
     _check(lib.rmsnorm_set_plan_override(op, ctypes.byref(p)), "rmsnorm_set_plan_override")

@@ -95,7 +95,8 @@ int plan_for(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int cus, rmsn
         q.vec = o.plan.vec;
         q.team = o.plan.team;
         q.threads = o.plan.threads;
-        q.depth = o.plan.depth;
+        if (o.plan.depth >= 0)
+            q.depth = o.plan.depth;
         q.grid = o.plan.grid;
         if (q.vec != 1 && !vec_ok)
             return fail(RMSNORM_EINVAL, "override asks for 16-byte accesses on unaligned data");

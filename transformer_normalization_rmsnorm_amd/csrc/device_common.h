@@ -214,7 +214,8 @@ __device__ __forceinline__ float block_sum(float v, float *slot, int threads)
 
 // ---- row pipeline ---------------------------------------------------------
 
-// A team walks rows row0, row0 + stride, ... < M.  It keeps D rows in flight:
+// A team walks rows row0, row0 + stride, ... < M.  It keeps D rows in flight
+// (D = 0: none, for launches where each team owns a single row):
 // the loads of row i + D * stride are issued before row i is reduced and
 // written, so each row's memory latency overlaps the work on the D rows before
 // it.  The D + 1 row buffers form a ring whose indices are compile-time
@@ -230,6 +231,14 @@ __device__ __forceinline__ float block_sum(float v, float *slot, int threads)
 template <int D, typename Row, typename LoadF, typename ProcF>
 __device__ __forceinline__ void row_pipeline(int64_t row0, int64_t stride, int64_t M, LoadF &&load, ProcF &&proc)
 {
+    if constexpr (D == 0) { // no prefetch: each row is loaded right before it is used
+        Row b;
+        for (int64_t r = row0; r < M; r += stride) {
+            load(b, r);
+            proc(b, r);
+        }
+        return;
+    }
     const int64_t last = row0 < M ? row0 + (M - 1 - row0) / stride * stride : M - 1;
     auto clamp = [&](int64_t r) __attribute__((always_inline)) { return r < last ? r : last; };
     Row buf[D + 1];
