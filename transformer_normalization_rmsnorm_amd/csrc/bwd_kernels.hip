@@ -53,7 +53,7 @@ __global__ void __launch_bounds__(rows_max_threads(true, TEAM, K)) bwd_rows_kern
         const int c = k * tl + lane;
         Chunk<T, V> g;
         if (EXACT || c < nchunks)
-            g.load(gp + (int64_t)c * V);
+            g.load_cached(gp + (int64_t)c * V);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
             w[k][e] = (EXACT || c < nchunks) ? g.get(e) + a.offset : 0.0f;
@@ -178,9 +178,9 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
         float dot = 0.0f;
         for (int c = threadIdx.x; c < nchunks; c += nt) {
             C v, d, g;
-            v.load(vp + base + (int64_t)c * V);
-            d.load(dyp + base + (int64_t)c * V);
-            g.load(gp + (int64_t)c * V);
+            v.load_cached(vp + base + (int64_t)c * V);
+            d.load_cached(dyp + base + (int64_t)c * V);
+            g.load_cached(gp + (int64_t)c * V);
 #pragma unroll
             for (int e = 0; e < V; ++e)
                 dot = fmaf(d.get(e) * (g.get(e) + a.offset), v.get(e), dot);
@@ -191,9 +191,9 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
         const float kc = rs * rs * rs * dot * inv_n;
         for (int c = threadIdx.x; c < nchunks; c += nt) {
             C v, d, g;
-            v.load(vp + base + (int64_t)c * V);
-            d.load(dyp + base + (int64_t)c * V);
-            g.load(gp + (int64_t)c * V);
+            v.load_cached(vp + base + (int64_t)c * V);
+            d.load_cached(dyp + base + (int64_t)c * V);
+            g.load_cached(gp + (int64_t)c * V);
             float o[V], pa[V];
             if (first) {
 #pragma unroll
@@ -204,7 +204,7 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
             }
             C dh;
             if constexpr (FUSED)
-                dh.load(dhp + base + (int64_t)c * V);
+                dh.load_cached(dhp + base + (int64_t)c * V);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const float xv = v.get(e);

@@ -54,7 +54,7 @@ __global__ void __launch_bounds__(rows_max_threads(false, TEAM, K)) fwd_rows_ker
     for (int k = 0; k < K; ++k) {
         const int c = k * tl + lane;
         if (EXACT || c < nchunks)
-            g[k].load(gamma + (int64_t)c * V);
+            g[k].load_cached(gamma + (int64_t)c * V);
     }
 
     auto load = [&](Row &b, int64_t row) __attribute__((always_inline)) {
@@ -144,10 +144,10 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
         float ss = 0.0f;
         for (int c = threadIdx.x; c < nchunks; c += nt) {
             C v;
-            v.load(x + base + (int64_t)c * V);
+            v.load_cached(x + base + (int64_t)c * V);
             if constexpr (FUSED) {
                 C rc;
-                rc.load(r + base + (int64_t)c * V);
+                rc.load_cached(r + base + (int64_t)c * V);
                 float f[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e)
@@ -170,10 +170,10 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
             continue;
         for (int c = threadIdx.x; c < nchunks; c += nt) {
             C v;
-            v.load(x + base + (int64_t)c * V);
+            v.load_cached(x + base + (int64_t)c * V);
             if constexpr (FUSED) {
                 C rc;
-                rc.load(r + base + (int64_t)c * V);
+                rc.load_cached(r + base + (int64_t)c * V);
                 float f[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e)
@@ -181,7 +181,7 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
                 v.set(f);
             }
             C g;
-            g.load(gamma + (int64_t)c * V);
+            g.load_cached(gamma + (int64_t)c * V);
             float f[V];
 #pragma unroll
             for (int e = 0; e < V; ++e)

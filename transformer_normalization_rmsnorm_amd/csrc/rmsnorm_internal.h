@@ -58,6 +58,7 @@ constexpr int kFinColsPerBlock = 32;
 #define RMSNORM_FWD_ROWS_CONFIGS(X)                                                      \
     X(1, 8, 1, 0) X(1, 16, 1, 0) X(1, 32, 1, 0) X(1, 64, 1, 0) X(1, 64, 2, 0)            \
     X(1, 64, 4, 0) X(1, 0, 1, 0) X(1, 0, 2, 0) X(1, 0, 3, 0) X(1, 0, 4, 0) X(1, 0, 6, 0) \
+    X(1, 0, 8, 0)                                                                        \
     X(1, 64, 8, 0) X(0, 64, 1, 0) X(0, 64, 2, 0) X(0, 64, 4, 0) X(0, 64, 8, 0)           \
     X(0, 0, 1, 0) X(0, 0, 2, 0) X(0, 0, 4, 0) X(0, 0, 8, 0) X(0, 0, 16, 0)               \
     X(1, 8, 1, 1) X(1, 16, 1, 1) X(1, 32, 1, 1) X(1, 16, 1, 2) X(1, 32, 1, 2)            \
