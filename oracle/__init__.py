@@ -96,10 +96,10 @@ def set_num_threads(n: int, lib=None):
 
 
 def fwd(v, gamma, dtype: str, eps: float, offset: float, *, want_y: bool = True, lib=None):
-    """Forward on rows of v [M, N]; returns (y64 or None, rstd64)."""
+    """Forward on rows of v [M, N]; returns (y64 or None, rstd64).  gamma None: non-affine."""
     lib = lib or load()
     v = _storage(v, dtype)
-    gamma = _storage(gamma, dtype)
+    gamma = None if gamma is None else _storage(gamma, dtype)
     M, N = v.shape
     y = np.empty((M, N), np.float64) if want_y else None
     rstd = np.empty(M, np.float64)
@@ -113,7 +113,7 @@ def fused_add_fwd(x, r, gamma, dtype: str, eps: float, offset: float, *, want_y:
     lib = lib or load()
     x = _storage(x, dtype)
     r = _storage(r, dtype)
-    gamma = _storage(gamma, dtype)
+    gamma = None if gamma is None else _storage(gamma, dtype)
     M, N = x.shape
     h = np.empty((M, N), NP_STORAGE[dtype])
     y = np.empty((M, N), np.float64) if want_y else None
@@ -132,7 +132,8 @@ def bwd(dy, v, gamma, dtype: str, eps: float, offset: float, *, dh=None, want_dx
     lib = lib or load()
     dy = _storage(dy, dtype)
     v = _storage(v, dtype)
-    gamma = _storage(gamma, dtype)
+    gamma = None if gamma is None else _storage(gamma, dtype)
+    want_dgamma = want_dgamma and gamma is not None
     if dh is not None:
         dh = _storage(dh, dtype)
     M, N = v.shape

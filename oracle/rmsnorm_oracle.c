@@ -33,6 +33,9 @@
  *     output, dh, to dx; dx is the residual gradient (FlyDSL PR #855,
  *     "Hybrid atomic / two-stage backward" and "Fused-add RMSNorm backward").
  *
+ * Non-affine RMSNorm (no gamma; Liger-Kernel PR #1388 "Validation" tests the
+ * affine and non-affine ops): gamma == NULL means w_j = 1, and offset must be 0.
+ *
  * Rounding to a storage type is round-to-nearest, ties to even (FlyDSL PR #855,
  * "512-thread vec8 fast path": software RNE / hardware conversion).
  *
@@ -143,6 +146,12 @@ int oracle_round(int dt, const double *src, int64_t n, void *dst)
     return ORACLE_OK;
 }
 
+/* w_j = gamma_j + offset, or 1 without gamma */
+static double scale_w(int dt, const void *gamma, int64_t j, double off)
+{
+    return gamma ? load_elem(dt, gamma, j) + off : 1.0;
+}
+
 /* rstd_i = 1 / sqrt((1/N) sum_j v_ij^2 + eps) */
 static double row_rstd(int dt, const void *v, int64_t row, int64_t N, double eps)
 {
@@ -159,7 +168,7 @@ static double row_rstd(int dt, const void *v, int64_t row, int64_t N, double eps
 int oracle_fwd(int dt, const void *v, const void *gamma, int64_t M, int64_t N,
                float eps, float offset, double *y64, double *rstd64)
 {
-    if (!dtype_ok(dt) || !v || !gamma || M < 0 || N <= 0)
+    if (!dtype_ok(dt) || !v || M < 0 || N <= 0 || (!gamma && offset != 0.0f))
         return ORACLE_EINVAL;
     const double e = (double)eps, off = (double)offset;
 #pragma omp parallel for schedule(static)
@@ -169,7 +178,7 @@ int oracle_fwd(int dt, const void *v, const void *gamma, int64_t M, int64_t N,
             rstd64[i] = rstd;
         if (y64) {
             for (int64_t j = 0; j < N; ++j) {
-                double w = load_elem(dt, gamma, j) + off;
+                double w = scale_w(dt, gamma, j, off);
                 y64[i * N + j] = load_elem(dt, v, i * N + j) * rstd * w;
             }
         }
@@ -183,7 +192,7 @@ int oracle_fused_add_fwd(int dt, const void *x, const void *r, const void *gamma
                          int64_t M, int64_t N, float eps, float offset,
                          void *h_out, double *y64, double *rstd64)
 {
-    if (!dtype_ok(dt) || !x || !r || !gamma || !h_out || M < 0 || N <= 0)
+    if (!dtype_ok(dt) || !x || !r || !h_out || M < 0 || N <= 0 || (!gamma && offset != 0.0f))
         return ORACLE_EINVAL;
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < M; ++i)
@@ -194,7 +203,8 @@ int oracle_fused_add_fwd(int dt, const void *x, const void *r, const void *gamma
 }
 
 /* Backward.  v is the forward's input (h for the fused-add variant); dh, when
- * not NULL, is added to dx.  Outputs (each may be NULL):
+ * not NULL, is added to dx; gamma NULL is the non-affine op (no dgamma).
+ * Outputs (each may be NULL):
  *   dx64 [M, N]; dgamma64 [N];
  *   c64 [M]     = (1/N) sum_j g_ij xhat_ij;
  *   sabs64 [M]  = (1/N) sum_j |g_ij xhat_ij|  (the size of the terms that
@@ -203,7 +213,7 @@ int oracle_bwd(int dt, const void *dy, const void *v, const void *gamma, const v
                int64_t M, int64_t N, float eps, float offset,
                double *dx64, double *dgamma64, double *c64, double *sabs64)
 {
-    if (!dtype_ok(dt) || !dy || !v || !gamma || M < 0 || N <= 0)
+    if (!dtype_ok(dt) || !dy || !v || M < 0 || N <= 0 || (!gamma && (offset != 0.0f || dgamma64)))
         return ORACLE_EINVAL;
     const double e = (double)eps, off = (double)offset;
 
@@ -217,7 +227,7 @@ int oracle_bwd(int dt, const void *dy, const void *v, const void *gamma, const v
         rstd[i] = row_rstd(dt, v, i, N, e);
         double dot = 0.0, dabs = 0.0;
         for (int64_t j = 0; j < N; ++j) {
-            double w = load_elem(dt, gamma, j) + off;
+            double w = scale_w(dt, gamma, j, off);
             double g = load_elem(dt, dy, i * N + j) * w;
             double xhat = load_elem(dt, v, i * N + j) * rstd[i];
             dot += g * xhat;
@@ -230,7 +240,7 @@ int oracle_bwd(int dt, const void *dy, const void *v, const void *gamma, const v
             sabs64[i] = dabs / (double)N;
         if (dx64) {
             for (int64_t j = 0; j < N; ++j) {
-                double w = load_elem(dt, gamma, j) + off;
+                double w = scale_w(dt, gamma, j, off);
                 double g = load_elem(dt, dy, i * N + j) * w;
                 double xhat = load_elem(dt, v, i * N + j) * rstd[i];
                 double d = rstd[i] * (g - xhat * c);

@@ -16,6 +16,7 @@ mismatch.  What pins what:
   golden               hand-worked fixtures (tests/golden/hand_worked.txt)
   storage_widening     bf16/f32 storage widened exactly (same answers as f64 storage)
   rounding             nearest-even rounding vs torch casts and brute force
+  non_affine           no gamma: finite differences, RMS invariant, gamma = 1 equivalence
 """
 
 from __future__ import annotations
@@ -401,7 +402,42 @@ def rounding(lib):
     assert np.isnan(bf16_bits_to_f32(oracle.round_to(np.array([np.nan]), "bf16", lib=lib)))[0]
 
 
+def non_affine(lib):
+    """Without gamma: the finite-difference gradient of sum dy * y, the RMS
+    invariant with w = 1, and (gamma = 1, offset = 0) giving the same values."""
+    rng = np.random.default_rng(21)
+    for M, N, eps in ((2, 1, 1e-6), (3, 5, 0.5), (2, 16, 1e-6)):
+        v = _rand(rng, (M, N))
+        dy = _rand(rng, (M, N))
+        y, rstd = oracle.fwd(v, None, "f64", eps, 0.0, lib=lib)
+        ms = np.mean(v * v, axis=1)
+        np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), np.sqrt(ms / (ms + _f32(eps))), rtol=1e-13)
+        out = oracle.bwd(dy, v, None, "f64", eps, 0.0, lib=lib)
+        assert out["dgamma64"] is None
+        s = _cancel_scale(v, np.ones(N), dy, eps, 0.0, out)
+        for i in range(M):
+            for j in range(N):
+                h = 1e-6 * max(1.0, abs(v[i, j]))
+                vp, vm = v.copy(), v.copy()
+                vp[i, j] += h
+                vm[i, j] -= h
+                lp = float(np.sum(dy * oracle.fwd(vp, None, "f64", eps, 0.0, lib=lib)[0]))
+                lm = float(np.sum(dy * oracle.fwd(vm, None, "f64", eps, 0.0, lib=lib)[0]))
+                fd = (lp - lm) / (vp[i, j] - vm[i, j])
+                ref = out["dx64"][i, j]
+                assert abs(fd - ref) <= 1e-7 * max(abs(ref), s[i, j]), (M, N, i, j, fd, ref)
+        y1, _ = oracle.fwd(v, np.ones(N), "f64", eps, 0.0, lib=lib)
+        np.testing.assert_array_equal(y, y1)
+        np.testing.assert_array_equal(out["dx64"], oracle.bwd(dy, v, np.ones(N), "f64", eps, 0.0, lib=lib)["dx64"])
+    try:
+        oracle.fwd(np.ones((1, 2)), None, "f64", 1e-6, 1.0, lib=lib)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("offset without gamma must be refused")
+
+
 ALL_PINS = [
     finite_differences, rms_invariant, orthogonality, closed_form_n1, constant_row, scale_invariance,
-    offset_equivalence, fused_reductions, torch_fp64, golden, storage_widening, rounding,
+    offset_equivalence, fused_reductions, torch_fp64, golden, storage_widening, rounding, non_affine,
 ]

@@ -33,6 +33,7 @@ MUTATIONS = [
     ("bf16_widen_shift", "uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;",
      "uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 15;", False),
     ("subnormal_spacing", "if (q < -126)\n        q = -126;", "if (q < -149)\n        q = -149;", False),
+    ("non_affine_scale", "return gamma ? load_elem(dt, gamma, j) + off : 1.0;", "return gamma ? load_elem(dt, gamma, j) + off : 1.0 + off + 0.5;", False),
 ]
 
 # fast pins first so a mutant usually fails within a second
@@ -40,7 +41,7 @@ PIN_ORDER = [
     oracle_pins.golden, oracle_pins.closed_form_n1, oracle_pins.constant_row, oracle_pins.rms_invariant,
     oracle_pins.orthogonality, oracle_pins.offset_equivalence, oracle_pins.scale_invariance,
     oracle_pins.fused_reductions, oracle_pins.storage_widening, oracle_pins.rounding, oracle_pins.torch_fp64,
-    oracle_pins.finite_differences,
+    oracle_pins.non_affine, oracle_pins.finite_differences,
 ]
 
 
