@@ -11,7 +11,9 @@ Default workload: bf16 rows of M=4096 x N=4096, eps 1e-6, offset 0.
 
 Prints ONE JSON line (driver contract) with, among others:
   value       achieved GB/s of the whole step (algorithmic bytes / time)
-  roofline    the dominant kernel (backward main) against the 8 TB/s HBM peak
+  roofline    the dominant kernel (backward main) against the 8 TB/s HBM peak,
+              and against the practical peak a plain three-stream kernel reaches
+  practical_ceilings  nontemporal copy / three-stream probe rates at this size
   cpu_baseline the fp64 reference timed on the host cores on the same workload
 
 Other modes:
@@ -41,15 +43,24 @@ METRIC = "RMSNorm fwd+bwd µs/call and achieved HBM GB/s (% of peak), bf16 4096x
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "bwd_main_bf16_4096x4096_hbm_traffic.txt")
 
 
-def source_hash() -> str:
+def source_hash(plan=None) -> str:
+    """Identity of the backward main kernel as measured: the sources that define
+    it and (when given) its launch plan.  Counters taken on a different identity
+    are stale."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "transformer_normalization_rmsnorm_amd", "csrc", "*")))
-    files.append(os.path.join(ROOT, "include", "rmsnorm.h"))
-    for f in files:
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode())
+    csrc = os.path.join(ROOT, "transformer_normalization_rmsnorm_amd", "csrc")
+    for name in ("device_common.h", "bwd_kernels.hip", "rmsnorm_internal.h"):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode())
             h.update(fh.read())
+    if plan is not None:
+        h.update(json.dumps(plan, sort_keys=True).encode())
     return h.hexdigest()[:16]
+
+
+def bwd_plan(rn, w):
+    op = rn.OP_FUSED_ADD_BWD if w.fused else rn.OP_BWD
+    return rn.rmsnorm_query_plan(op, w.M, w.N, rn.BF16 if w.dtype == "bf16" else rn.F32)
 
 
 class Sets:
@@ -229,6 +240,43 @@ def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
     return res
 
 
+def practical_ceilings(torch, tensor_bytes: int, iters: int = 50):
+    """Best measured GB/s of a plain nontemporal copy (1 read + 1 write stream)
+    and a three-stream kernel (2 reads + 1 write) over tensors of the
+    workload's size, on rotating cold buffers: what a streaming kernel with
+    the same traffic reaches on this GPU."""
+    from transformer_normalization_rmsnorm_amd import _build
+
+    lib = ctypes.CDLL(_build.PROBE_LIBRARY)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.stream_probe_copy.argtypes = [vp, vp, i64, i32, i32, vp]
+    lib.stream_probe_three.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+    n16 = tensor_bytes // 16
+    K = max(2, math.ceil((1 << 30) / (3 * tensor_bytes)) + 1)
+    bufs = [[torch.empty(n16 * 16, dtype=torch.uint8, device="cuda") for _ in range(3)] for _ in range(K)]
+    for b in bufs:
+        for t in b:
+            t.fill_(1)
+    best = {"copy": 0.0, "three": 0.0}
+    full = max(1, n16 // 256)
+    for kind, moved in (("copy", 2 * n16 * 16), ("three", 3 * n16 * 16)):
+        for unroll in (1, 2, 4):
+            for blocks in sorted({1024, 2048, 4096, max(1, full // unroll)}):
+                def fn(i, st, kind=kind, unroll=unroll, blocks=blocks):
+                    a, b, c = bufs[i % K]
+                    if kind == "copy":
+                        rc = lib.stream_probe_copy(a.data_ptr(), c.data_ptr(), n16, blocks, unroll, st)
+                    else:
+                        rc = lib.stream_probe_three(a.data_ptr(), b.data_ptr(), c.data_ptr(), n16, blocks, unroll, st)
+                    if rc != 0:
+                        raise RuntimeError(f"stream probe failed: {rc}")
+                us = time_direct(torch, fn, iters, 5, repeats=3)
+                best[kind] = max(best[kind], moved / (us * 1e3))
+    del bufs
+    torch.cuda.empty_cache()
+    return {"tensor_bytes": n16 * 16, "copy_GBs": round(best["copy"], 1), "three_stream_GBs": round(best["three"], 1)}
+
+
 def cpu_baseline(w, seconds: float):
     """The fp64 reference, as it stands, on the host cores (bounded run)."""
     import numpy as np
@@ -260,9 +308,9 @@ def cpu_baseline(w, seconds: float):
     }
 
 
-def counters_traffic():
+def counters_traffic(ident: str):
     """HBM bytes per backward-main dispatch from committed rocprofv3 counters,
-    or None when missing or taken on different kernel sources."""
+    or None when missing or taken on a different kernel (sources or plan)."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     vals = {}
@@ -271,7 +319,7 @@ def counters_traffic():
             if ":" in line and not line.startswith("#"):
                 k, _, v = line.partition(":")
                 vals[k.strip()] = v.strip()
-    if vals.get("source_hash") != source_hash():
+    if vals.get("source_hash") != ident:
         return None
     try:
         return float(vals["traffic_bytes_per_dispatch"])
@@ -370,10 +418,14 @@ def main():
     roofline = {
         "kernel": f"backward main ({'fused-add ' if w.fused else ''}rows, dx + dgamma partials)",
         "bound": "hbm", "achieved": detail["bytes"]["bwd_main"] / (main_us * 1e3), "peak": HBM_PEAK_GBS,
-        "unit": "GB/s", "frac": None, "traffic": counters_traffic(),
+        "unit": "GB/s", "frac": None, "traffic": counters_traffic(source_hash(bwd_plan(rn, w))),
         "bytes_per_launch": detail["bytes"]["bwd_main"], "avg_launch_us": main_us,
     }
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
+    ceil = practical_ceilings(torch, w.M * w.N * w.elem_bytes)
+    # the backward main kernel streams two tensors in and one out
+    roofline["practical_peak"] = ceil["three_stream_GBs"]
+    roofline["frac_of_practical"] = roofline["achieved"] / ceil["three_stream_GBs"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -393,8 +445,8 @@ def main():
         "fwd_GBs": round(cold["fwd_GBs"], 1), "bwd_GBs": round(cold["bwd_GBs"], 1),
         "fwd_pct_peak": round(cold["fwd_pct_peak"], 2), "bwd_pct_peak": round(cold["bwd_pct_peak"], 2),
         "bwd_main_us": round(main_us, 3), "finalize_us": round(cold["finalize_us"], 3),
-        "roofline": roofline, "cpu_baseline": cpu,
-        "source_hash": source_hash(), "wall_s_timed_region": round(wall, 4),
+        "roofline": roofline, "cpu_baseline": cpu, "practical_ceilings": ceil,
+        "source_hash": source_hash(bwd_plan(rn, w)), "wall_s_timed_region": round(wall, 4),
     }
     if args.report:
         line["hot_fwd_us"] = round(detail["hot"]["fwd_us"], 3)
@@ -402,11 +454,14 @@ def main():
         line["fwd_graph_us"] = round(cold["fwd_graph_us"], 3)
         line["bwd_graph_us"] = round(cold["bwd_graph_us"], 3)
         report = {"bench_line": line, "workloads": [detail]}
+        detail["ceilings"] = ceil
         if args.all_workloads:
             for name, ww in WORKLOADS.items():
                 if name != w.name:
                     print(f"measuring {name}", file=sys.stderr, flush=True)
-                    report["workloads"].append(measure_workload(ww, lib, rn, torch, iters=100, warmup=20))
+                    dd = measure_workload(ww, lib, rn, torch, iters=100, warmup=20)
+                    dd["ceilings"] = practical_ceilings(torch, ww.M * ww.N * ww.elem_bytes, iters=20)
+                    report["workloads"].append(dd)
         os.makedirs(os.path.dirname(os.path.abspath(args.report)), exist_ok=True)
         with open(args.report, "w") as f:
             json.dump(report, f, indent=1)

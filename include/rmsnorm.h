@@ -42,6 +42,10 @@
  *     alias dh (fused backward); any other overlap is undefined.
  *   - M = 0 is valid: the forward does nothing; the backward writes
  *     dgamma = 0.  N must be in [1, 2^31 - 1].
+ *   - gamma == NULL selects the non-affine op (no elementwise scale, w_j = 1;
+ *     Liger-Kernel PR #1388 "Validation" covers affine and non-affine).  offset
+ *     must then be 0 and dgamma NULL; the backward writes no partials, so it
+ *     needs a workspace only to recompute rstd.
  *   - Results are deterministic: for a given device, shape, dtype and pointer
  *     alignment every output, dgamma included, is bit-identical run to run.
  */
@@ -75,7 +79,7 @@ typedef enum rmsnorm_status {
 /* Forward (Liger-Kernel PR #1388, Summary and "Results" llama mode; FlyDSL
  * PR #855 "Implementation": two-pass row math with a block reduction).
  *   x      [M, N] T   input rows
- *   gamma  [N] T      scale; the kernel uses gamma_j + offset
+ *   gamma  [N] T      scale; the kernel uses gamma_j + offset (NULL: non-affine)
  *   y      [M, N] T   output, may be NULL to compute rstd only
  *   rstd   [M] f32    saved 1/rms per row for the backward, may be NULL
  *   eps >= 0 and offset: float32 runtime scalars. */
@@ -103,9 +107,9 @@ int rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *bytes);
 /* Backward (FlyDSL PR #855 "Hybrid atomic / two-stage backward"): a bounded
  * persistent grid writes dx and float32 dgamma partials into `workspace`, then
  * a finalizer sums the partials in a fixed order and writes dgamma in T.
- *   dy, x  [M, N] T;  gamma [N] T;
+ *   dy, x  [M, N] T;  gamma [N] T (NULL: non-affine, then dgamma NULL);
  *   rstd   [M] f32 from the forward, or NULL to recompute it from x with eps;
- *   dx     [M, N] T;  dgamma [N] T;
+ *   dx     [M, N] T;  dgamma [N] T (NULL exactly when gamma is NULL);
  *   workspace: device memory of at least rmsnorm_bwd_workspace_bytes(), 16-byte
  *   aligned, contents ignored on entry and undefined on return. */
 int rmsnorm_bwd(const void *dy, const void *x, const void *gamma, const float *rstd,

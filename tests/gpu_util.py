@@ -41,7 +41,8 @@ def check_values(what, got, ref64, dtype, scale=None):
 
 
 def check_forward(inp, dtype, eps, offset, y, rstd, h=None, rows=None):
-    """Compare GPU forward outputs (numpy, possibly a row sample) with the reference."""
+    """Compare GPU forward outputs (numpy, possibly a row sample) with the reference.
+    inp["gamma"] None: the non-affine op."""
     x = inp["x"] if rows is None else inp["x"][rows]
     g = inp["gamma"]
     if h is not None:
@@ -79,10 +80,13 @@ def check_backward(inp, dtype, eps, offset, dx, dgamma, *, v_full, dh_full=None,
     dh = None if dh_full is None else sel(dh_full)
     out = oracle.bwd(dy, v, g, dtype, eps, offset, dh=dh, want_dgamma=rows is None)
     rstd64 = 1.0 / np.sqrt(np.mean(widen(v, dtype) ** 2, axis=1) + float(np.float32(eps)))
-    s = cancel_scale(widen(v, dtype), widen(g, dtype), widen(dy, dtype), rstd64, out["c64"], out["sabs64"], offset,
+    g_wide = np.ones(v.shape[1]) if g is None else widen(g, dtype)
+    s = cancel_scale(widen(v, dtype), g_wide, widen(dy, dtype), rstd64, out["c64"], out["sabs64"], offset,
                      None if dh is None else widen(dh, dtype))
     reports = [check_values("dx", dx, out["dx64"], dtype, scale=s)]
-    if dgamma is not None:
+    if g is None:
+        assert dgamma is None
+    elif dgamma is not None:
         dg64 = out["dgamma64"] if rows is None else oracle.bwd(inp["dy"], v_full, g, dtype, eps, offset,
                                                                want_dx=False)["dgamma64"]
         err = dgamma_error(dgamma, dg64, dtype)
@@ -92,7 +96,7 @@ def check_backward(inp, dtype, eps, offset, dx, dgamma, *, v_full, dh_full=None,
 
 def gpu_forward(inp, dtype, eps, offset, fused):
     x = to_dev(inp["x"], dtype)
-    g = to_dev(inp["gamma"], dtype)
+    g = None if inp["gamma"] is None else to_dev(inp["gamma"], dtype)
     if fused:
         r = to_dev(inp["residual"], dtype)
         y, h, rstd = rn.rmsnorm_fused_add_fwd(x, r, g, eps, offset)
@@ -104,9 +108,14 @@ def gpu_forward(inp, dtype, eps, offset, fused):
 def gpu_backward(inp, dtype, eps, offset, fwd_out, fused, rstd="gpu"):
     dy = to_dev(inp["dy"], dtype)
     rs = fwd_out["rstd"] if rstd == "gpu" else (None if rstd is None else rstd)
+    dx_out, dg_out = None, None
     if fused:
         dh = to_dev(inp["dh"], dtype)
         dx, dg = rn.rmsnorm_fused_add_bwd(dy, dh, fwd_out["h"], fwd_out["gamma"], rs, eps, offset)
     else:
         dx, dg = rn.rmsnorm_bwd(dy, fwd_out["x"], fwd_out["gamma"], rs, eps, offset)
     return dx, dg
+
+
+def from_dev_opt(t):
+    return None if t is None else from_dev(t)

@@ -73,6 +73,9 @@ def test_fwd_argument_errors(lib):
     assert b"aliases" in lib.rmsnorm_last_error()
     # M = 0 is a successful no-op that needs no pointers at all
     assert fwd(lib, x=None, g=None, y=None, rstd=None, M=0) == OK
+    # without gamma (non-affine op) there is no offset
+    assert fwd(lib, g=None, off=1.0) == EINVAL
+    assert b"offset needs gamma" in lib.rmsnorm_last_error()
 
 
 def test_fused_fwd_argument_errors(lib):
@@ -99,6 +102,8 @@ def test_bwd_argument_errors(lib):
     assert call(ws=FAKE + 32768 + 8) == EINVAL  # workspace must be 16-byte aligned
     assert call(dx=args["dy"]) == EINVAL  # dx may alias only dh
     assert call(dg=FAKE + 1) == EINVAL
+    assert call(g=None) == EINVAL  # dgamma given without gamma
+    assert b"dgamma given without gamma" in lib.rmsnorm_last_error()
     fin = lib.rmsnorm_dgamma_finalize
     assert fin(None, 3, 8, FAKE, rn.BF16, None) == EINVAL
     assert fin(FAKE + 8, 3, 8, FAKE, rn.BF16, None) == EINVAL
@@ -140,11 +145,8 @@ def test_plans_for_workloads(M, N, dt, fused):
     # the forward tiles these rows exactly: no masked lanes
     lanes = f["team"] or f["threads"]
     assert lanes * f["chunks"] * f["vec"] == N
-    # persistent (one row ahead) only with 2..16 rows per compute unit
-    if f["team"] == 0 and 2 * CUS < M <= 16 * CUS:
-        assert (f["depth"], f["grid"]) == (1, 2 * CUS)
-    else:
-        assert f["depth"] == 0 and f["grid"] == -(-M // (1 if f["team"] == 0 else f["threads"] // f["team"]))
+    # one row per team, nothing prefetched
+    assert f["depth"] == 0 and f["grid"] == -(-M // (1 if f["team"] == 0 else f["threads"] // f["team"]))
     assert b["programs"] == b["grid"]
     ld = -(-N // 64) * 64
     assert b["workspace_bytes"] == -(-b["programs"] * ld * 4 // 256) * 256 + -(-M * 4 // 256) * 256
@@ -164,9 +166,13 @@ def test_plan_shapes_by_width():
     p = plan(rn.OP_BWD, 1024, 7168)
     assert (p["team"], p["threads"], p["chunks"]) == (0, 896, 1)
     p = plan(rn.OP_FWD, 1024, 6144, rn.F32)
-    assert (p["team"], p["threads"], p["chunks"]) == (0, 256, 6)
+    assert (p["team"], p["threads"], p["chunks"]) == (0, 192, 8)
     p = plan(rn.OP_FWD, 1024, 7168)
     assert (p["team"], p["threads"], p["chunks"]) == (0, 448, 2)
+    p = plan(rn.OP_FWD, 1024, 8192)
+    assert (p["team"], p["threads"], p["chunks"]) == (0, 128, 8)
+    p = plan(rn.OP_FWD, 4096, 4096)   # 16 rows per compute unit
+    assert (p["team"], p["threads"], p["chunks"]) == (0, 256, 2)
     p = plan(rn.OP_BWD, 1024, 6144, rn.F32)
     assert (p["team"], p["threads"], p["chunks"], p["depth"]) == (0, 512, 3, 1)
 

@@ -11,8 +11,8 @@ import torch
 
 import oracle
 import transformer_normalization_rmsnorm_amd as rn
-from gpu_util import (check_backward, check_forward, from_dev, gpu_backward,
-                      gpu_forward, reference_h, to_dev)
+from gpu_util import (check_backward, check_forward, from_dev, from_dev_opt,
+                      gpu_backward, gpu_forward, reference_h, to_dev)
 from rmsnorm_inputs import EPS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -141,6 +141,27 @@ def test_forced_layouts(kind, M, N, dt, fields, fused):
         for k, v in fields.items():
             assert p[k] == v, (k, p)
         run_case(M, N, dt, fused, dt == "f32")
+
+
+# Non-affine op (no gamma): rows and looped paths, plain and fused, with the
+# GPU's rstd and with rstd recomputed.
+NON_AFFINE = [(300, 4096, "bf16", False), (200, 7168, "bf16", True), (130, 6144, "f32", False),
+              (1000, 128, "bf16", True), (17, 4097, "bf16", False), (5, 20000, "f32", True)]
+
+
+@pytest.mark.parametrize("M,N,dt,fused", NON_AFFINE, ids=[f"{d}_{m}x{n}{'_fused' if f else ''}" for m, n, d, f in NON_AFFINE])
+def test_non_affine(M, N, dt, fused):
+    inp = make_inputs(M, N, dt, fused=fused)
+    inp["gamma"] = None
+    out = gpu_forward(inp, dt, EPS, 0.0, fused)
+    torch.cuda.synchronize()
+    check_forward(inp, dt, EPS, 0.0, from_dev(out["y"]), from_dev(out["rstd"]), from_dev(out["h"]) if fused else None)
+    v_ref = reference_h(inp, dt) if fused else inp["x"]
+    for rstd in ("gpu", None):
+        dx, dg = gpu_backward(inp, dt, EPS, 0.0, out, fused, rstd=rstd)
+        torch.cuda.synchronize()
+        assert dg is None
+        check_backward(inp, dt, EPS, 0.0, from_dev(dx), None, v_full=v_ref, dh_full=inp["dh"] if fused else None)
 
 
 def _offset_view(a: torch.Tensor, elems: int) -> torch.Tensor:

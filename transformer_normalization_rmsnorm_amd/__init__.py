@@ -166,13 +166,15 @@ def _stream(device):
 
 
 def rmsnorm_fwd(x, gamma, eps: float = 1e-6, offset: float = 0.0, *, y=None, rstd=None, save_rstd: bool = True):
-    """y = x * rstd * (gamma + offset) over the last dimension; returns (y, rstd)."""
+    """y = x * rstd * (gamma + offset) over the last dimension; returns (y, rstd).
+    gamma None: the non-affine op (offset must be 0)."""
     torch = _torch()
     lib = load_library()
     _require(x, "x")
     M, N = _rows(x)
     dev = x.device
-    _require(gamma, "gamma", (N,), x.dtype, dev)
+    if gamma is not None:
+        _require(gamma, "gamma", (N,), x.dtype, dev)
     if y is None:
         y = torch.empty_like(x)
     _require(y, "y", x.shape, x.dtype, dev)
@@ -197,7 +199,8 @@ def rmsnorm_fused_add_fwd(x, residual, gamma, eps: float = 1e-6, offset: float =
     M, N = _rows(x)
     dev = x.device
     _require(residual, "residual", x.shape, x.dtype, dev)
-    _require(gamma, "gamma", (N,), x.dtype, dev)
+    if gamma is not None:
+        _require(gamma, "gamma", (N,), x.dtype, dev)
     if y is None:
         y = torch.empty_like(x)
     if h_out is None:
@@ -244,15 +247,17 @@ def _bwd_common(name, dy, dh, v, gamma, rstd, eps, offset, dx, dgamma, workspace
     _require(dy, "dy", v.shape, v.dtype, dev)
     if dh is not None:
         _require(dh, "dh", v.shape, v.dtype, dev)
-    _require(gamma, "gamma", (N,), v.dtype, dev)
+    if gamma is not None:
+        _require(gamma, "gamma", (N,), v.dtype, dev)
     if rstd is not None:
         _require(rstd, "rstd", v.shape[:-1], torch.float32, dev)
     if dx is None:
         dx = torch.empty_like(v)
-    if dgamma is None:
-        dgamma = torch.empty_like(gamma)
+    if gamma is not None:
+        if dgamma is None:
+            dgamma = torch.empty_like(gamma)
+        _require(dgamma, "dgamma", (N,), v.dtype, dev)
     _require(dx, "dx", v.shape, v.dtype, dev)
-    _require(dgamma, "dgamma", (N,), v.dtype, dev)
     with _on_device(dev):
         if workspace is None:
             op = OP_BWD if name == "rmsnorm_bwd" else OP_FUSED_ADD_BWD
@@ -273,7 +278,8 @@ def _bwd_common(name, dy, dh, v, gamma, rstd, eps, offset, dx, dgamma, workspace
 
 def rmsnorm_bwd(dy, x, gamma, rstd, eps: float = 1e-6, offset: float = 0.0, *, dx=None, dgamma=None,
                 workspace=None):
-    """Gradients of rmsnorm_fwd; rstd=None recomputes it.  Returns (dx, dgamma)."""
+    """Gradients of rmsnorm_fwd; rstd=None recomputes it.  Returns (dx, dgamma);
+    dgamma is None for the non-affine op (gamma None)."""
     return _bwd_common("rmsnorm_bwd", dy, None, x, gamma, rstd, eps, offset, dx, dgamma, workspace)
 
 

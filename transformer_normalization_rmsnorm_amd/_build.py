@@ -20,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "librmsnorm_amd.so")
 SOURCES = ["api.cpp", "selector.cpp", "fwd_kernels.hip", "bwd_kernels.hip"]
+# measurement-only library (practical bandwidth ceilings for the benchmark)
+PROBE_SOURCE = "stream_probe.hip"
+PROBE_LIBRARY = os.path.join(PKG, "libstream_probe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -58,6 +61,12 @@ def build(verbose: bool = False, resource_report: bool = True, jobs: int = 4) ->
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
     os.replace(tmp, LIBRARY)
+    tmp = PROBE_LIBRARY + ".tmp"
+    cmd = [HIPCC, "-x", "hip", "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", tmp] + CFLAGS
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SOURCE}:\n{r.stderr[-4000:]}")
+    os.replace(tmp, PROBE_LIBRARY)
     if verbose:
         print(f"built {LIBRARY}")
         spills = [ln for ln in usage if re.search(r"(ScratchSize|Spill)\S*: [1-9]", ln)]

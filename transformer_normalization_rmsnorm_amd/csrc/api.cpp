@@ -122,15 +122,17 @@ int do_fwd(const void *x, const void *r, const void *gamma, void *y, void *h, fl
         return rc;
     if (M == 0)
         return ok();
-    if (!x || !gamma || (fused && (!r || !h)))
+    if (!x || (fused && (!r || !h)))
         return fail(RMSNORM_EINVAL, "null input pointer");
+    if (!gamma && offset != 0.0f)
+        return fail(RMSNORM_EINVAL, "offset needs gamma (gamma == NULL is the non-affine op)");
     if (!fused && !y && !rstd)
         return fail(RMSNORM_EINVAL, "y and rstd are both null: nothing to compute");
     const size_t eb = (size_t)elem_bytes(dtype);
     if (!aligned(x, eb) || !aligned(gamma, eb) || !aligned(y, eb) || !aligned(r, eb) || !aligned(h, eb) ||
         !aligned(rstd, 4))
         return fail(RMSNORM_EINVAL, "pointer not aligned to its element size");
-    if (y && (y == x || y == gamma || (fused && (y == r || y == h))))
+    if (y && (y == x || (gamma && y == gamma) || (fused && (y == r || y == h))))
         return fail(RMSNORM_EINVAL, "y aliases an input");
     if (fused && h == x)
         return fail(RMSNORM_EINVAL, "h_out aliases x (only residual may be overwritten)");
@@ -155,15 +157,17 @@ int do_partials(const void *dy, const void *v, const void *gamma, const float *r
     if (rc)
         return rc;
     const bool fused = (dh != nullptr);
-    if (M > 0 && (!dy || !v || !gamma || !dx))
+    if (M > 0 && (!dy || !v || !dx))
         return fail(RMSNORM_EINVAL, "null input pointer");
+    if (!gamma && offset != 0.0f)
+        return fail(RMSNORM_EINVAL, "offset needs gamma (gamma == NULL is the non-affine op)");
     const size_t eb = (size_t)elem_bytes(dtype);
     if (!aligned(dy, eb) || !aligned(v, eb) || !aligned(gamma, eb) || !aligned(dh, eb) || !aligned(dx, eb) ||
         !aligned(rstd, 4))
         return fail(RMSNORM_EINVAL, "pointer not aligned to its element size");
     if (!aligned(workspace, 16))
         return fail(RMSNORM_EINVAL, "workspace must be 16-byte aligned");
-    if (M > 0 && (dx == dy || dx == v || dx == gamma))
+    if (M > 0 && (dx == dy || dx == v || (gamma && dx == gamma)))
         return fail(RMSNORM_EINVAL, "dx aliases an input other than dh");
     const bool vec_ok = aligned(dy, 16) && aligned(v, 16) && aligned(gamma, 16) && aligned(dh, 16) && aligned(dx, 16);
     int cus = 0;
@@ -172,19 +176,22 @@ int do_partials(const void *dy, const void *v, const void *gamma, const float *r
     rmsnorm_plan p;
     if ((rc = plan_for(fused ? RMSNORM_OP_FUSED_ADD_BWD : RMSNORM_OP_BWD, M, N, dtype, vec_ok, cus, &p)))
         return rc;
-    if (p.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < (size_t)p.workspace_bytes))
+    // Workspace: the partial rows (affine op only), then M floats when rstd is recomputed.
+    const int64_t rstd_region = ((M * 4 + 255) / 256) * 256;
+    const int64_t partial_region = p.workspace_bytes - rstd_region;
+    const int64_t need = (gamma ? partial_region : 0) + (rstd ? 0 : rstd_region);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < (size_t)need))
         return fail(RMSNORM_EWORKSPACE, "workspace of %zu bytes at %p; %lld bytes needed", workspace_bytes,
-                    workspace, (long long)p.workspace_bytes);
-    *programs = p.programs;
+                    workspace, (long long)need);
+    *programs = gamma ? p.programs : 0;
     if (M == 0)
         return ok();
     const int64_t ld = partial_ld(N);
-    float *partials = static_cast<float *>(workspace);
+    float *partials = gamma ? static_cast<float *>(workspace) : nullptr;
     const float *rs = rstd;
     if (rs == nullptr) {
-        // recompute rstd from v into the workspace tail with an rstd-only forward
-        float *tail = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                                (p.workspace_bytes - ((M * 4 + 255) / 256) * 256));
+        // recompute rstd from v into the workspace with an rstd-only forward
+        float *tail = reinterpret_cast<float *>(static_cast<char *>(workspace) + (gamma ? partial_region : 0));
         rmsnorm_plan fp;
         rc = select_plan(RMSNORM_OP_FWD, M, N, dtype, aligned(v, 16) && aligned(gamma, 16), cus, &fp);
         if (rc)
@@ -215,6 +222,13 @@ int do_bwd(const void *dy, const void *dh, const void *v, const void *gamma, con
            void *dgamma, void *workspace, size_t workspace_bytes, int64_t M, int64_t N, float eps, float offset,
            int dtype, hipStream_t stream)
 {
+    if (!gamma) { // non-affine: no dgamma, no partials, no finalizer
+        if (dgamma)
+            return fail(RMSNORM_EINVAL, "dgamma given without gamma");
+        int64_t programs = 0;
+        return do_partials(dy, v, nullptr, rstd, dh, dx, workspace, workspace_bytes, &programs, M, N, eps, offset,
+                           dtype, stream);
+    }
     if (!dgamma)
         return fail(RMSNORM_EINVAL, "dgamma is null");
     if (!aligned(dgamma, (size_t)elem_bytes(dtype == RMSNORM_BF16 ? RMSNORM_BF16 : RMSNORM_F32)))

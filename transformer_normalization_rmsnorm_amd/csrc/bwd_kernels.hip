@@ -47,16 +47,16 @@ __global__ void __launch_bounds__(rows_max_threads(true, TEAM, K)) bwd_rows_kern
     T *dxp = static_cast<T *>(a.dx);
     const float *__restrict__ rstd = a.rstd;
 
-    float w[K][V], acc[K][V];
+    float w[K][V], acc[K][V]; // w = gamma + offset, or 1 for the non-affine op
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int c = k * tl + lane;
         Chunk<T, V> g;
-        if (EXACT || c < nchunks)
+        if (gp != nullptr && (EXACT || c < nchunks))
             g.load_cached(gp + (int64_t)c * V);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-            w[k][e] = (EXACT || c < nchunks) ? g.get(e) + a.offset : 0.0f;
+            w[k][e] = (EXACT || c < nchunks) ? (gp != nullptr ? g.get(e) + a.offset : 1.0f) : 0.0f;
             acc[k][e] = 0.0f;
         }
     }
@@ -122,6 +122,8 @@ __global__ void __launch_bounds__(rows_max_threads(true, TEAM, K)) bwd_rows_kern
 
     row_pipeline<D, Row>((int64_t)blockIdx.x * tpb + team, a.grid * tpb, a.M, load, proc);
 
+    if (a.partials == nullptr) // non-affine: no dgamma
+        return;
     float *__restrict__ part = a.partials + (int64_t)blockIdx.x * a.ld;
     if constexpr (TEAM == 0) {
 #pragma unroll
@@ -168,7 +170,7 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
     const T *__restrict__ gp = static_cast<const T *>(a.gamma);
     const T *dhp = static_cast<const T *>(a.dh);
     T *dxp = static_cast<T *>(a.dx);
-    float *part = a.partials + (int64_t)blockIdx.x * a.ld;
+    float *part = a.partials ? a.partials + (int64_t)blockIdx.x * a.ld : nullptr; // null: non-affine
 
     __shared__ float red[2][16];
     int parity = 0;
@@ -180,10 +182,11 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
             C v, d, g;
             v.load_cached(vp + base + (int64_t)c * V);
             d.load_cached(dyp + base + (int64_t)c * V);
-            g.load_cached(gp + (int64_t)c * V);
+            if (gp != nullptr)
+                g.load_cached(gp + (int64_t)c * V);
 #pragma unroll
             for (int e = 0; e < V; ++e)
-                dot = fmaf(d.get(e) * (g.get(e) + a.offset), v.get(e), dot);
+                dot = fmaf(d.get(e) * (gp != nullptr ? g.get(e) + a.offset : 1.0f), v.get(e), dot);
         }
         dot = block_sum(dot, red[parity], a.threads);
         parity ^= 1;
@@ -193,9 +196,10 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
             C v, d, g;
             v.load_cached(vp + base + (int64_t)c * V);
             d.load_cached(dyp + base + (int64_t)c * V);
-            g.load_cached(gp + (int64_t)c * V);
+            if (gp != nullptr)
+                g.load_cached(gp + (int64_t)c * V);
             float o[V], pa[V];
-            if (first) {
+            if (first || part == nullptr) {
 #pragma unroll
                 for (int e = 0; e < V; ++e)
                     pa[e] = 0.0f;
@@ -209,7 +213,7 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
             for (int e = 0; e < V; ++e) {
                 const float xv = v.get(e);
                 const float dv = d.get(e);
-                float dxv = fmaf(rs, dv * (g.get(e) + a.offset), -xv * kc);
+                float dxv = fmaf(rs, dv * (gp != nullptr ? g.get(e) + a.offset : 1.0f), -xv * kc);
                 if constexpr (FUSED)
                     dxv += dh.get(e);
                 o[e] = dxv;
@@ -218,7 +222,8 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
             C out;
             out.set(o);
             out.store(dxp + base + (int64_t)c * V);
-            store_f32<V>(part + (int64_t)c * V, pa);
+            if (part != nullptr)
+                store_f32<V>(part + (int64_t)c * V, pa);
         }
     }
 }

@@ -49,12 +49,22 @@ __global__ void __launch_bounds__(rows_max_threads(false, TEAM, K)) fwd_rows_ker
     T *__restrict__ y = static_cast<T *>(a.y);
     float *__restrict__ rstd = a.rstd;
 
-    C g[K];
+    C g[K]; // gamma, or ones for the non-affine op (offset is then 0)
+    if (gamma != nullptr) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int c = k * tl + lane;
-        if (EXACT || c < nchunks)
-            g[k].load_cached(gamma + (int64_t)c * V);
+        for (int k = 0; k < K; ++k) {
+            const int c = k * tl + lane;
+            if (EXACT || c < nchunks)
+                g[k].load_cached(gamma + (int64_t)c * V);
+        }
+    } else {
+        float one[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            one[e] = 1.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            g[k].set(one);
     }
 
     auto load = [&](Row &b, int64_t row) __attribute__((always_inline)) {
@@ -180,12 +190,18 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
                     f[e] = v.get(e) + rc.get(e);
                 v.set(f);
             }
-            C g;
-            g.load_cached(gamma + (int64_t)c * V);
             float f[V];
+            if (gamma != nullptr) {
+                C g;
+                g.load_cached(gamma + (int64_t)c * V);
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-                f[e] = (v.get(e) * rs) * (g.get(e) + a.offset);
+                for (int e = 0; e < V; ++e)
+                    f[e] = (v.get(e) * rs) * (g.get(e) + a.offset);
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    f[e] = v.get(e) * rs;
+            }
             C o;
             o.set(f);
             o.store(y + base + (int64_t)c * V);

@@ -22,7 +22,6 @@ constexpr int kLoopThreads = 1024;  // looped path workgroup size
 constexpr int kBwdProgramsPerCU = 1; // persistent backward workgroup teams per compute unit
 constexpr int kBwdTeamsPerCU = 2;    // persistent backward workgroups per compute unit (sub-wave teams)
 constexpr int64_t kMaxGrid = int64_t(1) << 30;
-constexpr int kFwdPersistPerCU = 2; // persistent forward workgroups per compute unit
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -76,10 +75,14 @@ bool pick_block_team(bool bwd, bool vec, int64_t nchunks, int depth, rmsnorm_pla
 
 // Forward workgroup team: among the compiled chunk counts that tile the row
 // exactly (no masked lanes) with a multiple of 64 threads, the one whose
-// thread count is closest to kFwdThreads; else the generic choice.
-constexpr int kFwdThreads = 256;
-bool pick_fwd_block_team(bool vec, int64_t nchunks, int depth, rmsnorm_plan *p)
+// thread count is closest to `target`; else the generic choice.  Measured on
+// MI355X: with few rows per compute unit fewer, fuller lanes win (1024 x 8192
+// bf16: 128 threads x 8 chunks 7.0 us, 256 x 4 7.8 us, 512 x 2 8.2 us); at 8-32
+// rows per unit 256 threads do (4096 x 4096: 256 x 2 13.5 us, 128 x 4 14.0 us).
+// Persistent forward variants were not faster.
+bool pick_fwd_block_team(bool vec, int64_t nchunks, int depth, int target, rmsnorm_plan *p)
 {
+    const int kFwdThreads = target;
     int best_k = 0;
     int64_t best_t = 0;
     for (int k = 1; k <= 16; ++k) {
@@ -197,8 +200,10 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             p.threads = kRowsThreads;
             placed = true;
         } else {
+            const int64_t rows_per_cu = M / std::max(num_cus, 1);
+            const int target = (rows_per_cu >= 8 && rows_per_cu < 32) ? 256 : 128;
             placed = bwd ? pick_block_team(true, true, nchunks, p.depth, &p)
-                         : pick_fwd_block_team(true, nchunks, p.depth, &p);
+                         : pick_fwd_block_team(true, nchunks, p.depth, target, &p);
         }
     } else {
         if (nchunks <= (bwd ? 128 : 512)) {
@@ -216,17 +221,6 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
     }
     if (!complete_plan(&p, M, N, dtype, num_cus, false))
         return RMSNORM_EUNSUPPORTED;
-    // A forward with a few rows per compute unit runs persistently, one row
-    // ahead (measured: 4096 x 4096 and 1024 x 8192 bf16 gain 5-10%); with
-    // one row per team or many rows per unit every team takes a single row.
-    if (!bwd && p.path == RMSNORM_PATH_ROWS && p.team == 0 && M > kFwdPersistPerCU * (int64_t)num_cus &&
-        M <= 16 * (int64_t)num_cus && compiled(false, p.vec != 1, 0, p.chunks, 1)) {
-        rmsnorm_plan q = p;
-        q.depth = 1;
-        q.grid = (int64_t)kFwdPersistPerCU * num_cus;
-        if (complete_plan(&q, M, N, dtype, num_cus, true))
-            p = q;
-    }
     *out = p;
     return RMSNORM_OK;
 }
