@@ -372,7 +372,7 @@ def main():
     import torch
 
     import transformer_normalization_rmsnorm_amd as rn
-    from rmsnorm_inputs import WORKLOADS, algorithmic_bytes
+    from rmsnorm_inputs import ALL_WORKLOADS as WORKLOADS, algorithmic_bytes
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

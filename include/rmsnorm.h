@@ -170,6 +170,9 @@ typedef struct rmsnorm_plan {
     int32_t threads;     /* threads per workgroup of the main kernel */
     int32_t chunks;      /* vector accesses per lane per row and tensor (ROWS path) */
     int32_t depth;       /* rows a team loads ahead of the one it computes (ROWS path) */
+    int32_t w_regs;      /* backward ROWS path: 1 = w = gamma + offset is loaded once per
+                            program and held in registers; 0 = gamma is re-read with every
+                            row (wide rows).  0 for the forward and the LOOP path. */
     int64_t grid;        /* workgroups of the main kernel (backward: partial programs) */
     int64_t programs;    /* backward: dgamma partial rows (= grid); forward: 0 */
     int64_t workspace_bytes; /* backward workspace; forward 0 */
@@ -186,9 +189,9 @@ int rmsnorm_query_plan(int op, int64_t M, int64_t N, int dtype, int vec_ok, int 
 
 /* Tuning and testing aid (the analogue of Liger-Kernel PR #1388's force
  * switches, "Behavior when the fast path does not apply"): later calls of `op`
- * use path, vec, team and threads from *plan, its depth when depth >= 0
- * and its grid when grid > 0 (else the selector's depth and grid for that
- * layout); chunks and the workspace follow.
+ * use path, vec, team and threads from *plan, its depth and w_regs when they
+ * are >= 0 and its grid when grid > 0 (else the selector's depth, w_regs and
+ * grid for that layout); chunks and the workspace follow.
  * vec = 1 forces scalar accesses on aligned data.  NULL clears.  Process-wide
  * and not thread-safe; a call that the override does not fit returns
  * RMSNORM_EINVAL. */
@@ -196,6 +199,9 @@ int rmsnorm_set_plan_override(int op, const rmsnorm_plan *plan);
 
 const char *rmsnorm_status_string(int status);
 const char *rmsnorm_last_error(void);
+/* The ABI version this header describes (RMSNORM_ABI_VERSION); a binding
+ * checks it before use.  2: rmsnorm_plan gained w_regs. */
+#define RMSNORM_ABI_VERSION 2
 int rmsnorm_version(void);
 
 #ifdef __cplusplus

@@ -16,6 +16,8 @@ Recipe (the same for every workload):
 The workloads are the pages' shapes: a 512x2048 and a 4096x4096 bf16 layer, wide
 rows (8192) in bf16, a Gemma-style float32 layer (6144 wide), a DeepSeek-like
 hidden size (7168) with a fused residual add, and a per-head norm (128 wide).
+WIDE_WORKLOADS are rows beyond the pages' 8192-wide scope (16384 and 32768
+wide, plain and fused, bf16 and float32) at 64-128 MiB per tensor.
 """
 
 from __future__ import annotations
@@ -63,6 +65,19 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("bf16_262144x128_per_head", 262144, 128, BF16),
     ]
 }
+
+WIDE_WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("bf16_4096x16384", 4096, 16384, BF16),
+        Workload("bf16_2048x32768", 2048, 32768, BF16),
+        Workload("bf16_4096x16384_fused_add", 4096, 16384, BF16, fused=True),
+        Workload("f32_4096x8192", 4096, 8192, F32),
+        Workload("f32_2048x16384_offset1", 2048, 16384, F32, gemma=True),
+    ]
+}
+
+ALL_WORKLOADS: Dict[str, Workload] = {**WORKLOADS, **WIDE_WORKLOADS}
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:

@@ -148,6 +148,8 @@ def test_plans_for_workloads(M, N, dt, fused):
     # one row per team, nothing prefetched
     assert f["depth"] == 0 and f["grid"] == -(-M // (1 if f["team"] == 0 else f["threads"] // f["team"]))
     assert b["programs"] == b["grid"]
+    # these widths keep w = gamma + offset in registers (the forward has no such field)
+    assert b["w_regs"] == 1 and f["w_regs"] == 0
     ld = -(-N // 64) * 64
     assert b["workspace_bytes"] == -(-b["programs"] * ld * 4 // 256) * 256 + -(-M * 4 // 256) * 256
     assert b["fin_grid"] == ld // 32
@@ -189,7 +191,32 @@ def test_unaligned_and_ragged_take_scalar_access():
                     assert covers(p, N), (op, N, p)
 
 
+@pytest.mark.parametrize("N,dt,fused,want", [
+    # (team, threads, chunks, depth, w_regs)
+    (12288, rn.BF16, False, (0, 512, 3, 1, 1)),     # still w in registers
+    (16384, rn.BF16, False, (0, 1024, 2, 1, 0)),    # gamma re-read with each row
+    (16384, rn.BF16, True, (0, 1024, 2, 1, 0)),
+    (20000, rn.BF16, False, (0, 896, 3, 0, 0)),     # masked lanes
+    (24576, rn.BF16, True, (0, 1024, 3, 0, 0)),
+    (32768, rn.BF16, False, (0, 1024, 4, 0, 0)),
+    (32768, rn.BF16, True, (0, 512, 8, 0, 0)),      # the fused op also holds dh: 512-thread bound
+    (8192, rn.F32, False, (0, 1024, 2, 1, 0)),
+    (12000, rn.F32, True, (0, 1024, 3, 0, 0)),
+    (16384, rn.F32, False, (0, 1024, 4, 0, 0)),
+    (16384, rn.F32, True, (0, 512, 8, 0, 0)),
+])
+def test_wide_backward_rows_stay_in_registers(N, dt, fused, want):
+    p = plan(rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD, 4096, N, dt)
+    assert p["path"] == rn.PATH_ROWS and covers(p, N)
+    assert (p["team"], p["threads"], p["chunks"], p["depth"], p["w_regs"]) == want
+    assert p["grid"] == CUS and p["programs"] == CUS
+
+
 def test_loop_path_beyond_registers():
+    for N, dt in ((40960, rn.BF16), (65536, rn.BF16), (20000, rn.F32), (32768, rn.F32)):
+        for op in (rn.OP_BWD, rn.OP_FUSED_ADD_BWD):
+            p = plan(op, 4096, N, dt)
+            assert p["path"] == rn.PATH_LOOP and p["w_regs"] == 0, (N, dt, p)
     p = plan(rn.OP_BWD, 64, 100000)
     assert p["path"] == rn.PATH_LOOP and p["grid"] == 64
     p = plan(rn.OP_FWD, 64, 1 << 20, rn.F32)
@@ -221,10 +248,28 @@ def test_override_round_trip():
         assert (p["vec"], p["team"], p["threads"], p["chunks"], p["depth"], p["grid"]) == (1, 0, 512, 4, 1, 100)
         assert p["workspace_bytes"] == 100 * 2048 * 4 + 4096 * 4
     assert plan(rn.OP_BWD, 4096, 2048) == base
-    # a workgroup team holding two chunks per lane is compiled for at most 512 threads
-    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=1024):
+    # with w in registers, two chunks per lane are compiled for at most 512 threads;
+    # with gamma re-read per row, for 1024
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=1024, w_regs=1):
         with pytest.raises(rn.RMSNormError):
             plan(rn.OP_BWD, 100, 16384)
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=1024, w_regs=0):
+        p = plan(rn.OP_BWD, 100, 16384)
+        assert (p["chunks"], p["depth"], p["w_regs"]) == (2, 1, 0)
+    # an unset w_regs takes the selector's (1 here), or the other one when only
+    # that one is compiled for the layout (two chunks, no prefetch)
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=512, depth=0):
+        p = plan(rn.OP_BWD, 100, 8192)
+        assert (p["chunks"], p["depth"], p["w_regs"]) == (2, 0, 0)
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=512, depth=0, w_regs=1):
+        with pytest.raises(rn.RMSNormError):
+            plan(rn.OP_BWD, 100, 8192)
+    # the fused op's bound for four chunks without prefetch is 512 threads
+    with rn.plan_override(rn.OP_FUSED_ADD_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=1024, depth=0):
+        with pytest.raises(rn.RMSNormError):
+            plan(rn.OP_FUSED_ADD_BWD, 100, 32768)
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=1024, depth=0):
+        assert plan(rn.OP_BWD, 100, 32768)["chunks"] == 4
     with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=512, depth=3):
         assert plan(rn.OP_BWD, 100, 4096)["depth"] == 3
     with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=512, depth=4):

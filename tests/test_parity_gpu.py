@@ -33,8 +33,16 @@ CASES = [
     (5, 1, "bf16", False, False),         # N = 1
     (7, 7, "f32", False, True),
     (11, 127, "bf16", True, False),
-    (6, 20000, "bf16", False, False),     # beyond the register path: looped rows
-    (4, 40000, "f32", True, True),
+    (6, 20000, "bf16", False, False),     # wide rows, gamma re-read per row, masked lanes
+    (70, 16384, "bf16", False, False),    # wide rows, two chunks per lane, one row ahead
+    (45, 16384, "bf16", True, False),
+    (9, 32768, "bf16", False, False),     # four chunks per lane x 1024 lanes
+    (9, 32768, "bf16", True, True),       # fused: eight chunks x 512 lanes, with offset
+    (20, 8192, "f32", False, True),
+    (5, 12000, "f32", True, False),
+    (7, 16384, "f32", True, False),
+    (4, 40000, "f32", True, True),        # beyond the register path: looped rows
+    (3, 40960, "bf16", False, False),
     (3, 4096, "bf16", False, False),      # fewer rows than programs
     (1, 3000, "f32", False, False),
 ]
@@ -143,10 +151,50 @@ def test_forced_layouts(kind, M, N, dt, fields, fused):
         run_case(M, N, dt, fused, dt == "f32")
 
 
+# Backward layouts that re-read gamma with every row (w_regs = 0), each
+# forced on a shape it tiles, with a small grid so that every program walks
+# several rows (prefetch ring, clamped tail, dgamma accumulation across rows).
+R = rn.PATH_ROWS
+WIDE_FORCED = [
+    # (fused ops too, M, N, dtype, plan fields)
+    (True, 40, 16384, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=0, w_regs=0, grid=7)),
+    (True, 40, 16000, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=1, w_regs=0, grid=6)),
+    (True, 60, 8192, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=2, w_regs=0, grid=9)),
+    (True, 60, 4096, "f32", dict(path=R, vec=4, team=0, threads=512, depth=2, w_regs=0, grid=13)),
+    (True, 30, 24576, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=0, w_regs=0, grid=4)),
+    (True, 30, 12000, "f32", dict(path=R, vec=4, team=0, threads=1024, depth=0, w_regs=0, grid=4)),
+    (True, 30, 12288, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=1, w_regs=0, grid=5)),
+    (False, 20, 32768, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=0, w_regs=0, grid=3)),
+    (False, 20, 16384, "f32", dict(path=R, vec=4, team=0, threads=1024, depth=0, w_regs=0, grid=3)),
+    (True, 30, 16384, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=1, w_regs=0, grid=4)),
+    (True, 30, 8000, "f32", dict(path=R, vec=4, team=0, threads=512, depth=1, w_regs=0, grid=4)),
+    (True, 20, 24576, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=0, w_regs=0, grid=3)),
+    (True, 20, 32768, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=0, w_regs=0, grid=3)),
+    (True, 20, 16384, "f32", dict(path=R, vec=4, team=0, threads=512, depth=0, w_regs=0, grid=3)),
+    # the same shape with w held in registers
+    (True, 60, 8192, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=2, w_regs=1, grid=9)),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["plain", "fused"])
+@pytest.mark.parametrize("fused_ok,M,N,dt,fields", WIDE_FORCED,
+                         ids=[f"{dt}_{M}x{N}_t{f['threads']}_d{f['depth']}_w{f['w_regs']}" for _, M, N, dt, f in WIDE_FORCED])
+def test_wide_backward_layouts(fused_ok, M, N, dt, fields, fused):
+    if fused and not fused_ok:
+        pytest.skip("layout not compiled for the fused op at this workgroup size")
+    op = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
+    with rn.plan_override(op, **fields):
+        p = rn.rmsnorm_query_plan(op, M, N, rn.BF16 if dt == "bf16" else rn.F32, True)
+        for k, v in fields.items():
+            assert p[k] == v, (k, p)
+        run_case(M, N, dt, fused, dt == "f32")
+
+
 # Non-affine op (no gamma): rows and looped paths, plain and fused, with the
 # GPU's rstd and with rstd recomputed.
 NON_AFFINE = [(300, 4096, "bf16", False), (200, 7168, "bf16", True), (130, 6144, "f32", False),
-              (1000, 128, "bf16", True), (17, 4097, "bf16", False), (5, 20000, "f32", True)]
+              (1000, 128, "bf16", True), (17, 4097, "bf16", False), (5, 20000, "f32", True),
+              (7, 16384, "bf16", False), (5, 32768, "bf16", True), (6, 12000, "f32", False)]
 
 
 @pytest.mark.parametrize("M,N,dt,fused", NON_AFFINE, ids=[f"{d}_{m}x{n}{'_fused' if f else ''}" for m, n, d, f in NON_AFFINE])

@@ -10,7 +10,7 @@ import torch
 import transformer_normalization_rmsnorm_amd as rn
 from gpu_util import (check_backward, check_forward, from_dev, gpu_forward,
                       reference_h, to_dev)
-from rmsnorm_inputs import WORKLOADS, make_workload_inputs, sample_rows
+from rmsnorm_inputs import ALL_WORKLOADS as WORKLOADS, make_workload_inputs, sample_rows
 
 pytestmark = pytest.mark.gpu
 

@@ -43,11 +43,15 @@ class RMSNormError(RuntimeError):
         self.status = status
 
 
+# RMSNORM_ABI_VERSION of include/rmsnorm.h that this binding marshals.
+ABI_VERSION = 2
+
+
 class Plan(ctypes.Structure):
     _fields_ = [
         ("op", ctypes.c_int32), ("path", ctypes.c_int32), ("vec", ctypes.c_int32), ("team", ctypes.c_int32),
         ("threads", ctypes.c_int32), ("chunks", ctypes.c_int32), ("depth", ctypes.c_int32),
-        ("grid", ctypes.c_int64),
+        ("w_regs", ctypes.c_int32), ("grid", ctypes.c_int64),
         ("programs", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64), ("fin_threads", ctypes.c_int32),
         ("fin_grid", ctypes.c_int64),
     ]
@@ -94,7 +98,11 @@ def load_library():
             raise RuntimeError(
                 f"{LIBRARY_PATH} is not built; run `python -m transformer_normalization_rmsnorm_amd._build` "
                 "(or __graft_entry__.build()) first")
-        _lib = _bind(ctypes.CDLL(LIBRARY_PATH))
+        lib = _bind(ctypes.CDLL(LIBRARY_PATH))
+        if lib.rmsnorm_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIBRARY_PATH} has ABI version {lib.rmsnorm_version()}, this binding "
+                               f"expects {ABI_VERSION}; rebuild the library")
+        _lib = lib
     return _lib
 
 
@@ -335,14 +343,15 @@ def rmsnorm_query_plan(op: int, M: int, N: int, dtype_code: int, vec_ok: bool = 
 
 
 def rmsnorm_set_plan_override(op: int, plan: Optional[dict]):
-    """Force (path, vec, team, threads[, depth][, grid]) for later calls of `op`;
-    None clears.  A missing depth or grid keeps the selector's."""
+    """Force (path, vec, team, threads[, depth][, w_regs][, grid]) for later calls
+    of `op`; None clears.  A missing depth, w_regs or grid keeps the selector's."""
     lib = load_library()
     if plan is None:
         _check(lib.rmsnorm_set_plan_override(op, None), "rmsnorm_set_plan_override")
         return
     p = Plan()
     p.depth = -1
+    p.w_regs = -1
     for k, v in plan.items():
         setattr(p, k, v)
     _check(lib.rmsnorm_set_plan_override(op, ctypes.byref(p)), "rmsnorm_set_plan_override")

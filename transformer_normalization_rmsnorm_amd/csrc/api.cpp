@@ -97,10 +97,17 @@ int plan_for(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int cus, rmsn
         q.threads = o.plan.threads;
         if (o.plan.depth >= 0)
             q.depth = o.plan.depth;
+        if (o.plan.w_regs >= 0)
+            q.w_regs = o.plan.w_regs;
         q.grid = o.plan.grid;
         if (q.vec != 1 && !vec_ok)
             return fail(RMSNORM_EINVAL, "override asks for 16-byte accesses on unaligned data");
-        if (!complete_plan(&q, M, N, dtype, cus, true))
+        bool fits = complete_plan(&q, M, N, dtype, cus, true);
+        if (!fits && o.plan.w_regs < 0) { // the selector's w_regs belongs to its own layout
+            q.w_regs ^= 1;
+            fits = complete_plan(&q, M, N, dtype, cus, true);
+        }
+        if (!fits)
             return fail(RMSNORM_EINVAL, "override plan does not fit M=%lld N=%lld", (long long)M, (long long)N);
         *p = q;
     }
@@ -360,6 +367,6 @@ const char *rmsnorm_status_string(int status)
 
 const char *rmsnorm_last_error(void) { return g_err; }
 
-int rmsnorm_version(void) { return 1; }
+int rmsnorm_version(void) { return RMSNORM_ABI_VERSION; }
 
 } // extern "C"

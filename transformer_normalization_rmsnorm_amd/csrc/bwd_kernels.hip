@@ -16,23 +16,31 @@
 // and no separate conversion kernel.  Unlike the page's kernel, each team keeps
 // D further rows in flight (row_pipeline) while it reduces and writes the
 // current one, so HBM latency overlaps the work instead of stalling it.
+//
+// Rows wider than the page's scope (it stops at N = 8192 and keeps atomics
+// above) use the same kernel with w_regs = 0: gamma is re-read through the
+// cache with every row instead of held as fp32 w, and the row's packed
+// registers are pinned between the two passes, so that up to 32 bf16 (16
+// fp32) elements per lane and 1024 lanes -- rows of 32768 bf16 / 16384 fp32
+// elements -- stay resident without spilling.
 #include "device_common.h"
 #include "rmsnorm_internal.h"
 
 namespace rmsnorm {
 
-template <typename T, int V, int K, bool FUSED>
+template <typename T, int V, int K, bool WR, bool FUSED>
 struct BwdRow {
     Chunk<T, V> v[K];
     Chunk<T, V> dy[K];
+    Chunk<T, V> g[WR ? 1 : K]; // gamma, when it travels with the row
     Chunk<T, V> dh[FUSED ? K : 1];
     float rs;
 };
 
-template <typename T, int V, int TEAM, int K, int D, bool FUSED, bool EXACT>
-__global__ void __launch_bounds__(rows_max_threads(true, TEAM, K)) bwd_rows_kernel(BwdArgs a)
+template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FUSED, bool EXACT>
+__global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
 {
-    using Row = BwdRow<T, V, K, FUSED>;
+    using Row = BwdRow<T, V, K, WR, FUSED>;
     const int tl = TEAM ? TEAM : a.threads;
     const int lane = TEAM ? (int)(threadIdx.x & (TEAM - 1)) : (int)threadIdx.x;
     const int tpb = TEAM ? a.threads / TEAM : 1;
@@ -47,31 +55,51 @@ __global__ void __launch_bounds__(rows_max_threads(true, TEAM, K)) bwd_rows_kern
     T *dxp = static_cast<T *>(a.dx);
     const float *__restrict__ rstd = a.rstd;
 
-    float w[K][V], acc[K][V]; // w = gamma + offset, or 1 for the non-affine op
+    constexpr int KW = WR ? K : 1;
+    float w[KW][V], acc[K][V]; // w = gamma + offset, or 1 for the non-affine op
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const int c = k * tl + lane;
-        Chunk<T, V> g;
-        if (gp != nullptr && (EXACT || c < nchunks))
-            g.load_cached(gp + (int64_t)c * V);
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-            w[k][e] = (EXACT || c < nchunks) ? (gp != nullptr ? g.get(e) + a.offset : 1.0f) : 0.0f;
+        for (int e = 0; e < V; ++e)
             acc[k][e] = 0.0f;
+    }
+    if constexpr (WR) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * tl + lane;
+            Chunk<T, V> g;
+            if (gp != nullptr && (EXACT || c < nchunks))
+                g.load_cached(gp + (int64_t)c * V);
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                w[k][e] = (EXACT || c < nchunks) ? (gp != nullptr ? g.get(e) + a.offset : 1.0f) : 0.0f;
         }
     }
+    // Every load is unconditional (see row_pipeline): lanes past the row's end
+    // re-read its last chunk and only their stores are masked; without gamma
+    // the row's weight loads read dy's first row and the values are ignored.
+    const T *__restrict__ gsrc = gp != nullptr ? gp : dyp;
+    const bool affine = gp != nullptr;
+    // weight of element e of chunk k of row buffer b
+    auto weight = [&](const Row &b, int k, int e) __attribute__((always_inline)) {
+        if constexpr (WR)
+            return w[k][e];
+        else
+            return affine ? b.g[k].get(e) + a.offset : 1.0f;
+    };
 
     auto load = [&](Row &b, int64_t row) __attribute__((always_inline)) {
         const int64_t base = row * N;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const int c = k * tl + lane;
-            if (EXACT || c < nchunks) {
-                b.v[k].load(vp + base + (int64_t)c * V);
-                b.dy[k].load(dyp + base + (int64_t)c * V);
-                if constexpr (FUSED)
-                    b.dh[k].load(dhp + base + (int64_t)c * V);
-            }
+            const int c0 = k * tl + lane;
+            const int c = EXACT ? c0 : min(c0, nchunks - 1);
+            b.v[k].load(vp + base + (int64_t)c * V);
+            b.dy[k].load(dyp + base + (int64_t)c * V);
+            if constexpr (!WR)
+                b.g[k].load_cached(gsrc + (int64_t)c * V);
+            if constexpr (FUSED)
+                b.dh[k].load(dhp + base + (int64_t)c * V);
         }
         b.rs = rstd[row];
     };
@@ -86,8 +114,18 @@ __global__ void __launch_bounds__(rows_max_threads(true, TEAM, K)) bwd_rows_kern
             if (EXACT || c < nchunks) {
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    dot = fmaf(b.dy[k].get(e) * w[k][e], b.v[k].get(e), dot);
+                    dot = fmaf(b.dy[k].get(e) * weight(b, k, e), b.v[k].get(e), dot);
             }
+        }
+        // values unpacked for the dot are formed again in the second pass
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            b.v[k].pin();
+            b.dy[k].pin();
+            if constexpr (!WR)
+                b.g[k].pin();
+            if constexpr (FUSED)
+                b.dh[k].pin();
         }
         if constexpr (TEAM == 0) {
             dot = block_sum(dot, red[parity], a.threads);
@@ -107,7 +145,7 @@ __global__ void __launch_bounds__(rows_max_threads(true, TEAM, K)) bwd_rows_kern
                 for (int e = 0; e < V; ++e) {
                     const float xv = b.v[k].get(e);
                     const float d = b.dy[k].get(e);
-                    float dxv = fmaf(rs, d * w[k][e], -xv * kc);
+                    float dxv = fmaf(rs, d * weight(b, k, e), -xv * kc);
                     if constexpr (FUSED)
                         dxv += b.dh[k].get(e);
                     o[e] = dxv;
@@ -288,7 +326,7 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(const float *__re
     }
 }
 
-template <typename T, int V, int TEAM, int K, int D, bool FUSED>
+template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FUSED>
 static void launch_bwd_rows(const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s)
 {
     const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
@@ -296,11 +334,12 @@ static void launch_bwd_rows(const rmsnorm_plan &p, const BwdArgs &a, hipStream_t
     const size_t lds = TEAM ? (size_t)(p.threads / TEAM) * (size_t)a.N * sizeof(float) : 0;
     if constexpr (V > 1) {
         if ((int64_t)lanes * K == a.N / V) {
-            hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, FUSED, true>), grid, block, lds, s, a);
+            hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, true>), grid, block, lds, s,
+                               a);
             return;
         }
     }
-    hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, FUSED, false>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, false>), grid, block, lds, s, a);
 }
 
 template <typename T, bool FUSED>
@@ -318,10 +357,10 @@ static hipError_t dispatch_bwd(const rmsnorm_plan &p, BwdArgs a, hipStream_t s)
         return hipGetLastError();
     }
     const bool vec = (p.vec == VV);
-#define RMSNORM_CASE(VEC, TEAM, K, D)                                                        \
-    if (vec == (VEC == 1) && p.team == TEAM && p.chunks == K && p.depth == D) {              \
-        launch_bwd_rows<T, (VEC == 1 ? VV : 1), TEAM, K, D, FUSED>(p, a, s);                 \
-        return hipGetLastError();                                                            \
+#define RMSNORM_CASE(VEC, TEAM, K, D, WR, BOUND, FBOUND)                                      \
+    if (vec == (VEC == 1) && p.team == TEAM && p.chunks == K && p.depth == D && p.w_regs == WR) { \
+        launch_bwd_rows<T, (VEC == 1 ? VV : 1), TEAM, K, D, WR == 1, (FUSED ? FBOUND : BOUND), FUSED>(p, a, s); \
+        return hipGetLastError();                                                                 \
     }
     RMSNORM_BWD_ROWS_CONFIGS(RMSNORM_CASE)
 #undef RMSNORM_CASE

@@ -34,12 +34,26 @@ __device__ __forceinline__ uint16_t to_bf16(float f)
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// Register barrier: an empty asm statement that claims to modify `x`, so the
+// compiler cannot carry values derived from `x` across it and must derive them
+// again from the (packed) register afterwards.  Used between a row's two
+// passes: without it the compiler keeps the unpacked fp32 copies of a bf16 row
+// (and products such as dy * w) live across the reduction, which doubles the
+// registers a row needs.
+template <typename U>
+__device__ __forceinline__ void pin_vgpr(U &x)
+{
+    static_assert(sizeof(U) == 4, "one 32-bit register");
+    asm volatile("" : "+v"(x));
+}
+
 // A chunk is the V consecutive elements of a row that one lane moves with one
 // memory instruction: 16 bytes (bf16 x8, f32 x4) on the vector path, one
 // element on the scalar path.  load/store stream the row tensors with the
 // nontemporal hint (each element is touched once per call; measured on
 // MI355X: about 10% more bandwidth for three-stream traffic); load_cached is
-// for gamma, which every team re-reads.
+// for gamma, which every team re-reads.  pin() applies the register barrier
+// to the chunk's registers.
 template <typename T, int V>
 struct Chunk;
 
@@ -74,6 +88,12 @@ struct Chunk<bf16_t, 8> {
         for (int i = 0; i < 4; ++i)
             w[i] = 0u;
     }
+    __device__ __forceinline__ void pin()
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            pin_vgpr(w[i]);
+    }
 };
 
 template <>
@@ -85,6 +105,12 @@ struct Chunk<bf16_t, 1> {
     __device__ __forceinline__ float get(int) const { return __uint_as_float((uint32_t)b << 16); }
     __device__ __forceinline__ void set(const float (&f)[1]) { b = to_bf16(f[0]); }
     __device__ __forceinline__ void zero() { b = 0; }
+    __device__ __forceinline__ void pin()
+    {
+        uint32_t t = b;
+        pin_vgpr(t);
+        b = (uint16_t)t;
+    }
 };
 
 template <>
@@ -118,6 +144,12 @@ struct Chunk<float, 4> {
         for (int i = 0; i < 4; ++i)
             v[i] = 0.0f;
     }
+    __device__ __forceinline__ void pin()
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            pin_vgpr(v[i]);
+    }
 };
 
 template <>
@@ -129,6 +161,7 @@ struct Chunk<float, 1> {
     __device__ __forceinline__ float get(int) const { return v; }
     __device__ __forceinline__ void set(const float (&f)[1]) { v = f[0]; }
     __device__ __forceinline__ void zero() { v = 0.0f; }
+    __device__ __forceinline__ void pin() { pin_vgpr(v); }
 };
 
 // V float32 values of a dgamma partial row: 16-byte accesses when V >= 4.

@@ -31,7 +31,7 @@ struct FwdRow {
 // smaller grid makes the kernel persistent.  EXACT: lanes x chunks covers the
 // row exactly, so no lane is masked.
 template <typename T, int V, int TEAM, int K, int D, bool FUSED, bool EXACT>
-__global__ void __launch_bounds__(rows_max_threads(false, TEAM, K)) fwd_rows_kernel(FwdArgs a)
+__global__ void __launch_bounds__(fwd_rows_bound_rule(TEAM, K)) fwd_rows_kernel(FwdArgs a)
 {
     using C = Chunk<T, V>;
     using Row = FwdRow<T, V, K, FUSED>;

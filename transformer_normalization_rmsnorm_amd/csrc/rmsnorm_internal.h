@@ -67,36 +67,57 @@ constexpr int kFinColsPerBlock = 32;
     X(1, 0, 1, 1) X(1, 0, 2, 1) X(1, 0, 3, 1) X(1, 0, 4, 1) X(1, 0, 6, 1)                \
     X(1, 0, 1, 2) X(1, 0, 2, 2) X(1, 0, 3, 2) X(1, 0, 4, 2) X(1, 0, 1, 3) X(1, 0, 2, 3)
 
+// Backward: X(vector access, team lanes, chunks per lane, rows loaded ahead,
+// w in registers, launch bound, launch bound of the fused-add op).  With w in
+// registers (1) each program loads w = gamma + offset once and keeps it for
+// all its rows, the layout of FlyDSL PR #855 ("Hybrid atomic / two-stage
+// backward"); with 0, gamma travels with every row through the cache instead,
+// which frees 8 (bf16) or 4 (fp32) registers per chunk and lets rows of up to
+// 32768 bf16 / 16384 fp32 elements stay in registers.  The launch bounds are
+// the largest workgroups for which the entry compiles without spilling (1024
+// threads: 128 VGPRs; 512: 256 VGPRs) in both dtypes; the fused-add op also
+// holds the dh row.
 #define RMSNORM_BWD_ROWS_CONFIGS(X)                                                      \
-    X(1, 8, 1, 1) X(1, 16, 1, 1) X(1, 32, 1, 1) X(1, 8, 1, 2) X(1, 16, 1, 2)             \
-    X(1, 32, 1, 2) X(1, 64, 1, 1) X(1, 64, 2, 1) X(1, 64, 1, 2)                          \
-    X(1, 0, 1, 1) X(1, 0, 1, 2) X(1, 0, 1, 3) X(1, 0, 2, 1) X(1, 0, 2, 2) X(1, 0, 3, 1)  \
-    X(0, 64, 1, 1) X(0, 64, 2, 1) X(0, 0, 1, 1) X(0, 0, 2, 1) X(0, 0, 4, 1)
+    X(1, 8, 1, 1, 1, 256, 256) X(1, 16, 1, 1, 1, 256, 256) X(1, 32, 1, 1, 1, 256, 256)   \
+    X(1, 8, 1, 2, 1, 256, 256) X(1, 16, 1, 2, 1, 256, 256) X(1, 32, 1, 2, 1, 256, 256)   \
+    X(1, 64, 1, 1, 1, 256, 256) X(1, 64, 2, 1, 1, 256, 256) X(1, 64, 1, 2, 1, 256, 256)  \
+    X(1, 0, 1, 1, 1, 1024, 1024) X(1, 0, 1, 2, 1, 1024, 1024) X(1, 0, 1, 3, 1, 1024, 1024) \
+    X(1, 0, 2, 1, 1, 512, 512) X(1, 0, 2, 2, 1, 512, 512) X(1, 0, 3, 1, 1, 512, 512)     \
+    X(1, 0, 2, 0, 0, 1024, 1024) X(1, 0, 2, 1, 0, 1024, 1024) X(1, 0, 2, 2, 0, 512, 512) \
+    X(1, 0, 3, 0, 0, 1024, 1024) X(1, 0, 3, 1, 0, 512, 512) X(1, 0, 4, 0, 0, 1024, 512)  \
+    X(1, 0, 4, 1, 0, 512, 512) X(1, 0, 6, 0, 0, 512, 512) X(1, 0, 8, 0, 0, 512, 512)     \
+    X(0, 64, 1, 1, 1, 256, 256) X(0, 64, 2, 1, 1, 256, 256) X(0, 0, 1, 1, 1, 1024, 1024) \
+    X(0, 0, 2, 1, 1, 512, 512) X(0, 0, 4, 1, 1, 512, 512)
 
-inline bool fwd_rows_compiled(bool vec, int team, int chunks, int depth)
+// Forward launch bound: teams of at most a wavefront run in 256-thread
+// workgroups; a workgroup team holding more than two chunks per lane is capped
+// at 512 threads so that it may use up to 256 VGPRs instead of spilling.
+constexpr int fwd_rows_bound_rule(int team, int chunks)
 {
-#define RMSNORM_MATCH(V, TEAM, K, D) \
-    || ((V) == (vec ? 1 : 0) && (TEAM) == team && (K) == chunks && (D) == depth)
-    return false RMSNORM_FWD_ROWS_CONFIGS(RMSNORM_MATCH);
-#undef RMSNORM_MATCH
+    return team != 0 ? 256 : (chunks > 2 ? 512 : 1024);
 }
 
-inline bool bwd_rows_compiled(bool vec, int team, int chunks, int depth)
+// Launch bound of a compiled forward configuration, 0 if it is not compiled.
+inline int fwd_rows_bound(bool vec, int team, int chunks, int depth)
 {
-#define RMSNORM_MATCH(V, TEAM, K, D) \
-    || ((V) == (vec ? 1 : 0) && (TEAM) == team && (K) == chunks && (D) == depth)
-    return false RMSNORM_BWD_ROWS_CONFIGS(RMSNORM_MATCH);
+#define RMSNORM_MATCH(V, TEAM, K, D)                                                     \
+    if ((V) == (vec ? 1 : 0) && (TEAM) == team && (K) == chunks && (D) == depth)          \
+        return fwd_rows_bound_rule(TEAM, K);
+    RMSNORM_FWD_ROWS_CONFIGS(RMSNORM_MATCH)
 #undef RMSNORM_MATCH
+    return 0;
 }
 
-// Workgroup-size bound each kernel is compiled for (its __launch_bounds__):
-// teams of at most a wavefront run in 256-thread workgroups; a workgroup team
-// holding more chunks per lane (backward: more than one, forward: more than
-// two) is capped at 512 threads so that it may use up to 256 VGPRs instead of
-// spilling.
-constexpr int rows_max_threads(bool bwd, int team, int chunks)
+// Launch bound of a compiled backward configuration, 0 if it is not compiled.
+inline int bwd_rows_bound(bool fused, bool vec, int team, int chunks, int depth, int w_regs)
 {
-    return team != 0 ? 256 : (chunks > (bwd ? 1 : 2) ? 512 : 1024);
+#define RMSNORM_MATCH(V, TEAM, K, D, WR, BOUND, FBOUND)                                  \
+    if ((V) == (vec ? 1 : 0) && (TEAM) == team && (K) == chunks && (D) == depth &&        \
+        (WR) == w_regs)                                                                   \
+        return fused ? (FBOUND) : (BOUND);
+    RMSNORM_BWD_ROWS_CONFIGS(RMSNORM_MATCH)
+#undef RMSNORM_MATCH
+    return 0;
 }
 
 // Elements per 16-byte access.

@@ -34,17 +34,22 @@ int pow2_at_least(int64_t v)
 }
 
 bool is_bwd(int op) { return op == RMSNORM_OP_BWD || op == RMSNORM_OP_FUSED_ADD_BWD; }
+bool is_fused(int op) { return op == RMSNORM_OP_FUSED_ADD_FWD || op == RMSNORM_OP_FUSED_ADD_BWD; }
 
-bool compiled(bool bwd, bool vec, int team, int k, int depth)
+// Launch bound of a compiled configuration, 0 if it is not compiled (the
+// forward has no w_regs variants: it is always 0 there).
+int bound(int op, bool vec, int team, int k, int depth, int w_regs)
 {
-    return bwd ? bwd_rows_compiled(vec, team, k, depth) : fwd_rows_compiled(vec, team, k, depth);
+    if (is_bwd(op))
+        return bwd_rows_bound(is_fused(op), vec, team, k, depth, w_regs);
+    return w_regs == 0 ? fwd_rows_bound(vec, team, k, depth) : 0;
 }
 
-// Smallest compiled chunk count >= need for (vec, team, depth).
-int pick_chunks(bool bwd, bool vec, int team, int depth, int64_t need)
+// Smallest compiled chunk count >= need for (vec, team, depth, w_regs).
+int pick_chunks(int op, bool vec, int team, int depth, int w_regs, int64_t need)
 {
     for (int k = 1; k <= 16; ++k)
-        if (k >= need && compiled(bwd, vec, team, k, depth))
+        if (k >= need && bound(op, vec, team, k, depth, w_regs) > 0)
             return k;
     return 0;
 }
@@ -53,19 +58,45 @@ int pick_chunks(bool bwd, bool vec, int team, int depth, int64_t need)
 // multiple of 64) fits the kernel's launch bound, preferring `cap` threads.
 // The backward prefers one chunk per lane (its registers also hold w, the
 // dgamma accumulators and the rows in flight).
-bool pick_block_team(bool bwd, bool vec, int64_t nchunks, int depth, rmsnorm_plan *p)
+bool pick_block_team(int op, bool vec, int64_t nchunks, int depth, rmsnorm_plan *p)
 {
+    const bool bwd = is_bwd(op);
     const int caps_fwd[2] = {512, 1024}, caps_bwd[2] = {1024, 1024};
+    const int wr = bwd ? 1 : 0;
     for (int cap : bwd ? caps_bwd : caps_fwd) {
         for (int k = 1; k <= 16; ++k) {
-            if (!compiled(bwd, vec, 0, k, depth))
+            const int b = bound(op, vec, 0, k, depth, wr);
+            if (b == 0)
                 continue;
             const int64_t threads = std::max<int64_t>(64, round_up(ceil_div(nchunks, k), 64));
-            if (threads <= cap && threads <= rows_max_threads(bwd, 0, k)) {
+            if (threads <= cap && threads <= b) {
                 p->team = 0;
                 p->threads = (int32_t)threads;
                 p->chunks = k;
                 p->depth = depth;
+                p->w_regs = wr;
+                return true;
+            }
+        }
+    }
+    return false;
+}
+
+// Backward rows too wide for w in registers: gamma is re-read with every row.
+// The fewest chunks per lane whose thread count fits a compiled launch bound,
+// with the deepest prefetch compiled at that size.
+bool pick_wide_bwd_team(int op, bool vec, int64_t nchunks, rmsnorm_plan *p)
+{
+    for (int k = 1; k <= 16; ++k) {
+        const int64_t threads = std::max<int64_t>(64, round_up(ceil_div(nchunks, k), 64));
+        for (int d = 3; d >= 0; --d) {
+            const int b = bound(op, vec, 0, k, d, 0);
+            if (b > 0 && threads <= b) {
+                p->team = 0;
+                p->threads = (int32_t)threads;
+                p->chunks = k;
+                p->depth = d;
+                p->w_regs = 0;
                 return true;
             }
         }
@@ -80,16 +111,17 @@ bool pick_block_team(bool bwd, bool vec, int64_t nchunks, int depth, rmsnorm_pla
 // bf16: 128 threads x 8 chunks 7.0 us, 256 x 4 7.8 us, 512 x 2 8.2 us); at 8-32
 // rows per unit 256 threads do (4096 x 4096: 256 x 2 13.5 us, 128 x 4 14.0 us).
 // Persistent forward variants were not faster.
-bool pick_fwd_block_team(bool vec, int64_t nchunks, int depth, int target, rmsnorm_plan *p)
+bool pick_fwd_block_team(int op, bool vec, int64_t nchunks, int depth, int target, rmsnorm_plan *p)
 {
     const int kFwdThreads = target;
     int best_k = 0;
     int64_t best_t = 0;
     for (int k = 1; k <= 16; ++k) {
-        if (!compiled(false, vec, 0, k, depth) || nchunks % k != 0)
+        const int b = bound(op, vec, 0, k, depth, 0);
+        if (b == 0 || nchunks % k != 0)
             continue;
         const int64_t t = nchunks / k;
-        if (t % 64 != 0 || t > rows_max_threads(false, 0, k))
+        if (t % 64 != 0 || t > b)
             continue;
         const int64_t d = t > kFwdThreads ? t - kFwdThreads : kFwdThreads - t;
         const int64_t bd = best_t > kFwdThreads ? best_t - kFwdThreads : kFwdThreads - best_t;
@@ -99,11 +131,12 @@ bool pick_fwd_block_team(bool vec, int64_t nchunks, int depth, int target, rmsno
         }
     }
     if (best_k == 0)
-        return pick_block_team(false, vec, nchunks, depth, p);
+        return pick_block_team(op, vec, nchunks, depth, p);
     p->team = 0;
     p->threads = (int32_t)best_t;
     p->chunks = best_k;
     p->depth = depth;
+    p->w_regs = 0;
     return true;
 }
 
@@ -127,6 +160,10 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
         return false;
     const int64_t nchunks = N / p->vec;
     int64_t rows_per_block = 1;
+    if (!bwd)
+        p->w_regs = 0;
+    if (p->w_regs != 0 && p->w_regs != 1)
+        return false;
     if (p->path == RMSNORM_PATH_ROWS) {
         if (p->team != 0) {
             if (p->team != 8 && p->team != 16 && p->team != 32 && p->team != 64)
@@ -136,8 +173,8 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
             rows_per_block = p->threads / p->team;
         }
         const int lanes = p->team ? p->team : p->threads;
-        const int k = pick_chunks(bwd, p->vec != 1, p->team, p->depth, ceil_div(nchunks, lanes));
-        if (k == 0 || p->threads > rows_max_threads(bwd, p->team, k))
+        const int k = pick_chunks(p->op, p->vec != 1, p->team, p->depth, p->w_regs, ceil_div(nchunks, lanes));
+        if (k == 0 || p->threads > bound(p->op, p->vec != 1, p->team, k, p->depth, p->w_regs))
             return false;
         p->chunks = k;
         if (bwd && p->team != 0 && rows_per_block * N * (int64_t)sizeof(float) > 65536)
@@ -146,6 +183,7 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
         p->team = 0;
         p->chunks = 0;
         p->depth = 0;
+        p->w_regs = 0;
     } else {
         return false;
     }
@@ -184,8 +222,10 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
     p.path = RMSNORM_PATH_ROWS;
     const bool vec = vec_ok && (N % VV == 0);
     p.vec = vec ? VV : 1;
-    // forward: one row per team, no prefetch; backward: persistent, one row ahead
+    // forward: one row per team, no prefetch; backward: persistent, one row
+    // ahead, w held in registers
     p.depth = bwd ? 1 : 0;
+    p.w_regs = bwd ? 1 : 0;
     const int64_t nchunks = N / p.vec;
     bool placed = false;
     if (vec) {
@@ -202,8 +242,11 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
         } else {
             const int64_t rows_per_cu = M / std::max(num_cus, 1);
             const int target = (rows_per_cu >= 8 && rows_per_cu < 32) ? 256 : 128;
-            placed = bwd ? pick_block_team(true, true, nchunks, p.depth, &p)
-                         : pick_fwd_block_team(true, nchunks, p.depth, target, &p);
+            if (bwd)
+                placed = pick_block_team(op, true, nchunks, p.depth, &p) ||
+                         pick_wide_bwd_team(op, true, nchunks, &p);
+            else
+                placed = pick_fwd_block_team(op, true, nchunks, p.depth, target, &p);
         }
     } else {
         if (nchunks <= (bwd ? 128 : 512)) {
@@ -211,7 +254,7 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             p.threads = kRowsThreads;
             placed = true;
         } else {
-            placed = pick_block_team(bwd, false, nchunks, p.depth, &p);
+            placed = pick_block_team(op, false, nchunks, p.depth, &p);
         }
     }
     if (!placed) {
