@@ -148,8 +148,9 @@ def test_plans_for_workloads(M, N, dt, fused):
     # one row per team, nothing prefetched
     assert f["depth"] == 0 and f["grid"] == -(-M // (1 if f["team"] == 0 else f["threads"] // f["team"]))
     assert b["programs"] == b["grid"]
-    # these widths keep w = gamma + offset in registers (the forward has no such field)
-    assert b["w_regs"] == 1 and f["w_regs"] == 0
+    # w = gamma + offset stays in registers when one chunk per lane covers the
+    # row; the forward has no such field
+    assert b["w_regs"] == (1 if N // vec <= 1024 else 0) and f["w_regs"] == 0
     ld = -(-N // 64) * 64
     assert b["workspace_bytes"] == -(-b["programs"] * ld * 4 // 256) * 256 + -(-M * 4 // 256) * 256
     assert b["fin_grid"] == ld // 32
@@ -176,7 +177,7 @@ def test_plan_shapes_by_width():
     p = plan(rn.OP_FWD, 4096, 4096)   # 16 rows per compute unit
     assert (p["team"], p["threads"], p["chunks"]) == (0, 256, 2)
     p = plan(rn.OP_BWD, 1024, 6144, rn.F32)
-    assert (p["team"], p["threads"], p["chunks"], p["depth"]) == (0, 512, 3, 1)
+    assert (p["team"], p["threads"], p["chunks"], p["depth"], p["w_regs"]) == (0, 768, 2, 1, 0)
 
 
 def test_unaligned_and_ragged_take_scalar_access():
@@ -193,7 +194,8 @@ def test_unaligned_and_ragged_take_scalar_access():
 
 @pytest.mark.parametrize("N,dt,fused,want", [
     # (team, threads, chunks, depth, w_regs)
-    (12288, rn.BF16, False, (0, 512, 3, 1, 1)),     # still w in registers
+    (8192, rn.BF16, False, (0, 1024, 1, 1, 1)),     # one chunk per lane: w in registers
+    (12288, rn.BF16, False, (0, 768, 2, 1, 0)),
     (16384, rn.BF16, False, (0, 1024, 2, 1, 0)),    # gamma re-read with each row
     (16384, rn.BF16, True, (0, 1024, 2, 1, 0)),
     (20000, rn.BF16, False, (0, 896, 3, 0, 0)),     # masked lanes

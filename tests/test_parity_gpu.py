@@ -171,8 +171,8 @@ WIDE_FORCED = [
     (True, 20, 24576, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=0, w_regs=0, grid=3)),
     (True, 20, 32768, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=0, w_regs=0, grid=3)),
     (True, 20, 16384, "f32", dict(path=R, vec=4, team=0, threads=512, depth=0, w_regs=0, grid=3)),
-    # the same shape with w held in registers
-    (True, 60, 8192, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=2, w_regs=1, grid=9)),
+    # w held in registers, several rows per program
+    (True, 60, 8192, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=2, w_regs=1, grid=9)),
 ]
 
 

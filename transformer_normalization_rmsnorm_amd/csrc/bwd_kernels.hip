@@ -17,7 +17,8 @@
 // D further rows in flight (row_pipeline) while it reduces and writes the
 // current one, so HBM latency overlaps the work instead of stalling it.
 //
-// Rows wider than the page's scope (it stops at N = 8192 and keeps atomics
+// Rows wider than one chunk per lane of a 1024-lane workgroup (8192 bf16 /
+// 4096 fp32 elements; the page's scope stops at N = 8192 and keeps atomics
 // above) use the same kernel with w_regs = 0: gamma is re-read through the
 // cache with every row instead of held as fp32 w, and the row's packed
 // registers are pinned between the two passes, so that up to 32 bf16 (16
@@ -117,15 +118,22 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
                     dot = fmaf(b.dy[k].get(e) * weight(b, k, e), b.v[k].get(e), dot);
             }
         }
-        // values unpacked for the dot are formed again in the second pass
+        // Values unpacked for the dot are formed again in the second pass where
+        // registers are scarce: gamma-per-row layouts and sub-workgroup teams
+        // (measured on MI355X: 262144 x 128 bf16 3% faster).  Workgroup teams
+        // with w in registers have registers to spare at one program per CU,
+        // and keeping the unpacked row there is 1.5% faster (4096 x 4096,
+        // 16384 x 8192 bf16).
+        if constexpr (!WR || TEAM != 0) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            b.v[k].pin();
-            b.dy[k].pin();
-            if constexpr (!WR)
-                b.g[k].pin();
-            if constexpr (FUSED)
-                b.dh[k].pin();
+            for (int k = 0; k < K; ++k) {
+                b.v[k].pin();
+                b.dy[k].pin();
+                if constexpr (!WR)
+                    b.g[k].pin();
+                if constexpr (FUSED)
+                    b.dh[k].pin();
+            }
         }
         if constexpr (TEAM == 0) {
             dot = block_sum(dot, red[parity], a.threads);

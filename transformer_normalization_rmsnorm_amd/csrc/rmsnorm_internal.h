@@ -82,7 +82,6 @@ constexpr int kFinColsPerBlock = 32;
     X(1, 8, 1, 2, 1, 256, 256) X(1, 16, 1, 2, 1, 256, 256) X(1, 32, 1, 2, 1, 256, 256)   \
     X(1, 64, 1, 1, 1, 256, 256) X(1, 64, 2, 1, 1, 256, 256) X(1, 64, 1, 2, 1, 256, 256)  \
     X(1, 0, 1, 1, 1, 1024, 1024) X(1, 0, 1, 2, 1, 1024, 1024) X(1, 0, 1, 3, 1, 1024, 1024) \
-    X(1, 0, 2, 1, 1, 512, 512) X(1, 0, 2, 2, 1, 512, 512) X(1, 0, 3, 1, 1, 512, 512)     \
     X(1, 0, 2, 0, 0, 1024, 1024) X(1, 0, 2, 1, 0, 1024, 1024) X(1, 0, 2, 2, 0, 512, 512) \
     X(1, 0, 3, 0, 0, 1024, 1024) X(1, 0, 3, 1, 0, 512, 512) X(1, 0, 4, 0, 0, 1024, 512)  \
     X(1, 0, 4, 1, 0, 512, 512) X(1, 0, 6, 0, 0, 512, 512) X(1, 0, 8, 0, 0, 512, 512)     \

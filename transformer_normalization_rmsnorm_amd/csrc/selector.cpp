@@ -56,8 +56,8 @@ int pick_chunks(int op, bool vec, int team, int depth, int w_regs, int64_t need)
 
 // Workgroup-wide team: the fewest chunks per lane whose thread count (a
 // multiple of 64) fits the kernel's launch bound, preferring `cap` threads.
-// The backward prefers one chunk per lane (its registers also hold w, the
-// dgamma accumulators and the rows in flight).
+// The backward (scalar access here) prefers one chunk per lane: its registers
+// also hold w, the dgamma accumulators and the rows in flight.
 bool pick_block_team(int op, bool vec, int64_t nchunks, int depth, rmsnorm_plan *p)
 {
     const bool bwd = is_bwd(op);
@@ -242,8 +242,13 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
         } else {
             const int64_t rows_per_cu = M / std::max(num_cus, 1);
             const int target = (rows_per_cu >= 8 && rows_per_cu < 32) ? 256 : 128;
+            // backward: w in registers with one chunk per lane (the pages'
+            // layout), else gamma re-read per row.  Measured on MI355X, gamma
+            // per row with two chunks per lane and one row ahead beats w in
+            // registers with three (bf16 8192 x 12288: 106.6 vs 109.3 us;
+            // fp32 16384 x 6144: 197.3 vs 204.1 us) and ties it at 10240 bf16.
             if (bwd)
-                placed = pick_block_team(op, true, nchunks, p.depth, &p) ||
+                placed = (nchunks <= 1024 && pick_block_team(op, true, nchunks, p.depth, &p)) ||
                          pick_wide_bwd_team(op, true, nchunks, &p);
             else
                 placed = pick_fwd_block_team(op, true, nchunks, p.depth, target, &p);
