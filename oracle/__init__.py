@@ -48,10 +48,14 @@ def _bind(lib):
     lib.oracle_bwd.argtypes = [ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_f, c_f,
                                c_dp, c_dp, c_dp, c_dp]
     lib.oracle_round.argtypes = [ctypes.c_int, c_dp, c_i64, c_vp]
+    lib.oracle_e4m3_encode.argtypes = [c_dp, c_i64, c_vp]
+    lib.oracle_e4m3_decode.argtypes = [c_vp, c_i64, c_dp]
+    lib.oracle_fwd_fp8.argtypes = [ctypes.c_int, c_vp, c_vp, c_i64, c_i64, c_f, c_f, c_f, ctypes.c_double,
+                                   c_vp, c_vp, c_vp, c_dp, c_dp]
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     lib.oracle_set_num_threads.restype = None
     for f in (lib.oracle_fwd, lib.oracle_fused_add_fwd, lib.oracle_bwd, lib.oracle_round,
-              lib.oracle_num_threads):
+              lib.oracle_num_threads, lib.oracle_e4m3_encode, lib.oracle_e4m3_decode, lib.oracle_fwd_fp8):
         f.restype = ctypes.c_int
     return lib
 
@@ -153,3 +157,42 @@ def round_to(a64, dtype: str, lib=None) -> np.ndarray:
     out = np.empty(a64.shape, NP_STORAGE[dtype])
     _check(lib.oracle_round(DTYPE_CODE[dtype], _ptr(a64), a64.size, _ptr(out)), "oracle_round")
     return out
+
+
+def e4m3_encode(t64, lib=None) -> np.ndarray:
+    """Nearest OCP E4M3 (FN) codes to float64 values, ties to even, saturating at +-448."""
+    lib = lib or load()
+    t64 = np.ascontiguousarray(t64, dtype=np.float64)
+    out = np.empty(t64.shape, np.uint8)
+    _check(lib.oracle_e4m3_encode(_ptr(t64), t64.size, _ptr(out)), "oracle_e4m3_encode")
+    return out
+
+
+def e4m3_decode(codes, lib=None) -> np.ndarray:
+    """Values of E4M3 (FN) codes as float64 (NaN for 0x7F / 0xFF)."""
+    lib = lib or load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, np.float64)
+    _check(lib.oracle_e4m3_decode(_ptr(codes), codes.size, _ptr(out)), "oracle_e4m3_decode")
+    return out
+
+
+def fwd_fp8(v, gamma, dtype: str, eps: float, offset: float, scale: float, *, tol: float = 0.0,
+            lib=None) -> Dict[str, np.ndarray]:
+    """fp8-output forward of v: code = E4M3(y64 * scale), amax = max |y64|.
+
+    With tol > 0 also code_lo / code_hi, the codes of t * (1 -+ tol) in value
+    order.  Returns code, code_lo, code_hi (or None), rstd64 [M], amax64 (float).
+    """
+    lib = lib or load()
+    v = _storage(v, dtype)
+    gamma = None if gamma is None else _storage(gamma, dtype)
+    M, N = v.shape
+    code = np.empty((M, N), np.uint8)
+    lo = np.empty((M, N), np.uint8) if tol > 0 else None
+    hi = np.empty((M, N), np.uint8) if tol > 0 else None
+    rstd = np.empty(M, np.float64)
+    amax = np.zeros(1, np.float64)
+    _check(lib.oracle_fwd_fp8(DTYPE_CODE[dtype], _ptr(v), _ptr(gamma), M, N, eps, offset, scale, tol,
+                              _ptr(code), _ptr(lo), _ptr(hi), _ptr(rstd), _ptr(amax)), "oracle_fwd_fp8")
+    return {"code": code, "code_lo": lo, "code_hi": hi, "rstd64": rstd, "amax64": float(amax[0])}

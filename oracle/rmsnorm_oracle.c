@@ -36,6 +36,17 @@
  * Non-affine RMSNorm (no gamma; Liger-Kernel PR #1388 "Validation" tests the
  * affine and non-affine ops): gamma == NULL means w_j = 1, and offset must be 0.
  *
+ * fp8 output (TransformerEngine PR #583: the normalization kernel's output
+ * type may be float8 E4M3, used by its fp8 training runs).  The page fixes
+ * only the type; the readings taken, after the usual delayed-scaling use of
+ * such an output:
+ *     t_ij   = y_ij * scale              (scale: the caller's float32 factor)
+ *     code_ij = E4M3(t_ij)               nearest, ties to even, saturating
+ *     amax   = max_ij |y_ij|             (before scaling)
+ * E4M3 is the OCP "FN" format: 1 sign bit, 4 exponent bits with bias 7,
+ * 3 mantissa bits, no infinities, largest finite 448 = 1.75 * 2^8, smallest
+ * normal 2^-6, subnormals m * 2^-9 (m = 1..7); codes 0x7F / 0xFF are NaN.
+ *
  * Rounding to a storage type is round-to-nearest, ties to even (FlyDSL PR #855,
  * "512-thread vec8 fast path": software RNE / hardware conversion).
  *
@@ -43,7 +54,8 @@
  * column ranges (dgamma, each column summed over rows in row order).  No sum is
  * reordered.
  *
- * Pins (tests/test_oracle_pins.py): finite differences, the RMS invariant, the
+ * Pins (tests/test_oracle_pins.py; the fp8 encoder also against a
+ * brute-force nearest-code search and torch's float8_e4m3fn cast): finite differences, the RMS invariant, the
  * sum_j v_j dx_j identity, closed forms (N = 1, constant rows, eps = 0 scale
  * invariance, gamma/offset equivalence, fused-add reductions), the fp64
  * torch.nn.functional.rms_norm with autograd, hand-worked fixtures under
@@ -270,5 +282,105 @@ int oracle_bwd(int dt, const void *dy, const void *v, const void *gamma, const v
         }
     }
     free(rstd);
+    return ORACLE_OK;
+}
+
+/* ---- fp8 E4M3 (OCP FN) -------------------------------------------------- */
+
+/* Nearest E4M3 code to t, ties to even, saturating at +-448.  As for bf16:
+ * below 2^-6 the spacing is fixed at 2^-9, above it is 2^(floor(log2|t|) - 3),
+ * and nearbyint of the exact quotient gives ties to even. */
+static uint8_t e4m3_from_double(double t)
+{
+    const uint8_t sign = signbit(t) ? 0x80 : 0x00;
+    double a = fabs(t);
+    if (isnan(t))
+        return (uint8_t)(sign | 0x7F);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7E);
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);
+    int q = e - 1; /* floor(log2 a) */
+    if (q < -6)
+        q = -6;
+    const double spacing = ldexp(1.0, q - 3);
+    const double r = nearbyint(a / spacing) * spacing; /* at most 448: a < 448 = 14 * 32 */
+    if (r == 0.0)
+        return sign;
+    if (r < 0x1p-6) /* subnormal: r = m * 2^-9 */
+        return (uint8_t)(sign | (uint8_t)(r / 0x1p-9));
+    frexp(r, &e);
+    const int E = e - 1;                               /* r = (1 + m/8) * 2^E */
+    const int m = (int)(r / ldexp(1.0, E - 3)) - 8;    /* exact: 0..7 */
+    return (uint8_t)(sign | (uint8_t)(((E + 7) << 3) | m));
+}
+
+static double e4m3_to_double(uint8_t c)
+{
+    const double s = (c & 0x80) ? -1.0 : 1.0;
+    const int e = (c >> 3) & 0xF, m = c & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        return s * ldexp((double)m, -9);
+    return s * ldexp(1.0 + m / 8.0, e - 7);
+}
+
+int oracle_e4m3_encode(const double *src, int64_t n, uint8_t *dst)
+{
+    if (!src || !dst || n < 0)
+        return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = e4m3_from_double(src[i]);
+    return ORACLE_OK;
+}
+
+int oracle_e4m3_decode(const uint8_t *src, int64_t n, double *dst)
+{
+    if (!src || !dst || n < 0)
+        return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = e4m3_to_double(src[i]);
+    return ORACLE_OK;
+}
+
+/* fp8-output forward of v (h for the fused-add op: the caller forms h first).
+ * code [M, N] = E4M3(y64 * scale).  With tol > 0, code_lo / code_hi [M, N]
+ * (each may be NULL) are the codes of t * (1 - tol) and t * (1 + tol): since
+ * the encoding is monotone, every value within a relative tol of t encodes
+ * to a code between them.  rstd64 [M] and amax64 (one value) may be NULL. */
+int oracle_fwd_fp8(int dt, const void *v, const void *gamma, int64_t M, int64_t N, float eps, float offset,
+                   float scale, double tol, uint8_t *code, uint8_t *code_lo, uint8_t *code_hi, double *rstd64,
+                   double *amax64)
+{
+    if (!dtype_ok(dt) || !v || !code || M < 0 || N <= 0 || tol < 0.0 || (!gamma && offset != 0.0f))
+        return ORACLE_EINVAL;
+    const double e = (double)eps, off = (double)offset, sc = (double)scale;
+    double amax = 0.0;
+#pragma omp parallel for schedule(static) reduction(max : amax)
+    for (int64_t i = 0; i < M; ++i) {
+        const double rstd = row_rstd(dt, v, i, N, e);
+        if (rstd64)
+            rstd64[i] = rstd;
+        for (int64_t j = 0; j < N; ++j) {
+            const double y = load_elem(dt, v, i * N + j) * rstd * scale_w(dt, gamma, j, off);
+            const double t = y * sc;
+            if (fabs(y) > amax)
+                amax = fabs(y);
+            code[i * N + j] = e4m3_from_double(t);
+            /* t * (1 -+ tol) toward / away from zero: the lower and upper ends
+             * of the interval in value order */
+            const double lo = t < 0 ? t * (1.0 + tol) : t * (1.0 - tol);
+            const double hi = t < 0 ? t * (1.0 - tol) : t * (1.0 + tol);
+            if (code_lo)
+                code_lo[i * N + j] = e4m3_from_double(lo);
+            if (code_hi)
+                code_hi[i * N + j] = e4m3_from_double(hi);
+        }
+    }
+    if (amax64)
+        *amax64 = amax;
     return ORACLE_OK;
 }

@@ -17,6 +17,9 @@ mismatch.  What pins what:
   storage_widening     bf16/f32 storage widened exactly (same answers as f64 storage)
   rounding             nearest-even rounding vs torch casts and brute force
   non_affine           no gamma: finite differences, RMS invariant, gamma = 1 equivalence
+  e4m3_brute_force     fp8 E4M3 encoder vs an exhaustive nearest-code search
+  e4m3_torch           fp8 E4M3 encoder vs torch's float8_e4m3fn cast; code round trip
+  fp8_forward          fp8-output forward = plain forward then the encoder; amax; brackets
 """
 
 from __future__ import annotations
@@ -267,6 +270,104 @@ def torch_fp64(lib):
         np.testing.assert_allclose(out["dgamma64"], tw.grad.numpy(), rtol=1e-11, atol=1e-12)
 
 
+def _e4m3_value(c: int) -> float:
+    """Value of an E4M3 (OCP FN) code from the format's definition (NaN codes excluded by callers)."""
+    sign = -1.0 if c & 0x80 else 1.0
+    e, m = (c >> 3) & 0xF, c & 7
+    return sign * (m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+
+
+def _e4m3_brute(t: float) -> int:
+    """Nearest finite E4M3 code by exhaustive search; ties to the even mantissa;
+    beyond the largest finite value, the largest finite value of that sign."""
+    neg = t < 0 or (t == 0 and np.signbit(t))
+    a = abs(t)
+    best_c, best_d = None, None
+    for c in range(0x7F):  # non-negative finite codes 0x00..0x7E
+        d = abs(_e4m3_value(c) - a)
+        if best_d is None or d < best_d or (d == best_d and (c & 1) == 0):
+            best_c, best_d = c, d
+    return best_c | (0x80 if neg else 0)
+
+
+def _e4m3_probe_values(rng):
+    pos = sorted({_e4m3_value(c) for c in range(0x7F)})
+    vals = []
+    for a, b in zip(pos[:-1], pos[1:]):
+        mid = (a + b) / 2
+        vals += [a, mid, np.nextafter(mid, 0.0), np.nextafter(mid, 1e9)]
+    vals += [448.0, 449.0, 463.9, 464.0, 464.1, 480.0, 1e4, 2.0 ** -10, 2.0 ** -11, 1e-12, 0.0]
+    vals += list(np.exp(rng.uniform(np.log(2.0 ** -12), np.log(600.0), 400)))
+    vals = np.array(vals, dtype=np.float64)
+    return np.concatenate([vals, -vals])
+
+
+def e4m3_brute_force(lib):
+    """The oracle's E4M3 encoder against an exhaustive nearest-code search."""
+    vals = _e4m3_probe_values(np.random.default_rng(23))
+    got = oracle.e4m3_encode(vals, lib=lib)
+    want = np.array([_e4m3_brute(float(v)) for v in vals], dtype=np.uint8)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(vals[i]), hex(int(got[i])), hex(int(want[i]))) for i in bad[:8]]
+
+
+def e4m3_torch(lib):
+    """Against torch's float8_e4m3fn cast (nearest, ties to even) of float32
+    values inside +-448, and the code round trip of every finite code."""
+    import torch
+
+    # float32 inputs: torch's cast from float64 goes through float32 and so
+    # rounds twice; from float32 it rounds once.  Midpoints +- one float32 ulp.
+    pos = sorted({_e4m3_value(c) for c in range(0x7F)})
+    v32 = []
+    for a, b in zip(pos[:-1], pos[1:]):
+        mid = np.float32((a + b) / 2)
+        v32 += [np.float32(a), mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1e9))]
+    v32 += list(np.exp(np.random.default_rng(29).uniform(np.log(2.0 ** -12), np.log(448.0), 400)).astype(np.float32))
+    v32 = np.array(v32, dtype=np.float32)
+    v32 = np.concatenate([v32, -v32])
+    v32 = v32[np.abs(v32) <= 448.0]
+    t = torch.from_numpy(v32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_encode(v32.astype(np.float64), lib=lib)
+    assert np.array_equal(got, t), np.nonzero(got != t)[0][:8]
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    dec = oracle.e4m3_decode(codes, lib=lib)
+    assert np.array_equal(dec, [_e4m3_value(int(c)) for c in codes])
+    assert np.array_equal(oracle.e4m3_encode(dec, lib=lib), codes)
+    assert np.isnan(oracle.e4m3_decode(np.array([0x7F, 0xFF], np.uint8), lib=lib)).all()
+
+
+def fp8_forward(lib):
+    """The fp8 forward is the plain forward followed by the encoder: codes of
+    y64 * scale, amax = max |y64|, and the tolerance brackets around them."""
+    rng = np.random.default_rng(31)
+    M, N = 5, 37
+    for dt, gemma, scale in (("f32", False, 1.0), ("bf16", True, 37.5), ("bf16", None, 300.0)):
+        conv = (lambda a: a.astype(np.float32)) if dt == "f32" else f32_to_bf16_bits
+        x = conv(rng.standard_normal((M, N)).astype(np.float32))
+        gamma = None if gemma is None else conv(((0.1 if gemma else 1.0) * rng.standard_normal(N) + (0 if gemma else 1)).astype(np.float32))
+        off = 1.0 if gemma else 0.0
+        y, rstd = oracle.fwd(x, gamma, dt, 1e-6, off, lib=lib)
+        out = oracle.fwd_fp8(x, gamma, dt, 1e-6, off, scale, tol=1e-5, lib=lib)
+        assert np.array_equal(out["code"], oracle.e4m3_encode(y * np.float64(np.float32(scale)), lib=lib))
+        assert np.array_equal(out["rstd64"], rstd)
+        assert out["amax64"] == np.abs(y).max()
+        t = y * np.float64(np.float32(scale))
+        dec = lambda c: oracle.e4m3_decode(c, lib=lib)
+        # brackets, checked exactly with a window wide enough that they usually differ
+        wide = oracle.fwd_fp8(x, gamma, dt, 1e-6, off, scale, tol=0.05, lib=lib)
+        lo_v, hi_v = np.where(t < 0, t * 1.05, t * 0.95), np.where(t < 0, t * 0.95, t * 1.05)
+        assert np.array_equal(wide["code_lo"], oracle.e4m3_encode(lo_v, lib=lib))
+        assert np.array_equal(wide["code_hi"], oracle.e4m3_encode(hi_v, lib=lib))
+        assert np.mean(dec(wide["code_lo"]) < dec(wide["code_hi"])) > 0.3
+        assert np.all(dec(out["code_lo"]) <= dec(out["code"])) and np.all(dec(out["code"]) <= dec(out["code_hi"]))
+        # correct rounding: no finite code is nearer to t than the chosen one
+        grid = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8), lib=lib)
+        ts = np.clip(np.abs(t), 0, 448).ravel()
+        nearest = np.min(np.abs(grid[None, :] - ts[:, None]), axis=1)
+        assert np.all(np.abs(np.abs(dec(out["code"])).ravel() - ts) <= nearest)
+
+
 def load_golden(path: str = GOLDEN):
     cases, cur = {}, None
     with open(path) as f:
@@ -280,8 +381,8 @@ def load_golden(path: str = GOLDEN):
                 continue
             key, _, val = line.partition(":")
             toks = val.split()
-            if key.strip() == "bits":
-                cur["bits"] = [int(t, 16) for t in toks]
+            if key.strip() in ("bits", "codes"):
+                cur[key.strip()] = [int(t, 16) for t in toks]
             else:
                 cur[key.strip()] = [float(t) for t in toks]
     return cases
@@ -293,6 +394,14 @@ def golden(lib):
         if name == "bf16_round":
             got = oracle.round_to(np.array(c["values"]), "bf16", lib=lib)
             assert list(map(int, got)) == c["bits"], (name, [hex(int(b)) for b in got])
+            continue
+        if "codes" in c:  # fp8 output
+            N = int(c["N"][0])
+            out = oracle.fwd_fp8(np.array(c["x"]).reshape(-1, N), np.array(c["gamma"]), "f64", c["eps"][0],
+                                 c["offset"][0], c["scale"][0], lib=lib)
+            assert list(map(int, out["code"].ravel())) == c["codes"], (name, [hex(int(b)) for b in out["code"].ravel()])
+            np.testing.assert_allclose(out["rstd64"], c["rstd"], rtol=1e-15, err_msg=name)
+            np.testing.assert_allclose(out["amax64"], c["amax"][0], rtol=1e-15, err_msg=name)
             continue
         N = int(c["N"][0])
         eps, off = c["eps"][0], c["offset"][0]
@@ -440,4 +549,5 @@ def non_affine(lib):
 ALL_PINS = [
     finite_differences, rms_invariant, orthogonality, closed_form_n1, constant_row, scale_invariance,
     offset_equivalence, fused_reductions, torch_fp64, golden, storage_widening, rounding, non_affine,
+    e4m3_brute_force, e4m3_torch, fp8_forward,
 ]

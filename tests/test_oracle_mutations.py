@@ -34,11 +34,24 @@ MUTATIONS = [
      "uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 15;", False),
     ("subnormal_spacing", "if (q < -126)\n        q = -126;", "if (q < -149)\n        q = -149;", False),
     ("non_affine_scale", "return gamma ? load_elem(dt, gamma, j) + off : 1.0;", "return gamma ? load_elem(dt, gamma, j) + off : 1.0 + off + 0.5;", False),
+    # fp8 E4M3 output
+    ("e4m3_ties_away", "const double r = nearbyint(a / spacing) * spacing;", "const double r = round(a / spacing) * spacing;", False),
+    ("e4m3_exponent_bias", "((E + 7) << 3) | m", "((E + 8) << 3) | m", False),
+    ("e4m3_no_saturation", "if (a >= 448.0)\n        return (uint8_t)(sign | 0x7E);",
+     "if (a >= 464.0)\n        return (uint8_t)(sign | 0x7F);", False),
+    ("e4m3_subnormal_boundary", "if (q < -6)\n        q = -6;", "if (q < -7)\n        q = -7;", False),
+    ("e4m3_mantissa_offset", "const int m = (int)(r / ldexp(1.0, E - 3)) - 8;", "const int m = (int)(r / ldexp(1.0, E - 3)) - 7;", False),
+    ("e4m3_decode_bias", "return s * ldexp(1.0 + m / 8.0, e - 7);", "return s * ldexp(1.0 + m / 8.0, e - 8);", False),
+    ("fp8_amax_after_scale", "if (fabs(y) > amax)\n                amax = fabs(y);", "if (fabs(t) > amax)\n                amax = fabs(t);", False),
+    ("fp8_scale_dropped", "const double t = y * sc;", "const double t = y;", False),
+    ("fp8_bracket_swapped", "const double lo = t < 0 ? t * (1.0 + tol) : t * (1.0 - tol);",
+     "const double lo = t < 0 ? t * (1.0 - tol) : t * (1.0 + tol);", False),
 ]
 
 # fast pins first so a mutant usually fails within a second
 PIN_ORDER = [
-    oracle_pins.golden, oracle_pins.closed_form_n1, oracle_pins.constant_row, oracle_pins.rms_invariant,
+    oracle_pins.golden, oracle_pins.e4m3_brute_force, oracle_pins.e4m3_torch, oracle_pins.fp8_forward,
+    oracle_pins.closed_form_n1, oracle_pins.constant_row, oracle_pins.rms_invariant,
     oracle_pins.orthogonality, oracle_pins.offset_equivalence, oracle_pins.scale_invariance,
     oracle_pins.fused_reductions, oracle_pins.storage_widening, oracle_pins.rounding, oracle_pins.torch_fp64,
     oracle_pins.non_affine, oracle_pins.finite_differences,
