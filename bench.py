@@ -85,6 +85,7 @@ class Sets:
         M, N = w.M, w.N
         self.dt = rn.BF16 if w.dtype == "bf16" else rn.F32
         self.ws_bytes = rn.rmsnorm_bwd_workspace_bytes(M, N, self.dt)
+        self.ws8_bytes = rn.rmsnorm_fwd_fp8_workspace_bytes(M, N, self.dt)
         self.sets = []
         for _ in range(n_sets):
             s = {
@@ -92,6 +93,11 @@ class Sets:
                 "y": torch.empty(M, N, dtype=td, device=dev), "rstd": torch.empty(M, dtype=torch.float32, device=dev),
                 "dx": torch.empty(M, N, dtype=td, device=dev), "dg": torch.empty(N, dtype=td, device=dev),
                 "ws": torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev),
+                # fp8-output forward: E4M3 codes, scale, amax and its partials
+                "y8": torch.empty(M, N, dtype=torch.uint8, device=dev),
+                "scale": torch.full((1,), 16.0, dtype=torch.float32, device=dev),
+                "amax": torch.zeros(1, dtype=torch.float32, device=dev),
+                "ws8": torch.empty(max(self.ws8_bytes, 16), dtype=torch.uint8, device=dev),
             }
             if w.fused:
                 s["residual"] = base["residual"].clone()
@@ -119,6 +125,19 @@ class Sets:
             rc = L.rmsnorm_fwd(s["x"].data_ptr(), s["gamma"].data_ptr(), s["y"].data_ptr(), s["rstd"].data_ptr(),
                                w.M, w.N, w.eps, w.offset, self.dt, st)
         self._check(rc, "fwd")
+
+    def fwd_fp8(self, i, st):
+        s, w, L = self.sets[i % len(self.sets)], self.w, self.lib
+        if w.fused:
+            rc = L.rmsnorm_fused_add_fwd_fp8(s["x"].data_ptr(), s["residual"].data_ptr(), s["gamma"].data_ptr(),
+                                             s["y8"].data_ptr(), s["h"].data_ptr(), s["rstd"].data_ptr(),
+                                             s["scale"].data_ptr(), s["amax"].data_ptr(), s["ws8"].data_ptr(),
+                                             self.ws8_bytes, w.M, w.N, w.eps, w.offset, self.dt, st)
+        else:
+            rc = L.rmsnorm_fwd_fp8(s["x"].data_ptr(), s["gamma"].data_ptr(), s["y8"].data_ptr(), s["rstd"].data_ptr(),
+                                   s["scale"].data_ptr(), s["amax"].data_ptr(), s["ws8"].data_ptr(), self.ws8_bytes,
+                                   w.M, w.N, w.eps, w.offset, self.dt, st)
+        self._check(rc, "fwd_fp8")
 
     def bwd(self, i, st):
         s, w, L = self.sets[i % len(self.sets)], self.w, self.lib
@@ -215,7 +234,8 @@ def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
     bytes_f = algorithmic_bytes(fop, w.M, w.N, w.elem_bytes)
     bytes_b = algorithmic_bytes(bop, w.M, w.N, w.elem_bytes)
     bytes_main = algorithmic_bytes(bop + "_main", w.M, w.N, w.elem_bytes)
-    res["bytes"] = {"fwd": bytes_f, "bwd": bytes_b, "bwd_main": bytes_main}
+    bytes_f8 = algorithmic_bytes(("fused_" if w.fused else "") + "fwd_fp8", w.M, w.N, w.elem_bytes)
+    res["bytes"] = {"fwd": bytes_f, "bwd": bytes_b, "bwd_main": bytes_main, "fwd_fp8": bytes_f8}
     for mode in (("cold", "hot") if detailed else ("cold",)):
         S = Sets(w, lib, rn, torch, n_sets_for(w, mode == "cold"))
         K = len(S.sets)
@@ -228,10 +248,12 @@ def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
         r["bwd_us"] = time_direct(torch, lambda i, s: S.bwd(i + K // 2, s), iters, warmup)
         r["bwd_main_us"] = time_direct(torch, S.bwd_main, iters, warmup)
         r["finalize_us"] = time_graph(torch, S.finalize, iters)
+        # fp8-output forward with amax (main kernel + amax fold)
+        r["fwd_fp8_us"] = time_direct(torch, S.fwd_fp8, iters, warmup)
         if detailed:
             r["fwd_graph_us"] = time_graph(torch, S.fwd, iters)
             r["bwd_graph_us"] = time_graph(torch, lambda i, s: S.bwd(i + K // 2, s), iters)
-        for op, b in (("fwd", bytes_f), ("bwd", bytes_b), ("bwd_main", bytes_main)):
+        for op, b in (("fwd", bytes_f), ("bwd", bytes_b), ("bwd_main", bytes_main), ("fwd_fp8", bytes_f8)):
             r[op + "_GBs"] = b / (r[op + "_us"] * 1e3)
             r[op + "_pct_peak"] = 100.0 * r[op + "_GBs"] / HBM_PEAK_GBS
         res[mode] = r
@@ -442,6 +464,7 @@ def main():
         "us_per_step": round(ms_per_step * 1e3, 3),
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "fwd_us": round(cold["fwd_us"], 3), "bwd_us": round(cold["bwd_us"], 3),
+        "fwd_fp8_us": round(cold["fwd_fp8_us"], 3), "fwd_fp8_GBs": round(cold["fwd_fp8_GBs"], 1),
         "fwd_GBs": round(cold["fwd_GBs"], 1), "bwd_GBs": round(cold["bwd_GBs"], 1),
         "fwd_pct_peak": round(cold["fwd_pct_peak"], 2), "bwd_pct_peak": round(cold["bwd_pct_peak"], 2),
         "bwd_main_us": round(main_us, 3), "finalize_us": round(cold["finalize_us"], 3),

@@ -97,6 +97,46 @@ int rmsnorm_fused_add_fwd(const void *x, const void *residual, const void *gamma
                           int64_t M, int64_t N, float eps, float offset,
                           int dtype, rmsnorm_stream_t stream);
 
+/* Forward with float8 E4M3 output (TransformerEngine PR #583: the
+ * normalization kernel's output type may be float8 E4M3, for its fp8 runs).
+ * The page fixes only the type.  The readings follow the delayed-scaling use
+ * of such an output:
+ *   y_ij   = v_ij * rstd_i * (gamma_j + offset), in float32 as rmsnorm_fwd;
+ *   y8_ij  = E4M3(y_ij * scale): OCP E4M3 "FN" (sign, 4 exponent bits with
+ *            bias 7, 3 mantissa bits; largest finite 448; no infinities),
+ *            nearest, ties to even, saturating at +-448;
+ *   *amax  = max(*amax, max_ij |y_ij|), y before scaling, when amax != NULL.
+ *   x      [M, N] T; gamma [N] T (NULL: non-affine)
+ *   y8     [M, N] bytes, the E4M3 codes (required)
+ *   rstd   [M] f32, may be NULL
+ *   scale  device pointer to one float32 (read by the kernel, so a captured
+ *          graph uses its value at replay)
+ *   amax   device pointer to one float32, or NULL.  The caller initialises it
+ *          (for example to 0) at the start of an amax window; each call folds
+ *          its maximum in.  No atomics: every workgroup writes its maximum to
+ *          `workspace` and a one-workgroup kernel folds them into *amax.
+ *   workspace: needed only when amax != NULL: rmsnorm_fwd_fp8_workspace_bytes()
+ *          bytes of device memory, 16-byte aligned, contents ignored on entry.
+ * The 16-byte access path needs x, gamma 16-byte aligned and y8 aligned to
+ * 16 / sizeof(T) bytes. */
+int rmsnorm_fwd_fp8(const void *x, const void *gamma, void *y8, float *rstd,
+                    const float *scale, float *amax, void *workspace, size_t workspace_bytes,
+                    int64_t M, int64_t N, float eps, float offset,
+                    int dtype, rmsnorm_stream_t stream);
+
+/* Fused residual add then the fp8-output forward: h_out receives
+ * round_T(x + residual) (may alias residual), y8/amax as rmsnorm_fwd_fp8 on h.
+ * The 16-byte path also needs residual and h_out 16-byte aligned. */
+int rmsnorm_fused_add_fwd_fp8(const void *x, const void *residual, const void *gamma,
+                              void *y8, void *h_out, float *rstd,
+                              const float *scale, float *amax, void *workspace, size_t workspace_bytes,
+                              int64_t M, int64_t N, float eps, float offset,
+                              int dtype, rmsnorm_stream_t stream);
+
+/* Workspace the fp8-output forwards need when amax is requested: one float
+ * per workgroup of the launch.  Writes the byte count to *bytes. */
+int rmsnorm_fwd_fp8_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *bytes);
+
 /* Workspace the backward needs on the current device (FlyDSL PR #855
  * "Runtime configuration and ownership": programs * N * sizeof(float) of
  * partials, here with each partial row padded to 64 floats, plus M floats used
@@ -154,7 +194,9 @@ typedef enum rmsnorm_op {
     RMSNORM_OP_FWD = 0,
     RMSNORM_OP_FUSED_ADD_FWD = 1,
     RMSNORM_OP_BWD = 2,
-    RMSNORM_OP_FUSED_ADD_BWD = 3
+    RMSNORM_OP_FUSED_ADD_BWD = 3,
+    RMSNORM_OP_FWD_FP8 = 4,
+    RMSNORM_OP_FUSED_ADD_FWD_FP8 = 5
 } rmsnorm_op;
 
 typedef enum rmsnorm_path {
@@ -174,10 +216,11 @@ typedef struct rmsnorm_plan {
                             program and held in registers; 0 = gamma is re-read with every
                             row (wide rows).  0 for the forward and the LOOP path. */
     int64_t grid;        /* workgroups of the main kernel (backward: partial programs) */
-    int64_t programs;    /* backward: dgamma partial rows (= grid); forward: 0 */
-    int64_t workspace_bytes; /* backward workspace; forward 0 */
-    int32_t fin_threads; /* backward finalizer workgroup size */
-    int64_t fin_grid;    /* backward finalizer workgroups */
+    int64_t programs;    /* backward: dgamma partial rows (= grid); fp8 forward: amax
+                            partials (= grid); plain forward: 0 */
+    int64_t workspace_bytes; /* backward and fp8-forward workspace; plain forward 0 */
+    int32_t fin_threads; /* finalizer workgroup size (dgamma, or amax for fp8) */
+    int64_t fin_grid;    /* finalizer workgroups */
 } rmsnorm_plan;
 
 /* Pure selector query: the plan for `op` at (M, N, dtype).  vec_ok != 0 says
@@ -200,8 +243,9 @@ int rmsnorm_set_plan_override(int op, const rmsnorm_plan *plan);
 const char *rmsnorm_status_string(int status);
 const char *rmsnorm_last_error(void);
 /* The ABI version this header describes (RMSNORM_ABI_VERSION); a binding
- * checks it before use.  2: rmsnorm_plan gained w_regs. */
-#define RMSNORM_ABI_VERSION 2
+ * checks it before use.  2: rmsnorm_plan gained w_regs.  3: fp8-output
+ * forwards (ops 4 and 5). */
+#define RMSNORM_ABI_VERSION 3
 int rmsnorm_version(void);
 
 #ifdef __cplusplus

@@ -163,9 +163,13 @@ def algorithmic_bytes(op: str, M: int, N: int, elem_bytes: int) -> int:
     fused fwd : read x, residual, gamma; write y, h, rstd = 4MNB + NB + 4M
     fused bwd : read dy, dh, h, gamma, rstd; write dx, dgamma = 4MNB + 2NB + 4M
     bwd main  : the backward without the dgamma write (3MNB + NB + 4M plain)
+    fp8 fwd   : read x, gamma; write y8 (1 byte), rstd  = MNB + MN + NB + 4M
+    fused fp8 : read x, residual, gamma; write y8, h, rstd = 3MNB + MN + NB + 4M
     """
     B = elem_bytes
     table = {
+        "fwd_fp8": M * N * B + M * N + N * B + 4 * M,
+        "fused_fwd_fp8": 3 * M * N * B + M * N + N * B + 4 * M,
         "fwd": 2 * M * N * B + N * B + 4 * M,
         "bwd": 3 * M * N * B + 2 * N * B + 4 * M,
         "fused_fwd": 4 * M * N * B + N * B + 4 * M,

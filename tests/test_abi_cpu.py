@@ -86,6 +86,31 @@ def test_fused_fwd_argument_errors(lib):
     assert f(FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 1e-6, 0.0, rn.F32, None) == EINVAL  # f32 misaligned
 
 
+def test_fp8_fwd_argument_errors(lib):
+    f = lib.rmsnorm_fwd_fp8
+
+    def call(x=FAKE, g=FAKE + 4096, y8=FAKE + 8192, rstd=None, scale=FAKE + 12288, amax=None, ws=None, M=4, N=8,
+             off=0.0, dt=rn.BF16):
+        return f(x, g, y8, rstd, scale, amax, ws, 0, M, N, 1e-6, off, dt, None)
+
+    assert call(scale=None) == EINVAL
+    assert b"y8 and scale" in lib.rmsnorm_last_error()
+    assert call(y8=None) == EINVAL
+    assert call(scale=FAKE + 12290) == EINVAL     # float32 alignment
+    assert call(amax=FAKE + 12294) == EINVAL
+    assert call(x=ODD) == EINVAL
+    assert call(y8=FAKE) == EINVAL                # y8 aliases x
+    assert call(g=None, off=1.0) == EINVAL
+    assert call(dt=9) == EUNSUPPORTED
+    assert call(M=0, x=None, g=None) == OK        # nothing to do
+    ff = lib.rmsnorm_fused_add_fwd_fp8
+    assert ff(FAKE, None, FAKE + 4096, FAKE + 8192, FAKE + 16384, None, FAKE + 12288, None, None, 0, 4, 8, 1e-6,
+              0.0, rn.BF16, None) == EINVAL      # residual
+    size = ctypes.c_size_t(0)
+    assert lib.rmsnorm_fwd_fp8_workspace_bytes(4, 0, rn.BF16, ctypes.byref(size)) == EINVAL
+    assert lib.rmsnorm_fwd_fp8_workspace_bytes(4, 8, rn.BF16, None) == EINVAL
+
+
 def test_bwd_argument_errors(lib):
     b = lib.rmsnorm_bwd
     args = dict(dy=FAKE, x=FAKE + 4096, g=FAKE + 8192, rstd=None, dx=FAKE + 12288, dg=FAKE + 16384, ws=FAKE + 32768)
@@ -212,6 +237,31 @@ def test_wide_backward_rows_stay_in_registers(N, dt, fused, want):
     assert p["path"] == rn.PATH_ROWS and covers(p, N)
     assert (p["team"], p["threads"], p["chunks"], p["depth"], p["w_regs"]) == want
     assert p["grid"] == CUS and p["programs"] == CUS
+
+
+@pytest.mark.parametrize("M,N,dt", [(4096, 4096, rn.BF16), (262144, 128, rn.BF16), (16384, 6144, rn.F32),
+                                    (1024, 8192, rn.BF16), (100, 4097, rn.BF16), (64, 100000, rn.BF16)])
+def test_fp8_plans_follow_the_forward(M, N, dt):
+    for op, op8 in ((rn.OP_FWD, rn.OP_FWD_FP8), (rn.OP_FUSED_ADD_FWD, rn.OP_FUSED_ADD_FWD_FP8)):
+        p, q = plan(op, M, N, dt), plan(op8, M, N, dt)
+        # the same kind of layout; workgroup teams aim at 256 threads for fp8 output
+        for k in ("path", "vec", "depth"):
+            assert p[k] == q[k], (k, p, q)
+        assert (p["team"] == 0) == (q["team"] == 0)
+        if q["path"] == rn.PATH_ROWS:
+            assert covers(q, N) and q["depth"] == 0
+            if q["team"] == 0 and q["vec"] > 1 and (N // q["vec"]) % 256 == 0 and N // q["vec"] // 256 <= 8:
+                assert q["threads"] == 256
+        assert q["programs"] == q["grid"] and q["fin_grid"] == 1 and q["fin_threads"] == 1024
+        assert q["workspace_bytes"] == -(-q["grid"] * 4 // 256) * 256
+        assert p["workspace_bytes"] == 0 and p["programs"] == 0
+    # the fp8 output exists only for the layouts without prefetch
+    with rn.plan_override(rn.OP_FWD_FP8, path=rn.PATH_ROWS, vec=8, team=0, threads=256, depth=1, grid=64):
+        with pytest.raises(rn.RMSNormError):
+            plan(rn.OP_FWD_FP8, 4096, 4096)
+    with rn.plan_override(rn.OP_FWD_FP8, path=rn.PATH_ROWS, vec=8, team=0, threads=256, depth=0, grid=64):
+        q = plan(rn.OP_FWD_FP8, 4096, 4096)
+        assert q["grid"] == 64 and q["workspace_bytes"] == 256
 
 
 def test_loop_path_beyond_registers():

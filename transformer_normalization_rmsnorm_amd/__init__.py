@@ -11,7 +11,10 @@ Functions mirror the C entry points:
   rmsnorm_bwd(dy, x, gamma, rstd, eps, offset)          -> (dx, dgamma)
   rmsnorm_fused_add_bwd(dy, dh, h, gamma, rstd, eps, offset) -> (dx, dgamma)
   rmsnorm_bwd_partials / rmsnorm_dgamma_finalize        (the two backward stages)
-  rmsnorm_bwd_workspace_bytes, rmsnorm_query_plan, rmsnorm_set_plan_override
+  rmsnorm_fwd_fp8(x, gamma, scale, eps, offset, amax=)  -> (y8, rstd)   (E4M3 output)
+  rmsnorm_fused_add_fwd_fp8(x, residual, gamma, scale, eps, offset, amax=) -> (y8, h, rstd)
+  rmsnorm_bwd_workspace_bytes, rmsnorm_fwd_fp8_workspace_bytes,
+  rmsnorm_query_plan, rmsnorm_set_plan_override
 """
 
 from __future__ import annotations
@@ -25,7 +28,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(PKG_DIR, "librmsnorm_amd.so")
 
 F32, BF16 = 0, 1
-OP_FWD, OP_FUSED_ADD_FWD, OP_BWD, OP_FUSED_ADD_BWD = 0, 1, 2, 3
+OP_FWD, OP_FUSED_ADD_FWD, OP_BWD, OP_FUSED_ADD_BWD, OP_FWD_FP8, OP_FUSED_ADD_FWD_FP8 = 0, 1, 2, 3, 4, 5
 PATH_ROWS, PATH_LOOP = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
 
@@ -34,6 +37,7 @@ EXPORTS = (
     "rmsnorm_fwd", "rmsnorm_fused_add_fwd", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd",
     "rmsnorm_fused_add_bwd", "rmsnorm_bwd_partials", "rmsnorm_dgamma_finalize", "rmsnorm_query_plan",
     "rmsnorm_set_plan_override", "rmsnorm_status_string", "rmsnorm_last_error", "rmsnorm_version",
+    "rmsnorm_fwd_fp8", "rmsnorm_fused_add_fwd_fp8", "rmsnorm_fwd_fp8_workspace_bytes",
 )
 
 
@@ -44,7 +48,7 @@ class RMSNormError(RuntimeError):
 
 
 # RMSNORM_ABI_VERSION of include/rmsnorm.h that this binding marshals.
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class Plan(ctypes.Structure):
@@ -78,6 +82,9 @@ def _bind(lib):
         "rmsnorm_status_string": [i32],
         "rmsnorm_last_error": [],
         "rmsnorm_version": [],
+        "rmsnorm_fwd_fp8": [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, f, f, i32, vp],
+        "rmsnorm_fused_add_fwd_fp8": [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, f, f, i32, vp],
+        "rmsnorm_fwd_fp8_workspace_bytes": [i64, i64, i32, ctypes.POINTER(sz)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -223,6 +230,80 @@ def rmsnorm_fused_add_fwd(x, residual, gamma, eps: float = 1e-6, offset: float =
         _check(lib.rmsnorm_fused_add_fwd(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(y), _ptr(h_out), _ptr(rstd),
                                          M, N, eps, offset, _dtype_code(x), _stream(dev)), "rmsnorm_fused_add_fwd")
     return y, h_out, rstd
+
+
+def rmsnorm_fwd_fp8_workspace_bytes(M: int, N: int, dtype_code: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    _check(lib.rmsnorm_fwd_fp8_workspace_bytes(M, N, dtype_code, ctypes.byref(out)),
+           "rmsnorm_fwd_fp8_workspace_bytes")
+    return int(out.value)
+
+
+def _fp8_common(x, residual, gamma, scale, eps, offset, amax, y8, h_out, rstd, save_rstd, workspace):
+    torch = _torch()
+    lib = load_library()
+    _require(x, "x")
+    M, N = _rows(x)
+    dev = x.device
+    fused = residual is not None
+    if fused:
+        _require(residual, "residual", x.shape, x.dtype, dev)
+    if gamma is not None:
+        _require(gamma, "gamma", (N,), x.dtype, dev)
+    _require(scale, "scale", None, torch.float32, dev)
+    if scale.numel() != 1:
+        raise ValueError("scale must hold one float32")
+    if amax is not None:
+        _require(amax, "amax", None, torch.float32, dev)
+        if amax.numel() != 1:
+            raise ValueError("amax must hold one float32")
+    if y8 is None:
+        y8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev)
+    _require(y8, "y8", x.shape, None, dev)
+    if y8.element_size() != 1:
+        raise ValueError("y8 must be a one-byte tensor (float8_e4m3fn or uint8)")
+    if fused and h_out is None:
+        h_out = torch.empty_like(x)
+    if fused:
+        _require(h_out, "h_out", x.shape, x.dtype, dev)
+    if rstd is None and save_rstd:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev)
+    if rstd is not None:
+        _require(rstd, "rstd", x.shape[:-1], torch.float32, dev)
+    ws_bytes = 0
+    if amax is not None:
+        if workspace is None:
+            ws_bytes = rmsnorm_fwd_fp8_workspace_bytes(M, N, _dtype_code(x))
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    with _on_device(dev):
+        if fused:
+            _check(lib.rmsnorm_fused_add_fwd_fp8(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(y8), _ptr(h_out),
+                                                 _ptr(rstd), _ptr(scale), _ptr(amax), _ptr(workspace), ws_bytes,
+                                                 M, N, eps, offset, _dtype_code(x), _stream(dev)),
+                   "rmsnorm_fused_add_fwd_fp8")
+        else:
+            _check(lib.rmsnorm_fwd_fp8(_ptr(x), _ptr(gamma), _ptr(y8), _ptr(rstd), _ptr(scale), _ptr(amax),
+                                       _ptr(workspace), ws_bytes, M, N, eps, offset, _dtype_code(x), _stream(dev)),
+                   "rmsnorm_fwd_fp8")
+    return y8, h_out, rstd
+
+
+def rmsnorm_fwd_fp8(x, gamma, scale, eps: float = 1e-6, offset: float = 0.0, *, amax=None, y8=None, rstd=None,
+                    save_rstd: bool = True, workspace=None):
+    """y8 = E4M3(x * rstd * (gamma + offset) * scale) (OCP E4M3, nearest even,
+    saturating at +-448); returns (y8, rstd).  scale: one float32 on the GPU;
+    amax: one float32 on the GPU, updated in place to max(amax, max |y|)."""
+    y8, _, rstd = _fp8_common(x, None, gamma, scale, eps, offset, amax, y8, None, rstd, save_rstd, workspace)
+    return y8, rstd
+
+
+def rmsnorm_fused_add_fwd_fp8(x, residual, gamma, scale, eps: float = 1e-6, offset: float = 0.0, *, amax=None,
+                              y8=None, h_out=None, rstd=None, save_rstd: bool = True, workspace=None):
+    """h = x + residual (rounded to the storage dtype), y8 = E4M3(rmsnorm(h) * scale);
+    returns (y8, h, rstd).  h_out=residual updates the residual stream in place."""
+    return _fp8_common(x, residual, gamma, scale, eps, offset, amax, y8, h_out, rstd, save_rstd, workspace)
 
 
 def rmsnorm_bwd_workspace_bytes(M: int, N: int, dtype_code: int) -> int:

@@ -42,7 +42,7 @@ struct Override {
     bool set = false;
     rmsnorm_plan plan = {};
 };
-Override g_override[4];
+Override g_override[6];
 
 int device_cus(int *cus)
 {
@@ -121,12 +121,28 @@ int launched(hipError_t e, const char *what)
     return ok();
 }
 
+// fp8 output (y holds E4M3 codes): the scale pointer, and the amax target
+// with the workspace for its per-workgroup partials.
+struct Fp8Out {
+    const float *scale;
+    float *amax;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
 int do_fwd(const void *x, const void *r, const void *gamma, void *y, void *h, float *rstd, int64_t M,
-           int64_t N, float eps, float offset, int dtype, hipStream_t stream, bool fused)
+           int64_t N, float eps, float offset, int dtype, hipStream_t stream, bool fused,
+           const Fp8Out *f8 = nullptr)
 {
     int rc = check_common(M, N, dtype, eps, offset);
     if (rc)
         return rc;
+    if (f8 && (!y || !f8->scale))
+        return fail(RMSNORM_EINVAL, "the fp8 forward needs y8 and scale");
+    if (f8 && f8->amax && !aligned(f8->amax, 4))
+        return fail(RMSNORM_EINVAL, "amax not aligned to 4 bytes");
+    if (f8 && !aligned(f8->scale, 4))
+        return fail(RMSNORM_EINVAL, "scale not aligned to 4 bytes");
     if (M == 0)
         return ok();
     if (!x || (fused && (!r || !h)))
@@ -136,22 +152,42 @@ int do_fwd(const void *x, const void *r, const void *gamma, void *y, void *h, fl
     if (!fused && !y && !rstd)
         return fail(RMSNORM_EINVAL, "y and rstd are both null: nothing to compute");
     const size_t eb = (size_t)elem_bytes(dtype);
-    if (!aligned(x, eb) || !aligned(gamma, eb) || !aligned(y, eb) || !aligned(r, eb) || !aligned(h, eb) ||
+    const size_t yb = f8 ? 1 : eb; // E4M3 codes are bytes
+    if (!aligned(x, eb) || !aligned(gamma, eb) || !aligned(y, yb) || !aligned(r, eb) || !aligned(h, eb) ||
         !aligned(rstd, 4))
         return fail(RMSNORM_EINVAL, "pointer not aligned to its element size");
     if (y && (y == x || (gamma && y == gamma) || (fused && (y == r || y == h))))
         return fail(RMSNORM_EINVAL, "y aliases an input");
     if (fused && h == x)
         return fail(RMSNORM_EINVAL, "h_out aliases x (only residual may be overwritten)");
-    const bool vec_ok = aligned(x, 16) && aligned(gamma, 16) && aligned(y, 16) && aligned(r, 16) && aligned(h, 16);
+    // 16-byte accesses of T; the fp8 output then moves 16 / sizeof(T) bytes per access
+    const size_t yv = f8 ? (size_t)vec_elems(dtype) : 16;
+    const bool vec_ok = aligned(x, 16) && aligned(gamma, 16) && aligned(y, yv) && aligned(r, 16) && aligned(h, 16);
     int cus = 0;
     if ((rc = device_cus(&cus)))
         return rc;
+    const int op = f8 ? (fused ? RMSNORM_OP_FUSED_ADD_FWD_FP8 : RMSNORM_OP_FWD_FP8)
+                      : (fused ? RMSNORM_OP_FUSED_ADD_FWD : RMSNORM_OP_FWD);
     rmsnorm_plan p;
-    if ((rc = plan_for(fused ? RMSNORM_OP_FUSED_ADD_FWD : RMSNORM_OP_FWD, M, N, dtype, vec_ok, cus, &p)))
+    if ((rc = plan_for(op, M, N, dtype, vec_ok, cus, &p)))
         return rc;
     FwdArgs a{x, r, gamma, y, h, rstd, M, (int32_t)N, eps, offset};
-    return launched(launch_fwd(dtype, fused, p, a, stream), "forward");
+    if (f8) {
+        a.scale = f8->scale;
+        if (f8->amax) {
+            if (!f8->workspace || f8->workspace_bytes < (size_t)p.workspace_bytes)
+                return fail(RMSNORM_EWORKSPACE, "workspace of %zu bytes given, %lld needed for amax",
+                            f8->workspace ? f8->workspace_bytes : (size_t)0, (long long)p.workspace_bytes);
+            if (!aligned(f8->workspace, 16))
+                return fail(RMSNORM_EINVAL, "workspace not 16-byte aligned");
+            a.amax_part = static_cast<float *>(f8->workspace);
+        }
+    }
+    if ((rc = launched(launch_fwd(dtype, fused, f8 != nullptr, p, a, stream), "forward")))
+        return rc;
+    if (f8 && f8->amax)
+        return launched(launch_amax_finalize(a.amax_part, p.programs, f8->amax, stream), "amax finalize");
+    return ok();
 }
 
 // Shared by the backward entry points.  Writes dx and the partials; returns
@@ -204,7 +240,7 @@ int do_partials(const void *dy, const void *v, const void *gamma, const float *r
         if (rc)
             return fail(rc, "no plan for the rstd recompute");
         FwdArgs fa{v, nullptr, gamma, nullptr, nullptr, tail, M, (int32_t)N, eps, offset};
-        if ((rc = launched(launch_fwd(dtype, false, fp, fa, stream), "rstd recompute")))
+        if ((rc = launched(launch_fwd(dtype, false, false, fp, fa, stream), "rstd recompute")))
             return rc;
         rs = tail;
     }
@@ -263,6 +299,44 @@ int rmsnorm_fused_add_fwd(const void *x, const void *residual, const void *gamma
                           rmsnorm_stream_t stream)
 {
     return do_fwd(x, residual, gamma, y, h_out, rstd, M, N, eps, offset, dtype, stream, true);
+}
+
+int rmsnorm_fwd_fp8(const void *x, const void *gamma, void *y8, float *rstd, const float *scale, float *amax,
+                    void *workspace, size_t workspace_bytes, int64_t M, int64_t N, float eps, float offset,
+                    int dtype, rmsnorm_stream_t stream)
+{
+    const Fp8Out f8{scale, amax, workspace, workspace_bytes};
+    return do_fwd(x, nullptr, gamma, y8, nullptr, rstd, M, N, eps, offset, dtype, stream, false, &f8);
+}
+
+int rmsnorm_fused_add_fwd_fp8(const void *x, const void *residual, const void *gamma, void *y8, void *h_out,
+                              float *rstd, const float *scale, float *amax, void *workspace,
+                              size_t workspace_bytes, int64_t M, int64_t N, float eps, float offset, int dtype,
+                              rmsnorm_stream_t stream)
+{
+    const Fp8Out f8{scale, amax, workspace, workspace_bytes};
+    return do_fwd(x, residual, gamma, y8, h_out, rstd, M, N, eps, offset, dtype, stream, true, &f8);
+}
+
+int rmsnorm_fwd_fp8_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *bytes)
+{
+    if (!bytes)
+        return fail(RMSNORM_EINVAL, "bytes is null");
+    int rc = check_common(M, N, dtype, 0.0f, 0.0f);
+    if (rc)
+        return rc;
+    int cus = 0;
+    if ((rc = device_cus(&cus)))
+        return rc;
+    int64_t need = 0;
+    for (int op : {RMSNORM_OP_FWD_FP8, RMSNORM_OP_FUSED_ADD_FWD_FP8})
+        for (bool vec_ok : {true, false}) {
+            rmsnorm_plan p;
+            if (select_plan(op, M, N, dtype, vec_ok, cus, &p) == RMSNORM_OK && p.workspace_bytes > need)
+                need = p.workspace_bytes;
+        }
+    *bytes = (size_t)need;
+    return ok();
 }
 
 int rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *bytes)
@@ -329,7 +403,7 @@ int rmsnorm_query_plan(int op, int64_t M, int64_t N, int dtype, int vec_ok, int 
         if (rc)
             return rc;
     }
-    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_FUSED_ADD_BWD)
+    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_FUSED_ADD_FWD_FP8)
         return fail(RMSNORM_EINVAL, "op %d unknown", op);
     rmsnorm_plan p;
     int rc = plan_for(op, M, N, dtype, vec_ok != 0, cus, &p);
@@ -341,7 +415,7 @@ int rmsnorm_query_plan(int op, int64_t M, int64_t N, int dtype, int vec_ok, int 
 
 int rmsnorm_set_plan_override(int op, const rmsnorm_plan *plan)
 {
-    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_FUSED_ADD_BWD)
+    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_FUSED_ADD_FWD_FP8)
         return fail(RMSNORM_EINVAL, "op %d unknown", op);
     if (plan == nullptr) {
         g_override[op].set = false;

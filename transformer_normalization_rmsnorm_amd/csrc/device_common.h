@@ -235,6 +235,26 @@ __device__ __forceinline__ float team_sum(float v)
     return v;
 }
 
+// Maximum over an aligned group of TEAM lanes, by the same exchanges as team_sum.
+template <int TEAM>
+__device__ __forceinline__ float team_max(float v)
+{
+    static_assert(TEAM == 8 || TEAM == 16 || TEAM == 32 || TEAM == 64, "team size");
+    v = fmaxf(v, dpp<kDppQuadXor1>(v));
+    v = fmaxf(v, dpp<kDppQuadXor2>(v));
+    v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+    if constexpr (TEAM >= 16)
+        v = fmaxf(v, dpp<kDppRowMirror>(v));
+    if constexpr (TEAM >= 32)
+        v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), kSwizzleXor16)));
+    if constexpr (TEAM == 64) {
+        const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+        const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+        v = fmaxf(lo, hi);
+    }
+    return v;
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences global
 // memory, which makes the compiler wait for every outstanding global load
 // (s_waitcnt vmcnt(0)) and so drains the rows a team has in flight; the
@@ -263,6 +283,59 @@ __device__ __forceinline__ float block_sum(float v, float *slot, int threads)
     for (int i = 1; i < nw; ++i)
         s += slot[i];
     return s;
+}
+
+// Maximum over the whole workgroup (as block_sum; `slot` holds 16 floats and
+// must not be in use by a concurrent block_sum).
+__device__ __forceinline__ float block_max(float v, float *slot, int threads)
+{
+    v = team_max<64>(v);
+    const int nw = threads >> 6;
+    if (nw == 1)
+        return v;
+    if ((threadIdx.x & 63) == 0)
+        slot[threadIdx.x >> 6] = v;
+    lds_barrier();
+    float s = slot[0];
+    for (int i = 1; i < nw; ++i)
+        s = fmaxf(s, slot[i]);
+    return s;
+}
+
+// ---- fp8 output -----------------------------------------------------------
+
+// OCP E4M3 ("FN") codes of V float32 values times `scale`, nearest even,
+// saturating at +-448, written with one store of V bytes (nontemporal like the
+// other row outputs).  The gfx950 pack conversion rounds to nearest even but
+// turns magnitudes past the format's range into NaN, so values are clamped to
+// +-448 (the largest finite code) first.  `am` accumulates max |f| (before
+// scaling).
+template <int V>
+__device__ __forceinline__ void store_e4m3(uint8_t *p, const float (&f)[V], float scale, float &am)
+{
+    float t[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        am = fmaxf(am, fabsf(f[e]));
+        t[e] = fminf(fmaxf(f[e] * scale, -448.0f), 448.0f);
+    }
+    if constexpr (V == 1) {
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], 0.0f, 0, false);
+        __builtin_nontemporal_store((uint8_t)(w & 0xff), p);
+    } else if constexpr (V == 4) {
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false); // bytes 0, 1
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], w, true);       // bytes 2, 3
+        __builtin_nontemporal_store((uint32_t)w, reinterpret_cast<uint32_t *>(p));
+    } else {
+        static_assert(V == 8, "fp8 store of 1, 4 or 8 values");
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], lo, true);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(t[4], t[5], 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(t[6], t[7], hi, true);
+        typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t u = {(unsigned)lo, (unsigned)hi};
+        __builtin_nontemporal_store(u, reinterpret_cast<u32x2_t *>(p));
+    }
 }
 
 // ---- row pipeline ---------------------------------------------------------

@@ -24,6 +24,10 @@ struct FwdArgs {
     float offset;
     int32_t threads; // workgroup size of the launch
     int64_t grid;    // workgroups of the launch
+    // fp8 output only: y holds E4M3 codes of y * (*scale); each workgroup
+    // writes max |y| to amax_part[blockIdx.x] when amax_part is not null
+    const float *scale = nullptr;
+    float *amax_part = nullptr;
 };
 
 struct BwdArgs {
@@ -130,8 +134,16 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
 bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus, bool keep_grid);
 int64_t bwd_workspace_bytes(int64_t programs, int64_t M, int64_t N);
 
-// Kernel launchers (fwd_kernels.hip, bwd_kernels.hip).
-hipError_t launch_fwd(int dtype, bool fused, const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s);
+// Ops with fp8 output (the forward with y in E4M3).
+inline bool is_fp8_op(int op) { return op == RMSNORM_OP_FWD_FP8 || op == RMSNORM_OP_FUSED_ADD_FWD_FP8; }
+
+// amax finalizer: one workgroup folds the per-workgroup maxima.
+constexpr int kAmaxThreads = 1024;
+
+// Kernel launchers (fwd_kernels.hip, bwd_kernels.hip).  fp8: y is E4M3 (only
+// the layouts without prefetch are compiled for it).
+hipError_t launch_fwd(int dtype, bool fused, bool fp8, const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s);
+hipError_t launch_amax_finalize(const float *part, int64_t programs, float *amax, hipStream_t s);
 hipError_t launch_bwd(int dtype, bool fused, const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s);
 hipError_t launch_finalize(int dtype, const float *partials, int64_t programs, int64_t ld, int64_t N,
                            void *dgamma, hipStream_t s);
