@@ -52,10 +52,14 @@ def _bind(lib):
     lib.oracle_e4m3_decode.argtypes = [c_vp, c_i64, c_dp]
     lib.oracle_fwd_fp8.argtypes = [ctypes.c_int, c_vp, c_vp, c_i64, c_i64, c_f, c_f, c_f, ctypes.c_double,
                                    c_vp, c_vp, c_vp, c_dp, c_dp]
+    lib.oracle_ln_fwd.argtypes = [ctypes.c_int, c_vp, c_vp, c_vp, c_i64, c_i64, c_f, c_f, c_dp, c_dp, c_dp]
+    lib.oracle_ln_bwd.argtypes = [ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_f, c_f, c_dp, c_dp, c_dp,
+                                  c_dp]
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     lib.oracle_set_num_threads.restype = None
     for f in (lib.oracle_fwd, lib.oracle_fused_add_fwd, lib.oracle_bwd, lib.oracle_round,
-              lib.oracle_num_threads, lib.oracle_e4m3_encode, lib.oracle_e4m3_decode, lib.oracle_fwd_fp8):
+              lib.oracle_num_threads, lib.oracle_e4m3_encode, lib.oracle_e4m3_decode, lib.oracle_fwd_fp8,
+              lib.oracle_ln_fwd, lib.oracle_ln_bwd):
         f.restype = ctypes.c_int
     return lib
 
@@ -196,3 +200,43 @@ def fwd_fp8(v, gamma, dtype: str, eps: float, offset: float, scale: float, *, to
     _check(lib.oracle_fwd_fp8(DTYPE_CODE[dtype], _ptr(v), _ptr(gamma), M, N, eps, offset, scale, tol,
                               _ptr(code), _ptr(lo), _ptr(hi), _ptr(rstd), _ptr(amax)), "oracle_fwd_fp8")
     return {"code": code, "code_lo": lo, "code_hi": hi, "rstd64": rstd, "amax64": float(amax[0])}
+
+
+def ln_fwd(v, gamma, beta, dtype: str, eps: float, offset: float, *, want_y: bool = True, lib=None):
+    """LayerNorm forward of rows of v; returns (y64 or None, mean64, rstd64).
+    gamma None: w = 1 (offset 0); beta None: no bias."""
+    lib = lib or load()
+    v = _storage(v, dtype)
+    gamma = None if gamma is None else _storage(gamma, dtype)
+    beta = None if beta is None else _storage(beta, dtype)
+    M, N = v.shape
+    y = np.empty((M, N), np.float64) if want_y else None
+    mean = np.empty(M, np.float64)
+    rstd = np.empty(M, np.float64)
+    _check(lib.oracle_ln_fwd(DTYPE_CODE[dtype], _ptr(v), _ptr(gamma), _ptr(beta), M, N, eps, offset, _ptr(y),
+                             _ptr(mean), _ptr(rstd)), "oracle_ln_fwd")
+    return y, mean, rstd
+
+
+def ln_bwd(dy, v, gamma, dtype: str, eps: float, offset: float, *, dh=None, want_dx: bool = True,
+           want_dgamma: bool = True, want_dbeta: bool = True, lib=None) -> Dict[str, np.ndarray]:
+    """LayerNorm backward of the forward of v (h for fused-add; dh is added to dx).
+
+    Returns dx64 [M, N], dgamma64 [N] (None without gamma), dbeta64 [N], and
+    stats64 [M, 4] = (mean g, mean g*xhat, mean |g|, mean |g*xhat|) per row.
+    """
+    lib = lib or load()
+    dy = _storage(dy, dtype)
+    v = _storage(v, dtype)
+    gamma = None if gamma is None else _storage(gamma, dtype)
+    want_dgamma = want_dgamma and gamma is not None
+    if dh is not None:
+        dh = _storage(dh, dtype)
+    M, N = v.shape
+    dx = np.empty((M, N), np.float64) if want_dx else None
+    dg = np.empty(N, np.float64) if want_dgamma else None
+    db = np.empty(N, np.float64) if want_dbeta else None
+    st = np.empty((M, 4), np.float64)
+    _check(lib.oracle_ln_bwd(DTYPE_CODE[dtype], _ptr(dy), _ptr(v), _ptr(gamma), _ptr(dh), M, N, eps, offset,
+                             _ptr(dx), _ptr(dg), _ptr(db), _ptr(st)), "oracle_ln_bwd")
+    return {"dx64": dx, "dgamma64": dg, "dbeta64": db, "stats64": st}

@@ -47,6 +47,19 @@
  * 3 mantissa bits, no infinities, largest finite 448 = 1.75 * 2^8, smallest
  * normal 2^-6, subnormals m * 2^-9 (m = 1..7); codes 0x7F / 0xFF are NaN.
  *
+ * LayerNorm on the same machinery (TransformerEngine PR #583: matching tuned
+ * configurations are registered for LayerNorm).  The page gives no formula;
+ * the standard LayerNorm is taken, with the same eps, offset and fused-add
+ * conventions as RMSNorm above and an optional bias beta:
+ *       mu_i   = (1/N) sum_j v_ij
+ *       var_i  = (1/N) sum_j (v_ij - mu_i)^2
+ *       rstd_i = 1 / sqrt(var_i + eps)
+ *       xhat_ij = (v_ij - mu_i) * rstd_i
+ *       y_ij   = xhat_ij * (gamma_j + offset) + beta_j
+ *   backward (chain rule), g = dy * w:
+ *       dx_ij  = rstd_i * (g_ij - mean_j(g) - xhat_ij * mean_j(g * xhat))  [+ dh_ij]
+ *       dgamma_j = sum_i dy_ij * xhat_ij,   dbeta_j = sum_i dy_ij
+ *
  * Rounding to a storage type is round-to-nearest, ties to even (FlyDSL PR #855,
  * "512-thread vec8 fast path": software RNE / hardware conversion).
  *
@@ -382,5 +395,128 @@ int oracle_fwd_fp8(int dt, const void *v, const void *gamma, int64_t M, int64_t 
     }
     if (amax64)
         *amax64 = amax;
+    return ORACLE_OK;
+}
+
+/* ---- LayerNorm ------------------------------------------------------------ */
+
+/* mu_i and rstd_i = 1 / sqrt(var_i + eps) of row i (two passes over the row) */
+static void ln_row_stats(int dt, const void *v, int64_t row, int64_t N, double eps, double *mu, double *rstd)
+{
+    double s = 0.0;
+    for (int64_t j = 0; j < N; ++j)
+        s += load_elem(dt, v, row * N + j);
+    const double m = s / (double)N;
+    double q = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+        const double d = load_elem(dt, v, row * N + j) - m;
+        q += d * d;
+    }
+    *mu = m;
+    *rstd = 1.0 / sqrt(q / (double)N + eps);
+}
+
+/* LayerNorm forward.  beta NULL means no bias; gamma NULL means w = 1 (offset
+ * 0).  y64 [M, N], mean64 [M], rstd64 [M] may each be NULL. */
+int oracle_ln_fwd(int dt, const void *v, const void *gamma, const void *beta, int64_t M, int64_t N, float eps,
+                  float offset, double *y64, double *mean64, double *rstd64)
+{
+    if (!dtype_ok(dt) || !v || M < 0 || N <= 0 || (!gamma && offset != 0.0f))
+        return ORACLE_EINVAL;
+    const double e = (double)eps, off = (double)offset;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        double mu, rstd;
+        ln_row_stats(dt, v, i, N, e, &mu, &rstd);
+        if (mean64)
+            mean64[i] = mu;
+        if (rstd64)
+            rstd64[i] = rstd;
+        if (y64) {
+            for (int64_t j = 0; j < N; ++j) {
+                const double xhat = (load_elem(dt, v, i * N + j) - mu) * rstd;
+                y64[i * N + j] = xhat * scale_w(dt, gamma, j, off) + (beta ? load_elem(dt, beta, j) : 0.0);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* LayerNorm backward of the forward of v (h for fused-add; dh is then added
+ * to dx).  Outputs (each may be NULL): dx64 [M, N]; dgamma64 [N] (needs
+ * gamma); dbeta64 [N]; and per row, for the tests' tolerance floor,
+ * c1 = mean_j(g), c2 = mean_j(g * xhat), s1 = mean_j |g|, s2 = mean_j |g * xhat|
+ * (stats64 [M, 4]). */
+int oracle_ln_bwd(int dt, const void *dy, const void *v, const void *gamma, const void *dh, int64_t M, int64_t N,
+                  float eps, float offset, double *dx64, double *dgamma64, double *dbeta64, double *stats64)
+{
+    if (!dtype_ok(dt) || !dy || !v || M < 0 || N <= 0 || (!gamma && (offset != 0.0f || dgamma64)))
+        return ORACLE_EINVAL;
+    const double e = (double)eps, off = (double)offset;
+    double *mu = (double *)malloc((size_t)(M > 0 ? M : 1) * sizeof(double));
+    double *rs = (double *)malloc((size_t)(M > 0 ? M : 1) * sizeof(double));
+    if (!mu || !rs) {
+        free(mu);
+        free(rs);
+        return ORACLE_ENOMEM;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        ln_row_stats(dt, v, i, N, e, &mu[i], &rs[i]);
+        double sg = 0.0, sgx = 0.0, ag = 0.0, agx = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            const double g = load_elem(dt, dy, i * N + j) * scale_w(dt, gamma, j, off);
+            const double xhat = (load_elem(dt, v, i * N + j) - mu[i]) * rs[i];
+            sg += g;
+            sgx += g * xhat;
+            ag += fabs(g);
+            agx += fabs(g * xhat);
+        }
+        const double c1 = sg / (double)N, c2 = sgx / (double)N;
+        if (stats64) {
+            stats64[4 * i + 0] = c1;
+            stats64[4 * i + 1] = c2;
+            stats64[4 * i + 2] = ag / (double)N;
+            stats64[4 * i + 3] = agx / (double)N;
+        }
+        if (dx64) {
+            for (int64_t j = 0; j < N; ++j) {
+                const double g = load_elem(dt, dy, i * N + j) * scale_w(dt, gamma, j, off);
+                const double xhat = (load_elem(dt, v, i * N + j) - mu[i]) * rs[i];
+                double d = rs[i] * (g - c1 - xhat * c2);
+                if (dh)
+                    d += load_elem(dt, dh, i * N + j);
+                dx64[i * N + j] = d;
+            }
+        }
+    }
+    /* columns, each summed over the rows in row order */
+    if (dgamma64 || dbeta64) {
+#pragma omp parallel
+        {
+            int64_t nt = 1, t = 0;
+#ifdef _OPENMP
+            nt = omp_get_num_threads();
+            t = omp_get_thread_num();
+#endif
+            int64_t j0 = N * t / nt, j1 = N * (t + 1) / nt;
+            for (int64_t j = j0; j < j1; ++j) {
+                if (dgamma64)
+                    dgamma64[j] = 0.0;
+                if (dbeta64)
+                    dbeta64[j] = 0.0;
+            }
+            for (int64_t i = 0; i < M; ++i)
+                for (int64_t j = j0; j < j1; ++j) {
+                    const double d = load_elem(dt, dy, i * N + j);
+                    if (dgamma64)
+                        dgamma64[j] += d * ((load_elem(dt, v, i * N + j) - mu[i]) * rs[i]);
+                    if (dbeta64)
+                        dbeta64[j] += d;
+                }
+        }
+    }
+    free(mu);
+    free(rs);
     return ORACLE_OK;
 }

@@ -20,6 +20,10 @@ mismatch.  What pins what:
   e4m3_brute_force     fp8 E4M3 encoder vs an exhaustive nearest-code search
   e4m3_torch           fp8 E4M3 encoder vs torch's float8_e4m3fn cast; code round trip
   fp8_forward          fp8-output forward = plain forward then the encoder; amax; brackets
+  ln_finite_differences  LayerNorm backward (dx, dgamma, dbeta, d/dresidual) vs central differences
+  ln_identities        LayerNorm: sum dx = 0, sum xhat dx = N c2 rstd^3 eps, normalised mean / mean square
+  ln_closed_forms      LayerNorm: N = 1, constant rows, shift invariance, offset, no gamma/beta
+  ln_torch_fp64        torch.nn.functional.layer_norm in float64 with autograd
 """
 
 from __future__ import annotations
@@ -368,6 +372,154 @@ def fp8_forward(lib):
         assert np.all(np.abs(np.abs(dec(out["code"])).ravel() - ts) <= nearest)
 
 
+def _ln_loss_grads(x, gamma, beta, dy, eps, off, lib, r=None):
+    """Central differences of L = sum dy * y (LayerNorm; fused: y of h = x + r)."""
+    def loss(xx, gg, bb, rr):
+        v = xx if rr is None else xx + rr
+        y, _, _ = oracle.ln_fwd(v, gg, bb, "f64", eps, off, lib=lib)
+        return float(np.sum(dy * y))
+
+    def central(arr, idx, f):
+        h = 1e-6 * max(1.0, abs(arr[idx]))
+        a = arr.copy(); a[idx] += h
+        b = arr.copy(); b[idx] -= h
+        return (f(a) - f(b)) / (2 * h)
+
+    dxn = np.zeros_like(x)
+    for idx in np.ndindex(*x.shape):
+        dxn[idx] = central(x, idx, lambda a: loss(a, gamma, beta, r))
+    dgn = np.array([central(gamma, (j,), lambda a: loss(x, a, beta, r)) for j in range(gamma.size)])
+    dbn = np.array([central(beta, (j,), lambda a: loss(x, gamma, a, r)) for j in range(beta.size)])
+    drn = None
+    if r is not None:
+        drn = np.zeros_like(r)
+        for idx in np.ndindex(*r.shape):
+            drn[idx] = central(r, idx, lambda a: loss(x, gamma, beta, a))
+    return dxn, dgn, dbn, drn
+
+
+def ln_finite_differences(lib):
+    """LayerNorm backward (dx, dgamma, dbeta, d/dresidual) against fp64 central differences."""
+    rng = np.random.default_rng(37)
+    for M, N in ((1, 2), (2, 3), (3, 7), (2, 16)):
+        for eps in (1e-6, 0.5):
+            for off in (0.0, 1.0):
+                x = rng.standard_normal((M, N))
+                gamma = rng.standard_normal(N) * 0.5 + (0.0 if off else 1.0)
+                beta = rng.standard_normal(N)
+                dy = rng.standard_normal((M, N))
+                out = oracle.ln_bwd(dy, x, gamma, "f64", eps, off, lib=lib)
+                dxn, dgn, dbn, _ = _ln_loss_grads(x, gamma, beta, dy, eps, off, lib)
+                rstd = oracle.ln_fwd(x, gamma, beta, "f64", eps, off, want_y=False, lib=lib)[2]
+                st = out["stats64"]
+                w = gamma + off
+                xhat = (x - x.mean(1, keepdims=True)) * rstd[:, None]
+                s = rstd[:, None] * (np.abs(dy * w) + st[:, 2:3] + np.abs(xhat) * (np.abs(st[:, 1:2]) + st[:, 3:4]))
+                assert np.all(np.abs(out["dx64"] - dxn) <= 1e-7 * np.maximum(np.abs(out["dx64"]), s)), (M, N, eps, off)
+                np.testing.assert_allclose(out["dgamma64"], dgn, rtol=1e-6, atol=1e-7)
+                np.testing.assert_allclose(out["dbeta64"], dbn, rtol=1e-6, atol=1e-7)
+                # fused: the residual's gradient equals x's
+                r = rng.standard_normal((M, N))
+                h = x + r
+                dh = rng.standard_normal((M, N))
+                fo = oracle.ln_bwd(dy, h, gamma, "f64", eps, off, dh=dh, lib=lib)
+                _, _, _, drn = _ln_loss_grads(x, gamma, beta, dy, eps, off, lib, r=r)
+                np.testing.assert_allclose(fo["dx64"] - dh, drn, rtol=1e-5, atol=1e-6)
+
+
+def ln_identities(lib):
+    """sum_j dx_j = 0; sum_j xhat_j dx_j = N * mean(g xhat) * rstd^3 * eps; the
+    normalised output has mean 0 and mean square var / (var + eps)."""
+    rng = np.random.default_rng(41)
+    M, N = 6, 33
+    x = rng.standard_normal((M, N)) * 3 + 1.5
+    gamma = rng.standard_normal(N) * 0.3 + 1
+    beta = rng.standard_normal(N)
+    dy = rng.standard_normal((M, N))
+    for eps in (1e-6, 0.25):
+        y, mu, rstd = oracle.ln_fwd(x, gamma, beta, "f64", eps, 0.0, lib=lib)
+        z = (y - beta) / gamma
+        np.testing.assert_allclose(z.mean(1), 0, atol=1e-14)
+        var = ((x - x.mean(1, keepdims=True)) ** 2).mean(1)
+        np.testing.assert_allclose((z ** 2).mean(1), var / (var + eps), rtol=1e-13)
+        out = oracle.ln_bwd(dy, x, gamma, "f64", eps, 0.0, lib=lib)
+        dx = out["dx64"]
+        scale = np.abs(dx).sum(1)
+        assert np.all(np.abs(dx.sum(1)) <= 1e-13 * scale)
+        xhat = (x - mu[:, None]) * rstd[:, None]
+        want = N * out["stats64"][:, 1] * rstd ** 3 * eps
+        np.testing.assert_allclose((xhat * dx).sum(1), want, rtol=1e-9, atol=1e-13 * scale.max())
+
+
+def ln_closed_forms(lib):
+    """N = 1 (y = beta, dx = 0, dbeta = dy, dgamma = 0); a constant row
+    (y = beta, dx = rstd (g - mean g) with rstd = 1/sqrt(eps) = 4); shift
+    invariance; (gamma, offset) = (gamma + offset, 0); no gamma / beta."""
+    rng = np.random.default_rng(43)
+    x = rng.standard_normal((5, 1))
+    g, b = np.array([1.7]), np.array([-0.3])
+    dy = rng.standard_normal((5, 1))
+    y, _, _ = oracle.ln_fwd(x, g, b, "f64", 1e-6, 0.0, lib=lib)
+    np.testing.assert_array_equal(y, np.full((5, 1), -0.3))
+    out = oracle.ln_bwd(dy, x, g, "f64", 1e-6, 0.0, lib=lib)
+    np.testing.assert_array_equal(out["dx64"], 0)
+    np.testing.assert_array_equal(out["dgamma64"], 0)
+    np.testing.assert_allclose(out["dbeta64"], dy.sum(0), rtol=1e-15)
+    N = 9
+    xc = np.full((2, N), 2.5)
+    gamma = rng.standard_normal(N)
+    beta = rng.standard_normal(N)
+    dyc = rng.standard_normal((2, N))
+    eps = 0.0625  # exact in float32: rstd = 1/sqrt(eps) = 4
+    y, mu, rstd = oracle.ln_fwd(xc, gamma, beta, "f64", eps, 0.0, lib=lib)
+    np.testing.assert_allclose(y, np.broadcast_to(beta, y.shape), rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(rstd, 4.0)
+    dx = oracle.ln_bwd(dyc, xc, gamma, "f64", eps, 0.0, lib=lib)["dx64"]
+    gg = dyc * gamma
+    np.testing.assert_allclose(dx, 4.0 * (gg - gg.mean(1, keepdims=True)), rtol=1e-13, atol=1e-14)
+    xs = rng.standard_normal((3, 20))
+    gs, bs, dys = rng.standard_normal(20), rng.standard_normal(20), rng.standard_normal((3, 20))
+    y0, _, _ = oracle.ln_fwd(xs, gs, bs, "f64", 1e-3, 0.0, lib=lib)
+    y1, _, _ = oracle.ln_fwd(xs + 7.25, gs, bs, "f64", 1e-3, 0.0, lib=lib)
+    np.testing.assert_allclose(y1, y0, rtol=1e-12, atol=1e-12)
+    y2, _, _ = oracle.ln_fwd(xs, gs - 1.0, bs, "f64", 1e-3, 1.0, lib=lib)
+    np.testing.assert_allclose(y2, y0, rtol=1e-14, atol=1e-15)
+    o0 = oracle.ln_bwd(dys, xs, gs, "f64", 1e-3, 0.0, lib=lib)
+    o2 = oracle.ln_bwd(dys, xs, gs - 1.0, "f64", 1e-3, 1.0, lib=lib)
+    np.testing.assert_allclose(o2["dx64"], o0["dx64"], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(o2["dgamma64"], o0["dgamma64"], rtol=1e-14)
+    yn, _, _ = oracle.ln_fwd(xs, None, None, "f64", 1e-3, 0.0, lib=lib)
+    yo, _, _ = oracle.ln_fwd(xs, np.ones(20), np.zeros(20), "f64", 1e-3, 0.0, lib=lib)
+    np.testing.assert_array_equal(yn, yo)
+    on = oracle.ln_bwd(dys, xs, None, "f64", 1e-3, 0.0, lib=lib)
+    oo = oracle.ln_bwd(dys, xs, np.ones(20), "f64", 1e-3, 0.0, lib=lib)
+    np.testing.assert_array_equal(on["dx64"], oo["dx64"])
+    assert on["dgamma64"] is None
+
+
+def ln_torch_fp64(lib):
+    """torch.nn.functional.layer_norm in float64 with autograd."""
+    import torch
+
+    rng = np.random.default_rng(47)
+    for M, N, eps, off in ((4, 64, 1e-6, 0.0), (3, 129, 0.1, 1.0), (2, 1000, 1e-5, 0.0)):
+        x = rng.standard_normal((M, N)) * 2 - 0.5
+        gamma = rng.standard_normal(N) * 0.2 + (0.0 if off else 1.0)
+        beta = rng.standard_normal(N)
+        dy = rng.standard_normal((M, N))
+        y, _, _ = oracle.ln_fwd(x, gamma, beta, "f64", eps, off, lib=lib)
+        out = oracle.ln_bwd(dy, x, gamma, "f64", eps, off, lib=lib)
+        tx = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+        tw = torch.tensor(gamma + _f32(off), dtype=torch.float64, requires_grad=True)
+        tb = torch.tensor(beta, dtype=torch.float64, requires_grad=True)
+        ty = torch.nn.functional.layer_norm(tx, (N,), weight=tw, bias=tb, eps=_f32(eps))
+        ty.backward(torch.tensor(dy, dtype=torch.float64))
+        np.testing.assert_allclose(y, ty.detach().numpy(), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(out["dx64"], tx.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(out["dgamma64"], tw.grad.numpy(), rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(out["dbeta64"], tb.grad.numpy(), rtol=1e-13, atol=1e-13)
+
+
 def load_golden(path: str = GOLDEN):
     cases, cur = {}, None
     with open(path) as f:
@@ -402,6 +554,27 @@ def golden(lib):
             assert list(map(int, out["code"].ravel())) == c["codes"], (name, [hex(int(b)) for b in out["code"].ravel()])
             np.testing.assert_allclose(out["rstd64"], c["rstd"], rtol=1e-15, err_msg=name)
             np.testing.assert_allclose(out["amax64"], c["amax"][0], rtol=1e-15, err_msg=name)
+            continue
+        if "mean" in c:  # LayerNorm
+            N = int(c["N"][0])
+            eps, off = c["eps"][0], c["offset"][0]
+            x = np.array(c["x"]).reshape(-1, N)
+            gamma, beta = np.array(c["gamma"]), np.array(c["beta"])
+            dy = np.array(c["dy"]).reshape(-1, N)
+            dh = None
+            if "r" in c:
+                h, _, _ = oracle.fused_add_fwd(x, np.array(c["r"]).reshape(-1, N), gamma, "f64", eps, off, lib=lib)
+                np.testing.assert_allclose(h.ravel(), c["h"], rtol=0, atol=0)
+                x = h
+                dh = np.array(c["dh"]).reshape(-1, N)
+            y, mu, rstd = oracle.ln_fwd(x, gamma, beta, "f64", eps, off, lib=lib)
+            out = oracle.ln_bwd(dy, x, gamma, "f64", eps, off, dh=dh, lib=lib)
+            np.testing.assert_allclose(mu, c["mean"], rtol=1e-15, atol=1e-16, err_msg=name)
+            np.testing.assert_allclose(rstd, c["rstd"], rtol=1e-15, err_msg=name)
+            np.testing.assert_allclose(y.ravel(), c["y"], rtol=1e-14, atol=1e-15, err_msg=name)
+            np.testing.assert_allclose(out["dx64"].ravel(), c["dx"], rtol=1e-14, atol=1e-15, err_msg=name)
+            np.testing.assert_allclose(out["dgamma64"], c["dgamma"], rtol=1e-14, atol=1e-15, err_msg=name)
+            np.testing.assert_allclose(out["dbeta64"], c["dbeta"], rtol=0, atol=0, err_msg=name)
             continue
         N = int(c["N"][0])
         eps, off = c["eps"][0], c["offset"][0]
@@ -550,4 +723,5 @@ ALL_PINS = [
     finite_differences, rms_invariant, orthogonality, closed_form_n1, constant_row, scale_invariance,
     offset_equivalence, fused_reductions, torch_fp64, golden, storage_widening, rounding, non_affine,
     e4m3_brute_force, e4m3_torch, fp8_forward,
+    ln_finite_differences, ln_identities, ln_closed_forms, ln_torch_fp64,
 ]

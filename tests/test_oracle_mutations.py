@@ -46,6 +46,19 @@ MUTATIONS = [
     ("fp8_scale_dropped", "const double t = y * sc;", "const double t = y;", False),
     ("fp8_bracket_swapped", "const double lo = t < 0 ? t * (1.0 + tol) : t * (1.0 - tol);",
      "const double lo = t < 0 ? t * (1.0 - tol) : t * (1.0 + tol);", False),
+    # LayerNorm
+    ("ln_mean_dropped", "const double m = s / (double)N;", "const double m = 0.0 * s;", False),
+    ("ln_var_divisor", "*rstd = 1.0 / sqrt(q / (double)N + eps);", "*rstd = 1.0 / sqrt(q / (double)(N > 1 ? N - 1 : N) + eps);", False),
+    ("ln_beta_dropped", "+ (beta ? load_elem(dt, beta, j) : 0.0);", "+ 0.0;", False),
+    ("ln_c1_dropped", "double d = rs[i] * (g - c1 - xhat * c2);", "double d = rs[i] * (g - xhat * c2);", False),
+    ("ln_c2_sign", "double d = rs[i] * (g - c1 - xhat * c2);", "double d = rs[i] * (g - c1 + xhat * c2);", False),
+    ("ln_dbeta_scaled", "dbeta64[j] += d;", "dbeta64[j] += d * scale_w(dt, gamma, j, off);", False),
+    ("ln_dgamma_unnormalised", "dgamma64[j] += d * ((load_elem(dt, v, i * N + j) - mu[i]) * rs[i]);",
+     "dgamma64[j] += d * (load_elem(dt, v, i * N + j) - mu[i]);", False),
+    ("ln_wrong_row_mean", "const double xhat = (load_elem(dt, v, i * N + j) - mu[i]) * rs[i];",
+     "const double xhat = (load_elem(dt, v, i * N + j) - mu[0]) * rs[i];", True),
+    ("ln_dh_sign", "double d = rs[i] * (g - c1 - xhat * c2);\n                if (dh)\n                    d += load_elem",
+     "double d = rs[i] * (g - c1 - xhat * c2);\n                if (dh)\n                    d -= load_elem", False),
 ]
 
 # fast pins first so a mutant usually fails within a second
@@ -55,6 +68,7 @@ PIN_ORDER = [
     oracle_pins.orthogonality, oracle_pins.offset_equivalence, oracle_pins.scale_invariance,
     oracle_pins.fused_reductions, oracle_pins.storage_widening, oracle_pins.rounding, oracle_pins.torch_fp64,
     oracle_pins.non_affine, oracle_pins.finite_differences,
+    oracle_pins.ln_closed_forms, oracle_pins.ln_identities, oracle_pins.ln_torch_fp64, oracle_pins.ln_finite_differences,
 ]
 
 
