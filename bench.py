@@ -86,13 +86,18 @@ class Sets:
         self.dt = rn.BF16 if w.dtype == "bf16" else rn.F32
         self.ws_bytes = rn.rmsnorm_bwd_workspace_bytes(M, N, self.dt)
         self.ws8_bytes = rn.rmsnorm_fwd_fp8_workspace_bytes(M, N, self.dt)
+        self.ws_ln_bytes = rn.layernorm_bwd_workspace_bytes(M, N, self.dt)
         self.sets = []
         for _ in range(n_sets):
             s = {
                 "x": base["x"].clone(), "dy": base["dy"].clone(), "gamma": base["gamma"].clone(),
                 "y": torch.empty(M, N, dtype=td, device=dev), "rstd": torch.empty(M, dtype=torch.float32, device=dev),
                 "dx": torch.empty(M, N, dtype=td, device=dev), "dg": torch.empty(N, dtype=td, device=dev),
-                "ws": torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev),
+                "ws": torch.empty(max(self.ws_bytes, self.ws_ln_bytes, 16), dtype=torch.uint8, device=dev),
+                # LayerNorm: bias (any values: timing only), saved statistics, dbeta
+                "beta": base["gamma"].clone(), "mean": torch.empty(M, dtype=torch.float32, device=dev),
+                "lrstd": torch.empty(M, dtype=torch.float32, device=dev),
+                "db": torch.empty(N, dtype=td, device=dev),
                 # fp8-output forward: E4M3 codes, scale, amax and its partials
                 "y8": torch.empty(M, N, dtype=torch.uint8, device=dev),
                 "scale": torch.full((1,), 16.0, dtype=torch.float32, device=dev),
@@ -138,6 +143,32 @@ class Sets:
                                    s["scale"].data_ptr(), s["amax"].data_ptr(), s["ws8"].data_ptr(), self.ws8_bytes,
                                    w.M, w.N, w.eps, w.offset, self.dt, st)
         self._check(rc, "fwd_fp8")
+
+    def ln_fwd(self, i, st):
+        s, w, L = self.sets[i % len(self.sets)], self.w, self.lib
+        if w.fused:
+            rc = L.layernorm_fused_add_fwd(s["x"].data_ptr(), s["residual"].data_ptr(), s["gamma"].data_ptr(),
+                                           s["beta"].data_ptr(), s["y"].data_ptr(), s["h"].data_ptr(),
+                                           s["mean"].data_ptr(), s["lrstd"].data_ptr(), w.M, w.N, w.eps, w.offset,
+                                           self.dt, st)
+        else:
+            rc = L.layernorm_fwd(s["x"].data_ptr(), s["gamma"].data_ptr(), s["beta"].data_ptr(), s["y"].data_ptr(),
+                                 s["mean"].data_ptr(), s["lrstd"].data_ptr(), w.M, w.N, w.eps, w.offset, self.dt, st)
+        self._check(rc, "ln_fwd")
+
+    def ln_bwd(self, i, st):
+        s, w, L = self.sets[i % len(self.sets)], self.w, self.lib
+        nb = s["ws"].numel()
+        if w.fused:
+            rc = L.layernorm_fused_add_bwd(s["dy"].data_ptr(), s["dh"].data_ptr(), s["h"].data_ptr(),
+                                           s["gamma"].data_ptr(), s["mean"].data_ptr(), s["lrstd"].data_ptr(),
+                                           s["dh"].data_ptr(), s["dg"].data_ptr(), s["db"].data_ptr(),
+                                           s["ws"].data_ptr(), nb, w.M, w.N, w.eps, w.offset, self.dt, st)
+        else:
+            rc = L.layernorm_bwd(s["dy"].data_ptr(), s["x"].data_ptr(), s["gamma"].data_ptr(), s["mean"].data_ptr(),
+                                 s["lrstd"].data_ptr(), s["dx"].data_ptr(), s["dg"].data_ptr(), s["db"].data_ptr(),
+                                 s["ws"].data_ptr(), nb, w.M, w.N, w.eps, w.offset, self.dt, st)
+        self._check(rc, "ln_bwd")
 
     def bwd(self, i, st):
         s, w, L = self.sets[i % len(self.sets)], self.w, self.lib
@@ -235,7 +266,10 @@ def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
     bytes_b = algorithmic_bytes(bop, w.M, w.N, w.elem_bytes)
     bytes_main = algorithmic_bytes(bop + "_main", w.M, w.N, w.elem_bytes)
     bytes_f8 = algorithmic_bytes(("fused_" if w.fused else "") + "fwd_fp8", w.M, w.N, w.elem_bytes)
-    res["bytes"] = {"fwd": bytes_f, "bwd": bytes_b, "bwd_main": bytes_main, "fwd_fp8": bytes_f8}
+    bytes_lf = algorithmic_bytes("ln_fused_fwd" if w.fused else "ln_fwd", w.M, w.N, w.elem_bytes)
+    bytes_lb = algorithmic_bytes("ln_fused_bwd" if w.fused else "ln_bwd", w.M, w.N, w.elem_bytes)
+    res["bytes"] = {"fwd": bytes_f, "bwd": bytes_b, "bwd_main": bytes_main, "fwd_fp8": bytes_f8,
+                    "ln_fwd": bytes_lf, "ln_bwd": bytes_lb}
     for mode in (("cold", "hot") if detailed else ("cold",)):
         S = Sets(w, lib, rn, torch, n_sets_for(w, mode == "cold"))
         K = len(S.sets)
@@ -250,10 +284,16 @@ def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
         r["finalize_us"] = time_graph(torch, S.finalize, iters)
         # fp8-output forward with amax (main kernel + amax fold)
         r["fwd_fp8_us"] = time_direct(torch, S.fwd_fp8, iters, warmup)
+        # LayerNorm on the same buffers (its statistics first, for the backward)
+        for i in range(K):
+            S.ln_fwd(i, st)
+        r["ln_fwd_us"] = time_direct(torch, S.ln_fwd, iters, warmup)
+        r["ln_bwd_us"] = time_direct(torch, lambda i, s: S.ln_bwd(i + K // 2, s), iters, warmup)
         if detailed:
             r["fwd_graph_us"] = time_graph(torch, S.fwd, iters)
             r["bwd_graph_us"] = time_graph(torch, lambda i, s: S.bwd(i + K // 2, s), iters)
-        for op, b in (("fwd", bytes_f), ("bwd", bytes_b), ("bwd_main", bytes_main), ("fwd_fp8", bytes_f8)):
+        for op, b in (("fwd", bytes_f), ("bwd", bytes_b), ("bwd_main", bytes_main), ("fwd_fp8", bytes_f8),
+                      ("ln_fwd", bytes_lf), ("ln_bwd", bytes_lb)):
             r[op + "_GBs"] = b / (r[op + "_us"] * 1e3)
             r[op + "_pct_peak"] = 100.0 * r[op + "_GBs"] / HBM_PEAK_GBS
         res[mode] = r
@@ -465,6 +505,7 @@ def main():
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "fwd_us": round(cold["fwd_us"], 3), "bwd_us": round(cold["bwd_us"], 3),
         "fwd_fp8_us": round(cold["fwd_fp8_us"], 3), "fwd_fp8_GBs": round(cold["fwd_fp8_GBs"], 1),
+        "ln_fwd_us": round(cold["ln_fwd_us"], 3), "ln_bwd_us": round(cold["ln_bwd_us"], 3),
         "fwd_GBs": round(cold["fwd_GBs"], 1), "bwd_GBs": round(cold["bwd_GBs"], 1),
         "fwd_pct_peak": round(cold["fwd_pct_peak"], 2), "bwd_pct_peak": round(cold["bwd_pct_peak"], 2),
         "bwd_main_us": round(main_us, 3), "finalize_us": round(cold["finalize_us"], 3),

@@ -196,7 +196,11 @@ typedef enum rmsnorm_op {
     RMSNORM_OP_BWD = 2,
     RMSNORM_OP_FUSED_ADD_BWD = 3,
     RMSNORM_OP_FWD_FP8 = 4,
-    RMSNORM_OP_FUSED_ADD_FWD_FP8 = 5
+    RMSNORM_OP_FUSED_ADD_FWD_FP8 = 5,
+    RMSNORM_OP_LN_FWD = 6,           /* LayerNorm (include/layernorm.h) */
+    RMSNORM_OP_LN_FUSED_ADD_FWD = 7,
+    RMSNORM_OP_LN_BWD = 8,
+    RMSNORM_OP_LN_FUSED_ADD_BWD = 9
 } rmsnorm_op;
 
 typedef enum rmsnorm_path {
@@ -244,8 +248,8 @@ const char *rmsnorm_status_string(int status);
 const char *rmsnorm_last_error(void);
 /* The ABI version this header describes (RMSNORM_ABI_VERSION); a binding
  * checks it before use.  2: rmsnorm_plan gained w_regs.  3: fp8-output
- * forwards (ops 4 and 5). */
-#define RMSNORM_ABI_VERSION 3
+ * forwards (ops 4 and 5).  4: LayerNorm (include/layernorm.h, ops 6-9). */
+#define RMSNORM_ABI_VERSION 4
 int rmsnorm_version(void);
 
 #ifdef __cplusplus

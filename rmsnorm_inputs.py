@@ -118,11 +118,15 @@ def make_inputs(
     gemma: bool = False,
     seed: int = 0,
     rows: Optional[np.ndarray] = None,
+    layernorm: bool = False,
 ) -> Dict[str, np.ndarray]:
-    """Generate storage-dtype arrays x, [residual], dy, [dh], gamma.
+    """Generate storage-dtype arrays x, [residual], dy, [dh], gamma [, beta].
 
     ``rows`` (optional) keeps only those rows of the [M, N] tensors after the
     full draw, so a sampled check sees exactly the values of the full workload.
+    ``layernorm``: after gamma also draw beta = 0.1 z, then a per-row shift
+    2 z_i added to x before the storage rounding, so that rows have the
+    nonzero means LayerNorm removes (the RMSNorm draws are unchanged).
     """
     rng = np.random.default_rng(seed)
     out: Dict[str, np.ndarray] = {}
@@ -131,15 +135,25 @@ def make_inputs(
         return rng.standard_normal(size=shape, dtype=np.float32)
 
     order = ["x"] + (["residual"] if fused else []) + ["dy"] + (["dh"] if fused else [])
+    x32 = None
     for name in order:
         a = draw((M, N))
         if rows is not None:
             a = a[rows]
-        out[name] = to_storage(a, dtype)
+        if name == "x" and layernorm:
+            x32 = a  # stored after the row shift is drawn
+        else:
+            out[name] = to_storage(a, dtype)
     z = draw((N,))
     g = (0.1 * z) if gemma else (1.0 + 0.1 * z)
     out["gamma"] = to_storage(g.astype(np.float32), dtype)
-    return out
+    if layernorm:
+        out["beta"] = to_storage((0.1 * draw((N,))).astype(np.float32), dtype)
+        shift = 2.0 * draw((M,))
+        if rows is not None:
+            shift = shift[rows]
+        out["x"] = to_storage((x32 + shift[:, None]).astype(np.float32), dtype)
+    return {k: out[k] for k in (["x"] + [n for n in out if n != "x"])}
 
 
 def make_workload_inputs(w: Workload, seed: int = 0, rows: Optional[np.ndarray] = None):
@@ -165,9 +179,16 @@ def algorithmic_bytes(op: str, M: int, N: int, elem_bytes: int) -> int:
     bwd main  : the backward without the dgamma write (3MNB + NB + 4M plain)
     fp8 fwd   : read x, gamma; write y8 (1 byte), rstd  = MNB + MN + NB + 4M
     fused fp8 : read x, residual, gamma; write y8, h, rstd = 3MNB + MN + NB + 4M
+    ln fwd    : read x, gamma, beta; write y, mean, rstd = 2MNB + 2NB + 8M
+    ln bwd    : read dy, x, gamma, mean, rstd; write dx, dgamma, dbeta = 3MNB + 3NB + 8M
+    (fused LayerNorm: + 2MNB forward (residual read, h write), + MNB backward (dh read))
     """
     B = elem_bytes
     table = {
+        "ln_fwd": 2 * M * N * B + 2 * N * B + 8 * M,
+        "ln_bwd": 3 * M * N * B + 3 * N * B + 8 * M,
+        "ln_fused_fwd": 4 * M * N * B + 2 * N * B + 8 * M,
+        "ln_fused_bwd": 4 * M * N * B + 3 * N * B + 8 * M,
         "fwd_fp8": M * N * B + M * N + N * B + 4 * M,
         "fused_fwd_fp8": 3 * M * N * B + M * N + N * B + 4 * M,
         "fwd": 2 * M * N * B + N * B + 4 * M,

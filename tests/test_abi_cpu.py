@@ -6,6 +6,7 @@ Calls here use fake device addresses only where an argument check must reject
 the call before anything touches a device."""
 
 import ctypes
+import glob
 import os
 import re
 
@@ -26,9 +27,12 @@ def lib():
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rmsnorm_[a-z0-9_]+)\s*\(", text)))
+    """Functions declared in every header under include/."""
+    names = set()
+    for h in sorted(glob.glob(os.path.join(os.path.dirname(HEADER), "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:rmsnorm|layernorm)_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_match_header(lib):
@@ -37,7 +41,7 @@ def test_exports_match_header(lib):
     for name in declared:
         assert hasattr(lib, name), name
     out = os.popen(f"nm -D --defined-only {rn.library_path()}").read()
-    exported = set(re.findall(r" T (rmsnorm_\w+)", out))
+    exported = set(re.findall(r" T ((?:rmsnorm|layernorm)_\w+)", out))
     assert exported == set(declared)
 
 
@@ -109,6 +113,31 @@ def test_fp8_fwd_argument_errors(lib):
     size = ctypes.c_size_t(0)
     assert lib.rmsnorm_fwd_fp8_workspace_bytes(4, 0, rn.BF16, ctypes.byref(size)) == EINVAL
     assert lib.rmsnorm_fwd_fp8_workspace_bytes(4, 8, rn.BF16, None) == EINVAL
+
+
+def test_layernorm_argument_errors(lib):
+    f = lib.layernorm_fwd
+    # x, gamma, beta, y, mean, rstd
+    assert f(FAKE, FAKE + 4096, FAKE + 8193, FAKE + 12288, None, None, 4, 8, 1e-5, 0.0, rn.BF16, None) == EINVAL
+    assert f(FAKE, FAKE + 4096, FAKE + 12288, FAKE + 12288, None, None, 4, 8, 1e-5, 0.0, rn.BF16, None) == EINVAL
+    assert b"aliases" in lib.rmsnorm_last_error()                       # y == beta
+    assert f(FAKE, None, FAKE + 8192, None, None, None, 4, 8, 1e-5, 0.0, rn.BF16, None) == EINVAL  # nothing to do
+    assert f(FAKE, None, None, FAKE + 12288, None, None, 4, 8, 1e-5, 1.0, rn.BF16, None) == EINVAL  # offset, no gamma
+    assert f(None, None, None, None, None, None, 0, 8, 1e-5, 0.0, rn.BF16, None) == OK
+    b = lib.layernorm_bwd
+    # dy, x, gamma, mean, rstd, dx, dgamma, dbeta, ws
+    args = [FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, None, FAKE + 16384, FAKE + 20480, FAKE + 24576,
+            FAKE + 32768, 1 << 20, 4, 8, 1e-5, 0.0, rn.BF16, None]
+    assert b(*args) == EINVAL                                             # mean without rstd
+    assert b"together" in lib.rmsnorm_last_error()
+    a2 = list(args); a2[2] = None; a2[3] = None
+    assert b(*a2) == EINVAL                                               # dgamma without gamma
+    a3 = list(args); a3[3] = None; a3[7] = a3[5]
+    assert b(*a3) == EINVAL                                               # dbeta == dx
+    a4 = list(args); a4[3] = None; a4[7] = FAKE + 24577
+    assert b(*a4) == EINVAL                                               # dbeta misaligned
+    size = ctypes.c_size_t(0)
+    assert lib.layernorm_bwd_workspace_bytes(4, -1, rn.BF16, ctypes.byref(size)) == EINVAL
 
 
 def test_bwd_argument_errors(lib):
@@ -264,6 +293,40 @@ def test_fp8_plans_follow_the_forward(M, N, dt):
         assert q["grid"] == 64 and q["workspace_bytes"] == 256
 
 
+@pytest.mark.parametrize("M,N,dt", [(4096, 4096, rn.BF16), (262144, 128, rn.BF16), (16384, 6144, rn.F32),
+                                    (1024, 8192, rn.BF16), (100, 4097, rn.BF16), (4096, 16384, rn.BF16),
+                                    (2048, 24576, rn.BF16), (64, 100000, rn.BF16)])
+def test_layernorm_plans(M, N, dt):
+    ld = -(-N // 64) * 64
+    for op, rop in ((rn.OP_LN_FWD, rn.OP_FWD), (rn.OP_LN_FUSED_ADD_FWD, rn.OP_FUSED_ADD_FWD)):
+        q = plan(op, M, N, dt)
+        assert q["workspace_bytes"] == 0 and q["depth"] == 0
+        if q["path"] == rn.PATH_ROWS:
+            assert covers(q, N) and q["chunks"] <= 6
+            p = plan(rop, M, N, dt)
+            if p["chunks"] <= 6:  # the same layout as RMSNorm's where it fits
+                assert (p["vec"], p["team"], p["threads"], p["chunks"]) == (q["vec"], q["team"], q["threads"], q["chunks"])
+    for op in (rn.OP_LN_BWD, rn.OP_LN_FUSED_ADD_BWD):
+        q = plan(op, M, N, dt)
+        if q["path"] == rn.PATH_ROWS:
+            assert covers(q, N)
+        assert q["programs"] == q["grid"]
+        # two sets of partial rows (dgamma, dbeta), then room for mean and rstd
+        assert q["workspace_bytes"] == -(-2 * q["programs"] * ld * 4 // 256) * 256 + 2 * (-(-M * 4 // 256) * 256)
+        assert q["fin_grid"] == 2 * (ld // 32)
+    assert plan(rn.OP_LN_BWD, 64, 100000)["path"] == rn.PATH_LOOP
+
+
+def test_layernorm_wide_backward_bounds():
+    # LayerNorm holds the mean and a second accumulator set: its own bounds
+    assert (lambda p: (p["threads"], p["chunks"], p["depth"], p["w_regs"]))(plan(rn.OP_LN_BWD, 4096, 16384)) == (1024, 2, 0, 0)
+    assert (lambda p: (p["threads"], p["chunks"], p["depth"], p["w_regs"]))(plan(rn.OP_LN_BWD, 4096, 4096)) == (512, 1, 1, 1)
+    assert plan(rn.OP_LN_BWD, 2048, 32768)["path"] == rn.PATH_LOOP
+    with rn.plan_override(rn.OP_LN_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=1024, depth=1, w_regs=0):
+        with pytest.raises(rn.RMSNormError):  # two chunks, one row ahead: 512 threads at most
+            plan(rn.OP_LN_BWD, 100, 16384)
+
+
 def test_loop_path_beyond_registers():
     for N, dt in ((40960, rn.BF16), (65536, rn.BF16), (20000, rn.F32), (32768, rn.F32)):
         for op in (rn.OP_BWD, rn.OP_FUSED_ADD_BWD):
@@ -286,7 +349,7 @@ def test_grid_caps_and_zero_rows():
 
 def test_selector_rejects_bad_queries():
     with pytest.raises(rn.RMSNormError):
-        plan(9, 4, 4)
+        plan(10, 4, 4)
     with pytest.raises(rn.RMSNormError):
         plan(rn.OP_FWD, 4, 0)
     with pytest.raises(rn.RMSNormError):

@@ -1,0 +1,194 @@
+"""GPU parity of LayerNorm (forward and backward, plain and fused residual add)
+against the fp64 reference.
+
+Rules as for RMSNorm: bf16 outputs within 2 ulp of the rounded reference,
+float32 within a relative 1e-5, each taken at a magnitude floored by the size
+of the terms that cancel:
+  y   s = rstd |w| (|v| + mean_j |v|) + |beta|
+  dx  s = rstd (|g| + mean_j |g| + |xhat| (|mean_j(g xhat)| + mean_j |g xhat|)) [+ |dh|]
+mean is a float32 result floored at mean_j |v|; dgamma and dbeta have
+RMSNorm's relative-L2 rule; h (fused add) is bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_normalization_rmsnorm_amd as rn
+from gpu_util import check_values, from_dev, to_dev, widen
+from rmsnorm_inputs import make_inputs
+from tolerance import DGAMMA_TOL, check_f32, dgamma_error
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-5
+
+
+def gpu_ln(inp, dt, offset, fused, stats="gpu", affine=True, bias=True):
+    x = to_dev(inp["x"], dt)
+    g = to_dev(inp["gamma"], dt) if affine else None
+    b = to_dev(inp["beta"], dt) if bias else None
+    out = {}
+    if fused:
+        r = to_dev(inp["residual"], dt)
+        y, h, mean, rstd = rn.layernorm_fused_add_fwd(x, r, g, b, EPS, offset)
+        out["h"] = h
+    else:
+        y, mean, rstd = rn.layernorm_fwd(x, g, b, EPS, offset)
+    out.update(y=y, mean=mean, rstd=rstd)
+    dy = to_dev(inp["dy"], dt)
+    m_in, r_in = (mean, rstd) if stats == "gpu" else (None, None)
+    if fused:
+        dx, dg, db = rn.layernorm_fused_add_bwd(dy, to_dev(inp["dh"], dt), out["h"], g, m_in, r_in, EPS, offset)
+    else:
+        dx, dg, db = rn.layernorm_bwd(dy, x, g, m_in, r_in, EPS, offset)
+    torch.cuda.synchronize()
+    out.update(dx=dx, dg=dg, db=db)
+    return {k: (None if v is None else from_dev(v)) for k, v in out.items()}
+
+
+def check_ln(inp, dt, offset, fused, got, affine=True, bias=True, rows=None):
+    g = inp["gamma"] if affine else None
+    beta = inp["beta"] if bias else None
+    v = inp["x"]
+    if fused:
+        v, _, _ = oracle.fused_add_fwd(inp["x"], inp["residual"], g, dt, EPS, offset, want_y=False)
+        assert np.array_equal(got["h"], v), "h differs"
+    y64, mean64, rstd64 = oracle.ln_fwd(v, g, beta, dt, EPS, offset)
+    vw = widen(v, dt)
+    w = (widen(g, dt) if g is not None else np.ones(vw.shape[1])) + float(np.float32(offset))
+    bw = widen(beta, dt) if beta is not None else np.zeros(vw.shape[1])
+    mabs = np.abs(vw).mean(1)
+    s_y = rstd64[:, None] * np.abs(w) * (np.abs(vw) + mabs[:, None]) + np.abs(bw)
+    check_values("y", got["y"], y64, dt, scale=s_y)
+    rr = check_f32("rstd", got["rstd"], rstd64)
+    assert rr.ok, str(rr)
+    rm = check_f32("mean", got["mean"], mean64, scale=mabs)
+    assert rm.ok, str(rm)
+    dh = inp["dh"] if fused else None
+    out = oracle.ln_bwd(inp["dy"], v, g, dt, EPS, offset, dh=dh)
+    st = out["stats64"]
+    gg = widen(inp["dy"], dt) * w
+    xhat = (vw - mean64[:, None]) * rstd64[:, None]
+    s_dx = rstd64[:, None] * (np.abs(gg) + st[:, 2:3] + np.abs(xhat) * (np.abs(st[:, 1:2]) + st[:, 3:4]))
+    if dh is not None:
+        s_dx = s_dx + np.abs(widen(dh, dt))
+    r_dx = check_values("dx", got["dx"], out["dx64"], dt, scale=s_dx)
+    if affine:
+        err = dgamma_error(got["dg"], out["dgamma64"], dt)
+        assert err <= DGAMMA_TOL[dt], f"dgamma relative L2 {err:.3g}"
+    else:
+        assert got["dg"] is None
+    err = dgamma_error(got["db"], out["dbeta64"], dt)
+    assert err <= DGAMMA_TOL[dt], f"dbeta relative L2 {err:.3g}"
+    return r_dx
+
+
+# (M, N, dtype, fused, gemma)
+CASES = [
+    (300, 4096, "bf16", False, False),    # workgroup teams, w in registers
+    (130, 6144, "f32", False, True),      # float32, gamma + offset
+    (200, 7168, "bf16", True, False),     # fused residual add
+    (1000, 128, "bf16", False, False),    # 16-lane teams
+    (1000, 128, "bf16", True, False),
+    (37, 64, "f32", False, False),
+    (257, 8192, "bf16", False, False),
+    (33, 5000, "bf16", False, False),     # ragged vector groups
+    (17, 4097, "bf16", False, False),     # scalar access
+    (9, 8200, "bf16", True, False),
+    (5, 2, "bf16", False, False),         # N = 2
+    (70, 16384, "bf16", False, False),    # wide rows: gamma per row
+    (45, 16384, "bf16", True, False),
+    (20, 24576, "bf16", False, False),
+    (7, 12000, "f32", True, True),
+    (6, 32768, "bf16", False, False),     # looped rows
+    (4, 40000, "f32", True, True),
+    (3, 4096, "bf16", False, False),      # fewer rows than programs
+]
+
+
+def case_id(c):
+    M, N, dt, fused, gemma = c
+    return f"{dt}_{M}x{N}" + ("_fused" if fused else "") + ("_offset1" if gemma else "")
+
+
+@pytest.mark.parametrize("case", CASES, ids=case_id)
+def test_layernorm_parity(case):
+    M, N, dt, fused, gemma = case
+    inp = make_inputs(M, N, dt, fused=fused, gemma=gemma, layernorm=True)
+    offset = 1.0 if gemma else 0.0
+    got = gpu_ln(inp, dt, offset, fused)
+    r = check_ln(inp, dt, offset, fused, got)
+    print(f"{case_id(case)}: {r}")
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[3], CASES[8], CASES[11], CASES[15]], ids=case_id)
+def test_layernorm_recomputes_statistics(case):
+    M, N, dt, fused, gemma = case
+    inp = make_inputs(M, N, dt, fused=fused, gemma=gemma, layernorm=True)
+    offset = 1.0 if gemma else 0.0
+    check_ln(inp, dt, offset, fused, gpu_ln(inp, dt, offset, fused, stats=None))
+
+
+@pytest.mark.parametrize("affine,bias", [(False, False), (True, False), (False, True)])
+def test_layernorm_without_gamma_or_beta(affine, bias):
+    for fused in (False, True):
+        inp = make_inputs(64, 2048, "bf16", fused=fused, layernorm=True)
+        got = gpu_ln(inp, "bf16", 0.0, fused, affine=affine, bias=bias)
+        check_ln(inp, "bf16", 0.0, fused, got, affine=affine, bias=bias)
+
+
+# Every LayerNorm backward layout, forced on a shape it tiles, with a small grid.
+R = rn.PATH_ROWS
+LN_FORCED = [
+    (True, 300, 1024, "bf16", dict(path=R, vec=8, team=64, threads=256)),
+    (True, 300, 512, "bf16", dict(path=R, vec=8, team=64, threads=256)),
+    (True, 1000, 256, "bf16", dict(path=R, vec=8, team=32, threads=256, grid=7)),
+    (True, 300, 4096, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=2, grid=9)),
+    (True, 40, 16384, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=0, w_regs=0, grid=7)),
+    (True, 40, 8192, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=1, w_regs=0, grid=6)),
+    (True, 30, 24576, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=0, w_regs=0, grid=4)),
+    (True, 30, 16384, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=0, w_regs=0, grid=4)),
+    (True, 30, 16384, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=1, w_regs=0, grid=4)),
+    (True, 20, 24576, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=0, w_regs=0, grid=3)),
+    (True, 100, 2048, "bf16", dict(path=R, vec=1, team=0, threads=512, grid=5)),
+    (True, 300, 128, "bf16", dict(path=R, vec=1, team=64, threads=256)),
+    (True, 60, 4096, "bf16", dict(path=rn.PATH_LOOP, vec=8, team=0, threads=512, grid=9)),
+    (True, 60, 4096, "f32", dict(path=rn.PATH_LOOP, vec=1, team=0, threads=256, grid=9)),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["plain", "fused"])
+@pytest.mark.parametrize("fused_ok,M,N,dt,fields", LN_FORCED,
+                         ids=[f"{dt}_{M}x{N}_" + "_".join(f"{a}{b}" for a, b in f.items()) for _, M, N, dt, f in LN_FORCED])
+def test_layernorm_backward_layouts(fused_ok, M, N, dt, fields, fused):
+    op = rn.OP_LN_FUSED_ADD_BWD if fused else rn.OP_LN_BWD
+    inp = make_inputs(M, N, dt, fused=fused, gemma=(dt == "f32"), layernorm=True)
+    offset = 1.0 if dt == "f32" else 0.0
+    with rn.plan_override(op, **fields):
+        p = rn.rmsnorm_query_plan(op, M, N, rn.BF16 if dt == "bf16" else rn.F32, True)
+        for k, v in fields.items():
+            assert p[k] == v, (k, p)
+        check_ln(inp, dt, offset, fused, gpu_ln(inp, dt, offset, fused))
+
+
+def test_layernorm_zero_rows_writes_zero_gradients():
+    x = torch.empty(0, 4096, dtype=torch.bfloat16, device="cuda")
+    g = torch.ones(4096, dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(4096, dtype=torch.bfloat16, device="cuda")
+    y, mean, rstd = rn.layernorm_fwd(x, g, b)
+    dg = torch.full((4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    db = torch.full((4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    rn.layernorm_bwd(torch.empty_like(x), x, g, mean, rstd, dgamma=dg, dbeta=db)
+    torch.cuda.synchronize()
+    assert torch.all(dg == 0) and torch.all(db == 0)
+
+
+def test_layernorm_gradients_are_bit_identical_run_to_run():
+    M, N, dt = 2048, 4096, "bf16"
+    inp = make_inputs(M, N, dt, layernorm=True)
+    first = gpu_ln(inp, dt, 0.0, False)
+    for _ in range(2):
+        again = gpu_ln(inp, dt, 0.0, False)
+        for k in ("y", "mean", "rstd", "dx", "dg", "db"):
+            assert np.array_equal(first[k], again[k]), k

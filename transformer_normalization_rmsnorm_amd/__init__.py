@@ -15,6 +15,11 @@ Functions mirror the C entry points:
   rmsnorm_fused_add_fwd_fp8(x, residual, gamma, scale, eps, offset, amax=) -> (y8, h, rstd)
   rmsnorm_bwd_workspace_bytes, rmsnorm_fwd_fp8_workspace_bytes,
   rmsnorm_query_plan, rmsnorm_set_plan_override
+  layernorm_fwd(x, gamma, beta, eps, offset)            -> (y, mean, rstd)
+  layernorm_fused_add_fwd(x, residual, gamma, beta, ...) -> (y, h, mean, rstd)
+  layernorm_bwd(dy, x, gamma, mean, rstd, ...)          -> (dx, dgamma, dbeta)
+  layernorm_fused_add_bwd(dy, dh, h, gamma, mean, rstd, ...) -> (dx, dgamma, dbeta)
+  layernorm_bwd_workspace_bytes
 """
 
 from __future__ import annotations
@@ -29,6 +34,7 @@ LIBRARY_PATH = os.path.join(PKG_DIR, "librmsnorm_amd.so")
 
 F32, BF16 = 0, 1
 OP_FWD, OP_FUSED_ADD_FWD, OP_BWD, OP_FUSED_ADD_BWD, OP_FWD_FP8, OP_FUSED_ADD_FWD_FP8 = 0, 1, 2, 3, 4, 5
+OP_LN_FWD, OP_LN_FUSED_ADD_FWD, OP_LN_BWD, OP_LN_FUSED_ADD_BWD = 6, 7, 8, 9
 PATH_ROWS, PATH_LOOP = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
 
@@ -38,6 +44,8 @@ EXPORTS = (
     "rmsnorm_fused_add_bwd", "rmsnorm_bwd_partials", "rmsnorm_dgamma_finalize", "rmsnorm_query_plan",
     "rmsnorm_set_plan_override", "rmsnorm_status_string", "rmsnorm_last_error", "rmsnorm_version",
     "rmsnorm_fwd_fp8", "rmsnorm_fused_add_fwd_fp8", "rmsnorm_fwd_fp8_workspace_bytes",
+    "layernorm_fwd", "layernorm_fused_add_fwd", "layernorm_bwd_workspace_bytes", "layernorm_bwd",
+    "layernorm_fused_add_bwd",
 )
 
 
@@ -48,7 +56,7 @@ class RMSNormError(RuntimeError):
 
 
 # RMSNORM_ABI_VERSION of include/rmsnorm.h that this binding marshals.
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class Plan(ctypes.Structure):
@@ -85,6 +93,11 @@ def _bind(lib):
         "rmsnorm_fwd_fp8": [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, f, f, i32, vp],
         "rmsnorm_fused_add_fwd_fp8": [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, f, f, i32, vp],
         "rmsnorm_fwd_fp8_workspace_bytes": [i64, i64, i32, ctypes.POINTER(sz)],
+        "layernorm_fwd": [vp, vp, vp, vp, vp, vp, i64, i64, f, f, i32, vp],
+        "layernorm_fused_add_fwd": [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, f, f, i32, vp],
+        "layernorm_bwd_workspace_bytes": [i64, i64, i32, ctypes.POINTER(sz)],
+        "layernorm_bwd": [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, f, f, i32, vp],
+        "layernorm_fused_add_bwd": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, f, f, i32, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -446,3 +459,125 @@ def plan_override(op: int, **fields):
         yield
     finally:
         rmsnorm_set_plan_override(op, None)
+
+
+# ---- LayerNorm ------------------------------------------------------------------
+
+def layernorm_bwd_workspace_bytes(M: int, N: int, dtype_code: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    _check(lib.layernorm_bwd_workspace_bytes(M, N, dtype_code, ctypes.byref(out)), "layernorm_bwd_workspace_bytes")
+    return int(out.value)
+
+
+def _ln_fwd_common(x, residual, gamma, beta, eps, offset, y, h_out, mean, rstd, save_stats):
+    torch = _torch()
+    lib = load_library()
+    _require(x, "x")
+    M, N = _rows(x)
+    dev = x.device
+    fused = residual is not None
+    if fused:
+        _require(residual, "residual", x.shape, x.dtype, dev)
+    for t, name in ((gamma, "gamma"), (beta, "beta")):
+        if t is not None:
+            _require(t, name, (N,), x.dtype, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _require(y, "y", x.shape, x.dtype, dev)
+    if fused and h_out is None:
+        h_out = torch.empty_like(x)
+    if fused:
+        _require(h_out, "h_out", x.shape, x.dtype, dev)
+    if save_stats:
+        mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev) if mean is None else mean
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev) if rstd is None else rstd
+    for t, name in ((mean, "mean"), (rstd, "rstd")):
+        if t is not None:
+            _require(t, name, x.shape[:-1], torch.float32, dev)
+    with _on_device(dev):
+        if fused:
+            _check(lib.layernorm_fused_add_fwd(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(h_out),
+                                               _ptr(mean), _ptr(rstd), M, N, eps, offset, _dtype_code(x),
+                                               _stream(dev)), "layernorm_fused_add_fwd")
+        else:
+            _check(lib.layernorm_fwd(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), M, N, eps,
+                                     offset, _dtype_code(x), _stream(dev)), "layernorm_fwd")
+    return y, h_out, mean, rstd
+
+
+def layernorm_fwd(x, gamma, beta, eps: float = 1e-5, offset: float = 0.0, *, y=None, mean=None, rstd=None,
+                  save_stats: bool = True):
+    """y = (x - mean) * rstd * (gamma + offset) + beta over the last dimension;
+    returns (y, mean, rstd).  gamma / beta None: no scale / no bias."""
+    y, _, mean, rstd = _ln_fwd_common(x, None, gamma, beta, eps, offset, y, None, mean, rstd, save_stats)
+    return y, mean, rstd
+
+
+def layernorm_fused_add_fwd(x, residual, gamma, beta, eps: float = 1e-5, offset: float = 0.0, *, y=None,
+                            h_out=None, mean=None, rstd=None, save_stats: bool = True):
+    """h = x + residual (rounded to the storage dtype), y = layernorm(h); returns (y, h, mean, rstd)."""
+    return _ln_fwd_common(x, residual, gamma, beta, eps, offset, y, h_out, mean, rstd, save_stats)
+
+
+def _ln_bwd_common(dy, dh, v, gamma, mean, rstd, eps, offset, dx, dgamma, dbeta, want_dbeta, workspace):
+    torch = _torch()
+    lib = load_library()
+    _require(v, "x" if dh is None else "h")
+    M, N = _rows(v)
+    dev = v.device
+    _require(dy, "dy", v.shape, v.dtype, dev)
+    if dh is not None:
+        _require(dh, "dh", v.shape, v.dtype, dev)
+    if gamma is not None:
+        _require(gamma, "gamma", (N,), v.dtype, dev)
+    for t, name in ((mean, "mean"), (rstd, "rstd")):
+        if t is not None:
+            _require(t, name, v.shape[:-1], torch.float32, dev)
+    if dx is None:
+        dx = torch.empty_like(v)
+    _require(dx, "dx", v.shape, v.dtype, dev)
+    if gamma is not None and dgamma is None:
+        dgamma = torch.empty(N, dtype=v.dtype, device=dev)
+    if want_dbeta and dbeta is None:
+        dbeta = torch.empty(N, dtype=v.dtype, device=dev)
+    for t, name in ((dgamma, "dgamma"), (dbeta, "dbeta")):
+        if t is not None:
+            _require(t, name, (N,), v.dtype, dev)
+    with _on_device(dev):
+        if workspace is None:
+            nbytes = layernorm_bwd_workspace_bytes(M, N, _dtype_code(v))
+            for op in (OP_LN_BWD, OP_LN_FUSED_ADD_BWD):  # also large enough for a forced plan
+                for vec_ok in (True, False):
+                    try:
+                        nbytes = max(nbytes, rmsnorm_query_plan(op, M, N, _dtype_code(v), vec_ok)["workspace_bytes"])
+                    except RMSNormError:
+                        pass
+            workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        else:
+            _require(workspace, "workspace", device=dev)
+            nbytes = workspace.numel() * workspace.element_size()
+        if dh is None:
+            rc = lib.layernorm_bwd(_ptr(dy), _ptr(v), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
+                                   _ptr(dbeta), _ptr(workspace), nbytes, M, N, eps, offset, _dtype_code(v),
+                                   _stream(dev))
+        else:
+            rc = lib.layernorm_fused_add_bwd(_ptr(dy), _ptr(dh), _ptr(v), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx),
+                                             _ptr(dgamma), _ptr(dbeta), _ptr(workspace), nbytes, M, N, eps, offset,
+                                             _dtype_code(v), _stream(dev))
+        _check(rc, "layernorm_bwd" if dh is None else "layernorm_fused_add_bwd")
+    return dx, dgamma, dbeta
+
+
+def layernorm_bwd(dy, x, gamma, mean, rstd, eps: float = 1e-5, offset: float = 0.0, *, dx=None, dgamma=None,
+                  dbeta=None, want_dbeta: bool = True, workspace=None):
+    """Gradients of layernorm_fwd; mean = rstd = None recomputes them.
+    Returns (dx, dgamma or None, dbeta or None)."""
+    return _ln_bwd_common(dy, None, x, gamma, mean, rstd, eps, offset, dx, dgamma, dbeta, want_dbeta, workspace)
+
+
+def layernorm_fused_add_bwd(dy, dh, h, gamma, mean, rstd, eps: float = 1e-5, offset: float = 0.0, *, dx=None,
+                            dgamma=None, dbeta=None, want_dbeta: bool = True, workspace=None):
+    """Gradients of layernorm_fused_add_fwd: dx (= dresidual), dgamma, dbeta.
+    dh may be None; pass dx=dh to accumulate in place."""
+    return _ln_bwd_common(dy, dh, h, gamma, mean, rstd, eps, offset, dx, dgamma, dbeta, want_dbeta, workspace)

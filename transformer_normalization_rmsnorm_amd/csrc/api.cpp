@@ -11,6 +11,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "layernorm.h"
 #include "rmsnorm_internal.h"
 
 using namespace rmsnorm;
@@ -42,7 +43,7 @@ struct Override {
     bool set = false;
     rmsnorm_plan plan = {};
 };
-Override g_override[6];
+Override g_override[10];
 
 int device_cus(int *cus)
 {
@@ -130,9 +131,15 @@ struct Fp8Out {
     size_t workspace_bytes;
 };
 
+// LayerNorm forward extras: the bias (may be null) and the saved means.
+struct LnFwd {
+    const void *beta;
+    float *mean;
+};
+
 int do_fwd(const void *x, const void *r, const void *gamma, void *y, void *h, float *rstd, int64_t M,
            int64_t N, float eps, float offset, int dtype, hipStream_t stream, bool fused,
-           const Fp8Out *f8 = nullptr)
+           const Fp8Out *f8 = nullptr, const LnFwd *ln = nullptr)
 {
     int rc = check_common(M, N, dtype, eps, offset);
     if (rc)
@@ -149,29 +156,35 @@ int do_fwd(const void *x, const void *r, const void *gamma, void *y, void *h, fl
         return fail(RMSNORM_EINVAL, "null input pointer");
     if (!gamma && offset != 0.0f)
         return fail(RMSNORM_EINVAL, "offset needs gamma (gamma == NULL is the non-affine op)");
-    if (!fused && !y && !rstd)
-        return fail(RMSNORM_EINVAL, "y and rstd are both null: nothing to compute");
+    const void *beta = ln ? ln->beta : nullptr;
+    float *mean = ln ? ln->mean : nullptr;
+    if (!fused && !y && !rstd && !mean)
+        return fail(RMSNORM_EINVAL, "no output requested: nothing to compute");
     const size_t eb = (size_t)elem_bytes(dtype);
     const size_t yb = f8 ? 1 : eb; // E4M3 codes are bytes
     if (!aligned(x, eb) || !aligned(gamma, eb) || !aligned(y, yb) || !aligned(r, eb) || !aligned(h, eb) ||
-        !aligned(rstd, 4))
+        !aligned(rstd, 4) || !aligned(beta, eb) || !aligned(mean, 4))
         return fail(RMSNORM_EINVAL, "pointer not aligned to its element size");
-    if (y && (y == x || (gamma && y == gamma) || (fused && (y == r || y == h))))
+    if (y && (y == x || (gamma && y == gamma) || (beta && y == beta) || (fused && (y == r || y == h))))
         return fail(RMSNORM_EINVAL, "y aliases an input");
     if (fused && h == x)
         return fail(RMSNORM_EINVAL, "h_out aliases x (only residual may be overwritten)");
     // 16-byte accesses of T; the fp8 output then moves 16 / sizeof(T) bytes per access
     const size_t yv = f8 ? (size_t)vec_elems(dtype) : 16;
-    const bool vec_ok = aligned(x, 16) && aligned(gamma, 16) && aligned(y, yv) && aligned(r, 16) && aligned(h, 16);
+    const bool vec_ok = aligned(x, 16) && aligned(gamma, 16) && aligned(y, yv) && aligned(r, 16) &&
+                        aligned(h, 16) && aligned(beta, 16);
     int cus = 0;
     if ((rc = device_cus(&cus)))
         return rc;
-    const int op = f8 ? (fused ? RMSNORM_OP_FUSED_ADD_FWD_FP8 : RMSNORM_OP_FWD_FP8)
+    const int op = ln ? (fused ? RMSNORM_OP_LN_FUSED_ADD_FWD : RMSNORM_OP_LN_FWD)
+                 : f8 ? (fused ? RMSNORM_OP_FUSED_ADD_FWD_FP8 : RMSNORM_OP_FWD_FP8)
                       : (fused ? RMSNORM_OP_FUSED_ADD_FWD : RMSNORM_OP_FWD);
     rmsnorm_plan p;
     if ((rc = plan_for(op, M, N, dtype, vec_ok, cus, &p)))
         return rc;
     FwdArgs a{x, r, gamma, y, h, rstd, M, (int32_t)N, eps, offset};
+    a.beta = beta;
+    a.mean = mean;
     if (f8) {
         a.scale = f8->scale;
         if (f8->amax) {
@@ -183,7 +196,8 @@ int do_fwd(const void *x, const void *r, const void *gamma, void *y, void *h, fl
             a.amax_part = static_cast<float *>(f8->workspace);
         }
     }
-    if ((rc = launched(launch_fwd(dtype, fused, f8 != nullptr, p, a, stream), "forward")))
+    const FwdKind kind = ln ? FWD_LN : f8 ? FWD_RMS_FP8 : FWD_RMS;
+    if ((rc = launched(launch_fwd(dtype, fused, kind, p, a, stream), "forward")))
         return rc;
     if (f8 && f8->amax)
         return launched(launch_amax_finalize(a.amax_part, p.programs, f8->amax, stream), "amax finalize");
@@ -192,14 +206,28 @@ int do_fwd(const void *x, const void *r, const void *gamma, void *y, void *h, fl
 
 // Shared by the backward entry points.  Writes dx and the partials; returns
 // the number of partial rows in *programs.
+// LayerNorm backward extras: the saved means (NULL together with rstd: both
+// recomputed) and whether the partial rows (dgamma, dbeta) are wanted.
+struct LnBwd {
+    const float *mean;
+    bool partials;
+};
+
 int do_partials(const void *dy, const void *v, const void *gamma, const float *rstd, const void *dh, void *dx,
                 void *workspace, size_t workspace_bytes, int64_t *programs, int64_t M, int64_t N, float eps,
-                float offset, int dtype, hipStream_t stream)
+                float offset, int dtype, hipStream_t stream, const LnBwd *ln = nullptr)
 {
     int rc = check_common(M, N, dtype, eps, offset);
     if (rc)
         return rc;
     const bool fused = (dh != nullptr);
+    const float *mean = ln ? ln->mean : nullptr;
+    if (ln && ((mean == nullptr) != (rstd == nullptr)))
+        return fail(RMSNORM_EINVAL, "mean and rstd must be given together (or both NULL to recompute)");
+    if (!aligned(mean, 4))
+        return fail(RMSNORM_EINVAL, "mean not aligned to 4 bytes");
+    // partial rows: RMSNorm for dgamma (affine op); LayerNorm when dgamma or dbeta is wanted
+    const bool want_partials = ln ? ln->partials : gamma != nullptr;
     if (M > 0 && (!dy || !v || !dx))
         return fail(RMSNORM_EINVAL, "null input pointer");
     if (!gamma && offset != 0.0f)
@@ -216,36 +244,47 @@ int do_partials(const void *dy, const void *v, const void *gamma, const float *r
     int cus = 0;
     if ((rc = device_cus(&cus)))
         return rc;
+    const int op = ln ? (fused ? RMSNORM_OP_LN_FUSED_ADD_BWD : RMSNORM_OP_LN_BWD)
+                      : (fused ? RMSNORM_OP_FUSED_ADD_BWD : RMSNORM_OP_BWD);
     rmsnorm_plan p;
-    if ((rc = plan_for(fused ? RMSNORM_OP_FUSED_ADD_BWD : RMSNORM_OP_BWD, M, N, dtype, vec_ok, cus, &p)))
+    if ((rc = plan_for(op, M, N, dtype, vec_ok, cus, &p)))
         return rc;
-    // Workspace: the partial rows (affine op only), then M floats when rstd is recomputed.
-    const int64_t rstd_region = ((M * 4 + 255) / 256) * 256;
-    const int64_t partial_region = p.workspace_bytes - rstd_region;
-    const int64_t need = (gamma ? partial_region : 0) + (rstd ? 0 : rstd_region);
+    // Workspace: the partial rows, then the recomputed row statistics (rstd;
+    // LayerNorm: means, then rstd), M floats each, when the caller has none.
+    const int64_t stat_region = ((M * 4 + 255) / 256) * 256;
+    const int64_t stats = ln ? 2 : 1;
+    const int64_t partial_region = p.workspace_bytes - stats * stat_region;
+    const int64_t need = (want_partials ? partial_region : 0) + (rstd ? 0 : stats * stat_region);
     if (need > 0 && (workspace == nullptr || workspace_bytes < (size_t)need))
         return fail(RMSNORM_EWORKSPACE, "workspace of %zu bytes at %p; %lld bytes needed", workspace_bytes,
                     workspace, (long long)need);
-    *programs = gamma ? p.programs : 0;
+    *programs = want_partials ? p.programs : 0;
     if (M == 0)
         return ok();
     const int64_t ld = partial_ld(N);
-    float *partials = gamma ? static_cast<float *>(workspace) : nullptr;
-    const float *rs = rstd;
+    float *partials = want_partials ? static_cast<float *>(workspace) : nullptr;
+    const float *rs = rstd, *mu = mean;
     if (rs == nullptr) {
-        // recompute rstd from v into the workspace with an rstd-only forward
-        float *tail = reinterpret_cast<float *>(static_cast<char *>(workspace) + (gamma ? partial_region : 0));
+        // recompute the statistics from v into the workspace with a forward
+        // that writes no y
+        float *tail = reinterpret_cast<float *>(static_cast<char *>(workspace) + (want_partials ? partial_region : 0));
+        float *tail_mu = ln ? tail : nullptr;
+        float *tail_rs = ln ? reinterpret_cast<float *>(reinterpret_cast<char *>(tail) + stat_region) : tail;
         rmsnorm_plan fp;
-        rc = select_plan(RMSNORM_OP_FWD, M, N, dtype, aligned(v, 16) && aligned(gamma, 16), cus, &fp);
+        rc = select_plan(ln ? RMSNORM_OP_LN_FWD : RMSNORM_OP_FWD, M, N, dtype, aligned(v, 16) && aligned(gamma, 16),
+                         cus, &fp);
         if (rc)
-            return fail(rc, "no plan for the rstd recompute");
-        FwdArgs fa{v, nullptr, gamma, nullptr, nullptr, tail, M, (int32_t)N, eps, offset};
-        if ((rc = launched(launch_fwd(dtype, false, false, fp, fa, stream), "rstd recompute")))
+            return fail(rc, "no plan for the statistics recompute");
+        FwdArgs fa{v, nullptr, gamma, nullptr, nullptr, tail_rs, M, (int32_t)N, eps, offset};
+        fa.mean = tail_mu;
+        if ((rc = launched(launch_fwd(dtype, false, ln ? FWD_LN : FWD_RMS, fp, fa, stream), "statistics recompute")))
             return rc;
-        rs = tail;
+        rs = tail_rs;
+        mu = tail_mu;
     }
     BwdArgs a{dy, v, gamma, rs, dh, dx, partials, ld, M, (int32_t)N, offset};
-    return launched(launch_bwd(dtype, fused, p, a, stream), "backward");
+    a.mean = mu;
+    return launched(launch_bwd(dtype, fused, ln != nullptr, p, a, stream), "backward");
 }
 
 int do_finalize(const float *partials, int64_t programs, int64_t N, void *dgamma, int dtype, hipStream_t stream)
@@ -258,7 +297,34 @@ int do_finalize(const float *partials, int64_t programs, int64_t N, void *dgamma
         return fail(RMSNORM_EINVAL, "null pointer");
     if (!aligned(partials, 16) || !aligned(dgamma, (size_t)elem_bytes(dtype)))
         return fail(RMSNORM_EINVAL, "misaligned partials or dgamma");
-    return launched(launch_finalize(dtype, partials, programs, partial_ld(N), N, dgamma, stream), "finalize");
+    return launched(launch_finalize(dtype, partials, programs, partial_ld(N), N, dgamma, nullptr, stream),
+                    "finalize");
+}
+
+// LayerNorm backward: dx and the partial rows, then dgamma and dbeta from a
+// finalizer with one row of workgroups per output.
+int do_ln_bwd(const void *dy, const void *dh, const void *v, const void *gamma, const float *mean,
+              const float *rstd, void *dx, void *dgamma, void *dbeta, void *workspace, size_t workspace_bytes,
+              int64_t M, int64_t N, float eps, float offset, int dtype, hipStream_t stream)
+{
+    if (!gamma && dgamma)
+        return fail(RMSNORM_EINVAL, "dgamma given without gamma");
+    if (dtype == RMSNORM_BF16 || dtype == RMSNORM_F32) {
+        const size_t eb = (size_t)elem_bytes(dtype);
+        if (!aligned(dgamma, eb) || !aligned(dbeta, eb))
+            return fail(RMSNORM_EINVAL, "dgamma or dbeta not aligned to its element size");
+    }
+    if (dbeta && (dbeta == dgamma || dbeta == dx))
+        return fail(RMSNORM_EINVAL, "dbeta aliases another output");
+    const LnBwd ln{mean, dgamma != nullptr || dbeta != nullptr};
+    int64_t programs = 0;
+    int rc = do_partials(dy, v, gamma, rstd, dh, dx, workspace, workspace_bytes, &programs, M, N, eps, offset,
+                         dtype, stream, &ln);
+    if (rc || !ln.partials)
+        return rc;
+    return launched(launch_finalize(dtype, static_cast<const float *>(workspace), programs, partial_ld(N), N,
+                                    dgamma, dbeta, stream),
+                    "finalize");
 }
 
 int do_bwd(const void *dy, const void *dh, const void *v, const void *gamma, const float *rstd, void *dx,
@@ -282,6 +348,27 @@ int do_bwd(const void *dy, const void *dh, const void *v, const void *gamma, con
     if (rc)
         return rc;
     return do_finalize(static_cast<const float *>(workspace), programs, N, dgamma, dtype, stream);
+}
+
+int workspace_for(int op_a, int op_b, int64_t M, int64_t N, int dtype, size_t *bytes)
+{
+    if (!bytes)
+        return fail(RMSNORM_EINVAL, "bytes is null");
+    int rc = check_common(M, N, dtype, 0.0f, 0.0f);
+    if (rc)
+        return rc;
+    int cus = 0;
+    if ((rc = device_cus(&cus)))
+        return rc;
+    int64_t need = 0;
+    for (int op : {op_a, op_b})
+        for (bool vec_ok : {true, false}) {
+            rmsnorm_plan p;
+            if (select_plan(op, M, N, dtype, vec_ok, cus, &p) == RMSNORM_OK && p.workspace_bytes > need)
+                need = p.workspace_bytes;
+        }
+    *bytes = (size_t)need;
+    return ok();
 }
 
 } // namespace
@@ -341,23 +428,44 @@ int rmsnorm_fwd_fp8_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *byt
 
 int rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *bytes)
 {
-    if (!bytes)
-        return fail(RMSNORM_EINVAL, "bytes is null");
-    int rc = check_common(M, N, dtype, 0.0f, 0.0f);
-    if (rc)
-        return rc;
-    int cus = 0;
-    if ((rc = device_cus(&cus)))
-        return rc;
-    int64_t need = 0;
-    for (int op : {RMSNORM_OP_BWD, RMSNORM_OP_FUSED_ADD_BWD})
-        for (bool vec_ok : {true, false}) {
-            rmsnorm_plan p;
-            if (select_plan(op, M, N, dtype, vec_ok, cus, &p) == RMSNORM_OK && p.workspace_bytes > need)
-                need = p.workspace_bytes;
-        }
-    *bytes = (size_t)need;
-    return ok();
+    return workspace_for(RMSNORM_OP_BWD, RMSNORM_OP_FUSED_ADD_BWD, M, N, dtype, bytes);
+}
+
+int layernorm_fwd(const void *x, const void *gamma, const void *beta, void *y, float *mean, float *rstd, int64_t M,
+                  int64_t N, float eps, float offset, int dtype, rmsnorm_stream_t stream)
+{
+    const LnFwd ln{beta, mean};
+    return do_fwd(x, nullptr, gamma, y, nullptr, rstd, M, N, eps, offset, dtype, stream, false, nullptr, &ln);
+}
+
+int layernorm_fused_add_fwd(const void *x, const void *residual, const void *gamma, const void *beta, void *y,
+                            void *h_out, float *mean, float *rstd, int64_t M, int64_t N, float eps, float offset,
+                            int dtype, rmsnorm_stream_t stream)
+{
+    const LnFwd ln{beta, mean};
+    return do_fwd(x, residual, gamma, y, h_out, rstd, M, N, eps, offset, dtype, stream, true, nullptr, &ln);
+}
+
+int layernorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *bytes)
+{
+    return workspace_for(RMSNORM_OP_LN_BWD, RMSNORM_OP_LN_FUSED_ADD_BWD, M, N, dtype, bytes);
+}
+
+int layernorm_bwd(const void *dy, const void *x, const void *gamma, const float *mean, const float *rstd, void *dx,
+                  void *dgamma, void *dbeta, void *workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                  float eps, float offset, int dtype, rmsnorm_stream_t stream)
+{
+    return do_ln_bwd(dy, nullptr, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace, workspace_bytes, M, N, eps,
+                     offset, dtype, stream);
+}
+
+int layernorm_fused_add_bwd(const void *dy, const void *dh, const void *h, const void *gamma, const float *mean,
+                            const float *rstd, void *dx, void *dgamma, void *dbeta, void *workspace,
+                            size_t workspace_bytes, int64_t M, int64_t N, float eps, float offset, int dtype,
+                            rmsnorm_stream_t stream)
+{
+    return do_ln_bwd(dy, dh, h, gamma, mean, rstd, dx, dgamma, dbeta, workspace, workspace_bytes, M, N, eps,
+                     offset, dtype, stream);
 }
 
 int rmsnorm_bwd(const void *dy, const void *x, const void *gamma, const float *rstd, void *dx, void *dgamma,
@@ -403,7 +511,7 @@ int rmsnorm_query_plan(int op, int64_t M, int64_t N, int dtype, int vec_ok, int 
         if (rc)
             return rc;
     }
-    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_FUSED_ADD_FWD_FP8)
+    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_LN_FUSED_ADD_BWD)
         return fail(RMSNORM_EINVAL, "op %d unknown", op);
     rmsnorm_plan p;
     int rc = plan_for(op, M, N, dtype, vec_ok != 0, cus, &p);
@@ -415,7 +523,7 @@ int rmsnorm_query_plan(int op, int64_t M, int64_t N, int dtype, int vec_ok, int 
 
 int rmsnorm_set_plan_override(int op, const rmsnorm_plan *plan)
 {
-    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_FUSED_ADD_FWD_FP8)
+    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_LN_FUSED_ADD_BWD)
         return fail(RMSNORM_EINVAL, "op %d unknown", op);
     if (plan == nullptr) {
         g_override[op].set = false;

@@ -24,6 +24,13 @@
 // registers are pinned between the two passes, so that up to 32 bf16 (16
 // fp32) elements per lane and 1024 lanes -- rows of 32768 bf16 / 16384 fp32
 // elements -- stay resident without spilling.
+//
+// LayerNorm (LN; TransformerEngine PR #583 registers matching LayerNorm
+// configurations) runs on the same layouts: with xhat = (v - mean) * rstd and
+// g = dy * w, one paired reduction gives mean(g) and mean(g * xhat), then
+// dx = rstd * (g - mean(g) - xhat * mean(g * xhat)) [+ dh]; each program keeps
+// two accumulator sets, dgamma (dy * xhat) and dbeta (dy), and writes two
+// partial rows, which the finalizer folds with a second row of workgroups.
 #include "device_common.h"
 #include "rmsnorm_internal.h"
 
@@ -36,9 +43,10 @@ struct BwdRow {
     Chunk<T, V> g[WR ? 1 : K]; // gamma, when it travels with the row
     Chunk<T, V> dh[FUSED ? K : 1];
     float rs;
+    float mu; // LayerNorm: the row mean
 };
 
-template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FUSED, bool EXACT>
+template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FUSED, bool EXACT, bool LN>
 __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
 {
     using Row = BwdRow<T, V, K, WR, FUSED>;
@@ -57,12 +65,20 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
     const float *__restrict__ rstd = a.rstd;
 
     constexpr int KW = WR ? K : 1;
+    constexpr int KB = LN ? K : 1;
     float w[KW][V], acc[K][V]; // w = gamma + offset, or 1 for the non-affine op
+    float accb[KB][V];         // LayerNorm: the dbeta accumulators
 #pragma unroll
     for (int k = 0; k < K; ++k) {
 #pragma unroll
         for (int e = 0; e < V; ++e)
             acc[k][e] = 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            accb[k][e] = 0.0f;
     }
     if constexpr (WR) {
 #pragma unroll
@@ -103,11 +119,80 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
                 b.dh[k].load(dhp + base + (int64_t)c * V);
         }
         b.rs = rstd[row];
+        if constexpr (LN)
+            b.mu = a.mean[row];
     };
 
-    __shared__ float red[2][16];
+    __shared__ float red[2][32]; // block_sum uses 16 floats a slot, block_sum2 32
     int parity = 0;
+    // values unpacked in the first pass are formed again in the second where
+    // registers are scarce (see below)
+    auto pin_row = [&](Row &b) __attribute__((always_inline)) {
+        if constexpr (!WR || TEAM != 0) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                b.v[k].pin();
+                b.dy[k].pin();
+                if constexpr (!WR)
+                    b.g[k].pin();
+                if constexpr (FUSED)
+                    b.dh[k].pin();
+            }
+        }
+    };
+    auto proc_ln = [&](Row &b, int64_t row) __attribute__((always_inline)) {
+        const float rs = b.rs, mu = b.mu;
+        float sg = 0.0f, sgx = 0.0f; // sum g, sum g * xhat
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * tl + lane;
+            if (EXACT || c < nchunks) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float gg = b.dy[k].get(e) * weight(b, k, e);
+                    sg += gg;
+                    sgx = fmaf(gg, (b.v[k].get(e) - mu) * rs, sgx);
+                }
+            }
+        }
+        pin_row(b);
+        if constexpr (TEAM == 0) {
+            block_sum2(sg, sgx, red[parity], a.threads);
+            parity ^= 1;
+        } else {
+            sg = team_sum<TEAM>(sg);
+            sgx = team_sum<TEAM>(sgx);
+        }
+        const float c1 = sg * inv_n, c2 = sgx * inv_n;
+        const int64_t base = row * N;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * tl + lane;
+            if (EXACT || c < nchunks) {
+                float o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float d = b.dy[k].get(e);
+                    const float xh = (b.v[k].get(e) - mu) * rs;
+                    float dxv = rs * fmaf(-xh, c2, d * weight(b, k, e) - c1);
+                    if constexpr (FUSED)
+                        dxv += b.dh[k].get(e);
+                    o[e] = dxv;
+                    acc[k][e] = fmaf(d, xh, acc[k][e]);
+                    if constexpr (LN)
+                        accb[k][e] += d;
+                }
+                Chunk<T, V> out;
+                out.set(o);
+                out.store(dxp + base + (int64_t)c * V);
+            }
+        }
+    };
     auto proc = [&](Row &b, int64_t row) __attribute__((always_inline)) {
+        if constexpr (LN) {
+            proc_ln(b, row);
+            return;
+        }
         float dot = 0.0f;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -124,17 +209,7 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
         // with w in registers have registers to spare at one program per CU,
         // and keeping the unpacked row there is 1.5% faster (4096 x 4096,
         // 16384 x 8192 bf16).
-        if constexpr (!WR || TEAM != 0) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                b.v[k].pin();
-                b.dy[k].pin();
-                if constexpr (!WR)
-                    b.g[k].pin();
-                if constexpr (FUSED)
-                    b.dh[k].pin();
-            }
-        }
+        pin_row(b);
         if constexpr (TEAM == 0) {
             dot = block_sum(dot, red[parity], a.threads);
             parity ^= 1;
@@ -168,26 +243,33 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
 
     row_pipeline<D, Row>((int64_t)blockIdx.x * tpb + team, a.grid * tpb, a.M, load, proc);
 
-    if (a.partials == nullptr) // non-affine: no dgamma
+    if (a.partials == nullptr) // no dgamma (non-affine) and no dbeta
         return;
     float *__restrict__ part = a.partials + (int64_t)blockIdx.x * a.ld;
+    float *__restrict__ partb = a.partials + (a.grid + (int64_t)blockIdx.x) * a.ld; // LayerNorm dbeta
     if constexpr (TEAM == 0) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int c = k * tl + lane;
-            if (EXACT || c < nchunks)
+            if (EXACT || c < nchunks) {
                 store_f32<V>(part + (int64_t)c * V, acc[k]);
+                if constexpr (LN)
+                    store_f32<V>(partb + (int64_t)c * V, accb[k]);
+            }
         }
     } else {
         // Several teams per workgroup: add their partials in team order.
-        extern __shared__ float team_acc[]; // [tpb][N]
+        extern __shared__ float team_acc[]; // [sets][tpb][N]
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int c = k * tl + lane;
             if (EXACT || c < nchunks) {
 #pragma unroll
-                for (int e = 0; e < V; ++e)
+                for (int e = 0; e < V; ++e) {
                     team_acc[team * N + c * V + e] = acc[k][e];
+                    if constexpr (LN)
+                        team_acc[(tpb + team) * N + c * V + e] = accb[k][e];
+                }
             }
         }
         __syncthreads();
@@ -196,14 +278,21 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
             for (int t = 1; t < tpb; ++t)
                 s += team_acc[t * N + j];
             part[j] = s;
+            if constexpr (LN) {
+                float sb = team_acc[tpb * N + j];
+                for (int t = 1; t < tpb; ++t)
+                    sb += team_acc[(tpb + t) * N + j];
+                partb[j] = sb;
+            }
         }
     }
 }
 
-// Any N: per row, pass 1 forms dot, pass 2 re-reads the row, writes dx and
-// accumulates this workgroup's partial row in place (each lane always owns the
-// same columns, so the read-modify-write is private to the lane).
-template <typename T, int V, bool FUSED>
+// Any N: per row, pass 1 forms the row sums (dot; LayerNorm: mean(g) and
+// mean(g * xhat)), pass 2 re-reads the row, writes dx and accumulates this
+// workgroup's partial rows in place (each lane always owns the same columns,
+// so the read-modify-write is private to the lane).
+template <typename T, int V, bool FUSED, bool LN>
 __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
 {
     using C = Chunk<T, V>;
@@ -216,14 +305,21 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
     const T *__restrict__ gp = static_cast<const T *>(a.gamma);
     const T *dhp = static_cast<const T *>(a.dh);
     T *dxp = static_cast<T *>(a.dx);
-    float *part = a.partials ? a.partials + (int64_t)blockIdx.x * a.ld : nullptr; // null: non-affine
+    // null: no dgamma (non-affine) and no dbeta
+    float *part = a.partials ? a.partials + (int64_t)blockIdx.x * a.ld : nullptr;
+    float *partb = (LN && a.partials) ? a.partials + (a.grid + (int64_t)blockIdx.x) * a.ld : nullptr;
+    auto wgt = [&](const C &g, int e) __attribute__((always_inline)) {
+        return gp != nullptr ? g.get(e) + a.offset : 1.0f;
+    };
 
-    __shared__ float red[2][16];
+    __shared__ float red[2][32];
     int parity = 0;
     for (int64_t row = blockIdx.x; row < a.M; row += a.grid) {
         const bool first = (row == (int64_t)blockIdx.x);
         const int64_t base = row * N;
-        float dot = 0.0f;
+        const float rs = a.rstd[row];
+        const float mu = LN ? a.mean[row] : 0.0f;
+        float s1 = 0.0f, s2 = 0.0f; // RMSNorm: s1 = dot; LayerNorm: sum g, sum g * xhat
         for (int c = threadIdx.x; c < nchunks; c += nt) {
             C v, d, g;
             v.load_cached(vp + base + (int64_t)c * V);
@@ -231,45 +327,69 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
             if (gp != nullptr)
                 g.load_cached(gp + (int64_t)c * V);
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-                dot = fmaf(d.get(e) * (gp != nullptr ? g.get(e) + a.offset : 1.0f), v.get(e), dot);
+            for (int e = 0; e < V; ++e) {
+                const float gg = d.get(e) * wgt(g, e);
+                if constexpr (LN) {
+                    s1 += gg;
+                    s2 = fmaf(gg, (v.get(e) - mu) * rs, s2);
+                } else {
+                    s1 = fmaf(gg, v.get(e), s1);
+                }
+            }
         }
-        dot = block_sum(dot, red[parity], a.threads);
+        if constexpr (LN) {
+            block_sum2(s1, s2, red[parity], a.threads);
+        } else {
+            s1 = block_sum(s1, red[parity], a.threads);
+        }
         parity ^= 1;
-        const float rs = a.rstd[row];
-        const float kc = rs * rs * rs * dot * inv_n;
+        const float kc = rs * rs * rs * s1 * inv_n;       // RMSNorm
+        const float c1 = s1 * inv_n, c2 = s2 * inv_n;     // LayerNorm
         for (int c = threadIdx.x; c < nchunks; c += nt) {
             C v, d, g;
             v.load_cached(vp + base + (int64_t)c * V);
             d.load_cached(dyp + base + (int64_t)c * V);
             if (gp != nullptr)
                 g.load_cached(gp + (int64_t)c * V);
-            float o[V], pa[V];
+            float o[V], pa[V], pb[V];
             if (first || part == nullptr) {
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    pa[e] = 0.0f;
+                    pa[e] = pb[e] = 0.0f;
             } else {
                 load_f32<V>(part + (int64_t)c * V, pa);
+                if constexpr (LN)
+                    load_f32<V>(partb + (int64_t)c * V, pb);
             }
             C dh;
             if constexpr (FUSED)
                 dh.load_cached(dhp + base + (int64_t)c * V);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const float xv = v.get(e);
                 const float dv = d.get(e);
-                float dxv = fmaf(rs, dv * (gp != nullptr ? g.get(e) + a.offset : 1.0f), -xv * kc);
+                float dxv;
+                if constexpr (LN) {
+                    const float xh = (v.get(e) - mu) * rs;
+                    dxv = rs * fmaf(-xh, c2, dv * wgt(g, e) - c1);
+                    pa[e] = fmaf(dv, xh, pa[e]);
+                    pb[e] += dv;
+                } else {
+                    const float xv = v.get(e);
+                    dxv = fmaf(rs, dv * wgt(g, e), -xv * kc);
+                    pa[e] = fmaf(dv, xv * rs, pa[e]);
+                }
                 if constexpr (FUSED)
                     dxv += dh.get(e);
                 o[e] = dxv;
-                pa[e] = fmaf(dv, xv * rs, pa[e]);
             }
             C out;
             out.set(o);
             out.store(dxp + base + (int64_t)c * V);
-            if (part != nullptr)
+            if (part != nullptr) {
                 store_f32<V>(part + (int64_t)c * V, pa);
+                if constexpr (LN)
+                    store_f32<V>(partb + (int64_t)c * V, pb);
+            }
         }
     }
 }
@@ -281,9 +401,16 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
 // latencies overlap; the 32 group sums are then added in pg order.  The order
 // depends only on P, so dgamma is bit-reproducible.
 template <typename T>
-__global__ void __launch_bounds__(kFinThreads) finalize_kernel(const float *__restrict__ part, int64_t P,
-                                                               int64_t ld, int64_t N, T *__restrict__ dg)
+__global__ void __launch_bounds__(kFinThreads) finalize_kernel(const float *__restrict__ part0, int64_t P,
+                                                               int64_t ld, int64_t N, T *__restrict__ dg0,
+                                                               T *__restrict__ db)
 {
+    // workgroup row 0: dgamma from the first P partial rows; row 1
+    // (LayerNorm): dbeta from the next P
+    const float *__restrict__ part = part0 + (int64_t)blockIdx.y * P * ld;
+    T *__restrict__ dg = blockIdx.y ? db : dg0;
+    if (dg == nullptr)
+        return; // the whole workgroup: this output was not asked for
     constexpr int CG = kFinColsPerBlock / 4; // float4 groups per workgroup
     constexpr int PG = kFinThreads / CG;     // partial-row groups
     constexpr int kFinDepth = 16;
@@ -334,23 +461,24 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(const float *__re
     }
 }
 
-template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FUSED>
+template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FUSED, bool LN>
 static void launch_bwd_rows(const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s)
 {
     const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
     const int lanes = TEAM ? TEAM : p.threads;
-    const size_t lds = TEAM ? (size_t)(p.threads / TEAM) * (size_t)a.N * sizeof(float) : 0;
+    const size_t sets = LN ? 2 : 1;
+    const size_t lds = TEAM ? sets * (size_t)(p.threads / TEAM) * (size_t)a.N * sizeof(float) : 0;
     if constexpr (V > 1) {
         if ((int64_t)lanes * K == a.N / V) {
-            hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, true>), grid, block, lds, s,
+            hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, true, LN>), grid, block, lds, s,
                                a);
             return;
         }
     }
-    hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, false>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, false, LN>), grid, block, lds, s, a);
 }
 
-template <typename T, bool FUSED>
+template <typename T, bool FUSED, bool LN>
 static hipError_t dispatch_bwd(const rmsnorm_plan &p, BwdArgs a, hipStream_t s)
 {
     constexpr int VV = 16 / (int)sizeof(T);
@@ -359,39 +487,49 @@ static hipError_t dispatch_bwd(const rmsnorm_plan &p, BwdArgs a, hipStream_t s)
     const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
     if (p.path == RMSNORM_PATH_LOOP) {
         if (p.vec == VV)
-            hipLaunchKernelGGL((bwd_loop_kernel<T, VV, FUSED>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((bwd_loop_kernel<T, VV, FUSED, LN>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((bwd_loop_kernel<T, 1, FUSED>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((bwd_loop_kernel<T, 1, FUSED, LN>), grid, block, 0, s, a);
         return hipGetLastError();
     }
     const bool vec = (p.vec == VV);
 #define RMSNORM_CASE(VEC, TEAM, K, D, WR, BOUND, FBOUND)                                      \
     if (vec == (VEC == 1) && p.team == TEAM && p.chunks == K && p.depth == D && p.w_regs == WR) { \
-        launch_bwd_rows<T, (VEC == 1 ? VV : 1), TEAM, K, D, WR == 1, (FUSED ? FBOUND : BOUND), FUSED>(p, a, s); \
+        launch_bwd_rows<T, (VEC == 1 ? VV : 1), TEAM, K, D, WR == 1, (FUSED ? FBOUND : BOUND), FUSED, LN>(p, a, s); \
         return hipGetLastError();                                                                 \
     }
-    RMSNORM_BWD_ROWS_CONFIGS(RMSNORM_CASE)
+    if constexpr (LN) {
+        RMSNORM_LN_BWD_ROWS_CONFIGS(RMSNORM_CASE)
+    } else {
+        RMSNORM_BWD_ROWS_CONFIGS(RMSNORM_CASE)
+    }
 #undef RMSNORM_CASE
     return hipErrorInvalidConfiguration;
 }
 
-hipError_t launch_bwd(int dtype, bool fused, const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s)
+hipError_t launch_bwd(int dtype, bool fused, bool ln, const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s)
 {
-    if (dtype == RMSNORM_BF16)
-        return fused ? dispatch_bwd<bf16_t, true>(p, a, s) : dispatch_bwd<bf16_t, false>(p, a, s);
-    return fused ? dispatch_bwd<float, true>(p, a, s) : dispatch_bwd<float, false>(p, a, s);
+    if (dtype == RMSNORM_BF16) {
+        if (ln)
+            return fused ? dispatch_bwd<bf16_t, true, true>(p, a, s) : dispatch_bwd<bf16_t, false, true>(p, a, s);
+        return fused ? dispatch_bwd<bf16_t, true, false>(p, a, s) : dispatch_bwd<bf16_t, false, false>(p, a, s);
+    }
+    if (ln)
+        return fused ? dispatch_bwd<float, true, true>(p, a, s) : dispatch_bwd<float, false, true>(p, a, s);
+    return fused ? dispatch_bwd<float, true, false>(p, a, s) : dispatch_bwd<float, false, false>(p, a, s);
 }
 
 hipError_t launch_finalize(int dtype, const float *partials, int64_t programs, int64_t ld, int64_t N,
-                           void *dgamma, hipStream_t s)
+                           void *dgamma, void *dbeta, hipStream_t s)
 {
-    const dim3 grid((unsigned)((ld + kFinColsPerBlock - 1) / kFinColsPerBlock)), block(kFinThreads);
+    const dim3 grid((unsigned)((ld + kFinColsPerBlock - 1) / kFinColsPerBlock), dbeta ? 2u : 1u),
+        block(kFinThreads);
     if (dtype == RMSNORM_BF16)
         hipLaunchKernelGGL((finalize_kernel<bf16_t>), grid, block, 0, s, partials, programs, ld, N,
-                           static_cast<bf16_t *>(dgamma));
+                           static_cast<bf16_t *>(dgamma), static_cast<bf16_t *>(dbeta));
     else
         hipLaunchKernelGGL((finalize_kernel<float>), grid, block, 0, s, partials, programs, ld, N,
-                           static_cast<float *>(dgamma));
+                           static_cast<float *>(dgamma), static_cast<float *>(dbeta));
     return hipGetLastError();
 }
 

@@ -285,6 +285,29 @@ __device__ __forceinline__ float block_sum(float v, float *slot, int threads)
     return s;
 }
 
+// Two sums over the whole workgroup with one barrier (as block_sum; `slot`
+// holds 32 floats, callers alternate slots as for block_sum).
+__device__ __forceinline__ void block_sum2(float &a, float &b, float *slot, int threads)
+{
+    a = team_sum<64>(a);
+    b = team_sum<64>(b);
+    const int nw = threads >> 6;
+    if (nw == 1)
+        return;
+    if ((threadIdx.x & 63) == 0) {
+        slot[threadIdx.x >> 6] = a;
+        slot[16 + (threadIdx.x >> 6)] = b;
+    }
+    lds_barrier();
+    float sa = slot[0], sb = slot[16];
+    for (int i = 1; i < nw; ++i) {
+        sa += slot[i];
+        sb += slot[16 + i];
+    }
+    a = sa;
+    b = sb;
+}
+
 // Maximum over the whole workgroup (as block_sum; `slot` holds 16 floats and
 // must not be in use by a concurrent block_sum).
 __device__ __forceinline__ float block_max(float v, float *slot, int threads)

@@ -20,6 +20,12 @@
 // caller's amax.  One atomic max per workgroup on a single address was
 // measured on MI355X at about 8.5 ns each, serialised (4096 workgroups: +35 us
 // on a 21 us kernel), hence the two stages.
+//
+// LayerNorm (LN; TransformerEngine PR #583 registers matching LayerNorm
+// configurations): the same layouts with two reductions per row, the mean
+// first and then the sum of squared deviations of the register-held row
+// (two-pass, so no cancellation between E[v^2] and E[v]^2), then
+// y = (v - mean) * rstd * (gamma + offset) + beta.
 #include <algorithm>
 
 #include "device_common.h"
@@ -62,7 +68,7 @@ __device__ __forceinline__ void write_amax_part(float am, const FwdArgs &a)
         a.amax_part[blockIdx.x] = am;
 }
 
-template <typename T, int V, int TEAM, int K, int D, bool FUSED, bool EXACT, bool F8>
+template <typename T, int V, int TEAM, int K, int D, bool FUSED, bool EXACT, bool F8, bool LN>
 __global__ void __launch_bounds__(fwd_rows_bound_rule(TEAM, K)) fwd_rows_kernel(FwdArgs a)
 {
     using C = Chunk<T, V>;
@@ -100,6 +106,18 @@ __global__ void __launch_bounds__(fwd_rows_bound_rule(TEAM, K)) fwd_rows_kernel(
         for (int k = 0; k < K; ++k)
             g[k].set(one);
     }
+    C bias[LN ? K : 1]; // LayerNorm bias, or zeros
+    if constexpr (LN) {
+        const T *__restrict__ beta = static_cast<const T *>(a.beta);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * tl + lane;
+            if (beta != nullptr && (EXACT || c < nchunks))
+                bias[k].load_cached(beta + (int64_t)c * V);
+            else
+                bias[k].zero();
+        }
+    }
 
     auto load = [&](Row &b, int64_t row) __attribute__((always_inline)) {
         const int64_t base = row * N;
@@ -116,45 +134,91 @@ __global__ void __launch_bounds__(fwd_rows_bound_rule(TEAM, K)) fwd_rows_kernel(
 
     __shared__ float red[2][16];
     int parity = 0;
+    auto reduce = [&](float v) __attribute__((always_inline)) {
+        if constexpr (TEAM == 0) {
+            v = block_sum(v, red[parity], a.threads);
+            parity ^= 1;
+        } else {
+            v = team_sum<TEAM>(v);
+        }
+        return v;
+    };
     auto proc = [&](Row &b, int64_t row) __attribute__((always_inline)) {
         const int64_t base = row * N;
-        float ss = 0.0f;
+        float ss = 0.0f; // sum of squares (LayerNorm: of the deviations from the mean)
+        float mu = 0.0f; // LayerNorm: the row mean
+        if constexpr (!LN) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int c = k * tl + lane;
-            if (EXACT || c < nchunks) {
-                if constexpr (FUSED) {
-                    float f[V];
+            for (int k = 0; k < K; ++k) {
+                const int c = k * tl + lane;
+                if (EXACT || c < nchunks) {
+                    if constexpr (FUSED) {
+                        float f[V];
+#pragma unroll
+                        for (int e = 0; e < V; ++e)
+                            f[e] = b.x[k].get(e) + b.r[k].get(e);
+                        b.x[k].set(f); // h, rounded to the storage type
+                        b.x[k].store(h + base + (int64_t)c * V);
+                    }
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        const float t = b.x[k].get(e);
+                        ss = fmaf(t, t, ss);
+                    }
+                }
+            }
+        } else {
+            float s1 = 0.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int c = k * tl + lane;
+                if (EXACT || c < nchunks) {
+                    if constexpr (FUSED) {
+                        float f[V];
+#pragma unroll
+                        for (int e = 0; e < V; ++e)
+                            f[e] = b.x[k].get(e) + b.r[k].get(e);
+                        b.x[k].set(f);
+                        b.x[k].store(h + base + (int64_t)c * V);
+                    }
 #pragma unroll
                     for (int e = 0; e < V; ++e)
-                        f[e] = b.x[k].get(e) + b.r[k].get(e);
-                    b.x[k].set(f); // h, rounded to the storage type
-                    b.x[k].store(h + base + (int64_t)c * V);
+                        s1 += b.x[k].get(e);
                 }
+            }
+            mu = reduce(s1) * inv_n;
 #pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    const float t = b.x[k].get(e);
-                    ss = fmaf(t, t, ss);
+            for (int k = 0; k < K; ++k) {
+                const int c = k * tl + lane;
+                if (EXACT || c < nchunks) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        const float t = b.x[k].get(e) - mu;
+                        ss = fmaf(t, t, ss);
+                    }
                 }
             }
         }
-        if constexpr (TEAM == 0) {
-            ss = block_sum(ss, red[parity], a.threads);
-            parity ^= 1;
-        } else {
-            ss = team_sum<TEAM>(ss);
-        }
+        ss = reduce(ss);
         const float rs = rsqrtf(fmaf(ss, inv_n, a.eps));
         if (rstd != nullptr)
             rstd[row] = rs; // every lane of the team stores the same value
+        if constexpr (LN) {
+            if (a.mean != nullptr)
+                a.mean[row] = mu;
+        }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int c = k * tl + lane;
             if (EXACT || c < nchunks) {
                 float f[V];
 #pragma unroll
-                for (int e = 0; e < V; ++e)
-                    f[e] = (b.x[k].get(e) * rs) * (g[k].get(e) + a.offset);
+                for (int e = 0; e < V; ++e) {
+                    if constexpr (LN)
+                        f[e] = fmaf((b.x[k].get(e) - mu) * rs, g[k].get(e) + a.offset, bias[k].get(e));
+                    else
+                        f[e] = (b.x[k].get(e) * rs) * (g[k].get(e) + a.offset);
+                }
                 store_row_out<T, V, F8>(y, base + (int64_t)c * V, f, scale, am);
             }
         }
@@ -167,7 +231,7 @@ __global__ void __launch_bounds__(fwd_rows_bound_rule(TEAM, K)) fwd_rows_kernel(
 
 // Any N: pass 1 sums squares (and writes h for fused-add), pass 2 re-reads the
 // row (recomputing h from x and r) and writes y.
-template <typename T, int V, bool FUSED, bool F8>
+template <typename T, int V, bool FUSED, bool F8, bool LN>
 __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
 {
     using C = Chunk<T, V>;
@@ -177,66 +241,102 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
     const float inv_n = 1.0f / (float)N;
     const T *__restrict__ x = static_cast<const T *>(a.x);
     const T *__restrict__ gamma = static_cast<const T *>(a.gamma);
+    const T *__restrict__ beta = static_cast<const T *>(a.beta);
     const T *r = static_cast<const T *>(a.r);
     T *h = static_cast<T *>(a.h);
     void *__restrict__ y = a.y;
     const float scale = F8 ? *a.scale : 1.0f;
     float am = 0.0f;
 
+    // chunk c of the row at base: x, or round(x + r) for fused-add (written to
+    // h on the first pass)
+    auto row_chunk = [&](int64_t base, int c, bool write_h) __attribute__((always_inline)) {
+        C v;
+        v.load_cached(x + base + (int64_t)c * V);
+        if constexpr (FUSED) {
+            C rc;
+            rc.load_cached(r + base + (int64_t)c * V);
+            float f[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                f[e] = v.get(e) + rc.get(e);
+            v.set(f);
+            if (write_h)
+                v.store(h + base + (int64_t)c * V);
+        }
+        return v;
+    };
+
     __shared__ float red[2][16];
     int parity = 0;
     for (int64_t row = blockIdx.x; row < a.M; row += a.grid) {
         const int64_t base = row * N;
-        float ss = 0.0f;
-        for (int c = threadIdx.x; c < nchunks; c += nt) {
-            C v;
-            v.load_cached(x + base + (int64_t)c * V);
-            if constexpr (FUSED) {
-                C rc;
-                rc.load_cached(r + base + (int64_t)c * V);
-                float f[V];
+        float mu = 0.0f;
+        if constexpr (LN) { // pass 1: the mean (and h)
+            float s1 = 0.0f;
+            for (int c = threadIdx.x; c < nchunks; c += nt) {
+                const C v = row_chunk(base, c, true);
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    f[e] = v.get(e) + rc.get(e);
-                v.set(f);
-                v.store(h + base + (int64_t)c * V);
+                    s1 += v.get(e);
             }
+            mu = block_sum(s1, red[parity], a.threads) * inv_n;
+            parity ^= 1;
+        }
+        float ss = 0.0f; // sum of squares (of deviations, LayerNorm)
+        for (int c = threadIdx.x; c < nchunks; c += nt) {
+            const C v = row_chunk(base, c, !LN);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const float t = v.get(e);
+                const float t = v.get(e) - mu;
                 ss = fmaf(t, t, ss);
             }
         }
         ss = block_sum(ss, red[parity], a.threads);
         parity ^= 1;
         const float rs = rsqrtf(fmaf(ss, inv_n, a.eps));
-        if (a.rstd != nullptr && threadIdx.x == 0)
-            a.rstd[row] = rs;
+        if (threadIdx.x == 0) {
+            if (a.rstd != nullptr)
+                a.rstd[row] = rs;
+            if constexpr (LN) {
+                if (a.mean != nullptr)
+                    a.mean[row] = mu;
+            }
+        }
         if (y == nullptr)
             continue;
         for (int c = threadIdx.x; c < nchunks; c += nt) {
-            C v;
-            v.load_cached(x + base + (int64_t)c * V);
-            if constexpr (FUSED) {
-                C rc;
-                rc.load_cached(r + base + (int64_t)c * V);
-                float f[V];
-#pragma unroll
-                for (int e = 0; e < V; ++e)
-                    f[e] = v.get(e) + rc.get(e);
-                v.set(f);
-            }
-            float f[V];
+            const C v = row_chunk(base, c, false);
+            float w[V], bb[V];
             if (gamma != nullptr) {
                 C g;
                 g.load_cached(gamma + (int64_t)c * V);
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    f[e] = (v.get(e) * rs) * (g.get(e) + a.offset);
+                    w[e] = g.get(e) + a.offset;
             } else {
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    f[e] = v.get(e) * rs;
+                    w[e] = 1.0f;
+            }
+            if (LN && beta != nullptr) {
+                C bc;
+                bc.load_cached(beta + (int64_t)c * V);
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    bb[e] = bc.get(e);
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    bb[e] = 0.0f;
+            }
+            float f[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                if constexpr (LN)
+                    f[e] = fmaf((v.get(e) - mu) * rs, w[e], bb[e]);
+                else
+                    f[e] = (v.get(e) * rs) * w[e];
             }
             store_row_out<T, V, F8>(y, base + (int64_t)c * V, f, scale, am);
         }
@@ -281,43 +381,45 @@ __global__ void __launch_bounds__(kAmaxThreads) amax_finalize_kernel(const float
         *amax = fmaxf(*amax, m);
 }
 
-template <typename T, int V, int TEAM, int K, int D, bool FUSED, bool F8>
+template <typename T, int V, int TEAM, int K, int D, bool FUSED, bool F8, bool LN>
 static void launch_fwd_rows(const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s)
 {
     const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
     const int lanes = TEAM ? TEAM : p.threads;
     if constexpr (V > 1) {
         if ((int64_t)lanes * K == a.N / V) {
-            hipLaunchKernelGGL((fwd_rows_kernel<T, V, TEAM, K, D, FUSED, true, F8>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((fwd_rows_kernel<T, V, TEAM, K, D, FUSED, true, F8, LN>), grid, block, 0, s, a);
             return;
         }
     }
-    hipLaunchKernelGGL((fwd_rows_kernel<T, V, TEAM, K, D, FUSED, false, F8>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fwd_rows_kernel<T, V, TEAM, K, D, FUSED, false, F8, LN>), grid, block, 0, s, a);
 }
 
-template <typename T, bool FUSED, bool F8>
+template <typename T, bool FUSED, bool F8, bool LN>
 static hipError_t dispatch_fwd(const rmsnorm_plan &p, FwdArgs a, hipStream_t s)
 {
     constexpr int VV = 16 / (int)sizeof(T);
     a.threads = p.threads;
     a.grid = p.grid;
     if (p.path == RMSNORM_PATH_LOOP || a.y == nullptr) {
-        // rstd-only forwards (y == nullptr) also take the looped kernel
+        // statistics-only forwards (y == nullptr) also take the looped kernel
         const dim3 grid((unsigned)std::min<int64_t>(a.M, 1 << 30)), block(256);
         a.threads = p.path == RMSNORM_PATH_LOOP ? p.threads : 256;
         a.grid = p.path == RMSNORM_PATH_LOOP ? p.grid : grid.x;
         const dim3 g2((unsigned)a.grid), b2((unsigned)a.threads);
         if (p.vec == VV)
-            hipLaunchKernelGGL((fwd_loop_kernel<T, VV, FUSED, F8>), g2, b2, 0, s, a);
+            hipLaunchKernelGGL((fwd_loop_kernel<T, VV, FUSED, F8, LN>), g2, b2, 0, s, a);
         else
-            hipLaunchKernelGGL((fwd_loop_kernel<T, 1, FUSED, F8>), g2, b2, 0, s, a);
+            hipLaunchKernelGGL((fwd_loop_kernel<T, 1, FUSED, F8, LN>), g2, b2, 0, s, a);
         return hipGetLastError();
     }
     const bool vec = (p.vec == VV);
+    // fp8 output and LayerNorm exist for the layouts without prefetch, and
+    // LayerNorm (which also holds beta) for at most kLnFwdMaxChunks chunks
 #define RMSNORM_CASE(VEC, TEAM, K, D)                                                        \
-    if constexpr (!F8 || D == 0) {                                                           \
+    if constexpr ((!F8 && !LN) || (D == 0 && (!LN || K <= kLnFwdMaxChunks))) {               \
         if (vec == (VEC == 1) && p.team == TEAM && p.chunks == K && p.depth == D) {          \
-            launch_fwd_rows<T, (VEC == 1 ? VV : 1), TEAM, K, D, FUSED, F8>(p, a, s);         \
+            launch_fwd_rows<T, (VEC == 1 ? VV : 1), TEAM, K, D, FUSED, F8, LN>(p, a, s);     \
             return hipGetLastError();                                                        \
         }                                                                                    \
     }
@@ -326,16 +428,21 @@ static hipError_t dispatch_fwd(const rmsnorm_plan &p, FwdArgs a, hipStream_t s)
     return hipErrorInvalidConfiguration;
 }
 
-hipError_t launch_fwd(int dtype, bool fused, bool fp8, const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s)
+template <typename T, bool FUSED>
+static hipError_t dispatch_fwd_kind(FwdKind kind, const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s)
 {
-    if (dtype == RMSNORM_BF16) {
-        if (fp8)
-            return fused ? dispatch_fwd<bf16_t, true, true>(p, a, s) : dispatch_fwd<bf16_t, false, true>(p, a, s);
-        return fused ? dispatch_fwd<bf16_t, true, false>(p, a, s) : dispatch_fwd<bf16_t, false, false>(p, a, s);
+    switch (kind) {
+    case FWD_RMS_FP8: return dispatch_fwd<T, FUSED, true, false>(p, a, s);
+    case FWD_LN: return dispatch_fwd<T, FUSED, false, true>(p, a, s);
+    default: return dispatch_fwd<T, FUSED, false, false>(p, a, s);
     }
-    if (fp8)
-        return fused ? dispatch_fwd<float, true, true>(p, a, s) : dispatch_fwd<float, false, true>(p, a, s);
-    return fused ? dispatch_fwd<float, true, false>(p, a, s) : dispatch_fwd<float, false, false>(p, a, s);
+}
+
+hipError_t launch_fwd(int dtype, bool fused, FwdKind kind, const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s)
+{
+    if (dtype == RMSNORM_BF16)
+        return fused ? dispatch_fwd_kind<bf16_t, true>(kind, p, a, s) : dispatch_fwd_kind<bf16_t, false>(kind, p, a, s);
+    return fused ? dispatch_fwd_kind<float, true>(kind, p, a, s) : dispatch_fwd_kind<float, false>(kind, p, a, s);
 }
 
 hipError_t launch_amax_finalize(const float *part, int64_t programs, float *amax, hipStream_t s)

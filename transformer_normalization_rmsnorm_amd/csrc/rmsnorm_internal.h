@@ -28,6 +28,9 @@ struct FwdArgs {
     // writes max |y| to amax_part[blockIdx.x] when amax_part is not null
     const float *scale = nullptr;
     float *amax_part = nullptr;
+    // LayerNorm only: bias (may be null) and the saved row means (may be null)
+    const void *beta = nullptr;
+    float *mean = nullptr;
 };
 
 struct BwdArgs {
@@ -44,6 +47,9 @@ struct BwdArgs {
     float offset;
     int32_t threads; // workgroup size of the launch
     int64_t grid;    // workgroups of the launch
+    // LayerNorm only: the saved row means; the dbeta partials follow the
+    // dgamma partials (program p's dbeta row at partials[(grid + p) * ld])
+    const float *mean = nullptr;
 };
 
 // Partial rows are padded to this many floats (256 bytes).
@@ -92,6 +98,21 @@ constexpr int kFinColsPerBlock = 32;
     X(0, 64, 1, 1, 1, 256, 256) X(0, 64, 2, 1, 1, 256, 256) X(0, 0, 1, 1, 1, 1024, 1024) \
     X(0, 0, 2, 1, 1, 512, 512) X(0, 0, 4, 1, 1, 512, 512)
 
+// LayerNorm backward: the same fields.  It also holds the row mean and a
+// second set of accumulators (dbeta), so its bounds are its own.
+#define RMSNORM_LN_BWD_ROWS_CONFIGS(X)                                                   \
+    X(1, 8, 1, 1, 1, 256, 256) X(1, 16, 1, 1, 1, 256, 256) X(1, 32, 1, 1, 1, 256, 256)   \
+    X(1, 64, 1, 1, 1, 256, 256) X(1, 64, 2, 1, 1, 256, 256)                              \
+    X(1, 0, 1, 1, 1, 1024, 1024) X(1, 0, 1, 2, 1, 1024, 1024)                            \
+    X(1, 0, 2, 0, 0, 1024, 1024) X(1, 0, 2, 1, 0, 512, 512) X(1, 0, 3, 0, 0, 1024, 1024) \
+    X(1, 0, 4, 0, 0, 512, 512) X(1, 0, 4, 1, 0, 512, 512) X(1, 0, 6, 0, 0, 512, 512)     \
+    X(0, 64, 1, 1, 1, 256, 256) X(0, 64, 2, 1, 1, 256, 256) X(0, 0, 1, 1, 1, 1024, 1024) \
+    X(0, 0, 2, 1, 1, 512, 512) X(0, 0, 4, 1, 1, 512, 512)
+
+// LayerNorm forward: the forward layouts without prefetch, up to this many
+// chunks per lane (it also holds beta; eight chunks spill).
+constexpr int kLnFwdMaxChunks = 6;
+
 // Forward launch bound: teams of at most a wavefront run in 256-thread
 // workgroups; a workgroup team holding more than two chunks per lane is capped
 // at 512 threads so that it may use up to 256 VGPRs instead of spilling.
@@ -112,13 +133,17 @@ inline int fwd_rows_bound(bool vec, int team, int chunks, int depth)
 }
 
 // Launch bound of a compiled backward configuration, 0 if it is not compiled.
-inline int bwd_rows_bound(bool fused, bool vec, int team, int chunks, int depth, int w_regs)
+inline int bwd_rows_bound(bool ln, bool fused, bool vec, int team, int chunks, int depth, int w_regs)
 {
 #define RMSNORM_MATCH(V, TEAM, K, D, WR, BOUND, FBOUND)                                  \
     if ((V) == (vec ? 1 : 0) && (TEAM) == team && (K) == chunks && (D) == depth &&        \
         (WR) == w_regs)                                                                   \
         return fused ? (FBOUND) : (BOUND);
-    RMSNORM_BWD_ROWS_CONFIGS(RMSNORM_MATCH)
+    if (ln) {
+        RMSNORM_LN_BWD_ROWS_CONFIGS(RMSNORM_MATCH)
+    } else {
+        RMSNORM_BWD_ROWS_CONFIGS(RMSNORM_MATCH)
+    }
 #undef RMSNORM_MATCH
     return 0;
 }
@@ -132,20 +157,37 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
 // Fill the derived fields (chunks, grid, programs, workspace, finalizer) of a
 // plan whose path/vec/team/threads are set; returns false if it cannot run.
 bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus, bool keep_grid);
-int64_t bwd_workspace_bytes(int64_t programs, int64_t M, int64_t N);
+int64_t bwd_workspace_bytes(int64_t programs, int64_t M, int64_t N, bool ln);
 
 // Ops with fp8 output (the forward with y in E4M3).
 inline bool is_fp8_op(int op) { return op == RMSNORM_OP_FWD_FP8 || op == RMSNORM_OP_FUSED_ADD_FWD_FP8; }
+// LayerNorm ops.
+inline bool is_ln_op(int op) { return op >= RMSNORM_OP_LN_FWD && op <= RMSNORM_OP_LN_FUSED_ADD_BWD; }
+inline bool is_bwd_op(int op)
+{
+    return op == RMSNORM_OP_BWD || op == RMSNORM_OP_FUSED_ADD_BWD || op == RMSNORM_OP_LN_BWD ||
+           op == RMSNORM_OP_LN_FUSED_ADD_BWD;
+}
+inline bool is_fused_op(int op)
+{
+    return op == RMSNORM_OP_FUSED_ADD_FWD || op == RMSNORM_OP_FUSED_ADD_BWD || op == RMSNORM_OP_FUSED_ADD_FWD_FP8 ||
+           op == RMSNORM_OP_LN_FUSED_ADD_FWD || op == RMSNORM_OP_LN_FUSED_ADD_BWD;
+}
+
+// Forward kernel families.
+enum FwdKind { FWD_RMS = 0, FWD_RMS_FP8 = 1, FWD_LN = 2 };
 
 // amax finalizer: one workgroup folds the per-workgroup maxima.
 constexpr int kAmaxThreads = 1024;
 
 // Kernel launchers (fwd_kernels.hip, bwd_kernels.hip).  fp8: y is E4M3 (only
 // the layouts without prefetch are compiled for it).
-hipError_t launch_fwd(int dtype, bool fused, bool fp8, const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s);
+hipError_t launch_fwd(int dtype, bool fused, FwdKind kind, const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s);
 hipError_t launch_amax_finalize(const float *part, int64_t programs, float *amax, hipStream_t s);
-hipError_t launch_bwd(int dtype, bool fused, const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s);
+hipError_t launch_bwd(int dtype, bool fused, bool ln, const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s);
+// dgamma_j = sum_p partials[p * ld + j]; with dbeta (LayerNorm) also
+// dbeta_j = sum_p partials[(programs + p) * ld + j].  Either output may be null.
 hipError_t launch_finalize(int dtype, const float *partials, int64_t programs, int64_t ld, int64_t N,
-                           void *dgamma, hipStream_t s);
+                           void *dgamma, void *dbeta, hipStream_t s);
 
 } // namespace rmsnorm

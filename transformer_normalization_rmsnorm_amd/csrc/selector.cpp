@@ -33,19 +33,19 @@ int pow2_at_least(int64_t v)
     return p;
 }
 
-bool is_bwd(int op) { return op == RMSNORM_OP_BWD || op == RMSNORM_OP_FUSED_ADD_BWD; }
-bool is_fused(int op)
-{
-    return op == RMSNORM_OP_FUSED_ADD_FWD || op == RMSNORM_OP_FUSED_ADD_BWD || op == RMSNORM_OP_FUSED_ADD_FWD_FP8;
-}
+bool is_bwd(int op) { return is_bwd_op(op); }
+bool is_fused(int op) { return is_fused_op(op); }
 
 // Launch bound of a compiled configuration, 0 if it is not compiled (the
 // forward has no w_regs variants: it is always 0 there).
 int bound(int op, bool vec, int team, int k, int depth, int w_regs)
 {
     if (is_bwd(op))
-        return bwd_rows_bound(is_fused(op), vec, team, k, depth, w_regs);
-    if (is_fp8_op(op) && depth != 0) // fp8 output: layouts without prefetch only
+        return bwd_rows_bound(is_ln_op(op), is_fused(op), vec, team, k, depth, w_regs);
+    // fp8 output and LayerNorm: the forward layouts without prefetch only
+    if ((is_fp8_op(op) || is_ln_op(op)) && depth != 0)
+        return 0;
+    if (is_ln_op(op) && k > kLnFwdMaxChunks)
         return 0;
     return w_regs == 0 ? fwd_rows_bound(vec, team, k, depth) : 0;
 }
@@ -147,10 +147,14 @@ bool pick_fwd_block_team(int op, bool vec, int64_t nchunks, int depth, int targe
 
 } // namespace
 
-int64_t bwd_workspace_bytes(int64_t programs, int64_t M, int64_t N)
+// Backward workspace: the partial rows (LayerNorm: dgamma's then dbeta's),
+// then room for the row statistics recomputed when the caller has none
+// (rstd; LayerNorm also the means).
+int64_t bwd_workspace_bytes(int64_t programs, int64_t M, int64_t N, bool ln)
 {
-    return round_up(programs * partial_ld(N) * (int64_t)sizeof(float), 256) +
-           round_up(M * (int64_t)sizeof(float), 256);
+    const int64_t sets = ln ? 2 : 1;
+    return round_up(sets * programs * partial_ld(N) * (int64_t)sizeof(float), 256) +
+           sets * round_up(M * (int64_t)sizeof(float), 256);
 }
 
 bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus, bool keep_grid)
@@ -182,7 +186,8 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
         if (k == 0 || p->threads > bound(p->op, p->vec != 1, p->team, k, p->depth, p->w_regs))
             return false;
         p->chunks = k;
-        if (bwd && p->team != 0 && rows_per_block * N * (int64_t)sizeof(float) > 65536)
+        const int64_t sets = is_ln_op(p->op) ? 2 : 1;
+        if (bwd && p->team != 0 && sets * rows_per_block * N * (int64_t)sizeof(float) > 65536)
             return false; // team partials are combined in LDS
     } else if (p->path == RMSNORM_PATH_LOOP) {
         p->team = 0;
@@ -198,9 +203,9 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
         const int64_t want = keep_grid && p->grid > 0 ? p->grid : (int64_t)per_cu * std::max(num_cus, 1);
         p->grid = M == 0 ? 0 : std::min(want, blocks_needed);
         p->programs = p->grid;
-        p->workspace_bytes = bwd_workspace_bytes(p->programs, M, N);
+        p->workspace_bytes = bwd_workspace_bytes(p->programs, M, N, is_ln_op(p->op));
         p->fin_threads = kFinThreads;
-        p->fin_grid = ceil_div(partial_ld(N), kFinColsPerBlock);
+        p->fin_grid = ceil_div(partial_ld(N), kFinColsPerBlock) * (is_ln_op(p->op) ? 2 : 1);
     } else {
         const int64_t want = keep_grid && p->grid > 0 ? p->grid : blocks_needed;
         p->grid = M == 0 ? 0 : std::min(std::min(want, blocks_needed), kMaxGrid);
@@ -221,7 +226,7 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
 
 int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cus, rmsnorm_plan *out)
 {
-    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_FUSED_ADD_FWD_FP8)
+    if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_LN_FUSED_ADD_BWD)
         return RMSNORM_EINVAL;
     if (dtype != RMSNORM_BF16 && dtype != RMSNORM_F32)
         return RMSNORM_EUNSUPPORTED;
