@@ -192,3 +192,100 @@ def test_layernorm_gradients_are_bit_identical_run_to_run():
         again = gpu_ln(inp, dt, 0.0, False)
         for k in ("y", "mean", "rstd", "dx", "dg", "db"):
             assert np.array_equal(first[k], again[k]), k
+
+
+def test_layernorm_graph_replay_matches_eager():
+    """Fused-add LayerNorm forward + backward captured in a HIP graph; every
+    replay, with eager work and synchronisations between them, equals eager."""
+    M, N, dt = 2048, 4096, "bf16"
+    inp = make_inputs(M, N, dt, fused=True, layernorm=True)
+    x, r, g, b = (to_dev(inp[k], dt) for k in ("x", "residual", "gamma", "beta"))
+    dy, dh = to_dev(inp["dy"], dt), to_dev(inp["dh"], dt)
+    y, h = torch.empty_like(x), torch.empty_like(x)
+    mean, rstd = torch.empty(M, device="cuda"), torch.empty(M, device="cuda")
+    dx, dg, db = torch.empty_like(x), torch.empty_like(g), torch.empty_like(g)
+    ws = torch.empty(rn.layernorm_bwd_workspace_bytes(M, N, rn.BF16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        rn.layernorm_fused_add_fwd(x, r, g, b, EPS, 0.0, y=y, h_out=h, mean=mean, rstd=rstd)
+        rn.layernorm_fused_add_bwd(dy, dh, h, g, mean, rstd, EPS, 0.0, dx=dx, dgamma=dg, dbeta=db, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (y, h, mean, rstd, dx, dg, db)]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for i in range(3):
+        for t in (y, h, mean, rstd, dx, dg, db):
+            t.fill_(float("nan"))
+        _ = (x.float() * 2).sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, c in zip(("y", "h", "mean", "rstd", "dx", "dgamma", "dbeta"), (y, h, mean, rstd, dx, dg, db), ref):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               c.view(torch.int16) if c.dtype == torch.bfloat16 else c.view(torch.int32)), \
+                f"replay {i}: {name} differs"
+
+
+@pytest.mark.parametrize("name", ["bf16_4096x4096", "bf16_16384x7168_fused_add", "f32_16384x6144_offset1",
+                                  "bf16_262144x128_per_head"])
+def test_layernorm_full_size(name):
+    """Benchmark workload shapes with the LayerNorm recipe: y, mean, rstd and dx
+    on a sample of rows, dgamma and dbeta over all rows."""
+    from rmsnorm_inputs import ALL_WORKLOADS, sample_rows
+
+    w = ALL_WORKLOADS[name]
+    print(f"workload {name}", flush=True)
+    inp = make_inputs(w.M, w.N, w.dtype, fused=w.fused, gemma=w.gemma, layernorm=True)
+    got = gpu_ln(inp, w.dtype, w.offset, w.fused)
+    rows = sample_rows(w.M, 48)
+    sub = {k: (v[rows] if v.ndim == 2 else v) for k, v in inp.items()}
+    got_s = {k: (v[rows] if (v is not None and k in ("y", "mean", "rstd", "dx", "h")) else v) for k, v in got.items()}
+    # dgamma / dbeta need every row: the sampled check skips them, the full reference checks them
+    v_full = inp["x"]
+    if w.fused:
+        v_full, _, _ = oracle.fused_add_fwd(inp["x"], inp["residual"], inp["gamma"], w.dtype, EPS, w.offset,
+                                            want_y=False)
+    full = oracle.ln_bwd(inp["dy"], v_full, inp["gamma"], w.dtype, EPS, w.offset,
+                         dh=inp["dh"] if w.fused else None, want_dx=False)
+    for k, ref in (("dg", full["dgamma64"]), ("db", full["dbeta64"])):
+        err = dgamma_error(got[k], ref, w.dtype)
+        assert err <= DGAMMA_TOL[w.dtype], f"{k} relative L2 {err:.3g}"
+    got_s["dg"], got_s["db"] = None, None
+    check_ln_rows(sub, w.dtype, w.offset, w.fused, got_s)
+
+
+def check_ln_rows(inp, dt, offset, fused, got):
+    """check_ln on a row sample: y, h, mean, rstd and dx only."""
+    g, beta = inp["gamma"], inp["beta"]
+    v = inp["x"]
+    if fused:
+        v, _, _ = oracle.fused_add_fwd(inp["x"], inp["residual"], g, dt, EPS, offset, want_y=False)
+        assert np.array_equal(got["h"], v), "h differs"
+    y64, mean64, rstd64 = oracle.ln_fwd(v, g, beta, dt, EPS, offset)
+    vw = widen(v, dt)
+    w = widen(g, dt) + float(np.float32(offset))
+    mabs = np.abs(vw).mean(1)
+    s_y = rstd64[:, None] * np.abs(w) * (np.abs(vw) + mabs[:, None]) + np.abs(widen(beta, dt))
+    check_values("y", got["y"], y64, dt, scale=s_y)
+    rr = check_f32("rstd", got["rstd"], rstd64)
+    assert rr.ok, str(rr)
+    rm = check_f32("mean", got["mean"], mean64, scale=mabs)
+    assert rm.ok, str(rm)
+    dh = inp["dh"] if fused else None
+    out = oracle.ln_bwd(inp["dy"], v, g, dt, EPS, offset, dh=dh, want_dgamma=False, want_dbeta=False)
+    st = out["stats64"]
+    gg = widen(inp["dy"], dt) * w
+    xhat = (vw - mean64[:, None]) * rstd64[:, None]
+    s_dx = rstd64[:, None] * (np.abs(gg) + st[:, 2:3] + np.abs(xhat) * (np.abs(st[:, 1:2]) + st[:, 3:4]))
+    if dh is not None:
+        s_dx = s_dx + np.abs(widen(dh, dt))
+    check_values("dx", got["dx"], out["dx64"], dt, scale=s_dx)
