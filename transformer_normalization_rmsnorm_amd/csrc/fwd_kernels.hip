@@ -119,16 +119,17 @@ __global__ void __launch_bounds__(fwd_rows_bound_rule(TEAM, K)) fwd_rows_kernel(
         }
     }
 
+    // Every row load is issued: lanes past the row's end re-read its last
+    // chunk, and only their sums and stores are masked.
     auto load = [&](Row &b, int64_t row) __attribute__((always_inline)) {
         const int64_t base = row * N;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const int c = k * tl + lane;
-            if (EXACT || c < nchunks) {
-                b.x[k].load(x + base + (int64_t)c * V);
-                if constexpr (FUSED)
-                    b.r[k].load(r + base + (int64_t)c * V);
-            }
+            const int c0 = k * tl + lane;
+            const int c = EXACT ? c0 : min(c0, nchunks - 1);
+            b.x[k].load(x + base + (int64_t)c * V);
+            if constexpr (FUSED)
+                b.r[k].load(r + base + (int64_t)c * V);
         }
     };
 
@@ -186,6 +187,10 @@ __global__ void __launch_bounds__(fwd_rows_bound_rule(TEAM, K)) fwd_rows_kernel(
                         s1 += b.x[k].get(e);
                 }
             }
+            // the row is unpacked again after each reduction, not held twice
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                b.x[k].pin();
             mu = reduce(s1) * inv_n;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
@@ -198,6 +203,9 @@ __global__ void __launch_bounds__(fwd_rows_bound_rule(TEAM, K)) fwd_rows_kernel(
                     }
                 }
             }
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                b.x[k].pin();
         }
         ss = reduce(ss);
         const float rs = rsqrtf(fmaf(ss, inv_n, a.eps));

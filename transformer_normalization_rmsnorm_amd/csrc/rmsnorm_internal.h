@@ -110,8 +110,8 @@ constexpr int kFinColsPerBlock = 32;
     X(0, 0, 2, 1, 1, 512, 512) X(0, 0, 4, 1, 1, 512, 512)
 
 // LayerNorm forward: the forward layouts without prefetch, up to this many
-// chunks per lane (it also holds beta; eight chunks spill).
-constexpr int kLnFwdMaxChunks = 6;
+// chunks per lane (it also holds beta).
+constexpr int kLnFwdMaxChunks = 8;
 
 // Forward launch bound: teams of at most a wavefront run in 256-thread
 // workgroups; a workgroup team holding more than two chunks per lane is capped
