@@ -302,9 +302,9 @@ def test_layernorm_plans(M, N, dt):
         q = plan(op, M, N, dt)
         assert q["workspace_bytes"] == 0 and q["depth"] == 0
         if q["path"] == rn.PATH_ROWS:
-            assert covers(q, N) and q["chunks"] <= 6
+            assert covers(q, N) and q["chunks"] <= 8
             p = plan(rop, M, N, dt)
-            if p["chunks"] <= 6:  # the same layout as RMSNorm's where it fits
+            if p["chunks"] <= 8:  # the same layout as RMSNorm's where it fits
                 assert (p["vec"], p["team"], p["threads"], p["chunks"]) == (q["vec"], q["team"], q["threads"], q["chunks"])
     for op in (rn.OP_LN_BWD, rn.OP_LN_FUSED_ADD_BWD):
         q = plan(op, M, N, dt)
@@ -321,7 +321,14 @@ def test_layernorm_wide_backward_bounds():
     # LayerNorm holds the mean and a second accumulator set: its own bounds
     assert (lambda p: (p["threads"], p["chunks"], p["depth"], p["w_regs"]))(plan(rn.OP_LN_BWD, 4096, 16384)) == (1024, 2, 0, 0)
     assert (lambda p: (p["threads"], p["chunks"], p["depth"], p["w_regs"]))(plan(rn.OP_LN_BWD, 4096, 4096)) == (512, 1, 1, 1)
-    assert plan(rn.OP_LN_BWD, 2048, 32768)["path"] == rn.PATH_LOOP
+    # dbeta in LDS at four or more chunks: plain rows of 32768 bf16 stay in registers;
+    # the fused op (also holding dh) stops at six chunks x 512 threads
+    assert (lambda p: (p["path"], p["threads"], p["chunks"]))(plan(rn.OP_LN_BWD, 2048, 32768)) == (rn.PATH_ROWS, 1024, 4)
+    assert plan(rn.OP_LN_FUSED_ADD_BWD, 2048, 32768)["path"] == rn.PATH_LOOP
+    assert (lambda p: (p["threads"], p["chunks"]))(plan(rn.OP_LN_FUSED_ADD_BWD, 2048, 24576)) == (1024, 3)
+    with rn.plan_override(rn.OP_LN_FUSED_ADD_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=512, depth=0, w_regs=0):
+        with pytest.raises(rn.RMSNormError):  # eight chunks are not compiled for the fused op
+            plan(rn.OP_LN_FUSED_ADD_BWD, 100, 32768)
     with rn.plan_override(rn.OP_LN_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=1024, depth=1, w_regs=0):
         with pytest.raises(rn.RMSNormError):  # two chunks, one row ahead: 512 threads at most
             plan(rn.OP_LN_BWD, 100, 16384)

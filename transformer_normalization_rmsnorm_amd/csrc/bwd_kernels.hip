@@ -64,10 +64,28 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
     T *dxp = static_cast<T *>(a.dx);
     const float *__restrict__ rstd = a.rstd;
 
+    // LayerNorm rows of four or more chunks per lane keep the dbeta
+    // accumulators in LDS instead of registers: each lane owns the slots of
+    // its own columns (no barriers), laid out as float4 planes [V / 4][nchunks]
+    // so that a wavefront's 16-byte accesses are contiguous.
+    constexpr bool BL = LN && TEAM == 0 && K >= 4 && V >= 4;
     constexpr int KW = WR ? K : 1;
-    constexpr int KB = LN ? K : 1;
+    constexpr int KB = (LN && !BL) ? K : 1;
+    constexpr int NPL = V / 4 > 0 ? V / 4 : 1; // float4 planes of the LDS dbeta row
     float w[KW][V], acc[K][V]; // w = gamma + offset, or 1 for the non-affine op
-    float accb[KB][V];         // LayerNorm: the dbeta accumulators
+    float accb[KB][V];         // LayerNorm: the dbeta accumulators (in registers)
+    extern __shared__ float4 lds_db[]; // [NPL][nchunks] when BL
+    if constexpr (BL) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * tl + lane;
+            if (EXACT || c < nchunks) {
+#pragma unroll
+                for (int h = 0; h < NPL; ++h)
+                    lds_db[h * nchunks + c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+        }
+    }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
 #pragma unroll
@@ -110,7 +128,11 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int c0 = k * tl + lane;
-            const int c = EXACT ? c0 : min(c0, nchunks - 1);
+            int c = EXACT ? c0 : min(c0, nchunks - 1);
+            // LayerNorm: form the chunk addresses per row rather than hold the
+            // row-invariant ones (gamma's) in registers across the loop
+            if constexpr (LN)
+                pin_vgpr(c);
             b.v[k].load(vp + base + (int64_t)c * V);
             b.dy[k].load(dyp + base + (int64_t)c * V);
             if constexpr (!WR)
@@ -179,8 +201,22 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
                         dxv += b.dh[k].get(e);
                     o[e] = dxv;
                     acc[k][e] = fmaf(d, xh, acc[k][e]);
-                    if constexpr (LN)
+                    if constexpr (LN && !BL)
                         accb[k][e] += d;
+                }
+                if constexpr (BL) {
+#pragma unroll
+                    for (int h = 0; h < NPL; ++h) {
+                        float4 t = lds_db[h * nchunks + c];
+                        t.x += b.dy[k].get(4 * h + 0);
+                        t.y += b.dy[k].get(4 * h + 1);
+                        t.z += b.dy[k].get(4 * h + 2);
+                        t.w += b.dy[k].get(4 * h + 3);
+                        lds_db[h * nchunks + c] = t;
+                    }
+                    // keep each chunk's LDS update in place: hoisting every
+                    // chunk's read to the top of the pass costs 8 VGPRs a chunk
+                    asm volatile("" ::: "memory");
                 }
                 Chunk<T, V> out;
                 out.set(o);
@@ -253,8 +289,13 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
             const int c = k * tl + lane;
             if (EXACT || c < nchunks) {
                 store_f32<V>(part + (int64_t)c * V, acc[k]);
-                if constexpr (LN)
+                if constexpr (BL) {
+#pragma unroll
+                    for (int h = 0; h < NPL; ++h)
+                        *reinterpret_cast<float4 *>(partb + (int64_t)c * V + 4 * h) = lds_db[h * nchunks + c];
+                } else if constexpr (LN) {
                     store_f32<V>(partb + (int64_t)c * V, accb[k]);
+                }
             }
         }
     } else {
@@ -467,7 +508,11 @@ static void launch_bwd_rows(const rmsnorm_plan &p, const BwdArgs &a, hipStream_t
     const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
     const int lanes = TEAM ? TEAM : p.threads;
     const size_t sets = LN ? 2 : 1;
-    const size_t lds = TEAM ? sets * (size_t)(p.threads / TEAM) * (size_t)a.N * sizeof(float) : 0;
+    // sub-workgroup teams: their partial rows; LayerNorm at four or more
+    // chunks per lane: the dbeta row (N floats)
+    constexpr bool BL = LN && TEAM == 0 && K >= 4 && V >= 4;
+    const size_t lds = TEAM ? sets * (size_t)(p.threads / TEAM) * (size_t)a.N * sizeof(float)
+                            : (BL ? (size_t)a.N * sizeof(float) : 0);
     if constexpr (V > 1) {
         if ((int64_t)lanes * K == a.N / V) {
             hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, true, LN>), grid, block, lds, s,
@@ -494,9 +539,11 @@ static hipError_t dispatch_bwd(const rmsnorm_plan &p, BwdArgs a, hipStream_t s)
     }
     const bool vec = (p.vec == VV);
 #define RMSNORM_CASE(VEC, TEAM, K, D, WR, BOUND, FBOUND)                                      \
-    if (vec == (VEC == 1) && p.team == TEAM && p.chunks == K && p.depth == D && p.w_regs == WR) { \
-        launch_bwd_rows<T, (VEC == 1 ? VV : 1), TEAM, K, D, WR == 1, (FUSED ? FBOUND : BOUND), FUSED, LN>(p, a, s); \
-        return hipGetLastError();                                                                 \
+    if constexpr ((FUSED ? FBOUND : BOUND) > 0) {                                                 \
+        if (vec == (VEC == 1) && p.team == TEAM && p.chunks == K && p.depth == D && p.w_regs == WR) { \
+            launch_bwd_rows<T, (VEC == 1 ? VV : 1), TEAM, K, D, WR == 1, (FUSED ? FBOUND : BOUND), FUSED, LN>(p, a, s); \
+            return hipGetLastError();                                                             \
+        }                                                                                         \
     }
     if constexpr (LN) {
         RMSNORM_LN_BWD_ROWS_CONFIGS(RMSNORM_CASE)

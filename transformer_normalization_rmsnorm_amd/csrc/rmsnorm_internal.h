@@ -99,13 +99,16 @@ constexpr int kFinColsPerBlock = 32;
     X(0, 0, 2, 1, 1, 512, 512) X(0, 0, 4, 1, 1, 512, 512)
 
 // LayerNorm backward: the same fields.  It also holds the row mean and a
-// second set of accumulators (dbeta), so its bounds are its own.
+// second set of accumulators (dbeta; in LDS at four or more vector chunks per
+// lane, N floats per workgroup), so its bounds are its own.  A bound of 0:
+// not compiled for that op.
 #define RMSNORM_LN_BWD_ROWS_CONFIGS(X)                                                   \
     X(1, 8, 1, 1, 1, 256, 256) X(1, 16, 1, 1, 1, 256, 256) X(1, 32, 1, 1, 1, 256, 256)   \
     X(1, 64, 1, 1, 1, 256, 256) X(1, 64, 2, 1, 1, 256, 256)                              \
     X(1, 0, 1, 1, 1, 1024, 1024) X(1, 0, 1, 2, 1, 1024, 1024)                            \
     X(1, 0, 2, 0, 0, 1024, 1024) X(1, 0, 2, 1, 0, 512, 512) X(1, 0, 3, 0, 0, 1024, 1024) \
-    X(1, 0, 4, 0, 0, 512, 512) X(1, 0, 4, 1, 0, 512, 512) X(1, 0, 6, 0, 0, 512, 512)     \
+    X(1, 0, 4, 0, 0, 1024, 512) X(1, 0, 4, 1, 0, 512, 512) X(1, 0, 6, 0, 0, 512, 512)    \
+    X(1, 0, 8, 0, 0, 512, 0)                                                             \
     X(0, 64, 1, 1, 1, 256, 256) X(0, 64, 2, 1, 1, 256, 256) X(0, 0, 1, 1, 1, 1024, 1024) \
     X(0, 0, 2, 1, 1, 512, 512) X(0, 0, 4, 1, 1, 512, 512)
 
