@@ -304,8 +304,11 @@ def test_layernorm_plans(M, N, dt):
         if q["path"] == rn.PATH_ROWS:
             assert covers(q, N) and q["chunks"] <= 8
             p = plan(rop, M, N, dt)
-            if p["chunks"] <= 8:  # the same layout as RMSNorm's where it fits
-                assert (p["vec"], p["team"], p["threads"], p["chunks"]) == (q["vec"], q["team"], q["threads"], q["chunks"])
+            assert (p["vec"], p["team"]) == (q["vec"], q["team"])  # the same kind of layout as RMSNorm's
+            nc = N // q["vec"]
+            if q["team"] == 0 and q["vec"] > 1 and nc <= 4 * 512:  # four chunks: 512-thread bound
+                # LayerNorm's forward keeps at most four chunks per lane when a tiling allows
+                assert q["chunks"] <= 4 and (q["team"] or q["threads"]) * q["chunks"] == nc, q
     for op in (rn.OP_LN_BWD, rn.OP_LN_FUSED_ADD_BWD):
         q = plan(op, M, N, dt)
         if q["path"] == rn.PATH_ROWS:

@@ -260,8 +260,14 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             // fp8 output (a quarter or half of the bf16 / fp32 output bytes):
             // 256 threads at every measured size (4096 x 4096 bf16: 10.4 us
             // against 10.7 us at 128; 16384 x 8192: 64.0 against 68.4 us)
+            // LayerNorm's forward also holds beta and makes two reductions: at
+            // most four chunks per lane where a tiling allows (measured: 4096 x
+            // 16384 bf16 50.5 us at 512 threads against 53.1 us at 256;
+            // 16384 x 8192: 91.4 us at 256 against 94.0 us at 128)
             const int64_t rows_per_cu = M / std::max(num_cus, 1);
-            const int target = is_fp8_op(op) || (rows_per_cu >= 8 && rows_per_cu < 32) ? 256 : 128;
+            int target = is_fp8_op(op) || (rows_per_cu >= 8 && rows_per_cu < 32) ? 256 : 128;
+            if (is_ln_op(op))
+                target = (int)std::max<int64_t>(256, nchunks / 4);
             // backward: w in registers with one chunk per lane (the pages'
             // layout), else gamma re-read per row.  Measured on MI355X, gamma
             // per row with two chunks per lane and one row ahead beats w in
