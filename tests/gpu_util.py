@@ -119,3 +119,77 @@ def gpu_backward(inp, dtype, eps, offset, fwd_out, fused, rstd="gpu"):
 
 def from_dev_opt(t):
     return None if t is None else from_dev(t)
+
+
+def gpu_ln(inp, dt, eps, offset, fused, stats="gpu", affine=True, bias=True):
+    """LayerNorm forward then backward through the binding; numpy results.
+    stats=None makes the backward recompute mean and rstd."""
+    x = to_dev(inp["x"], dt)
+    g = to_dev(inp["gamma"], dt) if affine else None
+    b = to_dev(inp["beta"], dt) if bias else None
+    out = {}
+    if fused:
+        r = to_dev(inp["residual"], dt)
+        y, h, mean, rstd = rn.layernorm_fused_add_fwd(x, r, g, b, eps, offset)
+        out["h"] = h
+    else:
+        y, mean, rstd = rn.layernorm_fwd(x, g, b, eps, offset)
+    out.update(y=y, mean=mean, rstd=rstd)
+    dy = to_dev(inp["dy"], dt)
+    m_in, r_in = (mean, rstd) if stats == "gpu" else (None, None)
+    if fused:
+        dx, dg, db = rn.layernorm_fused_add_bwd(dy, to_dev(inp["dh"], dt), out["h"], g, m_in, r_in, eps, offset)
+    else:
+        dx, dg, db = rn.layernorm_bwd(dy, x, g, m_in, r_in, eps, offset)
+    torch.cuda.synchronize()
+    out.update(dx=dx, dg=dg, db=db)
+    return {k: (None if v is None else from_dev(v)) for k, v in out.items()}
+
+
+def check_ln(inp, dt, eps, offset, fused, got, affine=True, bias=True, grads=True):
+    """Compare LayerNorm results with the reference.
+
+    Rules as for RMSNorm: bf16 within 2 ulp of the rounded reference, float32
+    within a relative 1e-5, each at a magnitude floored by the size of the
+    terms that cancel:
+      y   s = rstd |w| (|v| + mean_j |v|) + |beta|
+      dx  s = rstd (|g| + mean_j |g| + |xhat| (|mean_j(g xhat)| + mean_j |g xhat|)) [+ |dh|]
+    mean is a float32 result floored at mean_j |v|; dgamma and dbeta (checked
+    when grads is true, i.e. when inp holds every row) have the relative-L2
+    rule; h (fused add) is bit-exact."""
+    g = inp["gamma"] if affine else None
+    beta = inp["beta"] if bias else None
+    v = inp["x"]
+    if fused:
+        v, _, _ = oracle.fused_add_fwd(inp["x"], inp["residual"], g, dt, eps, offset, want_y=False)
+        assert np.array_equal(got["h"], v), "h differs"
+    y64, mean64, rstd64 = oracle.ln_fwd(v, g, beta, dt, eps, offset)
+    vw = widen(v, dt)
+    w = (widen(g, dt) if g is not None else np.ones(vw.shape[1])) + float(np.float32(offset))
+    bw = widen(beta, dt) if beta is not None else np.zeros(vw.shape[1])
+    mabs = np.abs(vw).mean(1)
+    s_y = rstd64[:, None] * np.abs(w) * (np.abs(vw) + mabs[:, None]) + np.abs(bw)
+    check_values("y", got["y"], y64, dt, scale=s_y)
+    rr = check_f32("rstd", got["rstd"], rstd64)
+    assert rr.ok, str(rr)
+    rm = check_f32("mean", got["mean"], mean64, scale=mabs)
+    assert rm.ok, str(rm)
+    dh = inp["dh"] if fused else None
+    out = oracle.ln_bwd(inp["dy"], v, g, dt, eps, offset, dh=dh, want_dgamma=grads, want_dbeta=grads)
+    st = out["stats64"]
+    gg = widen(inp["dy"], dt) * w
+    xhat = (vw - mean64[:, None]) * rstd64[:, None]
+    s_dx = rstd64[:, None] * (np.abs(gg) + st[:, 2:3] + np.abs(xhat) * (np.abs(st[:, 1:2]) + st[:, 3:4]))
+    if dh is not None:
+        s_dx = s_dx + np.abs(widen(dh, dt))
+    r_dx = check_values("dx", got["dx"], out["dx64"], dt, scale=s_dx)
+    if not grads:
+        return r_dx
+    if affine:
+        err = dgamma_error(got["dg"], out["dgamma64"], dt)
+        assert err <= DGAMMA_TOL[dt], f"dgamma relative L2 {err:.3g}"
+    else:
+        assert got["dg"] is None
+    err = dgamma_error(got["db"], out["dbeta64"], dt)
+    assert err <= DGAMMA_TOL[dt], f"dbeta relative L2 {err:.3g}"
+    return r_dx

@@ -1,0 +1,189 @@
+"""GPU parity on degenerate rows: the value patterns where the normalisation
+itself is at an edge, against the fp64 reference under the usual rules.
+
+Each case replaces the first rows of a seeded draw with one pattern each:
+  zero         all zeros: rstd = 1/sqrt(eps), y = 0, dx = rstd g
+  constant     every element 3: LayerNorm variance exactly 0, so y = beta
+  one_hot      a single nonzero element (2.5)
+  big          a normal draw times 2^40
+  small        a normal draw times 2^-40: the mean square is far below eps
+  tiny         a normal draw times 2^-100: the squares underflow float32
+               (the reference sees about 2^-200), eps dominates either way
+  alternating  +1, -1, ...: LayerNorm mean exactly 0
+  shifted      16 + 0.25 z: LayerNorm mean far above the spread
+  outlier      a normal draw with one element 2^20
+  dy_zero      a normal draw whose incoming gradient row is zero
+For the fused-add ops the pattern goes into the residual and x is zero on
+those rows, so h = residual keeps it.  With eps = 0 the zero and tiny rows are
+left out: there 1/sqrt(mean square) is infinite or beyond float32's range,
+outside what a float32 method can return."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_normalization_rmsnorm_amd as rn
+from gpu_util import (check_backward, check_forward, check_ln, from_dev,
+                      gpu_backward, gpu_forward, gpu_ln, reference_h, to_dev)
+from rmsnorm_inputs import make_inputs, storage_to_f32, to_storage
+from tolerance import check_f32
+
+pytestmark = pytest.mark.gpu
+
+PATTERNS = ["zero", "constant", "one_hot", "big", "small", "tiny", "alternating", "shifted", "outlier", "dy_zero"]
+NO_EPS_PATTERNS = [p for p in PATTERNS if p not in ("zero", "tiny")]
+EXTRA_ROWS = 6  # ordinary rows after the patterns
+
+
+def pattern_row(name, N, rng):
+    z = rng.standard_normal(N, dtype=np.float32)
+    if name == "zero":
+        return np.zeros(N, np.float32)
+    if name == "constant":
+        return np.full(N, 3.0, np.float32)
+    if name == "one_hot":
+        r = np.zeros(N, np.float32)
+        r[N // 3] = 2.5
+        return r
+    if name == "big":
+        return z * np.float32(2.0 ** 40)
+    if name == "small":
+        return z * np.float32(2.0 ** -40)
+    if name == "tiny":
+        return z * np.float32(2.0 ** -100)
+    if name == "alternating":
+        return np.where(np.arange(N) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    if name == "shifted":
+        return (16.0 + 0.25 * z).astype(np.float32)
+    if name == "outlier":
+        z[0] = 2.0 ** 20
+        return z
+    if name == "dy_zero":
+        return z
+    raise ValueError(name)
+
+
+def degenerate_inputs(N, dt, fused, gemma, patterns, layernorm=False, seed=7):
+    """A seeded draw of len(patterns) + EXTRA_ROWS rows with the pattern rows
+    written in (storage dtype)."""
+    M = len(patterns) + EXTRA_ROWS
+    inp = make_inputs(M, N, dt, fused=fused, gemma=gemma, seed=seed, layernorm=layernorm)
+    rng = np.random.default_rng(seed + 1)
+    target = "residual" if fused else "x"
+    t = storage_to_f32(inp[target], dt).copy()
+    x = storage_to_f32(inp["x"], dt).copy()
+    dy = storage_to_f32(inp["dy"], dt).copy()
+    for i, name in enumerate(patterns):
+        t[i] = pattern_row(name, N, rng)
+        if fused:
+            x[i] = 0.0
+        if name == "dy_zero":
+            dy[i] = 0.0
+    inp[target] = to_storage(t, dt)
+    if fused:
+        inp["x"] = to_storage(x, dt)
+    inp["dy"] = to_storage(dy, dt)
+    return inp
+
+
+# (N, dtype, fused, gemma): one shape per selector path
+SHAPES = [
+    (128, "bf16", False, False),    # 16-lane teams
+    (4096, "bf16", False, False),   # workgroup teams, w in registers
+    (6144, "f32", False, True),     # float32, gamma + offset
+    (7168, "bf16", True, False),    # fused residual add
+    (16384, "bf16", False, False),  # wide rows, gamma re-read per row
+    (4097, "bf16", False, False),   # scalar access
+    (40000, "f32", True, False),    # looped rows
+    (1, "bf16", False, False),      # one element per row
+]
+
+
+def shape_id(s):
+    N, dt, fused, gemma = s
+    return f"{dt}_N{N}" + ("_fused" if fused else "") + ("_offset1" if gemma else "")
+
+
+def run_rmsnorm(N, dt, fused, gemma, eps, patterns):
+    inp = degenerate_inputs(N, dt, fused, gemma, patterns)
+    offset = 1.0 if gemma else 0.0
+    out = gpu_forward(inp, dt, eps, offset, fused)
+    torch.cuda.synchronize()
+    y, rstd = from_dev(out["y"]), from_dev(out["rstd"])
+    assert np.all(np.isfinite(storage_to_f32(y, dt))), "non-finite y"
+    check_forward(inp, dt, eps, offset, y, rstd, from_dev(out["h"]) if fused else None)
+    v_ref = reference_h(inp, dt, eps, offset) if fused else inp["x"]
+    dx, dg = gpu_backward(inp, dt, eps, offset, out, fused)
+    torch.cuda.synchronize()
+    dx, dg = from_dev(dx), from_dev(dg)
+    check_backward(inp, dt, eps, offset, dx, dg, v_full=v_ref, dh_full=inp["dh"] if fused else None)
+    return inp, y, rstd, dx
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=shape_id)
+def test_rmsnorm_degenerate_rows(shape):
+    N, dt, fused, gemma = shape
+    eps = 1e-6
+    inp, y, rstd, dx = run_rmsnorm(N, dt, fused, gemma, eps, PATTERNS)
+    # the zero row: y is exactly 0 and rstd is 1/sqrt(eps) (checked above to
+    # float32's rule); its dx is rstd * dy * w [+ dh]
+    yz = storage_to_f32(y[PATTERNS.index("zero")], dt)
+    assert np.all(yz == 0.0), "zero row: y must be exactly 0"
+    # the dy_zero row of the plain op has dx exactly 0 (it has no dh term)
+    if not fused:
+        dxz = storage_to_f32(dx[PATTERNS.index("dy_zero")], dt)
+        assert np.all(dxz == 0.0), "zero incoming gradient: dx must be exactly 0"
+
+
+@pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[3], SHAPES[5]], ids=shape_id)
+def test_rmsnorm_zero_eps(shape):
+    N, dt, fused, gemma = shape
+    run_rmsnorm(N, dt, fused, gemma, 0.0, NO_EPS_PATTERNS)
+
+
+LN_EPS = 1e-5
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=shape_id)
+def test_layernorm_degenerate_rows(shape):
+    N, dt, fused, gemma = shape
+    inp = degenerate_inputs(N, dt, fused, gemma, PATTERNS, layernorm=True)
+    offset = 1.0 if gemma else 0.0
+    got = gpu_ln(inp, dt, LN_EPS, offset, fused)
+    check_ln(inp, dt, LN_EPS, offset, fused, got)
+    if N & (N - 1) == 0:
+        # With N a power of two the float32 mean of the constant row is exact
+        # (3 N and 1/N are), so the variance is exactly 0, xhat = 0 and y is
+        # beta itself.
+        i = PATTERNS.index("constant")
+        assert got["mean"][i] == 3.0
+        assert np.array_equal(got["y"][i], inp["beta"]), "constant row: y must equal beta"
+    if N == 1:
+        # one element per row: every row is constant, dx = rstd (g - mean(g)) = 0
+        assert np.all(storage_to_f32(got["dx"], dt) == 0.0)
+
+
+@pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[4]], ids=shape_id)
+def test_fp8_degenerate_rows(shape):
+    """E4M3 codes of y * scale on the pattern rows: zero rows give code 0, the
+    one-hot row (y = sqrt(N) at its element) saturates at 448."""
+    N, dt, fused, gemma = shape
+    inp = degenerate_inputs(N, dt, fused, gemma, PATTERNS)
+    scale = 16.0
+    x, g = to_dev(inp["x"], dt), to_dev(inp["gamma"], dt)
+    sc = torch.tensor([scale], dtype=torch.float32, device="cuda")
+    am = torch.zeros(1, dtype=torch.float32, device="cuda")
+    y8, rstd = rn.rmsnorm_fwd_fp8(x, g, sc, 1e-6, 0.0, amax=am)
+    torch.cuda.synchronize()
+    code = y8.view(torch.uint8).cpu().numpy()
+    ref = oracle.fwd_fp8(inp["x"], inp["gamma"], dt, 1e-6, 0.0, scale, tol=1e-5)
+    ok = (code == ref["code_lo"]) | (code == ref["code_hi"])
+    assert ok.all(), f"{int((~ok).sum())} codes outside the tolerance interval, first at {np.argwhere(~ok)[:4].tolist()}"
+    assert np.all(code[PATTERNS.index("zero")] & 0x7F == 0)
+    j = N // 3
+    assert code[PATTERNS.index("one_hot"), j] & 0x7F == 0x7E  # saturated at 448
+    rr = check_f32("rstd", from_dev(rstd), ref["rstd64"])
+    assert rr.ok, str(rr)
+    amax = float(am.item())
+    assert abs(amax - ref["amax64"]) <= 1e-5 * ref["amax64"], (amax, ref["amax64"])

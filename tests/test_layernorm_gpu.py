@@ -1,13 +1,7 @@
 """GPU parity of LayerNorm (forward and backward, plain and fused residual add)
 against the fp64 reference.
 
-Rules as for RMSNorm: bf16 outputs within 2 ulp of the rounded reference,
-float32 within a relative 1e-5, each taken at a magnitude floored by the size
-of the terms that cancel:
-  y   s = rstd |w| (|v| + mean_j |v|) + |beta|
-  dx  s = rstd (|g| + mean_j |g| + |xhat| (|mean_j(g xhat)| + mean_j |g xhat|)) [+ |dh|]
-mean is a float32 result floored at mean_j |v|; dgamma and dbeta have
-RMSNorm's relative-L2 rule; h (fused add) is bit-exact."""
+The rules are RMSNorm's, with LayerNorm's cancellation floors (gpu_util.check_ln)."""
 
 import numpy as np
 import pytest
@@ -15,73 +9,13 @@ import torch
 
 import oracle
 import transformer_normalization_rmsnorm_amd as rn
-from gpu_util import check_values, from_dev, to_dev, widen
+from gpu_util import check_ln, gpu_ln, to_dev
 from rmsnorm_inputs import make_inputs
-from tolerance import DGAMMA_TOL, check_f32, dgamma_error
+from tolerance import DGAMMA_TOL, dgamma_error
 
 pytestmark = pytest.mark.gpu
 
 EPS = 1e-5
-
-
-def gpu_ln(inp, dt, offset, fused, stats="gpu", affine=True, bias=True):
-    x = to_dev(inp["x"], dt)
-    g = to_dev(inp["gamma"], dt) if affine else None
-    b = to_dev(inp["beta"], dt) if bias else None
-    out = {}
-    if fused:
-        r = to_dev(inp["residual"], dt)
-        y, h, mean, rstd = rn.layernorm_fused_add_fwd(x, r, g, b, EPS, offset)
-        out["h"] = h
-    else:
-        y, mean, rstd = rn.layernorm_fwd(x, g, b, EPS, offset)
-    out.update(y=y, mean=mean, rstd=rstd)
-    dy = to_dev(inp["dy"], dt)
-    m_in, r_in = (mean, rstd) if stats == "gpu" else (None, None)
-    if fused:
-        dx, dg, db = rn.layernorm_fused_add_bwd(dy, to_dev(inp["dh"], dt), out["h"], g, m_in, r_in, EPS, offset)
-    else:
-        dx, dg, db = rn.layernorm_bwd(dy, x, g, m_in, r_in, EPS, offset)
-    torch.cuda.synchronize()
-    out.update(dx=dx, dg=dg, db=db)
-    return {k: (None if v is None else from_dev(v)) for k, v in out.items()}
-
-
-def check_ln(inp, dt, offset, fused, got, affine=True, bias=True, rows=None):
-    g = inp["gamma"] if affine else None
-    beta = inp["beta"] if bias else None
-    v = inp["x"]
-    if fused:
-        v, _, _ = oracle.fused_add_fwd(inp["x"], inp["residual"], g, dt, EPS, offset, want_y=False)
-        assert np.array_equal(got["h"], v), "h differs"
-    y64, mean64, rstd64 = oracle.ln_fwd(v, g, beta, dt, EPS, offset)
-    vw = widen(v, dt)
-    w = (widen(g, dt) if g is not None else np.ones(vw.shape[1])) + float(np.float32(offset))
-    bw = widen(beta, dt) if beta is not None else np.zeros(vw.shape[1])
-    mabs = np.abs(vw).mean(1)
-    s_y = rstd64[:, None] * np.abs(w) * (np.abs(vw) + mabs[:, None]) + np.abs(bw)
-    check_values("y", got["y"], y64, dt, scale=s_y)
-    rr = check_f32("rstd", got["rstd"], rstd64)
-    assert rr.ok, str(rr)
-    rm = check_f32("mean", got["mean"], mean64, scale=mabs)
-    assert rm.ok, str(rm)
-    dh = inp["dh"] if fused else None
-    out = oracle.ln_bwd(inp["dy"], v, g, dt, EPS, offset, dh=dh)
-    st = out["stats64"]
-    gg = widen(inp["dy"], dt) * w
-    xhat = (vw - mean64[:, None]) * rstd64[:, None]
-    s_dx = rstd64[:, None] * (np.abs(gg) + st[:, 2:3] + np.abs(xhat) * (np.abs(st[:, 1:2]) + st[:, 3:4]))
-    if dh is not None:
-        s_dx = s_dx + np.abs(widen(dh, dt))
-    r_dx = check_values("dx", got["dx"], out["dx64"], dt, scale=s_dx)
-    if affine:
-        err = dgamma_error(got["dg"], out["dgamma64"], dt)
-        assert err <= DGAMMA_TOL[dt], f"dgamma relative L2 {err:.3g}"
-    else:
-        assert got["dg"] is None
-    err = dgamma_error(got["db"], out["dbeta64"], dt)
-    assert err <= DGAMMA_TOL[dt], f"dbeta relative L2 {err:.3g}"
-    return r_dx
 
 
 # (M, N, dtype, fused, gemma)
@@ -119,8 +53,8 @@ def test_layernorm_parity(case):
     M, N, dt, fused, gemma = case
     inp = make_inputs(M, N, dt, fused=fused, gemma=gemma, layernorm=True)
     offset = 1.0 if gemma else 0.0
-    got = gpu_ln(inp, dt, offset, fused)
-    r = check_ln(inp, dt, offset, fused, got)
+    got = gpu_ln(inp, dt, EPS, offset, fused)
+    r = check_ln(inp, dt, EPS, offset, fused, got)
     print(f"{case_id(case)}: {r}")
 
 
@@ -129,15 +63,15 @@ def test_layernorm_recomputes_statistics(case):
     M, N, dt, fused, gemma = case
     inp = make_inputs(M, N, dt, fused=fused, gemma=gemma, layernorm=True)
     offset = 1.0 if gemma else 0.0
-    check_ln(inp, dt, offset, fused, gpu_ln(inp, dt, offset, fused, stats=None))
+    check_ln(inp, dt, EPS, offset, fused, gpu_ln(inp, dt, EPS, offset, fused, stats=None))
 
 
 @pytest.mark.parametrize("affine,bias", [(False, False), (True, False), (False, True)])
 def test_layernorm_without_gamma_or_beta(affine, bias):
     for fused in (False, True):
         inp = make_inputs(64, 2048, "bf16", fused=fused, layernorm=True)
-        got = gpu_ln(inp, "bf16", 0.0, fused, affine=affine, bias=bias)
-        check_ln(inp, "bf16", 0.0, fused, got, affine=affine, bias=bias)
+        got = gpu_ln(inp, "bf16", EPS, 0.0, fused, affine=affine, bias=bias)
+        check_ln(inp, "bf16", EPS, 0.0, fused, got, affine=affine, bias=bias)
 
 
 # Every LayerNorm backward layout, forced on a shape it tiles, with a small grid.
@@ -177,7 +111,7 @@ def test_layernorm_backward_layouts(fused_ok, M, N, dt, fields, fused):
         p = rn.rmsnorm_query_plan(op, M, N, rn.BF16 if dt == "bf16" else rn.F32, True)
         for k, v in fields.items():
             assert p[k] == v, (k, p)
-        check_ln(inp, dt, offset, fused, gpu_ln(inp, dt, offset, fused))
+        check_ln(inp, dt, EPS, offset, fused, gpu_ln(inp, dt, EPS, offset, fused))
 
 
 def test_layernorm_zero_rows_writes_zero_gradients():
@@ -195,9 +129,9 @@ def test_layernorm_zero_rows_writes_zero_gradients():
 def test_layernorm_gradients_are_bit_identical_run_to_run():
     M, N, dt = 2048, 4096, "bf16"
     inp = make_inputs(M, N, dt, layernorm=True)
-    first = gpu_ln(inp, dt, 0.0, False)
+    first = gpu_ln(inp, dt, EPS, 0.0, False)
     for _ in range(2):
-        again = gpu_ln(inp, dt, 0.0, False)
+        again = gpu_ln(inp, dt, EPS, 0.0, False)
         for k in ("y", "mean", "rstd", "dx", "dg", "db"):
             assert np.array_equal(first[k], again[k]), k
 
@@ -253,7 +187,7 @@ def test_layernorm_full_size(name):
     w = ALL_WORKLOADS[name]
     print(f"workload {name}", flush=True)
     inp = make_inputs(w.M, w.N, w.dtype, fused=w.fused, gemma=w.gemma, layernorm=True)
-    got = gpu_ln(inp, w.dtype, w.offset, w.fused)
+    got = gpu_ln(inp, w.dtype, EPS, w.offset, w.fused)
     rows = sample_rows(w.M, 48)
     sub = {k: (v[rows] if v.ndim == 2 else v) for k, v in inp.items()}
     got_s = {k: (v[rows] if (v is not None and k in ("y", "mean", "rstd", "dx", "h")) else v) for k, v in got.items()}
@@ -268,32 +202,5 @@ def test_layernorm_full_size(name):
         err = dgamma_error(got[k], ref, w.dtype)
         assert err <= DGAMMA_TOL[w.dtype], f"{k} relative L2 {err:.3g}"
     got_s["dg"], got_s["db"] = None, None
-    check_ln_rows(sub, w.dtype, w.offset, w.fused, got_s)
+    check_ln(sub, w.dtype, EPS, w.offset, w.fused, got_s, grads=False)
 
-
-def check_ln_rows(inp, dt, offset, fused, got):
-    """check_ln on a row sample: y, h, mean, rstd and dx only."""
-    g, beta = inp["gamma"], inp["beta"]
-    v = inp["x"]
-    if fused:
-        v, _, _ = oracle.fused_add_fwd(inp["x"], inp["residual"], g, dt, EPS, offset, want_y=False)
-        assert np.array_equal(got["h"], v), "h differs"
-    y64, mean64, rstd64 = oracle.ln_fwd(v, g, beta, dt, EPS, offset)
-    vw = widen(v, dt)
-    w = widen(g, dt) + float(np.float32(offset))
-    mabs = np.abs(vw).mean(1)
-    s_y = rstd64[:, None] * np.abs(w) * (np.abs(vw) + mabs[:, None]) + np.abs(widen(beta, dt))
-    check_values("y", got["y"], y64, dt, scale=s_y)
-    rr = check_f32("rstd", got["rstd"], rstd64)
-    assert rr.ok, str(rr)
-    rm = check_f32("mean", got["mean"], mean64, scale=mabs)
-    assert rm.ok, str(rm)
-    dh = inp["dh"] if fused else None
-    out = oracle.ln_bwd(inp["dy"], v, g, dt, EPS, offset, dh=dh, want_dgamma=False, want_dbeta=False)
-    st = out["stats64"]
-    gg = widen(inp["dy"], dt) * w
-    xhat = (vw - mean64[:, None]) * rstd64[:, None]
-    s_dx = rstd64[:, None] * (np.abs(gg) + st[:, 2:3] + np.abs(xhat) * (np.abs(st[:, 1:2]) + st[:, 3:4]))
-    if dh is not None:
-        s_dx = s_dx + np.abs(widen(dh, dt))
-    check_values("dx", got["dx"], out["dx64"], dt, scale=s_dx)

@@ -439,8 +439,10 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
 // [32b, 32b + 32) (one 128-byte line per partial row): lane (cg, pg) sums
 // float4 column group cg over the rows p = pg, pg + 32, pg + 64, ... in
 // increasing p, issuing kFinDepth loads before adding them so that their
-// latencies overlap; the 32 group sums are then added in pg order.  The order
-// depends only on P, so dgamma is bit-reproducible.
+// latencies overlap.  The 32 group sums are then folded in a fixed tree: the
+// 8 groups that share a wave by lane exchange (xor 8, 16, 32), the 4 wave
+// sums through LDS in wave order.  The order depends only on P, so dgamma is
+// bit-reproducible.
 template <typename T>
 __global__ void __launch_bounds__(kFinThreads) finalize_kernel(const float *__restrict__ part0, int64_t P,
                                                                int64_t ld, int64_t N, T *__restrict__ dg0,
@@ -454,7 +456,8 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(const float *__re
         return; // the whole workgroup: this output was not asked for
     constexpr int CG = kFinColsPerBlock / 4; // float4 groups per workgroup
     constexpr int PG = kFinThreads / CG;     // partial-row groups
-    constexpr int kFinDepth = 16;
+    constexpr int kFinDepth = 8;
+    static_assert(kFinThreads % 64 == 0 && 64 % CG == 0, "a wave holds whole row groups");
     const int cg = threadIdx.x % CG;
     const int pg = threadIdx.x / CG;
     const int64_t col = (int64_t)blockIdx.x * kFinColsPerBlock + cg * 4;
@@ -477,12 +480,22 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(const float *__re
             }
         }
     }
-    __shared__ float4 red[PG][CG];
-    red[pg][cg] = s;
+#pragma unroll
+    for (int off = CG; off < 64; off <<= 1) {
+        s.x += __shfl_xor(s.x, off);
+        s.y += __shfl_xor(s.y, off);
+        s.z += __shfl_xor(s.z, off);
+        s.w += __shfl_xor(s.w, off);
+    }
+    constexpr int NW = kFinThreads / 64;
+    __shared__ float4 red[NW][CG];
+    if (threadIdx.x % 64 < CG)
+        red[threadIdx.x / 64][cg] = s;
     __syncthreads();
     if (pg == 0) {
         float4 t = red[0][cg];
-        for (int i = 1; i < PG; ++i) {
+#pragma unroll
+        for (int i = 1; i < NW; ++i) {
             const float4 u = red[i][cg];
             t.x += u.x;
             t.y += u.y;
