@@ -41,7 +41,7 @@
  *   - Aliasing: only h_out may alias residual (fused forward) and only dx may
  *     alias dh (fused backward); any other overlap is undefined.
  *   - M = 0 is valid: the forward does nothing; the backward writes
- *     dgamma = 0.  N must be in [1, 2^31 - 1].
+ *     dgamma = 0.  N must be in [1, 2^24] (RMSNORM_MAX_N).
  *   - gamma == NULL selects the non-affine op (no elementwise scale, w_j = 1;
  *     Liger-Kernel PR #1388 "Validation" covers affine and non-affine).  offset
  *     must then be 0 and dgamma NULL; the backward writes no partials, so it
@@ -250,6 +250,9 @@ const char *rmsnorm_last_error(void);
  * checks it before use.  2: rmsnorm_plan gained w_regs.  3: fp8-output
  * forwards (ops 4 and 5).  4: LayerNorm (include/layernorm.h, ops 6-9). */
 #define RMSNORM_ABI_VERSION 4
+
+/* Longest row (elements) any entry point accepts. */
+#define RMSNORM_MAX_N (1 << 24)
 int rmsnorm_version(void);
 
 #ifdef __cplusplus

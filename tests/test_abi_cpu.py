@@ -64,6 +64,7 @@ def test_fwd_argument_errors(lib):
     assert fwd(lib, dt=7) == EUNSUPPORTED
     assert fwd(lib, M=-1) == EINVAL
     assert fwd(lib, N=0) == EINVAL
+    assert fwd(lib, N=2 ** 24 + 1) == EINVAL
     assert fwd(lib, N=2 ** 31) == EINVAL
     assert fwd(lib, eps=-1e-6) == EINVAL
     assert fwd(lib, eps=float("nan")) == EINVAL
@@ -355,6 +356,26 @@ def test_grid_caps_and_zero_rows():
     assert z["grid"] == 0 and z["programs"] == 0
     assert plan(rn.OP_FWD, 0, 4096)["grid"] == 0
     assert plan(rn.OP_BWD, 10 ** 6, 4096, cus=80)["grid"] == 80
+
+
+def test_row_limit_is_the_headers():
+    """RMSNORM_MAX_N in the header, the binding's MAX_N and the selector agree:
+    the longest row is planned (on the looped path), one more element is not."""
+    m = re.search(r"#define RMSNORM_MAX_N \(1 << (\d+)\)", open(HEADER).read())
+    assert m and (1 << int(m.group(1))) == rn.MAX_N
+    for op in (rn.OP_FWD, rn.OP_BWD, rn.OP_FWD_FP8, rn.OP_LN_FWD, rn.OP_LN_FUSED_ADD_BWD):
+        p = plan(op, 3, rn.MAX_N)
+        assert p["path"] == rn.PATH_LOOP
+        assert p["grid"] * p["threads"] < 2 ** 31 and p["fin_grid"] * max(p["fin_threads"], 1) < 2 ** 31
+        with pytest.raises(rn.RMSNormError):
+            plan(op, 3, rn.MAX_N + 1)
+
+
+def test_forward_grid_keeps_work_items_below_2_31():
+    """A forward over more rows than one launch can address becomes persistent."""
+    for op, N in ((rn.OP_FWD, 128), (rn.OP_FWD, 1), (rn.OP_LN_FWD, 64), (rn.OP_FWD_FP8, 8)):
+        p = plan(op, 2 ** 40, N)
+        assert p["grid"] * p["threads"] < 2 ** 31, p
 
 
 def test_selector_rejects_bad_queries():

@@ -36,6 +36,7 @@ F32, BF16 = 0, 1
 OP_FWD, OP_FUSED_ADD_FWD, OP_BWD, OP_FUSED_ADD_BWD, OP_FWD_FP8, OP_FUSED_ADD_FWD_FP8 = 0, 1, 2, 3, 4, 5
 OP_LN_FWD, OP_LN_FUSED_ADD_FWD, OP_LN_BWD, OP_LN_FUSED_ADD_BWD = 6, 7, 8, 9
 PATH_ROWS, PATH_LOOP = 0, 1
+MAX_N = 1 << 24  # longest row any entry point accepts (RMSNORM_MAX_N)
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
 
 # Exported symbols (kept equal to include/rmsnorm.h; a CPU test checks both).

@@ -16,6 +16,8 @@
 
 using namespace rmsnorm;
 
+static_assert(kMaxN == RMSNORM_MAX_N, "the header's row limit is the library's");
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -72,8 +74,8 @@ int check_common(int64_t M, int64_t N, int dtype, float eps, float offset)
         return fail(RMSNORM_EUNSUPPORTED, "dtype %d not supported (0 = f32, 1 = bf16)", dtype);
     if (M < 0)
         return fail(RMSNORM_EINVAL, "M = %lld < 0", (long long)M);
-    if (N <= 0 || N > INT32_MAX)
-        return fail(RMSNORM_EINVAL, "N = %lld outside [1, 2^31-1]", (long long)N);
+    if (N <= 0 || N > kMaxN)
+        return fail(RMSNORM_EINVAL, "N = %lld outside [1, 2^24]", (long long)N);
     if (M > 0 && M > INT64_MAX / N / 4)
         return fail(RMSNORM_EINVAL, "M * N too large");
     if (!(eps >= 0.0f) || !std::isfinite(eps))
@@ -291,7 +293,7 @@ int do_finalize(const float *partials, int64_t programs, int64_t N, void *dgamma
 {
     if (dtype != RMSNORM_BF16 && dtype != RMSNORM_F32)
         return fail(RMSNORM_EUNSUPPORTED, "dtype %d not supported", dtype);
-    if (N <= 0 || N > INT32_MAX || programs < 0)
+    if (N <= 0 || N > kMaxN || programs < 0)
         return fail(RMSNORM_EINVAL, "bad N or programs");
     if (!dgamma || (programs > 0 && !partials))
         return fail(RMSNORM_EINVAL, "null pointer");

@@ -52,6 +52,15 @@ struct BwdArgs {
     const float *mean = nullptr;
 };
 
+// Longest row accepted (2^24 elements).  Column and chunk indices, and the
+// strided loop counters of the looped kernels, stay far inside int32 and the
+// finalizer's launch inside HIP's 32-bit work-item count.
+constexpr int64_t kMaxN = int64_t(1) << 24;
+
+// Work-items of one launch are kept below 2^31; the row kernels stride over
+// the rows, so capping the grid only makes them persistent.
+constexpr int64_t kMaxWorkItems = int64_t(1) << 31;
+
 // Partial rows are padded to this many floats (256 bytes).
 constexpr int64_t kPartialAlign = 64;
 inline int64_t partial_ld(int64_t N) { return (N + kPartialAlign - 1) / kPartialAlign * kPartialAlign; }

@@ -21,7 +21,6 @@ constexpr int kRowsThreads = 256;   // workgroup size when a team is at most one
 constexpr int kLoopThreads = 1024;  // looped path workgroup size
 constexpr int kBwdProgramsPerCU = 1; // persistent backward workgroup teams per compute unit
 constexpr int kBwdTeamsPerCU = 2;    // persistent backward workgroups per compute unit (sub-wave teams)
-constexpr int64_t kMaxGrid = int64_t(1) << 30;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -208,7 +207,7 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
         p->fin_grid = ceil_div(partial_ld(N), kFinColsPerBlock) * (is_ln_op(p->op) ? 2 : 1);
     } else {
         const int64_t want = keep_grid && p->grid > 0 ? p->grid : blocks_needed;
-        p->grid = M == 0 ? 0 : std::min(std::min(want, blocks_needed), kMaxGrid);
+        p->grid = M == 0 ? 0 : std::min(std::min(want, blocks_needed), (kMaxWorkItems - 1) / p->threads);
         if (is_fp8_op(p->op)) { // one amax partial per workgroup
             p->programs = p->grid;
             p->workspace_bytes = round_up(std::max<int64_t>(p->grid, 1) * (int64_t)sizeof(float), 256);
@@ -230,7 +229,7 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
         return RMSNORM_EINVAL;
     if (dtype != RMSNORM_BF16 && dtype != RMSNORM_F32)
         return RMSNORM_EUNSUPPORTED;
-    if (M < 0 || N <= 0 || N > INT32_MAX)
+    if (M < 0 || N <= 0 || N > kMaxN)
         return RMSNORM_EINVAL;
     const bool bwd = is_bwd(op);
     const int VV = vec_elems(dtype);
