@@ -284,15 +284,26 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
     float *__restrict__ part = a.partials + (int64_t)blockIdx.x * a.ld;
     float *__restrict__ partb = a.partials + (a.grid + (int64_t)blockIdx.x) * a.ld; // LayerNorm dbeta
     if constexpr (TEAM == 0) {
+        // Rows of one or two chunks per lane write their partial rows with
+        // the nontemporal hint, as the finalizer reads them (measured on
+        // MI355X with one workspace reused call after call, backward of
+        // 1024 x 8192 bf16: RMSNorm 17.6 -> 16.8 us, LayerNorm 23.4 -> 21.0
+        // us; within noise with a fresh workspace per call).  Wider rows keep
+        // cached stores: there the hint cost 2048 x 32768 bf16 3.7 us.
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int c = k * tl + lane;
             if (EXACT || c < nchunks) {
-                store_f32<V>(part + (int64_t)c * V, acc[k]);
+                if constexpr (K <= 2)
+                    store_f32_nt<V>(part + (int64_t)c * V, acc[k]);
+                else
+                    store_f32<V>(part + (int64_t)c * V, acc[k]);
                 if constexpr (BL) {
 #pragma unroll
                     for (int h = 0; h < NPL; ++h)
                         *reinterpret_cast<float4 *>(partb + (int64_t)c * V + 4 * h) = lds_db[h * nchunks + c];
+                } else if constexpr (LN && K <= 2) {
+                    store_f32_nt<V>(partb + (int64_t)c * V, accb[k]);
                 } else if constexpr (LN) {
                     store_f32<V>(partb + (int64_t)c * V, accb[k]);
                 }
@@ -468,8 +479,10 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(const float *__re
 #pragma unroll
             for (int i = 0; i < kFinDepth; ++i) {
                 const int64_t p = p0 + (int64_t)i * PG;
-                t[i] = p < P ? *reinterpret_cast<const float4 *>(part + p * ld + col)
-                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                f32x4_t u = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (p < P) // read once: nontemporal, like the rows
+                    u = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(part + p * ld + col));
+                t[i] = make_float4(u.x, u.y, u.z, u.w);
             }
 #pragma unroll
             for (int i = 0; i < kFinDepth; ++i) {

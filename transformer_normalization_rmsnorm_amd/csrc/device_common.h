@@ -179,6 +179,24 @@ __device__ __forceinline__ void store_f32(float *p, const float (&a)[V])
     }
 }
 
+// The same with the nontemporal hint: a partial row written once at the end
+// of the backward and read once by the finalizer.
+template <int V>
+__device__ __forceinline__ void store_f32_nt(float *p, const float (&a)[V])
+{
+    if constexpr (V % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < V; i += 4) {
+            const f32x4_t u = {a[i], a[i + 1], a[i + 2], a[i + 3]};
+            __builtin_nontemporal_store(u, reinterpret_cast<f32x4_t *>(p + i));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            __builtin_nontemporal_store(a[i], p + i);
+    }
+}
+
 template <int V>
 __device__ __forceinline__ void load_f32(const float *p, float (&a)[V])
 {
