@@ -322,19 +322,33 @@ def test_layernorm_plans(M, N, dt):
 
 
 def test_layernorm_wide_backward_bounds():
-    # LayerNorm holds the mean and a second accumulator set: its own bounds
-    assert (lambda p: (p["threads"], p["chunks"], p["depth"], p["w_regs"]))(plan(rn.OP_LN_BWD, 4096, 16384)) == (1024, 2, 0, 0)
-    assert (lambda p: (p["threads"], p["chunks"], p["depth"], p["w_regs"]))(plan(rn.OP_LN_BWD, 4096, 4096)) == (512, 1, 1, 1)
-    # dbeta in LDS at four or more chunks: plain rows of 32768 bf16 stay in registers;
-    # the fused op (also holding dh) stops at six chunks x 512 threads
-    assert (lambda p: (p["path"], p["threads"], p["chunks"]))(plan(rn.OP_LN_BWD, 2048, 32768)) == (rn.PATH_ROWS, 1024, 4)
-    assert plan(rn.OP_LN_FUSED_ADD_BWD, 2048, 32768)["path"] == rn.PATH_LOOP
-    assert (lambda p: (p["threads"], p["chunks"]))(plan(rn.OP_LN_FUSED_ADD_BWD, 2048, 24576)) == (1024, 3)
-    with rn.plan_override(rn.OP_LN_FUSED_ADD_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=512, depth=0, w_regs=0):
-        with pytest.raises(rn.RMSNormError):  # eight chunks are not compiled for the fused op
-            plan(rn.OP_LN_FUSED_ADD_BWD, 100, 32768)
-    with rn.plan_override(rn.OP_LN_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=1024, depth=1, w_regs=0):
-        with pytest.raises(rn.RMSNormError):  # two chunks, one row ahead: 512 threads at most
+    shape = lambda p: (p["path"], p["threads"], p["chunks"], p["depth"], p["w_regs"])
+    R = rn.PATH_ROWS
+    # LayerNorm holds the mean and a second accumulator set: its own bounds.  Two
+    # chunks x 1024 threads with a row ahead fit (the fused op with dbeta in LDS)
+    for op in (rn.OP_LN_BWD, rn.OP_LN_FUSED_ADD_BWD):
+        assert shape(plan(op, 4096, 16384)) == (R, 1024, 2, 1, 0)
+        assert shape(plan(op, 4096, 8192, rn.F32)) == (R, 1024, 2, 1, 0)
+    assert shape(plan(rn.OP_LN_BWD, 4096, 4096)) == (R, 512, 1, 1, 1)
+    # rows of 32768 bf16 / 16384 fp32 stay in registers for both ops
+    for op in (rn.OP_LN_BWD, rn.OP_LN_FUSED_ADD_BWD):
+        assert shape(plan(op, 2048, 32768)) == (R, 1024, 4, 0, 0)
+        assert shape(plan(op, 2048, 16384, rn.F32)) == (R, 1024, 4, 0, 0)
+    assert shape(plan(rn.OP_LN_FUSED_ADD_BWD, 2048, 24576)) == (R, 1024, 3, 0, 0)
+    # bf16 fused: four chunks x 1024 threads exist only for exact tilings, so a
+    # ragged row takes eight chunks x 512 threads (masked); the plain op and
+    # fp32 keep four chunks
+    assert shape(plan(rn.OP_LN_FUSED_ADD_BWD, 2048, 30000)) == (R, 512, 8, 0, 0)
+    assert shape(plan(rn.OP_LN_BWD, 2048, 30000)) == (R, 960, 4, 0, 0)
+    assert shape(plan(rn.OP_LN_FUSED_ADD_BWD, 2048, 15000, rn.F32)) == (R, 960, 4, 0, 0)
+    assert shape(plan(rn.OP_LN_FUSED_ADD_BWD, 2048, 28672)) == (R, 896, 4, 0, 0)  # exact
+    with rn.plan_override(rn.OP_LN_FUSED_ADD_BWD, path=R, vec=8, team=0, threads=960, depth=0, w_regs=0):
+        with pytest.raises(rn.RMSNormError):  # the ragged instance is not compiled
+            plan(rn.OP_LN_FUSED_ADD_BWD, 100, 30000)
+    with rn.plan_override(rn.OP_LN_FUSED_ADD_BWD, path=R, vec=8, team=0, threads=512, depth=0, w_regs=0):
+        assert plan(rn.OP_LN_FUSED_ADD_BWD, 100, 32768)["chunks"] == 8  # exact rows run the masked instance
+    with rn.plan_override(rn.OP_LN_BWD, path=R, vec=8, team=0, threads=1024, depth=2, w_regs=0):
+        with pytest.raises(rn.RMSNormError):  # two chunks, two rows ahead: not compiled
             plan(rn.OP_LN_BWD, 100, 16384)
 
 

@@ -37,7 +37,9 @@ CASES = [
     (7, 12000, "f32", True, True),
     (6, 32768, "bf16", False, False),     # four chunks x 1024 lanes, dbeta in LDS
     (5, 16384, "f32", False, True),
-    (6, 32768, "bf16", True, False),      # fused: looped rows
+    (6, 32768, "bf16", True, False),      # fused: four chunks x 1024 lanes, exact tiling only
+    (5, 30000, "bf16", True, False),      # fused, ragged: eight chunks x 512 lanes, masked
+    (5, 16384, "f32", True, False),       # fused float32: four chunks x 1024 lanes
     (4, 40000, "f32", True, True),
     (3, 4096, "bf16", False, False),      # fewer rows than programs
 ]
@@ -87,9 +89,14 @@ LN_FORCED = [
     (True, 30, 16384, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=0, w_regs=0, grid=4)),
     (True, 30, 16384, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=1, w_regs=0, grid=4)),
     (True, 20, 24576, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=0, w_regs=0, grid=3)),
-    (False, 20, 32768, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=0, w_regs=0, grid=3)),
-    (False, 20, 32768, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=0, w_regs=0, grid=3)),
-    (False, 20, 16384, "f32", dict(path=R, vec=4, team=0, threads=512, depth=0, w_regs=0, grid=3)),
+    (True, 20, 32768, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=0, w_regs=0, grid=3)),
+    (True, 20, 32768, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=0, w_regs=0, grid=3)),
+    (True, 20, 30000, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=0, w_regs=0, grid=3)),
+    (True, 20, 16384, "f32", dict(path=R, vec=4, team=0, threads=512, depth=0, w_regs=0, grid=3)),
+    (True, 20, 15000, "f32", dict(path=R, vec=4, team=0, threads=960, depth=0, w_regs=0, grid=3)),
+    (True, 30, 16384, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=1, w_regs=0, grid=4)),
+    (True, 30, 8192, "f32", dict(path=R, vec=4, team=0, threads=1024, depth=1, w_regs=0, grid=4)),
+    (True, 30, 16000, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=1, w_regs=0, grid=4)),
     (True, 20, 4000, "f32", dict(path=R, vec=4, team=0, threads=256, depth=0, w_regs=0, grid=3)),
     (True, 100, 2048, "bf16", dict(path=R, vec=1, team=0, threads=512, grid=5)),
     (True, 300, 128, "bf16", dict(path=R, vec=1, team=64, threads=256)),

@@ -64,11 +64,11 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
     T *dxp = static_cast<T *>(a.dx);
     const float *__restrict__ rstd = a.rstd;
 
-    // LayerNorm rows of four or more chunks per lane keep the dbeta
-    // accumulators in LDS instead of registers: each lane owns the slots of
-    // its own columns (no barriers), laid out as float4 planes [V / 4][nchunks]
-    // so that a wavefront's 16-byte accesses are contiguous.
-    constexpr bool BL = LN && TEAM == 0 && K >= 4 && V >= 4;
+    // Wide LayerNorm rows (bwd_dbeta_in_lds) keep the dbeta accumulators in
+    // LDS instead of registers: each lane owns the slots of its own columns
+    // (no barriers), laid out as float4 planes [V / 4][nchunks] so that a
+    // wavefront's 16-byte accesses are contiguous.
+    constexpr bool BL = bwd_dbeta_in_lds(LN, FUSED, TEAM, K, V);
     constexpr int KW = WR ? K : 1;
     constexpr int KB = (LN && !BL) ? K : 1;
     constexpr int NPL = V / 4 > 0 ? V / 4 : 1; // float4 planes of the LDS dbeta row
@@ -529,24 +529,31 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(const float *__re
 }
 
 template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FUSED, bool LN>
-static void launch_bwd_rows(const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s)
+static hipError_t launch_bwd_rows(const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s)
 {
     const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
     const int lanes = TEAM ? TEAM : p.threads;
     const size_t sets = LN ? 2 : 1;
-    // sub-workgroup teams: their partial rows; LayerNorm at four or more
-    // chunks per lane: the dbeta row (N floats)
-    constexpr bool BL = LN && TEAM == 0 && K >= 4 && V >= 4;
+    // sub-workgroup teams: their partial rows; LayerNorm with dbeta in LDS:
+    // the dbeta row (N floats)
+    constexpr bool BL = bwd_dbeta_in_lds(LN, FUSED, TEAM, K, V);
     const size_t lds = TEAM ? sets * (size_t)(p.threads / TEAM) * (size_t)a.N * sizeof(float)
                             : (BL ? (size_t)a.N * sizeof(float) : 0);
-    if constexpr (V > 1) {
+    constexpr int kTiling = bwd_tiling(LN, FUSED, (int)sizeof(T), V, TEAM, K, BOUND);
+    if constexpr (V > 1 && kTiling != TILING_MASKED_ONLY) {
         if ((int64_t)lanes * K == a.N / V) {
             hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, true, LN>), grid, block, lds, s,
                                a);
-            return;
+            return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, false, LN>), grid, block, lds, s, a);
+    if constexpr (kTiling == TILING_EXACT_ONLY) {
+        return hipErrorInvalidConfiguration; // ragged row: the selector never plans it
+    } else {
+        hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, false, LN>), grid, block, lds, s,
+                           a);
+        return hipGetLastError();
+    }
 }
 
 template <typename T, bool FUSED, bool LN>
@@ -567,8 +574,8 @@ static hipError_t dispatch_bwd(const rmsnorm_plan &p, BwdArgs a, hipStream_t s)
 #define RMSNORM_CASE(VEC, TEAM, K, D, WR, BOUND, FBOUND)                                      \
     if constexpr ((FUSED ? FBOUND : BOUND) > 0) {                                                 \
         if (vec == (VEC == 1) && p.team == TEAM && p.chunks == K && p.depth == D && p.w_regs == WR) { \
-            launch_bwd_rows<T, (VEC == 1 ? VV : 1), TEAM, K, D, WR == 1, (FUSED ? FBOUND : BOUND), FUSED, LN>(p, a, s); \
-            return hipGetLastError();                                                             \
+            return launch_bwd_rows<T, (VEC == 1 ? VV : 1), TEAM, K, D, WR == 1, (FUSED ? FBOUND : BOUND), FUSED, \
+                                   LN>(p, a, s);                                                  \
         }                                                                                         \
     }
     if constexpr (LN) {

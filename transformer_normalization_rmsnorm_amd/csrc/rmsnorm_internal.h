@@ -108,18 +108,43 @@ constexpr int kFinColsPerBlock = 32;
     X(0, 0, 2, 1, 1, 512, 512) X(0, 0, 4, 1, 1, 512, 512)
 
 // LayerNorm backward: the same fields.  It also holds the row mean and a
-// second set of accumulators (dbeta; in LDS at four or more vector chunks per
-// lane, N floats per workgroup), so its bounds are its own.  A bound of 0:
-// not compiled for that op.
+// second set of accumulators (dbeta), so its bounds are its own.  The dbeta
+// accumulators of workgroup teams with vector access live in LDS (N floats per
+// workgroup) at four or more chunks per lane, and for the fused-add op, which
+// also holds the dh row, at two or more (bwd_dbeta_in_lds).  A bound of 0: not
+// compiled for that op.
 #define RMSNORM_LN_BWD_ROWS_CONFIGS(X)                                                   \
     X(1, 8, 1, 1, 1, 256, 256) X(1, 16, 1, 1, 1, 256, 256) X(1, 32, 1, 1, 1, 256, 256)   \
     X(1, 64, 1, 1, 1, 256, 256) X(1, 64, 2, 1, 1, 256, 256)                              \
     X(1, 0, 1, 1, 1, 1024, 1024) X(1, 0, 1, 2, 1, 1024, 1024)                            \
-    X(1, 0, 2, 0, 0, 1024, 1024) X(1, 0, 2, 1, 0, 512, 512) X(1, 0, 3, 0, 0, 1024, 1024) \
-    X(1, 0, 4, 0, 0, 1024, 512) X(1, 0, 4, 1, 0, 512, 512) X(1, 0, 6, 0, 0, 512, 512)    \
-    X(1, 0, 8, 0, 0, 512, 0)                                                             \
+    X(1, 0, 2, 0, 0, 1024, 1024) X(1, 0, 2, 1, 0, 1024, 1024) X(1, 0, 3, 0, 0, 1024, 1024) \
+    X(1, 0, 4, 0, 0, 1024, 1024) X(1, 0, 4, 1, 0, 512, 512) X(1, 0, 6, 0, 0, 512, 512)   \
+    X(1, 0, 8, 0, 0, 512, 512)                                                           \
     X(0, 64, 1, 1, 1, 256, 256) X(0, 64, 2, 1, 1, 256, 256) X(0, 0, 1, 1, 1, 1024, 1024) \
     X(0, 0, 2, 1, 1, 512, 512) X(0, 0, 4, 1, 1, 512, 512)
+
+// LayerNorm backward layouts with dbeta accumulated in LDS.
+constexpr bool bwd_dbeta_in_lds(bool ln, bool fused, int team, int chunks, int vec)
+{
+    return ln && team == 0 && vec >= 4 && (chunks >= 4 || (fused && chunks >= 2));
+}
+
+// Which instances of a backward register layout exist.  A row tiled exactly
+// (threads x chunks x vec == N) runs the instance without masking, a ragged
+// row the masked one, which is also correct for exact rows.  Two bf16
+// fused-add LayerNorm layouts fit their registers with only one of them: four
+// chunks x 1024 threads (128 VGPRs) only unmasked, so the selector takes it
+// only for exact tilings; eight chunks x 512 threads (256 VGPRs) only masked,
+// which then runs exact rows as well.
+enum BwdTiling { TILING_ANY = 0, TILING_EXACT_ONLY = 1, TILING_MASKED_ONLY = 2 };
+constexpr int bwd_tiling(bool ln, bool fused, int elem_size, int vec, int team, int chunks, int bound)
+{
+    if (!(ln && fused && elem_size == 2 && vec > 1 && team == 0))
+        return TILING_ANY;
+    if (chunks == 4 && bound == 1024)
+        return TILING_EXACT_ONLY;
+    return chunks == 8 ? TILING_MASKED_ONLY : TILING_ANY;
+}
 
 // LayerNorm forward: the forward layouts without prefetch, up to this many
 // chunks per lane (it also holds beta).

@@ -86,16 +86,24 @@ bool pick_block_team(int op, bool vec, int64_t nchunks, int depth, rmsnorm_plan 
     return false;
 }
 
+// Whether the compiled instances of a backward layout can run this tiling
+// (bwd_tiling: some layouts exist only for rows tiled exactly).
+bool tiling_ok(int op, int dtype, bool vec, int team, int k, int b, int64_t lanes, int64_t nchunks)
+{
+    const int t = bwd_tiling(is_ln_op(op), is_fused(op), elem_bytes(dtype), vec ? vec_elems(dtype) : 1, team, k, b);
+    return t != TILING_EXACT_ONLY || lanes * k == nchunks;
+}
+
 // Backward rows too wide for w in registers: gamma is re-read with every row.
 // The fewest chunks per lane whose thread count fits a compiled launch bound,
 // with the deepest prefetch compiled at that size.
-bool pick_wide_bwd_team(int op, bool vec, int64_t nchunks, rmsnorm_plan *p)
+bool pick_wide_bwd_team(int op, int dtype, bool vec, int64_t nchunks, rmsnorm_plan *p)
 {
     for (int k = 1; k <= 16; ++k) {
         const int64_t threads = std::max<int64_t>(64, round_up(ceil_div(nchunks, k), 64));
         for (int d = 3; d >= 0; --d) {
             const int b = bound(op, vec, 0, k, d, 0);
-            if (b > 0 && threads <= b) {
+            if (b > 0 && threads <= b && tiling_ok(op, dtype, vec, 0, k, b, threads, nchunks)) {
                 p->team = 0;
                 p->threads = (int32_t)threads;
                 p->chunks = k;
@@ -182,7 +190,10 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
         }
         const int lanes = p->team ? p->team : p->threads;
         const int k = pick_chunks(p->op, p->vec != 1, p->team, p->depth, p->w_regs, ceil_div(nchunks, lanes));
-        if (k == 0 || p->threads > bound(p->op, p->vec != 1, p->team, k, p->depth, p->w_regs))
+        const int b = k == 0 ? 0 : bound(p->op, p->vec != 1, p->team, k, p->depth, p->w_regs);
+        if (k == 0 || p->threads > b)
+            return false;
+        if (bwd && !tiling_ok(p->op, dtype, p->vec != 1, p->team, k, b, lanes, nchunks))
             return false;
         p->chunks = k;
         const int64_t sets = is_ln_op(p->op) ? 2 : 1;
@@ -274,7 +285,7 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             // fp32 16384 x 6144: 197.3 vs 204.1 us) and ties it at 10240 bf16.
             if (bwd)
                 placed = (nchunks <= 1024 && pick_block_team(op, true, nchunks, p.depth, &p)) ||
-                         pick_wide_bwd_team(op, true, nchunks, &p);
+                         pick_wide_bwd_team(op, dtype, true, nchunks, &p);
             else
                 placed = pick_fwd_block_team(op, true, nchunks, p.depth, target, &p);
         }
