@@ -428,7 +428,9 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} (WORLD_SIZE={world}) is not supported; "
-              "RMSNorm rows shard across GPUs with no exchange except dgamma, see DESIGN.md", file=sys.stderr)
+              "this benchmark runs on a single GPU.  Across GPUs the rows would shard with no exchange except "
+              "dgamma: each GPU's partial rows, finalized locally and then gathered and summed in rank order",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
