@@ -341,10 +341,17 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
 }
 
 // Any N: per row, pass 1 forms the row sums (dot; LayerNorm: mean(g) and
-// mean(g * xhat)), pass 2 re-reads the row, writes dx and accumulates this
-// workgroup's partial rows in place (each lane always owns the same columns,
-// so the read-modify-write is private to the lane).
-template <typename T, int V, bool FUSED, bool LN>
+// mean(g * xhat)), pass 2 re-reads the row (from cache) and writes dx.  Lane
+// t owns the chunks t, t + nt, t + 2 nt, ...  The dgamma (and dbeta)
+// accumulators of its first KA chunks stay in registers for all the
+// workgroup's rows and are written once at the end; those of later chunks
+// (rows wider than KA x nt x V) are read, updated and written back in the
+// partial rows with every row (the lane owns them, so the read-modify-write
+// is private).  The KA chunks are loaded unconditionally, a chunk past the
+// row's end re-reading its last one, so that their loads stay in flight
+// together (a load that may be skipped makes the compiler wait for all
+// outstanding ones).
+template <typename T, int V, bool FUSED, bool LN, int KA>
 __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
 {
     using C = Chunk<T, V>;
@@ -357,12 +364,24 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
     const T *__restrict__ gp = static_cast<const T *>(a.gamma);
     const T *dhp = static_cast<const T *>(a.dh);
     T *dxp = static_cast<T *>(a.dx);
+    // without gamma the weight loads read dy's first row and are ignored
+    const T *__restrict__ gsrc = gp != nullptr ? gp : dyp;
     // null: no dgamma (non-affine) and no dbeta
     float *part = a.partials ? a.partials + (int64_t)blockIdx.x * a.ld : nullptr;
     float *partb = (LN && a.partials) ? a.partials + (a.grid + (int64_t)blockIdx.x) * a.ld : nullptr;
     auto wgt = [&](const C &g, int e) __attribute__((always_inline)) {
         return gp != nullptr ? g.get(e) + a.offset : 1.0f;
     };
+    float acc[KA][V], accb[LN ? KA : 1][V];
+#pragma unroll
+    for (int j = 0; j < KA; ++j) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            acc[j][e] = 0.0f;
+            if constexpr (LN)
+                accb[j][e] = 0.0f;
+        }
+    }
 
     __shared__ float red[2][32];
     int parity = 0;
@@ -372,12 +391,7 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
         const float rs = a.rstd[row];
         const float mu = LN ? a.mean[row] : 0.0f;
         float s1 = 0.0f, s2 = 0.0f; // RMSNorm: s1 = dot; LayerNorm: sum g, sum g * xhat
-        for (int c = threadIdx.x; c < nchunks; c += nt) {
-            C v, d, g;
-            v.load_cached(vp + base + (int64_t)c * V);
-            d.load_cached(dyp + base + (int64_t)c * V);
-            if (gp != nullptr)
-                g.load_cached(gp + (int64_t)c * V);
+        auto sums = [&](const C &v, const C &d, const C &g) __attribute__((always_inline)) {
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const float gg = d.get(e) * wgt(g, e);
@@ -388,6 +402,29 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
                     s1 = fmaf(gg, v.get(e), s1);
                 }
             }
+        };
+#pragma unroll
+        for (int j = 0; j < KA; ++j) {
+            const int c = (int)threadIdx.x + j * nt;
+            int cc = min(c, nchunks - 1);
+            pin_vgpr(cc); // form the addresses per row rather than hold them
+            C v, d, g;
+            v.load_cached(vp + base + (int64_t)cc * V);
+            d.load_cached(dyp + base + (int64_t)cc * V);
+            g.load_cached(gsrc + (int64_t)cc * V);
+            if (c < nchunks)
+                sums(v, d, g);
+            // two chunks in flight at a time: the accumulators take the
+            // registers that hoisting every chunk's loads would need
+            if (j % 2 == 1)
+                asm volatile("" ::: "memory");
+        }
+        for (int c = (int)threadIdx.x + KA * nt; c < nchunks; c += nt) {
+            C v, d, g;
+            v.load_cached(vp + base + (int64_t)c * V);
+            d.load_cached(dyp + base + (int64_t)c * V);
+            g.load_cached(gsrc + (int64_t)c * V);
+            sums(v, d, g);
         }
         if constexpr (LN) {
             block_sum2(s1, s2, red[parity], a.threads);
@@ -397,25 +434,10 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
         parity ^= 1;
         const float kc = rs * rs * rs * s1 * inv_n;       // RMSNorm
         const float c1 = s1 * inv_n, c2 = s2 * inv_n;     // LayerNorm
-        for (int c = threadIdx.x; c < nchunks; c += nt) {
-            C v, d, g;
-            v.load_cached(vp + base + (int64_t)c * V);
-            d.load_cached(dyp + base + (int64_t)c * V);
-            if (gp != nullptr)
-                g.load_cached(gp + (int64_t)c * V);
-            float o[V], pa[V], pb[V];
-            if (first || part == nullptr) {
-#pragma unroll
-                for (int e = 0; e < V; ++e)
-                    pa[e] = pb[e] = 0.0f;
-            } else {
-                load_f32<V>(part + (int64_t)c * V, pa);
-                if constexpr (LN)
-                    load_f32<V>(partb + (int64_t)c * V, pb);
-            }
-            C dh;
-            if constexpr (FUSED)
-                dh.load_cached(dhp + base + (int64_t)c * V);
+        // dx of one chunk, with its dgamma / dbeta contributions added to pa / pb
+        auto chunk_dx = [&](int c, const C &v, const C &d, const C &g, const C &dh, float (&pa)[V],
+                            float (&pb)[V]) __attribute__((always_inline)) {
+            float o[V];
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const float dv = d.get(e);
@@ -437,11 +459,57 @@ __global__ void __launch_bounds__(1024) bwd_loop_kernel(BwdArgs a)
             C out;
             out.set(o);
             out.store(dxp + base + (int64_t)c * V);
+        };
+#pragma unroll
+        for (int j = 0; j < KA; ++j) {
+            const int c = (int)threadIdx.x + j * nt;
+            int cc = min(c, nchunks - 1);
+            pin_vgpr(cc);
+            C v, d, g, dh;
+            v.load_cached(vp + base + (int64_t)cc * V);
+            d.load_cached(dyp + base + (int64_t)cc * V);
+            g.load_cached(gsrc + (int64_t)cc * V);
+            if constexpr (FUSED)
+                dh.load_cached(dhp + base + (int64_t)cc * V);
+            if (c < nchunks)
+                chunk_dx(c, v, d, g, dh, acc[j], accb[LN ? j : 0]);
+            if (j % 2 == 1)
+                asm volatile("" ::: "memory");
+        }
+        for (int c = (int)threadIdx.x + KA * nt; c < nchunks; c += nt) {
+            C v, d, g, dh;
+            v.load_cached(vp + base + (int64_t)c * V);
+            d.load_cached(dyp + base + (int64_t)c * V);
+            g.load_cached(gsrc + (int64_t)c * V);
+            if constexpr (FUSED)
+                dh.load_cached(dhp + base + (int64_t)c * V);
+            float pa[V], pb[V];
+            if (first || part == nullptr) {
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    pa[e] = pb[e] = 0.0f;
+            } else {
+                load_f32<V>(part + (int64_t)c * V, pa);
+                if constexpr (LN)
+                    load_f32<V>(partb + (int64_t)c * V, pb);
+            }
+            chunk_dx(c, v, d, g, dh, pa, pb);
             if (part != nullptr) {
                 store_f32<V>(part + (int64_t)c * V, pa);
                 if constexpr (LN)
                     store_f32<V>(partb + (int64_t)c * V, pb);
             }
+        }
+    }
+    if (part == nullptr)
+        return;
+#pragma unroll
+    for (int j = 0; j < KA; ++j) {
+        const int c = (int)threadIdx.x + j * nt;
+        if (c < nchunks) {
+            store_f32<V>(part + (int64_t)c * V, acc[j]);
+            if constexpr (LN)
+                store_f32<V>(partb + (int64_t)c * V, accb[j]);
         }
     }
 }
@@ -556,6 +624,19 @@ static hipError_t launch_bwd_rows(const rmsnorm_plan &p, const BwdArgs &a, hipSt
     }
 }
 
+// Register accumulator slots of the looped backward (chunks per lane whose
+// dgamma / dbeta sums stay in registers): the most that compile for 1024
+// threads (128 VGPRs) without spilling.  bf16 chunks unpack to twice the
+// registers they load into, so they get fewer; LayerNorm holds two sets.
+template <typename T, int V, bool LN>
+constexpr int loop_slots()
+{
+    if constexpr (V > 1 && sizeof(T) == 2)
+        return LN ? 3 : 7;
+    else
+        return LN ? 4 : 8;
+}
+
 template <typename T, bool FUSED, bool LN>
 static hipError_t dispatch_bwd(const rmsnorm_plan &p, BwdArgs a, hipStream_t s)
 {
@@ -564,10 +645,22 @@ static hipError_t dispatch_bwd(const rmsnorm_plan &p, BwdArgs a, hipStream_t s)
     a.grid = p.grid;
     const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
     if (p.path == RMSNORM_PATH_LOOP) {
-        if (p.vec == VV)
-            hipLaunchKernelGGL((bwd_loop_kernel<T, VV, FUSED, LN>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((bwd_loop_kernel<T, 1, FUSED, LN>), grid, block, 0, s, a);
+        // register accumulator slots: four for rows of at most four chunks per
+        // lane, else the most that fit 1024-thread workgroups without spilling
+        constexpr int KV = loop_slots<T, VV, LN>(), K1 = loop_slots<T, 1, LN>();
+        const int64_t per_lane = ((int64_t)a.N / p.vec + p.threads - 1) / p.threads;
+        const bool few = per_lane <= 4;
+        if (p.vec == VV) {
+            if (few)
+                hipLaunchKernelGGL((bwd_loop_kernel<T, VV, FUSED, LN, (KV < 4 ? KV : 4)>), grid, block, 0, s, a);
+            else
+                hipLaunchKernelGGL((bwd_loop_kernel<T, VV, FUSED, LN, KV>), grid, block, 0, s, a);
+        } else {
+            if (few)
+                hipLaunchKernelGGL((bwd_loop_kernel<T, 1, FUSED, LN, (K1 < 4 ? K1 : 4)>), grid, block, 0, s, a);
+            else
+                hipLaunchKernelGGL((bwd_loop_kernel<T, 1, FUSED, LN, K1>), grid, block, 0, s, a);
+        }
         return hipGetLastError();
     }
     const bool vec = (p.vec == VV);
