@@ -135,10 +135,20 @@ def _check(rc: int, func: str):
 
 # ---- torch marshalling --------------------------------------------------------
 
-def _torch():
-    import torch
+_torch_mod = None
+_raw_stream = None
 
-    return torch
+
+def _torch():
+    global _torch_mod, _raw_stream
+    if _torch_mod is None:
+        import torch
+
+        # the current stream of a device as a raw handle, without building a
+        # Stream object per call (falls back to the public API)
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _torch_mod = torch
+    return _torch_mod
 
 
 def _dtype_code(t) -> int:
@@ -155,19 +165,19 @@ def _ptr(t) -> Optional[int]:
 
 
 def _require(t, name, shape=None, dtype=None, device=None):
-    torch = _torch()
     if t is None:
         raise ValueError(f"{name} is required")
-    if not t.is_cuda:
+    if device is not None:
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+    elif not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
-    if device is not None and t.device != device:
-        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
     return t
 
 
@@ -179,26 +189,72 @@ def _rows(x):
     return M, N
 
 
-@contextlib.contextmanager
-def _on_device(device):
-    """Enter the tensors' device only when it is not already current."""
+def _stream_handle(index: int) -> int:
+    """The caller's current stream on device `index` (what torch launches on)."""
     torch = _torch()
-    if torch.cuda.current_device() == device.index:
-        yield
+    if _raw_stream is not None:
+        return _raw_stream(index)
+    return torch.cuda.current_stream(index).cuda_stream
+
+
+def _launch(dev, name: str, *args):
+    """Call entry point `name` with the current stream of the tensors' device
+    appended, entering that device only when it is not already current."""
+    torch = _torch()
+    fn = getattr(load_library(), name)
+    idx = dev.index
+    if torch.cuda.current_device() == idx:
+        rc = fn(*args, _stream_handle(idx))
     else:
-        with torch.cuda.device(device):
-            yield
+        with torch.cuda.device(idx):
+            rc = fn(*args, _stream_handle(idx))
+    _check(rc, name)
 
 
-def _stream(device):
-    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+def _on_device_call(dev, f):
+    """f() with the tensors' device current (host queries that read it)."""
+    torch = _torch()
+    if torch.cuda.current_device() == dev.index:
+        return f()
+    with torch.cuda.device(dev.index):
+        return f()
+
+
+# Backward workspace sizes by (op family, M, N, dtype, device): they depend only
+# on those and the device's compute-unit count.  Ops with a forced plan
+# (rmsnorm_set_plan_override) are sized from their plans instead.
+_ws_cache: dict = {}
+_overridden: set = set()
+
+
+def _bwd_workspace(family: str, M: int, N: int, code: int, dev, ops):
+    torch = _torch()
+    key = (family, M, N, code, dev.index)
+    nbytes = _ws_cache.get(key)
+    if nbytes is None:
+        query = rmsnorm_bwd_workspace_bytes if family == "rms" else layernorm_bwd_workspace_bytes
+        nbytes = _on_device_call(dev, lambda: query(M, N, code))
+        if len(_ws_cache) > 4096:
+            _ws_cache.clear()
+        _ws_cache[key] = nbytes
+    if _overridden.intersection(ops):
+        def planned():
+            nb = nbytes
+            for op in ops:
+                for vec_ok in (True, False):
+                    try:
+                        nb = max(nb, rmsnorm_query_plan(op, M, N, code, vec_ok)["workspace_bytes"])
+                    except RMSNormError:
+                        pass  # a forced vector layout has no unaligned plan
+            return nb
+        nbytes = _on_device_call(dev, planned)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev), nbytes
 
 
 def rmsnorm_fwd(x, gamma, eps: float = 1e-6, offset: float = 0.0, *, y=None, rstd=None, save_rstd: bool = True):
     """y = x * rstd * (gamma + offset) over the last dimension; returns (y, rstd).
     gamma None: the non-affine op (offset must be 0)."""
     torch = _torch()
-    lib = load_library()
     _require(x, "x")
     M, N = _rows(x)
     dev = x.device
@@ -206,14 +262,14 @@ def rmsnorm_fwd(x, gamma, eps: float = 1e-6, offset: float = 0.0, *, y=None, rst
         _require(gamma, "gamma", (N,), x.dtype, dev)
     if y is None:
         y = torch.empty_like(x)
-    _require(y, "y", x.shape, x.dtype, dev)
-    if rstd is None and save_rstd:
-        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev)
-    if rstd is not None:
+    else:
+        _require(y, "y", x.shape, x.dtype, dev)
+    if rstd is None:
+        if save_rstd:
+            rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev)
+    else:
         _require(rstd, "rstd", x.shape[:-1], torch.float32, dev)
-    with _on_device(dev):
-        _check(lib.rmsnorm_fwd(_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, eps, offset, _dtype_code(x),
-                               _stream(dev)), "rmsnorm_fwd")
+    _launch(dev, "rmsnorm_fwd", _ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, eps, offset, _dtype_code(x))
     return y, rstd
 
 
@@ -223,7 +279,6 @@ def rmsnorm_fused_add_fwd(x, residual, gamma, eps: float = 1e-6, offset: float =
 
     Pass h_out=residual to update the residual stream in place."""
     torch = _torch()
-    lib = load_library()
     _require(x, "x")
     M, N = _rows(x)
     dev = x.device
@@ -232,17 +287,19 @@ def rmsnorm_fused_add_fwd(x, residual, gamma, eps: float = 1e-6, offset: float =
         _require(gamma, "gamma", (N,), x.dtype, dev)
     if y is None:
         y = torch.empty_like(x)
+    else:
+        _require(y, "y", x.shape, x.dtype, dev)
     if h_out is None:
         h_out = torch.empty_like(x)
-    _require(y, "y", x.shape, x.dtype, dev)
-    _require(h_out, "h_out", x.shape, x.dtype, dev)
-    if rstd is None and save_rstd:
-        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev)
-    if rstd is not None:
+    else:
+        _require(h_out, "h_out", x.shape, x.dtype, dev)
+    if rstd is None:
+        if save_rstd:
+            rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev)
+    else:
         _require(rstd, "rstd", x.shape[:-1], torch.float32, dev)
-    with _on_device(dev):
-        _check(lib.rmsnorm_fused_add_fwd(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(y), _ptr(h_out), _ptr(rstd),
-                                         M, N, eps, offset, _dtype_code(x), _stream(dev)), "rmsnorm_fused_add_fwd")
+    _launch(dev, "rmsnorm_fused_add_fwd", _ptr(x), _ptr(residual), _ptr(gamma), _ptr(y), _ptr(h_out), _ptr(rstd),
+            M, N, eps, offset, _dtype_code(x))
     return y, h_out, rstd
 
 
@@ -256,7 +313,6 @@ def rmsnorm_fwd_fp8_workspace_bytes(M: int, N: int, dtype_code: int) -> int:
 
 def _fp8_common(x, residual, gamma, scale, eps, offset, amax, y8, h_out, rstd, save_rstd, workspace):
     torch = _torch()
-    lib = load_library()
     _require(x, "x")
     M, N = _rows(x)
     dev = x.device
@@ -288,19 +344,15 @@ def _fp8_common(x, residual, gamma, scale, eps, offset, amax, y8, h_out, rstd, s
     ws_bytes = 0
     if amax is not None:
         if workspace is None:
-            ws_bytes = rmsnorm_fwd_fp8_workspace_bytes(M, N, _dtype_code(x))
+            ws_bytes = _on_device_call(dev, lambda: rmsnorm_fwd_fp8_workspace_bytes(M, N, _dtype_code(x)))
             workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size()
-    with _on_device(dev):
-        if fused:
-            _check(lib.rmsnorm_fused_add_fwd_fp8(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(y8), _ptr(h_out),
-                                                 _ptr(rstd), _ptr(scale), _ptr(amax), _ptr(workspace), ws_bytes,
-                                                 M, N, eps, offset, _dtype_code(x), _stream(dev)),
-                   "rmsnorm_fused_add_fwd_fp8")
-        else:
-            _check(lib.rmsnorm_fwd_fp8(_ptr(x), _ptr(gamma), _ptr(y8), _ptr(rstd), _ptr(scale), _ptr(amax),
-                                       _ptr(workspace), ws_bytes, M, N, eps, offset, _dtype_code(x), _stream(dev)),
-                   "rmsnorm_fwd_fp8")
+    if fused:
+        _launch(dev, "rmsnorm_fused_add_fwd_fp8", _ptr(x), _ptr(residual), _ptr(gamma), _ptr(y8), _ptr(h_out),
+                _ptr(rstd), _ptr(scale), _ptr(amax), _ptr(workspace), ws_bytes, M, N, eps, offset, _dtype_code(x))
+    else:
+        _launch(dev, "rmsnorm_fwd_fp8", _ptr(x), _ptr(gamma), _ptr(y8), _ptr(rstd), _ptr(scale), _ptr(amax),
+                _ptr(workspace), ws_bytes, M, N, eps, offset, _dtype_code(x))
     return y8, h_out, rstd
 
 
@@ -328,22 +380,18 @@ def rmsnorm_bwd_workspace_bytes(M: int, N: int, dtype_code: int) -> int:
 
 
 def alloc_workspace(M: int, N: int, dtype_code: int, device, op: Optional[int] = None):
-    """Workspace for a backward call; with `op`, also large enough for a plan
-    forced by rmsnorm_set_plan_override."""
+    """Workspace for a backward call on `device` (the RMSNorm ops; with `op`
+    a LayerNorm op, LayerNorm's), also large enough for a plan forced by
+    rmsnorm_set_plan_override.  Returns (tensor, bytes)."""
     torch = _torch()
-    nbytes = rmsnorm_bwd_workspace_bytes(M, N, dtype_code)
-    if op is not None:
-        for vec_ok in (True, False):
-            try:
-                nbytes = max(nbytes, rmsnorm_query_plan(op, M, N, dtype_code, vec_ok)["workspace_bytes"])
-            except RMSNormError:
-                pass  # a forced vector layout has no unaligned plan
-    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device), nbytes
+    device = torch.device(device)
+    if op in (OP_LN_BWD, OP_LN_FUSED_ADD_BWD):
+        return _bwd_workspace("ln", M, N, dtype_code, device, (OP_LN_BWD, OP_LN_FUSED_ADD_BWD))
+    return _bwd_workspace("rms", M, N, dtype_code, device, (OP_BWD, OP_FUSED_ADD_BWD))
 
 
 def _bwd_common(name, dy, dh, v, gamma, rstd, eps, offset, dx, dgamma, workspace):
     torch = _torch()
-    lib = load_library()
     _require(v, "x" if dh is None else "h")
     M, N = _rows(v)
     dev = v.device
@@ -356,26 +404,25 @@ def _bwd_common(name, dy, dh, v, gamma, rstd, eps, offset, dx, dgamma, workspace
         _require(rstd, "rstd", v.shape[:-1], torch.float32, dev)
     if dx is None:
         dx = torch.empty_like(v)
+    else:
+        _require(dx, "dx", v.shape, v.dtype, dev)
     if gamma is not None:
         if dgamma is None:
             dgamma = torch.empty_like(gamma)
-        _require(dgamma, "dgamma", (N,), v.dtype, dev)
-    _require(dx, "dx", v.shape, v.dtype, dev)
-    with _on_device(dev):
-        if workspace is None:
-            op = OP_BWD if name == "rmsnorm_bwd" else OP_FUSED_ADD_BWD
-            workspace, nbytes = alloc_workspace(M, N, _dtype_code(v), dev, op)
         else:
-            _require(workspace, "workspace", device=dev)
-            nbytes = workspace.numel() * workspace.element_size()
-        if name == "rmsnorm_bwd":
-            rc = lib.rmsnorm_bwd(_ptr(dy), _ptr(v), _ptr(gamma), _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(workspace),
-                                 nbytes, M, N, eps, offset, _dtype_code(v), _stream(dev))
-        else:
-            rc = lib.rmsnorm_fused_add_bwd(_ptr(dy), _ptr(dh), _ptr(v), _ptr(gamma), _ptr(rstd), _ptr(dx),
-                                           _ptr(dgamma), _ptr(workspace), nbytes, M, N, eps, offset, _dtype_code(v),
-                                           _stream(dev))
-        _check(rc, name)
+            _require(dgamma, "dgamma", (N,), v.dtype, dev)
+    code = _dtype_code(v)
+    if workspace is None:
+        workspace, nbytes = _bwd_workspace("rms", M, N, code, dev, (OP_BWD, OP_FUSED_ADD_BWD))
+    else:
+        _require(workspace, "workspace", device=dev)
+        nbytes = workspace.numel() * workspace.element_size()
+    if name == "rmsnorm_bwd":
+        _launch(dev, name, _ptr(dy), _ptr(v), _ptr(gamma), _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(workspace),
+                nbytes, M, N, eps, offset, code)
+    else:
+        _launch(dev, name, _ptr(dy), _ptr(dh), _ptr(v), _ptr(gamma), _ptr(rstd), _ptr(dx), _ptr(dgamma),
+                _ptr(workspace), nbytes, M, N, eps, offset, code)
     return dx, dgamma
 
 
@@ -398,30 +445,24 @@ def rmsnorm_bwd_partials(dy, v, gamma, rstd, dh=None, eps: float = 1e-6, offset:
     """First backward stage: returns (dx, workspace, programs); the float32 partials
     are workspace.view(float32)[: programs * ld] with ld = N rounded up to 64."""
     torch = _torch()
-    lib = load_library()
     M, N = _rows(v)
     dev = v.device
     if dx is None:
         dx = torch.empty_like(v)
     if workspace is None:
-        workspace, nbytes = alloc_workspace(M, N, _dtype_code(v), dev, OP_BWD if dh is None else OP_FUSED_ADD_BWD)
+        workspace, nbytes = _bwd_workspace("rms", M, N, _dtype_code(v), dev, (OP_BWD, OP_FUSED_ADD_BWD))
     else:
         nbytes = workspace.numel() * workspace.element_size()
     programs = ctypes.c_int64(0)
-    with _on_device(dev):
-        _check(lib.rmsnorm_bwd_partials(_ptr(dy), _ptr(v), _ptr(gamma), _ptr(rstd), _ptr(dh), _ptr(dx),
-                                        _ptr(workspace), nbytes, ctypes.byref(programs), M, N, eps, offset,
-                                        _dtype_code(v), _stream(dev)), "rmsnorm_bwd_partials")
+    _launch(dev, "rmsnorm_bwd_partials", _ptr(dy), _ptr(v), _ptr(gamma), _ptr(rstd), _ptr(dh), _ptr(dx),
+            _ptr(workspace), nbytes, ctypes.byref(programs), M, N, eps, offset, _dtype_code(v))
     return dx, workspace, int(programs.value)
 
 
 def rmsnorm_dgamma_finalize(partials, programs: int, N: int, dgamma):
     """Second backward stage: dgamma = fixed-order sum of `programs` partial rows."""
-    lib = load_library()
-    dev = dgamma.device
-    with _on_device(dev):
-        _check(lib.rmsnorm_dgamma_finalize(_ptr(partials), programs, N, _ptr(dgamma), _dtype_code(dgamma),
-                                           _stream(dev)), "rmsnorm_dgamma_finalize")
+    _launch(dgamma.device, "rmsnorm_dgamma_finalize", _ptr(partials), programs, N, _ptr(dgamma),
+            _dtype_code(dgamma))
     return dgamma
 
 
@@ -443,6 +484,7 @@ def rmsnorm_set_plan_override(op: int, plan: Optional[dict]):
     lib = load_library()
     if plan is None:
         _check(lib.rmsnorm_set_plan_override(op, None), "rmsnorm_set_plan_override")
+        _overridden.discard(op)
         return
     p = Plan()
     p.depth = -1
@@ -450,6 +492,7 @@ def rmsnorm_set_plan_override(op: int, plan: Optional[dict]):
     for k, v in plan.items():
         setattr(p, k, v)
     _check(lib.rmsnorm_set_plan_override(op, ctypes.byref(p)), "rmsnorm_set_plan_override")
+    _overridden.add(op)
 
 
 @contextlib.contextmanager
@@ -473,7 +516,6 @@ def layernorm_bwd_workspace_bytes(M: int, N: int, dtype_code: int) -> int:
 
 def _ln_fwd_common(x, residual, gamma, beta, eps, offset, y, h_out, mean, rstd, save_stats):
     torch = _torch()
-    lib = load_library()
     _require(x, "x")
     M, N = _rows(x)
     dev = x.device
@@ -496,14 +538,12 @@ def _ln_fwd_common(x, residual, gamma, beta, eps, offset, y, h_out, mean, rstd, 
     for t, name in ((mean, "mean"), (rstd, "rstd")):
         if t is not None:
             _require(t, name, x.shape[:-1], torch.float32, dev)
-    with _on_device(dev):
-        if fused:
-            _check(lib.layernorm_fused_add_fwd(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(h_out),
-                                               _ptr(mean), _ptr(rstd), M, N, eps, offset, _dtype_code(x),
-                                               _stream(dev)), "layernorm_fused_add_fwd")
-        else:
-            _check(lib.layernorm_fwd(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), M, N, eps,
-                                     offset, _dtype_code(x), _stream(dev)), "layernorm_fwd")
+    if fused:
+        _launch(dev, "layernorm_fused_add_fwd", _ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y),
+                _ptr(h_out), _ptr(mean), _ptr(rstd), M, N, eps, offset, _dtype_code(x))
+    else:
+        _launch(dev, "layernorm_fwd", _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), M, N, eps,
+                offset, _dtype_code(x))
     return y, h_out, mean, rstd
 
 
@@ -523,7 +563,6 @@ def layernorm_fused_add_fwd(x, residual, gamma, beta, eps: float = 1e-5, offset:
 
 def _ln_bwd_common(dy, dh, v, gamma, mean, rstd, eps, offset, dx, dgamma, dbeta, want_dbeta, workspace):
     torch = _torch()
-    lib = load_library()
     _require(v, "x" if dh is None else "h")
     M, N = _rows(v)
     dev = v.device
@@ -545,28 +584,18 @@ def _ln_bwd_common(dy, dh, v, gamma, mean, rstd, eps, offset, dx, dgamma, dbeta,
     for t, name in ((dgamma, "dgamma"), (dbeta, "dbeta")):
         if t is not None:
             _require(t, name, (N,), v.dtype, dev)
-    with _on_device(dev):
-        if workspace is None:
-            nbytes = layernorm_bwd_workspace_bytes(M, N, _dtype_code(v))
-            for op in (OP_LN_BWD, OP_LN_FUSED_ADD_BWD):  # also large enough for a forced plan
-                for vec_ok in (True, False):
-                    try:
-                        nbytes = max(nbytes, rmsnorm_query_plan(op, M, N, _dtype_code(v), vec_ok)["workspace_bytes"])
-                    except RMSNormError:
-                        pass
-            workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
-        else:
-            _require(workspace, "workspace", device=dev)
-            nbytes = workspace.numel() * workspace.element_size()
-        if dh is None:
-            rc = lib.layernorm_bwd(_ptr(dy), _ptr(v), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
-                                   _ptr(dbeta), _ptr(workspace), nbytes, M, N, eps, offset, _dtype_code(v),
-                                   _stream(dev))
-        else:
-            rc = lib.layernorm_fused_add_bwd(_ptr(dy), _ptr(dh), _ptr(v), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx),
-                                             _ptr(dgamma), _ptr(dbeta), _ptr(workspace), nbytes, M, N, eps, offset,
-                                             _dtype_code(v), _stream(dev))
-        _check(rc, "layernorm_bwd" if dh is None else "layernorm_fused_add_bwd")
+    code = _dtype_code(v)
+    if workspace is None:
+        workspace, nbytes = _bwd_workspace("ln", M, N, code, dev, (OP_LN_BWD, OP_LN_FUSED_ADD_BWD))
+    else:
+        _require(workspace, "workspace", device=dev)
+        nbytes = workspace.numel() * workspace.element_size()
+    if dh is None:
+        _launch(dev, "layernorm_bwd", _ptr(dy), _ptr(v), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
+                _ptr(dbeta), _ptr(workspace), nbytes, M, N, eps, offset, code)
+    else:
+        _launch(dev, "layernorm_fused_add_bwd", _ptr(dy), _ptr(dh), _ptr(v), _ptr(gamma), _ptr(mean), _ptr(rstd),
+                _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(workspace), nbytes, M, N, eps, offset, code)
     return dx, dgamma, dbeta
 
 
