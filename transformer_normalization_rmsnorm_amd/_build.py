@@ -75,6 +75,54 @@ def build(verbose: bool = False, resource_report: bool = True, jobs: int = 4) ->
     return LIBRARY
 
 
+FAMILIES = ("fwd_rows_kernel", "fwd_loop_kernel", "amax_finalize_kernel", "bwd_rows_kernel", "bwd_loop_kernel",
+            "finalize_kernel")
+
+
+def resource_summary(patterns=()) -> str:
+    """Per-kernel resource usage of the last build (``_build/resource_usage.txt``):
+    totals per kernel family, then every kernel whose demangled name contains
+    one of `patterns` (bf16_t shown as bf16)."""
+    path = os.path.join(BUILD, "resource_usage.txt")
+    kernels, cur = [], None
+    for ln in open(path):
+        m = re.search(r"Function Name: (\S+)", ln)
+        if m:
+            cur = {"mangled": m.group(1)}
+            kernels.append(cur)
+            continue
+        m = re.search(r"remark:\s+([A-Za-z /\[\]]+?): (\d+)", ln)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = int(m.group(2))
+    names = subprocess.run(["c++filt"], input="\n".join(k["mangled"] for k in kernels), capture_output=True,
+                           text=True).stdout.splitlines()
+    for k, n in zip(kernels, names):
+        k["name"] = n.replace("rmsnorm::", "").replace("unsigned short", "bf16").replace("(rmsnorm::FwdArgs)", "") \
+                     .replace("(rmsnorm::BwdArgs)", "").replace("(FwdArgs)", "").replace("(BwdArgs)", "")
+    spilled = lambda k: k.get("VGPRs Spill", 0) or k.get("SGPRs Spill", 0) or k.get("ScratchSize [bytes/lane]", 0)
+    out = [f"{'family':22s} {'kernels':>7s} {'max VGPRs':>9s} {'min occupancy':>13s} {'max LDS B':>9s} {'spilling':>8s}"]
+    for fam in FAMILIES:
+        ks = [k for k in kernels if re.search(r"\b" + fam + r"\b", k["name"])]
+        if ks:
+            out.append(f"{fam:22s} {len(ks):7d} {max(k.get('VGPRs', 0) for k in ks):9d} "
+                       f"{min(k.get('Occupancy [waves/SIMD]', 0) for k in ks):13d} "
+                       f"{max(k.get('LDS Size [bytes/block]', 0) for k in ks):9d} {sum(1 for k in ks if spilled(k)):8d}")
+    out.append(f"{'all':22s} {len(kernels):7d} {'':9s} {'':13s} {'':9s} {sum(1 for k in kernels if spilled(k)):8d}")
+    for pat in patterns:
+        out.append("")
+        out.append(f"kernels matching {pat!r}: VGPRs, SGPRs, occupancy (waves/SIMD), static LDS bytes, scratch bytes/lane")
+        for k in kernels:
+            if pat in k["name"]:
+                out.append(f"  {k.get('VGPRs', 0):4d} {k.get('TotalSGPRs', 0):4d} {k.get('Occupancy [waves/SIMD]', 0):3d} "
+                           f"{k.get('LDS Size [bytes/block]', 0):6d} {k.get('ScratchSize [bytes/lane]', 0):4d}  {k['name']}")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) > 1 and sys.argv[1] == "--resources":
+        if not os.path.exists(os.path.join(BUILD, "resource_usage.txt")):
+            build()
+        print(resource_summary(sys.argv[2:]))
+    else:
+        build(verbose=True)
     sys.exit(0)
