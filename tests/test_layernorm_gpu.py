@@ -70,10 +70,12 @@ def test_layernorm_recomputes_statistics(case):
 
 @pytest.mark.parametrize("affine,bias", [(False, False), (True, False), (False, True)])
 def test_layernorm_without_gamma_or_beta(affine, bias):
-    for fused in (False, True):
-        inp = make_inputs(64, 2048, "bf16", fused=fused, layernorm=True)
-        got = gpu_ln(inp, "bf16", EPS, 0.0, fused, affine=affine, bias=bias)
-        check_ln(inp, "bf16", EPS, 0.0, fused, got, affine=affine, bias=bias)
+    # rows in registers, and rows beyond them (looped kernels)
+    for M, N in ((64, 2048), (3, 40960)):
+        for fused in (False, True):
+            inp = make_inputs(M, N, "bf16", fused=fused, layernorm=True)
+            got = gpu_ln(inp, "bf16", EPS, 0.0, fused, affine=affine, bias=bias)
+            check_ln(inp, "bf16", EPS, 0.0, fused, got, affine=affine, bias=bias)
 
 
 # Every LayerNorm backward layout, forced on a shape it tiles, with a small grid.
