@@ -1,0 +1,114 @@
+"""GPU parity over a seeded spread of shapes and options.
+
+Forty-eight cases drawn once from a fixed seed: N log-uniform over [1, 70000]
+(so odd, ragged, narrow, wide and looped rows all occur), M up to 300 with at
+most three million elements, bf16 or fp32, plain or fused residual add,
+gamma + 0 or gamma + 1, eps from {1e-6, 1e-5, 0.1}, and in a quarter of the
+cases every tensor at a storage offset that is not 16-byte aligned.  Each case
+runs the RMSNorm and the LayerNorm forward and backward through the C ABI and
+compares every output with the fp64 reference under the usual rules."""
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_normalization_rmsnorm_amd as rn
+from gpu_util import check_backward, check_forward, check_ln, from_dev, reference_h, to_dev
+from rmsnorm_inputs import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def draw_cases(count=48, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        N = int(np.exp(rng.uniform(0.0, np.log(70000.0))))
+        N = max(1, N)
+        M = int(rng.integers(1, 301))
+        M = max(1, min(M, 3_000_000 // N))
+        dt = "bf16" if rng.random() < 0.6 else "f32"
+        fused = bool(rng.random() < 0.4)
+        gemma = bool(rng.random() < 0.3)
+        eps = float(rng.choice([1e-6, 1e-5, 0.1]))
+        unaligned = bool(rng.random() < 0.25)
+        cases.append((M, N, dt, fused, gemma, eps, unaligned))
+    return cases
+
+
+CASES = draw_cases()
+
+
+def case_id(c):
+    M, N, dt, fused, gemma, eps, unaligned = c
+    return (f"{dt}_{M}x{N}" + ("_fused" if fused else "") + ("_offset1" if gemma else "") + f"_eps{eps:g}"
+            + ("_unaligned" if unaligned else ""))
+
+
+def place(a: np.ndarray, dt: str, unaligned: bool, shift: int = 1) -> torch.Tensor:
+    t = to_dev(a, dt)
+    if not unaligned:
+        return t
+    flat = torch.empty(t.numel() + shift, dtype=t.dtype, device=t.device)
+    v = flat[shift:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def out_like(t: torch.Tensor, unaligned: bool, shift: int = 3) -> torch.Tensor:
+    if not unaligned:
+        return torch.empty_like(t)
+    flat = torch.empty(t.numel() + shift, dtype=t.dtype, device=t.device)
+    return flat[shift:].view(t.shape)
+
+
+@pytest.mark.parametrize("case", CASES, ids=case_id)
+def test_random_shape_parity(case):
+    M, N, dt, fused, gemma, eps, unaligned = case
+    offset = 1.0 if gemma else 0.0
+    print(f"case {case_id(case)}", flush=True)
+
+    # RMSNorm
+    inp = make_inputs(M, N, dt, fused=fused, gemma=gemma, seed=M * 131 + N)
+    x, g = place(inp["x"], dt, unaligned), place(inp["gamma"], dt, unaligned, 5)
+    if fused:
+        r = place(inp["residual"], dt, unaligned)
+        y, h, rstd = rn.rmsnorm_fused_add_fwd(x, r, g, eps, offset, y=out_like(x, unaligned),
+                                              h_out=out_like(x, unaligned, 7))
+    else:
+        y, rstd = rn.rmsnorm_fwd(x, g, eps, offset, y=out_like(x, unaligned))
+        h = None
+    torch.cuda.synchronize()
+    check_forward(inp, dt, eps, offset, from_dev(y), from_dev(rstd), None if h is None else from_dev(h))
+    dy = place(inp["dy"], dt, unaligned)
+    if fused:
+        dh = place(inp["dh"], dt, unaligned)
+        dx, dg = rn.rmsnorm_fused_add_bwd(dy, dh, h, g, rstd, eps, offset, dx=out_like(x, unaligned))
+    else:
+        dx, dg = rn.rmsnorm_bwd(dy, x, g, rstd, eps, offset, dx=out_like(x, unaligned))
+    torch.cuda.synchronize()
+    check_backward(inp, dt, eps, offset, from_dev(dx), from_dev(dg),
+                   v_full=reference_h(inp, dt, eps, offset) if fused else inp["x"],
+                   dh_full=inp["dh"] if fused else None)
+
+    # LayerNorm on a draw with nonzero row means
+    inp = make_inputs(M, N, dt, fused=fused, gemma=gemma, seed=M * 131 + N + 1, layernorm=True)
+    x, g, b = (place(inp[k], dt, unaligned, s) for k, s in (("x", 1), ("gamma", 5), ("beta", 3)))
+    got = {}
+    if fused:
+        r = place(inp["residual"], dt, unaligned)
+        y, h, mean, lrstd = rn.layernorm_fused_add_fwd(x, r, g, b, eps, offset, y=out_like(x, unaligned),
+                                                       h_out=out_like(x, unaligned, 7))
+        got["h"] = h
+    else:
+        y, mean, lrstd = rn.layernorm_fwd(x, g, b, eps, offset, y=out_like(x, unaligned))
+        h = x
+    dy = place(inp["dy"], dt, unaligned)
+    if fused:
+        dh = place(inp["dh"], dt, unaligned)
+        dx, dgl, db = rn.layernorm_fused_add_bwd(dy, dh, h, g, mean, lrstd, eps, offset, dx=out_like(x, unaligned))
+    else:
+        dx, dgl, db = rn.layernorm_bwd(dy, x, g, mean, lrstd, eps, offset, dx=out_like(x, unaligned))
+    torch.cuda.synchronize()
+    got.update(y=y, mean=mean, rstd=lrstd, dx=dx, dg=dgl, db=db)
+    check_ln(inp, dt, eps, offset, fused, {k: from_dev(v) for k, v in got.items()})
