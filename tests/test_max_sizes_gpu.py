@@ -8,7 +8,9 @@
     (built on the device), so each output row equals the reference for its
     source row and dgamma / dbeta equal 65 times the reference over the 1024
     rows.  Rows are compared on a sample that includes the rows on both sides
-    of element 2^31 and the last rows."""
+    of element 2^31 and the last rows.
+  * A statistics-only forward over 8.4 million rows: more workgroups than one
+    launch can hold, so the capped grid strides over the rows."""
 
 import numpy as np
 import pytest
@@ -159,3 +161,38 @@ def test_fp8_beyond_2_31_elements():
     assert abs(float(am.item()) - full["amax64"]) <= 1e-5 * full["amax64"]
     del x, y8
     torch.cuda.empty_cache()
+
+
+def test_statistics_only_forward_beyond_one_launch():
+    """rstd (and LayerNorm's mean) without y for more rows than one launch of
+    one 256-thread workgroup per row can address (2^31 work-items): the grid is
+    capped and the workgroups stride over the rows."""
+    base, reps, N, dt = 4096, 2051, 16, "bf16"
+    M = base * reps  # 8,400,896 rows
+    assert M * 256 > 2 ** 31
+    print(f"statistics-only forward {dt} {M}x{N}", flush=True)
+    lib = rn.load_library()
+    inp = make_inputs(base, N, dt, layernorm=True)
+    x = to_dev(inp["x"], dt).repeat(reps, 1)
+    rows = np.unique(np.concatenate([[0, base - 1, M - 2, M - 1, M // 2],
+                                     np.random.default_rng(3).choice(M, 27, replace=False)])).astype(np.int64)
+    idx = torch.from_numpy(rows).cuda()
+    src = inp["x"][rows % base]
+    stream = torch.cuda.current_stream().cuda_stream
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    assert lib.rmsnorm_fwd(x.data_ptr(), None, None, rstd.data_ptr(), M, N, EPS, 0.0, rn.BF16, stream) == 0
+    mean = torch.empty(M, dtype=torch.float32, device="cuda")
+    lrstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    assert lib.layernorm_fwd(x.data_ptr(), None, None, None, mean.data_ptr(), lrstd.data_ptr(), M, N, LN_EPS, 0.0,
+                             rn.BF16, stream) == 0
+    torch.cuda.synchronize()
+    from tolerance import check_f32
+    _, rstd64 = oracle.fwd(src, None, dt, EPS, 0.0, want_y=False)
+    r = check_f32("rstd", rstd[idx].cpu().numpy(), rstd64)
+    assert r.ok, str(r)
+    _, mean64, lrstd64 = oracle.ln_fwd(src, None, None, dt, LN_EPS, 0.0, want_y=False)
+    r = check_f32("layernorm rstd", lrstd[idx].cpu().numpy(), lrstd64)
+    assert r.ok, str(r)
+    from gpu_util import widen
+    r = check_f32("mean", mean[idx].cpu().numpy(), mean64, scale=np.abs(widen(src, dt)).mean(1))
+    assert r.ok, str(r)

@@ -410,10 +410,11 @@ static hipError_t dispatch_fwd(const rmsnorm_plan &p, FwdArgs a, hipStream_t s)
     a.threads = p.threads;
     a.grid = p.grid;
     if (p.path == RMSNORM_PATH_LOOP || a.y == nullptr) {
-        // statistics-only forwards (y == nullptr) also take the looped kernel
-        const dim3 grid((unsigned)std::min<int64_t>(a.M, 1 << 30)), block(256);
+        // statistics-only forwards (y == nullptr) also take the looped kernel,
+        // one 256-thread workgroup per row, the grid capped below 2^31
+        // work-items (the kernel strides over the rows)
         a.threads = p.path == RMSNORM_PATH_LOOP ? p.threads : 256;
-        a.grid = p.path == RMSNORM_PATH_LOOP ? p.grid : grid.x;
+        a.grid = p.path == RMSNORM_PATH_LOOP ? p.grid : std::min<int64_t>(a.M, (kMaxWorkItems - 1) / 256);
         const dim3 g2((unsigned)a.grid), b2((unsigned)a.threads);
         if (p.vec == VV)
             hipLaunchKernelGGL((fwd_loop_kernel<T, VV, FUSED, F8, LN>), g2, b2, 0, s, a);

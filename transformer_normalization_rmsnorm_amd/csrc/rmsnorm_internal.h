@@ -22,8 +22,8 @@ struct FwdArgs {
     int32_t N;
     float eps;
     float offset;
-    int32_t threads; // workgroup size of the launch
-    int64_t grid;    // workgroups of the launch
+    int32_t threads = 0; // workgroup size of the launch
+    int64_t grid = 0;    // workgroups of the launch
     // fp8 output only: y holds E4M3 codes of y * (*scale); each workgroup
     // writes max |y| to amax_part[blockIdx.x] when amax_part is not null
     const float *scale = nullptr;
@@ -45,8 +45,8 @@ struct BwdArgs {
     int64_t M;
     int32_t N;
     float offset;
-    int32_t threads; // workgroup size of the launch
-    int64_t grid;    // workgroups of the launch
+    int32_t threads = 0; // workgroup size of the launch
+    int64_t grid = 0;    // workgroups of the launch
     // LayerNorm only: the saved row means; the dbeta partials follow the
     // dgamma partials (program p's dbeta row at partials[(grid + p) * ld])
     const float *mean = nullptr;
