@@ -392,6 +392,19 @@ def test_forward_grid_keeps_work_items_below_2_31():
         assert p["grid"] * p["threads"] < 2 ** 31, p
 
 
+def test_backward_rows_in_flight_follow_rows_per_program():
+    """Two rows in flight from 32 rows per program (w in registers), one below;
+    fused-add LayerNorm keeps one."""
+    for op in (rn.OP_BWD, rn.OP_FUSED_ADD_BWD, rn.OP_LN_BWD):
+        assert plan(op, 16384, 8192)["depth"] == 2
+        assert plan(op, 256 * 32, 4096)["depth"] == 2
+        assert plan(op, 256 * 31, 4096)["depth"] == 1
+        assert plan(op, 1024, 8192)["depth"] == 1
+    assert plan(rn.OP_LN_FUSED_ADD_BWD, 16384, 8192)["depth"] == 1
+    assert plan(rn.OP_BWD, 16384, 8192, cus=80)["depth"] == 2
+    assert plan(rn.OP_BWD, 4096, 4096)["depth"] == 1  # 16 rows per program
+
+
 def test_selector_rejects_bad_queries():
     with pytest.raises(rn.RMSNormError):
         plan(10, 4, 4)

@@ -21,6 +21,7 @@ constexpr int kRowsThreads = 256;   // workgroup size when a team is at most one
 constexpr int kLoopThreads = 1024;  // looped path workgroup size
 constexpr int kBwdProgramsPerCU = 1; // persistent backward workgroup teams per compute unit
 constexpr int kBwdTeamsPerCU = 2;    // persistent backward workgroups per compute unit (sub-wave teams)
+constexpr int64_t kDeepRowsPerProgram = 32; // backward rows per program from which two rows are in flight
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -302,6 +303,15 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
         p.path = RMSNORM_PATH_LOOP;
         p.team = 0;
         p.threads = kLoopThreads;
+    } else if (bwd && p.team == 0 && p.w_regs == 1 && !(is_ln_op(op) && is_fused(op))) {
+        // Many rows per program: two rows in flight; with few, one (measured
+        // on MI355X: 16384 x 8192 bf16 RMSNorm 138.3 -> 134.5 us and LayerNorm
+        // 141.4 -> 136.3 us at two; 1024 x 8192, four rows per program, 16.0
+        // against 16.9 us at one).  Fused-add LayerNorm, which also holds dh
+        // and two accumulator sets, was 2.5% slower at two.
+        const int64_t programs = (int64_t)kBwdProgramsPerCU * std::max(num_cus, 1);
+        if (ceil_div(M, programs) >= kDeepRowsPerProgram && bound(op, vec, 0, p.chunks, 2, 1) >= p.threads)
+            p.depth = 2;
     }
     if (!complete_plan(&p, M, N, dtype, num_cus, false))
         return RMSNORM_EUNSUPPORTED;
