@@ -237,9 +237,15 @@ __global__ void __launch_bounds__(fwd_rows_bound_rule(TEAM, K)) fwd_rows_kernel(
         write_amax_part(am, a);
 }
 
-// Any N: pass 1 sums squares (and writes h for fused-add), pass 2 re-reads the
-// row (recomputing h from x and r) and writes y.
-template <typename T, int V, bool FUSED, bool F8, bool LN>
+// Any N: pass 1 sums squares (LayerNorm: the values, then a second pass the
+// squared deviations) and writes h for fused-add; the last pass writes y.
+// Lane t owns the chunks t, t + nt, ...  Its first KS chunks are loaded once,
+// in the first pass, and wait in LDS (each lane reads back only its own, so no
+// barrier) for the later passes; chunks beyond them are read again from
+// memory (from cache), h being formed again from x and r.  The KS chunks are
+// loaded unconditionally, a chunk past the row's end re-reading its last one,
+// so that their loads stay in flight together.
+template <typename T, int V, bool FUSED, bool F8, bool LN, int KS>
 __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
 {
     using C = Chunk<T, V>;
@@ -255,10 +261,13 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
     void *__restrict__ y = a.y;
     const float scale = F8 ? *a.scale : 1.0f;
     float am = 0.0f;
+    extern __shared__ __align__(16) unsigned char fwd_lds[]; // [KS][nt] chunks
+    auto staged = [&](int j) __attribute__((always_inline)) {
+        return reinterpret_cast<C *>(fwd_lds + ((size_t)j * nt + threadIdx.x) * sizeof(C));
+    };
 
-    // chunk c of the row at base: x, or round(x + r) for fused-add (written to
-    // h on the first pass)
-    auto row_chunk = [&](int64_t base, int c, bool write_h) __attribute__((always_inline)) {
+    // chunk c of the row at base: x, or round(x + r) for fused-add
+    auto row_chunk = [&](int64_t base, int c) __attribute__((always_inline)) {
         C v;
         v.load_cached(x + base + (int64_t)c * V);
         if constexpr (FUSED) {
@@ -269,8 +278,6 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
             for (int e = 0; e < V; ++e)
                 f[e] = v.get(e) + rc.get(e);
             v.set(f);
-            if (write_h)
-                v.store(h + base + (int64_t)c * V);
         }
         return v;
     };
@@ -279,29 +286,60 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
     int parity = 0;
     for (int64_t row = blockIdx.x; row < a.M; row += a.grid) {
         const int64_t base = row * N;
-        float mu = 0.0f;
-        if constexpr (LN) { // pass 1: the mean (and h)
-            float s1 = 0.0f;
-            for (int c = threadIdx.x; c < nchunks; c += nt) {
-                const C v = row_chunk(base, c, true);
-#pragma unroll
-                for (int e = 0; e < V; ++e)
-                    s1 += v.get(e);
-            }
-            mu = block_sum(s1, red[parity], a.threads) * inv_n;
-            parity ^= 1;
-        }
-        float ss = 0.0f; // sum of squares (of deviations, LayerNorm)
-        for (int c = threadIdx.x; c < nchunks; c += nt) {
-            const C v = row_chunk(base, c, !LN);
+        // first pass: load (write h), stage, and sum the values (LayerNorm)
+        // or their squares
+        float s1 = 0.0f;
+        auto first = [&](const C &v) __attribute__((always_inline)) {
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const float t = v.get(e) - mu;
-                ss = fmaf(t, t, ss);
+                if constexpr (LN)
+                    s1 += v.get(e);
+                else
+                    s1 = fmaf(v.get(e), v.get(e), s1);
+            }
+        };
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            const int c = (int)threadIdx.x + j * nt;
+            int cc = min(c, nchunks - 1);
+            pin_vgpr(cc);
+            const C v = row_chunk(base, cc);
+            *staged(j) = v;
+            if (c < nchunks) {
+                if constexpr (FUSED)
+                    v.store(h + base + (int64_t)c * V);
+                first(v);
             }
         }
-        ss = block_sum(ss, red[parity], a.threads);
+        for (int c = (int)threadIdx.x + KS * nt; c < nchunks; c += nt) {
+            const C v = row_chunk(base, c);
+            if constexpr (FUSED)
+                v.store(h + base + (int64_t)c * V);
+            first(v);
+        }
+        s1 = block_sum(s1, red[parity], a.threads);
         parity ^= 1;
+        float mu = 0.0f, ss = s1;
+        if constexpr (LN) { // second pass: squared deviations from the mean
+            mu = s1 * inv_n;
+            float s2 = 0.0f;
+            auto dev2 = [&](const C &v) __attribute__((always_inline)) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float t = v.get(e) - mu;
+                    s2 = fmaf(t, t, s2);
+                }
+            };
+#pragma unroll
+            for (int j = 0; j < KS; ++j) {
+                if ((int)threadIdx.x + j * nt < nchunks)
+                    dev2(*staged(j));
+            }
+            for (int c = (int)threadIdx.x + KS * nt; c < nchunks; c += nt)
+                dev2(row_chunk(base, c));
+            ss = block_sum(s2, red[parity], a.threads);
+            parity ^= 1;
+        }
         const float rs = rsqrtf(fmaf(ss, inv_n, a.eps));
         if (threadIdx.x == 0) {
             if (a.rstd != nullptr)
@@ -313,8 +351,7 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
         }
         if (y == nullptr)
             continue;
-        for (int c = threadIdx.x; c < nchunks; c += nt) {
-            const C v = row_chunk(base, c, false);
+        auto out = [&](const C &v, int c) __attribute__((always_inline)) {
             float w[V], bb[V];
             if (gamma != nullptr) {
                 C g;
@@ -347,7 +384,15 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
                     f[e] = (v.get(e) * rs) * w[e];
             }
             store_row_out<T, V, F8>(y, base + (int64_t)c * V, f, scale, am);
+        };
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            const int c = (int)threadIdx.x + j * nt;
+            if (c < nchunks)
+                out(*staged(j), c);
         }
+        for (int c = (int)threadIdx.x + KS * nt; c < nchunks; c += nt)
+            out(row_chunk(base, c), c);
     }
     if constexpr (F8)
         write_amax_part(am, a);
@@ -416,10 +461,26 @@ static hipError_t dispatch_fwd(const rmsnorm_plan &p, FwdArgs a, hipStream_t s)
         a.threads = p.path == RMSNORM_PATH_LOOP ? p.threads : 256;
         a.grid = p.path == RMSNORM_PATH_LOOP ? p.grid : std::min<int64_t>(a.M, (kMaxWorkItems - 1) / 256);
         const dim3 g2((unsigned)a.grid), b2((unsigned)a.threads);
-        if (p.vec == VV)
-            hipLaunchKernelGGL((fwd_loop_kernel<T, VV, FUSED, F8, LN>), g2, b2, 0, s, a);
-        else
-            hipLaunchKernelGGL((fwd_loop_kernel<T, 1, FUSED, F8, LN>), g2, b2, 0, s, a);
+        // 16-byte chunks: up to eight per lane staged in LDS (four when the
+        // row has at most four per lane).  Per-element rows are not staged,
+        // nor the fp8 output: with a third of the bytes to write it kept more
+        // workgroups per CU without the LDS (measured on MI355X, 2048 x 40960
+        // bf16: 62.6 us unstaged against 74.2 us staged; RMSNorm 72.4 -> 68.0
+        // us, LayerNorm 88.3 -> 79.6 us with staging)
+        const int64_t per_lane = ((int64_t)a.N / p.vec + a.threads - 1) / a.threads;
+        const size_t slot = (size_t)a.threads * 16;
+        if (p.vec == VV) {
+            if constexpr (F8) {
+                hipLaunchKernelGGL((fwd_loop_kernel<T, VV, FUSED, F8, LN, 0>), g2, b2, 0, s, a);
+            } else {
+                if (per_lane <= 4)
+                    hipLaunchKernelGGL((fwd_loop_kernel<T, VV, FUSED, F8, LN, 4>), g2, b2, 4 * slot, s, a);
+                else
+                    hipLaunchKernelGGL((fwd_loop_kernel<T, VV, FUSED, F8, LN, 8>), g2, b2, 8 * slot, s, a);
+            }
+        } else {
+            hipLaunchKernelGGL((fwd_loop_kernel<T, 1, FUSED, F8, LN, 0>), g2, b2, 0, s, a);
+        }
         return hipGetLastError();
     }
     const bool vec = (p.vec == VV);
