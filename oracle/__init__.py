@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py``, never by the GPU library or its
 Python binding.  Arrays are numpy; storage dtypes are "f32", "bf16" (raw
-uint16 bit patterns) and "f64".
+uint16 bit patterns), "f16" (numpy float16, IEEE binary16) and "f64".
 """
 
 from __future__ import annotations
@@ -20,8 +20,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "rmsnorm_oracle.c")
 LIBRARY = os.path.join(_HERE, "librmsnorm_oracle.so")
 
-DTYPE_CODE = {"f32": 0, "bf16": 1, "f64": 2}
-NP_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f64": np.float64}
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f64": 2, "f16": 3}
+NP_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f64": np.float64, "f16": np.float16}
 
 _lock = threading.Lock()
 _lib = None

@@ -62,6 +62,10 @@
  *
  * Rounding to a storage type is round-to-nearest, ties to even (FlyDSL PR #855,
  * "512-thread vec8 fast path": software RNE / hardware conversion).
+ * Storage types: float32, bfloat16, float64 and IEEE binary16 (FlyDSL PR #855
+ * "512-thread vec8 fast path": the 128-bit path serves FP16 and BF16, and the
+ * validation coverage there lists FP32, FP16 and BF16; binary16 takes the same
+ * single nearest-even rounding of each output).
  *
  * Parallelism: OpenMP over independent rows (forward, dx) and over independent
  * column ranges (dgamma, each column summed over rows in row order).  No sum is
@@ -84,18 +88,35 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2, ORACLE_F16 = 3 };
 enum { ORACLE_OK = 0, ORACLE_EINVAL = 1, ORACLE_ENOMEM = 2 };
 
-static int dtype_ok(int dt) { return dt == ORACLE_F32 || dt == ORACLE_BF16 || dt == ORACLE_F64; }
+static int dtype_ok(int dt) { return dt == ORACLE_F32 || dt == ORACLE_BF16 || dt == ORACLE_F64 || dt == ORACLE_F16; }
 
-/* Widen one stored element to double (exact for all three storage types). */
+/* Value of an IEEE binary16 bit pattern: 1 sign bit, 5 exponent bits with
+ * bias 15, 10 fraction bits; exponent field 0 holds the subnormals
+ * f * 2^-24, field 31 infinity (f = 0) and NaN. */
+static double f16_value(uint16_t b)
+{
+    const double sign = (b & 0x8000u) ? -1.0 : 1.0;
+    const int field = (b >> 10) & 0x1F;
+    const int frac = b & 0x3FF;
+    if (field == 0x1F)
+        return frac ? NAN : sign * INFINITY;
+    if (field == 0)
+        return sign * ldexp((double)frac, -24);
+    return sign * ldexp((double)(1024 + frac), field - 25);
+}
+
+/* Widen one stored element to double (exact for every storage type). */
 static double load_elem(int dt, const void *base, int64_t i)
 {
     if (dt == ORACLE_F64)
         return ((const double *)base)[i];
     if (dt == ORACLE_F32)
         return (double)((const float *)base)[i];
+    if (dt == ORACLE_F16)
+        return f16_value(((const uint16_t *)base)[i]);
     uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -131,6 +152,39 @@ static uint16_t bf16_bits_from_double(double v)
     return (uint16_t)(b >> 16);
 }
 
+/* Nearest binary16 to v, ties to even, as a bit pattern.
+ * 11 significant bits; at and below 2^-14 the spacing is fixed at 2^-24.  The
+ * largest finite value is 65504 = (2 - 2^-10) * 2^15; a value that rounds on
+ * this grid to 2^16 or beyond becomes infinity (so 65520, the midpoint between
+ * 65504 and 2^16, goes to infinity by the ties-to-even rule). */
+static uint16_t f16_bits_from_double(double v)
+{
+    const uint16_t sign = signbit(v) ? 0x8000u : 0;
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7E00u);
+    const double a = fabs(v);
+    if (isinf(v))
+        return (uint16_t)(sign | 0x7C00u);
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2);
+    int lg = e2 - 1; /* floor(log2 a) */
+    if (lg < -14)
+        lg = -14;
+    const double step = ldexp(1.0, lg - 10);
+    const double rounded = nearbyint(a / step) * step;
+    if (rounded >= 65536.0)
+        return (uint16_t)(sign | 0x7C00u);
+    if (rounded < 0x1p-14) /* subnormal or zero: the fraction counts units of 2^-24 */
+        return (uint16_t)(sign | (uint16_t)(rounded * 0x1p24));
+    int er;
+    frexp(rounded, &er); /* rounding may have carried into the next binade */
+    const int lr = er - 1;
+    const int frac = (int)(ldexp(rounded, 10 - lr)) - 1024;
+    return (uint16_t)(sign | (uint16_t)((lr + 15) << 10) | (uint16_t)frac);
+}
+
 /* Store v rounded (nearest, ties to even) into element i of a storage array. */
 static void store_elem(int dt, void *base, int64_t i, double v)
 {
@@ -138,6 +192,8 @@ static void store_elem(int dt, void *base, int64_t i, double v)
         ((double *)base)[i] = v;
     else if (dt == ORACLE_F32)
         ((float *)base)[i] = (float)v; /* C conversion: nearest, ties to even */
+    else if (dt == ORACLE_F16)
+        ((uint16_t *)base)[i] = f16_bits_from_double(v);
     else
         ((uint16_t *)base)[i] = bf16_bits_from_double(v);
 }

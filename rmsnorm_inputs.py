@@ -11,7 +11,8 @@ Recipe (the same for every workload):
     Gemma-style "gamma + offset" scaling);
   * eps = 1e-6 (the float32 nearest to it);
   * bf16 storage is the float32 draw rounded to nearest, ties to even, kept as
-    raw uint16 bit patterns.
+    raw uint16 bit patterns; f16 (IEEE binary16) storage is numpy's float16
+    cast of the float32 draw (also nearest, ties to even).
 
 The workloads are the pages' shapes: a 512x2048 and a 4096x4096 bf16 layer, wide
 rows (8192) in bf16, a Gemma-style float32 layer (6144 wide), a DeepSeek-like
@@ -29,9 +30,10 @@ import numpy as np
 
 EPS = 1e-6
 
-# storage dtype codes (match the C ABI: 0 = float32, 1 = bfloat16)
+# storage dtype codes (match the C ABI: 0 = float32, 1 = bfloat16, 2 = binary16)
 F32 = "f32"
 BF16 = "bf16"
+F16 = "f16"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -39,7 +41,7 @@ class Workload:
     name: str
     M: int
     N: int
-    dtype: str  # "bf16" or "f32"
+    dtype: str  # "bf16", "f16" or "f32"
     fused: bool = False
     gemma: bool = False  # gamma = 0.1 z with offset 1.0 instead of 1 + 0.1 z
     eps: float = EPS
@@ -50,7 +52,7 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
-        return 2 if self.dtype == BF16 else 4
+        return 4 if self.dtype == F32 else 2
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -102,11 +104,13 @@ def to_storage(a: np.ndarray, dtype: str) -> np.ndarray:
         return f32_to_bf16_bits(a)
     if dtype == F32:
         return np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == F16:
+        return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16)
     raise ValueError(f"unknown storage dtype {dtype!r}")
 
 
 def storage_to_f32(a: np.ndarray, dtype: str) -> np.ndarray:
-    return bf16_bits_to_f32(a) if dtype == BF16 else np.asarray(a, dtype=np.float32)
+    return bf16_bits_to_f32(a) if dtype == BF16 else np.asarray(a).astype(np.float32)
 
 
 def make_inputs(

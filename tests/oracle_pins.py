@@ -14,8 +14,9 @@ mismatch.  What pins what:
   fused_reductions     fused-add with r = 0 / dh = 0 reduces to the plain op
   torch_fp64           torch.nn.functional.rms_norm in float64 with autograd
   golden               hand-worked fixtures (tests/golden/hand_worked.txt)
-  storage_widening     bf16/f32 storage widened exactly (same answers as f64 storage)
+  storage_widening     bf16/f16/f32 storage widened exactly (same answers as f64 storage)
   rounding             nearest-even rounding vs torch casts and brute force
+  binary16             IEEE binary16 storage: exact widening, round trip, numpy casts, brute force
   non_affine           no gamma: finite differences, RMS invariant, gamma = 1 equivalence
   e4m3_brute_force     fp8 E4M3 encoder vs an exhaustive nearest-code search
   e4m3_torch           fp8 E4M3 encoder vs torch's float8_e4m3fn cast; code round trip
@@ -37,6 +38,12 @@ import oracle
 from rmsnorm_inputs import bf16_bits_to_f32, f32_to_bf16_bits
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_worked.txt")
+
+# float32 draws to each storage type, and storage back to float64 (exact)
+_CONV = {"f64": lambda a: a.astype(np.float64), "f32": lambda a: a.astype(np.float32), "bf16": f32_to_bf16_bits,
+         "f16": lambda a: a.astype(np.float16)}
+_WIDEN = {"f64": lambda a: a, "f32": lambda a: a.astype(np.float64),
+          "bf16": lambda a: bf16_bits_to_f32(a).astype(np.float64), "f16": lambda a: a.astype(np.float64)}
 
 
 def _f32(x: float) -> float:
@@ -231,13 +238,13 @@ def offset_equivalence(lib):
 
 def fused_reductions(lib):
     rng = np.random.default_rng(17)
-    for dt in ("f64", "f32", "bf16"):
+    for dt in ("f64", "f32", "bf16", "f16"):
         M, N = 3, 40
         x64 = rng.standard_normal((M, N)).astype(np.float32)
         g64 = (1 + 0.1 * rng.standard_normal(N)).astype(np.float32)
         dy32 = rng.standard_normal((M, N)).astype(np.float32)
         dh32 = rng.standard_normal((M, N)).astype(np.float32)
-        conv = {"f64": lambda a: a.astype(np.float64), "f32": lambda a: a, "bf16": f32_to_bf16_bits}[dt]
+        conv = _CONV[dt]
         x, gamma, dy, dh = conv(x64), conv(g64), conv(dy32), conv(dh32)
         zero = np.zeros_like(x)
         h, yf, rf = oracle.fused_add_fwd(x, zero, gamma, dt, 1e-6, 0.0, lib=lib)
@@ -249,7 +256,7 @@ def fused_reductions(lib):
         oz = oracle.bwd(dy, x, gamma, dt, 1e-6, 0.0, dh=zero, lib=lib)
         np.testing.assert_array_equal(op["dx64"], oz["dx64"])
         od = oracle.bwd(dy, x, gamma, dt, 1e-6, 0.0, dh=dh, lib=lib)
-        dh_wide = {"f64": dh, "f32": dh.astype(np.float64), "bf16": bf16_bits_to_f32(dh).astype(np.float64)}[dt]
+        dh_wide = _WIDEN[dt](dh)
         np.testing.assert_allclose(od["dx64"] - op["dx64"], dh_wide, rtol=1e-12, atol=1e-15)
         np.testing.assert_array_equal(od["dgamma64"], op["dgamma64"])
 
@@ -543,8 +550,10 @@ def load_golden(path: str = GOLDEN):
 def golden(lib):
     cases = load_golden()
     for name, c in cases.items():
-        if name == "bf16_round":
-            got = oracle.round_to(np.array(c["values"]), "bf16", lib=lib)
+        if name in ("bf16_round", "f16_round"):
+            dt = name.split("_")[0]
+            got = oracle.round_to(np.array(c["values"]), dt, lib=lib)
+            got = got.view(np.uint16)
             assert list(map(int, got)) == c["bits"], (name, [hex(int(b)) for b in got])
             continue
         if "codes" in c:  # fp8 output
@@ -600,9 +609,8 @@ def golden(lib):
 def storage_widening(lib):
     rng = np.random.default_rng(19)
     M, N = 3, 50
-    for dt in ("f32", "bf16"):
-        conv = (lambda a: a.astype(np.float32)) if dt == "f32" else f32_to_bf16_bits
-        widen = (lambda a: a.astype(np.float64)) if dt == "f32" else (lambda a: bf16_bits_to_f32(a).astype(np.float64))
+    for dt in ("f32", "bf16", "f16"):
+        conv, widen = _CONV[dt], _WIDEN[dt]
         x = conv(rng.standard_normal((M, N)).astype(np.float32))
         r = conv(rng.standard_normal((M, N)).astype(np.float32))
         gamma = conv((1 + 0.1 * rng.standard_normal(N)).astype(np.float32))
@@ -635,6 +643,20 @@ def _bf16_neighbours(v: float):
     return cands
 
 
+def _f16_neighbours(v: float):
+    """binary16 values around v: the patterns within 2 of the pattern of the
+    float32 image of v, clamped to the finite range."""
+    f = np.float32(min(max(v, -65504.0), 65504.0))
+    b = int(np.array([f], np.float32).astype(np.float16).view(np.uint16)[0])
+    cands = []
+    for d in range(-2, 3):
+        bb = (b + d) & 0xFFFF
+        val = float(np.array([bb], np.uint16).view(np.float16)[0])
+        if np.isfinite(val):
+            cands.append(val)
+    return cands
+
+
 def _brute_round(vals, dt):
     """Nearest representable value, ties to the even significand, by exact rational search."""
     out = []
@@ -644,6 +666,9 @@ def _brute_round(vals, dt):
             cands = [float(np.float32(v)), float(np.nextafter(np.float32(v), np.float32(np.inf))),
                      float(np.nextafter(np.float32(v), np.float32(-np.inf)))]
             bits = lambda c: int(np.array([c], np.float32).view(np.uint32)[0])
+        elif dt == "f16":
+            cands = _f16_neighbours(v)
+            bits = lambda c: int(np.array([c], np.float16).view(np.uint16)[0])
         else:
             cands = _bf16_neighbours(v)
             bits = lambda c: int(f32_to_bf16_bits(np.array([c], np.float32))[0])
@@ -684,6 +709,46 @@ def rounding(lib):
     assert np.isnan(bf16_bits_to_f32(oracle.round_to(np.array([np.nan]), "bf16", lib=lib)))[0]
 
 
+def binary16(lib):
+    """IEEE binary16 storage: every finite pattern widens exactly and rounds
+    back to itself; rounding of float64 values (ties, subnormals, overflow,
+    bits beyond float32) agrees with numpy's float64 -> float16 cast and with
+    an exact nearest-value search."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = pats.view(np.float16)
+    fin = pats[np.isfinite(vals)]  # 63488 patterns, +-0 included
+    wide = fin.view(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(oracle.round_to(wide, "f16", lib=lib).view(np.uint16), fin)
+    # the reference's widening of stored binary16 against numpy's: identical forward results
+    x = fin.view(np.float16).reshape(1024, 62)
+    y_s, r_s = oracle.fwd(x, None, "f16", 1e-6, 0.0, lib=lib)
+    y_d, r_d = oracle.fwd(x.astype(np.float64), None, "f64", 1e-6, 0.0, lib=lib)
+    np.testing.assert_array_equal(y_s, y_d)
+    np.testing.assert_array_equal(np.signbit(y_s), np.signbit(y_d))
+    np.testing.assert_array_equal(r_s, r_d)
+    # float64 values: midpoints of adjacent binary16 values (exact ties), points
+    # just off them, random magnitudes over the whole range, the overflow edge
+    rng = np.random.default_rng(22)
+    pos = np.sort(wide[wide > 0])
+    k = rng.integers(0, pos.size - 1, 3000)
+    mid = (pos[k] + pos[k + 1]) / 2
+    d = np.concatenate([
+        mid, np.nextafter(mid, 0), np.nextafter(mid, np.inf), -mid,
+        rng.standard_normal(4000) * 2.0 ** rng.integers(-28, 17, 4000),
+        np.array([65504.0, 65519.0, 65520.0, 65519.99999999999, 70000.0, 1e300, -65520.0, 2.0 ** -25,
+                  2.0 ** -25 * (1 + 2.0 ** -40), 2.0 ** -26, 2.0 ** -14 - 2.0 ** -25, 1 + 2.0 ** -11 + 2.0 ** -40,
+                  0.0, -0.0, np.inf, -np.inf]),
+    ])
+    with np.errstate(over="ignore"):
+        want = d.astype(np.float16).view(np.uint16)
+    got = oracle.round_to(d, "f16", lib=lib).view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+    sub = np.concatenate([d[:200], d[-16:-2], d[12000:12200]])
+    sub = sub[np.abs(sub) < 65504.0]
+    np.testing.assert_array_equal(oracle.round_to(sub, "f16", lib=lib).astype(np.float64), _brute_round(sub, "f16"))
+    assert np.isnan(oracle.round_to(np.array([np.nan]), "f16", lib=lib)[0])
+
+
 def non_affine(lib):
     """Without gamma: the finite-difference gradient of sum dy * y, the RMS
     invariant with w = 1, and (gamma = 1, offset = 0) giving the same values."""
@@ -721,7 +786,7 @@ def non_affine(lib):
 
 ALL_PINS = [
     finite_differences, rms_invariant, orthogonality, closed_form_n1, constant_row, scale_invariance,
-    offset_equivalence, fused_reductions, torch_fp64, golden, storage_widening, rounding, non_affine,
+    offset_equivalence, fused_reductions, torch_fp64, golden, storage_widening, rounding, binary16, non_affine,
     e4m3_brute_force, e4m3_torch, fp8_forward,
     ln_finite_differences, ln_identities, ln_closed_forms, ln_torch_fp64,
 ]

@@ -33,6 +33,14 @@ MUTATIONS = [
     ("bf16_widen_shift", "uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;",
      "uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 15;", False),
     ("subnormal_spacing", "if (q < -126)\n        q = -126;", "if (q < -149)\n        q = -149;", False),
+    # binary16 storage
+    ("f16_ties_away", "const double rounded = nearbyint(a / step) * step;",
+     "const double rounded = round(a / step) * step;", False),
+    ("f16_subnormal_spacing", "if (lg < -14)\n        lg = -14;", "if (lg < -15)\n        lg = -15;", False),
+    ("f16_overflow_edge", "if (rounded >= 65536.0)", "if (rounded >= 131072.0)", False),
+    ("f16_fraction_offset", "(int)(ldexp(rounded, 10 - lr)) - 1024;", "(int)(ldexp(rounded, 10 - lr)) - 1023;", False),
+    ("f16_widen_bias", "ldexp((double)(1024 + frac), field - 25)", "ldexp((double)(1024 + frac), field - 24)", False),
+    ("f16_widen_subnormal", "return sign * ldexp((double)frac, -24);", "return sign * ldexp((double)frac, -25);", False),
     ("non_affine_scale", "return gamma ? load_elem(dt, gamma, j) + off : 1.0;", "return gamma ? load_elem(dt, gamma, j) + off : 1.0 + off + 0.5;", False),
     # fp8 E4M3 output
     ("e4m3_ties_away", "const double r = nearbyint(a / spacing) * spacing;", "const double r = round(a / spacing) * spacing;", False),
@@ -66,7 +74,8 @@ PIN_ORDER = [
     oracle_pins.golden, oracle_pins.e4m3_brute_force, oracle_pins.e4m3_torch, oracle_pins.fp8_forward,
     oracle_pins.closed_form_n1, oracle_pins.constant_row, oracle_pins.rms_invariant,
     oracle_pins.orthogonality, oracle_pins.offset_equivalence, oracle_pins.scale_invariance,
-    oracle_pins.fused_reductions, oracle_pins.storage_widening, oracle_pins.rounding, oracle_pins.torch_fp64,
+    oracle_pins.fused_reductions, oracle_pins.storage_widening, oracle_pins.rounding, oracle_pins.binary16,
+    oracle_pins.torch_fp64,
     oracle_pins.non_affine, oracle_pins.finite_differences,
     oracle_pins.ln_closed_forms, oracle_pins.ln_identities, oracle_pins.ln_torch_fp64, oracle_pins.ln_finite_differences,
 ]

@@ -18,6 +18,9 @@ def test_rejects_bad_arguments(oracle_lib):
         oracle_lib_call = oracle.fwd(v[:, :0], np.zeros(0), "f64", 1e-6, 0.0, lib=oracle_lib)  # N = 0
     with pytest.raises(TypeError):
         oracle.fwd(v.astype(np.float32), np.zeros(3), "f64", 1e-6, 0.0, lib=oracle_lib)
+    src, dst = np.zeros(4), np.zeros(4, np.uint16)
+    assert oracle_lib.oracle_round(4, src.ctypes.data, 4, dst.ctypes.data) != 0  # unknown storage code
+    assert oracle_lib.oracle_round(3, src.ctypes.data, 4, dst.ctypes.data) == 0  # binary16
 
 
 def test_zero_rows(oracle_lib):
