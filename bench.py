@@ -49,7 +49,7 @@ def source_hash(plan=None) -> str:
     are stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "transformer_normalization_rmsnorm_amd", "csrc")
-    for name in ("device_common.h", "bwd_kernels.hip", "rmsnorm_internal.h"):
+    for name in ("device_common.h", "bwd_kernels.h", "bwd_bf16.hip", "rmsnorm_internal.h"):
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode())
             h.update(fh.read())
@@ -60,7 +60,11 @@ def source_hash(plan=None) -> str:
 
 def bwd_plan(rn, w):
     op = rn.OP_FUSED_ADD_BWD if w.fused else rn.OP_BWD
-    return rn.rmsnorm_query_plan(op, w.M, w.N, rn.BF16 if w.dtype == "bf16" else rn.F32)
+    return rn.rmsnorm_query_plan(op, w.M, w.N, dtype_code(rn, w.dtype))
+
+
+def dtype_code(rn, dtype: str) -> int:
+    return {"bf16": rn.BF16, "f16": rn.F16, "f32": rn.F32}[dtype]
 
 
 class Sets:
@@ -72,7 +76,7 @@ class Sets:
         self.w, self.lib, self.rn, self.torch = w, lib, rn, torch
         dev = torch.device("cuda:0")
         inp = make_workload_inputs(w)
-        td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        td = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
         import numpy as np
 
         def up(a):
@@ -83,7 +87,7 @@ class Sets:
         base = {k: up(v) for k, v in inp.items()}
         del inp
         M, N = w.M, w.N
-        self.dt = rn.BF16 if w.dtype == "bf16" else rn.F32
+        self.dt = dtype_code(rn, w.dtype)
         self.ws_bytes = rn.rmsnorm_bwd_workspace_bytes(M, N, self.dt)
         self.ws8_bytes = rn.rmsnorm_fwd_fp8_workspace_bytes(M, N, self.dt)
         self.ws_ln_bytes = rn.layernorm_bwd_workspace_bytes(M, N, self.dt)

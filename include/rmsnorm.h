@@ -28,7 +28,11 @@
  *     tensors are contiguous and row-major (row stride N); gamma and dgamma
  *     are [N]; rstd is [M] float32.  Any element-aligned address is accepted;
  *     16-byte alignment of every pointer enables the 128-bit access path.
- *   - dtype: RMSNORM_BF16 or RMSNORM_F32 for every T-typed tensor of a call.
+ *   - dtype: RMSNORM_BF16, RMSNORM_F16 or RMSNORM_F32 for every T-typed
+ *     tensor of a call (FlyDSL PR #855, "512-thread vec8 fast path": the
+ *     128-bit path serves FP16 and BF16, and its coverage list tests FP32,
+ *     FP16 and BF16).  Arithmetic is float32 for every dtype; each T-typed
+ *     output is rounded once, to nearest with ties to even.
  *   - Ownership: the caller owns every buffer, including the backward
  *     workspace.  The library allocates no device memory, keeps no per-call
  *     state, never synchronises, and launches only on `stream` (NULL = the
@@ -65,7 +69,8 @@ typedef struct ihipStream_t *rmsnorm_stream_t;
 
 typedef enum rmsnorm_dtype {
     RMSNORM_F32 = 0,
-    RMSNORM_BF16 = 1
+    RMSNORM_BF16 = 1,
+    RMSNORM_F16 = 2 /* IEEE binary16 */
 } rmsnorm_dtype;
 
 typedef enum rmsnorm_status {
@@ -248,8 +253,9 @@ const char *rmsnorm_status_string(int status);
 const char *rmsnorm_last_error(void);
 /* The ABI version this header describes (RMSNORM_ABI_VERSION); a binding
  * checks it before use.  2: rmsnorm_plan gained w_regs.  3: fp8-output
- * forwards (ops 4 and 5).  4: LayerNorm (include/layernorm.h, ops 6-9). */
-#define RMSNORM_ABI_VERSION 4
+ * forwards (ops 4 and 5).  4: LayerNorm (include/layernorm.h, ops 6-9).
+ * 5: binary16 storage (RMSNORM_F16). */
+#define RMSNORM_ABI_VERSION 5
 
 /* Longest row (elements) any entry point accepts. */
 #define RMSNORM_MAX_N (1 << 24)

@@ -9,17 +9,27 @@ import torch
 
 import oracle
 import transformer_normalization_rmsnorm_amd as rn
-from rmsnorm_inputs import BF16, bf16_bits_to_f32
-from tolerance import (DGAMMA_TOL, cancel_scale, check_bf16, check_f32,
-                       dgamma_error)
+from rmsnorm_inputs import BF16, F16, bf16_bits_to_f32
+from tolerance import (DGAMMA_TOL, cancel_scale, check_bf16, check_f16,
+                       check_f32, dgamma_error)
 
 DEV = "cuda:0"
-TORCH_DTYPE = {BF16: torch.bfloat16, "f32": torch.float32}
+TORCH_DTYPE = {BF16: torch.bfloat16, F16: torch.float16, "f32": torch.float32}
+CODE = {BF16: rn.BF16, F16: rn.F16, "f32": rn.F32}  # the C ABI's dtype codes
+
+
+def in_f16(rows):
+    """The bf16 rows of a case list again with binary16 storage (the kernels
+    for the two 16-bit types are the same templates with their own
+    conversions, so every 16-bit layout is run in both)."""
+    return [tuple(F16 if v == BF16 else v for v in r) for r in rows if BF16 in r]
 
 
 def to_dev(a: np.ndarray, dtype: str, device=DEV) -> torch.Tensor:
     if dtype == BF16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    if dtype == F16:
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16)).to(device)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
@@ -27,15 +37,16 @@ def from_dev(t: torch.Tensor) -> np.ndarray:
     t = t.detach().contiguous().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
-    return t.numpy()
+    return t.numpy()  # float32, or float16 as numpy float16
 
 
 def widen(a: np.ndarray, dtype: str) -> np.ndarray:
-    return (bf16_bits_to_f32(a) if dtype == BF16 else np.asarray(a, np.float32)).astype(np.float64)
+    return (bf16_bits_to_f32(a) if dtype == BF16 else np.asarray(a)).astype(np.float64)
 
 
 def check_values(what, got, ref64, dtype, scale=None):
-    r = check_bf16(what, got, ref64, scale=scale) if dtype == BF16 else check_f32(what, got, ref64, scale=scale)
+    check = {BF16: check_bf16, F16: check_f16}.get(dtype, check_f32)
+    r = check(what, got, ref64, scale=scale)
     assert r.ok, str(r)
     return r
 

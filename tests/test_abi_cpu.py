@@ -412,6 +412,18 @@ def test_selector_rejects_bad_queries():
         plan(rn.OP_FWD, 4, 0)
     with pytest.raises(rn.RMSNormError):
         plan(rn.OP_FWD, 4, 4, dt=3)
+    assert plan(rn.OP_FWD, 4, 4, dt=rn.F16)["vec"] == 1
+
+
+@pytest.mark.parametrize("M,N", [(4096, 4096), (1024, 8192), (16384, 7168), (262144, 128), (33, 5000), (7, 4097),
+                                 (4, 40960), (2048, 32768)])
+def test_binary16_plans_are_the_bf16_plans(M, N):
+    """binary16 has bf16's element size, so every op gets the same plan."""
+    ops = [rn.OP_FWD, rn.OP_FUSED_ADD_FWD, rn.OP_BWD, rn.OP_FUSED_ADD_BWD, rn.OP_FWD_FP8, rn.OP_FUSED_ADD_FWD_FP8,
+           rn.OP_LN_FWD, rn.OP_LN_FUSED_ADD_FWD, rn.OP_LN_BWD, rn.OP_LN_FUSED_ADD_BWD]
+    for op in ops:
+        for vec_ok in (True, False):
+            assert plan(op, M, N, rn.F16, vec_ok) == plan(op, M, N, rn.BF16, vec_ok), (op, vec_ok)
 
 
 def test_override_round_trip():

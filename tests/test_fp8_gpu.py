@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import transformer_normalization_rmsnorm_amd as rn
-from gpu_util import from_dev, to_dev
+from gpu_util import from_dev, in_f16, to_dev
 from rmsnorm_inputs import EPS, make_inputs
 from tolerance import check_f32
 
@@ -81,7 +81,7 @@ def case_id(c):
     return f"{dt}_{M}x{N}" + ("_fused" if fused else "") + ("_offset1" if gemma else "") + f"_s{scale:g}"
 
 
-@pytest.mark.parametrize("case", CASES, ids=case_id)
+@pytest.mark.parametrize("case", CASES + in_f16(CASES), ids=case_id)
 def test_fp8_forward_parity(case):
     M, N, dt, fused, gemma, scale = case
     inp = make_inputs(M, N, dt, fused=fused, gemma=gemma)

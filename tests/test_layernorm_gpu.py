@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import transformer_normalization_rmsnorm_amd as rn
-from gpu_util import check_ln, gpu_ln, to_dev
+from gpu_util import CODE, check_ln, gpu_ln, in_f16, to_dev
 from rmsnorm_inputs import make_inputs
 from tolerance import DGAMMA_TOL, dgamma_error
 
@@ -50,7 +50,7 @@ def case_id(c):
     return f"{dt}_{M}x{N}" + ("_fused" if fused else "") + ("_offset1" if gemma else "")
 
 
-@pytest.mark.parametrize("case", CASES, ids=case_id)
+@pytest.mark.parametrize("case", CASES + in_f16(CASES), ids=case_id)
 def test_layernorm_parity(case):
     M, N, dt, fused, gemma = case
     inp = make_inputs(M, N, dt, fused=fused, gemma=gemma, layernorm=True)
@@ -108,8 +108,9 @@ LN_FORCED = [
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["plain", "fused"])
-@pytest.mark.parametrize("fused_ok,M,N,dt,fields", LN_FORCED,
-                         ids=[f"{dt}_{M}x{N}_" + "_".join(f"{a}{b}" for a, b in f.items()) for _, M, N, dt, f in LN_FORCED])
+@pytest.mark.parametrize("fused_ok,M,N,dt,fields", LN_FORCED + in_f16(LN_FORCED),
+                         ids=[f"{dt}_{M}x{N}_" + "_".join(f"{a}{b}" for a, b in f.items())
+                              for _, M, N, dt, f in LN_FORCED + in_f16(LN_FORCED)])
 def test_layernorm_backward_layouts(fused_ok, M, N, dt, fields, fused):
     if fused and not fused_ok:
         pytest.skip("layout not compiled for the fused op")
@@ -117,7 +118,7 @@ def test_layernorm_backward_layouts(fused_ok, M, N, dt, fields, fused):
     inp = make_inputs(M, N, dt, fused=fused, gemma=(dt == "f32"), layernorm=True)
     offset = 1.0 if dt == "f32" else 0.0
     with rn.plan_override(op, **fields):
-        p = rn.rmsnorm_query_plan(op, M, N, rn.BF16 if dt == "bf16" else rn.F32, True)
+        p = rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)
         for k, v in fields.items():
             assert p[k] == v, (k, p)
         check_ln(inp, dt, EPS, offset, fused, gpu_ln(inp, dt, EPS, offset, fused))

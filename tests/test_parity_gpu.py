@@ -11,8 +11,8 @@ import torch
 
 import oracle
 import transformer_normalization_rmsnorm_amd as rn
-from gpu_util import (check_backward, check_forward, from_dev, from_dev_opt,
-                      gpu_backward, gpu_forward, reference_h, to_dev)
+from gpu_util import (CODE, check_backward, check_forward, from_dev, from_dev_opt,
+                      gpu_backward, gpu_forward, in_f16, reference_h, to_dev)
 from rmsnorm_inputs import EPS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -69,7 +69,7 @@ def run_case(M, N, dt, fused, gemma, seed=0):
     return inp, out, dx, dg
 
 
-@pytest.mark.parametrize("case", CASES, ids=case_id)
+@pytest.mark.parametrize("case", CASES + in_f16(CASES), ids=case_id)
 def test_fwd_bwd_parity(case):
     run_case(*case)
 
@@ -137,15 +137,16 @@ FORCED = [
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["plain", "fused"])
-@pytest.mark.parametrize("kind,M,N,dt,fields", FORCED,
-                         ids=[f"{k}_{dt}_{M}x{N}_" + "_".join(f"{a}{b}" for a, b in f.items()) for k, M, N, dt, f in FORCED])
+@pytest.mark.parametrize("kind,M,N,dt,fields", FORCED + in_f16(FORCED),
+                         ids=[f"{k}_{dt}_{M}x{N}_" + "_".join(f"{a}{b}" for a, b in f.items())
+                              for k, M, N, dt, f in FORCED + in_f16(FORCED)])
 def test_forced_layouts(kind, M, N, dt, fields, fused):
     if kind == "fwd":
         op = rn.OP_FUSED_ADD_FWD if fused else rn.OP_FWD
     else:
         op = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
     with rn.plan_override(op, **fields):
-        p = rn.rmsnorm_query_plan(op, M, N, rn.BF16 if dt == "bf16" else rn.F32, True)
+        p = rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)
         for k, v in fields.items():
             assert p[k] == v, (k, p)
         run_case(M, N, dt, fused, dt == "f32")
@@ -177,14 +178,15 @@ WIDE_FORCED = [
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["plain", "fused"])
-@pytest.mark.parametrize("fused_ok,M,N,dt,fields", WIDE_FORCED,
-                         ids=[f"{dt}_{M}x{N}_t{f['threads']}_d{f['depth']}_w{f['w_regs']}" for _, M, N, dt, f in WIDE_FORCED])
+@pytest.mark.parametrize("fused_ok,M,N,dt,fields", WIDE_FORCED + in_f16(WIDE_FORCED),
+                         ids=[f"{dt}_{M}x{N}_t{f['threads']}_d{f['depth']}_w{f['w_regs']}"
+                              for _, M, N, dt, f in WIDE_FORCED + in_f16(WIDE_FORCED)])
 def test_wide_backward_layouts(fused_ok, M, N, dt, fields, fused):
     if fused and not fused_ok:
         pytest.skip("layout not compiled for the fused op at this workgroup size")
     op = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
     with rn.plan_override(op, **fields):
-        p = rn.rmsnorm_query_plan(op, M, N, rn.BF16 if dt == "bf16" else rn.F32, True)
+        p = rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)
         for k, v in fields.items():
             assert p[k] == v, (k, p)
         run_case(M, N, dt, fused, dt == "f32")
@@ -197,7 +199,8 @@ NON_AFFINE = [(300, 4096, "bf16", False), (200, 7168, "bf16", True), (130, 6144,
               (7, 16384, "bf16", False), (5, 32768, "bf16", True), (6, 12000, "f32", False)]
 
 
-@pytest.mark.parametrize("M,N,dt,fused", NON_AFFINE, ids=[f"{d}_{m}x{n}{'_fused' if f else ''}" for m, n, d, f in NON_AFFINE])
+@pytest.mark.parametrize("M,N,dt,fused", NON_AFFINE + in_f16(NON_AFFINE[:2]),
+                         ids=[f"{d}_{m}x{n}{'_fused' if f else ''}" for m, n, d, f in NON_AFFINE + in_f16(NON_AFFINE[:2])])
 def test_non_affine(M, N, dt, fused):
     inp = make_inputs(M, N, dt, fused=fused)
     inp["gamma"] = None
@@ -220,7 +223,7 @@ def _offset_view(a: torch.Tensor, elems: int) -> torch.Tensor:
     return v
 
 
-@pytest.mark.parametrize("M,N,dt", [(100, 4096, "bf16"), (50, 6144, "f32"), (300, 128, "bf16")])
+@pytest.mark.parametrize("M,N,dt", [(100, 4096, "bf16"), (50, 6144, "f32"), (300, 128, "bf16"), (100, 4096, "f16")])
 def test_unaligned_storage_offsets(M, N, dt):
     for fused in (False, True):
         inp = make_inputs(M, N, dt, fused=fused)

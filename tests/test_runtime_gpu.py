@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import transformer_normalization_rmsnorm_amd as rn
-from gpu_util import (check_backward, check_forward, from_dev, gpu_forward,
+from gpu_util import (CODE, check_backward, check_forward, from_dev, gpu_forward,
                       reference_h, to_dev)
 from rmsnorm_inputs import EPS, make_inputs
 
@@ -105,7 +105,7 @@ def test_poisoned_outputs_and_workspace_are_overwritten(M, N, dt):
     y, h = torch.full_like(x, nan), torch.full_like(x, nan)
     rstd = torch.full((M,), nan, device="cuda")
     rn.rmsnorm_fused_add_fwd(x, r, g, EPS, 0.0, y=y, h_out=h, rstd=rstd)
-    ws, nbytes = rn.alloc_workspace(M, N, rn.BF16 if dt == "bf16" else rn.F32, x.device)
+    ws, nbytes = rn.alloc_workspace(M, N, CODE[dt], x.device)
     ws.view(torch.uint8).fill_(0xFF)  # all-ones bytes are NaNs as float32
     dx, dg = torch.full_like(x, nan), torch.full_like(g, nan)
     rn.rmsnorm_fused_add_bwd(dy, dh, h, g, rstd, EPS, 0.0, dx=dx, dgamma=dg, workspace=ws)

@@ -4,8 +4,8 @@ import numpy as np
 
 import oracle
 from rmsnorm_inputs import bf16_bits_to_f32
-from tolerance import (DGAMMA_TOL, check_bf16, check_f32, dgamma_error, rel_l2,
-                       ulp_bf16)
+from tolerance import (DGAMMA_TOL, check_bf16, check_f16, check_f32, dgamma_error,
+                       rel_l2, ulp_bf16, ulp_f16)
 
 
 def test_ulp_bf16_values():
@@ -65,3 +65,40 @@ def test_dgamma_rules():
     assert dgamma_error((ref * (1 + 2e-5)).astype(np.float32), ref, "f32") > DGAMMA_TOL["f32"]
     # the unrounded fp64 reference would be the wrong target for bf16 (final rounding alone ~1e-3)
     assert rel_l2(bf16_bits_to_f32(good), ref) > 1e-3
+
+
+def test_ulp_f16_values():
+    assert ulp_f16(1.0) == 2.0 ** -10
+    assert ulp_f16(1.99) == 2.0 ** -10
+    assert ulp_f16(65504.0) == 32.0
+    assert ulp_f16(-0.75) == 2.0 ** -11
+    assert ulp_f16(2.0 ** -20) == 2.0 ** -24
+    assert ulp_f16(0.0) == 2.0 ** -24
+
+
+def test_f16_rule():
+    rng = np.random.default_rng(3)
+    ref = rng.standard_normal(5000) + 3.0
+    got = oracle.round_to(ref, "f16")
+    assert check_f16("exact", got, ref).ok
+    pats = got.view(np.uint16).copy()
+    assert check_f16("1ulp", (pats + 1).view(np.float16), ref).ok
+    pats[77] += 3
+    r = check_f16("planted", pats.view(np.float16), ref)
+    assert not r.ok and r.fails == 1 and r.worst_index == 77
+    # the cancellation floor: a 30% error on a value cancelled 1e6-fold passes with scale 1 only
+    ref2 = np.array([1e-6, 1.0])
+    bad = oracle.round_to(ref2 + np.array([3e-7, 0.0]), "f16")
+    assert not check_f16("nofloor", bad, ref2).ok
+    assert check_f16("floor", bad, ref2, scale=np.ones(2)).ok
+    worse = oracle.round_to(ref2 + np.array([2e-6, 0.0]), "f16")
+    assert not check_f16("floor2", worse, ref2, scale=np.ones(2)).ok
+
+
+def test_f16_dgamma_rule():
+    rng = np.random.default_rng(4)
+    ref = rng.standard_normal(1) * 3  # a single column: one ulp off must still pass
+    one = oracle.round_to(ref, "f16")
+    up = (one.view(np.uint16) + 1).view(np.float16)
+    assert dgamma_error(up, ref, "f16") <= DGAMMA_TOL["f16"]
+    assert dgamma_error((one.view(np.uint16) + 3).view(np.float16), ref, "f16") > DGAMMA_TOL["f16"]

@@ -15,6 +15,16 @@ rounded to bf16 and bf16 dgamma relative L2 <= 1e-3), with these readings:
   * bf16 dgamma is compared with the fp64 dgamma rounded once to bf16; fp32
     dgamma with the fp64 dgamma itself.
   * Fused-add h = round(x + r) must be bit-exact.
+
+binary16 (f16) storage, for which no tolerance is stated, takes the bf16 rule
+with its own spacing: within 2 f16 ulp of the fp64 result rounded to f16, with
+ulp_f16(a) = 2^(floor(log2|a|) - 10) and the fixed subnormal spacing 2^-24
+below 2^-14.  The cancellation floor is 2^-11 s, which gives the same absolute
+allowance as bf16's (2 ulp_f16(2^-11 s) = 2 ulp_bf16(2^-14 s) = 2^-20 s): the
+float32 error of the difference does not depend on the storage type.  dgamma
+keeps the 16-bit bound, relative L2 <= 1e-3 against the fp64 dgamma rounded to
+f16; one element one f16 ulp off (relative 2^-10 at most) stays within it
+even for a one-column dgamma.
 """
 
 from __future__ import annotations
@@ -27,6 +37,7 @@ import oracle
 from rmsnorm_inputs import bf16_bits_to_f32
 
 BF16_FLOOR = 2.0 ** -14
+F16_FLOOR = 2.0 ** -11
 
 
 def ulp_bf16(a) -> np.ndarray:
@@ -35,6 +46,14 @@ def ulp_bf16(a) -> np.ndarray:
     q = np.maximum(e - 1, -126)
     u = np.ldexp(1.0, q - 7)
     return np.where(a == 0, 2.0 ** -133, u)
+
+
+def ulp_f16(a) -> np.ndarray:
+    a = np.abs(np.asarray(a, dtype=np.float64))
+    _, e = np.frexp(a)
+    q = np.maximum(e - 1, -14)
+    u = np.ldexp(1.0, q - 10)
+    return np.where(a == 0, 2.0 ** -24, u)
 
 
 @dataclasses.dataclass
@@ -81,6 +100,25 @@ def check_bf16(what, got_bits, ref64, *, scale=None, ulps=2.0) -> Report:
     return _report(what, err, ulps * ulp_bf16(mag), ulps * ulp_bf16(np.abs(ref64)), floor_mask)
 
 
+def check_f16(what, got, ref64, *, scale=None, ulps=2.0) -> Report:
+    """got (numpy float16) within `ulps` f16 ulp of round_f16(ref64)."""
+    ref64 = np.asarray(ref64, dtype=np.float64).ravel()
+    got = np.asarray(got).ravel()
+    assert got.dtype == np.float16, got.dtype
+    got = got.astype(np.float64)
+    ref_r = oracle.round_to(ref64, "f16").astype(np.float64)
+    mag = np.abs(ref64)
+    if scale is not None:
+        floor = F16_FLOOR * np.asarray(scale, dtype=np.float64).ravel()
+        floor_mask = floor > mag
+        mag = np.maximum(mag, floor)
+    else:
+        floor_mask = np.zeros(mag.shape, bool)
+    with np.errstate(invalid="ignore"):  # an infinity equal to the rounded reference is exact
+        err = np.where(got == ref_r, 0.0, np.abs(got - ref_r))
+    return _report(what, err, ulps * ulp_f16(mag), ulps * ulp_f16(np.abs(ref64)), floor_mask)
+
+
 def check_f32(what, got, ref64, *, scale=None, rel=1e-5) -> Report:
     """|got - ref64| <= rel * max(|ref64|, scale)."""
     ref64 = np.asarray(ref64, dtype=np.float64).ravel()
@@ -107,7 +145,11 @@ def rel_l2(got, ref) -> float:
 
 
 def dgamma_error(got_storage, ref64, dtype: str) -> float:
-    """Relative L2 of dgamma: bf16 against round_bf16(ref64), fp32 against ref64."""
+    """Relative L2 of dgamma: bf16 / f16 against ref64 rounded to that type, fp32 against ref64."""
+    if dtype == "f16":
+        got = np.asarray(got_storage)
+        assert got.dtype == np.float16, got.dtype
+        return rel_l2(got.astype(np.float64), oracle.round_to(ref64, "f16").astype(np.float64))
     if dtype == "bf16":
         got = bf16_bits_to_f32(np.asarray(got_storage)).astype(np.float64)
         ref = bf16_bits_to_f32(oracle.round_to(ref64, "bf16")).astype(np.float64)
@@ -115,7 +157,7 @@ def dgamma_error(got_storage, ref64, dtype: str) -> float:
     return rel_l2(np.asarray(got_storage, dtype=np.float64), ref64)
 
 
-DGAMMA_TOL = {"bf16": 1e-3, "f32": 1e-5}
+DGAMMA_TOL = {"bf16": 1e-3, "f16": 1e-3, "f32": 1e-5}
 
 
 def cancel_scale(v_wide, gamma_wide, dy_wide, rstd64, c64, sabs64, offset, dh_wide=None):

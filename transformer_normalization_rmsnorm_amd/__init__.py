@@ -32,7 +32,7 @@ from typing import Optional
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(PKG_DIR, "librmsnorm_amd.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 OP_FWD, OP_FUSED_ADD_FWD, OP_BWD, OP_FUSED_ADD_BWD, OP_FWD_FP8, OP_FUSED_ADD_FWD_FP8 = 0, 1, 2, 3, 4, 5
 OP_LN_FWD, OP_LN_FUSED_ADD_FWD, OP_LN_BWD, OP_LN_FUSED_ADD_BWD = 6, 7, 8, 9
 PATH_ROWS, PATH_LOOP = 0, 1
@@ -57,7 +57,7 @@ class RMSNormError(RuntimeError):
 
 
 # RMSNORM_ABI_VERSION of include/rmsnorm.h that this binding marshals.
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class Plan(ctypes.Structure):
@@ -157,7 +157,9 @@ def _dtype_code(t) -> int:
         return BF16
     if t.dtype == torch.float32:
         return F32
-    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+    if t.dtype == torch.float16:
+        return F16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16, float16 or float32")
 
 
 def _ptr(t) -> Optional[int]:

@@ -19,7 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "librmsnorm_amd.so")
-SOURCES = ["api.cpp", "selector.cpp", "fwd_kernels.hip", "bwd_kernels.hip"]
+# kernel instances per storage type in units of their own, compiled in parallel
+SOURCES = ["bwd_bf16.hip", "bwd_f32.hip", "bwd_f16.hip", "fwd_bf16.hip", "fwd_f32.hip", "fwd_f16.hip", "launch.hip",
+           "api.cpp", "selector.cpp"]
 # measurement-only library (practical bandwidth ceilings for the benchmark)
 PROBE_SOURCE = "stream_probe.hip"
 PROBE_LIBRARY = os.path.join(PKG, "libstream_probe.so")
@@ -46,7 +48,7 @@ def _compile(src: str, resource_report: bool) -> tuple:
     return obj, r.stderr
 
 
-def build(verbose: bool = False, resource_report: bool = True, jobs: int = 4) -> str:
+def build(verbose: bool = False, resource_report: bool = True, jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(lambda s: _compile(s, resource_report), SOURCES))
@@ -97,7 +99,7 @@ def resource_summary(patterns=()) -> str:
     names = subprocess.run(["c++filt"], input="\n".join(k["mangled"] for k in kernels), capture_output=True,
                            text=True).stdout.splitlines()
     for k, n in zip(kernels, names):
-        k["name"] = n.replace("rmsnorm::", "").replace("unsigned short", "bf16").replace("(rmsnorm::FwdArgs)", "") \
+        k["name"] = n.replace("rmsnorm::", "").replace("unsigned short", "bf16").replace("f16_t", "f16").replace("(rmsnorm::FwdArgs)", "") \
                      .replace("(rmsnorm::BwdArgs)", "").replace("(FwdArgs)", "").replace("(BwdArgs)", "")
     spilled = lambda k: k.get("VGPRs Spill", 0) or k.get("SGPRs Spill", 0) or k.get("ScratchSize [bytes/lane]", 0)
     out = [f"{'family':22s} {'kernels':>7s} {'max VGPRs':>9s} {'min occupancy':>13s} {'max LDS B':>9s} {'spilling':>8s}"]

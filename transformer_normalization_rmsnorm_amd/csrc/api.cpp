@@ -70,8 +70,8 @@ bool aligned(const void *p, size_t a) { return p == nullptr || (reinterpret_cast
 
 int check_common(int64_t M, int64_t N, int dtype, float eps, float offset)
 {
-    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_F32)
-        return fail(RMSNORM_EUNSUPPORTED, "dtype %d not supported (0 = f32, 1 = bf16)", dtype);
+    if (!dtype_known(dtype))
+        return fail(RMSNORM_EUNSUPPORTED, "dtype %d not supported (0 = f32, 1 = bf16, 2 = f16)", dtype);
     if (M < 0)
         return fail(RMSNORM_EINVAL, "M = %lld < 0", (long long)M);
     if (N <= 0 || N > kMaxN)
@@ -291,7 +291,7 @@ int do_partials(const void *dy, const void *v, const void *gamma, const float *r
 
 int do_finalize(const float *partials, int64_t programs, int64_t N, void *dgamma, int dtype, hipStream_t stream)
 {
-    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_F32)
+    if (!dtype_known(dtype))
         return fail(RMSNORM_EUNSUPPORTED, "dtype %d not supported", dtype);
     if (N <= 0 || N > kMaxN || programs < 0)
         return fail(RMSNORM_EINVAL, "bad N or programs");
@@ -311,7 +311,7 @@ int do_ln_bwd(const void *dy, const void *dh, const void *v, const void *gamma, 
 {
     if (!gamma && dgamma)
         return fail(RMSNORM_EINVAL, "dgamma given without gamma");
-    if (dtype == RMSNORM_BF16 || dtype == RMSNORM_F32) {
+    if (dtype_known(dtype)) {
         const size_t eb = (size_t)elem_bytes(dtype);
         if (!aligned(dgamma, eb) || !aligned(dbeta, eb))
             return fail(RMSNORM_EINVAL, "dgamma or dbeta not aligned to its element size");
@@ -342,7 +342,7 @@ int do_bwd(const void *dy, const void *dh, const void *v, const void *gamma, con
     }
     if (!dgamma)
         return fail(RMSNORM_EINVAL, "dgamma is null");
-    if (!aligned(dgamma, (size_t)elem_bytes(dtype == RMSNORM_BF16 ? RMSNORM_BF16 : RMSNORM_F32)))
+    if (dtype_known(dtype) && !aligned(dgamma, (size_t)elem_bytes(dtype)))
         return fail(RMSNORM_EINVAL, "dgamma not aligned to its element size");
     int64_t programs = 0;
     int rc = do_partials(dy, v, gamma, rstd, dh, dx, workspace, workspace_bytes, &programs, M, N, eps, offset,

@@ -31,6 +31,8 @@
 // dx = rstd * (g - mean(g) - xhat * mean(g * xhat)) [+ dh]; each program keeps
 // two accumulator sets, dgamma (dy * xhat) and dbeta (dy), and writes two
 // partial rows, which the finalizer folds with a second row of workgroups.
+#pragma once
+
 #include "device_common.h"
 #include "rmsnorm_internal.h"
 
@@ -601,10 +603,7 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(const float *__re
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             if (col + e < N) {
-                if constexpr (sizeof(T) == 2)
-                    dg[col + e] = to_bf16(f[e]);
-                else
-                    dg[col + e] = f[e];
+                dg[col + e] = to_storage<T>(f[e]);
             }
         }
     }
@@ -698,29 +697,24 @@ static hipError_t dispatch_bwd(const rmsnorm_plan &p, BwdArgs a, hipStream_t s)
     return hipErrorInvalidConfiguration;
 }
 
-hipError_t launch_bwd(int dtype, bool fused, bool ln, const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s)
+// Backward and finalizer launches for storage type T; explicitly instantiated
+// once per type in bwd_<type>.hip.
+template <typename T>
+hipError_t launch_bwd_typed(bool fused, bool ln, const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s)
 {
-    if (dtype == RMSNORM_BF16) {
-        if (ln)
-            return fused ? dispatch_bwd<bf16_t, true, true>(p, a, s) : dispatch_bwd<bf16_t, false, true>(p, a, s);
-        return fused ? dispatch_bwd<bf16_t, true, false>(p, a, s) : dispatch_bwd<bf16_t, false, false>(p, a, s);
-    }
     if (ln)
-        return fused ? dispatch_bwd<float, true, true>(p, a, s) : dispatch_bwd<float, false, true>(p, a, s);
-    return fused ? dispatch_bwd<float, true, false>(p, a, s) : dispatch_bwd<float, false, false>(p, a, s);
+        return fused ? dispatch_bwd<T, true, true>(p, a, s) : dispatch_bwd<T, false, true>(p, a, s);
+    return fused ? dispatch_bwd<T, true, false>(p, a, s) : dispatch_bwd<T, false, false>(p, a, s);
 }
 
-hipError_t launch_finalize(int dtype, const float *partials, int64_t programs, int64_t ld, int64_t N,
-                           void *dgamma, void *dbeta, hipStream_t s)
+template <typename T>
+hipError_t launch_finalize_typed(const float *partials, int64_t programs, int64_t ld, int64_t N, void *dgamma,
+                                 void *dbeta, hipStream_t s)
 {
     const dim3 grid((unsigned)((ld + kFinColsPerBlock - 1) / kFinColsPerBlock), dbeta ? 2u : 1u),
         block(kFinThreads);
-    if (dtype == RMSNORM_BF16)
-        hipLaunchKernelGGL((finalize_kernel<bf16_t>), grid, block, 0, s, partials, programs, ld, N,
-                           static_cast<bf16_t *>(dgamma), static_cast<bf16_t *>(dbeta));
-    else
-        hipLaunchKernelGGL((finalize_kernel<float>), grid, block, 0, s, partials, programs, ld, N,
-                           static_cast<float *>(dgamma), static_cast<float *>(dbeta));
+    hipLaunchKernelGGL((finalize_kernel<T>), grid, block, 0, s, partials, programs, ld, N, static_cast<T *>(dgamma),
+                       static_cast<T *>(dbeta));
     return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 // Device helpers for the gfx950 RMSNorm kernels: vector chunks of a row,
-// bf16 <-> f32 conversion, and wavefront / workgroup sum reductions.
+// bf16 / binary16 <-> f32 conversion, and wavefront / workgroup sum reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,6 +31,53 @@ __device__ __forceinline__ uint16_t to_bf16(float f)
     return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
+// IEEE binary16 is carried as its raw 16-bit pattern too, in a type of its own
+// so that the kernel templates tell it apart from bf16.
+struct alignas(2) f16_t {
+    uint16_t bits;
+};
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// binary16 -> f32 is exact (v_cvt_f32_f16); f32 -> binary16 rounds to nearest
+// even, with subnormal results and overflow to infinity, as the IEEE
+// conversion does.  Element 0 is in the low half.
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w).x; }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w).y; }
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
+{
+    f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+// The two 16-bit storage types: two values per 32-bit word.
+template <typename T>
+struct Pair16;
+
+template <>
+struct Pair16<bf16_t> {
+    static __device__ __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
+};
+
+template <>
+struct Pair16<f16_t> {
+    static __device__ __forceinline__ float lo(uint32_t w) { return f16_lo(w); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return f16_hi(w); }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_f16x2(a, b); }
+};
+
+// One f32 value rounded to the storage type T.
+template <typename T>
+__device__ __forceinline__ T to_storage(float f)
+{
+    if constexpr (sizeof(T) == 4)
+        return f;
+    else
+        return __builtin_bit_cast(T, (uint16_t)(Pair16<T>::pack(f, 0.0f) & 0xffffu));
+}
+
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -48,7 +95,7 @@ __device__ __forceinline__ void pin_vgpr(U &x)
 }
 
 // A chunk is the V consecutive elements of a row that one lane moves with one
-// memory instruction: 16 bytes (bf16 x8, f32 x4) on the vector path, one
+// memory instruction: 16 bytes (bf16 or binary16 x8, f32 x4) on the vector path, one
 // element on the scalar path.  load/store stream the row tensors with the
 // nontemporal hint (each element is touched once per call; measured on
 // MI355X: about 10% more bandwidth for three-stream traffic); load_cached is
@@ -57,30 +104,34 @@ __device__ __forceinline__ void pin_vgpr(U &x)
 template <typename T, int V>
 struct Chunk;
 
-template <>
-struct Chunk<bf16_t, 8> {
+// 8 elements of a 16-bit type (bf16 or binary16) in four packed words.
+template <typename T>
+struct Chunk16x8 {
     uint32_t w[4];
-    __device__ __forceinline__ void load(const bf16_t *p)
+    __device__ __forceinline__ void load(const T *p)
     {
         const u32x4_t u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
         w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
     }
-    __device__ __forceinline__ void load_cached(const bf16_t *p)
+    __device__ __forceinline__ void load_cached(const T *p)
     {
         const uint4 u = *reinterpret_cast<const uint4 *>(p);
         w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
     }
-    __device__ __forceinline__ void store(bf16_t *p) const
+    __device__ __forceinline__ void store(T *p) const
     {
         const u32x4_t u = {w[0], w[1], w[2], w[3]};
         __builtin_nontemporal_store(u, reinterpret_cast<u32x4_t *>(p));
     }
-    __device__ __forceinline__ float get(int e) const { return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]); }
+    __device__ __forceinline__ float get(int e) const
+    {
+        return (e & 1) ? Pair16<T>::hi(w[e >> 1]) : Pair16<T>::lo(w[e >> 1]);
+    }
     __device__ __forceinline__ void set(const float (&f)[8])
     {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+            w[i] = Pair16<T>::pack(f[2 * i], f[2 * i + 1]);
     }
     __device__ __forceinline__ void zero()
     {
@@ -96,14 +147,21 @@ struct Chunk<bf16_t, 8> {
     }
 };
 
-template <>
-struct Chunk<bf16_t, 1> {
+// One element of a 16-bit type.
+template <typename T>
+struct Chunk16x1 {
     uint16_t b;
-    __device__ __forceinline__ void load(const bf16_t *p) { b = __builtin_nontemporal_load(p); }
-    __device__ __forceinline__ void load_cached(const bf16_t *p) { b = *p; }
-    __device__ __forceinline__ void store(bf16_t *p) const { __builtin_nontemporal_store(b, p); }
-    __device__ __forceinline__ float get(int) const { return __uint_as_float((uint32_t)b << 16); }
-    __device__ __forceinline__ void set(const float (&f)[1]) { b = to_bf16(f[0]); }
+    __device__ __forceinline__ void load(const T *p)
+    {
+        b = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
+    }
+    __device__ __forceinline__ void load_cached(const T *p) { b = *reinterpret_cast<const uint16_t *>(p); }
+    __device__ __forceinline__ void store(T *p) const
+    {
+        __builtin_nontemporal_store(b, reinterpret_cast<uint16_t *>(p));
+    }
+    __device__ __forceinline__ float get(int) const { return Pair16<T>::lo((uint32_t)b); }
+    __device__ __forceinline__ void set(const float (&f)[1]) { b = (uint16_t)(Pair16<T>::pack(f[0], 0.0f) & 0xffffu); }
     __device__ __forceinline__ void zero() { b = 0; }
     __device__ __forceinline__ void pin()
     {
@@ -112,6 +170,15 @@ struct Chunk<bf16_t, 1> {
         b = (uint16_t)t;
     }
 };
+
+template <>
+struct Chunk<bf16_t, 8> : Chunk16x8<bf16_t> {};
+template <>
+struct Chunk<f16_t, 8> : Chunk16x8<f16_t> {};
+template <>
+struct Chunk<bf16_t, 1> : Chunk16x1<bf16_t> {};
+template <>
+struct Chunk<f16_t, 1> : Chunk16x1<f16_t> {};
 
 template <>
 struct Chunk<float, 4> {

@@ -26,6 +26,8 @@
 // first and then the sum of squared deviations of the register-held row
 // (two-pass, so no cancellation between E[v^2] and E[v]^2), then
 // y = (v - mean) * rstd * (gamma + offset) + beta.
+#pragma once
+
 #include <algorithm>
 
 #include "device_common.h"
@@ -398,42 +400,6 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
         write_amax_part(am, a);
 }
 
-// *amax = max(*amax, max_p part[p]), one workgroup.  The partials are read as
-// float4 with kAmaxLoads independent loads per lane in flight, so a round
-// covers kAmaxThreads * kAmaxLoads * 4 partials for one memory latency (a
-// dependent loop of scalar loads cost one latency per 256 partials: about 20
-// us at 16384 workgroups).  Every load is issued: lanes past the end re-read
-// the last group and their values are ignored.
-constexpr int kAmaxLoads = 4;
-
-__global__ void __launch_bounds__(kAmaxThreads) amax_finalize_kernel(const float *__restrict__ part, int64_t P,
-                                                                     float *amax)
-{
-    __shared__ float slot[16];
-    float m = 0.0f;
-    const int64_t P4 = P / 4;
-    const float4 *__restrict__ p4 = reinterpret_cast<const float4 *>(part);
-    for (int64_t b = 0; b < P4; b += (int64_t)kAmaxThreads * kAmaxLoads) {
-        float4 v[kAmaxLoads];
-#pragma unroll
-        for (int u = 0; u < kAmaxLoads; ++u) {
-            const int64_t i = b + (int64_t)u * kAmaxThreads + threadIdx.x;
-            v[u] = p4[i < P4 ? i : P4 - 1];
-        }
-#pragma unroll
-        for (int u = 0; u < kAmaxLoads; ++u) {
-            const int64_t i = b + (int64_t)u * kAmaxThreads + threadIdx.x;
-            if (i < P4)
-                m = fmaxf(m, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
-        }
-    }
-    for (int64_t i = P4 * 4 + threadIdx.x; i < P; i += kAmaxThreads)
-        m = fmaxf(m, part[i]);
-    m = block_max(m, slot, kAmaxThreads);
-    if (threadIdx.x == 0)
-        *amax = fmaxf(*amax, m);
-}
-
 template <typename T, int V, int TEAM, int K, int D, bool FUSED, bool F8, bool LN>
 static void launch_fwd_rows(const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s)
 {
@@ -508,17 +474,12 @@ static hipError_t dispatch_fwd_kind(FwdKind kind, const rmsnorm_plan &p, const F
     }
 }
 
-hipError_t launch_fwd(int dtype, bool fused, FwdKind kind, const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s)
+// Forward launch for storage type T; explicitly instantiated once per type in
+// fwd_<type>.hip, so that the three types compile in parallel.
+template <typename T>
+hipError_t launch_fwd_typed(bool fused, FwdKind kind, const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s)
 {
-    if (dtype == RMSNORM_BF16)
-        return fused ? dispatch_fwd_kind<bf16_t, true>(kind, p, a, s) : dispatch_fwd_kind<bf16_t, false>(kind, p, a, s);
-    return fused ? dispatch_fwd_kind<float, true>(kind, p, a, s) : dispatch_fwd_kind<float, false>(kind, p, a, s);
-}
-
-hipError_t launch_amax_finalize(const float *part, int64_t programs, float *amax, hipStream_t s)
-{
-    hipLaunchKernelGGL(amax_finalize_kernel, dim3(1), dim3(kAmaxThreads), 0, s, part, programs, amax);
-    return hipGetLastError();
+    return fused ? dispatch_fwd_kind<T, true>(kind, p, a, s) : dispatch_fwd_kind<T, false>(kind, p, a, s);
 }
 
 } // namespace rmsnorm

@@ -185,9 +185,11 @@ inline int bwd_rows_bound(bool ln, bool fused, bool vec, int team, int chunks, i
     return 0;
 }
 
-// Elements per 16-byte access.
-inline int vec_elems(int dtype) { return dtype == RMSNORM_BF16 ? 8 : 4; }
-inline int elem_bytes(int dtype) { return dtype == RMSNORM_BF16 ? 2 : 4; }
+// Storage dtypes the kernels are built for.
+inline bool dtype_known(int dtype) { return dtype == RMSNORM_F32 || dtype == RMSNORM_BF16 || dtype == RMSNORM_F16; }
+// Elements per 16-byte access, and bytes per element.
+inline int vec_elems(int dtype) { return dtype == RMSNORM_F32 ? 4 : 8; }
+inline int elem_bytes(int dtype) { return dtype == RMSNORM_F32 ? 4 : 2; }
 
 // Selector (pure; selector.cpp).
 int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cus, rmsnorm_plan *out);
@@ -217,7 +219,9 @@ enum FwdKind { FWD_RMS = 0, FWD_RMS_FP8 = 1, FWD_LN = 2 };
 // amax finalizer: one workgroup folds the per-workgroup maxima.
 constexpr int kAmaxThreads = 1024;
 
-// Kernel launchers (fwd_kernels.hip, bwd_kernels.hip).  fp8: y is E4M3 (only
+// Kernel launchers (launch.hip), dispatching on the storage dtype to the
+// per-type instances of the templates below (fwd_kernels.h, bwd_kernels.h,
+// instantiated in fwd_<type>.hip and bwd_<type>.hip).  fp8: y is E4M3 (only
 // the layouts without prefetch are compiled for it).
 hipError_t launch_fwd(int dtype, bool fused, FwdKind kind, const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s);
 hipError_t launch_amax_finalize(const float *part, int64_t programs, float *amax, hipStream_t s);
@@ -226,5 +230,13 @@ hipError_t launch_bwd(int dtype, bool fused, bool ln, const rmsnorm_plan &p, con
 // dbeta_j = sum_p partials[(programs + p) * ld + j].  Either output may be null.
 hipError_t launch_finalize(int dtype, const float *partials, int64_t programs, int64_t ld, int64_t N,
                            void *dgamma, void *dbeta, hipStream_t s);
+
+template <typename T>
+hipError_t launch_fwd_typed(bool fused, FwdKind kind, const rmsnorm_plan &p, const FwdArgs &a, hipStream_t s);
+template <typename T>
+hipError_t launch_bwd_typed(bool fused, bool ln, const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s);
+template <typename T>
+hipError_t launch_finalize_typed(const float *partials, int64_t programs, int64_t ld, int64_t N, void *dgamma,
+                                 void *dbeta, hipStream_t s);
 
 } // namespace rmsnorm

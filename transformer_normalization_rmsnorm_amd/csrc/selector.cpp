@@ -239,7 +239,7 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
 {
     if (op < RMSNORM_OP_FWD || op > RMSNORM_OP_LN_FUSED_ADD_BWD)
         return RMSNORM_EINVAL;
-    if (dtype != RMSNORM_BF16 && dtype != RMSNORM_F32)
+    if (!dtype_known(dtype))
         return RMSNORM_EUNSUPPORTED;
     if (M < 0 || N <= 0 || N > kMaxN)
         return RMSNORM_EINVAL;
