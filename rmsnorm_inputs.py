@@ -18,7 +18,8 @@ The workloads are the pages' shapes: a 512x2048 and a 4096x4096 bf16 layer, wide
 rows (8192) in bf16, a Gemma-style float32 layer (6144 wide), a DeepSeek-like
 hidden size (7168) with a fused residual add, and a per-head norm (128 wide).
 WIDE_WORKLOADS are rows beyond the pages' 8192-wide scope (16384 and 32768
-wide, plain and fused, bf16 and float32) at 64-128 MiB per tensor.
+wide, plain and fused, bf16 and float32) at 64-128 MiB per tensor;
+F16_WORKLOADS repeats the 4096 x 4096 layer with binary16 storage.
 """
 
 from __future__ import annotations
@@ -79,7 +80,12 @@ WIDE_WORKLOADS: Dict[str, Workload] = {
     ]
 }
 
-ALL_WORKLOADS: Dict[str, Workload] = {**WORKLOADS, **WIDE_WORKLOADS}
+# The 4096 x 4096 layer again with binary16 storage (same bytes as bf16).
+F16_WORKLOADS: Dict[str, Workload] = {
+    w.name: w for w in [Workload("f16_4096x4096", 4096, 4096, F16)]
+}
+
+ALL_WORKLOADS: Dict[str, Workload] = {**WORKLOADS, **WIDE_WORKLOADS, **F16_WORKLOADS}
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:

@@ -8,8 +8,9 @@ range, the full-size workload shapes, and zero rows.
   * Subnormal outputs: gamma small enough that y lies mostly below 2^-14,
     where binary16 spacing is fixed at 2^-24; the kernel's conversion must not
     flush them.
-  * Full size: the 4096 x 4096 layer and the 16384 x 7168 fused residual add
-    in binary16, forward outputs and dx on a row sample, dgamma in full."""
+  * Full size: the 16384 x 7168 fused residual add in binary16, forward
+    outputs and dx on a row sample, dgamma in full (the 4096 x 4096 layer in
+    binary16 is one of the benchmark workloads, tested with them)."""
 
 import numpy as np
 import pytest
@@ -59,7 +60,7 @@ def test_subnormal_outputs_are_kept(M, N, fused):
     assert np.count_nonzero((a > 0) & (a < 2.0 ** -14)) > y.size // 4
 
 
-@pytest.mark.parametrize("M,N,fused", [(4096, 4096, False), (16384, 7168, True)])
+@pytest.mark.parametrize("M,N,fused", [(16384, 7168, True)])  # 4096 x 4096 runs with the workloads
 def test_full_size(M, N, fused):
     print(f"f16 full size {M}x{N} fused={fused}", flush=True)
     inp = make_inputs(M, N, F16, fused=fused)

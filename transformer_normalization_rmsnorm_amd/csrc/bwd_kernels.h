@@ -164,6 +164,17 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
             }
         }
     };
+    // element e of a row chunk: get_unfused where it measured faster for
+    // binary16 (RMSNorm, workgroup teams with w in registers, one vector chunk
+    // per lane and at most one row in flight: 4096 x 4096 21.7 -> 20.3 us);
+    // with two rows in flight (16384 x 2048: 44.6 -> 46.4 us) and for
+    // LayerNorm (4096 x 4096: 24.9 -> 25.5 us) the extra registers cost more
+    auto elem = [&](const Chunk<T, V> &c, int e) __attribute__((always_inline)) {
+        if constexpr (!LN && TEAM == 0 && WR && K == 1 && D <= 1 && V > 1)
+            return c.get_unfused(e);
+        else
+            return c.get(e);
+    };
     auto proc_ln = [&](Row &b, int64_t row) __attribute__((always_inline)) {
         const float rs = b.rs, mu = b.mu;
         float sg = 0.0f, sgx = 0.0f; // sum g, sum g * xhat
@@ -173,9 +184,9 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
             if (EXACT || c < nchunks) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    const float gg = b.dy[k].get(e) * weight(b, k, e);
+                    const float gg = elem(b.dy[k], e) * weight(b, k, e);
                     sg += gg;
-                    sgx = fmaf(gg, (b.v[k].get(e) - mu) * rs, sgx);
+                    sgx = fmaf(gg, (elem(b.v[k], e) - mu) * rs, sgx);
                 }
             }
         }
@@ -196,8 +207,8 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
                 float o[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    const float d = b.dy[k].get(e);
-                    const float xh = (b.v[k].get(e) - mu) * rs;
+                    const float d = elem(b.dy[k], e);
+                    const float xh = (elem(b.v[k], e) - mu) * rs;
                     float dxv = rs * fmaf(-xh, c2, d * weight(b, k, e) - c1);
                     if constexpr (FUSED)
                         dxv += b.dh[k].get(e);
@@ -238,7 +249,7 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
             if (EXACT || c < nchunks) {
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    dot = fmaf(b.dy[k].get(e) * weight(b, k, e), b.v[k].get(e), dot);
+                    dot = fmaf(elem(b.dy[k], e) * weight(b, k, e), elem(b.v[k], e), dot);
             }
         }
         // Values unpacked for the dot are formed again in the second pass where
@@ -264,8 +275,8 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
                 float o[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    const float xv = b.v[k].get(e);
-                    const float d = b.dy[k].get(e);
+                    const float xv = elem(b.v[k], e);
+                    const float d = elem(b.dy[k], e);
                     float dxv = fmaf(rs, d * weight(b, k, e), -xv * kc);
                     if constexpr (FUSED)
                         dxv += b.dh[k].get(e);
