@@ -230,6 +230,10 @@ typedef struct rmsnorm_plan {
     int64_t workspace_bytes; /* backward and fp8-forward workspace; plain forward 0 */
     int32_t fin_threads; /* finalizer workgroup size (dgamma, or amax for fp8) */
     int64_t fin_grid;    /* finalizer workgroups */
+    int32_t rows_per_step; /* backward ROWS path: rows a workgroup reduces together.  2: two
+                              rows share one workgroup reduction and the next two are loaded
+                              ahead (plain RMSNorm, workgroup teams, w in registers, one chunk
+                              per lane, depth 1); otherwise 1. */
 } rmsnorm_plan;
 
 /* Pure selector query: the plan for `op` at (M, N, dtype).  vec_ok != 0 says
@@ -243,7 +247,8 @@ int rmsnorm_query_plan(int op, int64_t M, int64_t N, int dtype, int vec_ok, int 
  * switches, "Behavior when the fast path does not apply"): later calls of `op`
  * use path, vec, team and threads from *plan, its depth and w_regs when they
  * are >= 0 and its grid when grid > 0 (else the selector's depth, w_regs and
- * grid for that layout); chunks and the workspace follow.
+ * grid for that layout), and its rows_per_step when > 0 (else 1); chunks and
+ * the workspace follow.
  * vec = 1 forces scalar accesses on aligned data.  NULL clears.  Process-wide
  * and not thread-safe; a call that the override does not fit returns
  * RMSNORM_EINVAL. */
@@ -254,8 +259,8 @@ const char *rmsnorm_last_error(void);
 /* The ABI version this header describes (RMSNORM_ABI_VERSION); a binding
  * checks it before use.  2: rmsnorm_plan gained w_regs.  3: fp8-output
  * forwards (ops 4 and 5).  4: LayerNorm (include/layernorm.h, ops 6-9).
- * 5: binary16 storage (RMSNORM_F16). */
-#define RMSNORM_ABI_VERSION 5
+ * 5: binary16 storage (RMSNORM_F16).  6: rmsnorm_plan gained rows_per_step. */
+#define RMSNORM_ABI_VERSION 6
 
 /* Longest row (elements) any entry point accepts. */
 #define RMSNORM_MAX_N (1 << 24)

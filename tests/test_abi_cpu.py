@@ -405,6 +405,48 @@ def test_backward_rows_in_flight_follow_rows_per_program():
     assert plan(rn.OP_BWD, 4096, 4096)["depth"] == 1  # 16 rows per program
 
 
+@pytest.mark.parametrize("M,N,dt,want", [
+    (4096, 4096, rn.BF16, 2), (4096, 4096, rn.F16, 2), (4096, 4096, rn.F32, 2), (4096, 2048, rn.BF16, 2),
+    (1024, 8192, rn.BF16, 1),    # 4 rows per program: one row per reduction
+    (16384, 8192, rn.BF16, 1),   # 64 rows per program: two rows in flight, one at a time
+    (262144, 128, rn.BF16, 1),   # sub-workgroup teams
+    (4096, 16384, rn.BF16, 1),   # gamma re-read per row
+])
+def test_two_rows_per_reduction(M, N, dt, want):
+    """rows_per_step = 2 for plain RMSNorm workgroup teams with w in registers,
+    one chunk per lane, and 16 to 31 rows per program; never for fused-add or
+    LayerNorm, nor for the forward."""
+    p = plan(rn.OP_BWD, M, N, dt)
+    assert p["rows_per_step"] == want, p
+    if want == 2:
+        assert (p["team"], p["chunks"], p["depth"], p["w_regs"]) == (0, 1, 1, 1)
+    for op in (rn.OP_FUSED_ADD_BWD, rn.OP_LN_BWD, rn.OP_LN_FUSED_ADD_BWD, rn.OP_FWD, rn.OP_FUSED_ADD_FWD):
+        assert plan(op, M, N, dt)["rows_per_step"] == 1
+
+
+def test_two_rows_per_reduction_override_checks():
+    base = plan(rn.OP_BWD, 4096, 4096)
+    fields = {k: base[k] for k in ("path", "vec", "team", "threads", "depth", "w_regs")}
+    with rn.plan_override(rn.OP_BWD, **fields):  # rows_per_step not given: one row per reduction
+        assert plan(rn.OP_BWD, 4096, 4096)["rows_per_step"] == 1
+    with rn.plan_override(rn.OP_BWD, **fields, rows_per_step=2, grid=7):
+        p = plan(rn.OP_BWD, 4096, 4096)
+        assert p["rows_per_step"] == 2 and p["grid"] == 7
+    bad = [
+        (rn.OP_BWD, dict(fields, rows_per_step=3)),
+        (rn.OP_BWD, dict(fields, rows_per_step=2, depth=2)),
+        (rn.OP_BWD, dict(fields, rows_per_step=2, vec=1)),
+        (rn.OP_BWD, dict(path=rn.PATH_LOOP, vec=8, team=0, threads=512, rows_per_step=2)),
+        (rn.OP_FUSED_ADD_BWD, dict(fields, rows_per_step=2)),
+        (rn.OP_LN_BWD, dict(fields, rows_per_step=2)),
+        (rn.OP_FWD, dict(path=rn.PATH_ROWS, vec=8, team=0, threads=256, rows_per_step=2)),
+    ]
+    for op, f in bad:
+        with rn.plan_override(op, **f):
+            with pytest.raises(rn.RMSNormError):
+                plan(op, 4096, 4096)
+
+
 def test_selector_rejects_bad_queries():
     with pytest.raises(rn.RMSNormError):
         plan(10, 4, 4)

@@ -192,6 +192,39 @@ def test_wide_backward_layouts(fused_ok, M, N, dt, fields, fused):
         run_case(M, N, dt, fused, dt == "f32")
 
 
+# Two rows per reduction (rows_per_step = 2), forced with grids that give odd
+# and even row counts per program, one row per program (no second row
+# anywhere) and a ragged last vector group.
+PAIRS = [
+    (300, 4096, "bf16", dict(threads=512, grid=19)),
+    (257, 4096, "bf16", dict(threads=512, grid=128)),
+    (256, 4096, "bf16", dict(threads=512, grid=256)),
+    (100, 2048, "bf16", dict(threads=256, grid=7)),
+    (64, 8192, "bf16", dict(threads=1024, grid=5)),
+    (45, 5000, "bf16", dict(threads=640, grid=4)),
+    (300, 4096, "f32", dict(threads=1024, grid=17)),
+]
+
+
+@pytest.mark.parametrize("M,N,dt,fields", PAIRS + in_f16(PAIRS),
+                         ids=[f"{dt}_{M}x{N}_t{f['threads']}_g{f['grid']}" for M, N, dt, f in PAIRS + in_f16(PAIRS)])
+def test_two_rows_per_reduction(M, N, dt, fields):
+    vec = 4 if dt == "f32" else 8
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=vec, team=0, depth=1, w_regs=1, rows_per_step=2,
+                          **fields):
+        p = rn.rmsnorm_query_plan(rn.OP_BWD, M, N, CODE[dt], True)
+        assert (p["rows_per_step"], p["chunks"], p["grid"]) == (2, 1, fields["grid"]), p
+        run_case(M, N, dt, False, dt == "f32")
+        # non-affine
+        inp = make_inputs(M, N, dt, seed=3)
+        inp["gamma"] = None
+        out = gpu_forward(inp, dt, EPS, 0.0, False)
+        dx, dg = gpu_backward(inp, dt, EPS, 0.0, out, False)
+        torch.cuda.synchronize()
+        assert dg is None
+        check_backward(inp, dt, EPS, 0.0, from_dev(dx), None, v_full=inp["x"])
+
+
 # Non-affine op (no gamma): rows and looped paths, plain and fused, with the
 # GPU's rstd and with rstd recomputed.
 NON_AFFINE = [(300, 4096, "bf16", False), (200, 7168, "bf16", True), (130, 6144, "f32", False),

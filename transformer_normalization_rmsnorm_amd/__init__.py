@@ -57,7 +57,7 @@ class RMSNormError(RuntimeError):
 
 
 # RMSNORM_ABI_VERSION of include/rmsnorm.h that this binding marshals.
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class Plan(ctypes.Structure):
@@ -66,7 +66,7 @@ class Plan(ctypes.Structure):
         ("threads", ctypes.c_int32), ("chunks", ctypes.c_int32), ("depth", ctypes.c_int32),
         ("w_regs", ctypes.c_int32), ("grid", ctypes.c_int64),
         ("programs", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64), ("fin_threads", ctypes.c_int32),
-        ("fin_grid", ctypes.c_int64),
+        ("fin_grid", ctypes.c_int64), ("rows_per_step", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -481,8 +481,9 @@ def rmsnorm_query_plan(op: int, M: int, N: int, dtype_code: int, vec_ok: bool = 
 
 
 def rmsnorm_set_plan_override(op: int, plan: Optional[dict]):
-    """Force (path, vec, team, threads[, depth][, w_regs][, grid]) for later calls
-    of `op`; None clears.  A missing depth, w_regs or grid keeps the selector's."""
+    """Force (path, vec, team, threads[, depth][, w_regs][, grid][, rows_per_step])
+    for later calls of `op`; None clears.  A missing depth, w_regs or grid keeps
+    the selector's; a missing rows_per_step is 1."""
     lib = load_library()
     if plan is None:
         _check(lib.rmsnorm_set_plan_override(op, None), "rmsnorm_set_plan_override")

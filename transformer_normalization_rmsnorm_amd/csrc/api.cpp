@@ -102,6 +102,7 @@ int plan_for(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int cus, rmsn
             q.depth = o.plan.depth;
         if (o.plan.w_regs >= 0)
             q.w_regs = o.plan.w_regs;
+        q.rows_per_step = o.plan.rows_per_step > 0 ? o.plan.rows_per_step : 1;
         q.grid = o.plan.grid;
         if (q.vec != 1 && !vec_ok)
             return fail(RMSNORM_EINVAL, "override asks for 16-byte accesses on unaligned data");

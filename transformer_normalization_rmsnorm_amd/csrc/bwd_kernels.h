@@ -290,7 +290,67 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
         }
     };
 
-    row_pipeline<D, Row>((int64_t)blockIdx.x * tpb + team, a.grid * tpb, a.M, load, proc);
+    if constexpr (D == kDepthPairs) {
+        static_assert(bwd_pairs_compiled(LN, FUSED, TEAM, K, 1, WR, V), "two rows per step: not this layout");
+        // Two rows per step (rows_per_step = 2): both rows' dots go through
+        // one workgroup reduction (block_sum2, one barrier), and the next
+        // two rows are loaded before the current two are worked on.  A
+        // program's rows r0, r0 + s, r0 + 2s, ... pair up in order; a
+        // missing second row (odd count) is loaded clamped to the last row
+        // and neither written nor accumulated.
+        auto proc2 = [&](Row &b0, Row &b1, int64_t row, bool second) __attribute__((always_inline)) {
+            float dot0 = 0.0f, dot1 = 0.0f;
+            const int c = lane; // one chunk per lane
+            if (EXACT || c < nchunks) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    dot0 = fmaf(elem(b0.dy[0], e) * weight(b0, 0, e), elem(b0.v[0], e), dot0);
+                    dot1 = fmaf(elem(b1.dy[0], e) * weight(b1, 0, e), elem(b1.v[0], e), dot1);
+                }
+            }
+            block_sum2(dot0, dot1, red[parity], a.threads);
+            parity ^= 1;
+            auto pass2 = [&](Row &b, float dot, int64_t r) __attribute__((always_inline)) {
+                const float rs = b.rs;
+                const float kc = rs * rs * rs * dot * inv_n; // dx = rs * g - v * kc
+                if (EXACT || c < nchunks) {
+                    float o[V];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        const float xv = elem(b.v[0], e);
+                        const float d = elem(b.dy[0], e);
+                        o[e] = fmaf(rs, d * weight(b, 0, e), -xv * kc);
+                        acc[0][e] = fmaf(d, xv * rs, acc[0][e]);
+                    }
+                    Chunk<T, V> out;
+                    out.set(o);
+                    out.store(dxp + r * N + (int64_t)c * V);
+                }
+            };
+            pass2(b0, dot0, row);
+            if (second)
+                pass2(b1, dot1, row + a.grid);
+        };
+        const int64_t stride = a.grid, M = a.M, row0 = blockIdx.x;
+        const int64_t last = row0 < M ? row0 + (M - 1 - row0) / stride * stride : M - 1;
+        auto clamp = [&](int64_t r) __attribute__((always_inline)) { return r < last ? r : last; };
+        Row buf[2][2];
+        load(buf[0][0], clamp(row0));
+        load(buf[0][1], clamp(row0 + stride));
+        for (int64_t base = row0; base < M; base += 4 * stride) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int64_t r = base + (int64_t)s * 2 * stride;
+                if (r >= M)
+                    break;
+                load(buf[s ^ 1][0], clamp(r + 2 * stride));
+                load(buf[s ^ 1][1], clamp(r + 3 * stride));
+                proc2(buf[s][0], buf[s][1], r, r + stride < M);
+            }
+        }
+    } else {
+        row_pipeline<D, Row>((int64_t)blockIdx.x * tpb + team, a.grid * tpb, a.M, load, proc);
+    }
 
     if (a.partials == nullptr) // no dgamma (non-affine) and no dbeta
         return;
@@ -692,6 +752,13 @@ static hipError_t dispatch_bwd(const rmsnorm_plan &p, BwdArgs a, hipStream_t s)
         return hipGetLastError();
     }
     const bool vec = (p.vec == VV);
+    if constexpr (!LN && !FUSED) {
+        if (p.rows_per_step == 2) { // complete_plan admits it only for bwd_pairs_compiled layouts
+            if (!(vec && p.team == 0 && p.chunks == 1 && p.depth == 1 && p.w_regs == 1))
+                return hipErrorInvalidConfiguration;
+            return launch_bwd_rows<T, VV, 0, 1, kDepthPairs, true, 1024, false, false>(p, a, s);
+        }
+    }
 #define RMSNORM_CASE(VEC, TEAM, K, D, WR, BOUND, FBOUND)                                      \
     if constexpr ((FUSED ? FBOUND : BOUND) > 0) {                                                 \
         if (vec == (VEC == 1) && p.team == TEAM && p.chunks == K && p.depth == D && p.w_regs == WR) { \

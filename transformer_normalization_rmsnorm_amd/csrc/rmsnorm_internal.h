@@ -123,6 +123,16 @@ constexpr int kFinColsPerBlock = 32;
     X(0, 64, 1, 1, 1, 256, 256) X(0, 64, 2, 1, 1, 256, 256) X(0, 0, 1, 1, 1, 1024, 1024) \
     X(0, 0, 2, 1, 1, 512, 512) X(0, 0, 4, 1, 1, 512, 512)
 
+// Backward layouts that can reduce two rows together (rows_per_step = 2):
+// plain RMSNorm, workgroup teams, w in registers, one 16-byte chunk per lane,
+// one step loaded ahead.  They run an instance of their own, whose depth
+// template argument is kDepthPairs (no plan has that depth).
+constexpr bool bwd_pairs_compiled(bool ln, bool fused, int team, int chunks, int depth, bool w_regs, int vec)
+{
+    return !ln && !fused && team == 0 && chunks == 1 && depth == 1 && w_regs && vec > 1;
+}
+constexpr int kDepthPairs = 8;
+
 // LayerNorm backward layouts with dbeta accumulated in LDS.
 constexpr bool bwd_dbeta_in_lds(bool ln, bool fused, int team, int chunks, int vec)
 {

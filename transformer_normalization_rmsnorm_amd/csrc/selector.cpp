@@ -22,6 +22,12 @@ constexpr int kLoopThreads = 1024;  // looped path workgroup size
 constexpr int kBwdProgramsPerCU = 1; // persistent backward workgroup teams per compute unit
 constexpr int kBwdTeamsPerCU = 2;    // persistent backward workgroups per compute unit (sub-wave teams)
 constexpr int64_t kDeepRowsPerProgram = 32; // backward rows per program from which two rows are in flight
+// Below that, from this many rows per program two rows share each reduction
+// where the layout allows (measured on MI355X, backward main: 4096 x 4096 bf16
+// 19.6 -> 19.1 us, fp16 20.6 -> 19.4 us at 16 rows per program; 1024 x 8192
+// bf16 12.1 -> 13.6 us at 4 rows; 16384 x 8192 bf16 130.1 against 134.2 us
+// for two rows in flight one at a time at 64 rows)
+constexpr int64_t kPairRowsPerProgram = 16;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -179,6 +185,10 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
     int64_t rows_per_block = 1;
     if (!bwd)
         p->w_regs = 0;
+    if (p->rows_per_step <= 0)
+        p->rows_per_step = 1;
+    if (!bwd && p->rows_per_step != 1)
+        return false;
     if (p->w_regs != 0 && p->w_regs != 1)
         return false;
     if (p->path == RMSNORM_PATH_ROWS) {
@@ -197,10 +207,16 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
         if (bwd && !tiling_ok(p->op, dtype, p->vec != 1, p->team, k, b, lanes, nchunks))
             return false;
         p->chunks = k;
+        if (p->rows_per_step != 1 &&
+            (p->rows_per_step != 2 ||
+             !bwd_pairs_compiled(is_ln_op(p->op), is_fused(p->op), p->team, k, p->depth, p->w_regs, p->vec)))
+            return false;
         const int64_t sets = is_ln_op(p->op) ? 2 : 1;
         if (bwd && p->team != 0 && sets * rows_per_block * N * (int64_t)sizeof(float) > 65536)
             return false; // team partials are combined in LDS
     } else if (p->path == RMSNORM_PATH_LOOP) {
+        if (p->rows_per_step != 1)
+            return false;
         p->team = 0;
         p->chunks = 0;
         p->depth = 0;
@@ -254,6 +270,7 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
     // ahead, w held in registers
     p.depth = bwd ? 1 : 0;
     p.w_regs = bwd ? 1 : 0;
+    p.rows_per_step = 1;
     const int64_t nchunks = N / p.vec;
     bool placed = false;
     if (vec) {
@@ -310,8 +327,12 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
         // against 16.9 us at one).  Fused-add LayerNorm, which also holds dh
         // and two accumulator sets, was 2.5% slower at two.
         const int64_t programs = (int64_t)kBwdProgramsPerCU * std::max(num_cus, 1);
-        if (ceil_div(M, programs) >= kDeepRowsPerProgram && bound(op, vec, 0, p.chunks, 2, 1) >= p.threads)
+        const int64_t rows = ceil_div(M, programs);
+        if (rows >= kDeepRowsPerProgram && bound(op, vec, 0, p.chunks, 2, 1) >= p.threads)
             p.depth = 2;
+        else if (rows >= kPairRowsPerProgram &&
+                 bwd_pairs_compiled(is_ln_op(op), is_fused(op), p.team, p.chunks, p.depth, p.w_regs, p.vec))
+            p.rows_per_step = 2;
     }
     if (!complete_plan(&p, M, N, dtype, num_cus, false))
         return RMSNORM_EUNSUPPORTED;
