@@ -19,7 +19,7 @@ Prints ONE JSON line (driver contract) with, among others:
 Other modes:
   --report PATH      write a detailed JSON report (every op, cold/hot, direct/graph)
   --all-workloads    add every workload to the report
-  --counters-run     a short fixed sequence of launches for rocprofv3 --pmc runs
+  --counters-run     a short fixed sequence of launches for rocprofv3 --pmc runs (--workload NAME)
 """
 
 from __future__ import annotations
@@ -393,12 +393,13 @@ def counters_traffic(ident: str):
         return None
 
 
-def counters_run(rn, torch):
+def counters_run(rn, torch, workload: str = "bf16_4096x4096"):
     """Fixed launch sequence for rocprofv3 --pmc: a plain copy of known size,
-    then forward, backward main and finalizer on the default workload."""
-    from rmsnorm_inputs import WORKLOADS
+    then forward, backward main and finalizer on one workload (the default
+    one unless --workload names another)."""
+    from rmsnorm_inputs import ALL_WORKLOADS
 
-    w = WORKLOADS["bf16_4096x4096"]
+    w = ALL_WORKLOADS[workload]
     lib = rn.load_library()
     S = Sets(w, lib, rn, torch, 4)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -446,7 +447,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     if args.counters_run:
-        counters_run(rn, torch)
+        counters_run(rn, torch, args.workload)
         return
     lib = rn.load_library()
     w = WORKLOADS[args.workload]
