@@ -15,7 +15,9 @@
 // fixed order and writes dgamma in the parameter dtype: no atomics, no clear
 // and no separate conversion kernel.  Unlike the page's kernel, each team keeps
 // D further rows in flight (row_pipeline) while it reduces and writes the
-// current one, so HBM latency overlaps the work instead of stalling it.
+// current one, so HBM latency overlaps the work instead of stalling it.  With
+// 16 to 31 rows per program and one chunk per lane, two rows share each
+// workgroup reduction (the kDepthPairs instance, plan rows_per_step = 2).
 //
 // Rows wider than one chunk per lane of a 1024-lane workgroup (8192 bf16 /
 // 4096 fp32 elements; the page's scope stops at N = 8192 and keeps atomics
