@@ -203,18 +203,27 @@ PAIRS = [
     (64, 8192, "bf16", dict(threads=1024, grid=5)),
     (45, 5000, "bf16", dict(threads=640, grid=4)),
     (300, 4096, "f32", dict(threads=1024, grid=17)),
+    (300, 1024, "f32", dict(threads=256, grid=19)),
 ]
 
 
-@pytest.mark.parametrize("M,N,dt,fields", PAIRS + in_f16(PAIRS),
-                         ids=[f"{dt}_{M}x{N}_t{f['threads']}_g{f['grid']}" for M, N, dt, f in PAIRS + in_f16(PAIRS)])
-def test_two_rows_per_reduction(M, N, dt, fields):
+# the fused-add op's two-row instance is compiled for at most 256 threads
+PAIR_CASES = [(M, N, dt, f, False) for M, N, dt, f in PAIRS + in_f16(PAIRS)] + \
+    [(M, N, dt, f, True) for M, N, dt, f in PAIRS + in_f16(PAIRS) if f["threads"] <= 256]
+
+
+@pytest.mark.parametrize("M,N,dt,fields,fused", PAIR_CASES,
+                         ids=[f"{dt}_{M}x{N}_t{f['threads']}_g{f['grid']}" + ("_fused" if fu else "")
+                              for M, N, dt, f, fu in PAIR_CASES])
+def test_two_rows_per_reduction(M, N, dt, fields, fused):
     vec = 4 if dt == "f32" else 8
-    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=vec, team=0, depth=1, w_regs=1, rows_per_step=2,
-                          **fields):
-        p = rn.rmsnorm_query_plan(rn.OP_BWD, M, N, CODE[dt], True)
+    op = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
+    with rn.plan_override(op, path=rn.PATH_ROWS, vec=vec, team=0, depth=1, w_regs=1, rows_per_step=2, **fields):
+        p = rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)
         assert (p["rows_per_step"], p["chunks"], p["grid"]) == (2, 1, fields["grid"]), p
-        run_case(M, N, dt, False, dt == "f32")
+        run_case(M, N, dt, fused, dt == "f32")
+        if fused:
+            return
         # non-affine
         inp = make_inputs(M, N, dt, seed=3)
         inp["gamma"] = None

@@ -322,6 +322,8 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
                         const float xv = elem(b.v[0], e);
                         const float d = elem(b.dy[0], e);
                         o[e] = fmaf(rs, d * weight(b, 0, e), -xv * kc);
+                        if constexpr (FUSED)
+                            o[e] += b.dh[0].get(e);
                         acc[0][e] = fmaf(d, xv * rs, acc[0][e]);
                     }
                     Chunk<T, V> out;
@@ -754,11 +756,12 @@ static hipError_t dispatch_bwd(const rmsnorm_plan &p, BwdArgs a, hipStream_t s)
         return hipGetLastError();
     }
     const bool vec = (p.vec == VV);
-    if constexpr (!LN && !FUSED) {
+    if constexpr (!LN) {
         if (p.rows_per_step == 2) { // complete_plan admits it only for bwd_pairs_compiled layouts
-            if (!(vec && p.team == 0 && p.chunks == 1 && p.depth == 1 && p.w_regs == 1))
+            if (!(vec && p.team == 0 && p.chunks == 1 && p.depth == 1 && p.w_regs == 1 &&
+                  p.threads <= bwd_pairs_bound(FUSED)))
                 return hipErrorInvalidConfiguration;
-            return launch_bwd_rows<T, VV, 0, 1, kDepthPairs, true, 1024, false, false>(p, a, s);
+            return launch_bwd_rows<T, VV, 0, 1, kDepthPairs, true, bwd_pairs_bound(FUSED), FUSED, false>(p, a, s);
         }
     }
 #define RMSNORM_CASE(VEC, TEAM, K, D, WR, BOUND, FBOUND)                                      \

@@ -124,13 +124,19 @@ constexpr int kFinColsPerBlock = 32;
     X(0, 0, 2, 1, 1, 512, 512) X(0, 0, 4, 1, 1, 512, 512)
 
 // Backward layouts that can reduce two rows together (rows_per_step = 2):
-// plain RMSNorm, workgroup teams, w in registers, one 16-byte chunk per lane,
-// one step loaded ahead.  They run an instance of their own, whose depth
-// template argument is kDepthPairs (no plan has that depth).
+// RMSNorm (plain or fused-add), workgroup teams, w in registers, one 16-byte
+// chunk per lane, one step loaded ahead.  They run an instance of their own,
+// whose depth template argument is kDepthPairs (no plan has that depth),
+// compiled for up to bwd_pairs_bound(fused) threads.  The fused-add op also
+// holds the dh rows (146 VGPRs); it is used up to 256 threads, where it
+// measured faster (4096 x 2048 bf16 backward main 15.0 -> 14.1 us), and not
+// at 512 (4096 x 4096: 24.2 against 24.4 us).
 constexpr bool bwd_pairs_compiled(bool ln, bool fused, int team, int chunks, int depth, bool w_regs, int vec)
 {
-    return !ln && !fused && team == 0 && chunks == 1 && depth == 1 && w_regs && vec > 1;
+    (void)fused;
+    return !ln && team == 0 && chunks == 1 && depth == 1 && w_regs && vec > 1;
 }
+constexpr int bwd_pairs_bound(bool fused) { return fused ? 256 : 1024; }
 constexpr int kDepthPairs = 8;
 
 // LayerNorm backward layouts with dbeta accumulated in LDS.

@@ -209,7 +209,8 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
         p->chunks = k;
         if (p->rows_per_step != 1 &&
             (p->rows_per_step != 2 ||
-             !bwd_pairs_compiled(is_ln_op(p->op), is_fused(p->op), p->team, k, p->depth, p->w_regs, p->vec)))
+             !bwd_pairs_compiled(is_ln_op(p->op), is_fused(p->op), p->team, k, p->depth, p->w_regs, p->vec) ||
+             p->threads > bwd_pairs_bound(is_fused(p->op))))
             return false;
         const int64_t sets = is_ln_op(p->op) ? 2 : 1;
         if (bwd && p->team != 0 && sets * rows_per_block * N * (int64_t)sizeof(float) > 65536)
@@ -331,7 +332,8 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
         if (rows >= kDeepRowsPerProgram && bound(op, vec, 0, p.chunks, 2, 1) >= p.threads)
             p.depth = 2;
         else if (rows >= kPairRowsPerProgram &&
-                 bwd_pairs_compiled(is_ln_op(op), is_fused(op), p.team, p.chunks, p.depth, p.w_regs, p.vec))
+                 bwd_pairs_compiled(is_ln_op(op), is_fused(op), p.team, p.chunks, p.depth, p.w_regs, p.vec) &&
+                 p.threads <= bwd_pairs_bound(is_fused(op)))
             p.rows_per_step = 2;
     }
     if (!complete_plan(&p, M, N, dtype, num_cus, false))
