@@ -394,28 +394,35 @@ def test_forward_grid_keeps_work_items_below_2_31():
 
 def test_backward_rows_in_flight_follow_rows_per_program():
     """Two rows in flight from 32 rows per program (w in registers), one below;
-    fused-add LayerNorm keeps one."""
+    fused-add LayerNorm keeps one; layouts that reduce two rows together keep
+    depth 1 (their next two rows are in flight)."""
     for op in (rn.OP_BWD, rn.OP_FUSED_ADD_BWD, rn.OP_LN_BWD):
         assert plan(op, 16384, 8192)["depth"] == 2
+        assert plan(op, 1024, 8192)["depth"] == 1
+    for op in (rn.OP_FUSED_ADD_BWD, rn.OP_LN_BWD):  # 512 threads: no two-row reduction for these
         assert plan(op, 256 * 32, 4096)["depth"] == 2
         assert plan(op, 256 * 31, 4096)["depth"] == 1
-        assert plan(op, 1024, 8192)["depth"] == 1
+    p = plan(rn.OP_BWD, 256 * 32, 4096)
+    assert (p["depth"], p["rows_per_step"]) == (1, 2)
     assert plan(rn.OP_LN_FUSED_ADD_BWD, 16384, 8192)["depth"] == 1
     assert plan(rn.OP_BWD, 16384, 8192, cus=80)["depth"] == 2
     assert plan(rn.OP_BWD, 4096, 4096)["depth"] == 1  # 16 rows per program
 
 
 @pytest.mark.parametrize("M,N,dt,want", [
-    (4096, 4096, rn.BF16, 2), (4096, 4096, rn.F16, 2), (4096, 4096, rn.F32, 2), (4096, 2048, rn.BF16, 2),
-    (1024, 8192, rn.BF16, 1),    # 4 rows per program: one row per reduction
-    (16384, 8192, rn.BF16, 1),   # 64 rows per program: two rows in flight, one at a time
+    (4096, 4096, rn.BF16, 2), (4096, 4096, rn.F16, 2), (4096, 2048, rn.BF16, 2), (16384, 2048, rn.BF16, 2),
+    (512, 2048, rn.BF16, 2), (16384, 4096, rn.BF16, 2), (1024, 2048, rn.F32, 2),
+    (4096, 4096, rn.F32, 1),     # 1024-thread workgroups: one row per reduction
+    (1024, 8192, rn.BF16, 1), (4096, 8192, rn.BF16, 1),
+    (16384, 8192, rn.BF16, 1),   # 1024 threads, 64 rows per program: two rows in flight, one at a time
+    (256, 4096, rn.BF16, 1),     # one row per program
     (262144, 128, rn.BF16, 1),   # sub-workgroup teams
     (4096, 16384, rn.BF16, 1),   # gamma re-read per row
 ])
 def test_two_rows_per_reduction(M, N, dt, want):
     """rows_per_step = 2 for RMSNorm workgroup teams with w in registers, one
-    chunk per lane, and 16 to 31 rows per program (fused-add: at most 256
-    threads); never for LayerNorm, nor for the forward."""
+    chunk per lane, at most 512 threads (fused-add: 256) and two or more rows
+    per program; never for LayerNorm, nor for the forward."""
     p = plan(rn.OP_BWD, M, N, dt)
     assert p["rows_per_step"] == want, p
     if want == 2:

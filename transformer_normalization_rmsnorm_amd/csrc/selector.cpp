@@ -22,12 +22,17 @@ constexpr int kLoopThreads = 1024;  // looped path workgroup size
 constexpr int kBwdProgramsPerCU = 1; // persistent backward workgroup teams per compute unit
 constexpr int kBwdTeamsPerCU = 2;    // persistent backward workgroups per compute unit (sub-wave teams)
 constexpr int64_t kDeepRowsPerProgram = 32; // backward rows per program from which two rows are in flight
-// Below that, from this many rows per program two rows share each reduction
-// where the layout allows (measured on MI355X, backward main: 4096 x 4096 bf16
-// 19.6 -> 19.1 us, fp16 20.6 -> 19.4 us at 16 rows per program; 1024 x 8192
-// bf16 12.1 -> 13.6 us at 4 rows; 16384 x 8192 bf16 130.1 against 134.2 us
-// for two rows in flight one at a time at 64 rows)
-constexpr int64_t kPairRowsPerProgram = 16;
+// Workgroups of at most this many threads reduce two rows together wherever
+// the layout allows (bwd_pairs_compiled), ahead of two rows in flight one at
+// a time.  Measured on MI355X, bf16 backward main, one row / two rows in
+// flight / two rows per reduction: 256 threads 16384 x 2048 45.6 / 41.5 /
+// 34.9 us, 1024 x 2048 5.5 / 5.7 / 5.1 us; 512 threads 4096 x 4096 19.5 / 19.2
+// / 19.1 us, 16384 x 4096 65.5 / 64.6 / 64.3 us; but 1024 threads 4096 x 8192
+// 35.5 / 36.5 / 38.7 us and 2048 x 8192 19.7 / - / 23.0 us.  The fused-add op
+// (which also holds dh) gained at 256 threads (4096 x 2048: 14.9 -> 13.8 us)
+// and not at 512 (4096 x 4096: 24.0 / 24.0 us).
+constexpr int kPairMaxThreads = 512;
+constexpr int kPairMaxThreadsFused = 256;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -329,12 +334,12 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
         // and two accumulator sets, was 2.5% slower at two.
         const int64_t programs = (int64_t)kBwdProgramsPerCU * std::max(num_cus, 1);
         const int64_t rows = ceil_div(M, programs);
-        if (rows >= kDeepRowsPerProgram && bound(op, vec, 0, p.chunks, 2, 1) >= p.threads)
-            p.depth = 2;
-        else if (rows >= kPairRowsPerProgram &&
-                 bwd_pairs_compiled(is_ln_op(op), is_fused(op), p.team, p.chunks, p.depth, p.w_regs, p.vec) &&
-                 p.threads <= bwd_pairs_bound(is_fused(op)))
+        if (rows >= 2 && p.threads <= (is_fused(op) ? kPairMaxThreadsFused : kPairMaxThreads) &&
+            bwd_pairs_compiled(is_ln_op(op), is_fused(op), p.team, p.chunks, p.depth, p.w_regs, p.vec) &&
+            p.threads <= bwd_pairs_bound(is_fused(op)))
             p.rows_per_step = 2;
+        else if (rows >= kDeepRowsPerProgram && bound(op, vec, 0, p.chunks, 2, 1) >= p.threads)
+            p.depth = 2;
     }
     if (!complete_plan(&p, M, N, dtype, num_cus, false))
         return RMSNORM_EUNSUPPORTED;
