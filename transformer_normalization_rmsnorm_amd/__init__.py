@@ -4,6 +4,8 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in ``include/rmsnorm.h``.  PyTorch supplies
 device memory (``torch.empty``) and the current stream; nothing here computes.
 If the library has not been built, importing works but every call raises.
+Tensors are bfloat16, float16 or float32 (one dtype per call; rstd, mean,
+scale and amax are float32); arithmetic is float32 for every dtype.
 
 Functions mirror the C entry points:
   rmsnorm_fwd(x, gamma, eps, offset)                    -> (y, rstd)
