@@ -38,10 +38,15 @@ def test_dgamma_bit_identical_run_to_run(M, N, dt, fused):
         assert torch.equal(_bits(dx), _bits(runs[0][0]))
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("M,N,fused", [(2048, 4096, True), (4096, 4096, False), (4096, 2048, True)],
+                         ids=["fused_2048x4096", "plain_4096x4096_two_rows", "fused_4096x2048_two_rows"])
+def test_graph_replay_matches_eager(M, N, fused):
     """Capture fwd + bwd on the capture stream; replay several times with eager
-    work and synchronisations between replays; every replay equals eager bitwise."""
-    M, N, dt = 2048, 4096, "bf16"
+    work and synchronisations between replays; every replay equals eager bitwise.
+    The last two shapes reduce two rows together in the backward."""
+    dt = "bf16"
+    op = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
+    assert rn.rmsnorm_query_plan(op, M, N, rn.BF16)["rows_per_step"] == (1 if (M, N) == (2048, 4096) else 2)
     inp = make_inputs(M, N, dt, fused=True)
     x, r, g = to_dev(inp["x"], dt), to_dev(inp["residual"], dt), to_dev(inp["gamma"], dt)
     dy, dh = to_dev(inp["dy"], dt), to_dev(inp["dh"], dt)
@@ -50,8 +55,13 @@ def test_graph_replay_matches_eager():
     ws, _ = rn.alloc_workspace(M, N, rn.BF16, x.device)
 
     def step():
-        rn.rmsnorm_fused_add_fwd(x, r, g, EPS, 0.0, y=y, h_out=h, rstd=rstd)
-        rn.rmsnorm_fused_add_bwd(dy, dh, h, g, rstd, EPS, 0.0, dx=dx, dgamma=dg, workspace=ws)
+        if fused:
+            rn.rmsnorm_fused_add_fwd(x, r, g, EPS, 0.0, y=y, h_out=h, rstd=rstd)
+            rn.rmsnorm_fused_add_bwd(dy, dh, h, g, rstd, EPS, 0.0, dx=dx, dgamma=dg, workspace=ws)
+        else:
+            h.copy_(x)
+            rn.rmsnorm_fwd(x, g, EPS, 0.0, y=y, rstd=rstd)
+            rn.rmsnorm_bwd(dy, x, g, rstd, EPS, 0.0, dx=dx, dgamma=dg, workspace=ws)
 
     step()
     torch.cuda.synchronize()
