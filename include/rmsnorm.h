@@ -232,8 +232,9 @@ typedef struct rmsnorm_plan {
     int64_t fin_grid;    /* finalizer workgroups */
     int32_t rows_per_step; /* backward ROWS path: rows a workgroup reduces together.  2: two
                               rows share one workgroup reduction and the next two are loaded
-                              ahead (plain RMSNorm, workgroup teams, w in registers, one chunk
-                              per lane, depth 1); otherwise 1. */
+                              ahead (RMSNorm, plain or fused-add; workgroup teams, w in
+                              registers, one chunk per lane, depth 1; at most 1024 threads,
+                              256 for fused-add); otherwise 1. */
 } rmsnorm_plan;
 
 /* Pure selector query: the plan for `op` at (M, N, dtype).  vec_ok != 0 says
