@@ -221,8 +221,15 @@ def test_two_rows_per_reduction(M, N, dt, fields, fused):
     with rn.plan_override(op, path=rn.PATH_ROWS, vec=vec, team=0, depth=1, w_regs=1, rows_per_step=2, **fields):
         p = rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)
         assert (p["rows_per_step"], p["chunks"], p["grid"]) == (2, 1, fields["grid"]), p
-        run_case(M, N, dt, fused, dt == "f32")
+        inp, out, dx, _ = run_case(M, N, dt, fused, dt == "f32")
         if fused:
+            # dx written over dh (the residual gradient in place) gives the same bytes
+            dh = to_dev(inp["dh"], dt)
+            dx2, _ = rn.rmsnorm_fused_add_bwd(to_dev(inp["dy"], dt), dh, out["h"], out["gamma"], out["rstd"], EPS,
+                                              1.0 if dt == "f32" else 0.0, dx=dh)
+            torch.cuda.synchronize()
+            assert dx2.data_ptr() == dh.data_ptr()
+            assert np.array_equal(from_dev(dx2).view(np.uint8), from_dev(dx).view(np.uint8))
             return
         # non-affine
         inp = make_inputs(M, N, dt, seed=3)
