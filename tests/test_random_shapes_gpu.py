@@ -2,7 +2,8 @@
 
 Forty-eight cases drawn once from a fixed seed: N log-uniform over [1, 70000]
 (so odd, ragged, narrow, wide and looped rows all occur), M up to 300 with at
-most three million elements, bf16 or fp32, plain or fused residual add,
+most three million elements, bf16 or fp32 (and a second draw of twenty-four
+binary16 cases from another seed), plain or fused residual add,
 gamma + 0 or gamma + 1, eps from {1e-6, 1e-5, 0.1}, and in a quarter of the
 cases every tensor at a storage offset that is not 16-byte aligned.  Each case
 runs the RMSNorm and the LayerNorm forward and backward through the C ABI and
@@ -19,7 +20,9 @@ from rmsnorm_inputs import make_inputs
 pytestmark = pytest.mark.gpu
 
 
-def draw_cases(count=48, seed=2024):
+def draw_cases(count=48, seed=2024, storage=None):
+    """The case list; storage, if given, replaces the drawn storage type (the
+    draw itself is unchanged, so the other fields match a draw without it)."""
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < count:
@@ -28,6 +31,7 @@ def draw_cases(count=48, seed=2024):
         M = int(rng.integers(1, 301))
         M = max(1, min(M, 3_000_000 // N))
         dt = "bf16" if rng.random() < 0.6 else "f32"
+        dt = storage or dt
         fused = bool(rng.random() < 0.4)
         gemma = bool(rng.random() < 0.3)
         eps = float(rng.choice([1e-6, 1e-5, 0.1]))
@@ -36,7 +40,7 @@ def draw_cases(count=48, seed=2024):
     return cases
 
 
-CASES = draw_cases()
+CASES = draw_cases() + draw_cases(24, seed=2025, storage="f16")
 
 
 def case_id(c):
