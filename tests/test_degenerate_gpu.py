@@ -13,6 +13,16 @@ Each case replaces the first rows of a seeded draw with one pattern each:
   shifted      16 + 0.25 z: LayerNorm mean far above the spread
   outlier      a normal draw with one element 2^20
   dy_zero      a normal draw whose incoming gradient row is zero
+binary16 storage cannot hold the big, tiny and outlier rows; it takes its own
+set, which keeps the rows that fit and adds:
+  big16        a normal draw times 2^12
+  near_max     +-65504, binary16's largest finite value (squares far beyond
+               binary16's range, well inside float32's; dx is subnormal)
+  small16      a normal draw times 2^-12
+  subnormal    a normal draw times 2^-18: binary16 subnormal inputs
+  outlier16    a normal draw with one element 2^15
+  dy_subnormal a normal draw whose incoming gradient row is a normal draw
+               times 2^-18, so dx is subnormal
 For the fused-add ops the pattern goes into the residual and x is zero on
 those rows, so h = residual keeps it.  With eps = 0 the zero and tiny rows are
 left out: there 1/sqrt(mean square) is infinite or beyond float32's range,
@@ -33,6 +43,9 @@ pytestmark = pytest.mark.gpu
 
 PATTERNS = ["zero", "constant", "one_hot", "big", "small", "tiny", "alternating", "shifted", "outlier", "dy_zero"]
 NO_EPS_PATTERNS = [p for p in PATTERNS if p not in ("zero", "tiny")]
+F16_PATTERNS = ["zero", "constant", "one_hot", "big16", "near_max", "small16", "subnormal", "alternating", "shifted",
+                "outlier16", "dy_zero", "dy_subnormal"]
+F16_NO_EPS_PATTERNS = [p for p in F16_PATTERNS if p != "zero"]
 EXTRA_ROWS = 6  # ordinary rows after the patterns
 
 
@@ -61,6 +74,19 @@ def pattern_row(name, N, rng):
         return z
     if name == "dy_zero":
         return z
+    if name == "big16":
+        return z * np.float32(2.0 ** 12)
+    if name == "near_max":
+        return np.where(z < 0, -65504.0, 65504.0).astype(np.float32)
+    if name == "small16":
+        return z * np.float32(2.0 ** -12)
+    if name == "subnormal":
+        return z * np.float32(2.0 ** -18)
+    if name == "outlier16":
+        z[0] = 2.0 ** 15
+        return z
+    if name == "dy_subnormal":
+        return z
     raise ValueError(name)
 
 
@@ -80,6 +106,8 @@ def degenerate_inputs(N, dt, fused, gemma, patterns, layernorm=False, seed=7):
             x[i] = 0.0
         if name == "dy_zero":
             dy[i] = 0.0
+        if name == "dy_subnormal":
+            dy[i] *= np.float32(2.0 ** -18)
     inp[target] = to_storage(t, dt)
     if fused:
         inp["x"] = to_storage(x, dt)
@@ -98,6 +126,9 @@ SHAPES = [
     (40000, "f32", True, False),    # looped rows
     (1, "bf16", False, False),      # one element per row
 ]
+
+
+F16_SHAPES = [(N, "f16", fused, gemma) for N, _, fused, gemma in SHAPES]
 
 
 def shape_id(s):
@@ -121,34 +152,48 @@ def run_rmsnorm(N, dt, fused, gemma, eps, patterns):
     return inp, y, rstd, dx
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=shape_id)
+def patterns_for(dt):
+    return F16_PATTERNS if dt == "f16" else PATTERNS
+
+
+@pytest.mark.parametrize("shape", SHAPES + F16_SHAPES, ids=shape_id)
 def test_rmsnorm_degenerate_rows(shape):
     N, dt, fused, gemma = shape
     eps = 1e-6
-    inp, y, rstd, dx = run_rmsnorm(N, dt, fused, gemma, eps, PATTERNS)
+    pats = patterns_for(dt)
+    inp, y, rstd, dx = run_rmsnorm(N, dt, fused, gemma, eps, pats)
     # the zero row: y is exactly 0 and rstd is 1/sqrt(eps) (checked above to
     # float32's rule); its dx is rstd * dy * w [+ dh]
-    yz = storage_to_f32(y[PATTERNS.index("zero")], dt)
+    yz = storage_to_f32(y[pats.index("zero")], dt)
     assert np.all(yz == 0.0), "zero row: y must be exactly 0"
     # the dy_zero row of the plain op has dx exactly 0 (it has no dh term)
     if not fused:
-        dxz = storage_to_f32(dx[PATTERNS.index("dy_zero")], dt)
+        dxz = storage_to_f32(dx[pats.index("dy_zero")], dt)
         assert np.all(dxz == 0.0), "zero incoming gradient: dx must be exactly 0"
+    if dt == "f16" and not fused and N > 1:
+        # the subnormal dx rows were compared above at binary16's subnormal
+        # spacing; they must not have been flushed to zero (with N = 1, dx is
+        # rstd g (1 - xhat^2), far below binary16's range)
+        for name in ("near_max", "dy_subnormal"):
+            d = storage_to_f32(dx[pats.index(name)], dt)
+            assert np.count_nonzero((d != 0) & (np.abs(d) < 2.0 ** -14)) > 0, f"{name}: no subnormal dx"
 
 
-@pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[3], SHAPES[5]], ids=shape_id)
+@pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[3], SHAPES[5], F16_SHAPES[1], F16_SHAPES[3], F16_SHAPES[5]],
+                         ids=shape_id)
 def test_rmsnorm_zero_eps(shape):
     N, dt, fused, gemma = shape
-    run_rmsnorm(N, dt, fused, gemma, 0.0, NO_EPS_PATTERNS)
+    run_rmsnorm(N, dt, fused, gemma, 0.0, F16_NO_EPS_PATTERNS if dt == "f16" else NO_EPS_PATTERNS)
 
 
 LN_EPS = 1e-5
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=shape_id)
+@pytest.mark.parametrize("shape", SHAPES + F16_SHAPES, ids=shape_id)
 def test_layernorm_degenerate_rows(shape):
     N, dt, fused, gemma = shape
-    inp = degenerate_inputs(N, dt, fused, gemma, PATTERNS, layernorm=True)
+    pats = patterns_for(dt)
+    inp = degenerate_inputs(N, dt, fused, gemma, pats, layernorm=True)
     offset = 1.0 if gemma else 0.0
     got = gpu_ln(inp, dt, LN_EPS, offset, fused)
     check_ln(inp, dt, LN_EPS, offset, fused, got)
@@ -156,7 +201,7 @@ def test_layernorm_degenerate_rows(shape):
         # With N a power of two the float32 mean of the constant row is exact
         # (3 N and 1/N are), so the variance is exactly 0, xhat = 0 and y is
         # beta itself.
-        i = PATTERNS.index("constant")
+        i = pats.index("constant")
         assert got["mean"][i] == 3.0
         assert np.array_equal(got["y"][i], inp["beta"]), "constant row: y must equal beta"
     if N == 1:
