@@ -302,6 +302,13 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             int target = is_fp8_op(op) || (rows_per_cu >= 8 && rows_per_cu < 32) ? 256 : 128;
             if (is_ln_op(op))
                 target = (int)std::max<int64_t>(256, nchunks / 4);
+            // fp32 rows with at least 8 per compute unit: two chunks per lane
+            // (measured on MI355X against the 128/256 target: 16384 x 6144
+            // 127.6 vs 132.7 us, 2048 x 6144 18.8 vs 19.9, 16384 x 4096 86.0
+            // vs 88.4, 8192 x 2048 23.7 vs 24.2; at 4 rows per unit it loses,
+            // 1024 x 4096 8.3 vs 6.8 us)
+            else if (dtype == RMSNORM_F32 && !is_fp8_op(op) && rows_per_cu >= 8)
+                target = (int)std::max<int64_t>(64, nchunks / 2);
             // backward: w in registers with one chunk per lane (the pages'
             // layout), else gamma re-read per row.  Measured on MI355X, gamma
             // per row with two chunks per lane and one row ahead beats w in
