@@ -522,3 +522,21 @@ def test_override_round_trip():
     with rn.plan_override(rn.OP_FWD, path=rn.PATH_ROWS, vec=8, team=64, threads=256):
         with pytest.raises(rn.RMSNormError):
             plan(rn.OP_FWD, 10, 4096, vec_ok=False)
+
+
+@pytest.mark.parametrize("M,N,fused,chunks", [
+    (16384, 6144, False, 2), (2048, 6144, False, 2), (8192, 2048, False, 2), (4096, 6144, True, 2),
+    (1024, 4096, False, None), (1024, 8192, False, None),
+])
+def test_fp32_forward_two_chunks_from_8_rows_per_cu(M, N, fused, chunks):
+    """fp32 forwards with at least 8 rows per compute unit take two chunks per
+    lane; with fewer (4 here) they keep the fewer, fuller lanes."""
+    p = plan(rn.OP_FUSED_ADD_FWD if fused else rn.OP_FWD, M, N, rn.F32)
+    if chunks is not None:
+        assert (p["threads"], p["chunks"]) == (N // 4 // 2, 2)
+    else:
+        assert p["chunks"] > 2
+    if (M, N, fused) == (16384, 6144, False):
+        # not for the fp8 forward (256 threads) or LayerNorm (N / 16 threads)
+        assert plan(rn.OP_FWD_FP8, M, N, rn.F32)["threads"] == 256
+        assert plan(rn.OP_LN_FWD, M, N, rn.F32)["threads"] == 384
