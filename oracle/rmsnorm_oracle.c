@@ -42,7 +42,7 @@
  * such an output:
  *     t_ij   = y_ij * scale              (scale: the caller's float32 factor)
  *     code_ij = E4M3(t_ij)               nearest, ties to even, saturating
- *     amax   = max_ij |y_ij|             (before scaling)
+ *     amax   = max_ij |y_ij|             (before scaling; NaN if any y_ij is NaN)
  * E4M3 is the OCP "FN" format: 1 sign bit, 4 exponent bits with bias 7,
  * 3 mantissa bits, no infinities, largest finite 448 = 1.75 * 2^8, smallest
  * normal 2^-6, subnormals m * 2^-9 (m = 1..7); codes 0x7F / 0xFF are NaN.
@@ -428,7 +428,8 @@ int oracle_fwd_fp8(int dt, const void *v, const void *gamma, int64_t M, int64_t 
         return ORACLE_EINVAL;
     const double e = (double)eps, off = (double)offset, sc = (double)scale;
     double amax = 0.0;
-#pragma omp parallel for schedule(static) reduction(max : amax)
+    int any_nan = 0; /* a NaN y makes amax NaN: the window saw a non-number */
+#pragma omp parallel for schedule(static) reduction(max : amax) reduction(|| : any_nan)
     for (int64_t i = 0; i < M; ++i) {
         const double rstd = row_rstd(dt, v, i, N, e);
         if (rstd64)
@@ -436,7 +437,9 @@ int oracle_fwd_fp8(int dt, const void *v, const void *gamma, int64_t M, int64_t 
         for (int64_t j = 0; j < N; ++j) {
             const double y = load_elem(dt, v, i * N + j) * rstd * scale_w(dt, gamma, j, off);
             const double t = y * sc;
-            if (fabs(y) > amax)
+            if (isnan(y))
+                any_nan = 1;
+            else if (fabs(y) > amax)
                 amax = fabs(y);
             code[i * N + j] = e4m3_from_double(t);
             /* t * (1 -+ tol) toward / away from zero: the lower and upper ends
@@ -450,7 +453,7 @@ int oracle_fwd_fp8(int dt, const void *v, const void *gamma, int64_t M, int64_t 
         }
     }
     if (amax64)
-        *amax64 = amax;
+        *amax64 = any_nan ? NAN : amax;
     return ORACLE_OK;
 }
 

@@ -25,6 +25,9 @@ mismatch.  What pins what:
   ln_identities        LayerNorm: sum dx = 0, sum xhat dx = N c2 rstd^3 eps, normalised mean / mean square
   ln_closed_forms      LayerNorm: N = 1, constant rows, shift invariance, offset, no gamma/beta
   ln_torch_fp64        torch.nn.functional.layer_norm in float64 with autograd
+  floor_magnitudes     the row magnitudes behind the tolerance floor (c, S; LayerNorm's four
+                       row statistics): triangle-inequality bounds and their equality cases,
+                       scaling in dy and v (their exact values are in the golden fixtures)
 """
 
 from __future__ import annotations
@@ -377,6 +380,17 @@ def fp8_forward(lib):
         ts = np.clip(np.abs(t), 0, 448).ravel()
         nearest = np.min(np.abs(grid[None, :] - ts[:, None]), axis=1)
         assert np.all(np.abs(np.abs(dec(out["code"])).ravel() - ts) <= nearest)
+    # a NaN input: IEEE propagation makes its row's rstd and every y of the row
+    # NaN, so the row's codes are NaN codes (0x7F / 0xFF) and amax is NaN;
+    # the other rows are unchanged
+    x = rng.standard_normal((3, 8))
+    x[1, 5] = np.nan
+    out = oracle.fwd_fp8(x, None, "f64", 1e-6, 0.0, 4.0, lib=lib)
+    assert np.isnan(out["amax64"]) and np.isnan(out["rstd64"][1]) and not np.isnan(out["rstd64"][[0, 2]]).any()
+    assert np.all((out["code"][1] & 0x7F) == 0x7F)
+    rest = oracle.fwd_fp8(x[[0, 2]], None, "f64", 1e-6, 0.0, 4.0, lib=lib)
+    assert np.array_equal(out["code"][[0, 2]], rest["code"]) and rest["amax64"] == np.abs(
+        oracle.fwd(x[[0, 2]], None, "f64", 1e-6, 0.0, lib=lib)[0]).max()
 
 
 def _ln_loss_grads(x, gamma, beta, dy, eps, off, lib, r=None):
@@ -584,6 +598,7 @@ def golden(lib):
             np.testing.assert_allclose(out["dx64"].ravel(), c["dx"], rtol=1e-14, atol=1e-15, err_msg=name)
             np.testing.assert_allclose(out["dgamma64"], c["dgamma"], rtol=1e-14, atol=1e-15, err_msg=name)
             np.testing.assert_allclose(out["dbeta64"], c["dbeta"], rtol=0, atol=0, err_msg=name)
+            np.testing.assert_allclose(out["stats64"].ravel(), c["stats"], rtol=1e-14, atol=1e-15, err_msg=name)
             continue
         N = int(c["N"][0])
         eps, off = c["eps"][0], c["offset"][0]
@@ -604,6 +619,48 @@ def golden(lib):
         np.testing.assert_allclose(y.ravel(), c["y"], rtol=1e-15, atol=1e-16, err_msg=name)
         np.testing.assert_allclose(out["dx64"].ravel(), c["dx"], rtol=1e-14, atol=1e-16, err_msg=name)
         np.testing.assert_allclose(out["dgamma64"], c["dgamma"], rtol=1e-15, atol=1e-16, err_msg=name)
+        np.testing.assert_allclose(out["c64"], c["c"], rtol=1e-15, atol=1e-16, err_msg=name)
+        np.testing.assert_allclose(out["sabs64"], c["S"], rtol=1e-15, atol=1e-16, err_msg=name)
+
+
+def floor_magnitudes(lib):
+    """The magnitudes behind the tests' cancellation floor, by properties that
+    fix them: S = mean_j |g xhat| is at least |c| = |mean_j g xhat| (triangle
+    inequality) and equals it when every g xhat has one sign (dy = v, w > 0);
+    both scale with |dy| (S(a dy) = |a| S(dy)) and do not depend on the scale
+    of v at eps = 0.  LayerNorm's (mean |g|, mean |g xhat|) bound (|mean g|,
+    |mean g xhat|) the same way, with equality when g >= 0 and g xhat >= 0."""
+    rng = np.random.default_rng(41)
+    M, N = 6, 29
+    v = _rand(rng, (M, N))
+    dy = _rand(rng, (M, N))
+    gamma = np.abs(_rand(rng, (N,), 0.3)) + 0.5  # w > 0
+    out = oracle.bwd(dy, v, gamma, "f64", 1e-6, 0.0, lib=lib)
+    c, S = out["c64"], out["sabs64"]
+    assert np.all(S >= np.abs(c)) and np.all(S > 1.05 * np.abs(c)), (S, c)
+    same = oracle.bwd(v, v, gamma, "f64", 1e-6, 0.0, lib=lib)  # g xhat = w v^2 rstd >= 0
+    np.testing.assert_allclose(same["sabs64"], same["c64"], rtol=1e-14)
+    for a in (-3.0, 0.25):
+        sc = oracle.bwd(a * dy, v, gamma, "f64", 1e-6, 0.0, lib=lib)
+        np.testing.assert_allclose(sc["sabs64"], abs(a) * S, rtol=1e-14)
+        np.testing.assert_allclose(sc["c64"], a * c, rtol=1e-13)
+    big = oracle.bwd(dy, 8.0 * v, gamma, "f64", 0.0, 0.0, lib=lib)
+    small = oracle.bwd(dy, v, gamma, "f64", 0.0, 0.0, lib=lib)
+    np.testing.assert_allclose(big["sabs64"], small["sabs64"], rtol=1e-14)
+    # LayerNorm
+    st = oracle.ln_bwd(dy, v, gamma, "f64", 1e-5, 0.0, lib=lib)["stats64"]
+    assert np.all(st[:, 2] >= np.abs(st[:, 0])) and np.all(st[:, 3] >= np.abs(st[:, 1]))
+    assert np.all(st[:, 2] > 1.05 * np.abs(st[:, 0])) and np.all(st[:, 3] > 1.05 * np.abs(st[:, 1]))
+    dy_pos = np.abs(dy)
+    st_pos = oracle.ln_bwd(dy_pos, v, gamma, "f64", 1e-5, 0.0, lib=lib)["stats64"]
+    np.testing.assert_allclose(st_pos[:, 2], st_pos[:, 0], rtol=1e-14)  # g >= 0
+    # g xhat >= 0 when dy has the sign of (v - mean): dy = v - mean(v)
+    dy_al = v - v.mean(axis=1, keepdims=True)
+    st_al = oracle.ln_bwd(dy_al, v, gamma, "f64", 1e-5, 0.0, lib=lib)["stats64"]
+    np.testing.assert_allclose(st_al[:, 3], st_al[:, 1], rtol=1e-13)
+    st2 = oracle.ln_bwd(-2.0 * dy, v, gamma, "f64", 1e-5, 0.0, lib=lib)["stats64"]
+    np.testing.assert_allclose(st2[:, 2:], 2.0 * st[:, 2:], rtol=1e-14)
+    np.testing.assert_allclose(st2[:, :2], -2.0 * st[:, :2], rtol=1e-13)
 
 
 def storage_widening(lib):
@@ -788,5 +845,5 @@ ALL_PINS = [
     finite_differences, rms_invariant, orthogonality, closed_form_n1, constant_row, scale_invariance,
     offset_equivalence, fused_reductions, torch_fp64, golden, storage_widening, rounding, binary16, non_affine,
     e4m3_brute_force, e4m3_torch, fp8_forward,
-    ln_finite_differences, ln_identities, ln_closed_forms, ln_torch_fp64,
+    ln_finite_differences, ln_identities, ln_closed_forms, ln_torch_fp64, floor_magnitudes,
 ]

@@ -50,7 +50,8 @@ MUTATIONS = [
     ("e4m3_subnormal_boundary", "if (q < -6)\n        q = -6;", "if (q < -7)\n        q = -7;", False),
     ("e4m3_mantissa_offset", "const int m = (int)(r / ldexp(1.0, E - 3)) - 8;", "const int m = (int)(r / ldexp(1.0, E - 3)) - 7;", False),
     ("e4m3_decode_bias", "return s * ldexp(1.0 + m / 8.0, e - 7);", "return s * ldexp(1.0 + m / 8.0, e - 8);", False),
-    ("fp8_amax_after_scale", "if (fabs(y) > amax)\n                amax = fabs(y);", "if (fabs(t) > amax)\n                amax = fabs(t);", False),
+    ("fp8_amax_after_scale", "else if (fabs(y) > amax)\n                amax = fabs(y);", "else if (fabs(t) > amax)\n                amax = fabs(t);", False),
+    ("fp8_amax_drops_nan", "*amax64 = any_nan ? NAN : amax;", "*amax64 = amax;", False),
     ("fp8_scale_dropped", "const double t = y * sc;", "const double t = y;", False),
     ("fp8_bracket_swapped", "const double lo = t < 0 ? t * (1.0 + tol) : t * (1.0 - tol);",
      "const double lo = t < 0 ? t * (1.0 - tol) : t * (1.0 + tol);", False),
@@ -65,6 +66,15 @@ MUTATIONS = [
      "dgamma64[j] += d * (load_elem(dt, v, i * N + j) - mu[i]);", False),
     ("ln_wrong_row_mean", "const double xhat = (load_elem(dt, v, i * N + j) - mu[i]) * rs[i];",
      "const double xhat = (load_elem(dt, v, i * N + j) - mu[0]) * rs[i];", True),
+    # the magnitudes behind the tests' cancellation floor
+    ("sabs_missing_mean", "sabs64[i] = dabs / (double)N;", "sabs64[i] = dabs;", False),
+    ("sabs_signed", "dabs += fabs(g * xhat);", "dabs += g * xhat;", False),
+    ("sabs_drops_rstd", "dabs += fabs(g * xhat);", "dabs += fabs(g * load_elem(dt, v, i * N + j));", False),
+    ("ln_abs_g_unnormalised", "stats64[4 * i + 2] = ag / (double)N;", "stats64[4 * i + 2] = ag;", False),
+    ("ln_abs_gx_unnormalised", "stats64[4 * i + 3] = agx / (double)N;", "stats64[4 * i + 3] = agx;", False),
+    ("ln_abs_g_signed", "ag += fabs(g);", "ag += g;", False),
+    ("ln_abs_stats_swapped", "stats64[4 * i + 2] = ag / (double)N;\n            stats64[4 * i + 3] = agx / (double)N;",
+     "stats64[4 * i + 2] = agx / (double)N;\n            stats64[4 * i + 3] = ag / (double)N;", False),
     ("ln_dh_sign", "double d = rs[i] * (g - c1 - xhat * c2);\n                if (dh)\n                    d += load_elem",
      "double d = rs[i] * (g - c1 - xhat * c2);\n                if (dh)\n                    d -= load_elem", False),
 ]
@@ -78,6 +88,7 @@ PIN_ORDER = [
     oracle_pins.torch_fp64,
     oracle_pins.non_affine, oracle_pins.finite_differences,
     oracle_pins.ln_closed_forms, oracle_pins.ln_identities, oracle_pins.ln_torch_fp64, oracle_pins.ln_finite_differences,
+    oracle_pins.floor_magnitudes,
 ]
 
 
