@@ -207,3 +207,34 @@ def test_fp8_full_size(name):
                                            want_y=False)
     full = oracle.fwd_fp8(v_all, inp["gamma"], w.dtype, w.eps, w.offset, scale)
     assert abs(amax - full["amax64"]) <= TOL * full["amax64"], (amax, full["amax64"])
+
+
+# A NaN input makes its row's rstd and y NaN (IEEE propagation): that row's
+# codes are NaN codes (0x7F or 0xFF: the sign of a NaN is not fixed), the
+# other rows are unchanged, and amax reports the NaN.  Shapes cover the
+# narrow-row teams, the workgroup-team layouts (bf16, float32) and the looped
+# kernel, each with the NaN in a middle row.
+NAN_SHAPES = [(40, 128, "bf16"), (20, 4096, "bf16"), (12, 6144, "f32"), (6, 40000, "bf16")]
+
+
+@pytest.mark.parametrize("M,N,dt", NAN_SHAPES, ids=[f"{d}_{m}x{n}" for m, n, d in NAN_SHAPES])
+def test_fp8_nan_propagates(M, N, dt):
+    inp = make_inputs(M, N, dt)
+    bad_row = M // 2
+    x32 = np.asarray(inp["x"], dtype=np.uint16 if dt == "bf16" else np.float32).copy()
+    if dt == "bf16":
+        x32[bad_row, N // 3] = 0x7FC0  # bf16 quiet NaN
+    else:
+        x32[bad_row, N // 3] = np.nan
+    inp = dict(inp, x=x32)
+    code, rstd, amax, _ = run_fp8(inp, dt, 0.0, False, 16.0)
+    assert np.isnan(amax), f"amax {amax}: the NaN row was dropped"
+    assert np.isnan(rstd[bad_row])
+    assert np.all((code[bad_row] & 0x7F) == 0x7F), "NaN row: every code must be a NaN code"
+    keep = np.array([i for i in range(M) if i != bad_row])
+    ref = oracle.fwd_fp8(inp["x"][keep], inp["gamma"], dt, EPS, 0.0, 16.0, tol=TOL)
+    check_codes(code[keep], ref)
+    # the amax of the other rows alone is finite and matches the reference
+    sub = {k: (a[keep] if a.ndim == 2 else a) for k, a in inp.items()}
+    _, _, amax_ok, _ = run_fp8(sub, dt, 0.0, False, 16.0)
+    assert abs(amax_ok - ref["amax64"]) <= TOL * ref["amax64"]

@@ -11,11 +11,13 @@ import torch
 
 import oracle
 import transformer_normalization_rmsnorm_amd as rn
-from gpu_util import (CODE, check_backward, check_forward, from_dev, from_dev_opt,
+from gpu_util import (CODE, check_backward, check_forward, check_ln, from_dev, from_dev_opt,
                       gpu_backward, gpu_forward, in_f16, reference_h, to_dev)
 from rmsnorm_inputs import EPS, make_inputs
 
 pytestmark = pytest.mark.gpu
+
+LN_EPS = 1e-5
 
 # (M, N, dtype, fused, gemma)
 CASES = [
@@ -326,6 +328,61 @@ def test_in_place_fused_aliases():
     assert dx.data_ptr() == dh.data_ptr()
     torch.cuda.synchronize()
     check_backward(inp, dt, EPS, 0.0, from_dev(dx), from_dev(dg), v_full=reference_h(inp, dt), dh_full=inp["dh"])
+
+
+# Fused forwards on the looped path with h_out = residual: later passes must
+# read the h each lane stored, not x + residual (residual is h by then).
+# bf16 / fp32 N = 10001 at an odd storage offset take the per-element looped
+# kernel; bf16 N = 131072, aligned, the 16-byte one with chunks beyond those
+# staged in LDS.  Each op's plan is checked to be the looped one.
+IN_PLACE_LOOPED = [(24, 10001, "bf16", False), (24, 10001, "f32", False), (6, 131072, "bf16", True)]
+
+
+def _maybe_offset(t: torch.Tensor, aligned: bool, elems: int) -> torch.Tensor:
+    return t if aligned else _offset_view(t, elems)
+
+
+@pytest.mark.parametrize("M,N,dt,aligned", IN_PLACE_LOOPED,
+                         ids=[f"{d}_{m}x{n}" + ("" if a else "_unaligned") for m, n, d, a in IN_PLACE_LOOPED])
+def test_in_place_residual_looped(M, N, dt, aligned):
+    code = CODE[dt]
+    for op in (rn.OP_FUSED_ADD_FWD, rn.OP_FUSED_ADD_FWD_FP8, rn.OP_LN_FUSED_ADD_FWD):
+        assert rn.rmsnorm_query_plan(op, M, N, code, vec_ok=aligned)["path"] == rn.PATH_LOOP, op
+    inp = make_inputs(M, N, dt, fused=True)
+    x = _maybe_offset(to_dev(inp["x"], dt), aligned, 1)
+    g = _maybe_offset(to_dev(inp["gamma"], dt), aligned, 3)
+    # RMSNorm
+    r = _maybe_offset(to_dev(inp["residual"], dt), aligned, 1)
+    y, h, rstd = rn.rmsnorm_fused_add_fwd(x, r, g, EPS, 0.0, h_out=r)
+    assert h.data_ptr() == r.data_ptr()
+    torch.cuda.synchronize()
+    check_forward(inp, dt, EPS, 0.0, from_dev(y), from_dev(rstd), from_dev(h))
+    # fp8 output
+    r = _maybe_offset(to_dev(inp["residual"], dt), aligned, 1)
+    sc = torch.tensor([8.0], dtype=torch.float32, device="cuda")
+    am = torch.zeros(1, dtype=torch.float32, device="cuda")
+    y8, h, rstd = rn.rmsnorm_fused_add_fwd_fp8(x, r, g, sc, EPS, 0.0, amax=am, h_out=r)
+    torch.cuda.synchronize()
+    h_ref = reference_h(inp, dt)
+    assert np.array_equal(from_dev(h), h_ref), "fp8 fused: h differs"
+    ref = oracle.fwd_fp8(h_ref, inp["gamma"], dt, EPS, 0.0, 8.0, tol=1e-5)
+    codes = y8.view(torch.uint8).cpu().numpy()
+    ok = (codes == ref["code_lo"]) | (codes == ref["code_hi"])
+    assert ok.all(), f"fp8 fused: {int((~ok).sum())} codes outside the tolerance interval"
+    assert abs(float(am.item()) - ref["amax64"]) <= 1e-5 * ref["amax64"]
+    # LayerNorm, forward in place then its backward
+    lin = make_inputs(M, N, dt, fused=True, layernorm=True)
+    xl = _maybe_offset(to_dev(lin["x"], dt), aligned, 1)
+    gl = _maybe_offset(to_dev(lin["gamma"], dt), aligned, 3)
+    bl = _maybe_offset(to_dev(lin["beta"], dt), aligned, 5)
+    rl = _maybe_offset(to_dev(lin["residual"], dt), aligned, 1)
+    yl, hl, mean, lrstd = rn.layernorm_fused_add_fwd(xl, rl, gl, bl, LN_EPS, 0.0, h_out=rl)
+    assert hl.data_ptr() == rl.data_ptr()
+    dxl, dgl, dbl = rn.layernorm_fused_add_bwd(to_dev(lin["dy"], dt), to_dev(lin["dh"], dt), hl, gl, mean, lrstd,
+                                               LN_EPS, 0.0)
+    torch.cuda.synchronize()
+    got = {"y": yl, "h": hl, "mean": mean, "rstd": lrstd, "dx": dxl, "dg": dgl, "db": dbl}
+    check_ln(lin, dt, LN_EPS, 0.0, True, {k: from_dev(v) for k, v in got.items()})
 
 
 def test_workspace_too_small_is_refused_before_launch():

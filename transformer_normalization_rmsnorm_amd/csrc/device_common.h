@@ -335,22 +335,27 @@ __device__ __forceinline__ float team_sum(float v)
     return v;
 }
 
-// Maximum over an aligned group of TEAM lanes, by the same exchanges as team_sum.
+// Maximum that propagates NaN: NaN when either operand is NaN.  fmaxf returns
+// the other operand for a NaN, which would hide a NaN output from an amax.
+__device__ __forceinline__ float max_nan(float a, float b) { return (a > b || a != a) ? a : b; }
+
+// Maximum over an aligned group of TEAM lanes, by the same exchanges as
+// team_sum; NaN in any lane gives NaN.
 template <int TEAM>
 __device__ __forceinline__ float team_max(float v)
 {
     static_assert(TEAM == 8 || TEAM == 16 || TEAM == 32 || TEAM == 64, "team size");
-    v = fmaxf(v, dpp<kDppQuadXor1>(v));
-    v = fmaxf(v, dpp<kDppQuadXor2>(v));
-    v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+    v = max_nan(v, dpp<kDppQuadXor1>(v));
+    v = max_nan(v, dpp<kDppQuadXor2>(v));
+    v = max_nan(v, dpp<kDppRowHalfMirror>(v));
     if constexpr (TEAM >= 16)
-        v = fmaxf(v, dpp<kDppRowMirror>(v));
+        v = max_nan(v, dpp<kDppRowMirror>(v));
     if constexpr (TEAM >= 32)
-        v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), kSwizzleXor16)));
+        v = max_nan(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), kSwizzleXor16)));
     if constexpr (TEAM == 64) {
         const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
         const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-        v = fmaxf(lo, hi);
+        v = max_nan(lo, hi);
     }
     return v;
 }
@@ -408,8 +413,8 @@ __device__ __forceinline__ void block_sum2(float &a, float &b, float *slot, int 
     b = sb;
 }
 
-// Maximum over the whole workgroup (as block_sum; `slot` holds 16 floats and
-// must not be in use by a concurrent block_sum).
+// Maximum over the whole workgroup, NaN-propagating (as block_sum; `slot`
+// holds 16 floats and must not be in use by a concurrent block_sum).
 __device__ __forceinline__ float block_max(float v, float *slot, int threads)
 {
     v = team_max<64>(v);
@@ -421,7 +426,7 @@ __device__ __forceinline__ float block_max(float v, float *slot, int threads)
     lds_barrier();
     float s = slot[0];
     for (int i = 1; i < nw; ++i)
-        s = fmaxf(s, slot[i]);
+        s = max_nan(s, slot[i]);
     return s;
 }
 
@@ -430,17 +435,19 @@ __device__ __forceinline__ float block_max(float v, float *slot, int threads)
 // OCP E4M3 ("FN") codes of V float32 values times `scale`, nearest even,
 // saturating at +-448, written with one store of V bytes (nontemporal like the
 // other row outputs).  The gfx950 pack conversion rounds to nearest even but
-// turns magnitudes past the format's range into NaN, so values are clamped to
-// +-448 (the largest finite code) first.  `am` accumulates max |f| (before
-// scaling).
+// turns magnitudes past the format's range into NaN, so finite magnitudes
+// beyond 448 (the largest finite code) are clamped first; a NaN passes the
+// comparison unchanged and is written as a NaN code.  `am` accumulates max |f|
+// (before scaling), NaN-propagating.
 template <int V>
 __device__ __forceinline__ void store_e4m3(uint8_t *p, const float (&f)[V], float scale, float &am)
 {
     float t[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-        am = fmaxf(am, fabsf(f[e]));
-        t[e] = fminf(fmaxf(f[e] * scale, -448.0f), 448.0f);
+        am = max_nan(am, fabsf(f[e]));
+        const float s = f[e] * scale;
+        t[e] = fabsf(s) > 448.0f ? copysignf(448.0f, s) : s;
     }
     if constexpr (V == 1) {
         const int w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], 0.0f, 0, false);

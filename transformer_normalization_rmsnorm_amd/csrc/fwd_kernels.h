@@ -262,9 +262,12 @@ __global__ void __launch_bounds__(fwd_rows_bound_rule(TEAM, K)) fwd_rows_kernel(
 // Lane t owns the chunks t, t + nt, ...  Its first KS chunks are loaded once,
 // in the first pass, and wait in LDS (each lane reads back only its own, so no
 // barrier) for the later passes; chunks beyond them are read again from
-// memory (from cache), h being formed again from x and r.  The KS chunks are
-// loaded unconditionally, a chunk past the row's end re-reading its last one,
-// so that their loads stay in flight together.
+// memory (from cache): x, or for fused-add the h chunk the lane itself stored
+// in pass 1.  h may overwrite r, so forming x + r again would read h in place
+// of r; the lane's own earlier store is what its later load of the same
+// address returns.  The KS chunks are loaded unconditionally, a chunk past
+// the row's end re-reading its last one, so that their loads stay in flight
+// together.
 template <typename T, int V, bool FUSED, bool F8, bool LN, int KS>
 __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
 {
@@ -286,7 +289,7 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
         return reinterpret_cast<C *>(fwd_lds + ((size_t)j * nt + threadIdx.x) * sizeof(C));
     };
 
-    // chunk c of the row at base: x, or round(x + r) for fused-add
+    // chunk c of the row at base: x, or round(x + r) for fused-add (pass 1)
     auto row_chunk = [&](int64_t base, int c) __attribute__((always_inline)) {
         C v;
         v.load_cached(x + base + (int64_t)c * V);
@@ -299,6 +302,15 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
                 f[e] = v.get(e) + rc.get(e);
             v.set(f);
         }
+        return v;
+    };
+    // chunk c again in a later pass: x, or the h this lane stored in pass 1
+    auto row_chunk_again = [&](int64_t base, int c) __attribute__((always_inline)) {
+        C v;
+        if constexpr (FUSED)
+            v.load_cached(h + base + (int64_t)c * V);
+        else
+            v.load_cached(x + base + (int64_t)c * V);
         return v;
     };
 
@@ -356,7 +368,7 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
                     dev2(*staged(j));
             }
             for (int c = (int)threadIdx.x + KS * nt; c < nchunks; c += nt)
-                dev2(row_chunk(base, c));
+                dev2(row_chunk_again(base, c));
             ss = block_sum(s2, red[parity], a.threads);
             parity ^= 1;
         }
@@ -412,7 +424,7 @@ __global__ void __launch_bounds__(1024) fwd_loop_kernel(FwdArgs a)
                 out(*staged(j), c);
         }
         for (int c = (int)threadIdx.x + KS * nt; c < nchunks; c += nt)
-            out(row_chunk(base, c), c);
+            out(row_chunk_again(base, c), c);
     }
     if constexpr (F8)
         write_amax_part(am, a);

@@ -40,7 +40,8 @@ hipError_t launch_finalize(int dtype, const float *partials, int64_t programs, i
     }
 }
 
-// *amax = max(*amax, max_p part[p]), one workgroup.  The partials are read as
+// *amax = max(*amax, max_p part[p]), one workgroup; a NaN in any partial (or
+// in *amax) gives NaN.  The partials are read as
 // float4 with kAmaxLoads independent loads per lane in flight, so a round
 // covers kAmaxThreads * kAmaxLoads * 4 partials for one memory latency (a
 // dependent loop of scalar loads cost one latency per 256 partials: about 20
@@ -66,14 +67,14 @@ __global__ void __launch_bounds__(kAmaxThreads) amax_finalize_kernel(const float
         for (int u = 0; u < kAmaxLoads; ++u) {
             const int64_t i = b + (int64_t)u * kAmaxThreads + threadIdx.x;
             if (i < P4)
-                m = fmaxf(m, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+                m = max_nan(m, max_nan(max_nan(v[u].x, v[u].y), max_nan(v[u].z, v[u].w)));
         }
     }
     for (int64_t i = P4 * 4 + threadIdx.x; i < P; i += kAmaxThreads)
-        m = fmaxf(m, part[i]);
+        m = max_nan(m, part[i]);
     m = block_max(m, slot, kAmaxThreads);
     if (threadIdx.x == 0)
-        *amax = fmaxf(*amax, m);
+        *amax = max_nan(*amax, m);
 }
 
 hipError_t launch_amax_finalize(const float *part, int64_t programs, float *amax, hipStream_t s)
