@@ -10,8 +10,13 @@ import torch
 import oracle
 import transformer_normalization_rmsnorm_amd as rn
 from rmsnorm_inputs import BF16, F16, bf16_bits_to_f32
-from tolerance import (DGAMMA_TOL, cancel_scale, check_bf16, check_f16,
-                       check_f32, dgamma_error)
+from tolerance import (DGAMMA_TOL, FLOOR_BUDGET, FLOOR_FACTOR, LN_FLOOR_BUDGET, SMALL_ROW,
+                       budget_for, cancel_scale, check_bf16, check_f16, check_f32,
+                       dgamma_error, floor_within_budget, log_report)
+
+# Marker for checks whose rows are built to cancel (degenerate rows): the
+# floor's use is reported but not bounded.
+UNBOUNDED = None
 
 DEV = "cuda:0"
 TORCH_DTYPE = {BF16: torch.bfloat16, F16: torch.float16, "f32": torch.float32}
@@ -44,11 +49,27 @@ def widen(a: np.ndarray, dtype: str) -> np.ndarray:
     return (bf16_bits_to_f32(a) if dtype == BF16 else np.asarray(a)).astype(np.float64)
 
 
-def check_values(what, got, ref64, dtype, scale=None):
+def check_values(what, got, ref64, dtype, scale=None, budget=FLOOR_BUDGET):
+    """got against ref64 by the storage type's rule.  scale: the cancellation
+    scale s (None: no floor); the fp32 rule applies F32_FLOOR to it.  budget:
+    the largest fraction of elements the floor may decide, per storage type
+    (a dict) or one number (UNBOUNDED: report only); rows of at most
+    SMALL_ROW elements are not bounded."""
     check = {BF16: check_bf16, F16: check_f16}.get(dtype, check_f32)
-    r = check(what, got, ref64, scale=scale)
+    sc = None if scale is None else np.asarray(scale, dtype=np.float64) * FLOOR_FACTOR[dtype]
+    ref_arr = np.asarray(ref64)
+    N = ref_arr.shape[-1] if ref_arr.ndim >= 1 and ref_arr.size else 0
+    b = None if scale is None else budget_for(budget, dtype, N if ref_arr.ndim == 2 else SMALL_ROW + 1)
+    r = check(what, got, ref64, scale=sc)
+    log_report(r, dtype, b)
     assert r.ok, str(r)
+    assert floor_within_budget(r, b), f"floor decides too many elements ({b}): {r}"
     return r
+
+
+def check_stat(what, got, ref64, scale=None, budget=FLOOR_BUDGET):
+    """A float32 statistic (rstd, mean) by the float32 rule; scale as check_values."""
+    return check_values(what, got, ref64, "f32", scale=scale, budget=budget)
 
 
 def check_forward(inp, dtype, eps, offset, y, rstd, h=None, rows=None):
@@ -66,9 +87,7 @@ def check_forward(inp, dtype, eps, offset, y, rstd, h=None, rows=None):
     if y is not None:
         reports.append(check_values("y", y, y64, dtype))
     if rstd is not None:
-        rr = check_f32("rstd", rstd, rstd64)
-        assert rr.ok, str(rr)
-        reports.append(rr)
+        reports.append(check_stat("rstd", rstd, rstd64))
     return reports
 
 
@@ -78,7 +97,7 @@ def reference_h(inp, dtype, eps=1e-6, offset=0.0):
     return h
 
 
-def check_backward(inp, dtype, eps, offset, dx, dgamma, *, v_full, dh_full=None, rows=None):
+def check_backward(inp, dtype, eps, offset, dx, dgamma, *, v_full, dh_full=None, rows=None, budget=FLOOR_BUDGET):
     """Compare GPU backward outputs with the reference.
 
     v_full: the forward input from the reference side: x, or reference_h() for
@@ -89,12 +108,12 @@ def check_backward(inp, dtype, eps, offset, dx, dgamma, *, v_full, dh_full=None,
     v = sel(v_full)
     dy = sel(inp["dy"])
     dh = None if dh_full is None else sel(dh_full)
-    out = oracle.bwd(dy, v, g, dtype, eps, offset, dh=dh, want_dgamma=rows is None)
+    out = oracle.bwd(dy, v, g, dtype, eps, offset, dh=dh, want_dgamma=rows is None and dgamma is not None)
     rstd64 = 1.0 / np.sqrt(np.mean(widen(v, dtype) ** 2, axis=1) + float(np.float32(eps)))
     g_wide = np.ones(v.shape[1]) if g is None else widen(g, dtype)
     s = cancel_scale(widen(v, dtype), g_wide, widen(dy, dtype), rstd64, out["c64"], out["sabs64"], offset,
                      None if dh is None else widen(dh, dtype))
-    reports = [check_values("dx", dx, out["dx64"], dtype, scale=s)]
+    reports = [check_values("dx", dx, out["dx64"], dtype, scale=s, budget=budget)]
     if g is None:
         assert dgamma is None
     elif dgamma is not None:
@@ -157,7 +176,7 @@ def gpu_ln(inp, dt, eps, offset, fused, stats="gpu", affine=True, bias=True):
     return {k: (None if v is None else from_dev(v)) for k, v in out.items()}
 
 
-def check_ln(inp, dt, eps, offset, fused, got, affine=True, bias=True, grads=True):
+def check_ln(inp, dt, eps, offset, fused, got, affine=True, bias=True, grads=True, budget=LN_FLOOR_BUDGET):
     """Compare LayerNorm results with the reference.
 
     Rules as for RMSNorm: bf16 within 2 ulp of the rounded reference, float32
@@ -180,11 +199,9 @@ def check_ln(inp, dt, eps, offset, fused, got, affine=True, bias=True, grads=Tru
     bw = widen(beta, dt) if beta is not None else np.zeros(vw.shape[1])
     mabs = np.abs(vw).mean(1)
     s_y = rstd64[:, None] * np.abs(w) * (np.abs(vw) + mabs[:, None]) + np.abs(bw)
-    check_values("y", got["y"], y64, dt, scale=s_y)
-    rr = check_f32("rstd", got["rstd"], rstd64)
-    assert rr.ok, str(rr)
-    rm = check_f32("mean", got["mean"], mean64, scale=mabs)
-    assert rm.ok, str(rm)
+    check_values("ln y", got["y"], y64, dt, scale=s_y, budget=budget)
+    check_stat("ln rstd", got["rstd"], rstd64)
+    check_stat("ln mean", got["mean"], mean64, scale=mabs, budget=budget)
     dh = inp["dh"] if fused else None
     out = oracle.ln_bwd(inp["dy"], v, g, dt, eps, offset, dh=dh, want_dgamma=grads, want_dbeta=grads)
     st = out["stats64"]
@@ -193,7 +210,7 @@ def check_ln(inp, dt, eps, offset, fused, got, affine=True, bias=True, grads=Tru
     s_dx = rstd64[:, None] * (np.abs(gg) + st[:, 2:3] + np.abs(xhat) * (np.abs(st[:, 1:2]) + st[:, 3:4]))
     if dh is not None:
         s_dx = s_dx + np.abs(widen(dh, dt))
-    r_dx = check_values("dx", got["dx"], out["dx64"], dt, scale=s_dx)
+    r_dx = check_values("ln dx", got["dx"], out["dx64"], dt, scale=s_dx, budget=budget)
     if not grads:
         return r_dx
     if affine:

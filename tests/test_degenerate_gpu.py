@@ -34,7 +34,7 @@ import torch
 
 import oracle
 import transformer_normalization_rmsnorm_amd as rn
-from gpu_util import (check_backward, check_forward, check_ln, from_dev,
+from gpu_util import (UNBOUNDED, check_backward, check_forward, check_ln, from_dev,
                       gpu_backward, gpu_forward, gpu_ln, reference_h, to_dev)
 from rmsnorm_inputs import make_inputs, storage_to_f32, to_storage
 from tolerance import check_f32
@@ -148,7 +148,10 @@ def run_rmsnorm(N, dt, fused, gemma, eps, patterns):
     dx, dg = gpu_backward(inp, dt, eps, offset, out, fused)
     torch.cuda.synchronize()
     dx, dg = from_dev(dx), from_dev(dg)
-    check_backward(inp, dt, eps, offset, dx, dg, v_full=v_ref, dh_full=inp["dh"] if fused else None)
+    # rows built to cancel (constant rows, one-hot rows, eps-dominated rows):
+    # the floor's use is reported, not bounded
+    check_backward(inp, dt, eps, offset, dx, dg, v_full=v_ref, dh_full=inp["dh"] if fused else None,
+                   budget=UNBOUNDED)
     return inp, y, rstd, dx
 
 
@@ -196,7 +199,7 @@ def test_layernorm_degenerate_rows(shape):
     inp = degenerate_inputs(N, dt, fused, gemma, pats, layernorm=True)
     offset = 1.0 if gemma else 0.0
     got = gpu_ln(inp, dt, LN_EPS, offset, fused)
-    check_ln(inp, dt, LN_EPS, offset, fused, got)
+    check_ln(inp, dt, LN_EPS, offset, fused, got, budget=UNBOUNDED)
     if N & (N - 1) == 0:
         # With N a power of two the float32 mean of the constant row is exact
         # (3 N and 1/N are), so the variance is exactly 0, xhat = 0 and y is

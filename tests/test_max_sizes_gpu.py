@@ -28,6 +28,8 @@ pytestmark = pytest.mark.gpu
 EPS = 1e-6
 LN_EPS = 1e-5
 
+LONG_ROW_BUDGET = {"bf16": 1e-3, "f16": 1e-3, "f32": 4e-2}
+
 LONG = [
     (3, rn.MAX_N, "bf16", False),
     (2, rn.MAX_N, "f32", True),
@@ -46,7 +48,10 @@ def test_longest_rows(M, N, dt, fused):
     dx, dg = gpu_backward(inp, dt, EPS, 0.0, out, fused)
     torch.cuda.synchronize()
     v = reference_h(inp, dt, EPS, 0.0) if fused else inp["x"]
-    check_backward(inp, dt, EPS, 0.0, from_dev(dx), from_dev(dg), v_full=v, dh_full=inp["dh"] if fused else None)
+    # the row dot sums 2^24 float32 terms, so c carries a larger float32 error
+    # and more elements need the floor (1.3% measured for fused float32)
+    check_backward(inp, dt, EPS, 0.0, from_dev(dx), from_dev(dg), v_full=v, dh_full=inp["dh"] if fused else None,
+                   budget=LONG_ROW_BUDGET)
     del out, dx, dg
     print(f"layernorm {dt} {M}x{N} fused={fused}", flush=True)
     inp = make_inputs(M, N, dt, fused=fused, layernorm=True)
@@ -186,13 +191,9 @@ def test_statistics_only_forward_beyond_one_launch():
     assert lib.layernorm_fwd(x.data_ptr(), None, None, None, mean.data_ptr(), lrstd.data_ptr(), M, N, LN_EPS, 0.0,
                              rn.BF16, stream) == 0
     torch.cuda.synchronize()
-    from tolerance import check_f32
+    from gpu_util import check_stat, widen
     _, rstd64 = oracle.fwd(src, None, dt, EPS, 0.0, want_y=False)
-    r = check_f32("rstd", rstd[idx].cpu().numpy(), rstd64)
-    assert r.ok, str(r)
+    check_stat("rstd", rstd[idx].cpu().numpy(), rstd64)
     _, mean64, lrstd64 = oracle.ln_fwd(src, None, None, dt, LN_EPS, 0.0, want_y=False)
-    r = check_f32("layernorm rstd", lrstd[idx].cpu().numpy(), lrstd64)
-    assert r.ok, str(r)
-    from gpu_util import widen
-    r = check_f32("mean", mean[idx].cpu().numpy(), mean64, scale=np.abs(widen(src, dt)).mean(1))
-    assert r.ok, str(r)
+    check_stat("layernorm rstd", lrstd[idx].cpu().numpy(), lrstd64)
+    check_stat("mean", mean[idx].cpu().numpy(), mean64, scale=np.abs(widen(src, dt)).mean(1))

@@ -102,3 +102,49 @@ def test_f16_dgamma_rule():
     up = (one.view(np.uint16) + 1).view(np.float16)
     assert dgamma_error(up, ref, "f16") <= DGAMMA_TOL["f16"]
     assert dgamma_error((one.view(np.uint16) + 3).view(np.float16), ref, "f16") > DGAMMA_TOL["f16"]
+
+
+def test_floors_give_every_type_the_same_absolute_allowance():
+    """At a cancelling element (|dx| far below s) each storage type's rule
+    allows the same absolute error, 2^-20 s: the float32 error of the
+    difference does not depend on the storage type."""
+    from tolerance import BF16_FLOOR, F16_FLOOR, F32_FLOOR, F32_REL
+
+    s = 4.0  # a power of two: the 16-bit spacings are exact there
+    assert 2 * ulp_bf16(BF16_FLOOR * s) == 2 * ulp_f16(F16_FLOOR * s) == 2.0 ** -20 * s
+    assert abs(F32_REL * F32_FLOOR * s - 2.0 ** -20 * s) <= 1e-15 * 2.0 ** -20 * s
+    # float32: an error just inside 2^-20 s passes at a cancelling element, just outside fails
+    from gpu_util_cpu import check_values_cpu
+
+    ref = np.array([1e-9, 1.0])
+    scale = np.array([s, 1.0])
+    inside = np.array([1e-9 + 0.9 * 2.0 ** -20 * s, 1.0])
+    outside = np.array([1e-9 + 1.1 * 2.0 ** -20 * s, 1.0])
+    assert check_values_cpu(inside, ref, "f32", scale).ok
+    assert not check_values_cpu(outside, ref, "f32", scale).ok
+
+
+def test_floor_budget_counts_elements_the_floor_decides():
+    """floor_used counts the elements that pass only because of the floor; the
+    budget bounds it (a fraction of the elements plus two); rows of at most
+    four elements are not bounded."""
+    from tolerance import FLOOR_BUDGET, budget_for, floor_within_budget
+
+    assert budget_for(FLOOR_BUDGET, "bf16", 4096) == 1e-3 and budget_for(FLOOR_BUDGET, "f32", 4096) == 5e-3
+    assert budget_for(FLOOR_BUDGET, "f32", 4) is None and budget_for(None, "f32", 4096) is None
+    assert budget_for(0.25, "bf16", 100) == 0.25
+
+    n = 20000
+    ref = np.ones(n)
+    scale = np.ones(n)
+    got = ref.copy()
+    k = 30  # 30 elements at 1e-4 relative error: beyond 1e-5, inside the floor 2^-20 / 1e-5 * s
+    ref[:k] = 1e-4
+    got[:k] = 1e-4 + 5e-7
+    r = check_f32("budget", got.astype(np.float64), ref, scale=scale * (2.0 ** -20 / 1e-5))
+    assert r.ok and r.floor_used == k and r.pure_fails == k
+    assert not floor_within_budget(r, 1e-3)  # 30 > 0.001 * 20000 + 2
+    assert floor_within_budget(r, 1e-2) and floor_within_budget(r, None)
+    got[k - 10:k] = ref[k - 10:k]  # 20 left
+    r = check_f32("budget", got, ref, scale=scale * (2.0 ** -20 / 1e-5))
+    assert r.floor_used == 20 and floor_within_budget(r, 1e-3)
