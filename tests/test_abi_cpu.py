@@ -540,3 +540,49 @@ def test_fp32_forward_two_chunks_from_8_rows_per_cu(M, N, fused, chunks):
         # not for the fp8 forward (256 threads) or LayerNorm (N / 16 threads)
         assert plan(rn.OP_FWD_FP8, M, N, rn.F32)["threads"] == 256
         assert plan(rn.OP_LN_FWD, M, N, rn.F32)["threads"] == 384
+
+
+_LOG_SNIPPET = r"""
+import sys
+sys.path.insert(0, {root!r})
+import transformer_normalization_rmsnorm_amd as rn
+calls = [
+    (rn.OP_BWD, 4096, 4096, rn.BF16, 1), (rn.OP_BWD, 4096, 4096, rn.BF16, 1),   # same key twice
+    (rn.OP_BWD, 1024, 4096, rn.BF16, 1),                                        # same key, other M
+    (rn.OP_FWD, 4096, 4096, rn.BF16, 1), (rn.OP_FWD, 4096, 4097, rn.BF16, 1),   # N % 8 != 0: per-element
+    (rn.OP_FWD, 64, 4096, rn.BF16, 0), (rn.OP_FWD, 64, 4096, rn.BF16, 0),       # unaligned: per-element
+    (rn.OP_BWD, 8, 131072, rn.BF16, 1), (rn.OP_LN_BWD, 8, 4096, rn.F32, 1),     # looped; LayerNorm
+]
+for op, M, N, dt, vec_ok in calls:
+    rn.rmsnorm_query_plan(op, M, N, dt, vec_ok=bool(vec_ok), num_cus=256)
+"""
+
+
+def _run_logged(env_value):
+    import subprocess
+    import sys
+
+    env = dict(os.environ)
+    env.pop("RMSNORM_LOG", None)
+    if env_value is not None:
+        env["RMSNORM_LOG"] = env_value
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _LOG_SNIPPET.format(root=root)], env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return [ln for ln in r.stderr.splitlines() if ln.startswith("rmsnorm: ")]
+
+
+def test_plan_log_once_per_key():
+    """RMSNORM_LOG=1: one line per (op, path, access width, dtype, N), the
+    fallbacks marked with the reason; nothing without the variable or with 0."""
+    lines = _run_logged("1")
+    assert len(lines) == 6, "\n".join(lines)
+    assert sum("rmsnorm: bwd bf16 N=4096 " in ln for ln in lines) == 1
+    assert any("fwd bf16 N=4097" in ln and "N not a multiple" in ln for ln in lines)
+    assert any("fwd bf16 N=4096" in ln and "not 16-byte aligned" in ln for ln in lines)
+    assert any("bwd bf16 N=131072" in ln and "path=loop" in ln and "fallback: looped rows" in ln for ln in lines)
+    assert any(ln.startswith("rmsnorm: ln_bwd f32 N=4096") for ln in lines)
+    plain = [ln for ln in lines if "fallback" not in ln]
+    assert len(plain) == 3 and all("path=rows" in ln for ln in plain)
+    assert _run_logged(None) == [] and _run_logged("0") == []

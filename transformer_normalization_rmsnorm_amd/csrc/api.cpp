@@ -8,8 +8,11 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <set>
+#include <tuple>
 
 #include "layernorm.h"
 #include "rmsnorm_internal.h"
@@ -85,6 +88,52 @@ int check_common(int64_t M, int64_t N, int dtype, float eps, float offset)
     return RMSNORM_OK;
 }
 
+// One-time plan log.  RMSNORM_LOG (read once, when the library is loaded; a
+// value other than empty or "0" enables it) prints the plan a call takes, on
+// stderr, once per (op, path, access width, dtype, N): the analogue of
+// TransformerEngine PR #583's one-time warning with the type tuple when no
+// tuned configuration exists ("Description").  The looped and per-element
+// paths are such fallbacks here; their lines say so and why.
+const bool g_log_plans = [] {
+    const char *v = std::getenv("RMSNORM_LOG");
+    return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+}();
+std::mutex g_log_mu;
+std::set<std::tuple<int, int, int, int, int64_t>> g_logged;
+
+const char *op_name(int op)
+{
+    static const char *names[] = {"fwd", "fused_add_fwd", "bwd", "fused_add_bwd", "fwd_fp8", "fused_add_fwd_fp8",
+                                  "ln_fwd", "ln_fused_add_fwd", "ln_bwd", "ln_fused_add_bwd"};
+    return op >= 0 && op < 10 ? names[op] : "?";
+}
+
+const char *dtype_name(int dtype) { return dtype == RMSNORM_F32 ? "f32" : dtype == RMSNORM_BF16 ? "bf16" : "f16"; }
+
+void log_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, bool overridden, const rmsnorm_plan &p)
+{
+    {
+        std::lock_guard<std::mutex> lock(g_log_mu);
+        if (!g_logged.emplace(op, p.path, p.vec, dtype, N).second)
+            return;
+    }
+    const bool per_elem = p.vec == 1;
+    const char *why = "";
+    if (p.path == RMSNORM_PATH_LOOP)
+        why = per_elem ? " (fallback: looped rows, per-element access)" : " (fallback: looped rows, row too wide "
+                                                                          "for the register layouts)";
+    else if (per_elem)
+        why = vec_ok ? " (fallback: per-element access, N not a multiple of the 16-byte vector)"
+                     : " (fallback: per-element access, a pointer not 16-byte aligned)";
+    std::fprintf(stderr,
+                 "rmsnorm: %s %s N=%lld (first call M=%lld): path=%s vec=%d team=%d threads=%d chunks=%d depth=%d "
+                 "w_regs=%d rows_per_step=%d grid=%lld workspace=%lld%s%s\n",
+                 op_name(op), dtype_name(dtype), (long long)N, (long long)M,
+                 p.path == RMSNORM_PATH_LOOP ? "loop" : "rows", p.vec, p.team, p.threads, p.chunks, p.depth, p.w_regs,
+                 p.rows_per_step, (long long)p.grid, (long long)p.workspace_bytes, overridden ? " [override]" : "",
+                 why);
+}
+
 // Plan for this call: the selector's, or the override's layout fitted to it.
 int plan_for(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int cus, rmsnorm_plan *p)
 {
@@ -115,6 +164,8 @@ int plan_for(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int cus, rmsn
             return fail(RMSNORM_EINVAL, "override plan does not fit M=%lld N=%lld", (long long)M, (long long)N);
         *p = q;
     }
+    if (g_log_plans)
+        log_plan(op, M, N, dtype, vec_ok, o.set, *p);
     return RMSNORM_OK;
 }
 
