@@ -343,35 +343,115 @@ def practical_ceilings(torch, tensor_bytes: int, iters: int = 50):
     return {"tensor_bytes": n16 * 16, "copy_GBs": round(best["copy"], 1), "three_stream_GBs": round(best["three"], 1)}
 
 
-def cpu_baseline(w, seconds: float):
-    """The fp64 reference, as it stands, on the host cores (bounded run)."""
-    import numpy as np
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def _oracle_fwd_bwd_timers(w, lib):
+    """(fwd, bwd) closures running the fp64 reference on the workload's host arrays."""
     import oracle
-    from rmsnorm_inputs import algorithmic_bytes, make_workload_inputs
+    from rmsnorm_inputs import make_workload_inputs
 
-    lib = oracle.load()
     inp = make_workload_inputs(w)
-    fop, bop = ("fused_fwd", "fused_bwd") if w.fused else ("fwd", "bwd")
-    nbytes = algorithmic_bytes(fop, w.M, w.N, w.elem_bytes) + algorithmic_bytes(bop, w.M, w.N, w.elem_bytes)
+    if w.fused:
+        h, _, _ = oracle.fused_add_fwd(inp["x"], inp["residual"], inp["gamma"], w.dtype, w.eps, w.offset, lib=lib,
+                                       want_y=False)
+
+        def fwd():
+            oracle.fused_add_fwd(inp["x"], inp["residual"], inp["gamma"], w.dtype, w.eps, w.offset, lib=lib)
+
+        def bwd():
+            oracle.bwd(inp["dy"], h, inp["gamma"], w.dtype, w.eps, w.offset, dh=inp["dh"], lib=lib)
+    else:
+        def fwd():
+            oracle.fwd(inp["x"], inp["gamma"], w.dtype, w.eps, w.offset, lib=lib)
+
+        def bwd():
+            oracle.bwd(inp["dy"], inp["x"], inp["gamma"], w.dtype, w.eps, w.offset, lib=lib)
+    return fwd, bwd
+
+
+def _median_time(fn, seconds: float, min_runs: int = 3):
     times = []
     t_end = time.perf_counter() + seconds
-    while time.perf_counter() < t_end or len(times) < 1:
+    while time.perf_counter() < t_end or len(times) < min_runs:
         t0 = time.perf_counter()
-        if w.fused:
-            h, _, _ = oracle.fused_add_fwd(inp["x"], inp["residual"], inp["gamma"], w.dtype, w.eps, w.offset, lib=lib)
-            oracle.bwd(inp["dy"], h, inp["gamma"], w.dtype, w.eps, w.offset, dh=inp["dh"], lib=lib)
-        else:
-            oracle.fwd(inp["x"], inp["gamma"], w.dtype, w.eps, w.offset, lib=lib)
-            oracle.bwd(inp["dy"], inp["x"], inp["gamma"], w.dtype, w.eps, w.offset, lib=lib)
+        fn()
         times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
+    return statistics.median(times), len(times)
+
+
+def cpu_baseline(w, seconds: float, single_thread_workloads=("bf16_512x2048", "bf16_4096x4096", "bf16_1024x8192")):
+    """The fp64 reference, as it stands, on the host cores (bounded run):
+    forward and backward timed separately on the workload with every thread
+    the reference's OpenMP runtime uses, then with one thread on the smaller
+    workloads (median of at least 3 runs each)."""
+    import oracle
+    from rmsnorm_inputs import ALL_WORKLOADS, algorithmic_bytes
+
+    lib = oracle.load()
+    fop, bop = ("fused_fwd", "fused_bwd") if w.fused else ("fwd", "bwd")
+    fbytes = algorithmic_bytes(fop, w.M, w.N, w.elem_bytes)
+    bbytes = algorithmic_bytes(bop, w.M, w.N, w.elem_bytes)
+    threads = oracle.num_threads(lib)
+    fwd, bwd = _oracle_fwd_bwd_timers(w, lib)
+    tf, nf = _median_time(fwd, seconds / 2)
+    tb, nb = _median_time(bwd, seconds / 2)
+    single = {}
+    try:
+        oracle.set_num_threads(1, lib)
+        for name in single_thread_workloads:
+            ww = ALL_WORKLOADS[name]
+            f1, b1 = _oracle_fwd_bwd_timers(ww, lib)
+            t1f, _ = _median_time(f1, 0.0)
+            t1b, _ = _median_time(b1, 0.0)
+            fo, bo = ("fused_fwd", "fused_bwd") if ww.fused else ("fwd", "bwd")
+            single[name] = {"fwd_us": round(t1f * 1e6, 1), "bwd_us": round(t1b * 1e6, 1),
+                            "fwd_GBs": round(algorithmic_bytes(fo, ww.M, ww.N, ww.elem_bytes) / t1f / 1e9, 3),
+                            "bwd_GBs": round(algorithmic_bytes(bo, ww.M, ww.N, ww.elem_bytes) / t1b / 1e9, 3)}
+    finally:
+        oracle.set_num_threads(threads, lib)
+    t = tf + tb
     return {
-        "value": nbytes / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(lib), "kind": "oracle",
-        "sample": f"whole {w.name} workload (fwd + bwd, fp64 C reference, OpenMP), median of {len(times)} "
-                  f"runs in ~{seconds:.0f} s; {t * 1e6:.0f} us per fwd+bwd",
-        "us_per_call": t * 1e6,
+        "value": (fbytes + bbytes) / t / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
+        "sample": f"whole {w.name} workload, fp64 C reference (OpenMP, {threads} threads): forward median of "
+                  f"{nf} runs, backward median of {nb} runs, ~{seconds:.0f} s; value = compulsory bytes of fwd + "
+                  f"bwd / (fwd + bwd time); single_thread: the same reference on one thread, median of 3",
+        "us_per_call": t * 1e6, "fwd_us": round(tf * 1e6, 1), "bwd_us": round(tb * 1e6, 1),
+        "fwd_GBs": round(fbytes / tf / 1e9, 3), "bwd_GBs": round(bbytes / tb / 1e9, 3),
+        "single_thread": single,
     }
+
+
+def small_shape_launch_paths(lib, rn, torch, name: str = "bf16_512x2048", iters: int = 200):
+    """Forward and backward of a small, host-bound workload by direct launches
+    and by replay of a captured HIP graph of the same calls (cold buffers)."""
+    from rmsnorm_inputs import ALL_WORKLOADS, algorithmic_bytes
+
+    w = ALL_WORKLOADS[name]
+    S = Sets(w, lib, rn, torch, n_sets_for(w, True))
+    K = len(S.sets)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i in range(K):
+        S.fwd(i, st)
+    out = {"workload": name}
+    for op, fn in (("fwd", S.fwd), ("bwd", lambda i, s: S.bwd(i + K // 2, s))):
+        nbytes = algorithmic_bytes(op, w.M, w.N, w.elem_bytes)
+        d = time_direct(torch, fn, iters, 20)
+        g = time_graph(torch, fn, iters)
+        out[op] = {"direct_us": round(d, 3), "graph_us": round(g, 3),
+                   "direct_GBs": round(nbytes / (d * 1e3), 1), "graph_GBs": round(nbytes / (g * 1e3), 1)}
+    del S
+    torch.cuda.empty_cache()
+    return out
 
 
 def counters_traffic(ident: str):
@@ -496,6 +576,7 @@ def main():
     roofline["practical_peak"] = ceil["three_stream_GBs"]
     roofline["frac_of_practical"] = roofline["achieved"] / ceil["three_stream_GBs"]
 
+    small = small_shape_launch_paths(lib, rn, torch)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -516,7 +597,7 @@ def main():
         "fwd_GBs": round(cold["fwd_GBs"], 1), "bwd_GBs": round(cold["bwd_GBs"], 1),
         "fwd_pct_peak": round(cold["fwd_pct_peak"], 2), "bwd_pct_peak": round(cold["bwd_pct_peak"], 2),
         "bwd_main_us": round(main_us, 3), "finalize_us": round(cold["finalize_us"], 3),
-        "roofline": roofline, "cpu_baseline": cpu, "practical_ceilings": ceil,
+        "roofline": roofline, "cpu_baseline": cpu, "practical_ceilings": ceil, "small_shape_graph": small,
         "source_hash": source_hash(bwd_plan(rn, w)), "wall_s_timed_region": round(wall, 4),
     }
     if args.report:
