@@ -36,7 +36,8 @@
  *   - Ownership: the caller owns every buffer, including the backward
  *     workspace.  The library allocates no device memory, keeps no per-call
  *     state, never synchronises, and launches only on `stream` (NULL = the
- *     null stream), so every call may be captured into a HIP graph.
+ *     null stream), so every call may be captured into a HIP graph.  Its only
+ *     device memory is the fixed static scratch of rmsnorm_bwd_noalloc.
  *   - Errors: every function returns an rmsnorm_status.  All argument checks
  *     happen before any HIP call; a failed launch returns RMSNORM_EHIP.
  *     rmsnorm_last_error() gives a message for the calling thread's last
@@ -174,6 +175,27 @@ int rmsnorm_fused_add_bwd(const void *dy, const void *dh, const void *h, const v
                           int64_t M, int64_t N, float eps, float offset,
                           int dtype, rmsnorm_stream_t stream);
 
+/* Backward that allocates nothing, for callers that cannot call hipMalloc or
+ * hand over a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Arguments, results and checks are
+ * rmsnorm_bwd's without the workspace; the dgamma partial rows (and rstd, when
+ * it is recomputed) go to a library-owned static device buffer of
+ * RMSNORM_NOALLOC_SCRATCH_BYTES on each device, held until the process ends.
+ *   - A call whose workspace (rmsnorm_bwd_workspace_bytes, or its partial
+ *     rows alone when rstd is given) exceeds that size returns
+ *     RMSNORM_EWORKSPACE before any launch: at 256 compute units, rows up to
+ *     16384 elements with rstd given.
+ *   - Every call on a device shares that device's buffer, which keeps the last
+ *     call's contents: calls that may overlap on one device (other streams,
+ *     other threads) race and give undefined results.  Order them on one
+ *     stream.
+ *   - The first call on a device looks up the buffer's device address (no
+ *     allocation); making that call outside graph capture is safest. */
+#define RMSNORM_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int rmsnorm_bwd_noalloc(const void *dy, const void *x, const void *gamma, const float *rstd,
+                        void *dx, void *dgamma, int64_t M, int64_t N, float eps, float offset,
+                        int dtype, rmsnorm_stream_t stream);
+
 /* The two backward stages on their own, for callers that reduce the dgamma
  * partials themselves (for example across devices, in rank order) and for
  * per-stage timing.
@@ -260,8 +282,9 @@ const char *rmsnorm_last_error(void);
 /* The ABI version this header describes (RMSNORM_ABI_VERSION); a binding
  * checks it before use.  2: rmsnorm_plan gained w_regs.  3: fp8-output
  * forwards (ops 4 and 5).  4: LayerNorm (include/layernorm.h, ops 6-9).
- * 5: binary16 storage (RMSNORM_F16).  6: rmsnorm_plan gained rows_per_step. */
-#define RMSNORM_ABI_VERSION 6
+ * 5: binary16 storage (RMSNORM_F16).  6: rmsnorm_plan gained rows_per_step.
+ * 7: rmsnorm_bwd_noalloc. */
+#define RMSNORM_ABI_VERSION 7
 
 /* Longest row (elements) any entry point accepts. */
 #define RMSNORM_MAX_N (1 << 24)

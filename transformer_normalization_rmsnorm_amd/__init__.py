@@ -48,7 +48,7 @@ EXPORTS = (
     "rmsnorm_set_plan_override", "rmsnorm_status_string", "rmsnorm_last_error", "rmsnorm_version",
     "rmsnorm_fwd_fp8", "rmsnorm_fused_add_fwd_fp8", "rmsnorm_fwd_fp8_workspace_bytes",
     "layernorm_fwd", "layernorm_fused_add_fwd", "layernorm_bwd_workspace_bytes", "layernorm_bwd",
-    "layernorm_fused_add_bwd",
+    "layernorm_fused_add_bwd", "rmsnorm_bwd_noalloc",
 )
 
 
@@ -59,7 +59,7 @@ class RMSNormError(RuntimeError):
 
 
 # RMSNORM_ABI_VERSION of include/rmsnorm.h that this binding marshals.
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class Plan(ctypes.Structure):
@@ -85,6 +85,7 @@ def _bind(lib):
         "rmsnorm_fused_add_fwd": [vp, vp, vp, vp, vp, vp, i64, i64, f, f, i32, vp],
         "rmsnorm_bwd_workspace_bytes": [i64, i64, i32, ctypes.POINTER(sz)],
         "rmsnorm_bwd": [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, f, f, i32, vp],
+        "rmsnorm_bwd_noalloc": [vp, vp, vp, vp, vp, vp, i64, i64, f, f, i32, vp],
         "rmsnorm_fused_add_bwd": [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, f, f, i32, vp],
         "rmsnorm_bwd_partials": [vp, vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(i64), i64, i64, f, f, i32, vp],
         "rmsnorm_dgamma_finalize": [vp, i64, i64, vp, i32, vp],

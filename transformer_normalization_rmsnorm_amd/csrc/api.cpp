@@ -404,6 +404,43 @@ int do_bwd(const void *dy, const void *dh, const void *v, const void *gamma, con
     return do_finalize(static_cast<const float *>(workspace), programs, N, dgamma, dtype, stream);
 }
 
+// Fixed device scratch for rmsnorm_bwd_noalloc: the partial rows (and an
+// rstd recomputed when the caller has none) of one backward, for callers that
+// cannot allocate.  Each device holds its own copy for the life of the
+// process.  In host code the array's name is only a stand-in for the device
+// symbol: the device address of each device's copy comes from
+// hipGetSymbolAddress, once per device (with that device current), and only
+// that address is ever passed to a kernel.  Nothing in it needs clearing: the
+// backward writes every partial row and every recomputed rstd it later reads.
+constexpr size_t kScratchBytes = RMSNORM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(RMSNORM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(RMSNORM_EHIP, "device %d out of range", dev);
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || p == nullptr)
+                return fail(RMSNORM_EHIP, "device address of the scratch buffer on device %d: %s", dev,
+                            hipGetErrorString(e));
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return RMSNORM_OK;
+}
+
 int workspace_for(int op_a, int op_b, int64_t M, int64_t N, int dtype, size_t *bytes)
 {
     if (!bytes)
@@ -537,6 +574,23 @@ int rmsnorm_fused_add_bwd(const void *dy, const void *dh, const void *h, const v
     // With no incoming residual gradient the fused backward is the plain one on h.
     return do_bwd(dy, dh, h, gamma, rstd, dx, dgamma, workspace, workspace_bytes, M, N, eps, offset, dtype,
                   stream);
+}
+
+int rmsnorm_bwd_noalloc(const void *dy, const void *x, const void *gamma, const float *rstd, void *dx, void *dgamma,
+                        int64_t M, int64_t N, float eps, float offset, int dtype, rmsnorm_stream_t stream)
+{
+    void *ws = nullptr;
+    int rc = scratch_address(&ws);
+    if (rc)
+        return rc;
+    rc = do_bwd(dy, nullptr, x, gamma, rstd, dx, dgamma, ws, kScratchBytes, M, N, eps, offset, dtype, stream);
+    if (rc == RMSNORM_EWORKSPACE) {
+        char why[sizeof g_err];
+        std::snprintf(why, sizeof why, "%s", g_err);
+        return fail(rc, "rmsnorm_bwd_noalloc: this call needs more than the fixed %zu-byte scratch (%s); use "
+                        "rmsnorm_bwd with a workspace", kScratchBytes, why);
+    }
+    return rc;
 }
 
 int rmsnorm_bwd_partials(const void *dy, const void *v, const void *gamma, const float *rstd, const void *dh,
