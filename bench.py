@@ -20,6 +20,12 @@ Other modes:
   --report PATH      write a detailed JSON report (every op, cold/hot, direct/graph)
   --all-workloads    add every workload to the report
   --counters-run     a short fixed sequence of launches for rocprofv3 --pmc runs (--workload NAME)
+  --timeline-run     warmup, then a few timed steps only, for a rocprofv3 --kernel-trace timeline
+  --summarize-counters FETCH_DIR WRITE_DIR   per-kernel HBM bytes from two rocprofv3 --pmc runs of
+                     --counters-run (FETCH_SIZE, then WRITE_SIZE), calibrated on the copies in the
+                     same runs, against the algorithmic bytes (--workload NAME)
+  --summarize-pmc DIR  per-kernel medians of any rocprofv3 --pmc counters
+  --summarize-trace DIR  per-step kernel timeline of a rocprofv3 --kernel-trace run of --timeline-run
 """
 
 from __future__ import annotations
@@ -40,7 +46,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "RMSNorm fwd+bwd µs/call and achieved HBM GB/s (% of peak), bf16 4096x4096"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "bwd_main_bf16_4096x4096_hbm_traffic.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.txt")
 
 
 def source_hash(plan=None) -> str:
@@ -58,9 +64,10 @@ def source_hash(plan=None) -> str:
     return h.hexdigest()[:16]
 
 
-def bwd_plan(rn, w):
+def bwd_plan(rn, w, num_cus: int = 0):
+    """The backward plan of workload w (num_cus 0: the current device's count)."""
     op = rn.OP_FUSED_ADD_BWD if w.fused else rn.OP_BWD
-    return rn.rmsnorm_query_plan(op, w.M, w.N, dtype_code(rn, w.dtype))
+    return rn.rmsnorm_query_plan(op, w.M, w.N, dtype_code(rn, w.dtype), True, num_cus)
 
 
 def dtype_code(rn, dtype: str) -> int:
@@ -454,13 +461,14 @@ def small_shape_launch_paths(lib, rn, torch, name: str = "bf16_512x2048", iters:
     return out
 
 
-def counters_traffic(ident: str):
+def counters_traffic(ident: str, workload: str):
     """HBM bytes per backward-main dispatch from committed rocprofv3 counters,
     or None when missing or taken on a different kernel (sources or plan)."""
-    if not os.path.exists(COUNTERS_FILE):
+    path = COUNTERS_FILE.format(workload=workload)
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, _, v = line.partition(":")
@@ -497,6 +505,186 @@ def counters_run(rn, torch, workload: str = "bf16_4096x4096"):
     print("counters run done", flush=True)
 
 
+def _rocprof_rows(d: str, suffix: str):
+    import csv
+
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return rows
+
+
+def _short(name: str) -> str:
+    for a, b in (("(rmsnorm::BwdArgs)", ""), ("(rmsnorm::FwdArgs)", ""), ("rmsnorm::", ""), ("unsigned short", "bf16"),
+                 ("void ", "")):
+        name = name.replace(a, b)
+    return name
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str):
+    """HBM bytes per dispatch of each library kernel in a --counters-run, from
+    a FETCH_SIZE run and a WRITE_SIZE run.  FETCH_SIZE is calibrated on the
+    plain copies of the same runs (a copy reads what it writes, and WRITE_SIZE
+    counts written bytes exactly): factor = sum WRITE / sum FETCH over them."""
+    from rmsnorm_inputs import ALL_WORKLOADS, algorithmic_bytes
+
+    w = ALL_WORKLOADS[workload]
+    per = {}
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        for r in _rocprof_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            per.setdefault(counter, {}).setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    copies = [k for k in per["FETCH_SIZE"] if "copyBuffer" in k]
+    f_sum = sum(sum(per["FETCH_SIZE"][k]) for k in copies)
+    w_sum = sum(sum(per["WRITE_SIZE"].get(k, [])) for k in copies)
+    factor = w_sum / f_sum
+    fop, bop = ("fused_fwd", "fused_bwd") if w.fused else ("fwd", "bwd")
+    B = w.elem_bytes
+    programs = None
+    out = [f"# HBM traffic per dispatch, {workload} (rocprofv3 PMC counters)",
+           "#",
+           "# Commands (run from /tmp with TMPDIR=/tmp, repository root R):",
+           f"#   timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/pmc_fetch_{workload} "
+           f"-o fetch -- python3 $R/bench.py --counters-run --workload {workload}",
+           f"#   timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/pmc_write_{workload} "
+           f"-o write -- python3 $R/bench.py --counters-run --workload {workload}",
+           f"#   python3 $R/bench.py --summarize-counters $R/gpurun_out/pmc_fetch_{workload} "
+           f"$R/gpurun_out/pmc_write_{workload} --workload {workload}",
+           "# bench.py --counters-run launches five 256 MiB device copies, then five forward, five backward-main",
+           "# and five finalizer dispatches of the workload (four rotating buffer sets).",
+           "#",
+           f"# Calibration: the copies' WRITE_SIZE / FETCH_SIZE = {w_sum:.1f} / {f_sum:.1f} KiB -> fetch factor "
+           f"{factor:.4f} (WRITE_SIZE counts written bytes exactly).",
+           "# Medians over the dispatches; bytes = KiB x 1024 (FETCH x factor).",
+           "#",
+           f"{'kernel':72s} {'read MB':>9s} {'write MB':>9s} {'total MB':>9s} {'algorithmic MB':>15s} {'ratio':>6s}"]
+    rows = {}
+    for k, vals in per["FETCH_SIZE"].items():
+        if "rmsnorm::" not in k:
+            continue
+        rd = statistics.median(vals) * 1024 * factor
+        wr = statistics.median(per["WRITE_SIZE"].get(k, [0.0])) * 1024
+        if "finalize_kernel" in k:
+            plan = None
+            try:
+                import transformer_normalization_rmsnorm_amd as rn
+
+                op = rn.OP_FUSED_ADD_BWD if w.fused else rn.OP_BWD
+                plan = rn.rmsnorm_query_plan(op, w.M, w.N, dtype_code(rn, w.dtype), True, 256)
+            except Exception:
+                plan = None
+            programs = plan["programs"] if plan else 256
+            alg = programs * w.N * 4 + w.N * B
+            kind = "finalizer"
+        elif "bwd_" in k:
+            alg = algorithmic_bytes(bop + "_main", w.M, w.N, B)
+            kind = "backward main"
+        else:
+            alg = algorithmic_bytes(fop, w.M, w.N, B)
+            kind = "forward"
+        rows[kind] = (k, rd, wr, alg)
+        out.append(f"{_short(k)[:72]:72s} {rd / 1e6:9.3f} {wr / 1e6:9.3f} {(rd + wr) / 1e6:9.3f} {alg / 1e6:15.3f} "
+                   f"{(rd + wr) / alg:6.3f}")
+    out.append("#")
+    out.append("# Algorithmic bytes: forward 2MNB + NB + 4M (fused 4MNB + NB + 4M); backward main 3MNB + NB + 4M")
+    out.append("# (fused 4MNB + NB + 4M), its P x N x 4 partial-row writes not counted; finalizer P x N x 4 + NB.")
+    if "backward main" in rows:
+        k, rd, wr, alg = rows["backward main"]
+        out.append("")
+        out.append(f"workload: {workload}")
+        out.append(f"source_hash: {source_hash(bwd_plan_for(w))}")
+        out.append(f"fetch_factor: {factor:.6f}")
+        out.append(f"traffic_bytes_per_dispatch: {rd + wr:.0f}")
+        out.append(f"read_bytes_per_dispatch: {rd:.0f}")
+        out.append(f"write_bytes_per_dispatch: {wr:.0f}")
+        out.append(f"algorithmic_bytes_per_dispatch: {alg}")
+    print("\n".join(out))
+
+
+def bwd_plan_for(w, num_cus: int = 256):
+    """The plan on a device of num_cus compute units (MI355X: 256), so that a
+    summary made without a GPU hashes the plan the benchmark will see."""
+    import transformer_normalization_rmsnorm_amd as rn
+
+    return bwd_plan(rn, w, num_cus)
+
+
+def summarize_pmc(d: str):
+    """Per library kernel, the median of each counter over its dispatches."""
+    per = {}
+    for r in _rocprof_rows(d, "counter_collection.csv"):
+        if "rmsnorm::" in r["Kernel_Name"]:
+            per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    for k, cs in per.items():
+        print(_short(k))
+        for c, vals in sorted(cs.items()):
+            print(f"    {c:22s} {statistics.median(vals):16.1f}   ({len(vals)} dispatches)")
+
+
+def summarize_trace(d: str):
+    """Per-step timeline of a --timeline-run: each step is the forward of one
+    buffer set then the backward (main, finalizer) of another, back to back on
+    one stream.  Times relative to the step's first kernel start, in us,
+    median over the traced steps (the warmup steps excluded)."""
+    rows = _rocprof_rows(d, "kernel_trace.csv")
+    ks = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows
+                 if "rmsnorm::" in r["Kernel_Name"]), key=lambda t: t[0])
+    steps = []
+    i = 0
+    while i + 2 < len(ks):
+        a, b, c = ks[i], ks[i + 1], ks[i + 2]
+        if "fwd_" in a[2] and "bwd_" in b[2] and "finalize" in c[2]:
+            steps.append((a, b, c))
+            i += 3
+        else:
+            i += 1
+    steps = steps[-10:]
+    if not steps:
+        raise SystemExit("no fwd / bwd / finalize triples in the trace")
+    def med(f):
+        return statistics.median(f(s) for s in steps)
+    t0 = lambda s: s[0][0]
+    fields = [
+        ("forward kernel", lambda s: (s[0][1] - s[0][0]) / 1e3),
+        ("gap forward end -> backward main start", lambda s: (s[1][0] - s[0][1]) / 1e3),
+        ("backward main kernel", lambda s: (s[1][1] - s[1][0]) / 1e3),
+        ("gap backward main end -> finalizer start", lambda s: (s[2][0] - s[1][1]) / 1e3),
+        ("finalizer kernel", lambda s: (s[2][1] - s[2][0]) / 1e3),
+        ("step: forward start -> finalizer end", lambda s: (s[2][1] - t0(s)) / 1e3),
+    ]
+    nxt = [(steps[j + 1][0][0] - steps[j][2][1]) / 1e3 for j in range(len(steps) - 1)]
+    print(f"# kernels: {_short(steps[0][0][2])}; {_short(steps[0][1][2])}; {_short(steps[0][2][2])}")
+    print(f"# {len(steps)} steps traced (medians, us)")
+    for name, f in fields:
+        print(f"{name:45s} {med(f):8.2f}")
+    if nxt:
+        print(f"{'gap finalizer end -> next step forward start':45s} {statistics.median(nxt):8.2f}")
+
+
+def timeline_run(rn, torch, workload: str, steps: int = 10, warmup: int = 5):
+    """Only the bench step (forward of one set, backward of another), for a
+    kernel-trace timeline."""
+    from rmsnorm_inputs import ALL_WORKLOADS
+
+    w = ALL_WORKLOADS[workload]
+    lib = rn.load_library()
+    S = Sets(w, lib, rn, torch, n_sets_for(w, True))
+    K = len(S.sets)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i in range(K):
+        S.fwd(i, st)
+    torch.cuda.synchronize()
+    for i in range(warmup + steps):
+        S.fwd(i, st)
+        S.bwd(i + K // 2, st)
+    torch.cuda.synchronize()
+    print("timeline run done", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -508,7 +696,20 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters-run", action="store_true")
+    ap.add_argument("--timeline-run", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--summarize-trace", metavar="DIR")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -528,6 +729,9 @@ def main():
         sys.exit(1)
     if args.counters_run:
         counters_run(rn, torch, args.workload)
+        return
+    if args.timeline_run:
+        timeline_run(rn, torch, args.workload)
         return
     lib = rn.load_library()
     w = WORKLOADS[args.workload]
@@ -567,7 +771,7 @@ def main():
     roofline = {
         "kernel": f"backward main ({'fused-add ' if w.fused else ''}rows, dx + dgamma partials)",
         "bound": "hbm", "achieved": detail["bytes"]["bwd_main"] / (main_us * 1e3), "peak": HBM_PEAK_GBS,
-        "unit": "GB/s", "frac": None, "traffic": counters_traffic(source_hash(bwd_plan(rn, w))),
+        "unit": "GB/s", "frac": None, "traffic": counters_traffic(source_hash(bwd_plan(rn, w)), w.name),
         "bytes_per_launch": detail["bytes"]["bwd_main"], "avg_launch_us": main_us,
     }
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
