@@ -524,22 +524,13 @@ def test_override_round_trip():
             plan(rn.OP_FWD, 10, 4096, vec_ok=False)
 
 
-@pytest.mark.parametrize("M,N,fused,chunks", [
-    (16384, 6144, False, 2), (2048, 6144, False, 2), (8192, 2048, False, 2), (4096, 6144, True, 2),
-    (1024, 4096, False, None), (1024, 8192, False, None),
-])
-def test_fp32_forward_two_chunks_from_8_rows_per_cu(M, N, fused, chunks):
-    """fp32 forwards with at least 8 rows per compute unit take two chunks per
-    lane; with fewer (4 here) they keep the fewer, fuller lanes."""
-    p = plan(rn.OP_FUSED_ADD_FWD if fused else rn.OP_FWD, M, N, rn.F32)
-    if chunks is not None:
-        assert (p["threads"], p["chunks"]) == (N // 4 // 2, 2)
-    else:
-        assert p["chunks"] > 2
-    if (M, N, fused) == (16384, 6144, False):
-        # not for the fp8 forward (256 threads) or LayerNorm (N / 16 threads)
-        assert plan(rn.OP_FWD_FP8, M, N, rn.F32)["threads"] == 256
-        assert plan(rn.OP_LN_FWD, M, N, rn.F32)["threads"] == 384
+def test_fp8_and_layernorm_forwards_keep_their_targets():
+    """The RMSNorm forward rule does not apply to the fp8 forward (256 threads)
+    or LayerNorm (N / 16 threads)."""
+    M, N = 16384, 6144
+    assert plan(rn.OP_FWD, M, N, rn.F32)["threads"] == 768
+    assert plan(rn.OP_FWD_FP8, M, N, rn.F32)["threads"] == 256
+    assert plan(rn.OP_LN_FWD, M, N, rn.F32)["threads"] == 384
 
 
 _LOG_SNIPPET = r"""
@@ -586,3 +577,155 @@ def test_plan_log_once_per_key():
     plain = [ln for ln in lines if "fallback" not in ln]
     assert len(plain) == 3 and all("path=rows" in ln for ln in plain)
     assert _run_logged(None) == [] and _run_logged("0") == []
+
+
+# The forward layout sweep on MI355X (RMSNorm plain and fused-add, bf16 and
+# fp32, N = 2048 ... 32768, 2 ... 64 rows per compute unit; every exact
+# workgroup tiling; medians of 7 interleaved rounds on cold buffers).  Below
+# 16 rows per compute unit the selector takes the tiling measured fastest at
+# each swept point: (dtype, fused, M, N) -> threads.
+FWD_SWEPT_LATENCY = [
+    ("bf16", False, 512, 2048, 128),
+    ("bf16", False, 1024, 2048, 256),
+    ("bf16", False, 2048, 2048, 256),
+    ("bf16", False, 512, 4096, 128),
+    ("bf16", False, 1024, 4096, 256),
+    ("bf16", False, 2048, 4096, 64),
+    ("bf16", False, 512, 6144, 768),
+    ("bf16", False, 1024, 6144, 256),
+    ("bf16", False, 2048, 6144, 128),
+    ("bf16", False, 512, 8192, 512),
+    ("bf16", False, 1024, 8192, 128),
+    ("bf16", False, 2048, 8192, 512),
+    ("bf16", False, 512, 12288, 384),
+    ("bf16", False, 1024, 12288, 192),
+    ("bf16", False, 2048, 12288, 768),
+    ("bf16", False, 512, 16384, 512),
+    ("bf16", False, 1024, 16384, 512),
+    ("bf16", False, 2048, 16384, 1024),
+    ("bf16", False, 512, 24576, 512),
+    ("bf16", False, 1024, 24576, 512),
+    ("bf16", False, 2048, 24576, 512),
+    ("bf16", False, 512, 32768, 512),
+    ("bf16", False, 1024, 32768, 512),
+    ("bf16", False, 2048, 32768, 512),
+    ("f32", False, 512, 2048, 512),
+    ("f32", False, 1024, 2048, 128),
+    ("f32", False, 2048, 2048, 64),
+    ("f32", False, 512, 4096, 256),
+    ("f32", False, 1024, 4096, 128),
+    ("f32", False, 2048, 4096, 128),
+    ("f32", False, 512, 6144, 384),
+    ("f32", False, 1024, 6144, 192),
+    ("f32", False, 2048, 6144, 768),
+    ("f32", False, 512, 8192, 256),
+    ("f32", False, 1024, 8192, 256),
+    ("f32", False, 2048, 8192, 1024),
+    ("f32", False, 512, 12288, 384),
+    ("f32", False, 1024, 12288, 512),
+    ("f32", False, 2048, 12288, 512),
+    ("f32", False, 512, 16384, 512),
+    ("f32", False, 1024, 16384, 512),
+    ("f32", False, 2048, 16384, 512),
+    ("bf16", True, 512, 2048, 64),
+    ("bf16", True, 1024, 2048, 128),
+    ("bf16", True, 2048, 2048, 64),
+    ("bf16", True, 512, 4096, 64),
+    ("bf16", True, 1024, 4096, 128),
+    ("bf16", True, 2048, 4096, 64),
+    ("bf16", True, 512, 8192, 512),
+    ("bf16", True, 1024, 8192, 128),
+    ("bf16", True, 2048, 8192, 512),
+    ("bf16", True, 512, 16384, 256),
+    ("bf16", True, 1024, 16384, 256),
+    ("bf16", True, 2048, 16384, 1024),
+    ("bf16", True, 512, 24576, 512),
+    ("bf16", True, 1024, 24576, 512),
+    ("bf16", True, 2048, 24576, 384),
+]
+# From 16 rows per compute unit it takes two chunks per lane where that tiles
+# exactly within 1024 threads, else the fewest chunks whose tiling fits.
+FWD_SWEPT_THROUGHPUT = [
+    ("bf16", False, 4096, 2048),
+    ("bf16", False, 8192, 2048),
+    ("bf16", False, 16384, 2048),
+    ("bf16", False, 4096, 4096),
+    ("bf16", False, 8192, 4096),
+    ("bf16", False, 16384, 4096),
+    ("bf16", False, 4096, 6144),
+    ("bf16", False, 8192, 6144),
+    ("bf16", False, 16384, 6144),
+    ("bf16", False, 4096, 8192),
+    ("bf16", False, 8192, 8192),
+    ("bf16", False, 16384, 8192),
+    ("bf16", False, 4096, 12288),
+    ("bf16", False, 8192, 12288),
+    ("bf16", False, 16384, 12288),
+    ("bf16", False, 4096, 16384),
+    ("bf16", False, 8192, 16384),
+    ("bf16", False, 16384, 16384),
+    ("bf16", False, 4096, 24576),
+    ("bf16", False, 8192, 24576),
+    ("bf16", False, 4096, 32768),
+    ("bf16", False, 8192, 32768),
+    ("f32", False, 4096, 2048),
+    ("f32", False, 8192, 2048),
+    ("f32", False, 16384, 2048),
+    ("f32", False, 4096, 4096),
+    ("f32", False, 8192, 4096),
+    ("f32", False, 16384, 4096),
+    ("f32", False, 4096, 6144),
+    ("f32", False, 8192, 6144),
+    ("f32", False, 16384, 6144),
+    ("f32", False, 4096, 8192),
+    ("f32", False, 8192, 8192),
+    ("f32", False, 16384, 8192),
+    ("f32", False, 4096, 12288),
+    ("f32", False, 8192, 12288),
+    ("f32", False, 4096, 16384),
+    ("f32", False, 8192, 16384),
+    ("bf16", True, 4096, 2048),
+    ("bf16", True, 8192, 2048),
+    ("bf16", True, 16384, 2048),
+    ("bf16", True, 4096, 4096),
+    ("bf16", True, 8192, 4096),
+    ("bf16", True, 16384, 4096),
+    ("bf16", True, 4096, 8192),
+    ("bf16", True, 8192, 8192),
+    ("bf16", True, 16384, 8192),
+    ("bf16", True, 4096, 16384),
+    ("bf16", True, 8192, 16384),
+    ("bf16", True, 16384, 16384),
+    ("bf16", True, 4096, 24576),
+    ("bf16", True, 8192, 24576),
+]
+
+
+def _fewest_chunks_tiling(nchunks):
+    for k in (2, 3, 4, 6, 8):
+        t = nchunks // k
+        if nchunks % k == 0 and t % 64 == 0 and t <= (1024 if k <= 2 else 512):
+            return t, k
+    raise AssertionError(nchunks)
+
+
+@pytest.mark.parametrize("dt,fused,M,N,threads", FWD_SWEPT_LATENCY,
+                         ids=[f"{d}{'_fused' if f else ''}_{m}x{n}" for d, f, m, n, _ in FWD_SWEPT_LATENCY])
+def test_forward_plan_latency_regime(dt, fused, M, N, threads):
+    p = plan(rn.OP_FUSED_ADD_FWD if fused else rn.OP_FWD, M, N, rn.BF16 if dt == "bf16" else rn.F32)
+    V = 8 if dt == "bf16" else 4
+    assert (p["team"], p["threads"], p["chunks"]) == (0, threads, N // V // threads), p
+
+
+@pytest.mark.parametrize("dt,fused,M,N", FWD_SWEPT_THROUGHPUT,
+                         ids=[f"{d}{'_fused' if f else ''}_{m}x{n}" for d, f, m, n in FWD_SWEPT_THROUGHPUT])
+def test_forward_plan_throughput_regime(dt, fused, M, N):
+    p = plan(rn.OP_FUSED_ADD_FWD if fused else rn.OP_FWD, M, N, rn.BF16 if dt == "bf16" else rn.F32)
+    V = 8 if dt == "bf16" else 4
+    assert (p["threads"], p["chunks"]) == _fewest_chunks_tiling(N // V), p
+
+
+def test_forward_plan_24576_takes_six_chunks():
+    """bf16 4096 x 24576: 512 threads x 6 chunks (66.7 us measured against 74.1 us for 384 x 8)."""
+    p = plan(rn.OP_FWD, 4096, 24576, rn.BF16)
+    assert (p["threads"], p["chunks"]) == (512, 6)

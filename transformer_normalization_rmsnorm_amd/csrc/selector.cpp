@@ -10,6 +10,7 @@
 // (up to 32 vectors) are shared by teams of 8-32 lanes so a wavefront holds
 // several rows, and rows too wide for registers take the looped path.
 #include <algorithm>
+#include <cmath>
 
 #include "rmsnorm_internal.h"
 
@@ -128,13 +129,10 @@ bool pick_wide_bwd_team(int op, int dtype, bool vec, int64_t nchunks, rmsnorm_pl
     return false;
 }
 
-// Forward workgroup team: among the compiled chunk counts that tile the row
-// exactly (no masked lanes) with a multiple of 64 threads, the one whose
-// thread count is closest to `target`; else the generic choice.  Measured on
-// MI355X: with few rows per compute unit fewer, fuller lanes win (1024 x 8192
-// bf16: 128 threads x 8 chunks 7.0 us, 256 x 4 7.8 us, 512 x 2 8.2 us); at 8-32
-// rows per unit 256 threads do (4096 x 4096: 256 x 2 13.5 us, 128 x 4 14.0 us).
-// Persistent forward variants were not faster.
+// Forward workgroup team for LayerNorm and the fp8 output: among the compiled
+// chunk counts that tile the row exactly (no masked lanes) with a multiple of
+// 64 threads, the one whose thread count is closest to `target`; else the
+// generic choice.  Persistent forward variants were not faster.
 bool pick_fwd_block_team(int op, bool vec, int64_t nchunks, int depth, int target, rmsnorm_plan *p)
 {
     const int kFwdThreads = target;
@@ -162,6 +160,113 @@ bool pick_fwd_block_team(int op, bool vec, int64_t nchunks, int depth, int targe
     p->depth = depth;
     p->w_regs = 0;
     return true;
+}
+
+// ---- RMSNorm forward layout (plain and fused-add) -------------------------
+//
+// Chosen from a sweep on MI355X of every exact workgroup tiling compiled
+// (threads = row vectors / chunks, a multiple of 64, within the launch bound)
+// over N = 2048 ... 32768 and 2 ... 64 rows per compute unit, bf16 and fp32
+// rows, plain and fused-add, cold rotating buffers, medians of 7 interleaved
+// rounds.  Two regimes:
+//   * from 16 rows per compute unit (several rounds of workgroups per unit,
+//     so what one workgroup streams per unit time decides): two chunks per
+//     lane where that tiling fits, else the fewest that fit.  Within 3% of the
+//     fastest tiling at all but 5 of the 52 swept points of this regime, and
+//     within 5.2% at those (fp32 12288 wide, fused 8192 / 16384 / 24576 wide);
+//   * below (one round of workgroups, so one workgroup's latency decides): no
+//     closed rule came within 15% of the fastest at every point, so the
+//     chunks per lane measured fastest at the nearest swept (N, rows per unit)
+//     are taken (kFwdLatency*), and the exact tiling with the nearest chunk
+//     count is launched.
+// LayerNorm and the fp8-output forward keep their own targets.
+struct FwdLatencyRow {
+    int32_t n;
+    int8_t k[3]; // chunks per lane at 2, 4, 8 rows per compute unit
+};
+constexpr FwdLatencyRow kFwdLatency16[] = {
+    {2048, {2, 1, 1}},  {4096, {4, 2, 8}},  {6144, {1, 3, 6}},  {8192, {2, 8, 2}},
+    {12288, {4, 8, 2}}, {16384, {4, 4, 2}}, {24576, {6, 6, 6}}, {32768, {8, 8, 8}},
+};
+constexpr FwdLatencyRow kFwdLatency16Fused[] = {
+    {2048, {4, 2, 4}}, {4096, {8, 4, 8}}, {8192, {2, 8, 2}}, {16384, {8, 8, 2}}, {24576, {6, 6, 8}},
+};
+constexpr FwdLatencyRow kFwdLatency32[] = {
+    {2048, {1, 4, 8}}, {4096, {4, 8, 8}}, {6144, {4, 8, 2}}, {8192, {8, 8, 2}}, {12288, {8, 6, 6}}, {16384, {8, 8, 8}},
+};
+
+// Exact workgroup tiling (threads = nchunks / k a multiple of 64 within the
+// launch bound) with the compiled chunk count nearest `want` (log scale; ties
+// to the smaller count).  Returns false if the row has no exact tiling.
+bool pick_fwd_chunks(int op, bool vec, int64_t nchunks, int want, rmsnorm_plan *p)
+{
+    int best_k = 0;
+    double best_d = 0.0;
+    for (int k = 1; k <= 16; ++k) {
+        const int b = bound(op, vec, 0, k, 0, 0);
+        if (b == 0 || nchunks % k != 0)
+            continue;
+        const int64_t t = nchunks / k;
+        if (t % 64 != 0 || t > b)
+            continue;
+        const double d = std::fabs(std::log2((double)k / (double)want));
+        if (best_k == 0 || d < best_d - 1e-9) {
+            best_k = k;
+            best_d = d;
+        }
+    }
+    if (best_k == 0)
+        return false;
+    p->team = 0;
+    p->threads = (int32_t)(nchunks / best_k);
+    p->chunks = best_k;
+    p->depth = 0;
+    p->w_regs = 0;
+    return true;
+}
+
+// Fewest compiled chunks per lane, at least kmin, with an exact tiling.
+bool pick_fwd_fewest(int op, bool vec, int64_t nchunks, int kmin, rmsnorm_plan *p)
+{
+    for (int k = kmin; k <= 16; ++k) {
+        const int b = bound(op, vec, 0, k, 0, 0);
+        if (b == 0 || nchunks % k != 0)
+            continue;
+        const int64_t t = nchunks / k;
+        if (t % 64 == 0 && t <= b)
+            return pick_fwd_chunks(op, vec, nchunks, k, p);
+    }
+    return false;
+}
+
+bool pick_fwd_rms_team(int op, int dtype, int64_t M, int64_t N, int64_t nchunks, int num_cus, rmsnorm_plan *p)
+{
+    const double rows_per_cu = (double)M / (double)std::max(num_cus, 1);
+    // the nearest swept rows-per-unit bucket, on a log scale: 16 and up
+    // (from 8 * sqrt(2) rows per unit) is the throughput regime
+    if (rows_per_cu >= 8.0 * std::sqrt(2.0)) {
+        if (pick_fwd_fewest(op, true, nchunks, 2, p) || pick_fwd_fewest(op, true, nchunks, 1, p))
+            return true;
+        return pick_block_team(op, true, nchunks, 0, p);
+    }
+    const int bucket = rows_per_cu < 2.0 * std::sqrt(2.0) ? 0 : rows_per_cu < 4.0 * std::sqrt(2.0) ? 1 : 2;
+    const FwdLatencyRow *rows;
+    size_t nrows;
+    if (dtype == RMSNORM_F32) {
+        rows = kFwdLatency32;
+        nrows = sizeof kFwdLatency32 / sizeof kFwdLatency32[0];
+    } else if (is_fused(op)) {
+        rows = kFwdLatency16Fused;
+        nrows = sizeof kFwdLatency16Fused / sizeof kFwdLatency16Fused[0];
+    } else {
+        rows = kFwdLatency16;
+        nrows = sizeof kFwdLatency16 / sizeof kFwdLatency16[0];
+    }
+    size_t near = 0;
+    for (size_t i = 1; i < nrows; ++i)
+        if (std::fabs(std::log2((double)N / rows[i].n)) < std::fabs(std::log2((double)N / rows[near].n)))
+            near = i;
+    return pick_fwd_chunks(op, true, nchunks, rows[near].k[bucket], p) || pick_block_team(op, true, nchunks, 0, p);
 }
 
 } // namespace
@@ -298,17 +403,7 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             // most four chunks per lane where a tiling allows (measured: 4096 x
             // 16384 bf16 50.5 us at 512 threads against 53.1 us at 256;
             // 16384 x 8192: 91.4 us at 256 against 94.0 us at 128)
-            const int64_t rows_per_cu = M / std::max(num_cus, 1);
-            int target = is_fp8_op(op) || (rows_per_cu >= 8 && rows_per_cu < 32) ? 256 : 128;
-            if (is_ln_op(op))
-                target = (int)std::max<int64_t>(256, nchunks / 4);
-            // fp32 rows with at least 8 per compute unit: two chunks per lane
-            // (measured on MI355X against the 128/256 target: 16384 x 6144
-            // 127.6 vs 132.7 us, 2048 x 6144 18.8 vs 19.9, 16384 x 4096 86.0
-            // vs 88.4, 8192 x 2048 23.7 vs 24.2; at 4 rows per unit it loses,
-            // 1024 x 4096 8.3 vs 6.8 us)
-            else if (dtype == RMSNORM_F32 && !is_fp8_op(op) && rows_per_cu >= 8)
-                target = (int)std::max<int64_t>(64, nchunks / 2);
+            const int target = is_ln_op(op) ? (int)std::max<int64_t>(256, nchunks / 4) : 256;
             // backward: w in registers with one chunk per lane (the pages'
             // layout), else gamma re-read per row.  Measured on MI355X, gamma
             // per row with two chunks per lane and one row ahead beats w in
@@ -317,8 +412,10 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             if (bwd)
                 placed = (nchunks <= 1024 && pick_block_team(op, true, nchunks, p.depth, &p)) ||
                          pick_wide_bwd_team(op, dtype, true, nchunks, &p);
-            else
+            else if (is_ln_op(op) || is_fp8_op(op))
                 placed = pick_fwd_block_team(op, true, nchunks, p.depth, target, &p);
+            else
+                placed = pick_fwd_rms_team(op, dtype, M, N, nchunks, num_cus, &p);
         }
     } else {
         if (nchunks <= (bwd ? 128 : 512)) {
