@@ -26,6 +26,8 @@ Other modes:
                      same runs, against the algorithmic bytes (--workload NAME)
   --summarize-pmc DIR  per-kernel medians of any rocprofv3 --pmc counters
   --summarize-trace DIR  per-step kernel timeline of a rocprofv3 --kernel-trace run of --timeline-run
+  --summarize-stats DIR  the kernel table of a rocprofv3 --kernel-trace --stats run
+  --summarize-report REPORT_JSON  per-workload table of a --report run
 """
 
 from __future__ import annotations
@@ -272,6 +274,9 @@ def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
     from rmsnorm_inputs import algorithmic_bytes
 
     res = {"workload": w.name, "M": w.M, "N": w.N, "dtype": w.dtype, "fused": w.fused, "offset": w.offset}
+    dt = dtype_code(rn, w.dtype)
+    fop_code, bop_code = (rn.OP_FUSED_ADD_FWD, rn.OP_FUSED_ADD_BWD) if w.fused else (rn.OP_FWD, rn.OP_BWD)
+    res["plans"] = {"fwd": rn.rmsnorm_query_plan(fop_code, w.M, w.N, dt), "bwd": rn.rmsnorm_query_plan(bop_code, w.M, w.N, dt)}
     fop, bop = ("fused_fwd", "fused_bwd") if w.fused else ("fwd", "bwd")
     bytes_f = algorithmic_bytes(fop, w.M, w.N, w.elem_bytes)
     bytes_b = algorithmic_bytes(bop, w.M, w.N, w.elem_bytes)
@@ -625,6 +630,55 @@ def summarize_pmc(d: str):
             print(f"    {c:22s} {statistics.median(vals):16.1f}   ({len(vals)} dispatches)")
 
 
+def summarize_stats(d: str):
+    """The kernel table of a rocprofv3 --kernel-trace --stats run, per kernel
+    and launch geometry (workgroup size x workgroups: one kernel instance may
+    serve several workloads), from the per-dispatch trace: calls and average /
+    min / max duration, most total time first."""
+    rows = _rocprof_rows(d, "kernel_trace.csv")
+    groups = {}
+    for r in rows:
+        wg = int(r["Workgroup_Size_X"])
+        key = (r["Kernel_Name"], wg, int(r["Grid_Size_X"]) // max(wg, 1))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"# {'kernel':66s} {'wg x grid':>12s} {'calls':>6s} {'avg us':>8s} {'min us':>8s} {'max us':>8s}")
+    for (name, wg, grid), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"  {_short(name)[:66]:66s} {f'{wg}x{grid}':>12s} {len(ds):6d} {statistics.fmean(ds):8.2f} "
+              f"{min(ds):8.2f} {max(ds):8.2f}")
+
+
+def summarize_report(path: str):
+    """Per workload of a --report run: cold-buffer times of every op (direct
+    launches; the finalizer from a graph), GB/s and % of the 8 TB/s peak,
+    hot and graph-replay times, the streaming ceilings and the plans."""
+    with open(path) as f:
+        rep = json.load(f)
+
+    def fmt(v, spec, width):
+        return format(v, spec) if v is not None else "-".rjust(width)
+
+    print(f"# {'workload':28s} {'op':9s} {'cold us':>8s} {'GB/s':>7s} {'%peak':>6s} {'hot us':>7s} {'graph us':>9s}")
+    for wl in rep["workloads"]:
+        c, h = wl["cold"], wl.get("hot", {})
+        for op in ("fwd", "bwd", "bwd_main", "finalize", "fwd_fp8", "ln_fwd", "ln_bwd"):
+            if op + "_us" not in c:
+                continue
+            cells = [fmt(c[op + "_us"], "8.2f", 8), fmt(c.get(op + "_GBs"), "7.1f", 7),
+                     fmt(c.get(op + "_pct_peak"), "6.1f", 6), fmt(h.get(op + "_us"), "7.2f", 7),
+                     fmt(c.get(op + "_graph_us"), "9.2f", 9)]
+            print(f"  {wl['workload']:28s} {op:9s} " + " ".join(cells))
+        ce = wl.get("ceilings", {})
+        if ce:
+            print(f"  {wl['workload']:28s} ceilings: copy {ce['copy_GBs']:.0f} GB/s, three-stream "
+                  f"{ce['three_stream_GBs']:.0f} GB/s")
+        for k in ("fwd", "bwd"):
+            p = wl.get("plans", {}).get(k)
+            if p:
+                print(f"  {wl['workload']:28s} {k} plan: path {p['path']} vec {p['vec']} team {p['team']} threads "
+                      f"{p['threads']} chunks {p['chunks']} depth {p['depth']} w_regs {p['w_regs']} rows/step "
+                      f"{p['rows_per_step']} grid {p['grid']}")
+
+
 def summarize_trace(d: str):
     """Per-step timeline of a --timeline-run: each step is the forward of one
     buffer set then the backward (main, finalizer) of another, back to back on
@@ -700,7 +754,15 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-pmc", metavar="DIR")
     ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--summarize-report", metavar="REPORT_JSON")
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_report:
+        summarize_report(args.summarize_report)
+        return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload)
         return
