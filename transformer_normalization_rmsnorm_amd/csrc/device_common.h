@@ -443,12 +443,19 @@ template <int V>
 __device__ __forceinline__ void store_e4m3(uint8_t *p, const float (&f)[V], float scale, float &am)
 {
     float t[V];
+    // max |f| over bit patterns: with the sign cleared, unsigned order is
+    // numeric order and every NaN lies above +inf, so an integer max
+    // propagates NaN in one instruction (am is never negative).  The float
+    // form (compare, unordered compare, select) measured 3% slower on the
+    // 4096 x 4096 and 16384 x 8192 bf16 fp8 forwards.
+    uint32_t m = __builtin_bit_cast(uint32_t, am);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-        am = max_nan(am, fabsf(f[e]));
+        m = max(m, __builtin_bit_cast(uint32_t, f[e]) & 0x7fffffffu);
         const float s = f[e] * scale;
         t[e] = fabsf(s) > 448.0f ? copysignf(448.0f, s) : s;
     }
+    am = __builtin_bit_cast(float, m);
     if constexpr (V == 1) {
         const int w = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], 0.0f, 0, false);
         __builtin_nontemporal_store((uint8_t)(w & 0xff), p);

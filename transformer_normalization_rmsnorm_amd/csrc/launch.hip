@@ -45,8 +45,9 @@ hipError_t launch_finalize(int dtype, const float *partials, int64_t programs, i
 // float4 with kAmaxLoads independent loads per lane in flight, so a round
 // covers kAmaxThreads * kAmaxLoads * 4 partials for one memory latency (a
 // dependent loop of scalar loads cost one latency per 256 partials: about 20
-// us at 16384 workgroups).  Every load is issued: lanes past the end re-read
-// the last group and their values are ignored.
+// us at 16384 workgroups).  Lanes past the end load nothing: re-reading the
+// last group there kept this one compute unit's load path busy for loads
+// whose values were ignored (4096 x 4096 fp8 forward 14.46 -> 14.30 us).
 constexpr int kAmaxLoads = 4;
 
 __global__ void __launch_bounds__(kAmaxThreads) amax_finalize_kernel(const float *__restrict__ part, int64_t P,
@@ -61,7 +62,7 @@ __global__ void __launch_bounds__(kAmaxThreads) amax_finalize_kernel(const float
 #pragma unroll
         for (int u = 0; u < kAmaxLoads; ++u) {
             const int64_t i = b + (int64_t)u * kAmaxThreads + threadIdx.x;
-            v[u] = p4[i < P4 ? i : P4 - 1];
+            v[u] = i < P4 ? p4[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
 #pragma unroll
         for (int u = 0; u < kAmaxLoads; ++u) {
