@@ -286,6 +286,12 @@ def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
     bytes_lb = algorithmic_bytes("ln_fused_bwd" if w.fused else "ln_bwd", w.M, w.N, w.elem_bytes)
     res["bytes"] = {"fwd": bytes_f, "bwd": bytes_b, "bwd_main": bytes_main, "fwd_fp8": bytes_f8,
                     "ln_fwd": bytes_lf, "ln_bwd": bytes_lb}
+    # workspace traffic of the backward: its P partial rows of N floats (two
+    # sets for LayerNorm: dgamma and dbeta), written once and read once
+    ln_bop = rn.OP_LN_FUSED_ADD_BWD if w.fused else rn.OP_LN_BWD
+    P_rms = res["plans"]["bwd"]["programs"]
+    P_ln = rn.rmsnorm_query_plan(ln_bop, w.M, w.N, dt)["programs"]
+    res["workspace_bytes"] = {"bwd": 2 * P_rms * w.N * 4, "ln_bwd": 2 * 2 * P_ln * w.N * 4}
     for mode in (("cold", "hot") if detailed else ("cold",)):
         S = Sets(w, lib, rn, torch, n_sets_for(w, mode == "cold"))
         K = len(S.sets)
@@ -312,6 +318,10 @@ def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
                       ("ln_fwd", bytes_lf), ("ln_bwd", bytes_lb)):
             r[op + "_GBs"] = b / (r[op + "_us"] * 1e3)
             r[op + "_pct_peak"] = 100.0 * r[op + "_GBs"] / HBM_PEAK_GBS
+        # the backward's bandwidth with its workspace traffic counted too
+        for op, b in (("bwd", bytes_b + res["workspace_bytes"]["bwd"]),
+                      ("ln_bwd", bytes_lb + res["workspace_bytes"]["ln_bwd"])):
+            r[op + "_incl_ws_GBs"] = b / (r[op + "_us"] * 1e3)
         res[mode] = r
         del S
         torch.cuda.empty_cache()
@@ -657,7 +667,8 @@ def summarize_report(path: str):
     def fmt(v, spec, width):
         return format(v, spec) if v is not None else "-".rjust(width)
 
-    print(f"# {'workload':28s} {'op':9s} {'cold us':>8s} {'GB/s':>7s} {'%peak':>6s} {'hot us':>7s} {'graph us':>9s}")
+    print(f"# {'workload':28s} {'op':9s} {'cold us':>8s} {'GB/s':>7s} {'%peak':>6s} {'hot us':>7s} {'graph us':>9s} "
+          f"{'incl. ws GB/s':>13s}")
     for wl in rep["workloads"]:
         c, h = wl["cold"], wl.get("hot", {})
         for op in ("fwd", "bwd", "bwd_main", "finalize", "fwd_fp8", "ln_fwd", "ln_bwd"):
@@ -665,7 +676,7 @@ def summarize_report(path: str):
                 continue
             cells = [fmt(c[op + "_us"], "8.2f", 8), fmt(c.get(op + "_GBs"), "7.1f", 7),
                      fmt(c.get(op + "_pct_peak"), "6.1f", 6), fmt(h.get(op + "_us"), "7.2f", 7),
-                     fmt(c.get(op + "_graph_us"), "9.2f", 9)]
+                     fmt(c.get(op + "_graph_us"), "9.2f", 9), fmt(c.get(op + "_incl_ws_GBs"), "13.1f", 13)]
             print(f"  {wl['workload']:28s} {op:9s} " + " ".join(cells))
         ce = wl.get("ceilings", {})
         if ce:
@@ -861,6 +872,7 @@ def main():
         "fwd_fp8_us": round(cold["fwd_fp8_us"], 3), "fwd_fp8_GBs": round(cold["fwd_fp8_GBs"], 1),
         "ln_fwd_us": round(cold["ln_fwd_us"], 3), "ln_bwd_us": round(cold["ln_bwd_us"], 3),
         "fwd_GBs": round(cold["fwd_GBs"], 1), "bwd_GBs": round(cold["bwd_GBs"], 1),
+        "bwd_incl_ws_GBs": round(cold["bwd_incl_ws_GBs"], 1),
         "fwd_pct_peak": round(cold["fwd_pct_peak"], 2), "bwd_pct_peak": round(cold["bwd_pct_peak"], 2),
         "bwd_main_us": round(main_us, 3), "finalize_us": round(cold["finalize_us"], 3),
         "roofline": roofline, "cpu_baseline": cpu, "practical_ceilings": ceil, "small_shape_graph": small,
