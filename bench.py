@@ -311,6 +311,9 @@ def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
             S.ln_fwd(i, st)
         r["ln_fwd_us"] = time_direct(torch, S.ln_fwd, iters, warmup)
         r["ln_bwd_us"] = time_direct(torch, lambda i, s: S.ln_bwd(i + K // 2, s), iters, warmup)
+        if mode == "cold":
+            sh = shim_times(S, rn, torch, iters, warmup)
+            r["shim_fwd_us"], r["shim_bwd_us"] = sh["fwd_us"], sh["bwd_us"]
         if detailed:
             r["fwd_graph_us"] = time_graph(torch, S.fwd, iters)
             r["bwd_graph_us"] = time_graph(torch, lambda i, s: S.bwd(i + K // 2, s), iters)
@@ -453,6 +456,31 @@ def cpu_baseline(w, seconds: float, single_thread_workloads=("bf16_512x2048", "b
     }
 
 
+def shim_times(S, rn, torch, iters: int, warmup: int):
+    """Forward and backward through the Python binding, which allocates the
+    outputs (and the backward's workspace) with torch.empty on every call:
+    the cost a framework caller sees, beside the raw C-ABI launches."""
+    w, K = S.w, len(S.sets)
+    fwd = rn.rmsnorm_fused_add_fwd if w.fused else rn.rmsnorm_fwd
+    bwd = rn.rmsnorm_fused_add_bwd if w.fused else rn.rmsnorm_bwd
+
+    def f(i, st):
+        s = S.sets[i % K]
+        if w.fused:
+            fwd(s["x"], s["residual"], s["gamma"], w.eps, w.offset)
+        else:
+            fwd(s["x"], s["gamma"], w.eps, w.offset)
+
+    def b(i, st):
+        s = S.sets[(i + K // 2) % K]
+        if w.fused:
+            bwd(s["dy"], s["dh"], s["h"], s["gamma"], s["rstd"], w.eps, w.offset)
+        else:
+            bwd(s["dy"], s["x"], s["gamma"], s["rstd"], w.eps, w.offset)
+
+    return {"fwd_us": round(time_direct(torch, f, iters, warmup), 3), "bwd_us": round(time_direct(torch, b, iters, warmup), 3)}
+
+
 def small_shape_launch_paths(lib, rn, torch, name: str = "bf16_512x2048", iters: int = 200):
     """Forward and backward of a small, host-bound workload by direct launches
     and by replay of a captured HIP graph of the same calls (cold buffers)."""
@@ -471,6 +499,7 @@ def small_shape_launch_paths(lib, rn, torch, name: str = "bf16_512x2048", iters:
         g = time_graph(torch, fn, iters)
         out[op] = {"direct_us": round(d, 3), "graph_us": round(g, 3),
                    "direct_GBs": round(nbytes / (d * 1e3), 1), "graph_GBs": round(nbytes / (g * 1e3), 1)}
+    out["python_binding"] = shim_times(S, rn, torch, iters, 20)
     del S
     torch.cuda.empty_cache()
     return out
@@ -659,8 +688,9 @@ def summarize_stats(d: str):
 
 def summarize_report(path: str):
     """Per workload of a --report run: cold-buffer times of every op (direct
-    launches; the finalizer from a graph), GB/s and % of the 8 TB/s peak,
-    hot and graph-replay times, the streaming ceilings and the plans."""
+    launches; the finalizer from a graph; shim_*: through the Python binding,
+    outputs allocated per call), GB/s and % of the 8 TB/s peak, hot and
+    graph-replay times, the streaming ceilings and the plans."""
     with open(path) as f:
         rep = json.load(f)
 
@@ -671,7 +701,7 @@ def summarize_report(path: str):
           f"{'incl. ws GB/s':>13s}")
     for wl in rep["workloads"]:
         c, h = wl["cold"], wl.get("hot", {})
-        for op in ("fwd", "bwd", "bwd_main", "finalize", "fwd_fp8", "ln_fwd", "ln_bwd"):
+        for op in ("fwd", "bwd", "bwd_main", "finalize", "fwd_fp8", "ln_fwd", "ln_bwd", "shim_fwd", "shim_bwd"):
             if op + "_us" not in c:
                 continue
             cells = [fmt(c[op + "_us"], "8.2f", 8), fmt(c.get(op + "_GBs"), "7.1f", 7),
@@ -875,6 +905,7 @@ def main():
         "bwd_incl_ws_GBs": round(cold["bwd_incl_ws_GBs"], 1),
         "fwd_pct_peak": round(cold["fwd_pct_peak"], 2), "bwd_pct_peak": round(cold["bwd_pct_peak"], 2),
         "bwd_main_us": round(main_us, 3), "finalize_us": round(cold["finalize_us"], 3),
+        "python_binding_us": {"fwd": cold["shim_fwd_us"], "bwd": cold["shim_bwd_us"]},
         "roofline": roofline, "cpu_baseline": cpu, "practical_ceilings": ceil, "small_shape_graph": small,
         "source_hash": source_hash(bwd_plan(rn, w)), "wall_s_timed_region": round(wall, 4),
     }
