@@ -307,9 +307,9 @@ def test_layernorm_plans(M, N, dt):
             p = plan(rop, M, N, dt)
             assert (p["vec"], p["team"]) == (q["vec"], q["team"])  # the same kind of layout as RMSNorm's
             nc = N // q["vec"]
-            if q["team"] == 0 and q["vec"] > 1 and nc <= 4 * 512:  # four chunks: 512-thread bound
-                # LayerNorm's forward keeps at most four chunks per lane when a tiling allows
-                assert q["chunks"] <= 4 and (q["team"] or q["threads"]) * q["chunks"] == nc, q
+            if q["team"] == 0 and q["vec"] > 1 and nc % 64 == 0:
+                # an exact workgroup tiling wherever the row has one
+                assert q["threads"] * q["chunks"] == nc, q
     for op in (rn.OP_LN_BWD, rn.OP_LN_FUSED_ADD_BWD):
         q = plan(op, M, N, dt)
         if q["path"] == rn.PATH_ROWS:
@@ -524,13 +524,14 @@ def test_override_round_trip():
             plan(rn.OP_FWD, 10, 4096, vec_ok=False)
 
 
-def test_fp8_and_layernorm_forwards_keep_their_targets():
+def test_fp8_and_layernorm_forwards_keep_their_own_rules():
     """The RMSNorm forward rule does not apply to the fp8 forward (256 threads)
-    or LayerNorm (N / 16 threads)."""
+    or LayerNorm (its own sweep table)."""
     M, N = 16384, 6144
     assert plan(rn.OP_FWD, M, N, rn.F32)["threads"] == 768
     assert plan(rn.OP_FWD_FP8, M, N, rn.F32)["threads"] == 256
-    assert plan(rn.OP_LN_FWD, M, N, rn.F32)["threads"] == 384
+    assert plan(rn.OP_LN_FWD, M, N, rn.BF16)["chunks"] == 6  # 128 threads; RMSNorm: 384 x 2
+    assert plan(rn.OP_FWD, M, N, rn.BF16)["chunks"] == 2
 
 
 _LOG_SNIPPET = r"""
@@ -729,3 +730,130 @@ def test_forward_plan_24576_takes_six_chunks():
     """bf16 4096 x 24576: 512 threads x 6 chunks (66.7 us measured against 74.1 us for 384 x 8)."""
     p = plan(rn.OP_FWD, 4096, 24576, rn.BF16)
     assert (p["threads"], p["chunks"]) == (512, 6)
+
+
+# LayerNorm forward sweep on MI355X (every exact workgroup tiling, cold rotating
+# buffers, medians of 3 interleaved rounds): per point (storage, fused-add, M,
+# N), the chunks per lane whose layout came within 3% of the fastest.  M = 256
+# x rows per compute unit.
+LN_FWD_SWEPT = [
+    ('bf16', False, 512, 2048, (2,)),
+    ('bf16', False, 1024, 2048, (2,)),
+    ('bf16', False, 2048, 2048, (2, 4)),
+    ('bf16', False, 4096, 2048, (2, 4)),
+    ('bf16', False, 8192, 2048, (2, 4)),
+    ('bf16', False, 16384, 2048, (2, 4)),
+    ('bf16', False, 512, 4096, (1, 2)),
+    ('bf16', False, 1024, 4096, (2, 4)),
+    ('bf16', False, 2048, 4096, (2, 4, 8)),
+    ('bf16', False, 4096, 4096, (2, 4)),
+    ('bf16', False, 8192, 4096, (2, 4)),
+    ('bf16', False, 16384, 4096, (2, 4, 8)),
+    ('bf16', False, 512, 6144, (1, 3)),
+    ('bf16', False, 1024, 6144, (3, 4, 6)),
+    ('bf16', False, 2048, 6144, (2, 3, 4, 6)),
+    ('bf16', False, 4096, 6144, (2, 3, 4, 6)),
+    ('bf16', False, 8192, 6144, (3, 4, 6)),
+    ('bf16', False, 16384, 6144, (4, 6)),
+    ('bf16', False, 512, 8192, (2, 4)),
+    ('bf16', False, 1024, 8192, (8,)),
+    ('bf16', False, 2048, 8192, (2, 4)),
+    ('bf16', False, 4096, 8192, (4,)),
+    ('bf16', False, 8192, 8192, (2, 4, 8)),
+    ('bf16', False, 16384, 8192, (4, 8)),
+    ('bf16', False, 512, 12288, (6,)),
+    ('bf16', False, 1024, 12288, (8,)),
+    ('bf16', False, 2048, 12288, (3, 6)),
+    ('bf16', False, 4096, 12288, (3, 6, 8)),
+    ('bf16', False, 8192, 12288, (3, 8)),
+    ('bf16', False, 16384, 12288, (8,)),
+    ('bf16', False, 512, 16384, (4, 8)),
+    ('bf16', False, 1024, 16384, (4, 8)),
+    ('bf16', False, 2048, 16384, (8,)),
+    ('bf16', False, 4096, 16384, (8,)),
+    ('bf16', False, 8192, 16384, (4, 8)),
+    ('bf16', False, 16384, 16384, (2, 4, 8)),
+    ('bf16', False, 512, 24576, (6, 8)),
+    ('bf16', False, 1024, 24576, (6,)),
+    ('bf16', False, 2048, 24576, (6,)),
+    ('bf16', False, 4096, 24576, (6,)),
+    ('bf16', False, 8192, 24576, (6,)),
+    ('bf16', False, 512, 32768, (8,)),
+    ('bf16', False, 1024, 32768, (8,)),
+    ('bf16', False, 2048, 32768, (8,)),
+    ('bf16', False, 4096, 32768, (8,)),
+    ('bf16', False, 8192, 32768, (8,)),
+    ('bf16', True, 512, 2048, (1, 2)),
+    ('bf16', True, 1024, 2048, (2,)),
+    ('bf16', True, 2048, 2048, (4,)),
+    ('bf16', True, 4096, 2048, (1, 2, 4)),
+    ('bf16', True, 8192, 2048, (1,)),
+    ('bf16', True, 16384, 2048, (1, 2, 4)),
+    ('bf16', True, 512, 4096, (1, 2, 4)),
+    ('bf16', True, 1024, 4096, (2, 4)),
+    ('bf16', True, 2048, 4096, (1, 4, 8)),
+    ('bf16', True, 4096, 4096, (1, 2, 4)),
+    ('bf16', True, 8192, 4096, (1, 2, 4)),
+    ('bf16', True, 16384, 4096, (1,)),
+    ('bf16', True, 512, 8192, (1, 4)),
+    ('bf16', True, 1024, 8192, (4, 8)),
+    ('bf16', True, 2048, 8192, (1, 2, 4)),
+    ('bf16', True, 4096, 8192, (1, 2, 4)),
+    ('bf16', True, 8192, 8192, (1, 4, 8)),
+    ('bf16', True, 16384, 8192, (1, 4, 8)),
+    ('bf16', True, 512, 16384, (8,)),
+    ('bf16', True, 1024, 16384, (8,)),
+    ('bf16', True, 2048, 16384, (2, 4, 8)),
+    ('bf16', True, 4096, 16384, (2, 4, 8)),
+    ('bf16', True, 8192, 16384, (2, 4, 8)),
+    ('bf16', True, 16384, 16384, (2, 4, 8)),
+    ('bf16', True, 512, 24576, (6, 8)),
+    ('bf16', True, 1024, 24576, (6,)),
+    ('bf16', True, 2048, 24576, (6, 8)),
+    ('bf16', True, 4096, 24576, (6,)),
+    ('bf16', True, 8192, 24576, (6,)),
+    ('f32', False, 512, 2048, (2,)),
+    ('f32', False, 1024, 2048, (8,)),
+    ('f32', False, 2048, 2048, (8,)),
+    ('f32', False, 4096, 2048, (8,)),
+    ('f32', False, 8192, 2048, (2, 4, 8)),
+    ('f32', False, 16384, 2048, (2, 4, 8)),
+    ('f32', False, 512, 4096, (4,)),
+    ('f32', False, 1024, 4096, (8,)),
+    ('f32', False, 2048, 4096, (4, 8)),
+    ('f32', False, 4096, 4096, (2, 8)),
+    ('f32', False, 8192, 4096, (2, 4, 8)),
+    ('f32', False, 16384, 4096, (2, 4, 8)),
+    ('f32', False, 512, 6144, (8,)),
+    ('f32', False, 1024, 6144, (6, 8)),
+    ('f32', False, 2048, 6144, (2, 6)),
+    ('f32', False, 4096, 6144, (2, 6)),
+    ('f32', False, 8192, 6144, (2,)),
+    ('f32', False, 16384, 6144, (2,)),
+    ('f32', False, 512, 8192, (8,)),
+    ('f32', False, 1024, 8192, (8,)),
+    ('f32', False, 2048, 8192, (8,)),
+    ('f32', False, 4096, 8192, (8,)),
+    ('f32', False, 8192, 8192, (2, 4, 8)),
+    ('f32', False, 16384, 8192, (2,)),
+    ('f32', False, 512, 12288, (8,)),
+    ('f32', False, 1024, 12288, (6,)),
+    ('f32', False, 2048, 12288, (6,)),
+    ('f32', False, 4096, 12288, (6,)),
+    ('f32', False, 8192, 12288, (6,)),
+    ('f32', False, 512, 16384, (8,)),
+    ('f32', False, 1024, 16384, (8,)),
+    ('f32', False, 2048, 16384, (8,)),
+    ('f32', False, 4096, 16384, (8,)),
+    ('f32', False, 8192, 16384, (8,)),
+]
+
+
+@pytest.mark.parametrize("dt,fused,M,N,ok", LN_FWD_SWEPT,
+                         ids=[f"{d}{'_fused' if f else ''}_{m}x{n}" for d, f, m, n, _ in LN_FWD_SWEPT])
+def test_layernorm_forward_plan_at_swept_points(dt, fused, M, N, ok):
+    p = plan(rn.OP_LN_FUSED_ADD_FWD if fused else rn.OP_LN_FWD, M, N, rn.BF16 if dt == "bf16" else rn.F32)
+    V = 8 if dt == "bf16" else 4
+    assert p["path"] == rn.PATH_ROWS and p["team"] == 0 and p["depth"] == 0
+    assert p["threads"] * p["chunks"] * V == N
+    assert p["chunks"] in ok, (p["threads"], p["chunks"], ok)

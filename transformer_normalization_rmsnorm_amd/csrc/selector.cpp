@@ -129,7 +129,7 @@ bool pick_wide_bwd_team(int op, int dtype, bool vec, int64_t nchunks, rmsnorm_pl
     return false;
 }
 
-// Forward workgroup team for LayerNorm and the fp8 output: among the compiled
+// Forward workgroup team for the fp8 output: among the compiled
 // chunk counts that tile the row exactly (no masked lanes) with a multiple of
 // 64 threads, the one whose thread count is closest to `target`; else the
 // generic choice.  Persistent forward variants were not faster.
@@ -179,7 +179,7 @@ bool pick_fwd_block_team(int op, bool vec, int64_t nchunks, int depth, int targe
 //     chunks per lane measured fastest at the nearest swept (N, rows per unit)
 //     are taken (kFwdLatency*), and the exact tiling with the nearest chunk
 //     count is launched.
-// LayerNorm and the fp8-output forward keep their own targets.
+// LayerNorm has its own table (below); the fp8-output forward its own target.
 struct FwdLatencyRow {
     int32_t n;
     int8_t k[3]; // chunks per lane at 2, 4, 8 rows per compute unit
@@ -261,6 +261,59 @@ bool pick_fwd_rms_team(int op, int dtype, int64_t M, int64_t N, int64_t nchunks,
     } else {
         rows = kFwdLatency16;
         nrows = sizeof kFwdLatency16 / sizeof kFwdLatency16[0];
+    }
+    size_t near = 0;
+    for (size_t i = 1; i < nrows; ++i)
+        if (std::fabs(std::log2((double)N / rows[i].n)) < std::fabs(std::log2((double)N / rows[near].n)))
+            near = i;
+    return pick_fwd_chunks(op, true, nchunks, rows[near].k[bucket], p) || pick_block_team(op, true, nchunks, 0, p);
+}
+
+// ---- LayerNorm forward layout (plain and fused-add) ----------------------
+//
+// Chosen from a sweep on MI355X like the RMSNorm one (every exact workgroup
+// tiling compiled, N = 2048 ... 32768 bf16 and 2048 ... 16384 fp32 plain,
+// 2048 ... 24576 bf16 fused-add, 2 ... 64 rows per compute unit, cold rotating
+// buffers, medians of 3 interleaved rounds).  No rule on rows per unit alone
+// came within 13% of the fastest at every point (the previous target, N / 16
+// threads with at least 256, missed by up to 29%: 384 x 4 at 12288 bf16), so
+// the chunks per lane measured fastest at the nearest swept (N, rows per unit)
+// are taken, preferring the neighbouring bucket's count within 1%.  Within
+// 1% of the fastest tiling at every swept point.
+struct FwdTableRow {
+    int32_t n;
+    int8_t k[6]; // chunks per lane at 2, 4, 8, 16, 32, 64 rows per compute unit
+};
+constexpr FwdTableRow kLnFwd16[] = {
+    {2048, {2, 2, 2, 2, 4, 4}}, {4096, {2, 2, 8, 4, 4, 4}},  {6144, {3, 6, 4, 4, 6, 6}},
+    {8192, {4, 8, 4, 4, 4, 4}}, {12288, {6, 8, 6, 6, 8, 8}}, {16384, {8, 8, 8, 8, 8, 8}},
+    {24576, {6, 6, 6, 6, 6, 6}}, {32768, {8, 8, 8, 8, 8, 8}},
+};
+constexpr FwdTableRow kLnFwd16Fused[] = {
+    {2048, {2, 2, 4, 4, 1, 1}},  {4096, {1, 2, 8, 2, 2, 1}},  {8192, {4, 8, 4, 4, 4, 1}},
+    {16384, {8, 8, 8, 2, 2, 8}}, {24576, {6, 6, 6, 6, 6, 6}},
+};
+constexpr FwdTableRow kLnFwd32[] = {
+    {2048, {2, 8, 8, 8, 8, 8}}, {4096, {4, 8, 8, 8, 8, 4}},  {6144, {8, 6, 2, 2, 2, 2}},
+    {8192, {8, 8, 8, 8, 8, 2}}, {12288, {8, 6, 6, 6, 6, 6}}, {16384, {8, 8, 8, 8, 8, 8}},
+};
+
+bool pick_fwd_ln_team(int op, int dtype, int64_t M, int64_t N, int64_t nchunks, int num_cus, rmsnorm_plan *p)
+{
+    const double rows_per_cu = (double)M / (double)std::max(num_cus, 1);
+    // the nearest of 2, 4, ..., 64 rows per unit on a log scale
+    const int bucket = rows_per_cu < 2.0 ? 0 : (int)std::min<long>(5, std::lround(std::log2(rows_per_cu)) - 1);
+    const FwdTableRow *rows;
+    size_t nrows;
+    if (dtype == RMSNORM_F32) {
+        rows = kLnFwd32;
+        nrows = sizeof kLnFwd32 / sizeof kLnFwd32[0];
+    } else if (is_fused(op)) {
+        rows = kLnFwd16Fused;
+        nrows = sizeof kLnFwd16Fused / sizeof kLnFwd16Fused[0];
+    } else {
+        rows = kLnFwd16;
+        nrows = sizeof kLnFwd16 / sizeof kLnFwd16[0];
     }
     size_t near = 0;
     for (size_t i = 1; i < nrows; ++i)
@@ -399,11 +452,7 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             // fp8 output (a quarter or half of the bf16 / fp32 output bytes):
             // 256 threads at every measured size (4096 x 4096 bf16: 10.4 us
             // against 10.7 us at 128; 16384 x 8192: 64.0 against 68.4 us)
-            // LayerNorm's forward also holds beta and makes two reductions: at
-            // most four chunks per lane where a tiling allows (measured: 4096 x
-            // 16384 bf16 50.5 us at 512 threads against 53.1 us at 256;
-            // 16384 x 8192: 91.4 us at 256 against 94.0 us at 128)
-            const int target = is_ln_op(op) ? (int)std::max<int64_t>(256, nchunks / 4) : 256;
+            const int target = 256;
             // backward: w in registers with one chunk per lane (the pages'
             // layout), else gamma re-read per row.  Measured on MI355X, gamma
             // per row with two chunks per lane and one row ahead beats w in
@@ -412,8 +461,10 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             if (bwd)
                 placed = (nchunks <= 1024 && pick_block_team(op, true, nchunks, p.depth, &p)) ||
                          pick_wide_bwd_team(op, dtype, true, nchunks, &p);
-            else if (is_ln_op(op) || is_fp8_op(op))
+            else if (is_fp8_op(op))
                 placed = pick_fwd_block_team(op, true, nchunks, p.depth, target, &p);
+            else if (is_ln_op(op))
+                placed = pick_fwd_ln_team(op, dtype, M, N, nchunks, num_cus, &p);
             else
                 placed = pick_fwd_rms_team(op, dtype, M, N, nchunks, num_cus, &p);
         }
