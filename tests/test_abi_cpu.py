@@ -274,14 +274,15 @@ def test_wide_backward_rows_stay_in_registers(N, dt, fused, want):
 def test_fp8_plans_follow_the_forward(M, N, dt):
     for op, op8 in ((rn.OP_FWD, rn.OP_FWD_FP8), (rn.OP_FUSED_ADD_FWD, rn.OP_FUSED_ADD_FWD_FP8)):
         p, q = plan(op, M, N, dt), plan(op8, M, N, dt)
-        # the same kind of layout; workgroup teams aim at 256 threads for fp8 output
+        # the same kind of layout (the workgroup tiling from the fp8 forward's own table)
         for k in ("path", "vec", "depth"):
             assert p[k] == q[k], (k, p, q)
         assert (p["team"] == 0) == (q["team"] == 0)
         if q["path"] == rn.PATH_ROWS:
             assert covers(q, N) and q["depth"] == 0
-            if q["team"] == 0 and q["vec"] > 1 and (N // q["vec"]) % 256 == 0 and N // q["vec"] // 256 <= 8:
-                assert q["threads"] == 256
+            if q["team"] == 0 and q["vec"] > 1 and (N // q["vec"]) % 64 == 0:
+                # an exact workgroup tiling wherever the row has one
+                assert q["threads"] * q["chunks"] == N // q["vec"], q
         assert q["programs"] == q["grid"] and q["fin_grid"] == 1 and q["fin_threads"] == 1024
         assert q["workspace_bytes"] == -(-q["grid"] * 4 // 256) * 256
         assert p["workspace_bytes"] == 0 and p["programs"] == 0
@@ -525,12 +526,13 @@ def test_override_round_trip():
 
 
 def test_fp8_and_layernorm_forwards_keep_their_own_rules():
-    """The RMSNorm forward rule does not apply to the fp8 forward (256 threads)
-    or LayerNorm (its own sweep table)."""
+    """The RMSNorm forward rule applies to neither the fp8 forward nor
+    LayerNorm: each has its own sweep table."""
     M, N = 16384, 6144
     assert plan(rn.OP_FWD, M, N, rn.F32)["threads"] == 768
-    assert plan(rn.OP_FWD_FP8, M, N, rn.F32)["threads"] == 256
-    assert plan(rn.OP_LN_FWD, M, N, rn.BF16)["chunks"] == 6  # 128 threads; RMSNorm: 384 x 2
+    assert plan(rn.OP_FWD_FP8, M, N, rn.F32)["chunks"] == 6  # 256 threads
+    assert plan(rn.OP_LN_FWD, M, N, rn.BF16)["chunks"] == 6  # 128 threads
+    assert plan(rn.OP_FWD_FP8, M, N, rn.BF16)["chunks"] == 3  # 256 threads
     assert plan(rn.OP_FWD, M, N, rn.BF16)["chunks"] == 2
 
 
@@ -853,6 +855,130 @@ LN_FWD_SWEPT = [
                          ids=[f"{d}{'_fused' if f else ''}_{m}x{n}" for d, f, m, n, _ in LN_FWD_SWEPT])
 def test_layernorm_forward_plan_at_swept_points(dt, fused, M, N, ok):
     p = plan(rn.OP_LN_FUSED_ADD_FWD if fused else rn.OP_LN_FWD, M, N, rn.BF16 if dt == "bf16" else rn.F32)
+    V = 8 if dt == "bf16" else 4
+    assert p["path"] == rn.PATH_ROWS and p["team"] == 0 and p["depth"] == 0
+    assert p["threads"] * p["chunks"] * V == N
+    assert p["chunks"] in ok, (p["threads"], p["chunks"], ok)
+
+
+# fp8-output forward sweep on MI355X, as the LayerNorm one above.
+F8_FWD_SWEPT = [
+    ('bf16', False, 512, 2048, (1, 2, 4)),
+    ('bf16', False, 1024, 2048, (2,)),
+    ('bf16', False, 2048, 2048, (1, 4)),
+    ('bf16', False, 4096, 2048, (2,)),
+    ('bf16', False, 8192, 2048, (2, 4)),
+    ('bf16', False, 16384, 2048, (2, 4)),
+    ('bf16', False, 512, 4096, (2,)),
+    ('bf16', False, 1024, 4096, (2, 4, 8)),
+    ('bf16', False, 2048, 4096, (2, 4)),
+    ('bf16', False, 4096, 4096, (4, 8)),
+    ('bf16', False, 8192, 4096, (4, 8)),
+    ('bf16', False, 16384, 4096, (4, 8)),
+    ('bf16', False, 512, 6144, (1, 4, 6)),
+    ('bf16', False, 1024, 6144, (2, 3, 6)),
+    ('bf16', False, 2048, 6144, (3, 4)),
+    ('bf16', False, 4096, 6144, (3, 4)),
+    ('bf16', False, 8192, 6144, (3, 4, 6)),
+    ('bf16', False, 16384, 6144, (3, 4)),
+    ('bf16', False, 512, 8192, (1, 2, 4)),
+    ('bf16', False, 1024, 8192, (2, 4)),
+    ('bf16', False, 2048, 8192, (4,)),
+    ('bf16', False, 4096, 8192, (4, 8)),
+    ('bf16', False, 8192, 8192, (4, 8)),
+    ('bf16', False, 16384, 8192, (4, 8)),
+    ('bf16', False, 512, 12288, (6,)),
+    ('bf16', False, 1024, 12288, (8,)),
+    ('bf16', False, 2048, 12288, (6, 8)),
+    ('bf16', False, 4096, 12288, (8,)),
+    ('bf16', False, 8192, 12288, (8,)),
+    ('bf16', False, 16384, 12288, (8,)),
+    ('bf16', False, 512, 16384, (4, 8)),
+    ('bf16', False, 1024, 16384, (8,)),
+    ('bf16', False, 2048, 16384, (8,)),
+    ('bf16', False, 4096, 16384, (8,)),
+    ('bf16', False, 8192, 16384, (8,)),
+    ('bf16', False, 16384, 16384, (8,)),
+    ('bf16', False, 512, 24576, (8,)),
+    ('bf16', False, 1024, 24576, (6, 8)),
+    ('bf16', False, 2048, 24576, (8,)),
+    ('bf16', False, 4096, 24576, (8,)),
+    ('bf16', False, 8192, 24576, (8,)),
+    ('bf16', False, 512, 32768, (8,)),
+    ('bf16', False, 1024, 32768, (8,)),
+    ('bf16', False, 2048, 32768, (8,)),
+    ('bf16', False, 4096, 32768, (8,)),
+    ('bf16', False, 8192, 32768, (8,)),
+    ('bf16', True, 512, 2048, (1, 4)),
+    ('bf16', True, 1024, 2048, (2,)),
+    ('bf16', True, 2048, 2048, (4,)),
+    ('bf16', True, 4096, 2048, (2, 4)),
+    ('bf16', True, 8192, 2048, (1, 2, 4)),
+    ('bf16', True, 16384, 2048, (1, 2, 4)),
+    ('bf16', True, 512, 4096, (1, 2)),
+    ('bf16', True, 1024, 4096, (2, 4, 8)),
+    ('bf16', True, 2048, 4096, (2, 4, 8)),
+    ('bf16', True, 4096, 4096, (2, 4)),
+    ('bf16', True, 8192, 4096, (2, 4)),
+    ('bf16', True, 16384, 4096, (2, 4)),
+    ('bf16', True, 512, 8192, (2, 4)),
+    ('bf16', True, 1024, 8192, (2, 4)),
+    ('bf16', True, 2048, 8192, (2, 4)),
+    ('bf16', True, 4096, 8192, (2, 4)),
+    ('bf16', True, 8192, 8192, (2, 4)),
+    ('bf16', True, 16384, 8192, (2, 4)),
+    ('bf16', True, 512, 16384, (8,)),
+    ('bf16', True, 1024, 16384, (2, 4, 8)),
+    ('bf16', True, 2048, 16384, (2, 4, 8)),
+    ('bf16', True, 4096, 16384, (2, 4, 8)),
+    ('bf16', True, 8192, 16384, (2, 4, 8)),
+    ('bf16', True, 16384, 16384, (2, 4, 8)),
+    ('bf16', True, 512, 24576, (6,)),
+    ('bf16', True, 1024, 24576, (6,)),
+    ('bf16', True, 2048, 24576, (6,)),
+    ('bf16', True, 4096, 24576, (6,)),
+    ('bf16', True, 8192, 24576, (6,)),
+    ('f32', False, 512, 2048, (1, 4, 8)),
+    ('f32', False, 1024, 2048, (1, 2)),
+    ('f32', False, 2048, 2048, (8,)),
+    ('f32', False, 4096, 2048, (4, 8)),
+    ('f32', False, 8192, 2048, (4, 8)),
+    ('f32', False, 16384, 2048, (4, 8)),
+    ('f32', False, 512, 4096, (2, 4)),
+    ('f32', False, 1024, 4096, (8,)),
+    ('f32', False, 2048, 4096, (4, 8)),
+    ('f32', False, 4096, 4096, (4, 8)),
+    ('f32', False, 8192, 4096, (4, 8)),
+    ('f32', False, 16384, 4096, (4, 8)),
+    ('f32', False, 512, 6144, (6, 8)),
+    ('f32', False, 1024, 6144, (6, 8)),
+    ('f32', False, 2048, 6144, (6, 8)),
+    ('f32', False, 4096, 6144, (6, 8)),
+    ('f32', False, 8192, 6144, (6, 8)),
+    ('f32', False, 16384, 6144, (6, 8)),
+    ('f32', False, 512, 8192, (8,)),
+    ('f32', False, 1024, 8192, (8,)),
+    ('f32', False, 2048, 8192, (8,)),
+    ('f32', False, 4096, 8192, (8,)),
+    ('f32', False, 8192, 8192, (8,)),
+    ('f32', False, 16384, 8192, (8,)),
+    ('f32', False, 512, 12288, (6, 8)),
+    ('f32', False, 1024, 12288, (6,)),
+    ('f32', False, 2048, 12288, (6,)),
+    ('f32', False, 4096, 12288, (6,)),
+    ('f32', False, 8192, 12288, (6,)),
+    ('f32', False, 512, 16384, (8,)),
+    ('f32', False, 1024, 16384, (8,)),
+    ('f32', False, 2048, 16384, (8,)),
+    ('f32', False, 4096, 16384, (8,)),
+    ('f32', False, 8192, 16384, (8,)),
+]
+
+
+@pytest.mark.parametrize("dt,fused,M,N,ok", F8_FWD_SWEPT,
+                         ids=[f"{d}{'_fused' if f else ''}_{m}x{n}" for d, f, m, n, _ in F8_FWD_SWEPT])
+def test_fp8_forward_plan_at_swept_points(dt, fused, M, N, ok):
+    p = plan(rn.OP_FUSED_ADD_FWD_FP8 if fused else rn.OP_FWD_FP8, M, N, rn.BF16 if dt == "bf16" else rn.F32)
     V = 8 if dt == "bf16" else 4
     assert p["path"] == rn.PATH_ROWS and p["team"] == 0 and p["depth"] == 0
     assert p["threads"] * p["chunks"] * V == N

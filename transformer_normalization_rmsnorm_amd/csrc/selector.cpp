@@ -129,39 +129,6 @@ bool pick_wide_bwd_team(int op, int dtype, bool vec, int64_t nchunks, rmsnorm_pl
     return false;
 }
 
-// Forward workgroup team for the fp8 output: among the compiled
-// chunk counts that tile the row exactly (no masked lanes) with a multiple of
-// 64 threads, the one whose thread count is closest to `target`; else the
-// generic choice.  Persistent forward variants were not faster.
-bool pick_fwd_block_team(int op, bool vec, int64_t nchunks, int depth, int target, rmsnorm_plan *p)
-{
-    const int kFwdThreads = target;
-    int best_k = 0;
-    int64_t best_t = 0;
-    for (int k = 1; k <= 16; ++k) {
-        const int b = bound(op, vec, 0, k, depth, 0);
-        if (b == 0 || nchunks % k != 0)
-            continue;
-        const int64_t t = nchunks / k;
-        if (t % 64 != 0 || t > b)
-            continue;
-        const int64_t d = t > kFwdThreads ? t - kFwdThreads : kFwdThreads - t;
-        const int64_t bd = best_t > kFwdThreads ? best_t - kFwdThreads : kFwdThreads - best_t;
-        if (best_k == 0 || d < bd) {
-            best_k = k;
-            best_t = t;
-        }
-    }
-    if (best_k == 0)
-        return pick_block_team(op, vec, nchunks, depth, p);
-    p->team = 0;
-    p->threads = (int32_t)best_t;
-    p->chunks = best_k;
-    p->depth = depth;
-    p->w_regs = 0;
-    return true;
-}
-
 // ---- RMSNorm forward layout (plain and fused-add) -------------------------
 //
 // Chosen from a sweep on MI355X of every exact workgroup tiling compiled
@@ -179,7 +146,7 @@ bool pick_fwd_block_team(int op, bool vec, int64_t nchunks, int depth, int targe
 //     chunks per lane measured fastest at the nearest swept (N, rows per unit)
 //     are taken (kFwdLatency*), and the exact tiling with the nearest chunk
 //     count is launched.
-// LayerNorm has its own table (below); the fp8-output forward its own target.
+// LayerNorm and the fp8-output forward have their own tables (below).
 struct FwdLatencyRow {
     int32_t n;
     int8_t k[3]; // chunks per lane at 2, 4, 8 rows per compute unit
@@ -269,17 +236,19 @@ bool pick_fwd_rms_team(int op, int dtype, int64_t M, int64_t N, int64_t nchunks,
     return pick_fwd_chunks(op, true, nchunks, rows[near].k[bucket], p) || pick_block_team(op, true, nchunks, 0, p);
 }
 
-// ---- LayerNorm forward layout (plain and fused-add) ----------------------
+// ---- LayerNorm and fp8-output forward layouts (plain and fused-add) -------
 //
-// Chosen from a sweep on MI355X like the RMSNorm one (every exact workgroup
-// tiling compiled, N = 2048 ... 32768 bf16 and 2048 ... 16384 fp32 plain,
-// 2048 ... 24576 bf16 fused-add, 2 ... 64 rows per compute unit, cold rotating
-// buffers, medians of 3 interleaved rounds).  No rule on rows per unit alone
-// came within 13% of the fastest at every point (the previous target, N / 16
-// threads with at least 256, missed by up to 29%: 384 x 4 at 12288 bf16), so
-// the chunks per lane measured fastest at the nearest swept (N, rows per unit)
-// are taken, preferring the neighbouring bucket's count within 1%.  Within
-// 1% of the fastest tiling at every swept point.
+// Each chosen from a sweep on MI355X like the RMSNorm one (every exact
+// workgroup tiling compiled, N = 2048 ... 32768 bf16 and 2048 ... 16384 fp32
+// plain, 2048 ... 24576 bf16 fused-add, 2 ... 64 rows per compute unit, cold
+// rotating buffers, medians of 3 interleaved rounds).  No rule on rows per
+// unit alone came within 13% of the fastest at every point, and the previous
+// fixed targets missed by up to 29% (LayerNorm: N / 16 threads, at least 256,
+// e.g. 384 x 4 at 12288 bf16) and 33% (fp8: 256 threads, e.g. 256 x 1 at 2048
+// bf16 with 64 rows per unit).  So the chunks per lane measured fastest at the
+// nearest swept (N, rows per unit) are taken, preferring the neighbouring
+// bucket's count within 1%; within 1% of the fastest tiling at every swept
+// point of the sweep each table was built from.
 struct FwdTableRow {
     int32_t n;
     int8_t k[6]; // chunks per lane at 2, 4, 8, 16, 32, 64 rows per compute unit
@@ -297,24 +266,29 @@ constexpr FwdTableRow kLnFwd32[] = {
     {2048, {2, 8, 8, 8, 8, 8}}, {4096, {4, 8, 8, 8, 8, 4}},  {6144, {8, 6, 2, 2, 2, 2}},
     {8192, {8, 8, 8, 8, 8, 2}}, {12288, {8, 6, 6, 6, 6, 6}}, {16384, {8, 8, 8, 8, 8, 8}},
 };
+constexpr FwdTableRow kF8Fwd16[] = {
+    {2048, {2, 2, 4, 2, 2, 4}}, {4096, {2, 2, 2, 4, 8, 8}},  {6144, {4, 2, 3, 3, 3, 3}},
+    {8192, {4, 4, 4, 4, 8, 8}}, {12288, {6, 8, 8, 8, 8, 8}}, {16384, {8, 8, 8, 8, 8, 8}},
+    {24576, {8, 8, 8, 8, 8, 8}}, {32768, {8, 8, 8, 8, 8, 8}},
+};
+constexpr FwdTableRow kF8Fwd16Fused[] = {
+    {2048, {4, 2, 4, 4, 4, 4}},  {4096, {2, 8, 8, 4, 2, 2}},  {8192, {2, 2, 2, 2, 2, 2}},
+    {16384, {8, 2, 2, 2, 2, 2}}, {24576, {6, 6, 6, 6, 6, 6}},
+};
+constexpr FwdTableRow kF8Fwd32[] = {
+    {2048, {4, 2, 8, 8, 8, 8}}, {4096, {4, 8, 4, 8, 8, 8}},  {6144, {6, 6, 6, 6, 6, 6}},
+    {8192, {8, 8, 8, 8, 8, 8}}, {12288, {6, 6, 6, 6, 6, 6}}, {16384, {8, 8, 8, 8, 8, 8}},
+};
 
-bool pick_fwd_ln_team(int op, int dtype, int64_t M, int64_t N, int64_t nchunks, int num_cus, rmsnorm_plan *p)
+template <size_t A, size_t B, size_t C>
+bool pick_fwd_table(int op, int dtype, int64_t M, int64_t N, int64_t nchunks, int num_cus, const FwdTableRow (&t16)[A],
+                    const FwdTableRow (&t16_fused)[B], const FwdTableRow (&t32)[C], rmsnorm_plan *p)
 {
     const double rows_per_cu = (double)M / (double)std::max(num_cus, 1);
     // the nearest of 2, 4, ..., 64 rows per unit on a log scale
     const int bucket = rows_per_cu < 2.0 ? 0 : (int)std::min<long>(5, std::lround(std::log2(rows_per_cu)) - 1);
-    const FwdTableRow *rows;
-    size_t nrows;
-    if (dtype == RMSNORM_F32) {
-        rows = kLnFwd32;
-        nrows = sizeof kLnFwd32 / sizeof kLnFwd32[0];
-    } else if (is_fused(op)) {
-        rows = kLnFwd16Fused;
-        nrows = sizeof kLnFwd16Fused / sizeof kLnFwd16Fused[0];
-    } else {
-        rows = kLnFwd16;
-        nrows = sizeof kLnFwd16 / sizeof kLnFwd16[0];
-    }
+    const FwdTableRow *rows = dtype == RMSNORM_F32 ? t32 : is_fused(op) ? t16_fused : t16;
+    const size_t nrows = dtype == RMSNORM_F32 ? C : is_fused(op) ? B : A;
     size_t near = 0;
     for (size_t i = 1; i < nrows; ++i)
         if (std::fabs(std::log2((double)N / rows[i].n)) < std::fabs(std::log2((double)N / rows[near].n)))
@@ -449,10 +423,6 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             p.threads = kRowsThreads;
             placed = true;
         } else {
-            // fp8 output (a quarter or half of the bf16 / fp32 output bytes):
-            // 256 threads at every measured size (4096 x 4096 bf16: 10.4 us
-            // against 10.7 us at 128; 16384 x 8192: 64.0 against 68.4 us)
-            const int target = 256;
             // backward: w in registers with one chunk per lane (the pages'
             // layout), else gamma re-read per row.  Measured on MI355X, gamma
             // per row with two chunks per lane and one row ahead beats w in
@@ -462,9 +432,9 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
                 placed = (nchunks <= 1024 && pick_block_team(op, true, nchunks, p.depth, &p)) ||
                          pick_wide_bwd_team(op, dtype, true, nchunks, &p);
             else if (is_fp8_op(op))
-                placed = pick_fwd_block_team(op, true, nchunks, p.depth, target, &p);
+                placed = pick_fwd_table(op, dtype, M, N, nchunks, num_cus, kF8Fwd16, kF8Fwd16Fused, kF8Fwd32, &p);
             else if (is_ln_op(op))
-                placed = pick_fwd_ln_team(op, dtype, M, N, nchunks, num_cus, &p);
+                placed = pick_fwd_table(op, dtype, M, N, nchunks, num_cus, kLnFwd16, kLnFwd16Fused, kLnFwd32, &p);
             else
                 placed = pick_fwd_rms_team(op, dtype, M, N, nchunks, num_cus, &p);
         }
