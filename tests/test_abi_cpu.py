@@ -204,8 +204,12 @@ def test_plans_for_workloads(M, N, dt, fused):
     assert f["depth"] == 0 and f["grid"] == -(-M // (1 if f["team"] == 0 else f["threads"] // f["team"]))
     assert b["programs"] == b["grid"]
     # w = gamma + offset stays in registers when one chunk per lane covers the
-    # row; the forward has no such field
-    assert b["w_regs"] == (1 if N // vec <= 1024 else 0) and f["w_regs"] == 0
+    # row, except the fused-add op at 896 or more lanes with 8+ rows per program
+    # (half the lanes, two chunks, gamma re-read); the forward has no such field
+    half = fused and N // vec >= 896 and N // vec <= 1024 and M >= 8 * CUS
+    assert b["w_regs"] == (1 if N // vec <= 1024 and not half else 0) and f["w_regs"] == 0
+    if half:
+        assert (b["threads"], b["chunks"], b["depth"]) == (N // vec // 2, 2, 1)
     ld = -(-N // 64) * 64
     assert b["workspace_bytes"] == -(-b["programs"] * ld * 4 // 256) * 256 + -(-M * 4 // 256) * 256
     assert b["fin_grid"] == ld // 32
@@ -395,14 +399,21 @@ def test_forward_grid_keeps_work_items_below_2_31():
 
 def test_backward_rows_in_flight_follow_rows_per_program():
     """Two rows in flight from 32 rows per program (w in registers), one below;
-    fused-add LayerNorm keeps one; layouts that reduce two rows together keep
-    depth 1 (their next two rows are in flight)."""
-    for op in (rn.OP_BWD, rn.OP_FUSED_ADD_BWD, rn.OP_LN_BWD):
+    the fused-add ops keep one (RMSNorm's fused-add takes half the lanes with
+    two chunks at 896+ lanes from 8 rows per program); layouts that reduce two
+    rows together keep depth 1 (their next two rows are in flight)."""
+    for op in (rn.OP_BWD, rn.OP_LN_BWD):
         assert plan(op, 16384, 8192)["depth"] == 2
         assert plan(op, 1024, 8192)["depth"] == 1
-    for op in (rn.OP_FUSED_ADD_BWD, rn.OP_LN_BWD):  # 512 threads: no two-row reduction for these
-        assert plan(op, 256 * 32, 4096)["depth"] == 2
-        assert plan(op, 256 * 31, 4096)["depth"] == 1
+    p = plan(rn.OP_FUSED_ADD_BWD, 16384, 8192)
+    assert (p["threads"], p["chunks"], p["depth"], p["w_regs"]) == (512, 2, 1, 0)
+    p = plan(rn.OP_FUSED_ADD_BWD, 256 * 7, 8192)
+    assert (p["threads"], p["chunks"], p["depth"], p["w_regs"]) == (1024, 1, 1, 1)
+    assert plan(rn.OP_LN_BWD, 256 * 32, 4096)["depth"] == 2  # 512 threads: no two-row reduction
+    assert plan(rn.OP_LN_BWD, 256 * 31, 4096)["depth"] == 1
+    for M in (256 * 31, 256 * 32, 16384):  # 512 lanes: neither two rows in flight nor half the lanes
+        p = plan(rn.OP_FUSED_ADD_BWD, M, 4096)
+        assert (p["threads"], p["chunks"], p["depth"], p["w_regs"]) == (512, 1, 1, 1)
     p = plan(rn.OP_BWD, 256 * 32, 4096)
     assert (p["depth"], p["rows_per_step"]) == (1, 2)
     assert plan(rn.OP_LN_FUSED_ADD_BWD, 16384, 8192)["depth"] == 1
@@ -491,7 +502,7 @@ def test_override_round_trip():
         with pytest.raises(rn.RMSNormError):
             plan(rn.OP_BWD, 100, 16384)
     with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=1024, w_regs=0):
-        p = plan(rn.OP_BWD, 100, 16384)
+        p = plan(rn.OP_BWD, 4096, 16384)
         assert (p["chunks"], p["depth"], p["w_regs"]) == (2, 1, 0)
     # an unset w_regs takes the selector's (1 here), or the other one when only
     # that one is compiled for the layout (two chunks, no prefetch)
@@ -983,3 +994,16 @@ def test_fp8_forward_plan_at_swept_points(dt, fused, M, N, ok):
     assert p["path"] == rn.PATH_ROWS and p["team"] == 0 and p["depth"] == 0
     assert p["threads"] * p["chunks"] * V == N
     assert p["chunks"] in ok, (p["threads"], p["chunks"], ok)
+
+
+@pytest.mark.parametrize("dt,N", [(rn.BF16, 12288), (rn.BF16, 16384), (rn.F32, 6144), (rn.F32, 8192)])
+@pytest.mark.parametrize("op", [rn.OP_BWD, rn.OP_FUSED_ADD_BWD])
+def test_wide_backward_without_lookahead_at_two_rows_per_program(op, dt, N):
+    """Rows with gamma re-read per row take no row ahead when each program has
+    at most two rows (measured faster on MI355X), and keep it from three."""
+    programs = 256
+    for M, depth in ((2 * programs, 0), (2 * programs - 7, 0), (programs, 0), (2 * programs + 1, 1), (4 * programs, 1)):
+        p = plan(op, M, N, dt)
+        assert p["w_regs"] == 0 and p["depth"] == depth, (M, p)
+    # LayerNorm keeps its own (unswept) choice
+    assert plan(rn.OP_LN_BWD, 2 * programs, N, dt)["depth"] == plan(rn.OP_LN_BWD, 4 * programs, N, dt)["depth"]

@@ -23,6 +23,11 @@ constexpr int kLoopThreads = 1024;  // looped path workgroup size
 constexpr int kBwdProgramsPerCU = 1; // persistent backward workgroup teams per compute unit
 constexpr int kBwdTeamsPerCU = 2;    // persistent backward workgroups per compute unit (sub-wave teams)
 constexpr int64_t kDeepRowsPerProgram = 32; // backward rows per program from which two rows are in flight
+// fused-add backward: from this many rows per program, workgroups of at least
+// kFusedHalfMinThreads with one chunk per lane and w in registers take half
+// the lanes with two chunks each and gamma re-read per row
+constexpr int64_t kFusedHalfRowsPerProgram = 8;
+constexpr int kFusedHalfMinThreads = 896;
 // Workgroups of at most this many threads reduce two rows together wherever
 // the layout allows (bwd_pairs_compiled), ahead of two rows in flight one at
 // a time.  Measured on MI355X, bf16 backward main, one row / two rows in
@@ -463,8 +468,37 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             bwd_pairs_compiled(is_ln_op(op), is_fused(op), p.team, p.chunks, p.depth, p.w_regs, p.vec) &&
             p.threads <= bwd_pairs_bound(is_fused(op)))
             p.rows_per_step = 2;
-        else if (rows >= kDeepRowsPerProgram && bound(op, vec, 0, p.chunks, 2, 1) >= p.threads)
+        else if (is_fused(op) && p.chunks == 1 && p.threads >= kFusedHalfMinThreads &&
+                 rows >= kFusedHalfRowsPerProgram && (p.threads / 2) % 64 == 0 &&
+                 bound(op, vec, 0, 2, 1, 0) >= p.threads / 2 &&
+                 tiling_ok(op, dtype, vec, 0, 2, bound(op, vec, 0, 2, 1, 0), p.threads / 2, nchunks)) {
+            // The fused-add op also holds dh: at 896 or more lanes with w in
+            // registers, half the lanes with two chunks each and gamma re-read
+            // per row run faster once programs have several rows (sweep of the
+            // backward layouts on MI355X, bf16 8192 wide at 8 to 64 rows per
+            // compute unit 1-4.5%, fp32 4096 wide 1.4-2.9%; 16384 x 7168
+            // bf16 148.9 against 157.1 us).  At 768 lanes or fewer it was not
+            // faster.
+            p.threads /= 2;
+            p.chunks = 2;
+            p.w_regs = 0;
+            p.depth = 1;
+        } else if (!is_fused(op) && rows >= kDeepRowsPerProgram && bound(op, vec, 0, p.chunks, 2, 1) >= p.threads)
+            // (the fused-add op was 1.5-3.5% slower with two rows in flight in
+            // the same sweep)
             p.depth = 2;
+    } else if (bwd && p.team == 0 && p.w_regs == 0 && p.depth > 0 && !is_ln_op(op)) {
+        // Wide rows (gamma re-read per row) with at most two rows per
+        // program: no row ahead.  From a sweep of the backward layouts on
+        // MI355X at 2 rows per compute unit: fp32 8192 wide 13% and 6144 wide
+        // 9% faster (fused-add 16% and 15%), bf16 fused-add 12288 and 16384
+        // wide 7% and 10%, bf16 16384 wide 5%; at four rows per program the
+        // plain bf16 rows lost up to 7%, so the rule stops at two.
+        const int64_t programs = (int64_t)kBwdProgramsPerCU * std::max(num_cus, 1);
+        const int b0 = bound(op, vec, 0, p.chunks, 0, 0);
+        if (ceil_div(M, programs) <= 2 && b0 >= p.threads &&
+            tiling_ok(op, dtype, vec, 0, p.chunks, b0, p.threads, nchunks))
+            p.depth = 0;
     }
     if (!complete_plan(&p, M, N, dtype, num_cus, false))
         return RMSNORM_EUNSUPPORTED;
