@@ -487,13 +487,15 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             // (the fused-add op was 1.5-3.5% slower with two rows in flight in
             // the same sweep)
             p.depth = 2;
-    } else if (bwd && p.team == 0 && p.w_regs == 0 && p.depth > 0 && !is_ln_op(op)) {
+    } else if (bwd && p.team == 0 && p.w_regs == 0 && p.depth > 0) {
         // Wide rows (gamma re-read per row) with at most two rows per
-        // program: no row ahead.  From a sweep of the backward layouts on
-        // MI355X at 2 rows per compute unit: fp32 8192 wide 13% and 6144 wide
-        // 9% faster (fused-add 16% and 15%), bf16 fused-add 12288 and 16384
-        // wide 7% and 10%, bf16 16384 wide 5%; at four rows per program the
-        // plain bf16 rows lost up to 7%, so the rule stops at two.
+        // program: no row ahead.  From sweeps of the backward layouts on
+        // MI355X at 2 rows per compute unit, RMSNorm: fp32 8192 wide 13% and
+        // 6144 wide 9% faster (fused-add 16% and 15%), bf16 fused-add 12288
+        // and 16384 wide 7% and 10%, bf16 16384 wide 5%; LayerNorm: fp32
+        // 6144 and 8192 wide 7% and 5% (fused-add 17% and 12%), bf16 fused-add
+        // 12288 and 16384 wide 5% and 4%.  At four rows per program the plain
+        // bf16 rows lost up to 7%, so the rule stops at two.
         const int64_t programs = (int64_t)kBwdProgramsPerCU * std::max(num_cus, 1);
         const int b0 = bound(op, vec, 0, p.chunks, 0, 0);
         if (ceil_div(M, programs) <= 2 && b0 >= p.threads &&
