@@ -591,13 +591,13 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str):
     programs = None
     out = [f"# HBM traffic per dispatch, {workload} (rocprofv3 PMC counters)",
            "#",
-           "# Commands (run from /tmp with TMPDIR=/tmp, repository root R):",
-           f"#   timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/pmc_fetch_{workload} "
+           "# Commands (run from /tmp with TMPDIR=/tmp, repository root R, output directory O):",
+           f"#   timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $O/pmc_fetch_{workload} "
            f"-o fetch -- python3 $R/bench.py --counters-run --workload {workload}",
-           f"#   timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/pmc_write_{workload} "
+           f"#   timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $O/pmc_write_{workload} "
            f"-o write -- python3 $R/bench.py --counters-run --workload {workload}",
-           f"#   python3 $R/bench.py --summarize-counters $R/gpurun_out/pmc_fetch_{workload} "
-           f"$R/gpurun_out/pmc_write_{workload} --workload {workload}",
+           f"#   python3 $R/bench.py --summarize-counters $O/pmc_fetch_{workload} "
+           f"$O/pmc_write_{workload} --workload {workload}",
            "# bench.py --counters-run launches five 256 MiB device copies, then five forward, five backward-main",
            "# and five finalizer dispatches of the workload (four rotating buffer sets).",
            "#",
