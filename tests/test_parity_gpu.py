@@ -163,6 +163,12 @@ WIDE_FORCED = [
     (True, 40, 16384, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=0, w_regs=0, grid=7)),
     (True, 40, 16000, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=1, w_regs=0, grid=6)),
     (True, 60, 8192, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=2, w_regs=0, grid=9)),
+    # half the lanes with gamma re-read, one row ahead: the fused-add op's choice from 896 lanes and 8 rows
+    # per program; and no row ahead at two rows per program
+    (True, 60, 8192, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=1, w_regs=0, grid=7)),
+    (True, 60, 7168, "bf16", dict(path=R, vec=8, team=0, threads=448, depth=1, w_regs=0, grid=7)),
+    (True, 60, 4096, "f32", dict(path=R, vec=4, team=0, threads=512, depth=1, w_regs=0, grid=7)),
+    (True, 30, 6144, "f32", dict(path=R, vec=4, team=0, threads=768, depth=0, w_regs=0, grid=16)),
     (True, 60, 4096, "f32", dict(path=R, vec=4, team=0, threads=512, depth=2, w_regs=0, grid=13)),
     (True, 30, 24576, "bf16", dict(path=R, vec=8, team=0, threads=1024, depth=0, w_regs=0, grid=4)),
     (True, 30, 12000, "f32", dict(path=R, vec=4, team=0, threads=1024, depth=0, w_regs=0, grid=4)),
