@@ -433,15 +433,18 @@ def test_backward_rows_in_flight_follow_rows_per_program():
 ])
 def test_two_rows_per_reduction(M, N, dt, want):
     """rows_per_step = 2 for RMSNorm workgroup teams with w in registers, one
-    chunk per lane, at most 512 threads (fused-add: 256) and two or more rows
-    per program; never for LayerNorm, nor for the forward."""
+    chunk per lane, at most 512 threads (fused-add and plain LayerNorm: 256)
+    and two or more rows per program; never for fused-add LayerNorm, nor for
+    the forward."""
     p = plan(rn.OP_BWD, M, N, dt)
     assert p["rows_per_step"] == want, p
     if want == 2:
         assert (p["team"], p["chunks"], p["depth"], p["w_regs"]) == (0, 1, 1, 1)
     f = plan(rn.OP_FUSED_ADD_BWD, M, N, dt)
     assert f["rows_per_step"] == (2 if want == 2 and f["threads"] <= 256 else 1), f
-    for op in (rn.OP_LN_BWD, rn.OP_LN_FUSED_ADD_BWD, rn.OP_FWD, rn.OP_FUSED_ADD_FWD):
+    ln = plan(rn.OP_LN_BWD, M, N, dt)
+    assert ln["rows_per_step"] == (2 if want == 2 and ln["threads"] <= 256 else 1), ln
+    for op in (rn.OP_LN_FUSED_ADD_BWD, rn.OP_FWD, rn.OP_FUSED_ADD_FWD):
         assert plan(op, M, N, dt)["rows_per_step"] == 1
 
 
@@ -459,7 +462,8 @@ def test_two_rows_per_reduction_override_checks():
         (rn.OP_BWD, dict(fields, rows_per_step=2, vec=1)),
         (rn.OP_BWD, dict(path=rn.PATH_LOOP, vec=8, team=0, threads=512, rows_per_step=2)),
         (rn.OP_FUSED_ADD_BWD, dict(fields, rows_per_step=2)),  # fused: 256 threads at most
-        (rn.OP_LN_BWD, dict(fields, rows_per_step=2)),
+        (rn.OP_LN_BWD, dict(fields, threads=1024, rows_per_step=2)),  # LayerNorm: 512 threads at most
+        (rn.OP_LN_FUSED_ADD_BWD, dict(fields, threads=256, rows_per_step=2)),  # not compiled
         (rn.OP_FWD, dict(path=rn.PATH_ROWS, vec=8, team=0, threads=256, rows_per_step=2)),
     ]
     for op, f in bad:

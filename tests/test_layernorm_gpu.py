@@ -102,6 +102,12 @@ LN_FORCED = [
     (True, 20, 4000, "f32", dict(path=R, vec=4, team=0, threads=256, depth=0, w_regs=0, grid=3)),
     (True, 100, 2048, "bf16", dict(path=R, vec=1, team=0, threads=512, grid=5)),
     (True, 300, 128, "bf16", dict(path=R, vec=1, team=64, threads=256)),
+    # two rows per reduction (plain LayerNorm): odd and even rows per program, one row per program, ragged
+    (False, 300, 2048, "bf16", dict(path=R, vec=8, team=0, threads=256, depth=1, w_regs=1, rows_per_step=2, grid=19)),
+    (False, 257, 4096, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=1, w_regs=1, rows_per_step=2, grid=128)),
+    (False, 64, 2048, "bf16", dict(path=R, vec=8, team=0, threads=256, depth=1, w_regs=1, rows_per_step=2, grid=64)),
+    (False, 45, 4000, "bf16", dict(path=R, vec=8, team=0, threads=512, depth=1, w_regs=1, rows_per_step=2, grid=4)),
+    (False, 300, 1024, "f32", dict(path=R, vec=4, team=0, threads=256, depth=1, w_regs=1, rows_per_step=2, grid=17)),
     (True, 60, 4096, "bf16", dict(path=rn.PATH_LOOP, vec=8, team=0, threads=512, grid=9)),
     (True, 60, 4096, "f32", dict(path=rn.PATH_LOOP, vec=1, team=0, threads=256, grid=9)),
 ]

@@ -149,7 +149,7 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
             b.mu = a.mean[row];
     };
 
-    __shared__ float red[2][32]; // block_sum uses 16 floats a slot, block_sum2 32
+    __shared__ float red[2][LN ? 64 : 32]; // floats a slot: block_sum 16, block_sum2 32, block_sum4 64
     int parity = 0;
     // values unpacked in the first pass are formed again in the second where
     // registers are scarce (see below)
@@ -300,7 +300,51 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
         // program's rows r0, r0 + s, r0 + 2s, ... pair up in order; a
         // missing second row (odd count) is loaded clamped to the last row
         // and neither written nor accumulated.
+        // LayerNorm: the two rows' mean(g) and mean(g * xhat) go through one
+        // four-sum reduction.
+        auto proc2_ln = [&](Row &b0, Row &b1, int64_t row, bool second) __attribute__((always_inline)) {
+            float sg0 = 0.0f, sgx0 = 0.0f, sg1 = 0.0f, sgx1 = 0.0f;
+            const int c = lane; // one chunk per lane
+            if (EXACT || c < nchunks) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float g0 = elem(b0.dy[0], e) * weight(b0, 0, e);
+                    const float g1 = elem(b1.dy[0], e) * weight(b1, 0, e);
+                    sg0 += g0;
+                    sg1 += g1;
+                    sgx0 = fmaf(g0, (elem(b0.v[0], e) - b0.mu) * b0.rs, sgx0);
+                    sgx1 = fmaf(g1, (elem(b1.v[0], e) - b1.mu) * b1.rs, sgx1);
+                }
+            }
+            block_sum4(sg0, sgx0, sg1, sgx1, red[parity], a.threads);
+            parity ^= 1;
+            auto pass2 = [&](Row &b, float sg, float sgx, int64_t r) __attribute__((always_inline)) {
+                const float rs = b.rs, mu = b.mu;
+                const float c1 = sg * inv_n, c2 = sgx * inv_n;
+                if (EXACT || c < nchunks) {
+                    float o[V];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        const float d = elem(b.dy[0], e);
+                        const float xh = (elem(b.v[0], e) - mu) * rs;
+                        o[e] = rs * fmaf(-xh, c2, d * weight(b, 0, e) - c1);
+                        acc[0][e] = fmaf(d, xh, acc[0][e]);
+                        accb[0][e] += d;
+                    }
+                    Chunk<T, V> out;
+                    out.set(o);
+                    out.store(dxp + r * N + (int64_t)c * V);
+                }
+            };
+            pass2(b0, sg0, sgx0, row);
+            if (second)
+                pass2(b1, sg1, sgx1, row + a.grid);
+        };
         auto proc2 = [&](Row &b0, Row &b1, int64_t row, bool second) __attribute__((always_inline)) {
+            if constexpr (LN) {
+                proc2_ln(b0, b1, row, second);
+                return;
+            }
             float dot0 = 0.0f, dot1 = 0.0f;
             const int c = lane; // one chunk per lane
             if (EXACT || c < nchunks) {
@@ -756,12 +800,12 @@ static hipError_t dispatch_bwd(const rmsnorm_plan &p, BwdArgs a, hipStream_t s)
         return hipGetLastError();
     }
     const bool vec = (p.vec == VV);
-    if constexpr (!LN) {
+    if constexpr (bwd_pairs_compiled(LN, FUSED, 0, 1, 1, true, VV)) {
         if (p.rows_per_step == 2) { // complete_plan admits it only for bwd_pairs_compiled layouts
             if (!(vec && p.team == 0 && p.chunks == 1 && p.depth == 1 && p.w_regs == 1 &&
-                  p.threads <= bwd_pairs_bound(FUSED)))
+                  p.threads <= bwd_pairs_bound(FUSED, LN)))
                 return hipErrorInvalidConfiguration;
-            return launch_bwd_rows<T, VV, 0, 1, kDepthPairs, true, bwd_pairs_bound(FUSED), FUSED, false>(p, a, s);
+            return launch_bwd_rows<T, VV, 0, 1, kDepthPairs, true, bwd_pairs_bound(FUSED, LN), FUSED, LN>(p, a, s);
         }
     }
 #define RMSNORM_CASE(VEC, TEAM, K, D, WR, BOUND, FBOUND)                                      \

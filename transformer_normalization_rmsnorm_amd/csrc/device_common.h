@@ -413,6 +413,38 @@ __device__ __forceinline__ void block_sum2(float &a, float &b, float *slot, int 
     b = sb;
 }
 
+// Four sums over the whole workgroup with one barrier (as block_sum2; `slot`
+// holds 64 floats): LayerNorm's two row sums for two rows.
+__device__ __forceinline__ void block_sum4(float &a, float &b, float &c, float &d, float *slot, int threads)
+{
+    a = team_sum<64>(a);
+    b = team_sum<64>(b);
+    c = team_sum<64>(c);
+    d = team_sum<64>(d);
+    const int nw = threads >> 6;
+    if (nw == 1)
+        return;
+    if ((threadIdx.x & 63) == 0) {
+        const int w = threadIdx.x >> 6;
+        slot[w] = a;
+        slot[16 + w] = b;
+        slot[32 + w] = c;
+        slot[48 + w] = d;
+    }
+    lds_barrier();
+    float sa = slot[0], sb = slot[16], sc = slot[32], sd = slot[48];
+    for (int i = 1; i < nw; ++i) {
+        sa += slot[i];
+        sb += slot[16 + i];
+        sc += slot[32 + i];
+        sd += slot[48 + i];
+    }
+    a = sa;
+    b = sb;
+    c = sc;
+    d = sd;
+}
+
 // Maximum over the whole workgroup, NaN-propagating (as block_sum; `slot`
 // holds 16 floats and must not be in use by a concurrent block_sum).
 __device__ __forceinline__ float block_max(float v, float *slot, int threads)

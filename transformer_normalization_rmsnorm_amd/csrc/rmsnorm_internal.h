@@ -124,8 +124,9 @@ constexpr int kFinColsPerBlock = 32;
     X(0, 0, 2, 1, 1, 512, 512) X(0, 0, 4, 1, 1, 512, 512)
 
 // Backward layouts that can reduce two rows together (rows_per_step = 2):
-// RMSNorm (plain or fused-add), workgroup teams, w in registers, one 16-byte
-// chunk per lane, one step loaded ahead.  They run an instance of their own,
+// RMSNorm (plain or fused-add) and plain LayerNorm (its two row sums for both
+// rows in one four-sum reduction, up to 512 threads), workgroup teams, w in
+// registers, one 16-byte chunk per lane, one step loaded ahead.  They run an instance of their own,
 // whose depth template argument is kDepthPairs (no plan has that depth),
 // compiled for up to bwd_pairs_bound(fused) threads.  The fused-add op also
 // holds the dh rows (146 VGPRs); it is used up to 256 threads, where it
@@ -133,10 +134,9 @@ constexpr int kFinColsPerBlock = 32;
 // at 512 (4096 x 4096: 24.2 against 24.4 us).
 constexpr bool bwd_pairs_compiled(bool ln, bool fused, int team, int chunks, int depth, bool w_regs, int vec)
 {
-    (void)fused;
-    return !ln && team == 0 && chunks == 1 && depth == 1 && w_regs && vec > 1;
+    return !(ln && fused) && team == 0 && chunks == 1 && depth == 1 && w_regs && vec > 1;
 }
-constexpr int bwd_pairs_bound(bool fused) { return fused ? 256 : 1024; }
+constexpr int bwd_pairs_bound(bool fused, bool ln = false) { return fused ? 256 : ln ? 512 : 1024; }
 constexpr int kDepthPairs = 8;
 
 // LayerNorm backward layouts with dbeta accumulated in LDS.

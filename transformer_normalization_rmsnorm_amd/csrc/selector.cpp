@@ -39,6 +39,11 @@ constexpr int kFusedHalfMinThreads = 896;
 // and not at 512 (4096 x 4096: 24.0 / 24.0 us).
 constexpr int kPairMaxThreads = 512;
 constexpr int kPairMaxThreadsFused = 256;
+// Plain LayerNorm (two sums per row, so four per step): at 256 threads 4096 x
+// 2048 bf16 18.6 -> 16.7 us, 16384 x 2048 49.1 -> 42.2 us, fp32 4096 x 1024
+// 17.3 -> 15.4 us; at 512 threads within 2% either way (4096 x 4096 24.3 /
+// 24.0 us, 16384 x 4096 68.3 / 69.9 us), so it stops at 256.
+constexpr int kPairMaxThreadsLN = 256;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -352,7 +357,7 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
         if (p->rows_per_step != 1 &&
             (p->rows_per_step != 2 ||
              !bwd_pairs_compiled(is_ln_op(p->op), is_fused(p->op), p->team, k, p->depth, p->w_regs, p->vec) ||
-             p->threads > bwd_pairs_bound(is_fused(p->op))))
+             p->threads > bwd_pairs_bound(is_fused(p->op), is_ln_op(p->op))))
             return false;
         const int64_t sets = is_ln_op(p->op) ? 2 : 1;
         if (bwd && p->team != 0 && sets * rows_per_block * N * (int64_t)sizeof(float) > 65536)
@@ -464,9 +469,10 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
         // and two accumulator sets, was 2.5% slower at two.
         const int64_t programs = (int64_t)kBwdProgramsPerCU * std::max(num_cus, 1);
         const int64_t rows = ceil_div(M, programs);
-        if (rows >= 2 && p.threads <= (is_fused(op) ? kPairMaxThreadsFused : kPairMaxThreads) &&
+        if (rows >= 2 &&
+            p.threads <= (is_fused(op) ? kPairMaxThreadsFused : is_ln_op(op) ? kPairMaxThreadsLN : kPairMaxThreads) &&
             bwd_pairs_compiled(is_ln_op(op), is_fused(op), p.team, p.chunks, p.depth, p.w_regs, p.vec) &&
-            p.threads <= bwd_pairs_bound(is_fused(op)))
+            p.threads <= bwd_pairs_bound(is_fused(op), is_ln_op(op)))
             p.rows_per_step = 2;
         else if (is_fused(op) && p.chunks == 1 && p.threads >= kFusedHalfMinThreads &&
                  rows >= kFusedHalfRowsPerProgram && (p.threads / 2) % 64 == 0 &&
