@@ -86,6 +86,107 @@ def test_graph_replay_matches_eager(M, N, fused):
             assert torch.equal(_bits(a), _bits(b)), f"replay {i}: {name} differs"
 
 
+
+# Entry points with their own kernels or extra launches: the fp8 forward with
+# its amax finalizer, LayerNorm (saved statistics, and statistics recomputed
+# into the workspace inside the call), the looped kernels (rows beyond the
+# register layouts) and the per-element path (N not a multiple of the vector).
+OTHER_GRAPH_CASES = [("fp8_amax", 2048, 4096), ("fp8_fused_amax", 1024, 7168), ("layernorm_saved_stats", 1024, 4096),
+                     ("layernorm_recomputed_stats", 1024, 4096), ("looped", 64, 40000), ("per_element", 300, 1001)]
+
+
+@pytest.mark.parametrize("case,M,N", OTHER_GRAPH_CASES, ids=[c[0] for c in OTHER_GRAPH_CASES])
+def test_graph_replay_other_entry_points(case, M, N):
+    """As test_graph_replay_matches_eager, for the other entry points: every
+    replay writes what the eager calls wrote, bit for bit (amax is reset to 0
+    before the eager run and before each replay, as it accumulates)."""
+    dt = "bf16"
+    ln = case.startswith("layernorm")
+    inp = make_inputs(M, N, dt, fused=True, layernorm=ln)
+    x, r, g = to_dev(inp["x"], dt), to_dev(inp["residual"], dt), to_dev(inp["gamma"], dt)
+    dy = to_dev(inp["dy"], dt)
+    if case == "looped":
+        assert rn.rmsnorm_query_plan(rn.OP_BWD, M, N, rn.BF16)["path"] == rn.PATH_LOOP
+        assert rn.rmsnorm_query_plan(rn.OP_FWD, M, N, rn.BF16)["path"] == rn.PATH_LOOP
+    outs = {}
+    if case.startswith("fp8"):
+        fused = case == "fp8_fused_amax"
+        scale = torch.full((1,), 16.0, dtype=torch.float32, device="cuda")
+        outs = {"y8": torch.empty(M, N, dtype=torch.uint8, device="cuda"),
+                "rstd": torch.empty(M, device="cuda"), "amax": torch.zeros(1, device="cuda")}
+        if fused:
+            outs["h"] = torch.empty_like(x)
+        ws = torch.empty(max(rn.rmsnorm_fwd_fp8_workspace_bytes(M, N, rn.BF16), 16), dtype=torch.uint8, device="cuda")
+
+        def step():
+            if fused:
+                rn.rmsnorm_fused_add_fwd_fp8(x, r, g, scale, EPS, 0.0, amax=outs["amax"], y8=outs["y8"],
+                                             h_out=outs["h"], rstd=outs["rstd"], workspace=ws)
+            else:
+                rn.rmsnorm_fwd_fp8(x, g, scale, EPS, 0.0, amax=outs["amax"], y8=outs["y8"], rstd=outs["rstd"],
+                                   workspace=ws)
+    elif ln:
+        beta = to_dev(inp["beta"], dt)
+        saved = case == "layernorm_saved_stats"
+        outs = {"y": torch.empty_like(x), "mean": torch.empty(M, device="cuda"), "rstd": torch.empty(M, device="cuda"),
+                "dx": torch.empty_like(x), "dg": torch.empty_like(g), "db": torch.empty_like(g)}
+        ws, _ = rn.alloc_workspace(M, N, rn.BF16, x.device, op=rn.OP_LN_BWD)
+
+        def step():
+            rn.layernorm_fwd(x, g, beta, EPS, 0.0, y=outs["y"], mean=outs["mean"], rstd=outs["rstd"])
+            rn.layernorm_bwd(dy, x, g, outs["mean"] if saved else None, outs["rstd"] if saved else None, EPS, 0.0,
+                             dx=outs["dx"], dgamma=outs["dg"], dbeta=outs["db"], workspace=ws)
+    else:
+        outs = {"y": torch.empty_like(x), "rstd": torch.empty(M, device="cuda"), "dx": torch.empty_like(x),
+                "dg": torch.empty_like(g)}
+        ws, _ = rn.alloc_workspace(M, N, rn.BF16, x.device)
+
+        def step():
+            rn.rmsnorm_fwd(x, g, EPS, 0.0, y=outs["y"], rstd=outs["rstd"])
+            rn.rmsnorm_bwd(dy, x, g, outs["rstd"], EPS, 0.0, dx=outs["dx"], dgamma=outs["dg"], workspace=ws)
+
+    def reset_amax():
+        if "amax" in outs:
+            outs["amax"].zero_()
+
+    reset_amax()
+    step()
+    torch.cuda.synchronize()
+    ref = {k: t.clone() for k, t in outs.items()}
+    if "amax" in ref:
+        assert ref["amax"].item() > 0.0
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    # the graph holds raw pointers: every tensor it reads (x, r, g, dy, beta,
+    # scale, the workspace) stays bound to its own name until the replays end
+    for i in range(4):
+        for k, t in outs.items():
+            if t.dtype == torch.uint8:
+                t.fill_(0x7F)
+            else:
+                t.fill_(float("nan"))
+        reset_amax()
+        _ = (x.float() * 2).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        bad = []
+        for k, t in outs.items():
+            got, want = (t, ref[k]) if t.dtype == torch.uint8 else (_bits(t), _bits(ref[k]))
+            d = got != want
+            if bool(d.any()):
+                where = d.nonzero()
+                bad.append(f"{k}: {int(d.sum())} of {d.numel()} differ, first at {where[:4].tolist()}")
+        assert not bad, f"replay {i}: " + "; ".join(bad)
+
+
 def test_runs_on_the_callers_stream():
     """Two non-default streams, each with its own buffers and workspace."""
     dt = "bf16"
