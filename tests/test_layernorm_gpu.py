@@ -113,13 +113,15 @@ LN_FORCED = [
 ]
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["plain", "fused"])
-@pytest.mark.parametrize("fused_ok,M,N,dt,fields", LN_FORCED + in_f16(LN_FORCED),
-                         ids=[f"{dt}_{M}x{N}_" + "_".join(f"{a}{b}" for a, b in f.items())
-                              for _, M, N, dt, f in LN_FORCED + in_f16(LN_FORCED)])
-def test_layernorm_backward_layouts(fused_ok, M, N, dt, fields, fused):
-    if fused and not fused_ok:
-        pytest.skip("layout not compiled for the fused op")
+# every layout plain, and fused-add where it is compiled for the fused op
+LN_CASES = [(M, N, dt, f, fused) for ok, M, N, dt, f in LN_FORCED + in_f16(LN_FORCED)
+            for fused in ((False, True) if ok else (False,))]
+
+
+@pytest.mark.parametrize("M,N,dt,fields,fused", LN_CASES,
+                         ids=[f"{dt}_{M}x{N}_" + "_".join(f"{a}{b}" for a, b in f.items()) + "-" +
+                              ("fused" if fu else "plain") for M, N, dt, f, fu in LN_CASES])
+def test_layernorm_backward_layouts(M, N, dt, fields, fused):
     op = rn.OP_LN_FUSED_ADD_BWD if fused else rn.OP_LN_BWD
     inp = make_inputs(M, N, dt, fused=fused, gemma=(dt == "f32"), layernorm=True)
     offset = 1.0 if dt == "f32" else 0.0

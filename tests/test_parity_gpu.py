@@ -185,13 +185,15 @@ WIDE_FORCED = [
 ]
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["plain", "fused"])
-@pytest.mark.parametrize("fused_ok,M,N,dt,fields", WIDE_FORCED + in_f16(WIDE_FORCED),
-                         ids=[f"{dt}_{M}x{N}_t{f['threads']}_d{f['depth']}_w{f['w_regs']}"
-                              for _, M, N, dt, f in WIDE_FORCED + in_f16(WIDE_FORCED)])
-def test_wide_backward_layouts(fused_ok, M, N, dt, fields, fused):
-    if fused and not fused_ok:
-        pytest.skip("layout not compiled for the fused op at this workgroup size")
+# every layout plain, and fused-add where it is compiled for the fused op at that workgroup size
+WIDE_CASES = [(M, N, dt, f, fused) for ok, M, N, dt, f in WIDE_FORCED + in_f16(WIDE_FORCED)
+              for fused in ((False, True) if ok else (False,))]
+
+
+@pytest.mark.parametrize("M,N,dt,fields,fused", WIDE_CASES,
+                         ids=[f"{dt}_{M}x{N}_t{f['threads']}_d{f['depth']}_w{f['w_regs']}-" + ("fused" if fu else "plain")
+                              for M, N, dt, f, fu in WIDE_CASES])
+def test_wide_backward_layouts(M, N, dt, fields, fused):
     op = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
     with rn.plan_override(op, **fields):
         p = rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)
