@@ -405,17 +405,21 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
     float *__restrict__ part = a.partials + (int64_t)blockIdx.x * a.ld;
     float *__restrict__ partb = a.partials + (a.grid + (int64_t)blockIdx.x) * a.ld; // LayerNorm dbeta
     if constexpr (TEAM == 0) {
-        // Rows of one or two chunks per lane write their partial rows with
-        // the nontemporal hint, as the finalizer reads them (measured on
-        // MI355X with one workspace reused call after call, backward of
-        // 1024 x 8192 bf16: RMSNorm 17.6 -> 16.8 us, LayerNorm 23.4 -> 21.0
-        // us; within noise with a fresh workspace per call).  Wider rows keep
-        // cached stores: there the hint cost 2048 x 32768 bf16 3.7 us.
+        // LayerNorm rows of one or two chunks per lane, and RMSNorm rows of
+        // two, write their partial rows with the nontemporal hint, as the
+        // finalizer reads them (measured on MI355X with one workspace reused
+        // call after call, LayerNorm backward of 1024 x 8192 bf16: 23.4 ->
+        // 21.0 us; within noise with a fresh workspace per call).  RMSNorm
+        // rows of one chunk write them cached: with the hint (set in buffer
+        // stores) the backward of 4096 x 4096 and 1024 x 8192 bf16 took 1.4%
+        // and 4.9% longer.  Wider rows keep cached stores: there the hint
+        // cost 2048 x 32768 bf16 3.7 us.
+        constexpr bool kNtPartials = K == 2 || (K == 1 && LN);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int c = k * tl + lane;
             if (EXACT || c < nchunks) {
-                if constexpr (K <= 2)
+                if constexpr (kNtPartials)
                     store_f32_nt<V>(part + (int64_t)c * V, acc[k]);
                 else
                     store_f32<V>(part + (int64_t)c * V, acc[k]);
