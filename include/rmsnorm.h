@@ -153,6 +153,11 @@ int rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *bytes);
 /* Backward (FlyDSL PR #855 "Hybrid atomic / two-stage backward"): a bounded
  * persistent grid writes dx and float32 dgamma partials into `workspace`, then
  * a finalizer sums the partials in a fixed order and writes dgamma in T.
+ * With few rows (at most one or two per program; the plan's path is then
+ * RMSNORM_PATH_ROWS_COLS) one launch does both: its first workgroups write dx,
+ * the others sum dgamma_j = sum_i dy_ij * x_ij * rstd_i directly by columns,
+ * in a fixed order, and no partial rows are written.  Either way dgamma is
+ * bit-identical run to run for the same shape, dtype and device.
  *   dy, x  [M, N] T;  gamma [N] T (NULL: non-affine, then dgamma NULL);
  *   rstd   [M] f32 from the forward, or NULL to recompute it from x with eps;
  *   dx     [M, N] T;  dgamma [N] T (NULL exactly when gamma is NULL);
@@ -232,7 +237,13 @@ typedef enum rmsnorm_op {
 
 typedef enum rmsnorm_path {
     RMSNORM_PATH_ROWS = 0, /* each row held in registers by a team of lanes */
-    RMSNORM_PATH_LOOP = 1  /* rows streamed in passes (any N) */
+    RMSNORM_PATH_LOOP = 1, /* rows streamed in passes (any N) */
+    RMSNORM_PATH_ROWS_COLS = 2 /* RMSNorm backward with few rows: dx as on the ROWS path
+                                  (workgroup teams, w in registers, one chunk per lane),
+                                  and dgamma summed directly by fin_grid column workgroups
+                                  of the same launch, each owning col_chunks consecutive
+                                  chunks of the row over all rows: no partial rows and no
+                                  second kernel */
 } rmsnorm_path;
 
 typedef struct rmsnorm_plan {
@@ -246,17 +257,20 @@ typedef struct rmsnorm_plan {
     int32_t w_regs;      /* backward ROWS path: 1 = w = gamma + offset is loaded once per
                             program and held in registers; 0 = gamma is re-read with every
                             row (wide rows).  0 for the forward and the LOOP path. */
-    int64_t grid;        /* workgroups of the main kernel (backward: partial programs) */
-    int64_t programs;    /* backward: dgamma partial rows (= grid); fp8 forward: amax
-                            partials (= grid); plain forward: 0 */
+    int64_t grid;        /* workgroups of the main kernel (backward: row programs) */
+    int64_t programs;    /* backward: dgamma partial rows (= grid; 0 on ROWS_COLS); fp8
+                            forward: amax partials (= grid); plain forward: 0 */
     int64_t workspace_bytes; /* backward and fp8-forward workspace; plain forward 0 */
     int32_t fin_threads; /* finalizer workgroup size (dgamma, or amax for fp8) */
-    int64_t fin_grid;    /* finalizer workgroups */
+    int64_t fin_grid;    /* finalizer workgroups; ROWS_COLS: the column workgroups that
+                            follow the grid row programs in the same launch */
     int32_t rows_per_step; /* backward ROWS path: rows a workgroup reduces together.  2: two
                               rows share one workgroup reduction and the next two are loaded
                               ahead (RMSNorm, plain or fused-add; workgroup teams, w in
                               registers, one chunk per lane, depth 1; at most 1024 threads,
                               256 for fused-add); otherwise 1. */
+    int32_t col_chunks;  /* ROWS_COLS: 16-byte chunks of the row each column workgroup
+                            sums over all rows (1, 2, 4 or 8); otherwise 0 */
 } rmsnorm_plan;
 
 /* Pure selector query: the plan for `op` at (M, N, dtype).  vec_ok != 0 says
@@ -270,8 +284,9 @@ int rmsnorm_query_plan(int op, int64_t M, int64_t N, int dtype, int vec_ok, int 
  * switches, "Behavior when the fast path does not apply"): later calls of `op`
  * use path, vec, team and threads from *plan, its depth and w_regs when they
  * are >= 0 and its grid when grid > 0 (else the selector's depth, w_regs and
- * grid for that layout), and its rows_per_step when > 0 (else 1); chunks and
- * the workspace follow.
+ * grid for that layout), its rows_per_step when > 0 (else 1) and, on the
+ * ROWS_COLS path, its col_chunks when > 0 (else the selector's rule); chunks
+ * and the workspace follow.
  * vec = 1 forces scalar accesses on aligned data.  NULL clears.  Process-wide
  * and not thread-safe; a call that the override does not fit returns
  * RMSNORM_EINVAL. */
@@ -283,8 +298,9 @@ const char *rmsnorm_last_error(void);
  * checks it before use.  2: rmsnorm_plan gained w_regs.  3: fp8-output
  * forwards (ops 4 and 5).  4: LayerNorm (include/layernorm.h, ops 6-9).
  * 5: binary16 storage (RMSNORM_F16).  6: rmsnorm_plan gained rows_per_step.
- * 7: rmsnorm_bwd_noalloc. */
-#define RMSNORM_ABI_VERSION 7
+ * 7: rmsnorm_bwd_noalloc.  8: RMSNORM_PATH_ROWS_COLS; rmsnorm_plan gained
+ * col_chunks. */
+#define RMSNORM_ABI_VERSION 8
 
 /* Longest row (elements) any entry point accepts. */
 #define RMSNORM_MAX_N (1 << 24)

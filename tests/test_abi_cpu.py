@@ -191,8 +191,11 @@ def test_plans_for_workloads(M, N, dt, fused):
     f = plan(fop, M, N, dt)
     b = plan(bop, M, N, dt)
     vec = 8 if dt == rn.BF16 else 4
+    # the 512-row backward takes the one-launch path (two rows per program, 2 MiB rows)
+    cols = M <= 2 * CUS
+    assert f["path"] == rn.PATH_ROWS and b["path"] == (rn.PATH_ROWS_COLS if cols else rn.PATH_ROWS)
     for p in (f, b):
-        assert p["path"] == rn.PATH_ROWS and p["vec"] == vec and covers(p, N)
+        assert p["vec"] == vec and covers(p, N)
         assert p["threads"] % 64 == 0 and 64 <= p["threads"] <= 1024
     rows_per_block = 1 if b["team"] == 0 else b["threads"] // b["team"]
     per_cu = 1 if b["team"] == 0 else 2
@@ -202,7 +205,7 @@ def test_plans_for_workloads(M, N, dt, fused):
     assert lanes * f["chunks"] * f["vec"] == N
     # one row per team, nothing prefetched
     assert f["depth"] == 0 and f["grid"] == -(-M // (1 if f["team"] == 0 else f["threads"] // f["team"]))
-    assert b["programs"] == b["grid"]
+    assert b["programs"] == (0 if cols else b["grid"])
     # w = gamma + offset stays in registers when one chunk per lane covers the
     # row, except the fused-add op at 896 or more lanes with 8+ rows per program
     # (half the lanes, two chunks, gamma re-read); the forward has no such field
@@ -212,8 +215,72 @@ def test_plans_for_workloads(M, N, dt, fused):
         assert (b["threads"], b["chunks"], b["depth"]) == (N // vec // 2, 2, 1)
     ld = -(-N // 64) * 64
     assert b["workspace_bytes"] == -(-b["programs"] * ld * 4 // 256) * 256 + -(-M * 4 // 256) * 256
-    assert b["fin_grid"] == ld // 32
+    if cols:  # column workgroups in the same launch, in whole rounds of 8
+        assert b["col_chunks"] in (1, 2, 4, 8) and b["fin_threads"] == b["threads"]
+        assert b["fin_grid"] == -(-(-(-(N // vec) // b["col_chunks"])) // 8) * 8
+    else:
+        assert b["fin_grid"] == ld // 32 and b["col_chunks"] == 0
     assert f["workspace_bytes"] == 0
+
+
+# One-launch backward (PATH_ROWS_COLS): rows of one chunk per lane with w in
+# registers, at most one row per program, or two with at most 3 MiB of rows;
+# the slab rule: max(threads / M, chunks / CUs) as a power of two, at most 8.
+COLS_CASES = [  # (M, N, dtype, fused, expected path, expected col_chunks)
+    (1, 2048, rn.BF16, False, rn.PATH_ROWS_COLS, 8), (64, 2048, rn.BF16, False, rn.PATH_ROWS_COLS, 4),
+    (128, 8192, rn.BF16, False, rn.PATH_ROWS_COLS, 8), (256, 4096, rn.BF16, False, rn.PATH_ROWS_COLS, 2),
+    (256, 8192, rn.BF16, False, rn.PATH_ROWS_COLS, 4), (512, 2048, rn.BF16, False, rn.PATH_ROWS_COLS, 1),
+    (384, 4096, rn.BF16, False, rn.PATH_ROWS_COLS, 2), (256, 2048, rn.BF16, True, rn.PATH_ROWS_COLS, 1),
+    (128, 2048, rn.F32, False, rn.PATH_ROWS_COLS, 4), (256, 4096, rn.F16, False, rn.PATH_ROWS_COLS, 2),
+    (512, 4096, rn.BF16, False, rn.PATH_ROWS, 0), (512, 2048, rn.F32, False, rn.PATH_ROWS, 0),
+    (512, 8192, rn.BF16, False, rn.PATH_ROWS, 0), (768, 2048, rn.BF16, False, rn.PATH_ROWS, 0),
+    (4096, 4096, rn.BF16, False, rn.PATH_ROWS, 0), (0, 2048, rn.BF16, False, rn.PATH_ROWS, 0),
+    (256, 1024, rn.BF16, False, rn.PATH_ROWS, 0),    # one wavefront per row: not a workgroup team
+    (256, 16384, rn.BF16, False, rn.PATH_ROWS, 0),   # gamma re-read per row
+    (200, 2000, rn.BF16, False, rn.PATH_ROWS_COLS, 2),  # ragged row (masked lanes)
+]
+
+
+@pytest.mark.parametrize("M,N,dt,fused,path,cs", COLS_CASES)
+def test_one_launch_backward_rule(M, N, dt, fused, path, cs):
+    b = plan(rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD, M, N, dt)
+    assert (b["path"], b["col_chunks"]) == (path, cs), b
+    if path == rn.PATH_ROWS_COLS:
+        assert b["programs"] == 0 and b["team"] == 0 and b["chunks"] == 1 and b["w_regs"] == 1
+        assert b["workspace_bytes"] == -(-M * 4 // 256) * 256  # only a recomputed rstd
+    # never on unaligned data, never for LayerNorm
+    assert plan(rn.OP_BWD, M, N, dt, vec_ok=False)["path"] != rn.PATH_ROWS_COLS
+    assert plan(rn.OP_LN_BWD, M, N, dt)["path"] != rn.PATH_ROWS_COLS
+
+
+def test_one_launch_backward_workspace_covers_the_two_stage_layout():
+    """rmsnorm_bwd_workspace_bytes stays the two-stage size, which the stage
+    entry point (rmsnorm_bwd_partials) needs for the same shapes."""
+    for M, N in ((512, 2048), (64, 4096), (200, 2000)):
+        assert plan(rn.OP_BWD, M, N)["path"] == rn.PATH_ROWS_COLS
+        with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=plan(rn.OP_BWD, M, N)["threads"]):
+            two = plan(rn.OP_BWD, M, N)
+        assert two["path"] == rn.PATH_ROWS and two["programs"] > 0
+
+
+def test_one_launch_backward_override():
+    """The override can force the path and the slab width, and refuses the
+    layouts that carry no column workgroups."""
+    M, N = 300, 4096
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS_COLS, vec=8, team=0, threads=512, col_chunks=8, grid=37):
+        p = plan(rn.OP_BWD, M, N)
+    assert (p["path"], p["col_chunks"], p["grid"], p["fin_grid"]) == (rn.PATH_ROWS_COLS, 8, 37, 64)
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS_COLS, vec=8, team=0, threads=512):
+        assert plan(rn.OP_BWD, M, N)["col_chunks"] == 2  # the rule: 512 / 300 -> 2
+    for bad in (dict(col_chunks=3), dict(team=64, threads=256), dict(vec=1)):
+        fields = dict(path=rn.PATH_ROWS_COLS, vec=8, team=0, threads=512)
+        fields.update(bad)
+        with rn.plan_override(rn.OP_BWD, **fields):
+            with pytest.raises(rn.RMSNormError):
+                plan(rn.OP_BWD, M, N)
+    with rn.plan_override(rn.OP_LN_BWD, path=rn.PATH_ROWS_COLS, vec=8, team=0, threads=512):
+        with pytest.raises(rn.RMSNormError):
+            plan(rn.OP_LN_BWD, M, N)
 
 
 def test_plan_shapes_by_width():

@@ -251,6 +251,81 @@ def test_two_rows_per_reduction(M, N, dt, fields, fused):
         check_backward(inp, dt, EPS, 0.0, from_dev(dx), None, v_full=inp["x"])
 
 
+# One-launch backward (PATH_ROWS_COLS): dgamma summed by column workgroups of
+# the dx launch, no partial rows.  Forced at every slab width, with one row
+# per program and several, a grid that is not a multiple of 8, a ragged row
+# (masked lanes), two rows per reduction, plain and fused-add (dx also written
+# over dh), rstd given and recomputed, and run to run.
+COLS = [
+    (512, 2048, "bf16", dict(threads=256, col_chunks=1)),
+    (128, 8192, "bf16", dict(threads=1024, col_chunks=8)),
+    (256, 4096, "bf16", dict(threads=512, col_chunks=2)),
+    (300, 4096, "bf16", dict(threads=512, col_chunks=4, grid=37)),
+    (3, 2048, "bf16", dict(threads=256, col_chunks=8)),
+    (200, 2000, "bf16", dict(threads=256, col_chunks=2)),
+    (100, 4096, "f32", dict(threads=1024, col_chunks=4)),
+    (257, 1024, "f32", dict(threads=256, col_chunks=1, grid=100)),
+    (64, 2048, "bf16", dict(threads=256, col_chunks=4, rows_per_step=2, grid=16)),
+]
+COLS_CASES = [(M, N, dt, f, fu) for M, N, dt, f in COLS + in_f16(COLS) for fu in (False, True)]
+
+
+@pytest.mark.parametrize("M,N,dt,fields,fused", COLS_CASES,
+                         ids=[f"{dt}_{M}x{N}_t{f['threads']}_cs{f['col_chunks']}_g{f.get('grid', 0)}"
+                              + ("_pairs" if f.get("rows_per_step") == 2 else "") + ("_fused" if fu else "")
+                              for M, N, dt, f, fu in COLS_CASES])
+def test_one_launch_backward(M, N, dt, fields, fused):
+    vec = 4 if dt == "f32" else 8
+    gemma = dt == "f32"
+    offset = 1.0 if gemma else 0.0
+    op = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
+    with rn.plan_override(op, path=rn.PATH_ROWS_COLS, vec=vec, team=0, depth=1, w_regs=1, **fields):
+        p = rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)
+        assert (p["path"], p["col_chunks"], p["programs"], p["chunks"]) == (rn.PATH_ROWS_COLS, fields["col_chunks"],
+                                                                            0, 1), p
+        inp, out, dx, dg = run_case(M, N, dt, fused, gemma)
+        # bit-identical run to run
+        dx2, dg2 = gpu_backward(inp, dt, EPS, offset, out, fused)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(dx2).view(np.uint8), from_dev(dx).view(np.uint8))
+        assert np.array_equal(from_dev(dg2).view(np.uint8), from_dev(dg).view(np.uint8))
+        # rstd recomputed inside the call (a statistics forward, then the one launch)
+        dx3, dg3 = gpu_backward(inp, dt, EPS, offset, out, fused, rstd=None)
+        torch.cuda.synchronize()
+        v_ref = reference_h(inp, dt, EPS, offset) if fused else inp["x"]
+        check_backward(inp, dt, EPS, offset, from_dev(dx3), from_dev(dg3), v_full=v_ref,
+                       dh_full=inp["dh"] if fused else None)
+        if fused:  # dx written over dh gives the same bytes
+            dh = to_dev(inp["dh"], dt)
+            dx4, _ = rn.rmsnorm_fused_add_bwd(to_dev(inp["dy"], dt), dh, out["h"], out["gamma"], out["rstd"], EPS,
+                                              offset, dx=dh)
+            torch.cuda.synchronize()
+            assert dx4.data_ptr() == dh.data_ptr()
+            assert np.array_equal(from_dev(dx4).view(np.uint8), from_dev(dx).view(np.uint8))
+
+
+def test_one_launch_backward_is_the_default_for_few_rows():
+    """The selector takes the one-launch path for the 512 x 2048 workload and
+    it matches the two-stage backward's dx bit for bit and its dgamma to the
+    last rounding; the stage entry point still writes partial rows there."""
+    M, N, dt = 512, 2048, "bf16"
+    assert rn.rmsnorm_query_plan(rn.OP_BWD, M, N, rn.BF16)["path"] == rn.PATH_ROWS_COLS
+    inp = make_inputs(M, N, dt)
+    out = gpu_forward(inp, dt, EPS, 0.0, False)
+    dy = to_dev(inp["dy"], dt)
+    dx1, dg1 = rn.rmsnorm_bwd(dy, out["x"], out["gamma"], out["rstd"])
+    with rn.plan_override(rn.OP_BWD, path=rn.PATH_ROWS, vec=8, team=0, threads=256, depth=1, w_regs=1,
+                          rows_per_step=2):
+        dx2, dg2 = rn.rmsnorm_bwd(dy, out["x"], out["gamma"], out["rstd"])
+    dx3, ws, programs = rn.rmsnorm_bwd_partials(dy, out["x"], out["gamma"], out["rstd"])
+    torch.cuda.synchronize()
+    assert programs > 0 and torch.equal(dx1, dx3)
+    assert torch.equal(dx1.view(torch.int16), dx2.view(torch.int16))
+    a, b = dg1.float(), dg2.float()
+    assert ((a - b).abs() <= 2 ** -7 * b.abs()).all()  # at most one bf16 rounding apart
+    check_backward(inp, dt, EPS, 0.0, from_dev(dx1), from_dev(dg1), v_full=inp["x"])
+
+
 # Non-affine op (no gamma): rows and looped paths, plain and fused, with the
 # GPU's rstd and with rstd recomputed.
 NON_AFFINE = [(300, 4096, "bf16", False), (200, 7168, "bf16", True), (130, 6144, "f32", False),

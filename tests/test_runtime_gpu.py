@@ -90,9 +90,11 @@ def test_graph_replay_matches_eager(M, N, fused):
 # Entry points with their own kernels or extra launches: the fp8 forward with
 # its amax finalizer, LayerNorm (saved statistics, and statistics recomputed
 # into the workspace inside the call), the looped kernels (rows beyond the
-# register layouts) and the per-element path (N not a multiple of the vector).
+# register layouts), the per-element path (N not a multiple of the vector) and
+# the one-launch backward for few rows (dgamma by column workgroups).
 OTHER_GRAPH_CASES = [("fp8_amax", 2048, 4096), ("fp8_fused_amax", 1024, 7168), ("layernorm_saved_stats", 1024, 4096),
-                     ("layernorm_recomputed_stats", 1024, 4096), ("looped", 64, 40000), ("per_element", 300, 1001)]
+                     ("layernorm_recomputed_stats", 1024, 4096), ("looped", 64, 40000), ("per_element", 300, 1001),
+                     ("one_launch", 256, 4096)]
 
 
 @pytest.mark.parametrize("case,M,N", OTHER_GRAPH_CASES, ids=[c[0] for c in OTHER_GRAPH_CASES])
@@ -105,6 +107,8 @@ def test_graph_replay_other_entry_points(case, M, N):
     inp = make_inputs(M, N, dt, fused=True, layernorm=ln)
     x, r, g = to_dev(inp["x"], dt), to_dev(inp["residual"], dt), to_dev(inp["gamma"], dt)
     dy = to_dev(inp["dy"], dt)
+    if case == "one_launch":
+        assert rn.rmsnorm_query_plan(rn.OP_BWD, M, N, rn.BF16)["path"] == rn.PATH_ROWS_COLS
     if case == "looped":
         assert rn.rmsnorm_query_plan(rn.OP_BWD, M, N, rn.BF16)["path"] == rn.PATH_LOOP
         assert rn.rmsnorm_query_plan(rn.OP_FWD, M, N, rn.BF16)["path"] == rn.PATH_LOOP

@@ -37,7 +37,7 @@ LIBRARY_PATH = os.path.join(PKG_DIR, "librmsnorm_amd.so")
 F32, BF16, F16 = 0, 1, 2
 OP_FWD, OP_FUSED_ADD_FWD, OP_BWD, OP_FUSED_ADD_BWD, OP_FWD_FP8, OP_FUSED_ADD_FWD_FP8 = 0, 1, 2, 3, 4, 5
 OP_LN_FWD, OP_LN_FUSED_ADD_FWD, OP_LN_BWD, OP_LN_FUSED_ADD_BWD = 6, 7, 8, 9
-PATH_ROWS, PATH_LOOP = 0, 1
+PATH_ROWS, PATH_LOOP, PATH_ROWS_COLS = 0, 1, 2
 MAX_N = 1 << 24  # longest row any entry point accepts (RMSNORM_MAX_N)
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
 
@@ -59,7 +59,7 @@ class RMSNormError(RuntimeError):
 
 
 # RMSNORM_ABI_VERSION of include/rmsnorm.h that this binding marshals.
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class Plan(ctypes.Structure):
@@ -68,7 +68,7 @@ class Plan(ctypes.Structure):
         ("threads", ctypes.c_int32), ("chunks", ctypes.c_int32), ("depth", ctypes.c_int32),
         ("w_regs", ctypes.c_int32), ("grid", ctypes.c_int64),
         ("programs", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64), ("fin_threads", ctypes.c_int32),
-        ("fin_grid", ctypes.c_int64), ("rows_per_step", ctypes.c_int32),
+        ("fin_grid", ctypes.c_int64), ("rows_per_step", ctypes.c_int32), ("col_chunks", ctypes.c_int32),
     ]
 
     def as_dict(self):

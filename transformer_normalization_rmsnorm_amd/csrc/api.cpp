@@ -129,7 +129,8 @@ void log_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, bool overrid
                  "rmsnorm: %s %s N=%lld (first call M=%lld): path=%s vec=%d team=%d threads=%d chunks=%d depth=%d "
                  "w_regs=%d rows_per_step=%d grid=%lld workspace=%lld%s%s\n",
                  op_name(op), dtype_name(dtype), (long long)N, (long long)M,
-                 p.path == RMSNORM_PATH_LOOP ? "loop" : "rows", p.vec, p.team, p.threads, p.chunks, p.depth, p.w_regs,
+                 p.path == RMSNORM_PATH_LOOP ? "loop" : p.path == RMSNORM_PATH_ROWS_COLS ? "rows+columns" : "rows", p.vec,
+                 p.team, p.threads, p.chunks, p.depth, p.w_regs,
                  p.rows_per_step, (long long)p.grid, (long long)p.workspace_bytes, overridden ? " [override]" : "",
                  why);
 }
@@ -152,6 +153,7 @@ int plan_for(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int cus, rmsn
         if (o.plan.w_regs >= 0)
             q.w_regs = o.plan.w_regs;
         q.rows_per_step = o.plan.rows_per_step > 0 ? o.plan.rows_per_step : 1;
+        q.col_chunks = o.plan.col_chunks;
         q.grid = o.plan.grid;
         if (q.vec != 1 && !vec_ok)
             return fail(RMSNORM_EINVAL, "override asks for 16-byte accesses on unaligned data");
@@ -258,6 +260,19 @@ int do_fwd(const void *x, const void *r, const void *gamma, void *y, void *h, fl
     return ok();
 }
 
+// The two-stage layout a ROWS_COLS plan is built on (same rows layout and
+// grid, partial rows and a finalizer).
+bool two_stage(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int cus)
+{
+    rmsnorm_plan q = *p;
+    q.path = RMSNORM_PATH_ROWS;
+    q.col_chunks = 0;
+    if (!complete_plan(&q, M, N, dtype, cus, true))
+        return false;
+    *p = q;
+    return true;
+}
+
 // Shared by the backward entry points.  Writes dx and the partials; returns
 // the number of partial rows in *programs.
 // LayerNorm backward extras: the saved means (NULL together with rstd: both
@@ -267,9 +282,14 @@ struct LnBwd {
     bool partials;
 };
 
+// cols_dgamma: dgamma of a full RMSNorm backward, which a ROWS_COLS plan
+// writes in the same launch (then *cols_done is set); NULL for the stage
+// entry point, whose caller wants the partial rows, so such a plan runs as
+// the two-stage layout it is built on.
 int do_partials(const void *dy, const void *v, const void *gamma, const float *rstd, const void *dh, void *dx,
                 void *workspace, size_t workspace_bytes, int64_t *programs, int64_t M, int64_t N, float eps,
-                float offset, int dtype, hipStream_t stream, const LnBwd *ln = nullptr)
+                float offset, int dtype, hipStream_t stream, const LnBwd *ln = nullptr, void *cols_dgamma = nullptr,
+                bool *cols_done = nullptr)
 {
     int rc = check_common(M, N, dtype, eps, offset);
     if (rc)
@@ -303,6 +323,9 @@ int do_partials(const void *dy, const void *v, const void *gamma, const float *r
     rmsnorm_plan p;
     if ((rc = plan_for(op, M, N, dtype, vec_ok, cus, &p)))
         return rc;
+    if (p.path == RMSNORM_PATH_ROWS_COLS && (cols_dgamma == nullptr || !want_partials) &&
+        !two_stage(&p, M, N, dtype, cus))
+        return fail(RMSNORM_EINVAL, "no two-stage layout for this plan");
     // Workspace: the partial rows, then the recomputed row statistics (rstd;
     // LayerNorm: means, then rstd), M floats each, when the caller has none.
     const int64_t stat_region = ((M * 4 + 255) / 256) * 256;
@@ -338,6 +361,12 @@ int do_partials(const void *dy, const void *v, const void *gamma, const float *r
     }
     BwdArgs a{dy, v, gamma, rs, dh, dx, partials, ld, M, (int32_t)N, offset};
     a.mean = mu;
+    if (p.path == RMSNORM_PATH_ROWS_COLS) { // no partial rows: the column workgroups write dgamma
+        a.partials = nullptr;
+        a.dgamma = cols_dgamma;
+        a.col_cs = p.col_chunks;
+        *cols_done = true;
+    }
     return launched(launch_bwd(dtype, fused, ln != nullptr, p, a, stream), "backward");
 }
 
@@ -397,9 +426,10 @@ int do_bwd(const void *dy, const void *dh, const void *v, const void *gamma, con
     if (dtype_known(dtype) && !aligned(dgamma, (size_t)elem_bytes(dtype)))
         return fail(RMSNORM_EINVAL, "dgamma not aligned to its element size");
     int64_t programs = 0;
+    bool cols_done = false;
     int rc = do_partials(dy, v, gamma, rstd, dh, dx, workspace, workspace_bytes, &programs, M, N, eps, offset,
-                         dtype, stream);
-    if (rc)
+                         dtype, stream, nullptr, dgamma, &cols_done);
+    if (rc || cols_done) // the one-launch backward has written dgamma
         return rc;
     return do_finalize(static_cast<const float *>(workspace), programs, N, dgamma, dtype, stream);
 }
@@ -455,7 +485,10 @@ int workspace_for(int op_a, int op_b, int64_t M, int64_t N, int dtype, size_t *b
     for (int op : {op_a, op_b})
         for (bool vec_ok : {true, false}) {
             rmsnorm_plan p;
-            if (select_plan(op, M, N, dtype, vec_ok, cus, &p) == RMSNORM_OK && p.workspace_bytes > need)
+            // sized for the two-stage layout, which the stage entry point
+            // runs, also where the full backward takes one launch
+            if (select_plan(op, M, N, dtype, vec_ok, cus, &p) == RMSNORM_OK &&
+                (p.path != RMSNORM_PATH_ROWS_COLS || two_stage(&p, M, N, dtype, cus)) && p.workspace_bytes > need)
                 need = p.workspace_bytes;
         }
     *bytes = (size_t)need;

@@ -50,9 +50,107 @@ struct BwdRow {
     float mu; // LayerNorm: the row mean
 };
 
+// One-launch backward for few rows (RMSNORM_PATH_ROWS_COLS): the workgroups
+// after the row programs sum dgamma_j = sum_i dy_ij * v_ij * rstd_i directly,
+// by columns, instead of the row programs writing partial rows for a second
+// kernel.  dgamma needs no row sum, so the two roles are independent and run
+// side by side; the column workgroups read dy and v a second time (2MN
+// elements), which at these sizes costs less than the dependent launch it
+// saves.  Column workgroup b owns col_cs consecutive 16-byte chunks of the
+// row; its thread t takes the rows t / col_cs, t / col_cs + threads / col_cs,
+// ..., four at a time with their loads in flight together.  The per-thread
+// sums are folded by lane exchange within each wave and then in wave order
+// through LDS, so the order depends only on M, the workgroup size and col_cs.
+// The loads go through the cache: a 128-byte line holds 8 / col_cs slabs,
+// and the workgroups that share it are given one XCD (the dispatcher sends
+// workgroup g to XCD g mod 8, so b, b + 8, b + 16, ... get consecutive slabs).
+template <typename T, int V>
+__device__ __forceinline__ void dgamma_columns(const BwdArgs &a)
+{
+    using C = Chunk<T, V>;
+    const int cs = a.col_cs;
+    const int nt = a.threads;
+    const int N = a.N;
+    const int nchunks = N / V;
+    const int64_t b = (int64_t)blockIdx.x - a.grid;
+    const int64_t ncol = (nchunks + cs - 1) / cs;
+    const int64_t per = (ncol + 7) / 8;
+    const int64_t slab = (b % 8) * per + b / 8;
+    if (slab >= ncol) // one of the workgroups that round the launch up to whole XCD rounds
+        return;
+    const int lc = (int)threadIdx.x % cs;
+    const int phase = (int)threadIdx.x / cs;
+    const int nphase = nt / cs;
+    const int c = (int)(slab * cs) + lc;
+    const T *__restrict__ dyp = static_cast<const T *>(a.dy);
+    const T *__restrict__ vp = static_cast<const T *>(a.v);
+    float acc[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e)
+        acc[e] = 0.0f;
+    if (c < nchunks) {
+        int64_t r = phase;
+        for (; r + 3 * (int64_t)nphase < a.M; r += 4 * (int64_t)nphase) {
+            C d[4], x[4];
+            float rs[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t rr = r + u * (int64_t)nphase;
+                d[u].load_cached(dyp + rr * N + (int64_t)c * V);
+                x[u].load_cached(vp + rr * N + (int64_t)c * V);
+                rs[u] = a.rstd[rr];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    acc[e] = fmaf(d[u].get(e), x[u].get(e) * rs[u], acc[e]);
+            }
+        }
+        for (; r < a.M; r += nphase) {
+            C d, x;
+            d.load_cached(dyp + r * N + (int64_t)c * V);
+            x.load_cached(vp + r * N + (int64_t)c * V);
+            const float rs = a.rstd[r];
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                acc[e] = fmaf(d.get(e), x.get(e) * rs, acc[e]);
+        }
+    }
+    // lanes l and l ^ cs, l ^ 2 cs, ... of a wave hold the same chunk
+    for (int off = cs; off < 64; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            acc[e] += __shfl_xor(acc[e], off);
+    }
+    __shared__ float colred[16][64]; // [wave][chunk in slab * V + element]: cs * V <= 64
+    const int w = (int)threadIdx.x >> 6, l = (int)threadIdx.x & 63;
+    if (l < cs) {
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            colred[w][l * V + e] = acc[e];
+    }
+    __syncthreads();
+    const int j = (int)threadIdx.x; // element j of the slab
+    if (j < cs * V) {
+        float s = colred[0][j];
+        for (int q = 1; q < nt / 64; ++q)
+            s += colred[q][j];
+        const int64_t col = slab * cs * V + j;
+        if (col < N)
+            static_cast<T *>(a.dgamma)[col] = to_storage<T>(s);
+    }
+}
+
 template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FUSED, bool EXACT, bool LN>
 __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
 {
+    if constexpr (bwd_cols_layout(LN, TEAM, K, WR, V)) {
+        if (blockIdx.x >= a.grid) { // a dgamma column workgroup (a.col_cs > 0)
+            dgamma_columns<T, V>(a);
+            return;
+        }
+    }
     using Row = BwdRow<T, V, K, WR, FUSED>;
     const int tl = TEAM ? TEAM : a.threads;
     const int lane = TEAM ? (int)(threadIdx.x & (TEAM - 1)) : (int)threadIdx.x;
@@ -735,7 +833,9 @@ __global__ void __launch_bounds__(kFinThreads) finalize_kernel(const float *__re
 template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FUSED, bool LN>
 static hipError_t launch_bwd_rows(const rmsnorm_plan &p, const BwdArgs &a, hipStream_t s)
 {
-    const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
+    // the one-launch backward adds its dgamma column workgroups after the row programs
+    const int64_t cols = a.col_cs > 0 ? bwd_col_workgroups(a.N / V, a.col_cs) : 0;
+    const dim3 grid((unsigned)(p.grid + cols)), block((unsigned)p.threads);
     const int lanes = TEAM ? TEAM : p.threads;
     const size_t sets = LN ? 2 : 1;
     // sub-workgroup teams: their partial rows; LayerNorm with dbeta in LDS:

@@ -50,6 +50,11 @@ struct BwdArgs {
     // LayerNorm only: the saved row means; the dbeta partials follow the
     // dgamma partials (program p's dbeta row at partials[(grid + p) * ld])
     const float *mean = nullptr;
+    // One-launch backward (RMSNORM_PATH_ROWS_COLS, col_cs > 0): the
+    // workgroups from `grid` on each own col_cs consecutive chunks of the row
+    // and write dgamma (T) directly; the row programs write no partial rows.
+    void *dgamma = nullptr;
+    int32_t col_cs = 0;
 };
 
 // Longest row accepted (2^24 elements).  Column and chunk indices, and the
@@ -138,6 +143,21 @@ constexpr bool bwd_pairs_compiled(bool ln, bool fused, int team, int chunks, int
 }
 constexpr int bwd_pairs_bound(bool fused, bool ln = false) { return fused ? 256 : ln ? 512 : 1024; }
 constexpr int kDepthPairs = 8;
+
+// One-launch backward (RMSNORM_PATH_ROWS_COLS): the row layouts that carry
+// the column workgroups (RMSNorm, workgroup teams, w in registers, one vector
+// chunk per lane: the layouts of rows of up to 1024 chunks).
+constexpr bool bwd_cols_layout(bool ln, int team, int chunks, int w_regs, int vec)
+{
+    return !ln && team == 0 && chunks == 1 && w_regs == 1 && vec > 1;
+}
+// Column workgroups of a launch: one per col_cs chunks, rounded up to whole
+// rounds over the 8 XCDs (the extra ones exit at once).
+inline int64_t bwd_col_workgroups(int64_t nchunks, int col_cs)
+{
+    const int64_t ncol = (nchunks + col_cs - 1) / col_cs;
+    return (ncol + 7) / 8 * 8;
+}
 
 // LayerNorm backward layouts with dbeta accumulated in LDS.
 constexpr bool bwd_dbeta_in_lds(bool ln, bool fused, int team, int chunks, int vec)

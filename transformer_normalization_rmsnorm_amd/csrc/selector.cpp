@@ -44,6 +44,17 @@ constexpr int kPairMaxThreadsFused = 256;
 // 17.3 -> 15.4 us; at 512 threads within 2% either way (4096 x 4096 24.3 /
 // 24.0 us, 16384 x 4096 68.3 / 69.9 us), so it stops at 256.
 constexpr int kPairMaxThreadsLN = 256;
+// One-launch backward (RMSNORM_PATH_ROWS_COLS) for few rows: taken at up to
+// one row per program, and at up to two when the rows hold at most
+// kColsMaxBytes.  Measured on MI355X against the two-stage backward (cold
+// buffers, bf16 unless noted): one row per program 18-43% faster (64 x 2048
+// 6.24 -> 4.09 us, 128 x 8192 7.91 -> 4.72, 256 x 4096 7.35 -> 5.43, fp32
+// 128 x 2048 6.11 -> 3.99, fused-add 256 x 2048 6.52 -> 4.67); two rows per
+// program 512 x 2048 -10%, 384 x 4096 -13%, but 512 x 4096 -2%, fp32
+// 512 x 2048 +4% and 512 x 8192 +4%; three (768 x 2048) no gain.  The column
+// workgroups re-read dy and x, 2MN elements, and beyond these sizes that costs
+// more than the finalizer launch it saves.
+constexpr int64_t kColsMaxBytes = int64_t(3) << 20;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -338,7 +349,12 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
         return false;
     if (p->w_regs != 0 && p->w_regs != 1)
         return false;
-    if (p->path == RMSNORM_PATH_ROWS) {
+    const bool cols = p->path == RMSNORM_PATH_ROWS_COLS;
+    if (cols && (!bwd || is_ln_op(p->op) || p->team != 0 || p->vec == 1 || p->w_regs != 1))
+        return false;
+    if (!cols)
+        p->col_chunks = 0;
+    if (p->path == RMSNORM_PATH_ROWS || cols) {
         if (p->team != 0) {
             if (p->team != 8 && p->team != 16 && p->team != 32 && p->team != 64)
                 return false;
@@ -354,6 +370,20 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
         if (bwd && !tiling_ok(p->op, dtype, p->vec != 1, p->team, k, b, lanes, nchunks))
             return false;
         p->chunks = k;
+        if (cols) {
+            if (!bwd_cols_layout(false, p->team, k, p->w_regs, p->vec))
+                return false;
+            if (p->col_chunks <= 0) {
+                // slab width: about one row per thread of a column workgroup
+                // (threads / M) and about one column workgroup per compute
+                // unit (nchunks / num_cus), the larger, as a power of two
+                const int64_t want = std::max<int64_t>(ceil_div(p->threads, std::max<int64_t>(M, 1)),
+                                                       ceil_div(nchunks, std::max(num_cus, 1)));
+                p->col_chunks = (int32_t)std::min<int64_t>(8, pow2_at_least(want));
+            }
+            if (p->col_chunks != 1 && p->col_chunks != 2 && p->col_chunks != 4 && p->col_chunks != 8)
+                return false;
+        }
         if (p->rows_per_step != 1 &&
             (p->rows_per_step != 2 ||
              !bwd_pairs_compiled(is_ln_op(p->op), is_fused(p->op), p->team, k, p->depth, p->w_regs, p->vec) ||
@@ -377,10 +407,11 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
         const int per_cu = (p->path == RMSNORM_PATH_ROWS && p->team != 0) ? kBwdTeamsPerCU : kBwdProgramsPerCU;
         const int64_t want = keep_grid && p->grid > 0 ? p->grid : (int64_t)per_cu * std::max(num_cus, 1);
         p->grid = M == 0 ? 0 : std::min(want, blocks_needed);
-        p->programs = p->grid;
+        p->programs = cols ? 0 : p->grid;
         p->workspace_bytes = bwd_workspace_bytes(p->programs, M, N, is_ln_op(p->op));
-        p->fin_threads = kFinThreads;
-        p->fin_grid = ceil_div(partial_ld(N), kFinColsPerBlock) * (is_ln_op(p->op) ? 2 : 1);
+        p->fin_threads = cols ? p->threads : kFinThreads;
+        p->fin_grid = cols ? bwd_col_workgroups(nchunks, p->col_chunks)
+                           : ceil_div(partial_ld(N), kFinColsPerBlock) * (is_ln_op(p->op) ? 2 : 1);
     } else {
         const int64_t want = keep_grid && p->grid > 0 ? p->grid : blocks_needed;
         p->grid = M == 0 ? 0 : std::min(std::min(want, blocks_needed), (kMaxWorkItems - 1) / p->threads);
@@ -507,6 +538,14 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
         if (ceil_div(M, programs) <= 2 && b0 >= p.threads &&
             tiling_ok(op, dtype, vec, 0, p.chunks, b0, p.threads, nchunks))
             p.depth = 0;
+    }
+    if (placed && bwd && !is_ln_op(op) && p.path == RMSNORM_PATH_ROWS &&
+        bwd_cols_layout(false, p.team, p.chunks, p.w_regs, p.vec) && M >= 1) {
+        const int64_t programs = (int64_t)kBwdProgramsPerCU * std::max(num_cus, 1);
+        if (M <= programs || (M <= 2 * programs && M * N * elem_bytes(dtype) <= kColsMaxBytes)) {
+            p.path = RMSNORM_PATH_ROWS_COLS;
+            p.col_chunks = 0; // the rule in complete_plan
+        }
     }
     if (!complete_plan(&p, M, N, dtype, num_cus, false))
         return RMSNORM_EUNSUPPORTED;
