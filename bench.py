@@ -124,7 +124,10 @@ class Sets:
             self.sets.append(s)
         del base
         torch.cuda.synchronize()
-        self.programs = rn.rmsnorm_query_plan(rn.OP_FUSED_ADD_BWD if w.fused else rn.OP_BWD, M, N, self.dt)["programs"]
+        bp = rn.rmsnorm_query_plan(rn.OP_FUSED_ADD_BWD if w.fused else rn.OP_BWD, M, N, self.dt)
+        # partial rows of the stage entry point (bwd_main): the two-stage layout's, whose grid the
+        # one-launch backward of few rows shares
+        self.programs = bp["grid"] if bp["path"] == rn.PATH_ROWS_COLS else bp["programs"]
 
     def stream(self):
         return ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
@@ -286,12 +289,16 @@ def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
     bytes_lb = algorithmic_bytes("ln_fused_bwd" if w.fused else "ln_bwd", w.M, w.N, w.elem_bytes)
     res["bytes"] = {"fwd": bytes_f, "bwd": bytes_b, "bwd_main": bytes_main, "fwd_fp8": bytes_f8,
                     "ln_fwd": bytes_lf, "ln_bwd": bytes_lb}
-    # workspace traffic of the backward: its P partial rows of N floats (two
-    # sets for LayerNorm: dgamma and dbeta), written once and read once
+    # traffic of the backward's dgamma reduction beyond the compulsory bytes:
+    # its P partial rows of N floats (two sets for LayerNorm: dgamma and
+    # dbeta), written once and read once; or, for the one-launch backward of
+    # few rows, the column workgroups' second read of dy and x
     ln_bop = rn.OP_LN_FUSED_ADD_BWD if w.fused else rn.OP_LN_BWD
-    P_rms = res["plans"]["bwd"]["programs"]
+    bplan = res["plans"]["bwd"]
     P_ln = rn.rmsnorm_query_plan(ln_bop, w.M, w.N, dt)["programs"]
-    res["workspace_bytes"] = {"bwd": 2 * P_rms * w.N * 4, "ln_bwd": 2 * 2 * P_ln * w.N * 4}
+    extra_rms = (2 * w.M * w.N * w.elem_bytes if bplan["path"] == rn.PATH_ROWS_COLS
+                 else 2 * bplan["programs"] * w.N * 4)
+    res["workspace_bytes"] = {"bwd": extra_rms, "ln_bwd": 2 * 2 * P_ln * w.N * 4}
     for mode in (("cold", "hot") if detailed else ("cold",)):
         S = Sets(w, lib, rn, torch, n_sets_for(w, mode == "cold"))
         K = len(S.sets)
@@ -528,7 +535,8 @@ def counters_traffic(ident: str, workload: str):
 def counters_run(rn, torch, workload: str = "bf16_4096x4096"):
     """Fixed launch sequence for rocprofv3 --pmc: a plain copy of known size,
     then forward, backward main and finalizer on one workload (the default
-    one unless --workload names another)."""
+    one unless --workload names another); where the workload's backward is
+    the one-launch kernel (few rows), five of those too."""
     from rmsnorm_inputs import ALL_WORKLOADS
 
     w = ALL_WORKLOADS[workload]
@@ -545,6 +553,9 @@ def counters_run(rn, torch, workload: str = "bf16_4096x4096"):
         S.bwd_main(i + 1, st)
     for i in range(5):
         S.finalize(i, st)
+    if bwd_plan(rn, w)["path"] == rn.PATH_ROWS_COLS:
+        for i in range(5):
+            S.bwd(i + 1, st)
     torch.cuda.synchronize()
     print("counters run done", flush=True)
 
@@ -581,8 +592,9 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str):
         for r in _rocprof_rows(d, "counter_collection.csv"):
             if r["Counter_Name"] != counter:
                 continue
-            per.setdefault(counter, {}).setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-    copies = [k for k in per["FETCH_SIZE"] if "copyBuffer" in k]
+            key = (r["Kernel_Name"], int(r["Grid_Size"]))  # one kernel may run at two launch sizes
+            per.setdefault(counter, {}).setdefault(key, []).append(float(r["Counter_Value"]))
+    copies = [k for k in per["FETCH_SIZE"] if "copyBuffer" in k[0]]
     f_sum = sum(sum(per["FETCH_SIZE"][k]) for k in copies)
     w_sum = sum(sum(per["WRITE_SIZE"].get(k, [])) for k in copies)
     factor = w_sum / f_sum
@@ -599,7 +611,8 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str):
            f"#   python3 $R/bench.py --summarize-counters $O/pmc_fetch_{workload} "
            f"$O/pmc_write_{workload} --workload {workload}",
            "# bench.py --counters-run launches five 256 MiB device copies, then five forward, five backward-main",
-           "# and five finalizer dispatches of the workload (four rotating buffer sets).",
+           "# and five finalizer dispatches of the workload (four rotating buffer sets); where the backward takes",
+           "# one launch (few rows), also five of those: dx rows plus dgamma column workgroups.",
            "#",
            f"# Calibration: the copies' WRITE_SIZE / FETCH_SIZE = {w_sum:.1f} / {f_sum:.1f} KiB -> fetch factor "
            f"{factor:.4f} (WRITE_SIZE counts written bytes exactly).",
@@ -607,12 +620,21 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str):
            "#",
            f"{'kernel':72s} {'read MB':>9s} {'write MB':>9s} {'total MB':>9s} {'algorithmic MB':>15s} {'ratio':>6s}"]
     rows = {}
-    for k, vals in per["FETCH_SIZE"].items():
+    import transformer_normalization_rmsnorm_amd as rn
+
+    bplan = bwd_plan_for(w)
+    one_launch_threads = ((bplan["grid"] + bplan["fin_grid"]) * bplan["threads"]
+                          if bplan["path"] == rn.PATH_ROWS_COLS else None)
+    for key, vals in per["FETCH_SIZE"].items():
+        k, grid_threads = key
         if "rmsnorm::" not in k:
             continue
         rd = statistics.median(vals) * 1024 * factor
-        wr = statistics.median(per["WRITE_SIZE"].get(k, [0.0])) * 1024
-        if "finalize_kernel" in k:
+        wr = statistics.median(per["WRITE_SIZE"].get(key, [0.0])) * 1024
+        if "bwd_" in k and grid_threads == one_launch_threads:
+            alg = algorithmic_bytes(bop, w.M, w.N, B)
+            kind = "backward, one launch"
+        elif "finalize_kernel" in k:
             plan = None
             try:
                 import transformer_normalization_rmsnorm_amd as rn
@@ -621,7 +643,8 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str):
                 plan = rn.rmsnorm_query_plan(op, w.M, w.N, dtype_code(rn, w.dtype), True, 256)
             except Exception:
                 plan = None
-            programs = plan["programs"] if plan else 256
+            # the stage finalizer sums the two-stage layout's partial rows
+            programs = (plan["grid"] if plan["path"] == rn.PATH_ROWS_COLS else plan["programs"]) if plan else 256
             alg = programs * w.N * 4 + w.N * B
             kind = "finalizer"
         elif "bwd_" in k:
@@ -631,11 +654,14 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str):
             alg = algorithmic_bytes(fop, w.M, w.N, B)
             kind = "forward"
         rows[kind] = (k, rd, wr, alg)
-        out.append(f"{_short(k)[:72]:72s} {rd / 1e6:9.3f} {wr / 1e6:9.3f} {(rd + wr) / 1e6:9.3f} {alg / 1e6:15.3f} "
+        label = _short(k) if kind != "backward, one launch" else "(one launch) " + _short(k)
+        out.append(f"{label[:72]:72s} {rd / 1e6:9.3f} {wr / 1e6:9.3f} {(rd + wr) / 1e6:9.3f} {alg / 1e6:15.3f} "
                    f"{(rd + wr) / alg:6.3f}")
     out.append("#")
     out.append("# Algorithmic bytes: forward 2MNB + NB + 4M (fused 4MNB + NB + 4M); backward main 3MNB + NB + 4M")
-    out.append("# (fused 4MNB + NB + 4M), its P x N x 4 partial-row writes not counted; finalizer P x N x 4 + NB.")
+    out.append("# (fused 4MNB + NB + 4M), its P x N x 4 partial-row writes not counted; finalizer P x N x 4 + NB;")
+    out.append("# the one-launch backward 3MNB + 2NB + 4M (fused 4MNB + 2NB + 4M), its column workgroups' second")
+    out.append("# read of dy and x not counted.")
     if "backward main" in rows:
         k, rd, wr, alg = rows["backward main"]
         out.append("")
