@@ -224,33 +224,41 @@ def test_plans_for_workloads(M, N, dt, fused):
 
 
 # One-launch backward (PATH_ROWS_COLS): rows of one chunk per lane with w in
-# registers, at most one row per program, or two with at most 3 MiB of rows;
-# the slab rule: max(threads / M, chunks / CUs) as a power of two, at most 8.
-COLS_CASES = [  # (M, N, dtype, fused, expected path, expected col_chunks)
-    (1, 2048, rn.BF16, False, rn.PATH_ROWS_COLS, 8), (64, 2048, rn.BF16, False, rn.PATH_ROWS_COLS, 4),
-    (128, 8192, rn.BF16, False, rn.PATH_ROWS_COLS, 8), (256, 4096, rn.BF16, False, rn.PATH_ROWS_COLS, 2),
-    (256, 8192, rn.BF16, False, rn.PATH_ROWS_COLS, 4), (512, 2048, rn.BF16, False, rn.PATH_ROWS_COLS, 1),
-    (384, 4096, rn.BF16, False, rn.PATH_ROWS_COLS, 2), (256, 2048, rn.BF16, True, rn.PATH_ROWS_COLS, 1),
-    (128, 2048, rn.F32, False, rn.PATH_ROWS_COLS, 4), (256, 4096, rn.F16, False, rn.PATH_ROWS_COLS, 2),
-    (512, 4096, rn.BF16, False, rn.PATH_ROWS, 0), (512, 2048, rn.F32, False, rn.PATH_ROWS, 0),
-    (512, 8192, rn.BF16, False, rn.PATH_ROWS, 0), (768, 2048, rn.BF16, False, rn.PATH_ROWS, 0),
-    (4096, 4096, rn.BF16, False, rn.PATH_ROWS, 0), (0, 2048, rn.BF16, False, rn.PATH_ROWS, 0),
-    (256, 1024, rn.BF16, False, rn.PATH_ROWS, 0),    # one wavefront per row: not a workgroup team
-    (256, 16384, rn.BF16, False, rn.PATH_ROWS, 0),   # gamma re-read per row
-    (200, 2000, rn.BF16, False, rn.PATH_ROWS_COLS, 2),  # ragged row (masked lanes)
+# registers; RMSNorm at most one row per program, or two with at most 3 MiB of
+# rows; LayerNorm at most three with at most 6 MiB, or two of 16-bit
+# elements at any width; the slab rule:
+# max(threads / M, chunks / CUs) as a power of two, at most 8.
+COLS, ROWS = rn.PATH_ROWS_COLS, rn.PATH_ROWS
+COLS_CASES = [  # (M, N, dtype, fused, RMSNorm path, col_chunks, LayerNorm path, col_chunks)
+    (1, 2048, rn.BF16, False, COLS, 8, COLS, 8), (64, 2048, rn.BF16, False, COLS, 4, COLS, 4),
+    (128, 8192, rn.BF16, False, COLS, 8, COLS, 8), (256, 4096, rn.BF16, False, COLS, 2, COLS, 2),
+    (256, 8192, rn.BF16, False, COLS, 4, COLS, 4), (512, 2048, rn.BF16, False, COLS, 1, COLS, 1),
+    (384, 4096, rn.BF16, False, COLS, 2, COLS, 2), (256, 2048, rn.BF16, True, COLS, 1, COLS, 1),
+    (128, 2048, rn.F32, False, COLS, 4, COLS, 4), (256, 4096, rn.F16, False, COLS, 2, COLS, 2),
+    # two rows per program beyond 3 MiB, three up to 6 MiB: LayerNorm only
+    (512, 4096, rn.BF16, False, ROWS, 0, COLS, 2), (512, 2048, rn.F32, False, ROWS, 0, COLS, 2),
+    (512, 8192, rn.BF16, False, ROWS, 0, COLS, 4), (512, 4096, rn.F32, False, ROWS, 0, ROWS, 0),
+    (384, 4096, rn.F32, False, ROWS, 0, COLS, 4), (768, 2048, rn.BF16, False, ROWS, 0, COLS, 1),
+    (768, 4096, rn.BF16, False, ROWS, 0, COLS, 2), (768, 2048, rn.BF16, True, ROWS, 0, COLS, 1),
+    (768, 8192, rn.BF16, False, ROWS, 0, ROWS, 0), (1024, 2048, rn.BF16, False, ROWS, 0, ROWS, 0),
+    (4096, 4096, rn.BF16, False, ROWS, 0, ROWS, 0), (0, 2048, rn.BF16, False, ROWS, 0, ROWS, 0),
+    (256, 1024, rn.BF16, False, ROWS, 0, ROWS, 0),    # one wavefront per row: not a workgroup team
+    (256, 16384, rn.BF16, False, ROWS, 0, ROWS, 0),   # gamma re-read per row
+    (200, 2000, rn.BF16, False, COLS, 2, COLS, 2),    # ragged row (masked lanes)
 ]
 
 
-@pytest.mark.parametrize("M,N,dt,fused,path,cs", COLS_CASES)
-def test_one_launch_backward_rule(M, N, dt, fused, path, cs):
-    b = plan(rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD, M, N, dt)
-    assert (b["path"], b["col_chunks"]) == (path, cs), b
-    if path == rn.PATH_ROWS_COLS:
-        assert b["programs"] == 0 and b["team"] == 0 and b["chunks"] == 1 and b["w_regs"] == 1
-        assert b["workspace_bytes"] == -(-M * 4 // 256) * 256  # only a recomputed rstd
-    # never on unaligned data, never for LayerNorm
-    assert plan(rn.OP_BWD, M, N, dt, vec_ok=False)["path"] != rn.PATH_ROWS_COLS
-    assert plan(rn.OP_LN_BWD, M, N, dt)["path"] != rn.PATH_ROWS_COLS
+@pytest.mark.parametrize("M,N,dt,fused,path,cs,ln_path,ln_cs", COLS_CASES)
+def test_one_launch_backward_rule(M, N, dt, fused, path, cs, ln_path, ln_cs):
+    for op, stats, want in (((rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD), 1, (path, cs)),
+                            ((rn.OP_LN_FUSED_ADD_BWD if fused else rn.OP_LN_BWD), 2, (ln_path, ln_cs))):
+        b = plan(op, M, N, dt)
+        assert (b["path"], b["col_chunks"]) == want, b
+        if want[0] == COLS:
+            assert b["programs"] == 0 and b["team"] == 0 and b["chunks"] == 1 and b["w_regs"] == 1
+            assert b["workspace_bytes"] == stats * (-(-M * 4 // 256) * 256)  # only recomputed statistics
+        # never on unaligned data
+        assert plan(op, M, N, dt, vec_ok=False)["path"] != COLS
 
 
 def test_one_launch_backward_workspace_covers_the_two_stage_layout():
@@ -278,9 +286,12 @@ def test_one_launch_backward_override():
         with rn.plan_override(rn.OP_BWD, **fields):
             with pytest.raises(rn.RMSNormError):
                 plan(rn.OP_BWD, M, N)
+    # LayerNorm too, with at least two wavefronts (one folds dgamma, one dbeta)
     with rn.plan_override(rn.OP_LN_BWD, path=rn.PATH_ROWS_COLS, vec=8, team=0, threads=512):
+        assert plan(rn.OP_LN_BWD, M, N)["path"] == rn.PATH_ROWS_COLS
+    with rn.plan_override(rn.OP_LN_BWD, path=rn.PATH_ROWS_COLS, vec=8, team=0, threads=64):
         with pytest.raises(rn.RMSNormError):
-            plan(rn.OP_LN_BWD, M, N)
+            plan(rn.OP_LN_BWD, 8, 512)
 
 
 def test_plan_shapes_by_width():

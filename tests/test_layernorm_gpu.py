@@ -132,6 +132,53 @@ def test_layernorm_backward_layouts(M, N, dt, fields, fused):
         check_ln(inp, dt, EPS, offset, fused, gpu_ln(inp, dt, EPS, offset, fused))
 
 
+# One-launch LayerNorm backward (PATH_ROWS_COLS): dgamma and dbeta summed by
+# column workgroups of the dx launch, no partial rows.  Forced at every slab
+# width, one row per program and several, a grid that is not a multiple of 8,
+# a ragged row, two rows per reduction (plain op); statistics given and
+# recomputed, without gamma, and run to run.
+LN_COLS = [
+    (512, 2048, "bf16", dict(threads=256, col_chunks=1)),
+    (128, 8192, "bf16", dict(threads=1024, col_chunks=8)),
+    (300, 4096, "bf16", dict(threads=512, col_chunks=4, grid=37)),
+    (200, 2000, "bf16", dict(threads=256, col_chunks=2)),
+    (100, 4096, "f32", dict(threads=1024, col_chunks=4)),
+    (64, 2048, "bf16", dict(threads=256, col_chunks=4, rows_per_step=2, grid=16)),
+    (768, 2048, "bf16", dict(threads=256, col_chunks=1, rows_per_step=2)),  # three rows per program
+]
+LN_COLS_CASES = [(M, N, dt, f, fu) for M, N, dt, f in LN_COLS + in_f16(LN_COLS) for fu in (False, True)
+                 if not (fu and f.get("rows_per_step") == 2)]  # fused-add LayerNorm has no two-row instance
+
+
+@pytest.mark.parametrize("M,N,dt,fields,fused", LN_COLS_CASES,
+                         ids=[f"{dt}_{M}x{N}_t{f['threads']}_cs{f['col_chunks']}_g{f.get('grid', 0)}"
+                              + ("_pairs" if f.get("rows_per_step") == 2 else "") + ("_fused" if fu else "")
+                              for M, N, dt, f, fu in LN_COLS_CASES])
+def test_layernorm_one_launch_backward(M, N, dt, fields, fused):
+    op = rn.OP_LN_FUSED_ADD_BWD if fused else rn.OP_LN_BWD
+    vec = 4 if dt == "f32" else 8
+    with rn.plan_override(op, path=rn.PATH_ROWS_COLS, vec=vec, team=0, depth=1, w_regs=1, **fields):
+        p = rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)
+        assert (p["path"], p["col_chunks"], p["programs"]) == (rn.PATH_ROWS_COLS, fields["col_chunks"], 0), p
+        inp = make_inputs(M, N, dt, fused=fused, layernorm=True)
+        got = gpu_ln(inp, dt, EPS, 0.0, fused)
+        check_ln(inp, dt, EPS, 0.0, fused, got)
+        again = gpu_ln(inp, dt, EPS, 0.0, fused)
+        for k in ("dx", "dg", "db"):
+            assert np.array_equal(got[k].view(np.uint8), again[k].view(np.uint8)), k
+        check_ln(inp, dt, EPS, 0.0, fused, gpu_ln(inp, dt, EPS, 0.0, fused, stats=None))
+        check_ln(inp, dt, EPS, 0.0, fused, gpu_ln(inp, dt, EPS, 0.0, fused, affine=False), affine=False)
+
+
+@pytest.mark.parametrize("M,N,dt,fused", [(768, 4096, "bf16", False), (768, 2048, "bf16", True),
+                                          (512, 8192, "bf16", False), (600, 1024, "f32", True)])
+def test_layernorm_one_launch_backward_is_the_default_for_few_rows(M, N, dt, fused):
+    op = rn.OP_LN_FUSED_ADD_BWD if fused else rn.OP_LN_BWD
+    assert rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)["path"] == rn.PATH_ROWS_COLS
+    inp = make_inputs(M, N, dt, fused=fused, layernorm=True)
+    check_ln(inp, dt, EPS, 0.0, fused, gpu_ln(inp, dt, EPS, 0.0, fused))
+
+
 def test_layernorm_zero_rows_writes_zero_gradients():
     x = torch.empty(0, 4096, dtype=torch.bfloat16, device="cuda")
     g = torch.ones(4096, dtype=torch.bfloat16, device="cuda")

@@ -282,14 +282,20 @@ struct LnBwd {
     bool partials;
 };
 
-// cols_dgamma: dgamma of a full RMSNorm backward, which a ROWS_COLS plan
-// writes in the same launch (then *cols_done is set); NULL for the stage
-// entry point, whose caller wants the partial rows, so such a plan runs as
-// the two-stage layout it is built on.
+// The outputs a ROWS_COLS plan writes in the same launch as dx: dgamma (and
+// for LayerNorm dbeta; either may be null); done is set when it did.
+struct ColsOut {
+    void *dgamma;
+    void *dbeta;
+    bool done;
+};
+
+// cols: the outputs of a full backward, which a ROWS_COLS plan writes in the
+// same launch; NULL for the stage entry point, whose caller wants the partial
+// rows, so such a plan runs as the two-stage layout it is built on.
 int do_partials(const void *dy, const void *v, const void *gamma, const float *rstd, const void *dh, void *dx,
                 void *workspace, size_t workspace_bytes, int64_t *programs, int64_t M, int64_t N, float eps,
-                float offset, int dtype, hipStream_t stream, const LnBwd *ln = nullptr, void *cols_dgamma = nullptr,
-                bool *cols_done = nullptr)
+                float offset, int dtype, hipStream_t stream, const LnBwd *ln = nullptr, ColsOut *cols = nullptr)
 {
     int rc = check_common(M, N, dtype, eps, offset);
     if (rc)
@@ -323,8 +329,7 @@ int do_partials(const void *dy, const void *v, const void *gamma, const float *r
     rmsnorm_plan p;
     if ((rc = plan_for(op, M, N, dtype, vec_ok, cus, &p)))
         return rc;
-    if (p.path == RMSNORM_PATH_ROWS_COLS && (cols_dgamma == nullptr || !want_partials) &&
-        !two_stage(&p, M, N, dtype, cus))
+    if (p.path == RMSNORM_PATH_ROWS_COLS && (cols == nullptr || !want_partials) && !two_stage(&p, M, N, dtype, cus))
         return fail(RMSNORM_EINVAL, "no two-stage layout for this plan");
     // Workspace: the partial rows, then the recomputed row statistics (rstd;
     // LayerNorm: means, then rstd), M floats each, when the caller has none.
@@ -361,11 +366,12 @@ int do_partials(const void *dy, const void *v, const void *gamma, const float *r
     }
     BwdArgs a{dy, v, gamma, rs, dh, dx, partials, ld, M, (int32_t)N, offset};
     a.mean = mu;
-    if (p.path == RMSNORM_PATH_ROWS_COLS) { // no partial rows: the column workgroups write dgamma
+    if (p.path == RMSNORM_PATH_ROWS_COLS) { // no partial rows: the column workgroups write the outputs
         a.partials = nullptr;
-        a.dgamma = cols_dgamma;
+        a.dgamma = cols->dgamma;
+        a.dbeta = cols->dbeta;
         a.col_cs = p.col_chunks;
-        *cols_done = true;
+        cols->done = true;
     }
     return launched(launch_bwd(dtype, fused, ln != nullptr, p, a, stream), "backward");
 }
@@ -401,9 +407,10 @@ int do_ln_bwd(const void *dy, const void *dh, const void *v, const void *gamma, 
         return fail(RMSNORM_EINVAL, "dbeta aliases another output");
     const LnBwd ln{mean, dgamma != nullptr || dbeta != nullptr};
     int64_t programs = 0;
+    ColsOut cols{dgamma, dbeta, false};
     int rc = do_partials(dy, v, gamma, rstd, dh, dx, workspace, workspace_bytes, &programs, M, N, eps, offset,
-                         dtype, stream, &ln);
-    if (rc || !ln.partials)
+                         dtype, stream, &ln, &cols);
+    if (rc || !ln.partials || cols.done) // the one-launch backward has written dgamma and dbeta
         return rc;
     return launched(launch_finalize(dtype, static_cast<const float *>(workspace), programs, partial_ld(N), N,
                                     dgamma, dbeta, stream),
@@ -426,10 +433,10 @@ int do_bwd(const void *dy, const void *dh, const void *v, const void *gamma, con
     if (dtype_known(dtype) && !aligned(dgamma, (size_t)elem_bytes(dtype)))
         return fail(RMSNORM_EINVAL, "dgamma not aligned to its element size");
     int64_t programs = 0;
-    bool cols_done = false;
+    ColsOut cols{dgamma, nullptr, false};
     int rc = do_partials(dy, v, gamma, rstd, dh, dx, workspace, workspace_bytes, &programs, M, N, eps, offset,
-                         dtype, stream, nullptr, dgamma, &cols_done);
-    if (rc || cols_done) // the one-launch backward has written dgamma
+                         dtype, stream, nullptr, &cols);
+    if (rc || cols.done) // the one-launch backward has written dgamma
         return rc;
     return do_finalize(static_cast<const float *>(workspace), programs, N, dgamma, dtype, stream);
 }

@@ -61,10 +61,12 @@ struct BwdRow {
 // ..., four at a time with their loads in flight together.  The per-thread
 // sums are folded by lane exchange within each wave and then in wave order
 // through LDS, so the order depends only on M, the workgroup size and col_cs.
+// LayerNorm (LN): dgamma_j = sum_i dy_ij * (v_ij - mean_i) * rstd_i and
+// dbeta_j = sum_i dy_ij, the same way.
 // The loads go through the cache: a 128-byte line holds 8 / col_cs slabs,
 // and the workgroups that share it are given one XCD (the dispatcher sends
 // workgroup g to XCD g mod 8, so b, b + 8, b + 16, ... get consecutive slabs).
-template <typename T, int V>
+template <typename T, int V, bool LN>
 __device__ __forceinline__ void dgamma_columns(const BwdArgs &a)
 {
     using C = Chunk<T, V>;
@@ -84,70 +86,89 @@ __device__ __forceinline__ void dgamma_columns(const BwdArgs &a)
     const int c = (int)(slab * cs) + lc;
     const T *__restrict__ dyp = static_cast<const T *>(a.dy);
     const T *__restrict__ vp = static_cast<const T *>(a.v);
-    float acc[V];
+    constexpr int S = LN ? 2 : 1; // sums per element: dgamma (and dbeta)
+    float acc[S][V];
 #pragma unroll
-    for (int e = 0; e < V; ++e)
-        acc[e] = 0.0f;
+    for (int q = 0; q < S; ++q) {
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            acc[q][e] = 0.0f;
+    }
+    auto add = [&](const C &d, const C &x, float rs, float mu) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            if constexpr (LN) {
+                acc[0][e] = fmaf(d.get(e), (x.get(e) - mu) * rs, acc[0][e]);
+                acc[1][e] += d.get(e);
+            } else {
+                acc[0][e] = fmaf(d.get(e), x.get(e) * rs, acc[0][e]);
+            }
+        }
+    };
     if (c < nchunks) {
         int64_t r = phase;
         for (; r + 3 * (int64_t)nphase < a.M; r += 4 * (int64_t)nphase) {
             C d[4], x[4];
-            float rs[4];
+            float rs[4], mu[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int64_t rr = r + u * (int64_t)nphase;
                 d[u].load_cached(dyp + rr * N + (int64_t)c * V);
                 x[u].load_cached(vp + rr * N + (int64_t)c * V);
                 rs[u] = a.rstd[rr];
+                mu[u] = LN ? a.mean[rr] : 0.0f;
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-#pragma unroll
-                for (int e = 0; e < V; ++e)
-                    acc[e] = fmaf(d[u].get(e), x[u].get(e) * rs[u], acc[e]);
-            }
+            for (int u = 0; u < 4; ++u)
+                add(d[u], x[u], rs[u], mu[u]);
         }
         for (; r < a.M; r += nphase) {
             C d, x;
             d.load_cached(dyp + r * N + (int64_t)c * V);
             x.load_cached(vp + r * N + (int64_t)c * V);
-            const float rs = a.rstd[r];
-#pragma unroll
-            for (int e = 0; e < V; ++e)
-                acc[e] = fmaf(d.get(e), x.get(e) * rs, acc[e]);
+            add(d, x, a.rstd[r], LN ? a.mean[r] : 0.0f);
         }
     }
     // lanes l and l ^ cs, l ^ 2 cs, ... of a wave hold the same chunk
     for (int off = cs; off < 64; off <<= 1) {
 #pragma unroll
-        for (int e = 0; e < V; ++e)
-            acc[e] += __shfl_xor(acc[e], off);
+        for (int q = 0; q < S; ++q) {
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                acc[q][e] += __shfl_xor(acc[q][e], off);
+        }
     }
-    __shared__ float colred[16][64]; // [wave][chunk in slab * V + element]: cs * V <= 64
+    // [wave][sum][chunk in slab * V + element]: cs * V <= 64
+    __shared__ float colred[16][S][64];
     const int w = (int)threadIdx.x >> 6, l = (int)threadIdx.x & 63;
     if (l < cs) {
 #pragma unroll
-        for (int e = 0; e < V; ++e)
-            colred[w][l * V + e] = acc[e];
+        for (int q = 0; q < S; ++q) {
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                colred[w][q][l * V + e] = acc[q][e];
+        }
     }
     __syncthreads();
-    const int j = (int)threadIdx.x; // element j of the slab
-    if (j < cs * V) {
-        float s = colred[0][j];
-        for (int q = 1; q < nt / 64; ++q)
-            s += colred[q][j];
+    const int j = (int)threadIdx.x % 64; // element j of the slab, sum q
+    const int q = (int)threadIdx.x / 64;
+    if (j < cs * V && q < S) {
+        float s = colred[0][q][j];
+        for (int wv = 1; wv < nt / 64; ++wv)
+            s += colred[wv][q][j];
         const int64_t col = slab * cs * V + j;
-        if (col < N)
-            static_cast<T *>(a.dgamma)[col] = to_storage<T>(s);
+        T *out = static_cast<T *>(q == 0 ? a.dgamma : a.dbeta);
+        if (col < N && out != nullptr)
+            out[col] = to_storage<T>(s);
     }
 }
 
 template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FUSED, bool EXACT, bool LN>
 __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
 {
-    if constexpr (bwd_cols_layout(LN, TEAM, K, WR, V)) {
+    if constexpr (bwd_cols_layout(TEAM, K, WR, V)) {
         if (blockIdx.x >= a.grid) { // a dgamma column workgroup (a.col_cs > 0)
-            dgamma_columns<T, V>(a);
+            dgamma_columns<T, V, LN>(a);
             return;
         }
     }

@@ -52,8 +52,10 @@ struct BwdArgs {
     const float *mean = nullptr;
     // One-launch backward (RMSNORM_PATH_ROWS_COLS, col_cs > 0): the
     // workgroups from `grid` on each own col_cs consecutive chunks of the row
-    // and write dgamma (T) directly; the row programs write no partial rows.
+    // and write dgamma (and for LayerNorm dbeta; T, either may be null)
+    // directly; the row programs write no partial rows.
     void *dgamma = nullptr;
+    void *dbeta = nullptr;
     int32_t col_cs = 0;
 };
 
@@ -145,11 +147,11 @@ constexpr int bwd_pairs_bound(bool fused, bool ln = false) { return fused ? 256 
 constexpr int kDepthPairs = 8;
 
 // One-launch backward (RMSNORM_PATH_ROWS_COLS): the row layouts that carry
-// the column workgroups (RMSNorm, workgroup teams, w in registers, one vector
-// chunk per lane: the layouts of rows of up to 1024 chunks).
-constexpr bool bwd_cols_layout(bool ln, int team, int chunks, int w_regs, int vec)
+// the column workgroups (workgroup teams, w in registers, one vector chunk
+// per lane: the layouts of rows of up to 1024 chunks; RMSNorm and LayerNorm).
+constexpr bool bwd_cols_layout(int team, int chunks, int w_regs, int vec)
 {
-    return !ln && team == 0 && chunks == 1 && w_regs == 1 && vec > 1;
+    return team == 0 && chunks == 1 && w_regs == 1 && vec > 1;
 }
 // Column workgroups of a launch: one per col_cs chunks, rounded up to whole
 // rounds over the 8 XCDs (the extra ones exit at once).

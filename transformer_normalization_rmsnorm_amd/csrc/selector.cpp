@@ -55,6 +55,19 @@ constexpr int kPairMaxThreadsLN = 256;
 // workgroups re-read dy and x, 2MN elements, and beyond these sizes that costs
 // more than the finalizer launch it saves.
 constexpr int64_t kColsMaxBytes = int64_t(3) << 20;
+// LayerNorm's two-stage backward writes and sums two partial rows per program
+// (dgamma and dbeta), so one launch pays off further: taken at up to three
+// rows per program when the rows hold at most kColsMaxBytesLN, and at up to
+// two at any width it covers for 16-bit rows.  Measured (bf16 unless noted):
+// one row per program 14-36% faster (64 x 2048 -26%, 128 x 8192 -36%,
+// 256 x 4096 -32%, fp32 128 x 2048 -28%, fused-add 256 x 2048 -30%); two rows
+// 512 x 2048 -14%, 512 x 4096 -16%, 512 x 8192 -12%, fp32 512 x 2048 -13%,
+// but fp32 512 x 4096 (8 MiB) +3.5%; three 768 x 2048 -4%, 768 x 4096 -5%,
+// fused-add 768 x 2048 -7%, fp32 fused-add 600 x 1024 -16%, but 768 x 8192
+// +0.5%; four 1024 x 2048 +1-3%, 1024 x 4096 +7%, 1024 x 8192 +14%, fp32
+// 1024 x 2048 +12%.  Its column workgroups fold two sums with a wavefront
+// each, so they need at least 128 threads.
+constexpr int64_t kColsMaxBytesLN = int64_t(6) << 20;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -350,7 +363,7 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
     if (p->w_regs != 0 && p->w_regs != 1)
         return false;
     const bool cols = p->path == RMSNORM_PATH_ROWS_COLS;
-    if (cols && (!bwd || is_ln_op(p->op) || p->team != 0 || p->vec == 1 || p->w_regs != 1))
+    if (cols && (!bwd || p->team != 0 || p->vec == 1 || p->w_regs != 1))
         return false;
     if (!cols)
         p->col_chunks = 0;
@@ -371,7 +384,9 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
             return false;
         p->chunks = k;
         if (cols) {
-            if (!bwd_cols_layout(false, p->team, k, p->w_regs, p->vec))
+            // (LayerNorm's column workgroups fold dgamma and dbeta with one
+            // wavefront each)
+            if (!bwd_cols_layout(p->team, k, p->w_regs, p->vec) || p->threads < (is_ln_op(p->op) ? 128 : 64))
                 return false;
             if (p->col_chunks <= 0) {
                 // slab width: about one row per thread of a column workgroup
@@ -539,10 +554,14 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             tiling_ok(op, dtype, vec, 0, p.chunks, b0, p.threads, nchunks))
             p.depth = 0;
     }
-    if (placed && bwd && !is_ln_op(op) && p.path == RMSNORM_PATH_ROWS &&
-        bwd_cols_layout(false, p.team, p.chunks, p.w_regs, p.vec) && M >= 1) {
+    const bool ln = is_ln_op(op);
+    if (placed && bwd && p.path == RMSNORM_PATH_ROWS && bwd_cols_layout(p.team, p.chunks, p.w_regs, p.vec) &&
+        p.threads >= (ln ? 128 : 64) && M >= 1) {
         const int64_t programs = (int64_t)kBwdProgramsPerCU * std::max(num_cus, 1);
-        if (M <= programs || (M <= 2 * programs && M * N * elem_bytes(dtype) <= kColsMaxBytes)) {
+        const int64_t bytes = M * N * elem_bytes(dtype);
+        if (ln ? (M <= programs || (M <= 2 * programs && elem_bytes(dtype) == 2) ||
+                  (M <= 3 * programs && bytes <= kColsMaxBytesLN))
+               : (M <= programs || (M <= 2 * programs && bytes <= kColsMaxBytes))) {
             p.path = RMSNORM_PATH_ROWS_COLS;
             p.col_chunks = 0; // the rule in complete_plan
         }
