@@ -295,10 +295,12 @@ def measure_workload(w, lib, rn, torch, iters, warmup, detailed=True):
     # few rows, the column workgroups' second read of dy and x
     ln_bop = rn.OP_LN_FUSED_ADD_BWD if w.fused else rn.OP_LN_BWD
     bplan = res["plans"]["bwd"]
-    P_ln = rn.rmsnorm_query_plan(ln_bop, w.M, w.N, dt)["programs"]
-    extra_rms = (2 * w.M * w.N * w.elem_bytes if bplan["path"] == rn.PATH_ROWS_COLS
-                 else 2 * bplan["programs"] * w.N * 4)
-    res["workspace_bytes"] = {"bwd": extra_rms, "ln_bwd": 2 * 2 * P_ln * w.N * 4}
+    ln_plan = rn.rmsnorm_query_plan(ln_bop, w.M, w.N, dt)
+    res["plans"]["ln_bwd"] = ln_plan
+    second_read = 2 * w.M * w.N * w.elem_bytes
+    extra_rms = second_read if bplan["path"] == rn.PATH_ROWS_COLS else 2 * bplan["programs"] * w.N * 4
+    extra_ln = second_read if ln_plan["path"] == rn.PATH_ROWS_COLS else 2 * 2 * ln_plan["programs"] * w.N * 4
+    res["workspace_bytes"] = {"bwd": extra_rms, "ln_bwd": extra_ln}
     for mode in (("cold", "hot") if detailed else ("cold",)):
         S = Sets(w, lib, rn, torch, n_sets_for(w, mode == "cold"))
         K = len(S.sets)
@@ -738,7 +740,7 @@ def summarize_report(path: str):
         if ce:
             print(f"  {wl['workload']:28s} ceilings: copy {ce['copy_GBs']:.0f} GB/s, three-stream "
                   f"{ce['three_stream_GBs']:.0f} GB/s")
-        for k in ("fwd", "bwd"):
+        for k in ("fwd", "bwd", "ln_bwd"):
             p = wl.get("plans", {}).get(k)
             if p:
                 print(f"  {wl['workload']:28s} {k} plan: path {p['path']} vec {p['vec']} team {p['team']} threads "
