@@ -224,10 +224,9 @@ def test_plans_for_workloads(M, N, dt, fused):
 
 
 # One-launch backward (PATH_ROWS_COLS): rows of one chunk per lane with w in
-# registers; RMSNorm at most one row per program, or two with at most 3 MiB of
-# rows; LayerNorm at most three with at most 6 MiB, or two of 16-bit
-# elements at any width; the slab rule:
-# max(threads / M, chunks / CUs) as a power of two, at most 8.
+# registers; RMSNorm up to two rows per program, or four with at most 6 MiB
+# of rows; LayerNorm up to four; the slab rule: max(threads / M, chunks / CUs)
+# as a power of two, at most 8.
 COLS, ROWS = rn.PATH_ROWS_COLS, rn.PATH_ROWS
 COLS_CASES = [  # (M, N, dtype, fused, RMSNorm path, col_chunks, LayerNorm path, col_chunks)
     (1, 2048, rn.BF16, False, COLS, 8, COLS, 8), (64, 2048, rn.BF16, False, COLS, 4, COLS, 4),
@@ -235,12 +234,16 @@ COLS_CASES = [  # (M, N, dtype, fused, RMSNorm path, col_chunks, LayerNorm path,
     (256, 8192, rn.BF16, False, COLS, 4, COLS, 4), (512, 2048, rn.BF16, False, COLS, 1, COLS, 1),
     (384, 4096, rn.BF16, False, COLS, 2, COLS, 2), (256, 2048, rn.BF16, True, COLS, 1, COLS, 1),
     (128, 2048, rn.F32, False, COLS, 4, COLS, 4), (256, 4096, rn.F16, False, COLS, 2, COLS, 2),
-    # two rows per program beyond 3 MiB, three up to 6 MiB: LayerNorm only
-    (512, 4096, rn.BF16, False, ROWS, 0, COLS, 2), (512, 2048, rn.F32, False, ROWS, 0, COLS, 2),
-    (512, 8192, rn.BF16, False, ROWS, 0, COLS, 4), (512, 4096, rn.F32, False, ROWS, 0, ROWS, 0),
-    (384, 4096, rn.F32, False, ROWS, 0, COLS, 4), (768, 2048, rn.BF16, False, ROWS, 0, COLS, 1),
-    (768, 4096, rn.BF16, False, ROWS, 0, COLS, 2), (768, 2048, rn.BF16, True, ROWS, 0, COLS, 1),
-    (768, 8192, rn.BF16, False, ROWS, 0, ROWS, 0), (1024, 2048, rn.BF16, False, ROWS, 0, ROWS, 0),
+    (512, 4096, rn.BF16, False, COLS, 2, COLS, 2), (512, 2048, rn.F32, False, COLS, 2, COLS, 2),
+    (512, 8192, rn.BF16, False, COLS, 4, COLS, 4), (512, 4096, rn.F32, False, COLS, 4, COLS, 4),
+    # three and four rows per program: RMSNorm up to 6 MiB of rows
+    (768, 2048, rn.BF16, False, COLS, 1, COLS, 1), (768, 4096, rn.BF16, False, COLS, 2, COLS, 2),
+    (768, 2048, rn.BF16, True, COLS, 1, COLS, 1), (768, 2048, rn.F32, False, COLS, 2, COLS, 2),
+    (1024, 2048, rn.BF16, False, COLS, 1, COLS, 1), (1024, 1536, rn.BF16, False, COLS, 1, COLS, 1),
+    (768, 8192, rn.BF16, False, ROWS, 0, COLS, 4), (1024, 4096, rn.BF16, False, ROWS, 0, COLS, 2),
+    (1024, 8192, rn.BF16, False, ROWS, 0, COLS, 4), (1024, 2048, rn.F32, False, ROWS, 0, COLS, 2),
+    # more rows per program: two stages
+    (1536, 4096, rn.BF16, False, ROWS, 0, ROWS, 0), (2048, 2048, rn.BF16, False, ROWS, 0, ROWS, 0),
     (4096, 4096, rn.BF16, False, ROWS, 0, ROWS, 0), (0, 2048, rn.BF16, False, ROWS, 0, ROWS, 0),
     (256, 1024, rn.BF16, False, ROWS, 0, ROWS, 0),    # one wavefront per row: not a workgroup team
     (256, 16384, rn.BF16, False, ROWS, 0, ROWS, 0),   # gamma re-read per row
@@ -395,8 +398,11 @@ def test_layernorm_plans(M, N, dt):
                 assert q["threads"] * q["chunks"] == nc, q
     for op in (rn.OP_LN_BWD, rn.OP_LN_FUSED_ADD_BWD):
         q = plan(op, M, N, dt)
-        if q["path"] == rn.PATH_ROWS:
+        if q["path"] in (rn.PATH_ROWS, rn.PATH_ROWS_COLS):
             assert covers(q, N)
+        if q["path"] == rn.PATH_ROWS_COLS:  # one launch: no partial rows, only mean and rstd
+            assert q["programs"] == 0 and q["workspace_bytes"] == 2 * (-(-M * 4 // 256) * 256)
+            continue
         assert q["programs"] == q["grid"]
         # two sets of partial rows (dgamma, dbeta), then room for mean and rstd
         assert q["workspace_bytes"] == -(-2 * q["programs"] * ld * 4 // 256) * 256 + 2 * (-(-M * 4 // 256) * 256)

@@ -266,6 +266,7 @@ COLS = [
     (100, 4096, "f32", dict(threads=1024, col_chunks=4)),
     (257, 1024, "f32", dict(threads=256, col_chunks=1, grid=100)),
     (64, 2048, "bf16", dict(threads=256, col_chunks=4, rows_per_step=2, grid=16)),
+    (1024, 2048, "bf16", dict(threads=256, col_chunks=1, rows_per_step=2)),  # four rows per program
 ]
 COLS_CASES = [(M, N, dt, f, fu) for M, N, dt, f in COLS + in_f16(COLS) for fu in (False, True)]
 
@@ -302,6 +303,14 @@ def test_one_launch_backward(M, N, dt, fields, fused):
             torch.cuda.synchronize()
             assert dx4.data_ptr() == dh.data_ptr()
             assert np.array_equal(from_dev(dx4).view(np.uint8), from_dev(dx).view(np.uint8))
+
+
+@pytest.mark.parametrize("M,N,dt,fused", [(1024, 2048, "bf16", False), (768, 4096, "bf16", True),
+                                          (512, 8192, "bf16", False), (768, 2048, "f32", False)])
+def test_one_launch_backward_default_shapes(M, N, dt, fused):
+    op = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
+    assert rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)["path"] == rn.PATH_ROWS_COLS
+    run_case(M, N, dt, fused, gemma=dt == "f32")
 
 
 def test_one_launch_backward_is_the_default_for_few_rows():

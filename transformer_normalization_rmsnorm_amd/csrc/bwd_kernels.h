@@ -163,11 +163,17 @@ __device__ __forceinline__ void dgamma_columns(const BwdArgs &a)
     }
 }
 
-template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FUSED, bool EXACT, bool LN>
+// COLS: the one-launch backward (col_cs > 0): the row programs, then from
+// `grid` on the dgamma (and dbeta) column workgroups.  They read dy and x a
+// second time, so its row programs load the rows through the cache, where
+// the second read finds them (the two-stage backward streams them with the
+// nontemporal hint).
+template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FUSED, bool EXACT, bool LN, bool COLS>
 __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
 {
-    if constexpr (bwd_cols_layout(TEAM, K, WR, V)) {
-        if (blockIdx.x >= a.grid) { // a dgamma column workgroup (a.col_cs > 0)
+    if constexpr (COLS) {
+        static_assert(bwd_cols_layout(TEAM, K, WR, V), "column workgroups need one chunk per lane, w in registers");
+        if (blockIdx.x >= a.grid) {
             dgamma_columns<T, V, LN>(a);
             return;
         }
@@ -256,8 +262,13 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
             // row-invariant ones (gamma's) in registers across the loop
             if constexpr (LN)
                 pin_vgpr(c);
-            b.v[k].load(vp + base + (int64_t)c * V);
-            b.dy[k].load(dyp + base + (int64_t)c * V);
+            if constexpr (COLS) {
+                b.v[k].load_cached(vp + base + (int64_t)c * V);
+                b.dy[k].load_cached(dyp + base + (int64_t)c * V);
+            } else {
+                b.v[k].load(vp + base + (int64_t)c * V);
+                b.dy[k].load(dyp + base + (int64_t)c * V);
+            }
             if constexpr (!WR)
                 b.g[k].load_cached(gsrc + (int64_t)c * V);
             if constexpr (FUSED)
@@ -865,9 +876,24 @@ static hipError_t launch_bwd_rows(const rmsnorm_plan &p, const BwdArgs &a, hipSt
     const size_t lds = TEAM ? sets * (size_t)(p.threads / TEAM) * (size_t)a.N * sizeof(float)
                             : (BL ? (size_t)a.N * sizeof(float) : 0);
     constexpr int kTiling = bwd_tiling(LN, FUSED, (int)sizeof(T), V, TEAM, K, BOUND);
+    const bool exact = (int64_t)lanes * K == a.N / V;
+    if (cols) {
+        // (layouts of one chunk per lane have both instances)
+        if constexpr (bwd_cols_layout(TEAM, K, WR, V) && kTiling == TILING_ANY) {
+            if (exact)
+                hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, true, LN, true>), grid, block,
+                                   lds, s, a);
+            else
+                hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, false, LN, true>), grid, block,
+                                   lds, s, a);
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidConfiguration; // the selector plans column workgroups only on these layouts
+        }
+    }
     if constexpr (V > 1 && kTiling != TILING_MASKED_ONLY) {
-        if ((int64_t)lanes * K == a.N / V) {
-            hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, true, LN>), grid, block, lds, s,
+        if (exact) {
+            hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, true, LN, false>), grid, block, lds, s,
                                a);
             return hipGetLastError();
         }
@@ -875,7 +901,7 @@ static hipError_t launch_bwd_rows(const rmsnorm_plan &p, const BwdArgs &a, hipSt
     if constexpr (kTiling == TILING_EXACT_ONLY) {
         return hipErrorInvalidConfiguration; // ragged row: the selector never plans it
     } else {
-        hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, false, LN>), grid, block, lds, s,
+        hipLaunchKernelGGL((bwd_rows_kernel<T, V, TEAM, K, D, WR, BOUND, FUSED, false, LN, false>), grid, block, lds, s,
                            a);
         return hipGetLastError();
     }

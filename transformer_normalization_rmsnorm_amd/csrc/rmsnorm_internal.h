@@ -146,9 +146,10 @@ constexpr bool bwd_pairs_compiled(bool ln, bool fused, int team, int chunks, int
 constexpr int bwd_pairs_bound(bool fused, bool ln = false) { return fused ? 256 : ln ? 512 : 1024; }
 constexpr int kDepthPairs = 8;
 
-// One-launch backward (RMSNORM_PATH_ROWS_COLS): the row layouts that carry
-// the column workgroups (workgroup teams, w in registers, one vector chunk
-// per lane: the layouts of rows of up to 1024 chunks; RMSNorm and LayerNorm).
+// One-launch backward (RMSNORM_PATH_ROWS_COLS): the row layouts that have
+// instances with column workgroups (workgroup teams, w in registers, one
+// vector chunk per lane: the layouts of rows of up to 1024 chunks; RMSNorm
+// and LayerNorm).
 constexpr bool bwd_cols_layout(int team, int chunks, int w_regs, int vec)
 {
     return team == 0 && chunks == 1 && w_regs == 1 && vec > 1;

@@ -44,30 +44,30 @@ constexpr int kPairMaxThreadsFused = 256;
 // 17.3 -> 15.4 us; at 512 threads within 2% either way (4096 x 4096 24.3 /
 // 24.0 us, 16384 x 4096 68.3 / 69.9 us), so it stops at 256.
 constexpr int kPairMaxThreadsLN = 256;
-// One-launch backward (RMSNORM_PATH_ROWS_COLS) for few rows: taken at up to
-// one row per program, and at up to two when the rows hold at most
-// kColsMaxBytes.  Measured on MI355X against the two-stage backward (cold
-// buffers, bf16 unless noted): one row per program 18-43% faster (64 x 2048
-// 6.24 -> 4.09 us, 128 x 8192 7.91 -> 4.72, 256 x 4096 7.35 -> 5.43, fp32
-// 128 x 2048 6.11 -> 3.99, fused-add 256 x 2048 6.52 -> 4.67); two rows per
-// program 512 x 2048 -10%, 384 x 4096 -13%, but 512 x 4096 -2%, fp32
-// 512 x 2048 +4% and 512 x 8192 +4%; three (768 x 2048) no gain.  The column
-// workgroups re-read dy and x, 2MN elements, and beyond these sizes that costs
-// more than the finalizer launch it saves.
-constexpr int64_t kColsMaxBytes = int64_t(3) << 20;
-// LayerNorm's two-stage backward writes and sums two partial rows per program
-// (dgamma and dbeta), so one launch pays off further: taken at up to three
-// rows per program when the rows hold at most kColsMaxBytesLN, and at up to
-// two at any width it covers for 16-bit rows.  Measured (bf16 unless noted):
-// one row per program 14-36% faster (64 x 2048 -26%, 128 x 8192 -36%,
-// 256 x 4096 -32%, fp32 128 x 2048 -28%, fused-add 256 x 2048 -30%); two rows
-// 512 x 2048 -14%, 512 x 4096 -16%, 512 x 8192 -12%, fp32 512 x 2048 -13%,
-// but fp32 512 x 4096 (8 MiB) +3.5%; three 768 x 2048 -4%, 768 x 4096 -5%,
-// fused-add 768 x 2048 -7%, fp32 fused-add 600 x 1024 -16%, but 768 x 8192
-// +0.5%; four 1024 x 2048 +1-3%, 1024 x 4096 +7%, 1024 x 8192 +14%, fp32
-// 1024 x 2048 +12%.  Its column workgroups fold two sums with a wavefront
-// each, so they need at least 128 threads.
-constexpr int64_t kColsMaxBytesLN = int64_t(6) << 20;
+// One-launch backward (RMSNORM_PATH_ROWS_COLS) for few rows.  Its column
+// workgroups read dy and x a second time; its row programs load the rows
+// through the cache, so that read mostly finds them there.  Measured on
+// MI355X against the two-stage backward at the same layout (cold buffers,
+// bf16 unless noted), RMSNorm: one row per program 27-39% faster (64 x 2048
+// 7.53 -> 5.35 us, 128 x 8192 -39%, 256 x 4096 -35%, 256 x 8192 -27%, fp32
+// 128 x 2048 -29%, fused-add 256 x 2048 -34%); two rows 13-27% (512 x 2048
+// -27%, 512 x 4096 -23%, 512 x 8192 -15%, fp32 512 x 4096 -13%, fused-add
+// 512 x 4096 -16%); three 768 x 2048 -16%, 768 x 4096 -17%, fp32 768 x 2048
+// -18%, but 768 x 8192 (12 MiB) -0.8%; four 1024 x 2048 -10%, but
+// 1024 x 4096 (8 MiB) +3% and 1024 x 8192 +13%; eight (2048 x 2048) +8%.
+// So: up to two rows per program, or up to four while the rows hold at most
+// kColsMaxBytes.
+constexpr int64_t kColsMaxBytes = int64_t(6) << 20;
+// LayerNorm's two-stage backward writes and sums two partial rows per
+// program (dgamma and dbeta), so one launch pays off further: up to four rows
+// per program at any width it covers (16 MiB of rows).  Measured: one row per
+// program 256 x 4096 -33%; two 512 x 4096 -24%, 512 x 8192 -21%, fp32
+// 512 x 4096 -15%; three 768 x 4096 -18%, 768 x 8192 -13%; four 1024 x 2048
+// -11%, 1024 x 4096 -7%, 1024 x 8192 -3%, fp32 1024 x 2048 -8%, fused-add
+// 1024 x 4096 -2%; six (1536 x 4096) +2%, eight (2048 x 2048) +7%.  Its
+// column workgroups fold two sums with a wavefront each, so they need at
+// least 128 threads.
+constexpr int64_t kColsMaxRowsPerProgramLN = 4;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -559,9 +559,8 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
         p.threads >= (ln ? 128 : 64) && M >= 1) {
         const int64_t programs = (int64_t)kBwdProgramsPerCU * std::max(num_cus, 1);
         const int64_t bytes = M * N * elem_bytes(dtype);
-        if (ln ? (M <= programs || (M <= 2 * programs && elem_bytes(dtype) == 2) ||
-                  (M <= 3 * programs && bytes <= kColsMaxBytesLN))
-               : (M <= programs || (M <= 2 * programs && bytes <= kColsMaxBytes))) {
+        if (ln ? M <= kColsMaxRowsPerProgramLN * programs
+               : (M <= 2 * programs || (M <= 4 * programs && bytes <= kColsMaxBytes))) {
             p.path = RMSNORM_PATH_ROWS_COLS;
             p.col_chunks = 0; // the rule in complete_plan
         }
