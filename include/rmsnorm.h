@@ -153,10 +153,11 @@ int rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *bytes);
 /* Backward (FlyDSL PR #855 "Hybrid atomic / two-stage backward"): a bounded
  * persistent grid writes dx and float32 dgamma partials into `workspace`, then
  * a finalizer sums the partials in a fixed order and writes dgamma in T.
- * With few rows (at most one or two per program; the plan's path is then
- * RMSNORM_PATH_ROWS_COLS) one launch does both: its first workgroups write dx,
- * the others sum dgamma_j = sum_i dy_ij * x_ij * rstd_i directly by columns,
- * in a fixed order, and no partial rows are written.  Either way dgamma is
+ * With few rows (up to two per program, or four while the rows hold at most
+ * 6 MiB; the plan's path is then RMSNORM_PATH_ROWS_COLS) one launch does both:
+ * its first workgroups write dx, the others sum
+ * dgamma_j = sum_i dy_ij * x_ij * rstd_i directly by columns, in a fixed
+ * order, and no partial rows are written.  Either way dgamma is
  * bit-identical run to run for the same shape, dtype and device.
  *   dy, x  [M, N] T;  gamma [N] T (NULL: non-affine, then dgamma NULL);
  *   rstd   [M] f32 from the forward, or NULL to recompute it from x with eps;
@@ -238,7 +239,7 @@ typedef enum rmsnorm_op {
 typedef enum rmsnorm_path {
     RMSNORM_PATH_ROWS = 0, /* each row held in registers by a team of lanes */
     RMSNORM_PATH_LOOP = 1, /* rows streamed in passes (any N) */
-    RMSNORM_PATH_ROWS_COLS = 2 /* RMSNorm backward with few rows: dx as on the ROWS path
+    RMSNORM_PATH_ROWS_COLS = 2 /* backward with few rows: dx as on the ROWS path
                                   (workgroup teams, w in registers, one chunk per lane),
                                   and dgamma summed directly by fin_grid column workgroups
                                   of the same launch, each owning col_chunks consecutive
