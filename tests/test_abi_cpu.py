@@ -224,13 +224,15 @@ def test_plans_for_workloads(M, N, dt, fused):
 
 
 # One-launch backward (PATH_ROWS_COLS): rows of one chunk per lane with w in
-# registers; RMSNorm up to two rows per program, or four with at most 6 MiB
-# of rows; LayerNorm up to four; the slab rule: max(threads / M, chunks / CUs)
-# as a power of two, at most 8.
+# registers, or of more than 512 chunks two chunks per lane at half the lanes
+# with gamma re-read; RMSNorm up to two rows per program, or four with at most
+# 6 MiB of rows, or three at more than 768 chunks; LayerNorm up to
+# four; the slab rule: max(threads / M, chunks / CUs) as a power of two, at
+# most 8.
 COLS, ROWS = rn.PATH_ROWS_COLS, rn.PATH_ROWS
 COLS_CASES = [  # (M, N, dtype, fused, RMSNorm path, col_chunks, LayerNorm path, col_chunks)
     (1, 2048, rn.BF16, False, COLS, 8, COLS, 8), (64, 2048, rn.BF16, False, COLS, 4, COLS, 4),
-    (128, 8192, rn.BF16, False, COLS, 8, COLS, 8), (256, 4096, rn.BF16, False, COLS, 2, COLS, 2),
+    (256, 4096, rn.BF16, False, COLS, 2, COLS, 2),
     (256, 8192, rn.BF16, False, COLS, 4, COLS, 4), (512, 2048, rn.BF16, False, COLS, 1, COLS, 1),
     (384, 4096, rn.BF16, False, COLS, 2, COLS, 2), (256, 2048, rn.BF16, True, COLS, 1, COLS, 1),
     (128, 2048, rn.F32, False, COLS, 4, COLS, 4), (256, 4096, rn.F16, False, COLS, 2, COLS, 2),
@@ -240,8 +242,14 @@ COLS_CASES = [  # (M, N, dtype, fused, RMSNorm path, col_chunks, LayerNorm path,
     (768, 2048, rn.BF16, False, COLS, 1, COLS, 1), (768, 4096, rn.BF16, False, COLS, 2, COLS, 2),
     (768, 2048, rn.BF16, True, COLS, 1, COLS, 1), (768, 2048, rn.F32, False, COLS, 2, COLS, 2),
     (1024, 2048, rn.BF16, False, COLS, 1, COLS, 1), (1024, 1536, rn.BF16, False, COLS, 1, COLS, 1),
-    (768, 8192, rn.BF16, False, ROWS, 0, COLS, 4), (1024, 4096, rn.BF16, False, ROWS, 0, COLS, 2),
-    (1024, 8192, rn.BF16, False, ROWS, 0, COLS, 4), (1024, 2048, rn.F32, False, ROWS, 0, COLS, 2),
+    (1024, 4096, rn.BF16, False, ROWS, 0, COLS, 2), (1024, 2048, rn.F32, False, ROWS, 0, COLS, 2),
+    # rows of more than 512 chunks: two chunks per lane at half the lanes, up to three rows per
+    # program for RMSNorm, four for LayerNorm
+    (768, 8192, rn.BF16, False, COLS, 4, COLS, 4), (1024, 8192, rn.BF16, False, ROWS, 0, COLS, 4),
+    (768, 8192, rn.BF16, True, COLS, 4, COLS, 4), (768, 4096, rn.F32, False, COLS, 4, COLS, 4),
+    (1024, 7168, rn.BF16, False, ROWS, 0, COLS, 4),
+    (1024, 4096, rn.F32, False, ROWS, 0, COLS, 4), (1280, 8192, rn.BF16, False, ROWS, 0, ROWS, 0),
+    (300, 6144, rn.BF16, False, COLS, 4, COLS, 4), (128, 8192, rn.BF16, False, COLS, 8, COLS, 4),
     # more rows per program: two stages
     (1536, 4096, rn.BF16, False, ROWS, 0, ROWS, 0), (2048, 2048, rn.BF16, False, ROWS, 0, ROWS, 0),
     (4096, 4096, rn.BF16, False, ROWS, 0, ROWS, 0), (0, 2048, rn.BF16, False, ROWS, 0, ROWS, 0),
@@ -258,7 +266,12 @@ def test_one_launch_backward_rule(M, N, dt, fused, path, cs, ln_path, ln_cs):
         b = plan(op, M, N, dt)
         assert (b["path"], b["col_chunks"]) == want, b
         if want[0] == COLS:
-            assert b["programs"] == 0 and b["team"] == 0 and b["chunks"] == 1 and b["w_regs"] == 1
+            # two chunks per lane with gamma re-read: LayerNorm rows of more than 512 chunks,
+            # RMSNorm rows of more than 768 from one row per program on
+            nc = N // (4 if dt == rn.F32 else 8)
+            half = nc > 768 and M >= CUS if stats == 1 else nc > 512
+            assert b["programs"] == 0 and b["team"] == 0
+            assert (b["chunks"], b["w_regs"]) == ((2, 0) if half else (1, 1)), b
             assert b["workspace_bytes"] == stats * (-(-M * 4 // 256) * 256)  # only recomputed statistics
         # never on unaligned data
         assert plan(op, M, N, dt, vec_ok=False)["path"] != COLS
@@ -308,6 +321,8 @@ def test_plan_shapes_by_width():
     assert (p["team"], p["threads"], p["chunks"]) == (0, 512, 1)
     p = plan(rn.OP_BWD, 1024, 7168)
     assert (p["team"], p["threads"], p["chunks"]) == (0, 896, 1)
+    p = plan(rn.OP_BWD, 768, 7168)  # one launch: half the lanes, two chunks each
+    assert (p["path"], p["team"], p["threads"], p["chunks"]) == (rn.PATH_ROWS_COLS, 0, 448, 2)
     p = plan(rn.OP_FWD, 1024, 6144, rn.F32)
     assert (p["team"], p["threads"], p["chunks"]) == (0, 192, 8)
     p = plan(rn.OP_FWD, 1024, 7168)

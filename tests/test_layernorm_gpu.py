@@ -145,6 +145,9 @@ LN_COLS = [
     (100, 4096, "f32", dict(threads=1024, col_chunks=4)),
     (64, 2048, "bf16", dict(threads=256, col_chunks=4, rows_per_step=2, grid=16)),
     (768, 2048, "bf16", dict(threads=256, col_chunks=1, rows_per_step=2)),  # three rows per program
+    # two chunks per lane, gamma re-read (rows of more than 512 chunks)
+    (1000, 8192, "bf16", dict(threads=512, col_chunks=4, w_regs=0)),
+    (300, 4000, "f32", dict(threads=512, col_chunks=2, w_regs=0, grid=37)),
 ]
 LN_COLS_CASES = [(M, N, dt, f, fu) for M, N, dt, f in LN_COLS + in_f16(LN_COLS) for fu in (False, True)
                  if not (fu and f.get("rows_per_step") == 2)]  # fused-add LayerNorm has no two-row instance
@@ -157,9 +160,12 @@ LN_COLS_CASES = [(M, N, dt, f, fu) for M, N, dt, f in LN_COLS + in_f16(LN_COLS) 
 def test_layernorm_one_launch_backward(M, N, dt, fields, fused):
     op = rn.OP_LN_FUSED_ADD_BWD if fused else rn.OP_LN_BWD
     vec = 4 if dt == "f32" else 8
-    with rn.plan_override(op, path=rn.PATH_ROWS_COLS, vec=vec, team=0, depth=1, w_regs=1, **fields):
+    over = dict(path=rn.PATH_ROWS_COLS, vec=vec, team=0, depth=1, w_regs=1)
+    over.update(fields)
+    with rn.plan_override(op, **over):
         p = rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)
-        assert (p["path"], p["col_chunks"], p["programs"]) == (rn.PATH_ROWS_COLS, fields["col_chunks"], 0), p
+        assert (p["path"], p["col_chunks"], p["programs"], p["chunks"]) == (rn.PATH_ROWS_COLS, fields["col_chunks"],
+                                                                            0, 2 - over["w_regs"]), p
         inp = make_inputs(M, N, dt, fused=fused, layernorm=True)
         got = gpu_ln(inp, dt, EPS, 0.0, fused)
         check_ln(inp, dt, EPS, 0.0, fused, got)

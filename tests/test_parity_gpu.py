@@ -267,6 +267,11 @@ COLS = [
     (257, 1024, "f32", dict(threads=256, col_chunks=1, grid=100)),
     (64, 2048, "bf16", dict(threads=256, col_chunks=4, rows_per_step=2, grid=16)),
     (1024, 2048, "bf16", dict(threads=256, col_chunks=1, rows_per_step=2)),  # four rows per program
+    # two chunks per lane, gamma re-read (rows of more than 512 chunks)
+    (256, 8192, "bf16", dict(threads=512, col_chunks=4, w_regs=0)),
+    (1000, 8192, "bf16", dict(threads=512, col_chunks=4, w_regs=0)),
+    (300, 8000, "bf16", dict(threads=512, col_chunks=2, w_regs=0, grid=37)),
+    (600, 4096, "f32", dict(threads=512, col_chunks=4, w_regs=0, depth=0)),
 ]
 COLS_CASES = [(M, N, dt, f, fu) for M, N, dt, f in COLS + in_f16(COLS) for fu in (False, True)]
 
@@ -280,10 +285,12 @@ def test_one_launch_backward(M, N, dt, fields, fused):
     gemma = dt == "f32"
     offset = 1.0 if gemma else 0.0
     op = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
-    with rn.plan_override(op, path=rn.PATH_ROWS_COLS, vec=vec, team=0, depth=1, w_regs=1, **fields):
+    over = dict(path=rn.PATH_ROWS_COLS, vec=vec, team=0, depth=1, w_regs=1)
+    over.update(fields)
+    with rn.plan_override(op, **over):
         p = rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)
         assert (p["path"], p["col_chunks"], p["programs"], p["chunks"]) == (rn.PATH_ROWS_COLS, fields["col_chunks"],
-                                                                            0, 1), p
+                                                                            0, 2 - over["w_regs"]), p
         inp, out, dx, dg = run_case(M, N, dt, fused, gemma)
         # bit-identical run to run
         dx2, dg2 = gpu_backward(inp, dt, EPS, offset, out, fused)
@@ -306,7 +313,8 @@ def test_one_launch_backward(M, N, dt, fields, fused):
 
 
 @pytest.mark.parametrize("M,N,dt,fused", [(1024, 2048, "bf16", False), (768, 4096, "bf16", True),
-                                          (512, 8192, "bf16", False), (768, 2048, "f32", False)])
+                                          (512, 8192, "bf16", False), (768, 2048, "f32", False),
+                                          (768, 8192, "bf16", True), (768, 4096, "f32", False)])
 def test_one_launch_backward_default_shapes(M, N, dt, fused):
     op = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
     assert rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)["path"] == rn.PATH_ROWS_COLS

@@ -147,12 +147,12 @@ constexpr int bwd_pairs_bound(bool fused, bool ln = false) { return fused ? 256 
 constexpr int kDepthPairs = 8;
 
 // One-launch backward (RMSNORM_PATH_ROWS_COLS): the row layouts that have
-// instances with column workgroups (workgroup teams, w in registers, one
-// vector chunk per lane: the layouts of rows of up to 1024 chunks; RMSNorm
-// and LayerNorm).
+// instances with column workgroups (workgroup teams of 16-byte chunks: one
+// chunk per lane with w in registers, the layouts of rows of up to 1024
+// chunks, or two with gamma re-read per row; RMSNorm and LayerNorm).
 constexpr bool bwd_cols_layout(int team, int chunks, int w_regs, int vec)
 {
-    return team == 0 && chunks == 1 && w_regs == 1 && vec > 1;
+    return team == 0 && vec > 1 && ((chunks == 1 && w_regs == 1) || (chunks == 2 && w_regs == 0));
 }
 // Column workgroups of a launch: one per col_cs chunks, rounded up to whole
 // rounds over the 8 XCDs (the extra ones exit at once).

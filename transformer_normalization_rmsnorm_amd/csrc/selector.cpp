@@ -68,6 +68,31 @@ constexpr int64_t kColsMaxBytes = int64_t(6) << 20;
 // column workgroups fold two sums with a wavefront each, so they need at
 // least 128 threads.
 constexpr int64_t kColsMaxRowsPerProgramLN = 4;
+// Rows of more than 512 16-byte chunks (bf16 4097-8192, fp32 2049-4096
+// wide): the one-chunk layout needs 1024 lanes, a whole compute unit, so the
+// column workgroups can only start once the row programs are done.  With two
+// chunks per lane, gamma re-read per row and 512 lanes, they run beside the
+// row programs.  Measured on MI355X (one launch at 1024 lanes / at 512 lanes
+// with two chunks, one row ahead; bf16 unless noted), RMSNorm: 256 x 8192
+// 7.81 / 6.41 us, 512 x 8192 10.31 / 8.84, fp32 512 x 4096 9.49 / 8.57;
+// against the two-stage backward 768 x 8192 13.96 / 12.42, fp32 768 x 4096
+// 13.30 / 11.97, 1024 x 8192 15.63 / 15.25, but fp32 1024 x 4096 14.96 /
+// 15.21 and 1536 x 8192 19.55 / 21.26; in a second run against the
+// two-stage backward 1024 x 8192 15.67 / 15.54 and 1024 x 7168 14.42 /
+// 14.92.  So RMSNorm rows of this width take one launch up to three rows per
+// program.  With fewer rows
+// than programs, or at 768 lanes, the compute units without a row program
+// already take the column workgroups, and half the lanes cost RMSNorm time
+// (128 x 8192 5.07 / 5.28 us, 300 x 6144 6.27 / 6.76): it takes them above
+// 768 lanes (measured at 1024; at 896 the row program likewise leaves no
+// room for a second workgroup of its size) from one row per program on.  LayerNorm, whose rows hold two
+// sums, takes them from 768 lanes on: 512 x 8192 12.37 / 9.60, 768 x 8192
+// 15.70 / 13.20, 1024 x 8192 19.10 / 16.34, 300 x 6144 8.49 / 7.25, 128 x
+// 8192 5.95 / 5.88 (and the two-stage 1536 x 8192 23.45 / 22.27).  At 512
+// chunks (bf16 4096) two chunks at 256 lanes gained only 4% (768 x 4096
+// 8.05 / 7.75 us).
+constexpr int kColsHalfLanesAbove = 512;
+constexpr int kColsHalfLanesAboveRMS = 768;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -363,7 +388,7 @@ bool complete_plan(rmsnorm_plan *p, int64_t M, int64_t N, int dtype, int num_cus
     if (p->w_regs != 0 && p->w_regs != 1)
         return false;
     const bool cols = p->path == RMSNORM_PATH_ROWS_COLS;
-    if (cols && (!bwd || p->team != 0 || p->vec == 1 || p->w_regs != 1))
+    if (cols && (!bwd || p->team != 0 || p->vec == 1))
         return false;
     if (!cols)
         p->col_chunks = 0;
@@ -555,14 +580,27 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
             p.depth = 0;
     }
     const bool ln = is_ln_op(op);
-    if (placed && bwd && p.path == RMSNORM_PATH_ROWS && bwd_cols_layout(p.team, p.chunks, p.w_regs, p.vec) &&
-        p.threads >= (ln ? 128 : 64) && M >= 1) {
+    if (placed && bwd && p.path == RMSNORM_PATH_ROWS && p.chunks == 1 &&
+        bwd_cols_layout(p.team, p.chunks, p.w_regs, p.vec) && p.threads >= (ln ? 128 : 64) && M >= 1) {
         const int64_t programs = (int64_t)kBwdProgramsPerCU * std::max(num_cus, 1);
         const int64_t bytes = M * N * elem_bytes(dtype);
+        // rows of more than 512 chunks: the row programs take two chunks per
+        // lane with gamma re-read, at half the lanes (kColsHalfLanesAbove)
+        const int b2 = bound(op, vec, 0, 2, 1, 0);
+        const bool half = (ln ? p.threads > kColsHalfLanesAbove : (p.threads > kColsHalfLanesAboveRMS && M >= programs)) &&
+                          b2 >= p.threads / 2 && tiling_ok(op, dtype, vec, 0, 2, b2, p.threads / 2, nchunks);
+        const int64_t rms_rows = half ? 3 : 2;
         if (ln ? M <= kColsMaxRowsPerProgramLN * programs
-               : (M <= 2 * programs || (M <= 4 * programs && bytes <= kColsMaxBytes))) {
+               : (M <= rms_rows * programs || (M <= 4 * programs && bytes <= kColsMaxBytes))) {
             p.path = RMSNORM_PATH_ROWS_COLS;
             p.col_chunks = 0; // the rule in complete_plan
+            if (half) {
+                p.threads /= 2;
+                p.chunks = 2;
+                p.w_regs = 0;
+                p.depth = 1;
+                p.rows_per_step = 1;
+            }
         }
     }
     if (!complete_plan(&p, M, N, dtype, num_cus, false))
