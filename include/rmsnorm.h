@@ -153,8 +153,9 @@ int rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *bytes);
 /* Backward (FlyDSL PR #855 "Hybrid atomic / two-stage backward"): a bounded
  * persistent grid writes dx and float32 dgamma partials into `workspace`, then
  * a finalizer sums the partials in a fixed order and writes dgamma in T.
- * With few rows (up to two per program, or four while the rows hold at most
- * 6 MiB; the plan's path is then RMSNORM_PATH_ROWS_COLS) one launch does both:
+ * With few rows (up to two per program, four while the rows hold at most
+ * 6 MiB, three on rows of more than 768 16-byte chunks; the plan's path is
+ * then RMSNORM_PATH_ROWS_COLS) one launch does both:
  * its first workgroups write dx, the others sum
  * dgamma_j = sum_i dy_ij * x_ij * rstd_i directly by columns, in a fixed
  * order, and no partial rows are written.  Either way dgamma is
@@ -240,7 +241,8 @@ typedef enum rmsnorm_path {
     RMSNORM_PATH_ROWS = 0, /* each row held in registers by a team of lanes */
     RMSNORM_PATH_LOOP = 1, /* rows streamed in passes (any N) */
     RMSNORM_PATH_ROWS_COLS = 2 /* backward with few rows: dx as on the ROWS path
-                                  (workgroup teams, w in registers, one chunk per lane),
+                                  (workgroup teams, one chunk per lane with w in
+                                  registers, or two with gamma re-read),
                                   and dgamma summed directly by fin_grid column workgroups
                                   of the same launch, each owning col_chunks consecutive
                                   chunks of the row over all rows: no partial rows and no
