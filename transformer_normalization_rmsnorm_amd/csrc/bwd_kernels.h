@@ -33,6 +33,13 @@
 // dx = rstd * (g - mean(g) - xhat * mean(g * xhat)) [+ dh]; each program keeps
 // two accumulator sets, dgamma (dy * xhat) and dbeta (dy), and writes two
 // partial rows, which the finalizer folds with a second row of workgroups.
+//
+// With few rows per program one launch does both (the COLS instances, plan
+// path RMSNORM_PATH_ROWS_COLS): dgamma_j needs no row sum, so workgroups after
+// the row programs each read dy and x over all rows for a slab of columns
+// and write dgamma (and dbeta) directly, in a fixed order.  The row programs
+// then write no partial rows, and load their rows through the cache, where
+// that second read finds them.
 #pragma once
 
 #include "device_common.h"
@@ -172,7 +179,7 @@ template <typename T, int V, int TEAM, int K, int D, bool WR, int BOUND, bool FU
 __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
 {
     if constexpr (COLS) {
-        static_assert(bwd_cols_layout(TEAM, K, WR, V), "column workgroups need one chunk per lane, w in registers");
+        static_assert(bwd_cols_layout(TEAM, K, WR, V), "column workgroups run beside the layouts bwd_cols_layout names");
         if (blockIdx.x >= a.grid) {
             dgamma_columns<T, V, LN>(a);
             return;
