@@ -277,6 +277,20 @@ def test_one_launch_backward_rule(M, N, dt, fused, path, cs, ln_path, ln_cs):
         assert plan(op, M, N, dt, vec_ok=False)["path"] != COLS
 
 
+def test_every_backward_width_has_a_plan_around_the_one_launch_rule():
+    """Every backward op plans every width from 64 to 8192 bf16 / 4096 fp32
+    (whole and ragged chunks) at the row counts where the one-launch rule
+    changes, and its one-launch layouts are whole wavefronts."""
+    for dt, vec in ((rn.BF16, 8), (rn.F32, 4)):
+        for N in list(range(64 * vec, 1024 * vec + 1, 8 * vec)) + [1000 * vec + 8, 777 * vec, 513 * vec]:
+            for M in (1, 200, 256, 300, 512, 600, 768, 1024, 1100):
+                for op in (rn.OP_BWD, rn.OP_FUSED_ADD_BWD, rn.OP_LN_BWD, rn.OP_LN_FUSED_ADD_BWD):
+                    p = plan(op, M, N, dt)
+                    assert p["threads"] % 64 == 0 and covers(p, N), (op, M, N, dt, p)
+                    if p["path"] == COLS:
+                        assert p["col_chunks"] in (1, 2, 4, 8) and p["programs"] == 0
+
+
 def test_one_launch_backward_workspace_covers_the_two_stage_layout():
     """rmsnorm_bwd_workspace_bytes stays the two-stage size, which the stage
     entry point (rmsnorm_bwd_partials) needs for the same shapes."""

@@ -588,7 +588,8 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
         // lane with gamma re-read, at half the lanes (kColsHalfLanesAbove)
         const int b2 = bound(op, vec, 0, 2, 1, 0);
         const bool half = (ln ? p.threads > kColsHalfLanesAbove : (p.threads > kColsHalfLanesAboveRMS && M >= programs)) &&
-                          b2 >= p.threads / 2 && tiling_ok(op, dtype, vec, 0, 2, b2, p.threads / 2, nchunks);
+                          (p.threads / 2) % 64 == 0 && b2 >= p.threads / 2 &&
+                          tiling_ok(op, dtype, vec, 0, 2, b2, p.threads / 2, nchunks);
         const int64_t rms_rows = half ? 3 : 2;
         if (ln ? M <= kColsMaxRowsPerProgramLN * programs
                : (M <= rms_rows * programs || (M <= 4 * programs && bytes <= kColsMaxBytes))) {
