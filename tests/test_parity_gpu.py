@@ -314,7 +314,8 @@ def test_one_launch_backward(M, N, dt, fields, fused):
 
 @pytest.mark.parametrize("M,N,dt,fused", [(1024, 2048, "bf16", False), (768, 4096, "bf16", True),
                                           (512, 8192, "bf16", False), (768, 2048, "f32", False),
-                                          (768, 8192, "bf16", True), (768, 4096, "f32", False)])
+                                          (768, 8192, "bf16", True), (768, 4096, "f32", False),
+                                          (512, 6656, "bf16", False)])  # 832 lanes: not halved
 def test_one_launch_backward_default_shapes(M, N, dt, fused):
     op = rn.OP_FUSED_ADD_BWD if fused else rn.OP_BWD
     assert rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)["path"] == rn.PATH_ROWS_COLS
