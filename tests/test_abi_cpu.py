@@ -226,9 +226,9 @@ def test_plans_for_workloads(M, N, dt, fused):
 # One-launch backward (PATH_ROWS_COLS): rows of one chunk per lane with w in
 # registers, or of more than 512 chunks two chunks per lane at half the lanes
 # with gamma re-read; RMSNorm up to two rows per program, or four with at most
-# 6 MiB of rows, or three at more than 768 chunks; LayerNorm up to
-# four; the slab rule: max(threads / M, chunks / CUs) as a power of two, at
-# most 8.
+# 6 MiB of rows, or three at more than 768 chunks; LayerNorm up to four, or
+# five at more than 512 chunks; the slab rule: max(threads / M, chunks / CUs)
+# as a power of two, at most 8.
 COLS, ROWS = rn.PATH_ROWS_COLS, rn.PATH_ROWS
 COLS_CASES = [  # (M, N, dtype, fused, RMSNorm path, col_chunks, LayerNorm path, col_chunks)
     (1, 2048, rn.BF16, False, COLS, 8, COLS, 8), (64, 2048, rn.BF16, False, COLS, 4, COLS, 4),
@@ -244,11 +244,12 @@ COLS_CASES = [  # (M, N, dtype, fused, RMSNorm path, col_chunks, LayerNorm path,
     (1024, 2048, rn.BF16, False, COLS, 1, COLS, 1), (1024, 1536, rn.BF16, False, COLS, 1, COLS, 1),
     (1024, 4096, rn.BF16, False, ROWS, 0, COLS, 2), (1024, 2048, rn.F32, False, ROWS, 0, COLS, 2),
     # rows of more than 512 chunks: two chunks per lane at half the lanes, up to three rows per
-    # program for RMSNorm, four for LayerNorm
+    # program for RMSNorm, five for LayerNorm
     (768, 8192, rn.BF16, False, COLS, 4, COLS, 4), (1024, 8192, rn.BF16, False, ROWS, 0, COLS, 4),
     (768, 8192, rn.BF16, True, COLS, 4, COLS, 4), (768, 4096, rn.F32, False, COLS, 4, COLS, 4),
-    (1024, 7168, rn.BF16, False, ROWS, 0, COLS, 4),
-    (1024, 4096, rn.F32, False, ROWS, 0, COLS, 4), (1280, 8192, rn.BF16, False, ROWS, 0, ROWS, 0),
+    (1024, 7168, rn.BF16, False, ROWS, 0, COLS, 4), (1280, 8192, rn.BF16, True, ROWS, 0, COLS, 4),
+    (1280, 4096, rn.F32, False, ROWS, 0, COLS, 4), (1536, 8192, rn.BF16, False, ROWS, 0, ROWS, 0),
+    (1024, 4096, rn.F32, False, ROWS, 0, COLS, 4), (1280, 8192, rn.BF16, False, ROWS, 0, COLS, 4),
     (300, 6144, rn.BF16, False, COLS, 4, COLS, 4), (128, 8192, rn.BF16, False, COLS, 8, COLS, 4),
     # more rows per program: two stages
     (1536, 4096, rn.BF16, False, ROWS, 0, ROWS, 0), (2048, 2048, rn.BF16, False, ROWS, 0, ROWS, 0),

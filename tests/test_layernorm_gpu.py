@@ -179,7 +179,8 @@ def test_layernorm_one_launch_backward(M, N, dt, fields, fused):
 @pytest.mark.parametrize("M,N,dt,fused", [(768, 4096, "bf16", False), (768, 2048, "bf16", True),
                                           (512, 8192, "bf16", False), (600, 1024, "f32", True),
                                           (1024, 8192, "bf16", False), (1024, 2048, "f32", False),
-                                          (600, 4608, "bf16", True)])  # 576 lanes: not halved
+                                          (600, 4608, "bf16", True),  # 576 lanes: not halved
+                                          (1280, 8192, "bf16", True)])  # five rows per program
 def test_layernorm_one_launch_backward_is_the_default_for_few_rows(M, N, dt, fused):
     op = rn.OP_LN_FUSED_ADD_BWD if fused else rn.OP_LN_BWD
     assert rn.rmsnorm_query_plan(op, M, N, CODE[dt], True)["path"] == rn.PATH_ROWS_COLS

@@ -93,6 +93,12 @@ constexpr int64_t kColsMaxRowsPerProgramLN = 4;
 // 8.05 / 7.75 us).
 constexpr int kColsHalfLanesAbove = 512;
 constexpr int kColsHalfLanesAboveRMS = 768;
+// LayerNorm at half the lanes pays off up to five rows per program: against
+// the two-stage backward 1280 x 8192 21.87 / 19.26 us, fused-add 25.56 /
+// 23.15, fp32 1280 x 4096 19.34 / 18.71, 1280 x 6144 17.65 / 17.25; six
+// 1536 x 8192 -5% but fp32 1536 x 4096 +1% and 1536 x 6144 +2.5%; eight
+// (2048 x 8192) +3.6%.
+constexpr int64_t kColsMaxRowsPerProgramLNHalf = 5;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -591,7 +597,7 @@ int select_plan(int op, int64_t M, int64_t N, int dtype, bool vec_ok, int num_cu
                           (p.threads / 2) % 64 == 0 && b2 >= p.threads / 2 &&
                           tiling_ok(op, dtype, vec, 0, 2, b2, p.threads / 2, nchunks);
         const int64_t rms_rows = half ? 3 : 2;
-        if (ln ? M <= kColsMaxRowsPerProgramLN * programs
+        if (ln ? M <= (half ? kColsMaxRowsPerProgramLNHalf : kColsMaxRowsPerProgramLN) * programs
                : (M <= rms_rows * programs || (M <= 4 * programs && bytes <= kColsMaxBytes))) {
             p.path = RMSNORM_PATH_ROWS_COLS;
             p.col_chunks = 0; // the rule in complete_plan
