@@ -55,7 +55,8 @@ int layernorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype, size_t *bytes
 /* LayerNorm backward: a bounded persistent grid writes dx and the dgamma and
  * dbeta partials into `workspace`; a finalizer sums each set in a fixed
  * order and writes dgamma and dbeta in T.  With up to four rows per program
- * (plan path RMSNORM_PATH_ROWS_COLS) one launch does both: its first
+ * (five on rows of more than 512 16-byte chunks; plan path
+ * RMSNORM_PATH_ROWS_COLS) one launch does both: its first
  * workgroups write dx, the others sum dgamma_j = sum_i dy_ij * xhat_ij and
  * dbeta_j = sum_i dy_ij directly by columns in a fixed order, and the
  * workspace holds only recomputed mean and rstd.
