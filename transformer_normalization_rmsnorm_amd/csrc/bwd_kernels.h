@@ -211,7 +211,9 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
     float w[KW][V], acc[K][V]; // w = gamma + offset, or 1 for the non-affine op
     float accb[KB][V];         // LayerNorm: the dbeta accumulators (in registers)
     extern __shared__ float4 lds_db[]; // [NPL][nchunks] when BL
-    if constexpr (BL) {
+    // (COLS: the column workgroups sum dgamma and dbeta; the row programs
+    // accumulate nothing)
+    if constexpr (BL && !COLS) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int c = k * tl + lane;
@@ -352,11 +354,12 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
                     if constexpr (FUSED)
                         dxv += b.dh[k].get(e);
                     o[e] = dxv;
-                    acc[k][e] = fmaf(d, xh, acc[k][e]);
-                    if constexpr (LN && !BL)
+                    if constexpr (!COLS)
+                        acc[k][e] = fmaf(d, xh, acc[k][e]);
+                    if constexpr (LN && !BL && !COLS)
                         accb[k][e] += d;
                 }
-                if constexpr (BL) {
+                if constexpr (BL && !COLS) {
 #pragma unroll
                     for (int h = 0; h < NPL; ++h) {
                         float4 t = lds_db[h * nchunks + c];
@@ -420,7 +423,8 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
                     if constexpr (FUSED)
                         dxv += b.dh[k].get(e);
                     o[e] = dxv;
-                    acc[k][e] = fmaf(d, xv * rs, acc[k][e]);
+                    if constexpr (!COLS)
+                        acc[k][e] = fmaf(d, xv * rs, acc[k][e]);
                 }
                 Chunk<T, V> out;
                 out.set(o);
@@ -465,8 +469,10 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
                         const float d = elem(b.dy[0], e);
                         const float xh = (elem(b.v[0], e) - mu) * rs;
                         o[e] = rs * fmaf(-xh, c2, d * weight(b, 0, e) - c1);
-                        acc[0][e] = fmaf(d, xh, acc[0][e]);
-                        accb[0][e] += d;
+                        if constexpr (!COLS) {
+                            acc[0][e] = fmaf(d, xh, acc[0][e]);
+                            accb[0][e] += d;
+                        }
                     }
                     Chunk<T, V> out;
                     out.set(o);
@@ -505,7 +511,8 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
                         o[e] = fmaf(rs, d * weight(b, 0, e), -xv * kc);
                         if constexpr (FUSED)
                             o[e] += b.dh[0].get(e);
-                        acc[0][e] = fmaf(d, xv * rs, acc[0][e]);
+                        if constexpr (!COLS)
+                            acc[0][e] = fmaf(d, xv * rs, acc[0][e]);
                     }
                     Chunk<T, V> out;
                     out.set(o);
@@ -537,6 +544,8 @@ __global__ void __launch_bounds__(BOUND) bwd_rows_kernel(BwdArgs a)
         row_pipeline<D, Row>((int64_t)blockIdx.x * tpb + team, a.grid * tpb, a.M, load, proc);
     }
 
+    if constexpr (COLS)
+        return; // the column workgroups write dgamma and dbeta
     if (a.partials == nullptr) // no dgamma (non-affine) and no dbeta
         return;
     float *__restrict__ part = a.partials + (int64_t)blockIdx.x * a.ld;
